@@ -1,0 +1,123 @@
+"""Adaptive KV Selection, written plainly (oracle; test infrastructure only).
+
+Follows the FlashVDM summary page, section 4.1 item 2: split the decoded
+volume into sub-volumes; in each, a few probe queries attend to every latent
+token; the attention scores pick the top-K tokens for that sub-volume; every
+other query of the sub-volume attends only to those tokens. The techwalker
+article (part 5) describes the same probe-then-reuse scheme.
+
+Readings (the pages leave these open):
+  * sub-volumes are blocks of 8x8x8 grid points of the current level (block
+    b spans indices 8b .. min(8b+7, R) on each axis), at every level;
+  * the probes are the block's 8 corner points (the pages sample random
+    queries; corners make the selection deterministic);
+  * a token's score for a probe is the head-mean of its softmax probability;
+  * each probe keeps its top-k tokens (ties go to the lower token index); the
+    block keeps the union; if the union exceeds ``cap`` tokens, those with the
+    largest max-over-probes score are kept (ties to the lower index);
+  * the kept set is stored in ascending token order;
+  * ranking uses float32 scores (the precision a GPU kernel ranks in).
+"""
+
+from __future__ import annotations
+
+import itertools
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import decoder as dec
+from . import hvd as hv
+
+
+def block_corner_indices(R: int, bijk: np.ndarray, block: int = 8) -> np.ndarray:
+    """[nblk, 8, 3] grid indices of the 8 corner probes of blocks (bi, bj, bk).
+    Corner order: i in {lo, hi} outermost, then j, then k."""
+    bijk = np.asarray(bijk, np.int64).reshape(-1, 3)
+    lo = bijk * block
+    hi = np.minimum(lo + block - 1, R)
+    out = np.empty((bijk.shape[0], 8, 3), np.int64)
+    for n, (a, b, c) in enumerate(itertools.product((0, 1), repeat=3)):
+        out[:, n, 0] = np.where(a, hi[:, 0], lo[:, 0])
+        out[:, n, 1] = np.where(b, hi[:, 1], lo[:, 1])
+        out[:, n, 2] = np.where(c, hi[:, 2], lo[:, 2])
+    return out
+
+
+def block_ijk(b: np.ndarray, NB: int) -> np.ndarray:
+    b = np.asarray(b, np.int64)
+    bi, r = np.divmod(b, NB * NB)
+    bj, bk = np.divmod(r, NB)
+    return np.stack([bi, bj, bk], axis=-1)
+
+
+def probe_scores(Qp: np.ndarray, K: np.ndarray, H: int) -> np.ndarray:
+    """[n_probe, M]: mean over heads of each probe's softmax probability."""
+    return dec.attention_probs(np.asarray(Qp, np.float64), np.asarray(K, np.float64), H).mean(axis=0)
+
+
+def topk_ids(score: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores; equal scores go to the lower index."""
+    M = score.shape[0]
+    order = np.lexsort((np.arange(M), -score))  # primary: score descending
+    return order[:k]
+
+
+def select(scores: np.ndarray, k: int, cap: int) -> np.ndarray:
+    """Ascending token set for one block from its probes' scores [n_probe, M]."""
+    s32 = np.asarray(scores, np.float64).astype(np.float32)
+    union = np.unique(np.concatenate([topk_ids(s, k) for s in s32]))
+    if union.size > cap:
+        key = s32[:, union].max(axis=0)
+        order = np.lexsort((union, -key))
+        union = np.sort(union[order[:cap]])
+    return union
+
+
+def near_tie_tokens(scores: np.ndarray, k: int, rel: float = 1e-4) -> np.ndarray:
+    """Tokens whose score, for some probe, lies within ``rel`` (relative) of
+    that probe's k-th largest score: their membership can flip under a
+    perturbation of that size."""
+    s = np.asarray(scores, np.float64)
+    amb = np.zeros(s.shape[1], bool)
+    for row in s:
+        kth = np.sort(row)[::-1][k - 1]
+        amb |= np.abs(row - kth) <= rel * abs(kth)
+    return np.flatnonzero(amb)
+
+
+def select_blocks(decoder: dec.Decoder, R: int, blocks: np.ndarray, k: int, cap: int,
+                  block: int = 8, Qfn=None) -> Dict[int, np.ndarray]:
+    """Token sets for the given block ids of the R-cell grid. ``Qfn`` maps
+    float32 probe points to projections (default: the oracle's own)."""
+    NB = hv.nblocks(R + 1, block)
+    idx = block_corner_indices(R, block_ijk(blocks, NB), block)
+    out = {}
+    for n, b in enumerate(np.asarray(blocks, np.int64)):
+        pts = dec.grid_coord(idx[n], R).astype(np.float32)
+        Qp = decoder.q(pts) if Qfn is None else Qfn(pts)
+        out[int(b)] = select(probe_scores(Qp, decoder.K, decoder.H), k, cap)
+    return out
+
+
+def make_decode(decoder: dec.Decoder, k: int, cap: int, block: int = 8, record: Optional[dict] = None):
+    """A ``decode(R, lin)`` for ``hvd.hvd`` that groups the queries by block,
+    selects each block's tokens with its corner probes, and decodes the
+    block's queries against those tokens only."""
+
+    def decode(R: int, lin: np.ndarray) -> np.ndarray:
+        P = R + 1
+        blk = hv.block_of(lin, P, block)
+        ub = np.unique(blk)
+        sets = select_blocks(decoder, R, ub, k, cap, block)
+        if record is not None:
+            record[R] = sets
+        out = np.empty(lin.size, np.float64)
+        pts = dec.grid_points(R, lin)
+        for b in ub:
+            m = blk == b
+            sel = sets[int(b)]
+            out[m] = decoder.sdf(pts[m], decoder.K[sel], decoder.V[sel])
+        return out
+
+    return decode
