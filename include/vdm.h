@@ -1,0 +1,248 @@
+/*
+ * vdm.h -- C ABI of the MI355X (gfx950) vecset SDF decoder library (libvdm.so).
+ *
+ * What the calls compute follows the FlashVDM pages:
+ *   - "Unleashing Vecset Diffusion Model for Fast Shape Generation" (aipaper.cc
+ *     summary), section 3: a vecset is an unordered set of latent tokens; the
+ *     decoder cross-attends from any query point to the tokens and yields the
+ *     SDF there.
+ *   - same page, section 4.1 "Lightning Vecset Decoder":
+ *       item 1, Hierarchical Volume Decoding (coarse volume, sign-change voxels,
+ *       truncated-SDF band for thin parts, one dilation, refine only selected
+ *       voxels, repeat to the target resolution);
+ *       item 2, Adaptive KV Selection (per sub-volume, probe queries attend to
+ *       all tokens, the top-K tokens serve every query of that sub-volume,
+ *       queries of different sub-volumes packed together);
+ *       item 3, the slim decoder (narrow width, low MLP ratio, no LayerNorm).
+ *   - the techwalker article on FlashVDM, parts 2 and 5 (same three pieces;
+ *     regions wholly inside/outside keep their label without detailed queries).
+ *
+ * Decoder (readings of details the pages leave open are listed where they apply):
+ *   e(p)  = [x, y, z, sin(f_k x).., sin(f_k y).., sin(f_k z).., cos(..same..)],
+ *           f_k = 2^k * pi, k = 0..7; 51 features; the argument is the float32
+ *           product f_k * c
+ *   q     = Wq e;   k_j = Wk z_j;   v_j = Wv z_j        (no biases)
+ *   o_h   = softmax_j(q_h . k_hj / 8) v_hj, heads of 64 columns
+ *   a     = Wo o;   y = a + W2 GELU(W1 a) (exact-erf GELU);   net = w_head . y
+ *   SDF   = analytic(p) + net_scale * net, analytic = min over primitives of the
+ *           sphere / box signed distance.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, row-major, and
+ *     16-byte aligned (xyz and list: 4-byte aligned). The library keeps no
+ *     pointer after a call returns.
+ *   - Scratch memory is a caller-provided device workspace of at least the size
+ *     the matching vdm_*_workspace_size() returns (256-byte aligned). Nothing is
+ *     allocated by the library.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronises it.
+ *   - Every call returns a vdm_status and never aborts; on failure,
+ *     vdm_last_error() (thread-local) describes it and no kernel was launched
+ *     (VDM_ERR_HIP: a launch failed; earlier launches of that call may have run).
+ *   - N = 0 queries is a successful no-op.
+ *   - Supported decoders: n_freq = 8; dtype BF16 with D = 64 or 256, or F32 with
+ *     D = 64; H = D / 64; F a multiple of 128 (BF16, D = 256) or 64 (D = 64),
+ *     at most 4096; M >= 1 tokens.
+ *   - NaN/Inf in inputs propagate to the affected outputs; a NaN SDF value never
+ *     makes a voxel active (every comparison with NaN is false).
+ */
+#ifndef VDM_H
+#define VDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VDM_VERSION 1
+#define VDM_MAX_PRIMS 16
+#define VDM_MAX_LEVELS 6
+#define VDM_E_DIM 51
+
+typedef void* vdm_stream; /* hipStream_t */
+
+typedef enum {
+  VDM_OK = 0,
+  VDM_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, bad parameter */
+  VDM_ERR_UNSUPPORTED = -2, /* decoder dims / dtype outside the supported set */
+  VDM_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  VDM_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} vdm_status;
+
+typedef enum { VDM_F32 = 0, VDM_BF16 = 1 } vdm_dtype;
+
+typedef enum { VDM_PRIM_SPHERE = 0, VDM_PRIM_BOX = 1 } vdm_prim_kind;
+
+/* One analytic primitive of the SDF prior.
+ * SPHERE: size[0] = radius (size[1..2] ignored).  BOX: size = half extents. */
+typedef struct {
+  int32_t kind;
+  float centre[3];
+  float size[3];
+} vdm_prim;
+
+/* A decoder instance. Weight pointers are device pointers in `dtype`,
+ * row-major [out, in]; w_head is float32 [D]. */
+typedef struct {
+  int32_t D;        /* width = 64 * H */
+  int32_t H;        /* attention heads of 64 columns */
+  int32_t F;        /* MLP hidden width */
+  int32_t n_freq;   /* Fourier frequencies per axis; must be 8 */
+  int32_t dtype;    /* vdm_dtype of weights, latents, Q, K and V */
+  float net_scale;  /* SDF = analytic + net_scale * net */
+  const void* Wq;   /* [D, 51] */
+  const void* Wk;   /* [D, D]  */
+  const void* Wv;   /* [D, D]  */
+  const void* Wo;   /* [D, D]  */
+  const void* W1;   /* [F, D]  */
+  const void* W2;   /* [D, F]  */
+  const float* w_head; /* [D], float32 */
+  int32_t n_prims;  /* 1 .. VDM_MAX_PRIMS */
+  vdm_prim prims[VDM_MAX_PRIMS];
+} vdm_decoder;
+
+/* Where the queries are.
+ * Grid point (i, j, k) of an R-cell grid (R + 1 points per axis) over [-1, 1]^3
+ * has coordinates c = float32((2i - R) / R) per axis and row-major linear index
+ * (i * (R + 1) + j) * (R + 1) + k (x slowest, z fastest). */
+typedef enum {
+  VDM_Q_POINTS = 0,    /* xyz[N, 3] float32 */
+  VDM_Q_GRID = 1,      /* every grid point in linear order; N must be (R + 1)^3 */
+  VDM_Q_GRID_LIST = 2  /* list[N] int32 linear grid indices */
+} vdm_qmode;
+
+typedef struct {
+  int32_t mode;          /* vdm_qmode */
+  int32_t R;             /* grid modes: cells per axis, 1 .. 4096 */
+  int64_t N;             /* number of queries */
+  const float* xyz;      /* VDM_Q_POINTS */
+  const int32_t* list;   /* VDM_Q_GRID_LIST */
+} vdm_queries;
+
+/* Per-block token sets for decoding with adaptive KV selection.
+ * Block b of an R-cell grid groups points whose indices lie in
+ * [block*bi, block*bi + block - 1] per axis (clipped to R); blocks are numbered
+ * b = (bi * NB + bj) * NB + bk with NB = ceil((R + 1) / block). */
+typedef struct {
+  int32_t block;            /* block edge in grid points (8) */
+  int32_t cap;              /* row stride of sel_idx */
+  const int32_t* sel_idx;   /* [rows, cap] ascending token ids (first sel_cnt valid) */
+  const int32_t* sel_cnt;   /* [rows], 1 .. cap */
+  const int32_t* block_row; /* [NB^3] block id -> row of sel_idx, or NULL (row = block id) */
+} vdm_kvsel;
+
+/* Hierarchical decoding parameters. Level L has R0 * 2^L cells per axis. */
+typedef struct {
+  int32_t R0;        /* coarse cells per axis (75) */
+  int32_t levels;    /* 1 .. VDM_MAX_LEVELS (3: 75 -> 150 -> 300) */
+  int32_t dilation;  /* 3x3x3 dilations applied to the active cells (1) */
+  float tau;         /* band: a tested cell is active if min |SDF| over its corners < tau */
+  int32_t use_kvsel; /* 0: full attention; 1: adaptive KV selection at every level */
+  int32_t block;     /* KV selection block edge in points (8) */
+  int32_t k;         /* tokens kept per probe (64) */
+  int32_t cap;       /* token cap per block (512) */
+} vdm_hier_params;
+
+/* Per-level counters written by vdm_decode_hier to a DEVICE array of int64:
+ * stats[L * VDM_STAT_FIELDS + field]. */
+enum {
+  VDM_STAT_R = 0,       /* cells per axis */
+  VDM_STAT_TESTED = 1,  /* cells whose 8 corners were all computed */
+  VDM_STAT_ACTIVE = 2,  /* tested cells with a sign change or min |s| < tau */
+  VDM_STAT_KEPT = 3,    /* cells after dilation (0 on the last level) */
+  VDM_STAT_QUERIES = 4, /* points decoded at this level */
+  VDM_STAT_BLOCKS = 5,  /* blocks holding at least one query */
+  VDM_STAT_ITEMS = 6,   /* decode work items (block, query chunk) */
+  VDM_STAT_SELECTED = 7,/* sum over blocks of selected tokens (KV selection) */
+  VDM_STAT_FIELDS = 8
+};
+
+/* Optional DEVICE outputs of vdm_decode_hier for inspection (NULL = skip).
+ * Level L: R = R0 * 2^L, P = R + 1, NB = ceil(P / block). */
+typedef struct {
+  float* vol[VDM_MAX_LEVELS];       /* [P^3] volume after level L's decode */
+  uint8_t* active[VDM_MAX_LEVELS];  /* [R^3] 1 = active cell */
+  uint8_t* kept[VDM_MAX_LEVELS];    /* [R^3] 1 = kept after dilation */
+  int32_t* list[VDM_MAX_LEVELS];    /* [P^3] level L's query list (blocked order) */
+  int32_t* sel_blocks[VDM_MAX_LEVELS]; /* [NB^3] occupied block ids, ascending */
+  int32_t* sel_cnt[VDM_MAX_LEVELS];    /* [NB^3] selected tokens per occupied block */
+  int32_t* sel_idx[VDM_MAX_LEVELS];    /* [NB^3, cap] selected token ids */
+} vdm_hier_debug;
+
+/* ---------------------------------------------------------------- calls */
+
+/* Fused Fourier embedding + query projection (FlashVDM summary section 3; the
+ * decoder's first step). Q[n, :] = Wq e(xyz[n]) rounded to `dtype`.
+ * xyz: [N, 3] float32. Q: [N, D] in dtype. */
+vdm_status vdm_embed_queries(const vdm_decoder* dec, const float* xyz, int64_t N, void* Q,
+                             vdm_stream stream);
+
+/* Key/value projection of the vecset, once per shape (section 3: the tokens
+ * are projected for cross-attention). K = Z Wk^T, V = Z Wv^T rounded to dtype.
+ * Z, K, V: [M, D] in dtype. */
+vdm_status vdm_project_kv(const vdm_decoder* dec, const void* Z, int64_t M, void* K, void* V,
+                          vdm_stream stream);
+
+/* SDF at N query points (section 3; dense decoding, or with the token subsets of
+ * adaptive KV selection, section 4.1 item 2).
+ * K, V: [M, D] in dtype (from vdm_project_kv). sdf: [N] float32, sdf[n] for the
+ * n-th query. sel: NULL = full attention; otherwise queries must be
+ * VDM_Q_GRID_LIST entries sorted by blocked key (block id, then row-major inside
+ * the block; as vdm_decode_hier produces) and each query attends to its block's
+ * token set. Workspace: vdm_dense_workspace_size(dec, M, N, sel != NULL). */
+vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K,
+                            const void* V, int64_t M, const vdm_kvsel* sel, float* sdf, void* ws,
+                            size_t ws_bytes, vdm_stream stream);
+
+/* Adaptive KV selection (section 4.1 item 2) for blocks of an R-cell grid.
+ * For each listed block: its 8 corner points (indices block*b and
+ * min(block*b + block - 1, R) per axis) are probes; a token's score for a probe
+ * is the head-mean softmax probability; each probe keeps its top-k tokens (equal
+ * scores: lower index first); the block keeps their union, reduced to the `cap`
+ * tokens of largest max-over-probes score when larger (ties: lower index).
+ * Output row r (for blocks[r], or block r when blocks == NULL and
+ * nblk = NB^3): sel_idx[r, 0 .. sel_cnt[r]) ascending, rest -1.
+ * Requires 1 <= k <= M, k <= cap, M <= 4096. Workspace:
+ * vdm_select_workspace_size(dec, M). */
+vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,
+                         const void* K, int64_t M, const int32_t* blocks, int64_t nblk,
+                         int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes,
+                         vdm_stream stream);
+
+/* Hierarchical volume decoding (section 4.1 item 1), optionally with adaptive KV
+ * selection at every level (item 2). Writes the final (R0*2^(levels-1) + 1)^3
+ * float32 volume `vol` (vol_elems must be at least that), per-level counters to
+ * the device array `stats` ([levels * VDM_STAT_FIELDS] int64, may be NULL) and
+ * the optional inspection outputs `dbg` (may be NULL).
+ * Level 0 decodes every point. At each level, tested cells are active when their
+ * corner SDFs include both s < 0 and s >= 0 or min |s| < tau; active cells are
+ * dilated `dilation` times with the 3x3x3 stencil; every corner of every child of
+ * a kept cell that was not decoded before is decoded at the next level; every
+ * other point takes its nearest ancestor's value (the point (i/2, j/2, k/2) of the
+ * previous level, integer division). No host synchronisation. Workspace:
+ * vdm_hier_workspace_size(dec, params, M). */
+vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* params, const void* K,
+                           const void* V, int64_t M, float* vol, int64_t vol_elems,
+                           int64_t* stats, const vdm_hier_debug* dbg, void* ws, size_t ws_bytes,
+                           vdm_stream stream);
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Workspace bytes for the calls above (0 with vdm_last_error set on bad args). */
+size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, int32_t with_sel);
+size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M);
+size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M);
+
+/* VDM_VERSION of the built library. */
+int32_t vdm_version(void);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* vdm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDM_H */

@@ -1,0 +1,320 @@
+"""Python binding of libvdm.so, the gfx950 vecset SDF decoder (see include/vdm.h).
+
+Argument marshalling only: every step of the decoder runs in the library's HIP
+kernels. PyTorch supplies device memory and the current stream. Importing this
+module raises if the built library is missing; there is no fallback path.
+
+Functions carry the C names: vdm_embed_queries, vdm_project_kv,
+vdm_decode_dense, vdm_select_kv, vdm_decode_hier, plus the workspace-size
+helpers. ``Decoder`` bundles a vdm_decoder struct with the tensors it points to.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvdm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m shape_vae_decoding_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+VDM_OK, VDM_ERR_INVALID_ARG, VDM_ERR_UNSUPPORTED, VDM_ERR_WORKSPACE, VDM_ERR_HIP = 0, -1, -2, -3, -4
+VDM_F32, VDM_BF16 = 0, 1
+VDM_Q_POINTS, VDM_Q_GRID, VDM_Q_GRID_LIST = 0, 1, 2
+MAX_PRIMS, MAX_LEVELS, STAT_FIELDS = 16, 6, 8
+STAT_NAMES = ["R", "tested", "active", "kept", "queries", "blocks", "items", "selected"]
+EXPORTS = [
+    "vdm_embed_queries", "vdm_project_kv", "vdm_decode_dense", "vdm_select_kv", "vdm_decode_hier",
+    "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_version",
+    "vdm_last_error",
+]
+
+
+class VdmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"vdm status {status}: {msg}")
+        self.status = status
+
+
+class _Prim(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("centre", C.c_float * 3), ("size", C.c_float * 3)]
+
+
+class _Decoder(C.Structure):
+    _fields_ = [
+        ("D", C.c_int32), ("H", C.c_int32), ("F", C.c_int32), ("n_freq", C.c_int32), ("dtype", C.c_int32),
+        ("net_scale", C.c_float),
+        ("Wq", C.c_void_p), ("Wk", C.c_void_p), ("Wv", C.c_void_p), ("Wo", C.c_void_p),
+        ("W1", C.c_void_p), ("W2", C.c_void_p), ("w_head", C.c_void_p),
+        ("n_prims", C.c_int32), ("prims", _Prim * MAX_PRIMS),
+    ]
+
+
+class _Queries(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("R", C.c_int32), ("N", C.c_int64), ("xyz", C.c_void_p), ("list", C.c_void_p)]
+
+
+class _KvSel(C.Structure):
+    _fields_ = [("block", C.c_int32), ("cap", C.c_int32), ("sel_idx", C.c_void_p), ("sel_cnt", C.c_void_p),
+                ("block_row", C.c_void_p)]
+
+
+class _HierParams(C.Structure):
+    _fields_ = [("R0", C.c_int32), ("levels", C.c_int32), ("dilation", C.c_int32), ("tau", C.c_float),
+                ("use_kvsel", C.c_int32), ("block", C.c_int32), ("k", C.c_int32), ("cap", C.c_int32)]
+
+
+_PtrArr = C.c_void_p * MAX_LEVELS
+
+
+class _HierDebug(C.Structure):
+    _fields_ = [("vol", _PtrArr), ("active", _PtrArr), ("kept", _PtrArr), ("list", _PtrArr),
+                ("sel_blocks", _PtrArr), ("sel_cnt", _PtrArr), ("sel_idx", _PtrArr)]
+
+
+_st = C.c_int32
+_lib.vdm_embed_queries.argtypes = [C.POINTER(_Decoder), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+_lib.vdm_embed_queries.restype = _st
+_lib.vdm_project_kv.argtypes = [C.POINTER(_Decoder), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]
+_lib.vdm_project_kv.restype = _st
+_lib.vdm_decode_dense.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_void_p, C.c_void_p, C.c_int64,
+                                  C.POINTER(_KvSel), C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.vdm_decode_dense.restype = _st
+_lib.vdm_select_kv.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                               C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                               C.c_void_p]
+_lib.vdm_select_kv.restype = _st
+_lib.vdm_decode_hier.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_void_p, C.c_void_p, C.c_int64,
+                                 C.c_void_p, C.c_int64, C.c_void_p, C.POINTER(_HierDebug), C.c_void_p, C.c_size_t,
+                                 C.c_void_p]
+_lib.vdm_decode_hier.restype = _st
+_lib.vdm_dense_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64, C.c_int64, C.c_int32]
+_lib.vdm_dense_workspace_size.restype = C.c_size_t
+_lib.vdm_select_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64]
+_lib.vdm_select_workspace_size.restype = C.c_size_t
+_lib.vdm_hier_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int64]
+_lib.vdm_hier_workspace_size.restype = C.c_size_t
+_lib.vdm_version.restype = C.c_int32
+_lib.vdm_last_error.restype = C.c_char_p
+
+
+def vdm_version() -> int:
+    return int(_lib.vdm_version())
+
+
+def vdm_last_error() -> str:
+    return _lib.vdm_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != VDM_OK:
+        raise VdmError(status, vdm_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+class Decoder:
+    """A vdm_decoder plus the device tensors it points to.
+
+    weights: Wq [D,51], Wk/Wv/Wo [D,D], W1 [F,D], W2 [D,F] in the decoder dtype
+    and w_head [D] float32 (device tensors). prims: objects with .kind, .centre,
+    .size (sphere: size[0] = radius; box: half extents)."""
+
+    def __init__(self, weights: Dict[str, torch.Tensor], prims: Sequence, net_scale: float = 0.05):
+        wq = weights["Wq"]
+        self.torch_dtype = wq.dtype
+        dtype = {torch.bfloat16: VDM_BF16, torch.float32: VDM_F32}[wq.dtype]
+        D = wq.shape[0]
+        F = weights["W1"].shape[0]
+        self.tensors = {}
+        for k in ("Wq", "Wk", "Wv", "Wo", "W1", "W2"):
+            self.tensors[k] = _dev(weights[k], wq.dtype, k)
+        self.tensors["w_head"] = _dev(weights["w_head"], torch.float32, "w_head")
+        s = _Decoder()
+        s.D, s.H, s.F, s.n_freq, s.dtype = D, D // 64, F, 8, dtype
+        s.net_scale = float(net_scale)
+        for k, t in self.tensors.items():
+            setattr(s, k, t.data_ptr())
+        if len(prims) > MAX_PRIMS:
+            raise ValueError("too many primitives")
+        s.n_prims = len(prims)
+        for i, p in enumerate(prims):
+            s.prims[i].kind = int(p.kind)
+            for c in range(3):
+                s.prims[i].centre[c] = float(p.centre[c])
+                s.prims[i].size[c] = float(p.size[c])
+        self.struct = s
+        self.D, self.H, self.F, self.dtype = D, D // 64, F, dtype
+
+    @property
+    def ref(self):
+        return C.byref(self.struct)
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A device byte buffer usable as a workspace (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+# ---------------------------------------------------------------- calls
+
+def vdm_embed_queries(dec: Decoder, xyz: torch.Tensor, Q: torch.Tensor, stream=None) -> None:
+    _dev(xyz, torch.float32, "xyz")
+    _dev(Q, dec.torch_dtype, "Q")
+    _check(_lib.vdm_embed_queries(dec.ref, xyz.data_ptr(), xyz.shape[0], Q.data_ptr(), _stream(stream)))
+
+
+def vdm_project_kv(dec: Decoder, Z: torch.Tensor, K: torch.Tensor, V: torch.Tensor, stream=None) -> None:
+    for n, t in (("Z", Z), ("K", K), ("V", V)):
+        _dev(t, dec.torch_dtype, n)
+    _check(_lib.vdm_project_kv(dec.ref, Z.data_ptr(), Z.shape[0], K.data_ptr(), V.data_ptr(), _stream(stream)))
+
+
+def queries_points(xyz: torch.Tensor) -> _Queries:
+    _dev(xyz, torch.float32, "xyz")
+    return _Queries(VDM_Q_POINTS, 0, xyz.shape[0], xyz.data_ptr(), None)
+
+
+def queries_grid(R: int) -> _Queries:
+    return _Queries(VDM_Q_GRID, R, (R + 1) ** 3, None, None)
+
+
+def queries_list(R: int, lin: torch.Tensor) -> _Queries:
+    _dev(lin, torch.int32, "list")
+    return _Queries(VDM_Q_GRID_LIST, R, lin.shape[0], None, lin.data_ptr())
+
+
+def kvsel(block: int, cap: int, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+          block_row: Optional[torch.Tensor] = None) -> _KvSel:
+    _dev(sel_idx, torch.int32, "sel_idx")
+    _dev(sel_cnt, torch.int32, "sel_cnt")
+    if block_row is not None:
+        _dev(block_row, torch.int32, "block_row")
+    return _KvSel(block, cap, sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(block_row))
+
+
+def vdm_dense_workspace_size(dec: Decoder, M: int, N: int, with_sel: bool = False) -> int:
+    n = int(_lib.vdm_dense_workspace_size(dec.ref, M, N, int(with_sel)))
+    if n == 0:
+        raise VdmError(VDM_ERR_INVALID_ARG, vdm_last_error())
+    return n
+
+
+def vdm_select_workspace_size(dec: Decoder, M: int) -> int:
+    return int(_lib.vdm_select_workspace_size(dec.ref, M))
+
+
+def vdm_hier_workspace_size(dec: Decoder, params: _HierParams, M: int) -> int:
+    n = int(_lib.vdm_hier_workspace_size(dec.ref, C.byref(params), M))
+    if n == 0:
+        raise VdmError(VDM_ERR_INVALID_ARG, vdm_last_error())
+    return n
+
+
+def vdm_decode_dense(dec: Decoder, q: _Queries, K: torch.Tensor, V: torch.Tensor, sdf: torch.Tensor,
+                     sel: Optional[_KvSel] = None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    _dev(K, dec.torch_dtype, "K")
+    _dev(V, dec.torch_dtype, "V")
+    _dev(sdf, torch.float32, "sdf")
+    M = K.shape[0]
+    if ws is None:
+        ws = workspace(vdm_dense_workspace_size(dec, M, q.N, sel is not None), sdf.device)
+    _check(_lib.vdm_decode_dense(dec.ref, C.byref(q), K.data_ptr(), V.data_ptr(), M,
+                                 C.byref(sel) if sel is not None else None, sdf.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), _stream(stream)))
+
+
+def vdm_select_kv(dec: Decoder, R: int, block: int, k: int, cap: int, K: torch.Tensor,
+                  blocks: Optional[torch.Tensor], sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                  nblk: Optional[int] = None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    _dev(K, dec.torch_dtype, "K")
+    _dev(sel_idx, torch.int32, "sel_idx")
+    _dev(sel_cnt, torch.int32, "sel_cnt")
+    if blocks is not None:
+        _dev(blocks, torch.int32, "blocks")
+        nblk = blocks.shape[0]
+    elif nblk is None:
+        nb = -(-(R + 1) // block)
+        nblk = nb ** 3
+    _check(_lib.vdm_select_kv(dec.ref, R, block, k, cap, K.data_ptr(), K.shape[0], _ptr(blocks), nblk,
+                              sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(stream)))
+
+
+def hier_params(R0=75, levels=3, tau=2 * 2 / 300, dilation=1, kvsel: Optional[dict] = None) -> _HierParams:
+    p = _HierParams(R0, levels, dilation, float(tau), 0, 8, 64, 512)
+    if kvsel:
+        p.use_kvsel, p.block, p.k, p.cap = 1, kvsel.get("block", 8), kvsel["k"], kvsel["cap"]
+    return p
+
+
+class HierDebug:
+    """Device buffers for the inspection outputs of vdm_decode_hier."""
+
+    def __init__(self, params: _HierParams, device=None, with_sel: bool = False):
+        dev = device or "cuda"
+        self.levels = []
+        s = _HierDebug()
+        for L in range(params.levels):
+            R = params.R0 << L
+            P = R + 1
+            nb = -(-P // 8)
+            d = {
+                "vol": torch.empty(P ** 3, dtype=torch.float32, device=dev),
+                "active": torch.empty(R ** 3, dtype=torch.uint8, device=dev),
+                "kept": torch.zeros(R ** 3, dtype=torch.uint8, device=dev),
+                "list": torch.empty(P ** 3, dtype=torch.int32, device=dev),
+            }
+            if with_sel:
+                d["sel_blocks"] = torch.empty(nb ** 3, dtype=torch.int32, device=dev)
+                d["sel_cnt"] = torch.empty(nb ** 3, dtype=torch.int32, device=dev)
+                d["sel_idx"] = torch.empty(nb ** 3 * params.cap, dtype=torch.int32, device=dev)
+            for k, t in d.items():
+                getattr(s, k)[L] = t.data_ptr()
+            self.levels.append(d)
+        self.struct = s
+
+
+def vdm_decode_hier(dec: Decoder, params: _HierParams, K: torch.Tensor, V: torch.Tensor, vol: torch.Tensor,
+                    stats: Optional[torch.Tensor] = None, dbg: Optional[HierDebug] = None,
+                    ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    _dev(K, dec.torch_dtype, "K")
+    _dev(V, dec.torch_dtype, "V")
+    _dev(vol, torch.float32, "vol")
+    if stats is not None:
+        _dev(stats, torch.int64, "stats")
+    M = K.shape[0]
+    if ws is None:
+        ws = workspace(vdm_hier_workspace_size(dec, params, M), vol.device)
+    _check(_lib.vdm_decode_hier(dec.ref, C.byref(params), K.data_ptr(), V.data_ptr(), M, vol.data_ptr(),
+                                vol.numel(), _ptr(stats), C.byref(dbg.struct) if dbg is not None else None,
+                                ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def stats_dict(stats: torch.Tensor, levels: int):
+    s = stats.view(-1)[: levels * STAT_FIELDS].cpu().view(levels, STAT_FIELDS).tolist()
+    return [dict(zip(STAT_NAMES, row)) for row in s]

@@ -1,0 +1,451 @@
+// Hierarchical Volume Decoding: the memory-bound stages between two decodes.
+// FlashVDM summary page, section 4.1 item 1 (decode a coarse volume, find the
+// voxels the surface crosses by a sign change between neighbouring samples,
+// refine only those; key details: a truncated-SDF band keeps thin parts and one
+// dilation guards against discretisation misses); techwalker article, part 2
+// (wholly inside / outside regions keep their label without detailed queries).
+//
+// Bit masks use a blocked layout: point or cell (i, j, k) of a level with P
+// points per axis lives in 64-bit word ((bi*NB + bj)*NB + bk)*8 + i%8, bit
+// (j%8)*8 + k%8, with b = index/8 and NB = ceil(P/8). One 8x8x8 block is 8
+// words; a workgroup of 8 waves covers one block with one lane per point
+// (wave = i%8, lane = (j%8)*8 + k%8), so a wave ballot produces one word.
+// Query lists are emitted in this same block order (blocked key order).
+#include "vdm_device.hpp"
+#include "vdm_hvd.hpp"
+
+namespace vdm {
+
+__device__ __forceinline__ bool mask_bit(const uint64_t* m, int NB, int i, int j, int k) {
+  const int64_t w = ((int64_t)((i >> 3) * NB + (j >> 3)) * NB + (k >> 3)) * 8 + (i & 7);
+  return (m[w] >> (((j & 7) << 3) | (k & 7))) & 1ull;
+}
+
+__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* red, int tid, int nt) {
+  // workgroup sum in fixed order (LDS of nt/64 slots)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor((long long)v, o);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  int64_t s = 0;
+  if (tid == 0)
+    for (int w = 0; w < nt / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+__global__ void zero_u64_kernel(uint64_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0ull;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 8);
+  if (n <= 0) return hipSuccess;
+  int64_t g = (n + 255) / 256;
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)g), dim3(256), 0, s, (uint64_t*)p, n);
+  return hipGetLastError();
+}
+
+__global__ void stats_init_kernel(int64_t* stats, int levels, int R0) {
+  const int i = threadIdx.x;
+  if (i < levels * VDM_STAT_FIELDS) stats[i] = (i % VDM_STAT_FIELDS) == VDM_STAT_R ? (int64_t)R0 << (i / VDM_STAT_FIELDS) : 0;
+}
+
+hipError_t launch_stats_init(int64_t* stats, int levels, int R0, hipStream_t s) {
+  hipLaunchKernelGGL(stats_init_kernel, dim3(1), dim3(VDM_MAX_LEVELS * VDM_STAT_FIELDS), 0, s, stats, levels, R0);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ cell test
+// Cell (i, j, k) of level L (R cells per axis) is tested when all 8 corners were
+// computed: every cell at level 0, the children of kept parents afterwards
+// (kept_prev = the previous level's kept cells; null at level 0). A tested cell
+// is active when its corner values include s < 0 and s >= 0, or min |s| < tau.
+__global__ __launch_bounds__(512) void cell_test_kernel(const float* __restrict__ vol, int R, int NB,
+                                                        const uint64_t* __restrict__ kept_prev, int NBp,
+                                                        float tau, uint64_t* __restrict__ active,
+                                                        int64_t* stat_tested, int64_t* stat_active) {
+  __shared__ int64_t red[8];
+  const int64_t b = blockIdx.x;
+  const int bi = (int)(b / ((int64_t)NB * NB)), bj = (int)((b / NB) % NB), bk = (int)(b % NB);
+  const int ii = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = 8 * bi + ii, j = 8 * bj + (lane >> 3), k = 8 * bk + (lane & 7);
+  bool tested = i < R && j < R && k < R;
+  if (tested && kept_prev) tested = mask_bit(kept_prev, NBp, i >> 1, j >> 1, k >> 1);
+  bool act = false;
+  if (tested) {
+    const int64_t P = R + 1;
+    const float* v = vol + ((int64_t)i * P + j) * P + k;
+    bool neg = false, nonneg = false;
+    float mn = __builtin_inff();
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const float s = v[(a * P + c) * P + d];
+          neg |= s < 0.f;
+          nonneg |= s >= 0.f;
+          mn = fminf(mn, fabsf(s));
+        }
+    act = (neg && nonneg) || mn < tau;
+  }
+  const uint64_t word = __ballot(act);
+  if (lane == 0) active[b * 8 + ii] = word;
+  const int64_t nt = block_sum_i64(tested ? 1 : 0, red, threadIdx.x, 512);
+  const int64_t na = block_sum_i64(act ? 1 : 0, red, threadIdx.x, 512);
+  if (threadIdx.x == 0) {
+    if (nt) atomicAdd((unsigned long long*)stat_tested, (unsigned long long)nt);
+    if (na) atomicAdd((unsigned long long*)stat_active, (unsigned long long)na);
+  }
+}
+
+hipError_t launch_cell_test(const float* vol, int R, const uint64_t* kept_prev, float tau, uint64_t* active,
+                            int64_t* stat_tested, int64_t* stat_active, hipStream_t s) {
+  const int NB = nblocks8(R + 1), NBp = nblocks8(R / 2 + 1);
+  hipLaunchKernelGGL(cell_test_kernel, dim3((unsigned)((int64_t)NB * NB * NB)), dim3(512), 0, s, vol, R, NB,
+                     kept_prev, NBp, tau, active, stat_tested, stat_active);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ dilation
+// One thread per word: OR over the 3x3x3 neighbourhood, separably along k
+// (bit shifts inside each 8-bit row), j (shifts by 8) and i (neighbour words),
+// with neighbour blocks supplying the halo. Cells outside [0, R)^3 stay clear.
+__device__ __forceinline__ uint64_t dil_k(uint64_t w, uint64_t wl, uint64_t wr) {
+  const uint64_t C0 = 0x0101010101010101ull, C7 = 0x8080808080808080ull;
+  return w | ((w << 1) & ~C0) | ((wl >> 7) & C0) | ((w >> 1) & ~C7) | ((wr << 7) & C7);
+}
+__device__ __forceinline__ uint64_t dil_j(uint64_t t, uint64_t td, uint64_t tu) {
+  return t | (t << 8) | (td >> 56) | (t >> 8) | (tu << 56);
+}
+
+__global__ void dilate_kernel(const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int R, int NB,
+                              int identity, int64_t* stat) {
+  __shared__ int64_t red[4];
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nw = (int64_t)NB * NB * NB * 8;
+  uint64_t res = 0;
+  if (w < nw) {
+    const int64_t b = w >> 3;
+    const int ii = (int)(w & 7);
+    const int bi = (int)(b / ((int64_t)NB * NB)), bj = (int)((b / NB) % NB), bk = (int)(b % NB);
+    const int i = 8 * bi + ii;
+    if (i < R && identity) {
+      res = in[w];
+    } else if (i < R) {
+      for (int di = -1; di <= 1; ++di) {
+        const int i2 = i + di;
+        if (i2 < 0 || i2 >= R) continue;
+        const int bi2 = i2 >> 3, ii2 = i2 & 7;
+        uint64_t W[3][3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+          for (int c = 0; c < 3; ++c) {
+            const int bj2 = bj + a - 1, bk2 = bk + c - 1;
+            W[a][c] = (bj2 >= 0 && bj2 < NB && bk2 >= 0 && bk2 < NB)
+                          ? in[(((int64_t)bi2 * NB + bj2) * NB + bk2) * 8 + ii2]
+                          : 0ull;
+          }
+        const uint64_t t0 = dil_k(W[0][1], W[0][0], W[0][2]);
+        const uint64_t t1 = dil_k(W[1][1], W[1][0], W[1][2]);
+        const uint64_t t2 = dil_k(W[2][1], W[2][0], W[2][2]);
+        res |= dil_j(t1, t0, t2);
+      }
+    }
+    if (i < R) {  // clip to cells inside the grid
+      const int nj = min(max(R - 8 * bj, 0), 8), nk = min(max(R - 8 * bk, 0), 8);
+      const uint64_t row = nk >= 8 ? 0xffull : ((1ull << nk) - 1ull);
+      uint64_t m = 0;
+      for (int jj = 0; jj < nj; ++jj) m |= row << (8 * jj);
+      res &= m;
+    }
+    out[w] = res;
+  }
+  if (stat) {
+    const int64_t n = block_sum_i64(__popcll(res), red, threadIdx.x, 256);
+    if (threadIdx.x == 0 && n) atomicAdd((unsigned long long*)stat, (unsigned long long)n);
+  }
+}
+
+hipError_t launch_dilate(const uint64_t* in, uint64_t* out, int R, int identity, int64_t* stat, hipStream_t s) {
+  const int NB = nblocks8(R + 1);
+  const int64_t nw = (int64_t)NB * NB * NB * 8;
+  hipLaunchKernelGGL(dilate_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, in, out, R, NB, identity,
+                     stat);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ child marking
+// Point (I, J, K) of level L+1 (Rn = 2R cells) is a candidate when it is a corner
+// of a child of a kept level-L cell: per axis, even I has parents I/2 - 1 and I/2,
+// odd I has parent (I-1)/2. It is new when it was not computed before: a point
+// with all-even indices was computed iff its level-L point (I/2, J/2, K/2) was
+// (every point at level 0). all_new: every in-range point is new (level 0 list).
+__global__ __launch_bounds__(512) void mark_kernel(const uint64_t* __restrict__ kept, int R,
+                                                   const uint64_t* __restrict__ comp_prev, int all_new,
+                                                   int Rn, uint64_t* __restrict__ newmask,
+                                                   uint64_t* __restrict__ comp_next, int32_t* __restrict__ counts) {
+  __shared__ int cnt[8];
+  const int NBn = nblocks8(Rn + 1), NB = nblocks8(R + 1);
+  const int64_t b = blockIdx.x;
+  const int bi = (int)(b / ((int64_t)NBn * NBn)), bj = (int)((b / NBn) % NBn), bk = (int)(b % NBn);
+  const int ii = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int I = 8 * bi + ii, J = 8 * bj + (lane >> 3), K = 8 * bk + (lane & 7);
+  const bool in = I <= Rn && J <= Rn && K <= Rn;
+  bool isnew = false, prev = false;
+  if (in) {
+    if (all_new) {
+      isnew = true;
+    } else {
+      if (((I | J | K) & 1) == 0) prev = comp_prev ? mask_bit(comp_prev, NB, I >> 1, J >> 1, K >> 1) : true;
+      if (!prev) {
+        // parents along an axis: odd X -> X/2 only; even X -> X/2 - 1 and X/2
+        const int i1 = I >> 1, i0 = (I & 1) ? i1 : i1 - 1;
+        const int j1 = J >> 1, j0 = (J & 1) ? j1 : j1 - 1;
+        const int k1 = K >> 1, k0 = (K & 1) ? k1 : k1 - 1;
+        bool cand = false;
+        for (int a = max(i0, 0); a <= min(i1, R - 1) && !cand; ++a)
+          for (int c = max(j0, 0); c <= min(j1, R - 1) && !cand; ++c)
+            for (int d = max(k0, 0); d <= min(k1, R - 1) && !cand; ++d) cand = mask_bit(kept, NB, a, c, d);
+        isnew = cand;
+      }
+    }
+  }
+  const uint64_t wn = __ballot(isnew);
+  const uint64_t wp = __ballot(prev);
+  if (lane == 0) {
+    newmask[b * 8 + ii] = wn;
+    if (comp_next) comp_next[b * 8 + ii] = wn | wp;
+    cnt[ii] = __popcll(wn);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0;
+    for (int w = 0; w < 8; ++w) c += cnt[w];
+    counts[b] = c;
+  }
+}
+
+hipError_t launch_mark(const uint64_t* kept, int R, const uint64_t* comp_prev, int all_new, int Rn,
+                       uint64_t* newmask, uint64_t* comp_next, int32_t* counts, hipStream_t s) {
+  const int NBn = nblocks8(Rn + 1);
+  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((int64_t)NBn * NBn * NBn)), dim3(512), 0, s, kept, R, comp_prev,
+                     all_new, Rn, newmask, comp_next, counts);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ scan of per-block counts
+// For each block: queries q = counts[b], work items ceil(q / bq), occupied (q > 0).
+// Exclusive prefix sums give each block's offsets in the list, the item array and
+// the occupied-block array; totals go to tot[0..2] and to the level's stats.
+constexpr int SCAN_NT = 256;
+constexpr int SCAN_PER = 8;
+constexpr int SCAN_CHUNK = SCAN_NT * SCAN_PER;
+
+__device__ __forceinline__ int4 tuple_of(int c, int bq) { return make_int4(c, (c + bq - 1) / bq, c > 0, 0); }
+__device__ __forceinline__ int4 add4(int4 a, int4 b) { return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, 0); }
+
+__device__ int4 block_excl_scan(int4 v, int4* sh, int tid, int4* total) {
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < SCAN_NT; o <<= 1) {
+    int4 u = tid >= o ? sh[tid - o] : make_int4(0, 0, 0, 0);
+    __syncthreads();
+    sh[tid] = add4(sh[tid], u);
+    __syncthreads();
+  }
+  const int4 incl = sh[tid];
+  *total = sh[SCAN_NT - 1];
+  __syncthreads();
+  return make_int4(incl.x - v.x, incl.y - v.y, incl.z - v.z, 0);
+}
+
+__global__ __launch_bounds__(SCAN_NT) void scan_reduce_kernel(const int32_t* counts, int64_t n, int bq, int4* partial) {
+  __shared__ int4 sh[SCAN_NT];
+  const int64_t base = (int64_t)blockIdx.x * SCAN_CHUNK + threadIdx.x * SCAN_PER;
+  int4 s = make_int4(0, 0, 0, 0);
+  for (int e = 0; e < SCAN_PER; ++e)
+    if (base + e < n) s = add4(s, tuple_of(counts[base + e], bq));
+  int4 tot;
+  block_excl_scan(s, sh, threadIdx.x, &tot);
+  if (threadIdx.x == 0) partial[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(SCAN_NT) void scan_top_kernel(int4* partial, int np, int32_t* tot, int64_t* stats_level) {
+  __shared__ int4 sh[SCAN_NT];
+  int4 carry = make_int4(0, 0, 0, 0);
+  for (int base = 0; base < np; base += SCAN_NT) {
+    const int i = base + threadIdx.x;
+    const int4 v = i < np ? partial[i] : make_int4(0, 0, 0, 0);
+    int4 t;
+    const int4 ex = block_excl_scan(v, sh, threadIdx.x, &t);
+    if (i < np) partial[i] = add4(ex, carry);
+    carry = add4(carry, t);
+  }
+  if (threadIdx.x == 0) {
+    tot[0] = carry.x;
+    tot[1] = carry.y;
+    tot[2] = carry.z;
+    if (stats_level) {
+      stats_level[VDM_STAT_QUERIES] = carry.x;
+      stats_level[VDM_STAT_ITEMS] = carry.y;
+      stats_level[VDM_STAT_BLOCKS] = carry.z;
+    }
+  }
+}
+
+__global__ __launch_bounds__(SCAN_NT) void scan_apply_kernel(const int32_t* counts, int64_t n, int bq,
+                                                             const int4* partial, int4* offs) {
+  __shared__ int4 sh[SCAN_NT];
+  const int64_t base = (int64_t)blockIdx.x * SCAN_CHUNK + threadIdx.x * SCAN_PER;
+  int4 v[SCAN_PER];
+  int4 s = make_int4(0, 0, 0, 0);
+  for (int e = 0; e < SCAN_PER; ++e) {
+    v[e] = base + e < n ? tuple_of(counts[base + e], bq) : make_int4(0, 0, 0, 0);
+    s = add4(s, v[e]);
+  }
+  int4 tot;
+  int4 run = add4(block_excl_scan(s, sh, threadIdx.x, &tot), partial[blockIdx.x]);
+  for (int e = 0; e < SCAN_PER; ++e) {
+    if (base + e < n) offs[base + e] = run;
+    run = add4(run, v[e]);
+  }
+}
+
+hipError_t launch_scan(const int32_t* counts, int64_t n, int bq, int4* partial, int4* offs, int32_t* tot,
+                       int64_t* stats_level, hipStream_t s) {
+  const int np = (int)((n + SCAN_CHUNK - 1) / SCAN_CHUNK);
+  hipLaunchKernelGGL(scan_reduce_kernel, dim3(np), dim3(SCAN_NT), 0, s, counts, n, bq, partial);
+  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(SCAN_NT), 0, s, partial, np, tot, stats_level);
+  hipLaunchKernelGGL(scan_apply_kernel, dim3(np), dim3(SCAN_NT), 0, s, counts, n, bq, (const int4*)partial, offs);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ emit lists
+// Block b writes its new points (row-major linear indices, in-block row-major
+// order) at its list offset, its work items (query chunks of at most bq, all
+// attending to occupied-block row occ) and its id in the occupied-block array.
+__global__ __launch_bounds__(512) void emit_kernel(const uint64_t* __restrict__ newmask, const int32_t* __restrict__ counts,
+                                                   const int4* __restrict__ offs, int Rn, int bq,
+                                                   int32_t* __restrict__ list, Item* __restrict__ items,
+                                                   int32_t* __restrict__ occ) {
+  __shared__ int pre[8];
+  const int64_t b = blockIdx.x;
+  const int c = counts[b];
+  if (c == 0) return;
+  const int NB = nblocks8(Rn + 1);
+  const int ii = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t w = newmask[b * 8 + ii];
+  if (lane == 0) pre[ii] = __popcll(w);
+  __syncthreads();
+  int before = 0;
+  for (int x = 0; x < ii; ++x) before += pre[x];
+  const int4 o = offs[b];
+  if ((w >> lane) & 1ull) {
+    const int rank = before + __popcll(w & ((1ull << lane) - 1ull));
+    const int bi = (int)(b / ((int64_t)NB * NB)), bj = (int)((b / NB) % NB), bk = (int)(b % NB);
+    const int64_t P = Rn + 1;
+    const int I = 8 * bi + ii, J = 8 * bj + (lane >> 3), K = 8 * bk + (lane & 7);
+    list[o.x + rank] = (int32_t)(((int64_t)I * P + J) * P + K);
+  }
+  const int nchunks = (c + bq - 1) / bq;
+  if ((int)threadIdx.x < nchunks) {
+    const int q0 = o.x + threadIdx.x * bq;
+    items[o.y + threadIdx.x] = Item{q0, min(q0 + bq, o.x + c), o.z, 0};
+  }
+  if (threadIdx.x == 0) occ[o.z] = (int32_t)b;
+}
+
+hipError_t launch_emit(const uint64_t* newmask, const int32_t* counts, const int4* offs, int Rn, int bq,
+                       int32_t* list, Item* items, int32_t* occ, hipStream_t s) {
+  const int NB = nblocks8(Rn + 1);
+  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)((int64_t)NB * NB * NB)), dim3(512), 0, s, newmask, counts, offs, Rn,
+                     bq, list, items, occ);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ nearest-ancestor fill
+// vol_next[I][J][K] = vol_prev[I/2][J/2][K/2] (integer division) for every point.
+__global__ void fill_kernel(const float* __restrict__ prev, int Pp, float* __restrict__ next, int Pn) {
+  const int64_t n = (int64_t)Pn * Pn * Pn;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+    const int I = (int)(t / ((int64_t)Pn * Pn));
+    const int64_t r = t - (int64_t)I * Pn * Pn;
+    const int J = (int)(r / Pn), K = (int)(r - (int64_t)J * Pn);
+    next[t] = prev[((int64_t)(I >> 1) * Pp + (J >> 1)) * Pp + (K >> 1)];
+  }
+}
+
+hipError_t launch_fill(const float* prev, int Pp, float* next, int Pn, hipStream_t s) {
+  const int64_t n = (int64_t)Pn * Pn * Pn;
+  int64_t g = (n + 255) / 256;
+  if (g > 8192) g = 8192;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)g), dim3(256), 0, s, prev, Pp, next, Pn);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ inspection export
+// Row-major byte mask of an n^3 region of a blocked bit mask.
+__global__ void bits_to_bytes_kernel(const uint64_t* __restrict__ m, int n, int NB, uint8_t* __restrict__ out) {
+  const int64_t tot = (int64_t)n * n * n;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tot; t += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(t / ((int64_t)n * n));
+    const int64_t r = t - (int64_t)i * n * n;
+    const int j = (int)(r / n), k = (int)(r - (int64_t)j * n);
+    out[t] = mask_bit(m, NB, i, j, k) ? 1 : 0;
+  }
+}
+
+hipError_t launch_bits_to_bytes(const uint64_t* m, int n, int NB, uint8_t* out, hipStream_t s) {
+  const int64_t tot = (int64_t)n * n * n;
+  int64_t g = (tot + 255) / 256;
+  if (g > 8192) g = 8192;
+  hipLaunchKernelGGL(bits_to_bytes_kernel, dim3((unsigned)g), dim3(256), 0, s, m, n, NB, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ work items from a query list
+// For a grid-list decode with per-block token sets: every maximal run of list
+// entries in one block (at most block^3 entries are scanned) is cut into chunks
+// of at most bq queries; n_items counts them (the order of items does not affect
+// any result, each query's value depends only on its own block's token set).
+__global__ void items_from_list_kernel(const int32_t* __restrict__ list, int64_t N, int R, int block,
+                                       const int32_t* __restrict__ block_row, int bq, Item* __restrict__ items,
+                                       int32_t* n_items) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= N) return;
+  const int64_t P = R + 1;
+  const int NB = (R + block) / block;
+  auto blk = [&](int64_t lin) -> int64_t {
+    const int i = (int)(lin / (P * P));
+    const int64_t r = lin - (int64_t)i * P * P;
+    const int j = (int)(r / P), k = (int)(r - (int64_t)j * P);
+    return ((int64_t)(i / block) * NB + j / block) * NB + k / block;
+  };
+  const int64_t b = blk(list[q]);
+  if (q > 0 && blk(list[q - 1]) == b) return;
+  const int64_t lim = (int64_t)block * block * block;
+  int64_t e = q + 1;
+  while (e < N && e - q < lim && blk(list[e]) == b) ++e;
+  const int nch = (int)((e - q + bq - 1) / bq);
+  const int at = atomicAdd(n_items, nch);
+  const int row = block_row ? block_row[b] : (int)b;
+  for (int c = 0; c < nch; ++c) {
+    const int64_t q0 = q + (int64_t)c * bq;
+    items[at + c] = Item{(int32_t)q0, (int32_t)min(q0 + bq, e), row, 0};
+  }
+}
+
+hipError_t launch_items_from_list(const int32_t* list, int64_t N, int R, int block, const int32_t* block_row, int bq,
+                                  Item* items, int32_t* n_items, hipStream_t s) {
+  hipLaunchKernelGGL(items_from_list_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, list, N, R, block,
+                     block_row, bq, items, n_items);
+  return hipGetLastError();
+}
+
+}  // namespace vdm

@@ -1,0 +1,131 @@
+// Per-shape preparation kernels: key/value projection (K = Z Wk^T, V = Z Wv^T),
+// repacking of K/V into the tile layout the decoder streams, and the standalone
+// embedding + Q projection.
+//
+// The vecset decoder of the FlashVDM pages (aipaper.cc summary, section 3)
+// projects the latent tokens once per shape for cross-attention; these are the
+// one-time steps before the per-query decode.
+#include "vdm_device.hpp"
+
+namespace vdm {
+
+// ------------------------------------------------------------------ K/V packing
+// Kp[m][d] = K[m][d] (zero rows up to Mpad).
+// Vt[t][d][p] = V[32t + perm_key(p)][d]: V transposed per 32-token tile, with the
+// token order inside the tile permuted so that the A-operand fragments of the
+// P.V product are contiguous 16-byte reads (see perm_key).
+
+template <typename T>
+__global__ void pack_kv_kernel(const T* __restrict__ K, const T* __restrict__ V, int M, int D, int Mpad,
+                               T* __restrict__ Kp, T* __restrict__ Vt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)Mpad * D;
+  if (i >= n) return;
+  {
+    const int64_t m = i / D;
+    Kp[i] = m < M ? K[i] : to_t<T>(0.f);
+  }
+  {
+    const int64_t t = i / (32 * D);
+    const int rem = (int)(i - t * 32 * D);
+    const int d = rem / 32, p = rem % 32;
+    const int64_t key = 32 * t + perm_key<T>(p);
+    Vt[i] = key < M ? V[key * D + d] : to_t<T>(0.f);
+  }
+}
+
+hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D, int Mpad, void* Kp,
+                          void* Vt, hipStream_t s) {
+  const int64_t n = (int64_t)Mpad * D;
+  const int bs = 256;
+  const dim3 g((unsigned)((n + bs - 1) / bs));
+  if (dtype == VDM_BF16)
+    hipLaunchKernelGGL(pack_kv_kernel<bf16>, g, dim3(bs), 0, s, (const bf16*)K, (const bf16*)V, M, D, Mpad,
+                       (bf16*)Kp, (bf16*)Vt);
+  else
+    hipLaunchKernelGGL(pack_kv_kernel<float>, g, dim3(bs), 0, s, (const float*)K, (const float*)V, M, D, Mpad,
+                       (float*)Kp, (float*)Vt);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ K/V projection
+// C^T[n][m] = sum_k W[n][k] Z[m][k] on MFMA; block tile 64 tokens x 64 outputs,
+// one 32x32 tile per wave; blockIdx.z selects K (Wk) or V (Wv).
+
+template <typename T>
+__global__ __launch_bounds__(256) void project_kv_kernel(const T* __restrict__ Z, const T* __restrict__ Wk,
+                                                         const T* __restrict__ Wv, int M, int D,
+                                                         T* __restrict__ K, T* __restrict__ V) {
+  using MM = Mma<T>;
+  const T* W = blockIdx.z == 0 ? Wk : Wv;
+  T* C = blockIdx.z == 0 ? K : V;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * 64 + 32 * (wave & 1);
+  const int n0 = blockIdx.y * 64 + 32 * (wave >> 1);
+  const int mrow = min(m0 + (lane & 31), M - 1);  // clamp reads of the ragged last tile
+  const T* zb = Z + (int64_t)mrow * D + MM::KW * (lane >> 5);
+  const T* wb = W + (int64_t)(n0 + (lane & 31)) * D + MM::KW * (lane >> 5);
+  f32x16 acc = zero16();
+  for (int k = 0; k < D; k += MM::KS) {
+    const auto a = *reinterpret_cast<const typename MM::frag*>(wb + k);
+    const auto b = *reinterpret_cast<const typename MM::frag*>(zb + k);
+    acc = MM::mma(a, b, acc);
+  }
+  const int m = m0 + (lane & 31);
+  if (m < M) store_ct_row<T>(C + (int64_t)m * D + n0, acc, lane);
+}
+
+hipError_t launch_project_kv(int dtype, const void* Z, const void* Wk, const void* Wv, int M, int D, void* K,
+                             void* V, hipStream_t s) {
+  const dim3 g((M + 63) / 64, D / 64, 2);
+  if (dtype == VDM_BF16)
+    hipLaunchKernelGGL(project_kv_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)Z, (const bf16*)Wk,
+                       (const bf16*)Wv, M, D, (bf16*)K, (bf16*)V);
+  else
+    hipLaunchKernelGGL(project_kv_kernel<float>, g, dim3(256), 0, s, (const float*)Z, (const float*)Wk,
+                       (const float*)Wv, M, D, (float*)K, (float*)V);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ embedding + Q projection
+
+constexpr int EMB_BQ = 128;
+constexpr int EMB_NT = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(EMB_NT) void embed_kernel(QuerySrc qs, int64_t N, const T* __restrict__ Wq,
+                                                       T* __restrict__ Q) {
+  extern __shared__ __align__(16) char lds[];
+  using L = EmbedLds<T, EMB_BQ, D>;
+  const int64_t q0 = (int64_t)blockIdx.x * EMB_BQ;
+  const int64_t q1 = min(q0 + EMB_BQ, N);
+  embed_qproj<T, EMB_BQ, D, EMB_NT>(qs, q0, q1, Wq, lds, threadIdx.x);
+  const T* Qs = reinterpret_cast<const T*>(lds + L::QS);
+  constexpr int CH = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  for (int c = threadIdx.x; c < EMB_BQ * CH; c += EMB_NT) {
+    const int qi = c / CH, ch = c % CH;
+    if (q0 + qi < q1) {
+      const int e = ch * 16 / (int)sizeof(T);
+      *reinterpret_cast<uint4*>(Q + (q0 + qi) * D + e) = *reinterpret_cast<const uint4*>(Qs + qi * L::DPAD + e);
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t embed_t(const QuerySrc& qs, int64_t N, const void* Wq, void* Q, hipStream_t s) {
+  using L = EmbedLds<T, EMB_BQ, D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&embed_kernel<T, D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, L::END);
+  if (e != hipSuccess) return e;
+  const dim3 g((unsigned)((N + EMB_BQ - 1) / EMB_BQ));
+  hipLaunchKernelGGL((embed_kernel<T, D>), g, dim3(EMB_NT), L::END, s, qs, N, (const T*)Wq, (T*)Q);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(int dtype, int D, const QuerySrc& qs, int64_t N, const void* Wq, void* Q,
+                        hipStream_t s) {
+  if (dtype == VDM_BF16) return D == 64 ? embed_t<bf16, 64>(qs, N, Wq, Q, s) : embed_t<bf16, 256>(qs, N, Wq, Q, s);
+  return embed_t<float, 64>(qs, N, Wq, Q, s);
+}
+
+}  // namespace vdm

@@ -1,0 +1,109 @@
+// Internal argument structs shared by the host API layer and the kernels, and
+// the host-side launchers each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/vdm.h"
+
+namespace vdm {
+
+struct PrimDev {
+  int kind;
+  float c[3];
+  float s[3];
+};
+
+struct PrimSet {
+  int n;
+  PrimDev p[VDM_MAX_PRIMS];
+};
+
+// Where a tile's queries come from.
+//   mode 0: xyz[3q..3q+2]; 1: grid point with linear index q; 2: grid point list[q];
+//   3: corner probe q % 8 of block q / 8 (block id list[q / 8], or q / 8 when list
+//      is null) of an R-cell grid split into blocks of `block` points per axis.
+struct QuerySrc {
+  int mode;
+  int R;
+  const float* xyz;
+  const int32_t* list;
+  int block;
+};
+
+// A decode work item: queries [q0, q1) of the query source, attending to token
+// row `row` of the selection (gathered mode) or to every token (row < 0).
+struct Item {
+  int32_t q0, q1, row, pad;
+};
+
+struct DecodeArgs {
+  QuerySrc qs;
+  int64_t N;            // number of queries (dense tiles)
+  const void* Wq;       // [D][51]
+  const void* Kp;       // dense: [Mpad][D]; gathered: K [M][D]
+  const void* Vt;       // dense: [Mpad/32][D][32] permuted; gathered: V [M][D]
+  int M;                // tokens (dense)
+  const void* Wo;
+  const void* W1;
+  const void* W2;
+  const float* w_head;
+  int F;
+  float net_scale;
+  PrimSet prims;
+  float* out;           // sdf
+  int scatter;          // 1: out[linear grid index] (grid modes), 0: out[q]
+  // tiles: items == null -> tiles of BQ consecutive queries of N (or *d_N) queries;
+  //        items != null -> n_tiles (or *d_n_items) work items
+  const int32_t* d_N;       // device query count, or null (use N)
+  int64_t n_tiles;          // host item count
+  const int32_t* d_n_items; // device item count, or null (use n_tiles)
+  const Item* items;
+  // gathered
+  const int32_t* sel_idx;
+  const int32_t* sel_cnt;
+  int cap;
+};
+
+struct DevInfo {
+  int cus;
+  int max_lds;
+};
+
+DevInfo dev_info();
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.
+
+// K, V [M][D] -> Kp [Mpad][D] and Vt [Mpad/32][D][32] (token order permuted per 32-tile)
+hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D, int Mpad, void* Kp,
+                          void* Vt, hipStream_t s);
+// K = Z Wk^T, V = Z Wv^T
+hipError_t launch_project_kv(int dtype, const void* Z, const void* Wk, const void* Wv, int M, int D,
+                             void* K, void* V, hipStream_t s);
+// Q [N][D] = Wq e(xyz)
+hipError_t launch_embed(int dtype, int D, const QuerySrc& qs, int64_t N, const void* Wq, void* Q,
+                        hipStream_t s);
+// the decoder over tiles (dense) or items (list/gathered)
+hipError_t launch_decode(int dtype, int D, bool gathered, const DecodeArgs& a, hipStream_t s);
+int decode_tile_queries(int dtype, int D);
+int decode_f_chunk(int dtype, int D);
+
+// KV selection for blocks; blocks == null: block id = row. n_blocks from host or *d_n_blocks.
+struct SelectArgs {
+  int R, block, k, cap, M, H, D;
+  const void* Wq;  // [D][51]
+  const void* K;  // [M][D]
+  const int32_t* blocks;
+  int64_t n_blocks;
+  const int32_t* d_n_blocks;
+  int32_t* sel_idx;
+  int32_t* sel_cnt;
+  int64_t* stat_selected;  // optional: += sum of sel_cnt
+};
+hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s);
+size_t select_lds_bytes(int dtype, int D, int M);
+
+}  // namespace vdm

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status codes
+before any device work."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "vdm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(vdm_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_five_calls():
+    fns = header_functions()
+    for f in ["vdm_embed_queries", "vdm_project_kv", "vdm_decode_dense", "vdm_decode_hier", "vdm_select_kv"]:
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol():
+    import shape_vae_decoding_amd as V
+
+    lib = C.CDLL(V.LIB_PATH)
+    missing = [f for f in header_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+    assert sorted(V.EXPORTS) == header_functions()
+    assert V.vdm_version() == 1
+
+
+def _decoder(D=256, F=1024, dtype=1, n_prims=1):
+    import shape_vae_decoding_amd as V
+
+    d = V._Decoder()
+    d.D, d.H, d.F, d.n_freq, d.dtype = D, D // 64, F, 8, dtype
+    d.net_scale = 0.05
+    for k in ("Wq", "Wk", "Wv", "Wo", "W1", "W2", "w_head"):
+        setattr(d, k, 0x100000)  # never dereferenced: every case fails validation first
+    d.n_prims = n_prims
+    d.prims[0].kind = 0
+    return d
+
+
+def test_status_codes_for_bad_decoders():
+    import shape_vae_decoding_amd as V
+
+    lib = V._lib
+    assert lib.vdm_embed_queries(None, None, 5, None, None) == V.VDM_ERR_INVALID_ARG
+    assert "NULL" in V.vdm_last_error()
+    d = _decoder(D=128)
+    assert lib.vdm_embed_queries(C.byref(d), None, 5, None, None) == V.VDM_ERR_UNSUPPORTED
+    d = _decoder(F=1000)
+    assert lib.vdm_embed_queries(C.byref(d), None, 5, None, None) == V.VDM_ERR_UNSUPPORTED
+    d = _decoder(D=256, dtype=0)  # fp32 is supported only at D = 64
+    assert lib.vdm_embed_queries(C.byref(d), None, 5, None, None) == V.VDM_ERR_UNSUPPORTED
+    d = _decoder(n_prims=0)
+    assert lib.vdm_embed_queries(C.byref(d), None, 5, None, None) == V.VDM_ERR_INVALID_ARG
+    d = _decoder()
+    d.n_freq = 6
+    assert lib.vdm_embed_queries(C.byref(d), None, 5, None, None) == V.VDM_ERR_UNSUPPORTED
+    d = _decoder()
+    d.Wk = 0x100002  # misaligned
+    assert lib.vdm_project_kv(C.byref(d), 0x1000, 4, 0x2000, 0x3000, None) == V.VDM_ERR_INVALID_ARG
+
+
+def test_zero_sized_calls_are_noops():
+    import shape_vae_decoding_amd as V
+
+    d = _decoder()
+    assert V._lib.vdm_embed_queries(C.byref(d), None, 0, None, None) == V.VDM_OK
+    assert V._lib.vdm_project_kv(C.byref(d), None, 0, None, None, None) == V.VDM_OK
+    q = V._Queries(V.VDM_Q_POINTS, 0, 0, None, None)
+    assert V._lib.vdm_decode_dense(C.byref(d), C.byref(q), None, None, 1, None, None, None, 0, None) == V.VDM_OK
+
+
+def test_decode_argument_checks():
+    import shape_vae_decoding_amd as V
+
+    d = _decoder()
+    lib = V._lib
+    q = V._Queries(V.VDM_Q_GRID, 16, 17 ** 3 - 1, None, None)  # N != (R+1)^3
+    assert lib.vdm_decode_dense(C.byref(d), C.byref(q), 0x1000, 0x1000, 10, None, 0x1000, 0x1000, 1 << 30,
+                                None) == V.VDM_ERR_INVALID_ARG
+    q = V._Queries(V.VDM_Q_GRID, 16, 17 ** 3, None, None)
+    assert lib.vdm_decode_dense(C.byref(d), C.byref(q), 0x1000, 0x1000, 0, None, 0x1000, 0x1000, 1 << 30,
+                                None) == V.VDM_ERR_INVALID_ARG  # M = 0
+    assert lib.vdm_decode_dense(C.byref(d), C.byref(q), 0x1000, 0x1000, 10, None, 0x1000, 0x1000, 16,
+                                None) == V.VDM_ERR_WORKSPACE
+    sel = V._KvSel(8, 64, 0x1000, 0x1000, None)
+    assert lib.vdm_decode_dense(C.byref(d), C.byref(q), 0x1000, 0x1000, 10, C.byref(sel), 0x1000, 0x1000,
+                                1 << 30, None) == V.VDM_ERR_INVALID_ARG  # selection needs a list
+    need = lib.vdm_dense_workspace_size(C.byref(d), 3072, 1000, 0)
+    assert need >= 2 * 3072 * 256 * 2
+
+
+def test_select_and_hier_argument_checks():
+    import shape_vae_decoding_amd as V
+
+    d = _decoder()
+    lib = V._lib
+    # k > M, cap < k, M beyond the selection limit
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 65, 512, 0x1000, 64, None, 1000, 0x1000, 0x1000, None, 0,
+                             None) == V.VDM_ERR_INVALID_ARG
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 32, 0x1000, 3072, None, 1000, 0x1000, 0x1000, None, 0,
+                             None) == V.VDM_ERR_INVALID_ARG
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0x1000, 40960, None, 1000, 0x1000, 0x1000, None, 0,
+                             None) == V.VDM_ERR_UNSUPPORTED
+    # blocks == NULL requires nblk = NB^3 (76 points per axis -> 10 blocks)
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0x1000, 3072, None, 999, 0x1000, 0x1000, None, 0,
+                             None) == V.VDM_ERR_INVALID_ARG
+    p = V.hier_params(R0=75, levels=3)
+    assert lib.vdm_hier_workspace_size(C.byref(d), C.byref(p), 3072) > 27 * 10 ** 6 * 4
+    bad = V.hier_params(R0=75, levels=7)
+    assert lib.vdm_hier_workspace_size(C.byref(d), C.byref(bad), 3072) == 0
+    bad = V.hier_params(tau=float("nan"))
+    assert lib.vdm_decode_hier(C.byref(d), C.byref(bad), 0x1000, 0x1000, 3072, 0x1000, 301 ** 3, None, None,
+                               0x1000, 1 << 40, None) == V.VDM_ERR_INVALID_ARG
+    p = V.hier_params(kvsel=dict(k=64, cap=512, block=4))
+    assert lib.vdm_decode_hier(C.byref(d), C.byref(p), 0x1000, 0x1000, 3072, 0x1000, 301 ** 3, None, None,
+                               0x1000, 1 << 40, None) == V.VDM_ERR_UNSUPPORTED
+    p = V.hier_params()
+    assert lib.vdm_decode_hier(C.byref(d), C.byref(p), 0x1000, 0x1000, 3072, 0x1000, 300 ** 3, None, None,
+                               0x1000, 1 << 40, None) == V.VDM_ERR_INVALID_ARG  # volume too small
+    assert lib.vdm_decode_hier(C.byref(d), C.byref(p), 0x1000, 0x1000, 3072, 0x1000, 301 ** 3, None, None,
+                               0x1000, 1024, None) == V.VDM_ERR_WORKSPACE
