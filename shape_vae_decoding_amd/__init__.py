@@ -194,27 +194,50 @@ def vdm_project_kv(dec: Decoder, Z: torch.Tensor, K: torch.Tensor, V: torch.Tens
     _check(_lib.vdm_project_kv(dec.ref, Z.data_ptr(), Z.shape[0], K.data_ptr(), V.data_ptr(), _stream(stream)))
 
 
-def queries_points(xyz: torch.Tensor) -> _Queries:
+class Queries:
+    """A vdm_queries struct plus the device tensors it points to (kept alive for
+    as long as this object is)."""
+
+    def __init__(self, struct: _Queries, *keep: torch.Tensor):
+        self.struct = struct
+        self.keep = keep
+
+    @property
+    def N(self) -> int:
+        return int(self.struct.N)
+
+
+def queries_points(xyz: torch.Tensor) -> Queries:
     _dev(xyz, torch.float32, "xyz")
-    return _Queries(VDM_Q_POINTS, 0, xyz.shape[0], xyz.data_ptr(), None)
+    return Queries(_Queries(VDM_Q_POINTS, 0, xyz.shape[0], xyz.data_ptr(), None), xyz)
 
 
-def queries_grid(R: int) -> _Queries:
-    return _Queries(VDM_Q_GRID, R, (R + 1) ** 3, None, None)
+def queries_grid(R: int) -> Queries:
+    return Queries(_Queries(VDM_Q_GRID, R, (R + 1) ** 3, None, None))
 
 
-def queries_list(R: int, lin: torch.Tensor) -> _Queries:
+def queries_list(R: int, lin: torch.Tensor) -> Queries:
     _dev(lin, torch.int32, "list")
-    return _Queries(VDM_Q_GRID_LIST, R, lin.shape[0], None, lin.data_ptr())
+    return Queries(_Queries(VDM_Q_GRID_LIST, R, lin.shape[0], None, lin.data_ptr()), lin)
+
+
+class KvSel:
+    """A vdm_kvsel struct plus the device tensors it points to."""
+
+    def __init__(self, struct: _KvSel, *keep: torch.Tensor):
+        self.struct = struct
+        self.keep = keep
 
 
 def kvsel(block: int, cap: int, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
-          block_row: Optional[torch.Tensor] = None) -> _KvSel:
+          block_row: Optional[torch.Tensor] = None) -> KvSel:
     _dev(sel_idx, torch.int32, "sel_idx")
     _dev(sel_cnt, torch.int32, "sel_cnt")
+    keep = [sel_idx, sel_cnt]
     if block_row is not None:
         _dev(block_row, torch.int32, "block_row")
-    return _KvSel(block, cap, sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(block_row))
+        keep.append(block_row)
+    return KvSel(_KvSel(block, cap, sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(block_row)), *keep)
 
 
 def vdm_dense_workspace_size(dec: Decoder, M: int, N: int, with_sel: bool = False) -> int:
@@ -235,16 +258,16 @@ def vdm_hier_workspace_size(dec: Decoder, params: _HierParams, M: int) -> int:
     return n
 
 
-def vdm_decode_dense(dec: Decoder, q: _Queries, K: torch.Tensor, V: torch.Tensor, sdf: torch.Tensor,
-                     sel: Optional[_KvSel] = None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+def vdm_decode_dense(dec: Decoder, q: Queries, K: torch.Tensor, V: torch.Tensor, sdf: torch.Tensor,
+                     sel: Optional[KvSel] = None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
     _dev(K, dec.torch_dtype, "K")
     _dev(V, dec.torch_dtype, "V")
     _dev(sdf, torch.float32, "sdf")
     M = K.shape[0]
     if ws is None:
         ws = workspace(vdm_dense_workspace_size(dec, M, q.N, sel is not None), sdf.device)
-    _check(_lib.vdm_decode_dense(dec.ref, C.byref(q), K.data_ptr(), V.data_ptr(), M,
-                                 C.byref(sel) if sel is not None else None, sdf.data_ptr(), ws.data_ptr(),
+    _check(_lib.vdm_decode_dense(dec.ref, C.byref(q.struct), K.data_ptr(), V.data_ptr(), M,
+                                 C.byref(sel.struct) if sel is not None else None, sdf.data_ptr(), ws.data_ptr(),
                                  ws.numel(), _stream(stream)))
 
 

@@ -60,5 +60,13 @@ def ulp_bf16(x: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, e - 8)
 
 
+def bf16_close(g: np.ndarray, r: np.ndarray, abs_terms: np.ndarray, n_terms: int) -> np.ndarray:
+    """Both sides round a dot product to bf16: the GPU from an fp32 sum (error at
+    most n_terms * 2^-24 * sum |terms|), the oracle from the exact value. They agree
+    to one bf16 step plus that accumulation error (which matters only where the
+    terms cancel to a small result)."""
+    return np.abs(g - r) <= ulp_bf16(r) * 1.0001 + 2.0 * n_terms * 2.0 ** -24 * abs_terms
+
+
 def report(name, err, tol):
     print(f"[parity] {name}: max|d| = {err:.3e} (tol {tol:.1e})", flush=True)

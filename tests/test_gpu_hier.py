@@ -1,0 +1,193 @@
+"""GPU parity of hierarchical volume decoding through the C ABI.
+
+Lockstep: at every level the oracle's own steps (cell test, dilation, child
+marking, list order, nearest-ancestor fill) are applied to the GPU's volume of
+that level and must reproduce the GPU's masks, lists and inherited values bit
+for bit; the GPU's decoded values at the listed points are compared with the
+oracle decoder (sampled at full size). End to end: on a small grid the oracle
+runs the whole method itself. Special cases: tau = inf equals dense decoding
+bitwise; computed points equal the dense decode of the same points bitwise."""
+
+import numpy as np
+import pytest
+import torch
+
+import vdm_workloads as W
+from oracle import decoder as odec
+from oracle import hvd as hv
+from tests.helpers import TOL_BF16, TOL_F32, dev, f64, gpu_decoder, gpu_kv, oracle_decoder, report
+
+pytestmark = pytest.mark.gpu
+
+
+def V():
+    import shape_vae_decoding_amd as mod
+
+    return mod
+
+
+def run_hier(dec, params, K, Vv, with_sel=False):
+    levels = params.levels
+    Rf = params.R0 << (levels - 1)
+    vol = torch.empty((Rf + 1) ** 3, dtype=torch.float32, device=dev())
+    stats = torch.zeros(levels * V().STAT_FIELDS, dtype=torch.int64, device=dev())
+    dbg = V().HierDebug(params, with_sel=with_sel)
+    V().vdm_decode_hier(dec, params, K, Vv, vol, stats, dbg)
+    torch.cuda.synchronize()
+    return vol.cpu().numpy(), V().stats_dict(stats, levels), dbg
+
+
+def lockstep(params, vol, stats, dbg, decode_ref=None, sample=1500, tol=TOL_BF16, bq=128):
+    """Check every level's GPU outputs against the oracle steps applied to the
+    GPU's own data. decode_ref(R, lin) -> oracle SDF at those grid points."""
+    rng = np.random.default_rng(5)
+    computed = None
+    tested = None
+    worst = 0.0
+    for L in range(params.levels):
+        R = params.R0 << L
+        P = R + 1
+        d = dbg.levels[L]
+        vol_L = d["vol"].cpu().numpy().reshape(P, P, P)
+        if L == params.levels - 1:
+            np.testing.assert_array_equal(vol_L.reshape(-1), vol)
+        st = stats[L]
+        n = st["queries"]
+        lst = d["list"][:n].cpu().numpy().astype(np.int64)
+        if L == 0:
+            tested = np.ones((R,) * 3, bool)
+            computed = np.ones((P,) * 3, bool)
+            assert n == P ** 3
+            np.testing.assert_array_equal(lst, hv.blocked_order(np.ones((P,) * 3, bool)))
+        active = d["active"].cpu().numpy().reshape(R, R, R).astype(bool)
+        ref_active = hv.cell_test(vol_L, tested, params.tau)
+        assert np.array_equal(active, ref_active), f"level {L} active cells"
+        assert st["tested"] == int(tested.sum()) and st["active"] == int(active.sum())
+        # block-level bookkeeping of the list
+        blk = hv.block_of(lst, P)
+        ub, cnt = np.unique(blk, return_counts=True)
+        assert st["blocks"] == ub.size and st["items"] == int(np.sum((cnt + bq - 1) // bq))
+        # decoded values at the listed points
+        if decode_ref is not None and n:
+            pick = lst if n <= sample else np.sort(rng.choice(lst, sample, replace=False))
+            ref = decode_ref(R, pick)
+            err = np.abs(vol_L.reshape(-1)[pick].astype(np.float64) - ref).max()
+            worst = max(worst, err)
+            report(f"level {L} R={R} decoded points ({pick.size} of {n})", err, tol)
+            assert err <= tol
+        if L == params.levels - 1:
+            break
+        kept = d["kept"].cpu().numpy().reshape(R, R, R).astype(bool)
+        ref = hv.refine_step(vol_L, computed, tested, params.tau, params.dilation)
+        assert np.array_equal(kept, ref["kept"]), f"level {L} kept cells"
+        assert st["kept"] == int(kept.sum())
+        nxt = dbg.levels[L + 1]
+        n1 = stats[L + 1]["queries"]
+        lst1 = nxt["list"][:n1].cpu().numpy().astype(np.int64)
+        assert np.array_equal(lst1, ref["list"]), f"level {L + 1} list"
+        P1 = 2 * R + 1
+        vol1 = nxt["vol"].cpu().numpy().reshape(-1)
+        inherited = np.ones(P1 ** 3, bool)
+        inherited[lst1] = False
+        assert np.array_equal(vol1[inherited], ref["vol_inherited"].reshape(-1)[inherited]), f"level {L + 1} fill"
+        computed, tested = ref["computed_next"], ref["tested_next"]
+    return worst
+
+
+def test_hier_tiny_fp32_end_to_end():
+    w = W.make(0)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    params = V().hier_params(R0=8, levels=3, tau=2 * 2 / 32, dilation=1)
+    vol, stats, dbg = run_hier(dec, params, K, Vv)
+    od = oracle_decoder(w)
+    lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=10 ** 9, tol=TOL_F32)
+    # the oracle's own end-to-end run: same masks except cells within 1e-4 of a threshold
+    res = hv.hvd(lambda R, lin: od.sdf_grid(R, lin), 8, 3, params.tau, 1)
+    for L, rec in enumerate(res["levels"]):
+        R = rec["R"]
+        g = dbg.levels[L]["active"].cpu().numpy().reshape(R, R, R).astype(bool)
+        diff = g != rec["active"]
+        near = hv.near_threshold_cells(rec["vol"], params.tau)
+        print(f"[parity] end-to-end level {L}: {int(diff.sum())} differing cells, {int((diff & ~near).sum())} "
+              f"outside the 1e-4 window", flush=True)
+        assert not np.any(diff & ~near)
+    err = np.abs(vol.astype(np.float64) - res["vol"].reshape(-1)).max()
+    report("tiny fp32 HVD final volume", err, TOL_F32)
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("dil,levels", [(0, 3), (2, 3), (1, 1), (1, 4)])
+def test_hier_variants_lockstep(dil, levels):
+    w = W.gen.small_decoder(51, 256, 1024, 300, "bf16")
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    params = V().hier_params(R0=6, levels=levels, tau=0.05, dilation=dil)
+    vol, stats, dbg = run_hier(dec, params, K, Vv)
+    od = oracle_decoder(w)
+    od.K, od.V = f64(K), f64(Vv)
+    lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=400)
+
+
+def test_hier_tau_inf_equals_dense_bitwise():
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    params = V().hier_params(R0=10, levels=3, tau=float("inf"), dilation=1)
+    vol, stats, dbg = run_hier(dec, params, K, Vv)
+    Rf = 40
+    dense = torch.empty((Rf + 1) ** 3, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_grid(Rf), K, Vv, dense)
+    torch.cuda.synchronize()
+    assert np.array_equal(vol, dense.cpu().numpy())
+    for L in range(3):
+        assert stats[L]["active"] == stats[L]["tested"] == (10 << L) ** 3
+
+
+def test_hier_full_workload_lockstep():
+    # the 75 -> 150 -> 300 workload in the launch configuration the benchmark times
+    w = W.make(2)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    q = w.query
+    params = V().hier_params(R0=q["R0"], levels=q["levels"], tau=q["tau"], dilation=q["dilation"])
+    vol, stats, dbg = run_hier(dec, params, K, Vv)
+    for s in stats:
+        print(f"[hier] R={s['R']}: tested {s['tested']} active {s['active']} ({s['active'] / s['R'] ** 3:.3%}) "
+              f"kept {s['kept']} queries {s['queries']} ({s['queries'] / (s['R'] + 1) ** 3:.3%}) blocks {s['blocks']}",
+              flush=True)
+    total = sum(s["queries"] for s in stats)
+    print(f"[hier] decoded {total} of 301^3 points ({total / 301 ** 3:.2%})", flush=True)
+    od = oracle_decoder(w)
+    od.K, od.V = f64(K), f64(Vv)
+    lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=600)
+
+
+def test_hier_computed_points_equal_dense_decode():
+    # hierarchical decoding without selection equals dense decoding: bitwise at
+    # every decoded point; inherited points keep the dense sign (counted)
+    w = W.make(2)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    q = w.query
+    params = V().hier_params(R0=q["R0"], levels=q["levels"], tau=q["tau"], dilation=q["dilation"])
+    vol, stats, dbg = run_hier(dec, params, K, Vv)
+    Rf = 300
+    dense = torch.empty((Rf + 1) ** 3, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_grid(Rf), K, Vv, dense)
+    torch.cuda.synchronize()
+    dense = dense.cpu().numpy()
+    computed = np.zeros(301 ** 3, bool)
+    for L in range(3):
+        R = 75 << L
+        lst = dbg.levels[L]["list"][: stats[L]["queries"]].cpu().numpy().astype(np.int64)
+        I, r = np.divmod(lst, (R + 1) ** 2)
+        J, Kk = np.divmod(r, R + 1)
+        s = 300 // R
+        computed[((I * s) * 301 + J * s) * 301 + Kk * s] = True
+    assert np.array_equal(vol[computed], dense[computed])
+    inh = ~computed
+    flips = int(np.sum((vol[inh] < 0) != (dense[inh] < 0)))
+    print(f"[hier] {int(computed.sum())} decoded points equal dense bitwise; {flips} of {int(inh.sum())} "
+          f"inherited points have a sign different from dense", flush=True)
+    assert flips <= 1e-4 * inh.sum()
