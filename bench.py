@@ -1,0 +1,229 @@
+"""Benchmark of the vecset SDF decoder on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic shape (3072
+tokens x 256 wide, 1024-wide MLP, bf16, seed 0):
+  1. K/V projection of the vecset,
+  2. dense decode of the 129^3 grid (2,146,689 query points),
+  3. hierarchical volume decoding 75 -> 150 -> 300 (a 301^3 volume),
+  4. hierarchical decoding with adaptive KV selection (k = 64, cap 512).
+`value` = query points decoded per second over the step (dense points plus the
+points each hierarchical pass decodes). Per-row times come from HIP events on
+the stream the library launches on. The roofline object covers the dominant
+kernel, the dense decode launch (MFMA-bound); the CPU baseline is the oracle on
+a bounded sample of the dense workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--skip-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_dense_129cubed_traffic.json")
+DECODE_SOURCES = ["shape_vae_decoding_amd/csrc/k_decode.hip", "shape_vae_decoding_amd/csrc/vdm_device.hpp"]
+
+
+def flops_per_query(E, D, M, F):
+    """Algorithmic FLOPs of one query: Q projection, QK^T and PV over M tokens,
+    out-projection, MLP and head."""
+    return 2 * (E * D + 2 * M * D + D * D + 2 * D * F + D)
+
+
+def decode_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, target_s: float = 12.0):
+    """The oracle, as it stands, on a bounded sample of the dense 129^3 workload."""
+    import numpy as np
+
+    from oracle import decoder as odec
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    od = odec.Decoder.from_workload(w)
+    R = w.query["R"]
+    rng = np.random.default_rng(0)
+    n_done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < target_s:
+        lin = rng.integers(0, (R + 1) ** 3, 512)
+        od.sdf_grid(R, lin)
+        n_done += lin.size
+    dt = time.perf_counter() - t0
+    return {
+        "value": n_done / dt,
+        "unit": "query points/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{n_done} random points of the 129^3 grid decoded by the float64 oracle "
+                  f"(M=3072, D=256, F=1024) in {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU baseline (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decoder path here has no "
+              f"multi-GPU part: queries shard by independent slabs, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import shape_vae_decoding_amd as V
+    import vdm_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.make(1)
+    w2 = W.make(2)
+    w3 = W.make(3)
+    wt = {k: torch.from_numpy(v).to(dev) for k, v in w.weights.items()}
+    wt = {k: (v if k == "w_head" else v.to(torch.bfloat16)) for k, v in wt.items()}
+    dec = V.Decoder(wt, w.prims, w.net_scale)
+    Z = torch.from_numpy(w.Z).to(dev).to(torch.bfloat16)
+    K = torch.empty_like(Z)
+    Vv = torch.empty_like(Z)
+    R = w.query["R"]
+    N = (R + 1) ** 3
+    sdf = torch.empty(N, dtype=torch.float32, device=dev)
+    q = V.queries_grid(R)
+    ws_dense = V.workspace(V.vdm_dense_workspace_size(dec, w.M, N), dev)
+    hq = w2.query
+    p_h = V.hier_params(R0=hq["R0"], levels=hq["levels"], tau=hq["tau"], dilation=hq["dilation"])
+    aq = w3.query
+    p_a = V.hier_params(R0=aq["R0"], levels=aq["levels"], tau=aq["tau"], dilation=aq["dilation"], kvsel=aq["kvsel"])
+    Pf = (hq["R0"] << (hq["levels"] - 1)) + 1
+    vol_h = torch.empty(Pf ** 3, dtype=torch.float32, device=dev)
+    vol_a = torch.empty(Pf ** 3, dtype=torch.float32, device=dev)
+    st_h = torch.zeros(hq["levels"] * V.STAT_FIELDS, dtype=torch.int64, device=dev)
+    st_a = torch.zeros(aq["levels"] * V.STAT_FIELDS, dtype=torch.int64, device=dev)
+    ws_h = V.workspace(V.vdm_hier_workspace_size(dec, p_h, w.M), dev)
+    ws_a = V.workspace(V.vdm_hier_workspace_size(dec, p_a, w.M), dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        V.vdm_project_kv(dec, Z, K, Vv)
+        if ev:
+            ev[1].record()
+        V.vdm_decode_dense(dec, q, K, Vv, sdf, ws=ws_dense)
+        if ev:
+            ev[2].record()
+        V.vdm_decode_hier(dec, p_h, K, Vv, vol_h, st_h, ws=ws_h)
+        if ev:
+            ev[3].record()
+        V.vdm_decode_hier(dec, p_a, K, Vv, vol_a, st_a, ws=ws_a)
+        if ev:
+            ev[4].record()
+
+    log(f"device {torch.cuda.get_device_name(0)}; warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    rows = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in events])
+    row_ms = rows.mean(axis=0)
+    sh = V.stats_dict(st_h, hq["levels"])
+    sa = V.stats_dict(st_a, aq["levels"])
+    q_h = sum(s["queries"] for s in sh)
+    q_a = sum(s["queries"] for s in sa)
+    total_q = N + q_h + q_a
+    value = total_q / (ms_step / 1e3)
+
+    phi = flops_per_query(51, w.D, w.M, w.F)
+    dense_flop = phi * N
+    achieved = dense_flop / (row_ms[1] / 1e3) / 1e12
+    traffic = None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_source_sha") == decode_source_sha():
+            traffic = t.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": "vdm_decode_dense on the 129^3 grid (pack + fused decode launch)",
+        "flop_per_launch": dense_flop,
+        "launch_ms": round(float(row_ms[1]), 4),
+    }
+    out = {
+        "metric": "query points/sec (dense & hierarchical) + ms per 300^3 volume decode; % roofline",
+        "value": round(value, 1),
+        "unit": "query points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "one shape, 3072 tokens x 256 (4 heads), MLP 256-1024-256, bf16: KV projection + dense "
+                        "129^3 grid + hierarchical 75->150->300 + hierarchical with KV selection (k=64, cap 512)",
+            "tokens": w.M,
+            "dense_grid_points": N,
+            "hier_decoded_points": q_h,
+            "akvs_decoded_points": q_a,
+        },
+        "breakdown": {
+            "kv_projection_ms": round(float(row_ms[0]), 4),
+            "dense_129cubed_ms": round(float(row_ms[1]), 4),
+            "dense_query_points_per_s": round(N / (row_ms[1] / 1e3), 1),
+            "hier_ms_per_300cubed_volume": round(float(row_ms[2]), 4),
+            "hier_decoded_points_per_s": round(q_h / (row_ms[2] / 1e3), 1),
+            "hier_volume_points_per_s": round(Pf ** 3 / (row_ms[2] / 1e3), 1),
+            "akvs_ms_per_300cubed_volume": round(float(row_ms[3]), 4),
+            "akvs_volume_points_per_s": round(Pf ** 3 / (row_ms[3] / 1e3), 1),
+            "hier_levels": sh,
+            "akvs_levels": sa,
+        },
+        "roofline": roofline,
+    }
+    if not args.skip_cpu:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
