@@ -10,27 +10,35 @@
 namespace vdm {
 
 // ------------------------------------------------------------------ K/V packing
-// Kp[m][d] = K[m][d] (zero rows up to Mpad).
-// Vt[t][d][p] = V[32t + perm_key(p)][d]: V transposed per 32-token tile, with the
-// token order inside the tile permuted so that the A-operand fragments of the
-// P.V product are contiguous 16-byte reads (see perm_key).
+// The decoder's token loop reads, per 32-token tile t and head h, one contiguous
+// run of 32 elements per lane l (64 lanes): exactly the lane's MFMA operands.
+//   K run, element e: A operand of S^T = K_h Q_h^T, step ks = e / KW, slot v = e % KW:
+//       K[32t + l%32][64h + KS*ks + KW*(l/32) + v]
+//   V run, element e: A operand of O^T += V_h^T P^T, row block db = e / 16, step
+//       ps = (e % 16) / KW, slot v = e % KW:
+//       V[32t + perm_key(KS*ps + KW*(l/32) + v)][64h + 32db + l%32]
+// Tokens past M are zero.
 
 template <typename T>
 __global__ void pack_kv_kernel(const T* __restrict__ K, const T* __restrict__ V, int M, int D, int Mpad,
                                T* __restrict__ Kp, T* __restrict__ Vt) {
+  using MM = Mma<T>;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (int64_t)Mpad * D;
   if (i >= n) return;
+  const int64_t t = i / (32 * D);
+  const int rem = (int)(i - t * 32 * D);
+  const int h = rem / 2048, l = (rem % 2048) / 32, e = rem % 32;
+  const int r = l & 31, half = l >> 5;
   {
-    const int64_t m = i / D;
-    Kp[i] = m < M ? K[i] : to_t<T>(0.f);
+    const int ks = e / MM::KW, v = e % MM::KW;
+    const int64_t m = 32 * t + r;
+    Kp[i] = m < M ? K[m * D + 64 * h + MM::KS * ks + MM::KW * half + v] : to_t<T>(0.f);
   }
   {
-    const int64_t t = i / (32 * D);
-    const int rem = (int)(i - t * 32 * D);
-    const int d = rem / 32, p = rem % 32;
-    const int64_t key = 32 * t + perm_key<T>(p);
-    Vt[i] = key < M ? V[key * D + d] : to_t<T>(0.f);
+    const int db = e / 16, f = e % 16, ps = f / MM::KW, v = f % MM::KW;
+    const int64_t m = 32 * t + perm_key<T>(MM::KS * ps + MM::KW * half + v);
+    Vt[i] = m < M ? V[m * D + 64 * h + 32 * db + r] : to_t<T>(0.f);
   }
 }
 
@@ -45,6 +53,33 @@ hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D,
   else
     hipLaunchKernelGGL(pack_kv_kernel<float>, g, dim3(bs), 0, s, (const float*)K, (const float*)V, M, D, Mpad,
                        (float*)Kp, (float*)Vt);
+  return hipGetLastError();
+}
+
+// kmax[h] = max over tokens of the Euclidean norm of head h's 64 key columns
+// (float32; norms are non-negative, so their bit patterns order like integers).
+template <typename T>
+__global__ void key_norms_kernel(const T* __restrict__ K, int M, int H, float* kmax) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * H) return;
+  const int64_t m = i / H;
+  const int h = (int)(i % H);
+  const T* k = K + m * 64 * H + 64 * h;
+  float s = 0.f;
+  for (int d = 0; d < 64; ++d) {
+    const float x = to_f(k[d]);
+    s += x * x;
+  }
+  atomicMax(reinterpret_cast<unsigned*>(kmax + h), __float_as_uint(sqrtf(s)));
+}
+
+hipError_t launch_key_norms(int dtype, const void* K, int M, int H, float* kmax, hipStream_t s) {
+  const int64_t n = (int64_t)M * H;
+  const dim3 g((unsigned)((n + 255) / 256));
+  if (dtype == VDM_BF16)
+    hipLaunchKernelGGL(key_norms_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)K, M, H, kmax);
+  else
+    hipLaunchKernelGGL(key_norms_kernel<float>, g, dim3(256), 0, s, (const float*)K, M, H, kmax);
   return hipGetLastError();
 }
 

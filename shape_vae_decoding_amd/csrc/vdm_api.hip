@@ -120,6 +120,7 @@ static int64_t mpad(int64_t M) { return (M + 31) / 32 * 32; }
 struct DenseWs {
   void* Kp;
   void* Vt;
+  float* kmax;
   Item* items;
   int32_t* n_items;
 };
@@ -128,8 +129,9 @@ static size_t dense_ws(const vdm_decoder* d, int64_t M, int64_t N, bool sel, voi
   Carve c(base);
   DenseWs x;
   const size_t kv = (size_t)mpad(M) * d->D * esize(d->dtype);
-  x.Kp = c.take<char>(kv);
-  x.Vt = c.take<char>(kv);
+  x.Kp = sel ? nullptr : c.take<char>(kv);
+  x.Vt = sel ? nullptr : c.take<char>(kv);
+  x.kmax = c.take<float>(256);
   x.items = sel ? c.take<Item>((size_t)(N > 0 ? N : 1) * sizeof(Item)) : nullptr;
   x.n_items = sel ? c.take<int32_t>(256) : nullptr;
   if (w) *w = x;
@@ -140,6 +142,7 @@ static size_t dense_ws(const vdm_decoder* d, int64_t M, int64_t N, bool sel, voi
 struct HierWs {
   void* Kp;
   void* Vt;
+  float* kmax;
   float* vol[VDM_MAX_LEVELS];
   uint64_t* active[VDM_MAX_LEVELS];
   uint64_t* kept[VDM_MAX_LEVELS];
@@ -165,6 +168,7 @@ static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M,
   const size_t kv = (size_t)mpad(M) * d->D * esize(d->dtype);
   x.Kp = c.take<char>(kv);
   x.Vt = c.take<char>(kv);
+  x.kmax = c.take<float>(256);
   int64_t maxP3 = 0, maxNB3 = 0, maxWords = 0;
   for (int L = 0; L < p->levels; ++L) {
     const int64_t R = (int64_t)p->R0 << L, P = R + 1;
@@ -306,6 +310,9 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
   a.N = q->N;
   a.out = sdf;
   a.scatter = 0;
+  a.kmax = w.kmax;
+  VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
+  VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
   if (!sel) {
     VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
     a.Kp = w.Kp;
@@ -391,6 +398,8 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
   const bool kv = p->use_kvsel != 0;
 
   VDM_HIP(launch_stats_init(S, p->levels, p->R0, s), "stats init");
+  VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
+  VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
   if (!kv) VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
 
   auto vol_of = [&](int L) { return L == p->levels - 1 ? vol : w.vol[L]; };
@@ -420,6 +429,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
     }
     DecodeArgs a = base_args(dec);
     a.qs = QuerySrc{VDM_Q_GRID_LIST, R, nullptr, w.list, 0};
+    a.kmax = w.kmax;
     a.out = vol_of(L);
     a.scatter = 1;
     a.M = (int)M;

@@ -79,6 +79,20 @@ __device__ __forceinline__ float to_t<float>(float x) { return x; }
 template <typename T>
 __device__ __forceinline__ float to_f(T x) { return (float)x; }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a bf16 pair in one v_cvt_pk_bf16_f32 (round to nearest even).
+__device__ __forceinline__ bf16x2 cvt2(float a, float b) { return __builtin_convertvector((f32x2){a, b}, bf16x2); }
+
+// Eight floats to the eight bf16 of one MFMA operand fragment.
+__device__ __forceinline__ bf16x8 cvt8(const float* x) {
+  const bf16x2 a = cvt2(x[0], x[1]), b = cvt2(x[2], x[3]), c = cvt2(x[4], x[5]), d = cvt2(x[6], x[7]);
+  const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Store 4 consecutive C-layout rows (r = 4g .. 4g+3 of one lane) to dst[0..3].
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
@@ -191,8 +205,23 @@ __device__ __forceinline__ float analytic_sdf(Coords p, const PrimSet& ps) {
   return best;
 }
 
-// Exact GELU x * Phi(x) = x/2 (1 + erf(x / sqrt 2)).
-__device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+// GELU x * Phi(x) = x/2 (1 + erf(x / sqrt 2)), with erf from Abramowitz & Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 for all
+// arguments; far below the bf16 rounding the hidden activations get next):
+// erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z), z >= 0.
+// Branch-free: one reciprocal and one exp2 per value.
+__device__ __forceinline__ float gelu(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.f));
+  float y = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+  y = __builtin_fmaf(t, y, 1.421413741f);
+  y = __builtin_fmaf(t, y, -0.284496736f);
+  y = __builtin_fmaf(t, y, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
+  const float erf_abs = __builtin_fmaf(-(t * y), e, 1.f);
+  const float erf = __builtin_copysignf(erf_abs, x);
+  return 0.5f * x * (1.f + erf);
+}
 
 // ------------------------------------------------------------------ embedding + Q projection
 
@@ -222,12 +251,17 @@ __device__ __forceinline__ typename Mma<T>::frag load_wq_frag(const T* __restric
   using MM = Mma<T>;
   const int f0 = ks * MM::KS + MM::KW * (lane >> 5);
   const T* p = Wq + (row0 + (lane & 31)) * VDM_E_DIM;
+  // loads stay inside the row (index clamped), then the padding features are zeroed
   if constexpr (MM::KW == 1) {
-    return f0 < VDM_E_DIM ? p[f0] : 0.f;
+    const float w = p[f0 < VDM_E_DIM ? f0 : VDM_E_DIM - 1];
+    return f0 < VDM_E_DIM ? w : 0.f;
   } else {
     typename MM::frag f;
 #pragma unroll
-    for (int v = 0; v < MM::KW; ++v) f[v] = f0 + v < VDM_E_DIM ? p[f0 + v] : to_t<T>(0.f);
+    for (int v = 0; v < MM::KW; ++v) {
+      const T w = p[f0 + v < VDM_E_DIM ? f0 + v : VDM_E_DIM - 1];
+      f[v] = f0 + v < VDM_E_DIM ? w : to_t<T>(0.f);
+    }
     return f;
   }
 }

@@ -43,8 +43,9 @@ struct DecodeArgs {
   QuerySrc qs;
   int64_t N;            // number of queries (dense tiles)
   const void* Wq;       // [D][51]
-  const void* Kp;       // dense: [Mpad][D]; gathered: K [M][D]
-  const void* Vt;       // dense: [Mpad/32][D][32] permuted; gathered: V [M][D]
+  const void* Kp;       // dense: packed K tiles [Mpad/32][H][64 lanes][32]; gathered: K [M][D]
+  const void* Vt;       // dense: packed V^T tiles [Mpad/32][H][64 lanes][32]; gathered: V [M][D]
+  const float* kmax;    // [H] max over tokens of ||k_h|| (softmax shift bound)
   int M;                // tokens (dense)
   const void* Wo;
   const void* W1;
@@ -77,9 +78,11 @@ DevInfo dev_info();
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 
-// K, V [M][D] -> Kp [Mpad][D] and Vt [Mpad/32][D][32] (token order permuted per 32-tile)
+// K, V [M][D] -> per-(32-token tile, head) operand runs of 64 lanes x 32 elements (see k_prep.hip)
 hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D, int Mpad, void* Kp,
                           void* Vt, hipStream_t s);
+// kmax[h] = max_m ||K[m][64h .. 64h+63]||_2 (kmax must be zeroed first)
+hipError_t launch_key_norms(int dtype, const void* K, int M, int H, float* kmax, hipStream_t s);
 // K = Z Wk^T, V = Z Wv^T
 hipError_t launch_project_kv(int dtype, const void* Z, const void* Wk, const void* Wv, int M, int D,
                              void* K, void* V, hipStream_t s);
