@@ -18,7 +18,8 @@ from typing import Dict, Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvdm.so")
+# VDM_LIB names another build of the library (e.g. an instrumented one); default: the in-tree build
+LIB_PATH = os.environ.get("VDM_LIB") or os.path.join(_HERE, "libvdm.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m shape_vae_decoding_amd.build`")

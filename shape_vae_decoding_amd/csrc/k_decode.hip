@@ -23,10 +23,12 @@
 // sum is accumulated from the bf16-rounded p_j (dot2 with ones), the same
 // values the P.V product uses.
 //
-// Dense mode streams per-(tile, head) operand fragments from the packed K/V
-// (each lane loads one contiguous 64-byte run) straight into registers, one
-// tile ahead; no LDS and no barrier in the token loop. Gathered mode stages the
-// selected tokens' rows through LDS (one copy per workgroup, all heads).
+// Token tiles are staged through LDS once per workgroup (all heads, double
+// buffered, one barrier per 32-token tile) so every K/V byte is fetched once per
+// BQ queries; dense mode copies pre-packed tiles (K rows, per-tile V^T), gathered
+// mode reads the selected tokens' rows and transposes V on the way into LDS.
+// The epilogue streams each weight row once per workgroup from L2 with a 4-deep
+// register prefetch ring.
 #include "vdm_device.hpp"
 
 namespace vdm {
@@ -60,13 +62,14 @@ struct DecCfg {
   static constexpr int RED = 2 * BQ * DPAD * SZ;
   static constexpr int EPI_END = RED + NW * BQ * 4;
   static constexpr int EMB_END = EmbedLds<T, BQ, D>::END;
-  static constexpr int LDS_DENSE = EPI_END > EMB_END ? EPI_END : EMB_END;
-  static constexpr int LDS_GATHER = LDS_DENSE > ATT_END ? LDS_DENSE : ATT_END;
-  // epilogue tiling: wave w owns C tiles [w*TPW, (w+1)*TPW) of (D/32) x (BQ/32), rb-major
+  static constexpr int LDS_PRE = EPI_END > EMB_END ? EPI_END : EMB_END;
+  static constexpr int LDS = LDS_PRE > ATT_END ? LDS_PRE : ATT_END;
+  // epilogue tiling: wave w owns C tiles [w*TPW, (w+1)*TPW) of (D/32) x (BQ/32), rb-major:
+  // one row block of weights (loaded once per workgroup) for TPW column blocks
   static constexpr int CB = BQ / 32;
   static constexpr int TPW = (D / 32) * CB / NW;
   static constexpr int TPH = (FC / 32) * CB / NW;
-  // gathered staging: 16-byte chunks per thread per tile
+  // staging: 16-byte chunks per thread per tile (K and V each)
   static constexpr int KCH = KT * D * SZ / 16;
   static constexpr int NCK = KCH / NT;
   static constexpr int EPC = 16 / SZ;
@@ -75,9 +78,9 @@ struct DecCfg {
   static_assert(QW % 32 == 0, "query groups are whole MFMA columns");
   static_assert(BQ * HPAD * SZ <= ABUF, "GELU chunk fits where O was");
   static_assert(((D / 32) * CB) % NW == 0 && ((FC / 32) * CB) % NW == 0, "epilogue tiles split evenly");
-  static_assert((TPW % CB == 0 || CB % TPW == 0) && (TPH % CB == 0 || CB % TPH == 0), "epilogue tile rows");
+  static_assert(TPW <= CB && CB % TPW == 0 && TPH <= CB && CB % TPH == 0, "one weight row block per wave");
   static_assert(KCH % NT == 0, "staging chunks split evenly");
-  static_assert(LDS_GATHER <= 160 * 1024, "fits gfx950 LDS");
+  static_assert(LDS <= 160 * 1024, "fits gfx950 LDS");
 };
 
 // log2(e) / sqrt(64): logits are scaled once into base 2.
@@ -93,6 +96,21 @@ __device__ __forceinline__ void load_run(const typename C::T* __restrict__ base,
   const uint4* p = reinterpret_cast<const uint4*>(base + ((int64_t)(kt * C::H + h) * 64 + lane) * 32);
 #pragma unroll
   for (int i = 0; i < C::RUN_U4; ++i) r[i] = p[i];
+}
+
+template <typename C>
+__device__ __forceinline__ void as_frags(const uint4 (&kr)[C::RUN_U4], const uint4 (&vr)[C::RUN_U4],
+                                         typename Mma<typename C::T>::frag (&kf)[C::KSTEPS],
+                                         typename Mma<typename C::T>::frag (&vf)[2][C::PSTEPS]) {
+  using Frag = typename Mma<typename C::T>::frag;
+  const Frag* kp = reinterpret_cast<const Frag*>(kr);
+  const Frag* vp = reinterpret_cast<const Frag*>(vr);
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = kp[ks];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int ps = 0; ps < C::PSTEPS; ++ps) vf[db][ps] = vp[db * C::PSTEPS + ps];
 }
 
 // Softmax numerators of one 32x32 S^T block for this lane's query column:
@@ -133,38 +151,77 @@ __device__ __forceinline__ void softmax_block(const f32x16& S, float nb, float& 
   }
 }
 
-// ---------------------------------------------------------------- gathered staging (LDS)
-template <typename C>
-__device__ __forceinline__ void gather_load(const typename C::T* __restrict__ Kg, const typename C::T* __restrict__ Vg,
-                                            const int32_t* sel, int nkeys, int M, int kt, int tid,
-                                            uint4 (&rk)[C::NCK], uint4 (&rv)[C::NCK]) {
+// ---------------------------------------------------------------- token-tile staging (LDS)
+// Global -> registers for tile kt. Dense: 32 rows of packed K and the packed V^T
+// tile, both contiguous. Gathered: rows sel[32kt + j] of K and V (zero past nkeys).
+template <typename C, bool GATHER>
+__device__ __forceinline__ void tile_load(const typename C::T* __restrict__ Kg, const typename C::T* __restrict__ Vg,
+                                          const int32_t* sel, int nkeys, int M, int kt, int tid, uint4 (&rk)[C::NCK],
+                                          uint4 (&rv)[C::NCK]) {
   constexpr int CPR = C::D / C::EPC;
+  if constexpr (!GATHER) {
+    const uint4* ks = reinterpret_cast<const uint4*>(Kg + (int64_t)kt * C::KT * C::D);
+    const uint4* vs = reinterpret_cast<const uint4*>(Vg + (int64_t)kt * C::KT * C::D);
 #pragma unroll
-  for (int i = 0; i < C::NCK; ++i) {
-    const int c = tid + i * C::NT, j = kt * C::KT + c / CPR, e = (c % CPR) * C::EPC;
-    const int64_t row = (int64_t)tok_clamp(j < nkeys ? sel[j] : 0, M) * C::D + e;
-    rk[i] = j < nkeys ? *reinterpret_cast<const uint4*>(Kg + row) : uint4{0, 0, 0, 0};
-    rv[i] = j < nkeys ? *reinterpret_cast<const uint4*>(Vg + row) : uint4{0, 0, 0, 0};
+    for (int i = 0; i < C::NCK; ++i) {
+      rk[i] = ks[tid + i * C::NT];
+      rv[i] = vs[tid + i * C::NT];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::NCK; ++i) {
+      const int c = tid + i * C::NT, j = kt * C::KT + c / CPR, e = (c % CPR) * C::EPC;
+      const int64_t row = (int64_t)tok_clamp(j < nkeys ? sel[j] : 0, M) * C::D + e;
+      rk[i] = j < nkeys ? *reinterpret_cast<const uint4*>(Kg + row) : uint4{0, 0, 0, 0};
+      rv[i] = j < nkeys ? *reinterpret_cast<const uint4*>(Vg + row) : uint4{0, 0, 0, 0};
+    }
   }
 }
 
-// K rows as they are; each thread's 16-byte run of one token's V row goes to
-// column vpos (the token's slot in perm_key order) of V^T.
-template <typename C>
-__device__ __forceinline__ void gather_store(char* lds, int buf, int tid, const int (&vpos)[C::NCK],
-                                             const uint4 (&rk)[C::NCK], const uint4 (&rv)[C::NCK]) {
+// Registers -> LDS buffer `buf`: K rows [KT][DPAD]; V^T [D][VPAD] in perm_key token
+// order (dense: already packed that way; gathered: each thread's 16-byte run of
+// one token's V row goes to column vpos of V^T).
+template <typename C, bool GATHER>
+__device__ __forceinline__ void tile_store(char* lds, int buf, int tid, const int (&vpos)[C::NCK],
+                                           const uint4 (&rk)[C::NCK], const uint4 (&rv)[C::NCK]) {
   using T = typename C::T;
   constexpr int CPR = C::D / C::EPC;
+  constexpr int VCPR = C::KT / C::EPC;
   T* Kb = reinterpret_cast<T*>(lds + buf * C::KBYTES);
   T* Vb = reinterpret_cast<T*>(lds + 2 * C::KBYTES + buf * C::VBYTES);
 #pragma unroll
   for (int i = 0; i < C::NCK; ++i) {
     const int c = tid + i * C::NT;
     *reinterpret_cast<uint4*>(Kb + (c / CPR) * C::DPAD + (c % CPR) * C::EPC) = rk[i];
-    const int e = (c % CPR) * C::EPC;
-    const T* v = reinterpret_cast<const T*>(&rv[i]);
+    if constexpr (!GATHER) {
+      *reinterpret_cast<uint4*>(Vb + (c / VCPR) * C::VPAD + (c % VCPR) * C::EPC) = rv[i];
+    } else {
+      const int e = (c % CPR) * C::EPC;
+      const T* v = reinterpret_cast<const T*>(&rv[i]);
 #pragma unroll
-    for (int x = 0; x < C::EPC; ++x) Vb[(e + x) * C::VPAD + vpos[i]] = v[x];
+      for (int x = 0; x < C::EPC; ++x) Vb[(e + x) * C::VPAD + vpos[i]] = v[x];
+    }
+  }
+}
+
+// acc[i] += W[rows 32 rb ..][k0 + ..] x B[columns 32 (cb0 + i) ..]^T over nks MFMA
+// steps: W from global memory through a 4-deep register prefetch ring, B from LDS.
+template <typename T, int NKS, int NTILE>
+__device__ __forceinline__ void gemm_wrow(const T* __restrict__ Wrow, int ldw, const T* B, int ldb, int cb0,
+                                          f32x16 (&acc)[NTILE], int lane) {
+  using MM = Mma<T>;
+  using Frag = typename MM::frag;
+  constexpr int PF = NKS < 4 ? NKS : 4;
+  Frag ring[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) ring[p] = load_frag<T>(Wrow + p * MM::KS, ldw, lane);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const Frag a = ring[ks % PF];
+    if (ks + PF < NKS) ring[ks % PF] = load_frag<T>(Wrow + (ks + PF) * MM::KS, ldw, lane);
+#pragma unroll
+    for (int i = 0; i < NTILE; ++i)
+      acc[i] = MM::mma(a, load_frag<T>(B + (32 * (cb0 + i)) * ldb + ks * MM::KS, ldb, lane), acc[i]);
   }
 }
 
@@ -202,21 +259,6 @@ __device__ __forceinline__ void tile_compute(const typename Mma<typename C::T>::
   }
 }
 
-template <typename C>
-__device__ __forceinline__ void as_frags(const uint4 (&kr)[C::RUN_U4], const uint4 (&vr)[C::RUN_U4],
-                                         typename Mma<typename C::T>::frag (&kf)[C::KSTEPS],
-                                         typename Mma<typename C::T>::frag (&vf)[2][C::PSTEPS]) {
-  using Frag = typename Mma<typename C::T>::frag;
-  const Frag* kp = reinterpret_cast<const Frag*>(kr);
-  const Frag* vp = reinterpret_cast<const Frag*>(vr);
-#pragma unroll
-  for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = kp[ks];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int ps = 0; ps < C::PSTEPS; ++ps) vf[db][ps] = vp[db * C::PSTEPS + ps];
-}
-
 template <typename C, bool GATHER>
 __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   extern __shared__ __align__(16) char lds[];
@@ -236,7 +278,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   const T* __restrict__ W2 = (const T*)A.W2;
   const float kmax = A.kmax[hw];
 
-  int vpos[C::NCK];
+  int vpos[C::NCK] = {};
   if constexpr (GATHER) {
     constexpr int CPR = C::D / C::EPC;
 #pragma unroll
@@ -330,12 +372,12 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       }
     } else {
       uint4 rk[C::NCK], rv[C::NCK];
-      gather_load<C>(Kg, Vg, sel, nkeys, A.M, 0, tid, rk, rv);
-      gather_store<C>(lds, 0, tid, vpos, rk, rv);
+      tile_load<C, GATHER>(Kg, Vg, sel, nkeys, A.M, 0, tid, rk, rv);
+      tile_store<C, GATHER>(lds, 0, tid, vpos, rk, rv);
       __syncthreads();
       for (int kt = 0; kt < nkt; ++kt) {
-        const int knext = kt + 1 < nkt ? kt + 1 : kt;
-        gather_load<C>(Kg, Vg, sel, nkeys, A.M, knext, tid, rk, rv);
+        // prefetch the next tile (clamped: the last step reloads its own tile)
+        tile_load<C, GATHER>(Kg, Vg, sel, nkeys, A.M, kt + 1 < nkt ? kt + 1 : kt, tid, rk, rv);
         const T* Kb = reinterpret_cast<const T*>(lds + (kt & 1) * C::KBYTES);
         const T* Vb = reinterpret_cast<const T*>(lds + 2 * C::KBYTES + (kt & 1) * C::VBYTES);
         Frag kf[KS], vf[2][PS];
@@ -351,7 +393,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
         else
           tile_compute<C, false>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
         // the other buffer was last read before the previous barrier
-        gather_store<C>(lds, (kt + 1) & 1, tid, vpos, rk, rv);
+        tile_store<C, GATHER>(lds, (kt + 1) & 1, tid, vpos, rk, rv);
         __syncthreads();
       }
     }
@@ -370,97 +412,53 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     __syncthreads();
 
     // ---------------------------------------------------------------- a = Wo o  (kept in fp32 as y)
-    // this wave's epilogue tiles i = 0..TPW-1: row block rb0 + (cb0 + i) / CB, column block (cb0 + i) % CB
-    constexpr int RBW = C::TPW >= C::CB ? C::TPW / C::CB : 1;
+    // this wave's epilogue tiles: weight row block rb0, column blocks cb0 .. cb0 + TPW - 1
     const int rb0 = (wave * C::TPW) / C::CB, cb0 = (wave * C::TPW) % C::CB;
     f32x16 Y[C::TPW];
 #pragma unroll
     for (int i = 0; i < C::TPW; ++i) Y[i] = zero16();
-    for (int ks = 0; ks < C::D / MM::KS; ++ks) {
-      Frag af[RBW];
-#pragma unroll
-      for (int r = 0; r < RBW; ++r) af[r] = load_frag<T>(Wo + (32 * (rb0 + r)) * C::D + ks * MM::KS, C::D, lane);
-#pragma unroll
-      for (int i = 0; i < C::TPW; ++i) {
-        const int cb = (cb0 + i) % C::CB;
-        Y[i] = MM::mma(af[(cb0 + i) / C::CB], load_frag<T>(Ob + (32 * cb) * C::DPAD + ks * MM::KS, C::DPAD, lane),
-                       Y[i]);
-      }
-    }
+    gemm_wrow<T, C::D / MM::KS, C::TPW>(Wo + (32 * rb0) * C::D, C::D, Ob, C::DPAD, cb0, Y, lane);
     T* Ab = reinterpret_cast<T*>(lds + C::ABUF);
 #pragma unroll
-    for (int i = 0; i < C::TPW; ++i)
-      store_ct<T>(Ab + (32 * ((cb0 + i) % C::CB)) * C::DPAD + 32 * (rb0 + (cb0 + i) / C::CB), C::DPAD, Y[i], lane);
+    for (int i = 0; i < C::TPW; ++i) store_ct<T>(Ab + (32 * (cb0 + i)) * C::DPAD + 32 * rb0, C::DPAD, Y[i], lane);
     __syncthreads();
 
     // ---------------------------------------------------------------- y = a + W2 GELU(W1 a)
     T* Hb = reinterpret_cast<T*>(lds + C::OBUF);
-    constexpr int RBH = C::TPH >= C::CB ? C::TPH / C::CB : 1;
     const int rh0 = (wave * C::TPH) / C::CB, ch0 = (wave * C::TPH) % C::CB;
     for (int f0 = 0; f0 < A.F; f0 += C::FC) {
       f32x16 Hc[C::TPH];
 #pragma unroll
       for (int j = 0; j < C::TPH; ++j) Hc[j] = zero16();
-      for (int ks = 0; ks < C::D / MM::KS; ++ks) {
-        Frag af[RBH];
-#pragma unroll
-        for (int r = 0; r < RBH; ++r)
-          af[r] = load_frag<T>(W1 + (int64_t)(f0 + 32 * (rh0 + r)) * C::D + ks * MM::KS, C::D, lane);
-#pragma unroll
-        for (int j = 0; j < C::TPH; ++j) {
-          const int cb = (ch0 + j) % C::CB;
-          Hc[j] = MM::mma(af[(ch0 + j) / C::CB], load_frag<T>(Ab + (32 * cb) * C::DPAD + ks * MM::KS, C::DPAD, lane),
-                          Hc[j]);
-        }
-      }
+      gemm_wrow<T, C::D / MM::KS, C::TPH>(W1 + (int64_t)(f0 + 32 * rh0) * C::D, C::D, Ab, C::DPAD, ch0, Hc, lane);
 #pragma unroll
       for (int j = 0; j < C::TPH; ++j) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) Hc[j][r] = gelu(Hc[j][r]);
-        store_ct<T>(Hb + (32 * ((ch0 + j) % C::CB)) * C::HPAD + 32 * (rh0 + (ch0 + j) / C::CB), C::HPAD, Hc[j],
-                    lane);
+        store_ct<T>(Hb + (32 * (ch0 + j)) * C::HPAD + 32 * rh0, C::HPAD, Hc[j], lane);
       }
       __syncthreads();
-      for (int ks = 0; ks < C::FC / MM::KS; ++ks) {
-        Frag af[RBW];
-#pragma unroll
-        for (int r = 0; r < RBW; ++r)
-          af[r] = load_frag<T>(W2 + (int64_t)(32 * (rb0 + r)) * A.F + f0 + ks * MM::KS, A.F, lane);
-#pragma unroll
-        for (int i = 0; i < C::TPW; ++i) {
-          const int cb = (cb0 + i) % C::CB;
-          Y[i] = MM::mma(af[(cb0 + i) / C::CB], load_frag<T>(Hb + (32 * cb) * C::HPAD + ks * MM::KS, C::HPAD, lane),
-                         Y[i]);
-        }
-      }
+      gemm_wrow<T, C::FC / MM::KS, C::TPW>(W2 + (int64_t)(32 * rb0) * A.F + f0, A.F, Hb, C::HPAD, cb0, Y, lane);
       __syncthreads();
     }
 
     // ---------------------------------------------------------------- net = w_head . y, SDF
     float* red = reinterpret_cast<float*>(lds + C::RED);
     {
-      // column blocks this wave covers: cb0 .. cb0 + CPW - 1 (all of them when TPW >= CB)
-      constexpr int CPW = C::TPW >= C::CB ? C::CB : C::TPW;
-      float part[CPW];
+      float w[16];
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) part[c] = 0.f;
+      for (int r = 0; r < 16; ++r) w[r] = A.w_head[32 * rb0 + crow(r, lane)];
 #pragma unroll
       for (int i = 0; i < C::TPW; ++i) {
-        const int rb = rb0 + (cb0 + i) / C::CB;
         float s = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += A.w_head[32 * rb + crow(r, lane)] * Y[i][r];
-        part[i % CPW] += s;
+        for (int r = 0; r < 16; ++r) s += w[r] * Y[i][r];
+        s += __shfl_xor(s, 32);
+        if (lane < 32) red[wave * C::BQ + 32 * (cb0 + i) + lane] = s;
       }
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) {
-        const float s = part[c] + __shfl_xor(part[c], 32);
-        if (lane < 32) red[wave * C::BQ + 32 * ((cb0 + c) % C::CB) + lane] = s;
-      }
-      for (int cb = 0; cb < C::CB; ++cb) {
-        const int rel = (cb - cb0 + C::CB) % C::CB;
-        if (rel >= CPW && lane < 32) red[wave * C::BQ + 32 * cb + lane] = 0.f;
-      }
+      // column blocks this wave does not cover contribute zero
+      for (int cb = 0; cb < C::CB; ++cb)
+        if ((cb < cb0 || cb >= cb0 + C::TPW) && lane < 32) red[wave * C::BQ + 32 * cb + lane] = 0.f;
     }
     __syncthreads();
     for (int t = tid; t < C::BQ; t += C::NT) {
@@ -480,13 +478,13 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   }
 }
 
-typedef DecCfg<bf16, 4, 8, 64, 128> CfgB256;
+typedef DecCfg<bf16, 4, 8, 64, 256> CfgB256;
 typedef DecCfg<bf16, 1, 4, 32, 64> CfgB64;
 typedef DecCfg<float, 1, 4, 32, 64> CfgF64;
 
 template <typename C, bool GATHER>
 static hipError_t run(const DecodeArgs& a, hipStream_t s) {
-  constexpr int lds = GATHER ? C::LDS_GATHER : C::LDS_DENSE;
+  constexpr int lds = C::LDS;
   static bool attr = false;
   const void* fn = reinterpret_cast<const void*>(&decode_kernel<C, GATHER>);
   if (!attr) {
