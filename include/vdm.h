@@ -41,7 +41,7 @@
  *     (VDM_ERR_HIP: a launch failed; earlier launches of that call may have run).
  *   - N = 0 queries is a successful no-op.
  *   - Supported decoders: n_freq = 8; dtype BF16 with D = 64 or 256, or F32 with
- *     D = 64; H = D / 64; F a multiple of 128 (BF16, D = 256) or 64 (D = 64),
+ *     D = 64; H = D / 64; F a multiple of 256 (BF16, D = 256) or 64 (D = 64),
  *     at most 4096; M >= 1 tokens.
  *   - NaN/Inf in inputs propagate to the affected outputs; a NaN SDF value never
  *     makes a voxel active (every comparison with NaN is false).
@@ -234,6 +234,29 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* params
 size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, int32_t with_sel);
 size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M);
 size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M);
+
+/* ---------------------------------------------------------------- kernel timing */
+
+/* Kinds of launches the library can time. */
+enum {
+  VDM_TIME_DECODE = 0,      /* fused decode over the whole token set (dense, hierarchical levels) */
+  VDM_TIME_DECODE_GATHERED, /* fused decode over per-block token sets (adaptive KV selection) */
+  VDM_TIME_SELECT,          /* probe scoring, top-k and union (vdm_select_kv, hierarchical levels) */
+  VDM_TIME_EMBED,           /* vdm_embed_queries */
+  VDM_TIME_PROJECT_KV,      /* vdm_project_kv */
+  VDM_TIME_MASKS,           /* per-level bookkeeping of vdm_decode_hier: cell test, dilation,
+                               child marking, scan, list emission, ancestor fill */
+  VDM_TIME_KINDS
+};
+
+/* Launch timing with HIP events: while on, every launch of the kinds above is
+ * bracketed by two events recorded on the call's stream (host-side state shared
+ * by all threads; nothing is synchronised when recording).
+ * mode: 1 = on, 0 = off (records kept), 2 = drop all records (state unchanged).
+ * vdm_timing_read waits for the recorded events of one kind and returns how many
+ * launches were recorded and their summed durations in milliseconds. */
+vdm_status vdm_timing(int32_t mode);
+vdm_status vdm_timing_read(int32_t kind, int64_t* launches, double* total_ms);
 
 /* VDM_VERSION of the built library. */
 int32_t vdm_version(void);

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("VDM_LIB") or os.path.join(_HERE, "libvdm.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m shape_vae_decoding_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python shape_vae_decoding_amd/build.py`")
 _lib = C.CDLL(LIB_PATH)
 
 VDM_OK, VDM_ERR_INVALID_ARG, VDM_ERR_UNSUPPORTED, VDM_ERR_WORKSPACE, VDM_ERR_HIP = 0, -1, -2, -3, -4
@@ -32,9 +32,10 @@ MAX_PRIMS, MAX_LEVELS, STAT_FIELDS = 16, 6, 8
 STAT_NAMES = ["R", "tested", "active", "kept", "queries", "blocks", "items", "selected"]
 EXPORTS = [
     "vdm_embed_queries", "vdm_project_kv", "vdm_decode_dense", "vdm_select_kv", "vdm_decode_hier",
-    "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_version",
-    "vdm_last_error",
+    "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_timing",
+    "vdm_timing_read", "vdm_version", "vdm_last_error",
 ]
+TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "masks"]
 
 
 class VdmError(RuntimeError):
@@ -101,6 +102,10 @@ _lib.vdm_select_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64]
 _lib.vdm_select_workspace_size.restype = C.c_size_t
 _lib.vdm_hier_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int64]
 _lib.vdm_hier_workspace_size.restype = C.c_size_t
+_lib.vdm_timing.argtypes = [C.c_int32]
+_lib.vdm_timing.restype = C.c_int
+_lib.vdm_timing_read.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
+_lib.vdm_timing_read.restype = C.c_int
 _lib.vdm_version.restype = C.c_int32
 _lib.vdm_last_error.restype = C.c_char_p
 
@@ -116,6 +121,18 @@ def vdm_last_error() -> str:
 def _check(status: int) -> None:
     if status != VDM_OK:
         raise VdmError(status, vdm_last_error())
+
+
+def vdm_timing(mode: int) -> None:
+    """1 = record launch events, 0 = stop (records kept), 2 = drop records."""
+    _check(_lib.vdm_timing(mode))
+
+
+def vdm_timing_read(kind: str):
+    """(launches, total ms) recorded for one of TIME_KINDS; waits for the events."""
+    n, ms = C.c_int64(), C.c_double()
+    _check(_lib.vdm_timing_read(TIME_KINDS.index(kind), C.byref(n), C.byref(ms)))
+    return int(n.value), float(ms.value)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

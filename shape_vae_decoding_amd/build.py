@@ -1,7 +1,7 @@
 """Build libvdm.so (HIP for gfx950) in-tree: every csrc/*.hip compiled to an
 object under _build/, then linked into shape_vae_decoding_amd/libvdm.so.
 
-    python -m shape_vae_decoding_amd.build
+    python shape_vae_decoding_amd/build.py
 """
 
 from __future__ import annotations

@@ -5,7 +5,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "vdm_hvd.hpp"
 #include "vdm_internal.hpp"
@@ -31,6 +34,13 @@ static vdm_status fail(vdm_status st, const char* fmt, ...) {
     if (e_ != hipSuccess) return fail(VDM_ERR_HIP, "%s: %s", what, hipGetErrorString(e_));          \
   } while (0)
 
+// VDM_HIP for a launch of timing kind `kind` (see vdm_timing)
+#define VDM_HIP_T(kind, s, call, what) \
+  do {                                 \
+    Timed tm_((kind), (s));            \
+    VDM_HIP(call, what);               \
+  } while (0)
+
 DevInfo dev_info() {
   static DevInfo cache[64];
   static bool have[64];
@@ -45,6 +55,67 @@ DevInfo dev_info() {
   }
   return cache[dev];
 }
+
+// ------------------------------------------------------------------ launch timing
+namespace {
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> free_events;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[VDM_TIME_KINDS];
+  hipEvent_t get() {  // caller holds mu
+    if (!free_events.empty()) {
+      hipEvent_t e = free_events.back();
+      free_events.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) == hipSuccess) return e;
+    (void)hipGetLastError();
+    return nullptr;
+  }
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+// Records an event on `s` now and another when it goes out of scope, if timing is on.
+class Timed {
+ public:
+  Timed(int kind, hipStream_t s) : kind_(kind), s_(s) {
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (!t.on) return;
+    a_ = t.get();
+    b_ = t.get();
+    if (a_ && b_ && hipEventRecord(a_, s_) == hipSuccess) return;
+    (void)hipGetLastError();  // a failed record must not be reported by the launch that follows
+    if (a_) t.free_events.push_back(a_);
+    if (b_) t.free_events.push_back(b_);
+    a_ = b_ = nullptr;
+  }
+  ~Timed() {
+    if (!a_) return;
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (hipEventRecord(b_, s_) == hipSuccess) {
+      t.rec[kind_].emplace_back(a_, b_);
+    } else {
+      (void)hipGetLastError();
+      t.free_events.push_back(a_);
+      t.free_events.push_back(b_);
+    }
+  }
+  Timed(const Timed&) = delete;
+  Timed& operator=(const Timed&) = delete;
+
+ private:
+  int kind_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+}  // namespace
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 static size_t esize(int dtype) { return dtype == VDM_BF16 ? 2 : 4; }
@@ -225,6 +296,41 @@ using namespace vdm;
 extern "C" {
 
 const char* vdm_last_error(void) { return g_err.c_str(); }
+vdm_status vdm_timing(int32_t mode) {
+  if (mode < 0 || mode > 2) return fail(VDM_ERR_INVALID_ARG, "timing mode %d is not 0, 1 or 2", mode);
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (mode == 2) {
+    for (auto& r : t.rec) {
+      for (auto& e : r) {
+        t.free_events.push_back(e.first);
+        t.free_events.push_back(e.second);
+      }
+      r.clear();
+    }
+  } else {
+    t.on = mode == 1;
+  }
+  return VDM_OK;
+}
+
+vdm_status vdm_timing_read(int32_t kind, int64_t* launches, double* total_ms) {
+  if (kind < 0 || kind >= VDM_TIME_KINDS) return fail(VDM_ERR_INVALID_ARG, "timing kind %d out of range", kind);
+  if (!launches || !total_ms) return fail(VDM_ERR_INVALID_ARG, "null output pointer");
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  double sum = 0.0;
+  for (auto& e : t.rec[kind]) {
+    VDM_HIP(hipEventSynchronize(e.second), "timing event wait");
+    float ms = 0.f;
+    VDM_HIP(hipEventElapsedTime(&ms, e.first, e.second), "timing event read");
+    sum += ms;
+  }
+  *launches = (int64_t)t.rec[kind].size();
+  *total_ms = sum;
+  return VDM_OK;
+}
+
 int32_t vdm_version(void) { return VDM_VERSION; }
 
 size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, int32_t with_sel) {
@@ -256,7 +362,7 @@ vdm_status vdm_embed_queries(const vdm_decoder* dec, const float* xyz, int64_t N
   if (!aligned(xyz, 4) || !aligned(Q, 16)) return fail(VDM_ERR_INVALID_ARG, "misaligned xyz or Q");
   QuerySrc qs{0, 0, xyz, nullptr, 0};
   (void)hipGetLastError();
-  VDM_HIP(launch_embed(dec->dtype, dec->D, qs, N, dec->Wq, Q, (hipStream_t)stream), "embed launch");
+  VDM_HIP_T(VDM_TIME_EMBED, (hipStream_t)stream, launch_embed(dec->dtype, dec->D, qs, N, dec->Wq, Q, (hipStream_t)stream), "embed launch");
   return VDM_OK;
 }
 
@@ -268,7 +374,7 @@ vdm_status vdm_project_kv(const vdm_decoder* dec, const void* Z, int64_t M, void
   if (!Z || !K || !V) return fail(VDM_ERR_INVALID_ARG, "Z, K or V is NULL");
   if (!aligned(Z, 16) || !aligned(K, 16) || !aligned(V, 16)) return fail(VDM_ERR_INVALID_ARG, "misaligned Z, K or V");
   (void)hipGetLastError();
-  VDM_HIP(launch_project_kv(dec->dtype, Z, dec->Wk, dec->Wv, (int)M, dec->D, K, V, (hipStream_t)stream),
+  VDM_HIP_T(VDM_TIME_PROJECT_KV, (hipStream_t)stream, launch_project_kv(dec->dtype, Z, dec->Wk, dec->Wv, (int)M, dec->D, K, V, (hipStream_t)stream),
           "project_kv launch");
   return VDM_OK;
 }
@@ -319,7 +425,7 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
     a.Vt = w.Vt;
     a.M = (int)M;
     a.n_tiles = (q->N + decode_tile_queries(dec->dtype, dec->D) - 1) / decode_tile_queries(dec->dtype, dec->D);
-    VDM_HIP(launch_decode(dec->dtype, dec->D, false, a, s), "decode launch");
+    VDM_HIP_T(VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, false, a, s), "decode launch");
   } else {
     const int bq = decode_tile_queries(dec->dtype, dec->D);
     VDM_HIP(launch_zero(w.n_items, 256, s), "zero launch");
@@ -334,7 +440,7 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
     a.sel_idx = sel->sel_idx;
     a.sel_cnt = sel->sel_cnt;
     a.cap = sel->cap;
-    VDM_HIP(launch_decode(dec->dtype, dec->D, true, a, s), "gathered decode launch");
+    VDM_HIP_T(VDM_TIME_DECODE_GATHERED, s, launch_decode(dec->dtype, dec->D, true, a, s), "gathered decode launch");
   }
   return VDM_OK;
 }
@@ -370,7 +476,7 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
   (void)hipGetLastError();
-  VDM_HIP(launch_select(dec->dtype, a, (hipStream_t)stream), "select launch");
+  VDM_HIP_T(VDM_TIME_SELECT, (hipStream_t)stream, launch_select(dec->dtype, a, (hipStream_t)stream), "select launch");
   return VDM_OK;
 }
 
@@ -425,7 +531,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       sa.sel_idx = w.sel_idx;
       sa.sel_cnt = w.sel_cnt;
       sa.stat_selected = S + L * VDM_STAT_FIELDS + VDM_STAT_SELECTED;
-      VDM_HIP(launch_select(dec->dtype, sa, s), "select launch");
+      VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, sa, s), "select launch");
     }
     DecodeArgs a = base_args(dec);
     a.qs = QuerySrc{VDM_Q_GRID_LIST, R, nullptr, w.list, 0};
@@ -446,7 +552,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       a.Vt = w.Vt;
       a.d_N = tot;
     }
-    VDM_HIP(launch_decode(dec->dtype, dec->D, kv, a, s), "decode launch");
+    VDM_HIP_T(kv ? VDM_TIME_DECODE_GATHERED : VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, kv, a, s), "decode launch");
     return VDM_OK;
   };
 
@@ -454,16 +560,16 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
   {
     const int NB = nblocks8(p->R0 + 1);
     const int64_t nb3 = (int64_t)NB * NB * NB;
-    VDM_HIP(launch_mark(nullptr, 1, nullptr, 1, p->R0, w.newmask, nullptr, w.counts, s), "mark launch");
-    VDM_HIP(launch_scan(w.counts, nb3, bq, w.partial, w.offs, w.totals, S, s), "scan launch");
-    VDM_HIP(launch_emit(w.newmask, w.counts, w.offs, p->R0, bq, w.list, w.items, w.occ, s), "emit launch");
+    VDM_HIP_T(VDM_TIME_MASKS, s, launch_mark(nullptr, 1, nullptr, 1, p->R0, w.newmask, nullptr, w.counts, s), "mark launch");
+    VDM_HIP_T(VDM_TIME_MASKS, s, launch_scan(w.counts, nb3, bq, w.partial, w.offs, w.totals, S, s), "scan launch");
+    VDM_HIP_T(VDM_TIME_MASKS, s, launch_emit(w.newmask, w.counts, w.offs, p->R0, bq, w.list, w.items, w.occ, s), "emit launch");
     st = decode_level(0);
     if (st != VDM_OK) return st;
   }
   for (int L = 0; L < p->levels; ++L) {
     const int R = p->R0 << L, P = R + 1, NB = nblocks8(P);
     int64_t* SL = S + L * VDM_STAT_FIELDS;
-    VDM_HIP(launch_cell_test(vol_of(L), R, L ? w.kept[L - 1] : nullptr, p->tau, w.active[L], SL + VDM_STAT_TESTED,
+    VDM_HIP_T(VDM_TIME_MASKS, s, launch_cell_test(vol_of(L), R, L ? w.kept[L - 1] : nullptr, p->tau, w.active[L], SL + VDM_STAT_TESTED,
                              SL + VDM_STAT_ACTIVE, s),
             "cell test launch");
     if (dbg) {
@@ -484,24 +590,24 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
     if (L == p->levels - 1) break;
     // kept = active dilated `dilation` times (ping-pong through tmp)
     if (p->dilation == 0) {
-      VDM_HIP(launch_dilate(w.active[L], w.kept[L], R, 1, SL + VDM_STAT_KEPT, s), "copy launch");
+      VDM_HIP_T(VDM_TIME_MASKS, s, launch_dilate(w.active[L], w.kept[L], R, 1, SL + VDM_STAT_KEPT, s), "copy launch");
     } else {
       const uint64_t* src = w.active[L];
       for (int t = 0; t < p->dilation; ++t) {
         uint64_t* dst = ((p->dilation - 1 - t) % 2 == 0) ? w.kept[L] : w.tmp;
-        VDM_HIP(launch_dilate(src, dst, R, 0, t == p->dilation - 1 ? SL + VDM_STAT_KEPT : nullptr, s), "dilate launch");
+        VDM_HIP_T(VDM_TIME_MASKS, s, launch_dilate(src, dst, R, 0, t == p->dilation - 1 ? SL + VDM_STAT_KEPT : nullptr, s), "dilate launch");
         src = dst;
       }
     }
     if (dbg && dbg->kept[L]) VDM_HIP(launch_bits_to_bytes(w.kept[L], R, NB, dbg->kept[L], s), "debug export");
     const int Rn = 2 * R, Pn = Rn + 1, NBn = nblocks8(Pn);
-    VDM_HIP(launch_mark(w.kept[L], R, L ? w.comp[L] : nullptr, 0, Rn, w.newmask, w.comp[L + 1], w.counts, s),
+    VDM_HIP_T(VDM_TIME_MASKS, s, launch_mark(w.kept[L], R, L ? w.comp[L] : nullptr, 0, Rn, w.newmask, w.comp[L + 1], w.counts, s),
             "mark launch");
-    VDM_HIP(launch_scan(w.counts, (int64_t)NBn * NBn * NBn, bq, w.partial, w.offs, w.totals + 4 * (L + 1),
+    VDM_HIP_T(VDM_TIME_MASKS, s, launch_scan(w.counts, (int64_t)NBn * NBn * NBn, bq, w.partial, w.offs, w.totals + 4 * (L + 1),
                         S + (L + 1) * VDM_STAT_FIELDS, s),
             "scan launch");
-    VDM_HIP(launch_emit(w.newmask, w.counts, w.offs, Rn, bq, w.list, w.items, w.occ, s), "emit launch");
-    VDM_HIP(launch_fill(vol_of(L), P, vol_of(L + 1), Pn, s), "fill launch");
+    VDM_HIP_T(VDM_TIME_MASKS, s, launch_emit(w.newmask, w.counts, w.offs, Rn, bq, w.list, w.items, w.occ, s), "emit launch");
+    VDM_HIP_T(VDM_TIME_MASKS, s, launch_fill(vol_of(L), P, vol_of(L + 1), Pn, s), "fill launch");
     st = decode_level(L + 1);
     if (st != VDM_OK) return st;
   }

@@ -128,3 +128,17 @@ def test_select_and_hier_argument_checks():
                                0x1000, 1 << 40, None) == V.VDM_ERR_INVALID_ARG  # volume too small
     assert lib.vdm_decode_hier(C.byref(d), C.byref(p), 0x1000, 0x1000, 3072, 0x1000, 301 ** 3, None, None,
                                0x1000, 1024, None) == V.VDM_ERR_WORKSPACE
+
+
+def test_timing_api_without_launches():
+    import shape_vae_decoding_amd as V
+
+    V.vdm_timing(2)
+    V.vdm_timing(1)
+    assert V.vdm_timing_read("decode") == (0, 0.0)  # nothing launched: no events to wait for
+    V.vdm_timing(0)
+    assert V._lib.vdm_timing(3) == V.VDM_ERR_INVALID_ARG
+    assert "timing mode" in V.vdm_last_error()
+    n, ms = C.c_int64(), C.c_double()
+    assert V._lib.vdm_timing_read(len(V.TIME_KINDS), C.byref(n), C.byref(ms)) == V.VDM_ERR_INVALID_ARG
+    assert V._lib.vdm_timing_read(0, None, C.byref(ms)) == V.VDM_ERR_INVALID_ARG
