@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_dense_129cubed_traffic.json")
+COPY_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_dense_129cubed_traffic.md")
 DECODE_SOURCES = ["shape_vae_decoding_amd/csrc/k_decode.hip", "shape_vae_decoding_amd/csrc/vdm_device.hpp"]
 
 
@@ -44,6 +45,22 @@ def decode_source_sha() -> str:
     for p in DECODE_SOURCES:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per dense decode launch from the committed counter summary
+    (`key: value` lines), or None when it was taken on other kernel sources."""
+    try:
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha") != decode_source_sha():
+        return None
+    try:
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -87,6 +104,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU baseline (profiling runs)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="after the steps, copy 512 MiB device-to-device 3 times (a known-size kernel for "
+                         "calibrating the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decoder path here has no "
@@ -133,8 +153,10 @@ def main():
         V.vdm_project_kv(dec, Z, K, Vv)
         if ev:
             ev[1].record()
+            V.vdm_timing(1)  # the library brackets the dense decode launch with HIP events
         V.vdm_decode_dense(dec, q, K, Vv, sdf, ws=ws_dense)
         if ev:
+            V.vdm_timing(0)
             ev[2].record()
         V.vdm_decode_hier(dec, p_h, K, Vv, vol_h, st_h, ws=ws_h)
         if ev:
@@ -148,6 +170,7 @@ def main():
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    V.vdm_timing(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -164,16 +187,26 @@ def main():
     total_q = N + q_h + q_a
     value = total_q / (ms_step / 1e3)
 
+    n_launch, decode_ms = V.vdm_timing_read("decode")
+    assert n_launch == args.steps, (n_launch, args.steps)
+    launch_ms = decode_ms / n_launch
+    V.vdm_timing(2)
+
+    # one more pass with every launch timed, for the per-kernel-kind breakdown
+    V.vdm_timing(1)
+    step()
+    V.vdm_timing(0)
+    kinds = {}
+    for kind in V.TIME_KINDS:
+        n, ms = V.vdm_timing_read(kind)
+        if n:
+            kinds[kind] = {"launches": n, "ms": round(ms, 4)}
+    V.vdm_timing(2)
+
     phi = flops_per_query(51, w.D, w.M, w.F)
     dense_flop = phi * N
-    achieved = dense_flop / (row_ms[1] / 1e3) / 1e12
-    traffic = None
-    try:
-        t = json.load(open(TRAFFIC_FILE))
-        if t.get("kernel_source_sha") == decode_source_sha():
-            traffic = t.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    achieved = dense_flop / (launch_ms / 1e3) / 1e12
+    traffic = read_traffic()
     roofline = {
         "bound": "mfma",
         "achieved": round(achieved, 2),
@@ -181,9 +214,9 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": traffic,
-        "kernel": "vdm_decode_dense on the 129^3 grid (pack + fused decode launch)",
+        "kernel": "fused decode launch of vdm_decode_dense on the 129^3 grid (embed, Q-proj, attention, MLP, head)",
         "flop_per_launch": dense_flop,
-        "launch_ms": round(float(row_ms[1]), 4),
+        "launch_ms": round(launch_ms, 4),
     }
     out = {
         "metric": "query points/sec (dense & hierarchical) + ms per 300^3 volume decode; % roofline",
@@ -215,11 +248,20 @@ def main():
             "hier_volume_points_per_s": round(Pf ** 3 / (row_ms[2] / 1e3), 1),
             "akvs_ms_per_300cubed_volume": round(float(row_ms[3]), 4),
             "akvs_volume_points_per_s": round(Pf ** 3 / (row_ms[3] / 1e3), 1),
+            "kernel_kinds_one_step": kinds,
             "hier_levels": sh,
             "akvs_levels": sa,
         },
         "roofline": roofline,
     }
+    if args.copy_calib:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
