@@ -110,7 +110,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decoder path here has no "
-              f"multi-GPU part: queries shard by independent slabs, see DESIGN.md", file=sys.stderr)
+              f"multi-GPU part (queries would shard by independent z-slabs with K/V replicated per GPU)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -1,6 +1,6 @@
 """Seeded workload generator (data only; see the package docstring).
 
-Recipe (readings of the pages are listed in the design doc):
+Recipe (the pages leave these details open; the plainest reading is taken):
 
 * Decoder weights are N(0, 1/fan_in): Wq [D,51], Wk/Wv/Wo [D,D], W1 [F,D],
   W2 [D,F], w_head [D]. The 1024-wide decoder is drawn once and shared by the
