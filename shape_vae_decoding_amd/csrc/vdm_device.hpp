@@ -292,6 +292,20 @@ __device__ void embed_qproj(const QuerySrc& qs, int64_t q0, int64_t q1, const T*
   T* e_hi = reinterpret_cast<T*>(lds + L::E_HI);
   T* e_lo = reinterpret_cast<T*>(lds + L::E_LO);
   T* Qs = reinterpret_cast<T*>(lds + L::QS);
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  constexpr int NW = NT / 64;
+  constexpr int RB = D / 32, CB = BQ / 32, KS = 64 / MM::KS;
+  // wave w owns row blocks w, w + NW, .. (RB > NW) or row block w % RB and every
+  // (NW / RB)-th column block (RB <= NW); each of its Wq fragments is loaded once
+  constexpr int RPW = RB > NW ? RB / NW : 1;
+  constexpr int CSTEP = RB > NW ? 1 : NW / RB;
+  static_assert(RB % NW == 0 || NW % RB == 0, "row blocks split evenly over waves");
+  // the first row block's fragments are issued before the embedding so that
+  // their latency overlaps it
+  typename MM::frag wq[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) wq[ks] = load_wq_frag<T>(Wq, 32 * (wave % RB), ks, lane);
   for (int idx = tid; idx < BQ * 4; idx += NT) {
     const int qi = idx % BQ;
     const int part = idx / BQ;
@@ -315,21 +329,24 @@ __device__ void embed_qproj(const QuerySrc& qs, int64_t q0, int64_t q1, const T*
     }
   }
   __syncthreads();
-  const int lane = lane_id();
-  const int wave = tid >> 6;
-  constexpr int NW = NT / 64;
-  constexpr int RB = D / 32, CB = BQ / 32;
-  for (int t = wave; t < RB * CB; t += NW) {
-    const int rb = t / CB, cb = t % CB;
-    f32x16 acc = zero16();
 #pragma unroll
-    for (int ks = 0; ks < 64 / MM::KS; ++ks) {
-      const auto a = load_wq_frag<T>(Wq, 32 * rb, ks, lane);
-      acc = MM::mma(a, load_frag<T>(e_hi + (32 * cb) * L::EPAD + ks * MM::KS, L::EPAD, lane), acc);
-      if constexpr (L::SPLIT)
-        acc = MM::mma(a, load_frag<T>(e_lo + (32 * cb) * L::EPAD + ks * MM::KS, L::EPAD, lane), acc);
+  for (int j = 0; j < RPW; ++j) {
+    const int rb = RB > NW ? wave + NW * j : wave % RB;
+    if (j > 0) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) wq[ks] = load_wq_frag<T>(Wq, 32 * rb, ks, lane);
     }
-    store_ct<T>(Qs + (32 * cb) * L::DPAD + 32 * rb, L::DPAD, acc, lane);
+#pragma unroll
+    for (int cb = RB > NW ? 0 : wave / RB; cb < CB; cb += CSTEP) {
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc = MM::mma(wq[ks], load_frag<T>(e_hi + (32 * cb) * L::EPAD + ks * MM::KS, L::EPAD, lane), acc);
+        if constexpr (L::SPLIT)
+          acc = MM::mma(wq[ks], load_frag<T>(e_lo + (32 * cb) * L::EPAD + ks * MM::KS, L::EPAD, lane), acc);
+      }
+      store_ct<T>(Qs + (32 * cb) * L::DPAD + 32 * rb, L::DPAD, acc, lane);
+    }
   }
   __syncthreads();
 }
