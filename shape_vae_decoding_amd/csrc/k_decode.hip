@@ -33,6 +33,11 @@
 
 namespace vdm {
 
+// segments of the bf16 GELU table (see gelu_lookup)
+constexpr int GELU_SEGS = 2048;
+constexpr float GELU_LIM = 8.f;
+constexpr float GELU_SCALE = GELU_SEGS / (2.f * GELU_LIM);
+
 template <typename T_, int H_, int NW_, int QW_, int FC_>
 struct DecCfg {
   typedef T_ T;
@@ -63,7 +68,11 @@ struct DecCfg {
   static constexpr int EPI_END = RED + NW * BQ * 4;
   static constexpr int EMB_END = EmbedLds<T, BQ, D>::END;
   static constexpr int LDS_PRE = EPI_END > EMB_END ? EPI_END : EMB_END;
-  static constexpr int LDS = LDS_PRE > ATT_END ? LDS_PRE : ATT_END;
+  static constexpr int LDS_MAIN = LDS_PRE > ATT_END ? LDS_PRE : ATT_END;
+  // bf16: GELU table (value, slope) per segment, resident for the whole kernel
+  static constexpr bool GELU_TABLE = sizeof(T) == 2;
+  static constexpr int GTAB = LDS_MAIN;
+  static constexpr int LDS = LDS_MAIN + (GELU_TABLE ? GELU_SEGS * 8 : 0);
   // epilogue tiling: wave w owns C tiles [w*TPW, (w+1)*TPW) of (D/32) x (BQ/32), rb-major:
   // one row block of weights (loaded once per workgroup) for TPW column blocks
   static constexpr int CB = BQ / 32;
@@ -82,6 +91,44 @@ struct DecCfg {
   static_assert(KCH % NT == 0, "staging chunks split evenly");
   static_assert(LDS <= 160 * 1024, "fits gfx950 LDS");
 };
+
+// GELU by table for bf16 decoders: GELU_SEGS linear segments over [-GELU_LIM, GELU_LIM]
+// (width 1/128), each stored as (GELU(x_i), GELU(x_{i+1}) - GELU(x_i)); interpolation
+// error <= h^2/8 max|GELU''| < 7e-6, far below the bf16 rounding of the hidden
+// activations. Beyond the range GELU(x) = x (x > 8; the difference is below 1e-14)
+// or GELU(-8) (x < -8, |value| < 1e-14).
+
+__device__ __forceinline__ void gelu_table_fill(float2* tab, int tid, int nt) {
+  for (int i = tid; i < GELU_SEGS; i += nt) {
+    const float x0 = -GELU_LIM + (float)i / GELU_SCALE, x1 = -GELU_LIM + (float)(i + 1) / GELU_SCALE;
+    const float g0 = gelu(x0);
+    tab[i] = make_float2(g0, gelu(x1) - g0);
+  }
+}
+
+// GELU of the 16 values of one C tile; all 16 table reads are issued before the
+// first is used, so their LDS latency overlaps.
+template <typename C>
+__device__ __forceinline__ void gelu_tile(f32x16& h, const float2* tab) {
+  if constexpr (C::GELU_TABLE) {
+    float t[16];
+    float2 e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      t[r] = __builtin_amdgcn_fmed3f(__builtin_fmaf(h[r], GELU_SCALE, GELU_LIM * GELU_SCALE), 0.f,
+                                     (float)GELU_SEGS - 0.001f);
+      e[r] = tab[(int)t[r]];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float g = __builtin_fmaf(e[r].y, t[r] - (float)(int)t[r], e[r].x);
+      h[r] = !(h[r] <= GELU_LIM) ? h[r] : g;  // also passes NaN through
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) h[r] = gelu(h[r]);
+  }
+}
 
 // log2(e) / sqrt(64): logits are scaled once into base 2.
 constexpr float SOFTMAX_SCALE_LOG2 = 0.18033688011112042f;
@@ -205,23 +252,48 @@ __device__ __forceinline__ void tile_store(char* lds, int buf, int tid, const in
 }
 
 // acc[i] += W[rows 32 rb ..][k0 + ..] x B[columns 32 (cb0 + i) ..]^T over nks MFMA
-// steps: W from global memory through a 4-deep register prefetch ring, B from LDS.
-template <typename T, int NKS, int NTILE>
+// steps: W from global memory through a 4-deep register prefetch ring, B from LDS
+// one step ahead (double-buffered), so no MFMA waits on the LDS read it consumes.
+// `step(ks)` runs after the MFMAs of step ks are issued: independent VALU work
+// placed there overlaps the matrix pipe.
+struct NoStep {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// B_AHEAD: B fragments are read one step ahead (double-buffered); otherwise right
+// before use (for callers whose `step` work covers the LDS latency, at fewer registers).
+template <typename T, int NKS, int NTILE, bool B_AHEAD = true, int RING = 4, typename Step = NoStep>
 __device__ __forceinline__ void gemm_wrow(const T* __restrict__ Wrow, int ldw, const T* B, int ldb, int cb0,
-                                          f32x16 (&acc)[NTILE], int lane) {
+                                          f32x16 (&acc)[NTILE], int lane, Step step = Step()) {
   using MM = Mma<T>;
   using Frag = typename MM::frag;
-  constexpr int PF = NKS < 4 ? NKS : 4;
+  constexpr int PF = NKS < RING ? NKS : RING;
   Frag ring[PF];
 #pragma unroll
   for (int p = 0; p < PF; ++p) ring[p] = load_frag<T>(Wrow + p * MM::KS, ldw, lane);
+  Frag b[B_AHEAD ? 2 : 1][NTILE];
+  if constexpr (B_AHEAD) {
+#pragma unroll
+    for (int i = 0; i < NTILE; ++i) b[0][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb, ldb, lane);
+  }
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const Frag a = ring[ks % PF];
     if (ks + PF < NKS) ring[ks % PF] = load_frag<T>(Wrow + (ks + PF) * MM::KS, ldw, lane);
+    if constexpr (B_AHEAD) {
+      if (ks + 1 < NKS) {
 #pragma unroll
-    for (int i = 0; i < NTILE; ++i)
-      acc[i] = MM::mma(a, load_frag<T>(B + (32 * (cb0 + i)) * ldb + ks * MM::KS, ldb, lane), acc[i]);
+        for (int i = 0; i < NTILE; ++i)
+          b[(ks + 1) & 1][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb + (ks + 1) * MM::KS, ldb, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < NTILE; ++i) acc[i] = MM::mma(a, b[ks & 1][i], acc[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NTILE; ++i)
+        acc[i] = MM::mma(a, load_frag<T>(B + (32 * (cb0 + i)) * ldb + ks * MM::KS, ldb, lane), acc[i]);
+    }
+    step(ks);
   }
 }
 
@@ -277,6 +349,10 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   const T* __restrict__ W1 = (const T*)A.W1;
   const T* __restrict__ W2 = (const T*)A.W2;
   const float kmax = A.kmax[hw];
+
+  const float2* gtab = reinterpret_cast<const float2*>(lds + C::GTAB);
+  if constexpr (C::GELU_TABLE) gelu_table_fill(reinterpret_cast<float2*>(lds + C::GTAB), tid, C::NT);
+  // (the first barrier of the tile loop orders the fill before any lookup)
 
   int vpos[C::NCK] = {};
   if constexpr (GATHER) {
@@ -433,8 +509,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       gemm_wrow<T, C::D / MM::KS, C::TPH>(W1 + (int64_t)(f0 + 32 * rh0) * C::D, C::D, Ab, C::DPAD, ch0, Hc, lane);
 #pragma unroll
       for (int j = 0; j < C::TPH; ++j) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Hc[j][r] = gelu(Hc[j][r]);
+        gelu_tile<C>(Hc[j], gtab);
         store_ct<T>(Hb + (32 * (ch0 + j)) * C::HPAD + 32 * rh0, C::HPAD, Hc[j], lane);
       }
       __syncthreads();

@@ -209,18 +209,22 @@ __device__ __forceinline__ float analytic_sdf(Coords p, const PrimSet& ps) {
 // Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 for all
 // arguments; far below the bf16 rounding the hidden activations get next):
 // erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z), z >= 0.
-// Branch-free: one reciprocal and one exp2 per value.
+// With z = |x| / sqrt 2 folded into the constants, and the sign handled by
+// x/2 (1 + sign(x) erf|z|) = (x + |x| erf|z|) / 2. Branch-free: one reciprocal
+// and one exp2 per value.
 __device__ __forceinline__ float gelu(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.f));
+  constexpr float P_X = (float)(0.3275911 * 0.70710678118654752);  // p / sqrt 2
+  constexpr float C_X = 0.84932180028801904f;                       // sqrt(log2(e) / 2)
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(P_X, ax, 1.f));
   float y = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
   y = __builtin_fmaf(t, y, 1.421413741f);
   y = __builtin_fmaf(t, y, -0.284496736f);
   y = __builtin_fmaf(t, y, 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
+  const float u = x * C_X;
+  const float e = __builtin_amdgcn_exp2f(-(u * u));  // exp(-x^2 / 2)
   const float erf_abs = __builtin_fmaf(-(t * y), e, 1.f);
-  const float erf = __builtin_copysignf(erf_abs, x);
-  return 0.5f * x * (1.f + erf);
+  return 0.5f * __builtin_fmaf(ax, erf_abs, x);
 }
 
 // ------------------------------------------------------------------ embedding + Q projection
