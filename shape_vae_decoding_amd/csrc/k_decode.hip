@@ -78,16 +78,23 @@ struct DecCfg {
   static constexpr int CB = BQ / 32;
   static constexpr int TPW = (D / 32) * CB / NW;
   static constexpr int TPH = (FC / 32) * CB / NW;
+  // a wave owns RPW row blocks x CPW column blocks of the D x BQ outputs (RPH x CPH
+  // of an FC x BQ hidden chunk): whole rows of column blocks when it has that many
+  static constexpr int RPW = TPW >= CB ? TPW / CB : 1, CPW = TPW >= CB ? CB : TPW;
+  static constexpr int RPH = TPH >= CB ? TPH / CB : 1, CPH = TPH >= CB ? CB : TPH;
   // staging: 16-byte chunks per thread per tile (K and V each)
   static constexpr int KCH = KT * D * SZ / 16;
   static constexpr int NCK = KCH / NT;
   static constexpr int EPC = 16 / SZ;
+  // explicit MFMA / softmax interleaving in the token loop (bf16, 2+ query blocks)
+  static constexpr bool SCHED_ATT = SZ == 2 && QB >= 2;
 
   static_assert(NW % H == 0, "waves cover whole heads");
   static_assert(QW % 32 == 0, "query groups are whole MFMA columns");
   static_assert(BQ * HPAD * SZ <= ABUF, "GELU chunk fits where O was");
   static_assert(((D / 32) * CB) % NW == 0 && ((FC / 32) * CB) % NW == 0, "epilogue tiles split evenly");
-  static_assert(TPW <= CB && CB % TPW == 0 && TPH <= CB && CB % TPH == 0, "one weight row block per wave");
+  static_assert(TPW >= CB ? TPW % CB == 0 : CB % TPW == 0, "output tiles split evenly");
+  static_assert(TPH >= CB ? TPH % CB == 0 : CB % TPH == 0, "hidden tiles split evenly");
   static_assert(KCH % NT == 0, "staging chunks split evenly");
   static_assert(LDS <= 160 * 1024, "fits gfx950 LDS");
 };
@@ -136,13 +143,26 @@ constexpr float SOFTMAX_SCALE_LOG2 = 0.18033688011112042f;
 // token ids of a selection are clamped into [0, M) so that no input can index past K/V
 __device__ __forceinline__ int tok_clamp(int t, int M) { return t < 0 ? 0 : (t >= M ? M - 1 : t); }
 
+// Packed K/V operands are read with buffer loads: the tile/head base is a scalar
+// offset, the lane's run a fixed vector offset; reads past the buffer's size
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, int64_t bytes) {
+  constexpr int GFX9_RAW_BUFFER = 0x00020000;  // descriptor word 3: raw (untyped) buffer
+  const int n = bytes < 0x7fffffff ? (int)bytes : 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, GFX9_RAW_BUFFER);
+}
+
 // One lane's operand run (32 elements) of packed tile `kt`, head h.
 template <typename C>
-__device__ __forceinline__ void load_run(const typename C::T* __restrict__ base, int kt, int h, int lane,
+__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t buf, int kt, int h, int lane,
                                          uint4 (&r)[C::RUN_U4]) {
-  const uint4* p = reinterpret_cast<const uint4*>(base + ((int64_t)(kt * C::H + h) * 64 + lane) * 32);
+  const int soff = (kt * C::H + h) * 64 * 32 * C::SZ;
+  const int voff = lane * 32 * C::SZ;
 #pragma unroll
-  for (int i = 0; i < C::RUN_U4; ++i) r[i] = p[i];
+  for (int i = 0; i < C::RUN_U4; ++i) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(buf, voff + 16 * i, soff, 0);
+    r[i] = uint4{v[0], v[1], v[2], v[3]};
+  }
 }
 
 template <typename C>
@@ -251,49 +271,40 @@ __device__ __forceinline__ void tile_store(char* lds, int buf, int tid, const in
   }
 }
 
-// acc[i] += W[rows 32 rb ..][k0 + ..] x B[columns 32 (cb0 + i) ..]^T over nks MFMA
-// steps: W from global memory through a 4-deep register prefetch ring, B from LDS
-// one step ahead (double-buffered), so no MFMA waits on the LDS read it consumes.
-// `step(ks)` runs after the MFMAs of step ks are issued: independent VALU work
-// placed there overlaps the matrix pipe.
-struct NoStep {
-  __device__ __forceinline__ void operator()(int) const {}
-};
-
-// B_AHEAD: B fragments are read one step ahead (double-buffered); otherwise right
-// before use (for callers whose `step` work covers the LDS latency, at fewer registers).
-template <typename T, int NKS, int NTILE, bool B_AHEAD = true, int RING = 4, typename Step = NoStep>
-__device__ __forceinline__ void gemm_wrow(const T* __restrict__ Wrow, int ldw, const T* B, int ldb, int cb0,
-                                          f32x16 (&acc)[NTILE], int lane, Step step = Step()) {
+// acc[r][i] += W[rows 32 r ..][..] x B[columns 32 (cb0 + i) ..]^T for NR consecutive
+// row blocks of W (global memory, each through a RING-deep register prefetch ring)
+// and NC column blocks of B (LDS, read one step ahead, each fragment used NR times).
+template <typename T, int NKS, int NR, int NC, int RING = 4>
+__device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, const T* B, int ldb, int cb0,
+                                          f32x16 (&acc)[NR][NC], int lane) {
   using MM = Mma<T>;
   using Frag = typename MM::frag;
   constexpr int PF = NKS < RING ? NKS : RING;
-  Frag ring[PF];
+  Frag ring[NR][PF];
 #pragma unroll
-  for (int p = 0; p < PF; ++p) ring[p] = load_frag<T>(Wrow + p * MM::KS, ldw, lane);
-  Frag b[B_AHEAD ? 2 : 1][NTILE];
-  if constexpr (B_AHEAD) {
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int i = 0; i < NTILE; ++i) b[0][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb, ldb, lane);
-  }
+    for (int p = 0; p < PF; ++p) ring[r][p] = load_frag<T>(W + (int64_t)(32 * r) * ldw + p * MM::KS, ldw, lane);
+  Frag b[2][NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) b[0][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb, ldb, lane);
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const Frag a = ring[ks % PF];
-    if (ks + PF < NKS) ring[ks % PF] = load_frag<T>(Wrow + (ks + PF) * MM::KS, ldw, lane);
-    if constexpr (B_AHEAD) {
-      if (ks + 1 < NKS) {
+    Frag a[NR];
 #pragma unroll
-        for (int i = 0; i < NTILE; ++i)
-          b[(ks + 1) & 1][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb + (ks + 1) * MM::KS, ldb, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < NTILE; ++i) acc[i] = MM::mma(a, b[ks & 1][i], acc[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NTILE; ++i)
-        acc[i] = MM::mma(a, load_frag<T>(B + (32 * (cb0 + i)) * ldb + ks * MM::KS, ldb, lane), acc[i]);
+    for (int r = 0; r < NR; ++r) {
+      a[r] = ring[r][ks % PF];
+      if (ks + PF < NKS) ring[r][ks % PF] = load_frag<T>(W + (int64_t)(32 * r) * ldw + (ks + PF) * MM::KS, ldw, lane);
     }
-    step(ks);
+    if (ks + 1 < NKS) {
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+        b[(ks + 1) & 1][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb + (ks + 1) * MM::KS, ldb, lane);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < NC; ++i) acc[r][i] = MM::mma(a[r], b[ks & 1][i], acc[r][i]);
   }
 }
 
@@ -329,6 +340,89 @@ __device__ __forceinline__ void tile_compute(const typename Mma<typename C::T>::
 #pragma unroll
       for (int ps = 0; ps < C::PSTEPS; ++ps) O[db][qb] = MM::mma(vf[db][ps], pf[ps], O[db][qb]);
   }
+  if constexpr (!RAGGED && C::SCHED_ATT) {
+    // Issue order for the scheduler: S of block 0; then one MFMA (S of the next
+    // block, or P.V of the previous one) per slice of the softmax VALU work, so the
+    // wave keeps the matrix pipe fed while it computes exponentials; P.V of the
+    // last block at the end.
+    constexpr int NM = (2 * C::QB - 2) * C::KSTEPS;  // MFMAs that have softmax work beside them
+    constexpr int VPM = (C::QB * 48 + NM - 1) / NM;   // VALU instructions per such MFMA
+    // the next tile's operand loads first, so they have the whole tile to land
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * C::RUN_U4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, C::KSTEPS, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::PSTEPS, 0);
+  }
+}
+
+// ---------------------------------------------------------------- pipelined dense token loop
+// Iteration k of the loop over 32-token tiles issues three independent pieces of
+// work so that the matrix pipe and the VALU run side by side:
+//   O += V(k-1) P(k-1)          P.V of the previous tile            (MFMA)
+//   P(k) = exp2(S(k) scale - b)  softmax numerators of this tile     (VALU)
+//   S(k+1) = K(k+1) Q^T          logits of the next tile             (MFMA)
+// and the loads of K(k+2) and V(k). Before the first tile P(-1) = 0 and V(-1) = 0.
+
+template <typename C>
+__device__ __forceinline__ f32x16 s_block(const typename Mma<typename C::T>::frag (&kf)[C::KSTEPS],
+                                          const typename Mma<typename C::T>::frag (&q)[C::KSTEPS]) {
+  using MM = Mma<typename C::T>;
+  const f32x16 Z = {};
+  f32x16 S = MM::mma(kf[0], q[0], Z);
+#pragma unroll
+  for (int ks = 1; ks < C::KSTEPS; ++ks) S = MM::mma(kf[ks], q[ks], S);
+  return S;
+}
+
+// LAST: the final tile (no S of a next tile, no K load); RAGGED: it is partial.
+template <typename C, bool LAST, bool RAGGED>
+__device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], const uint4 (&v_prev)[C::RUN_U4],
+                                          uint4 (&k_load)[C::RUN_U4], uint4 (&v_load)[C::RUN_U4],
+                                          __amdgpu_buffer_rsrc_t Kg, __amdgpu_buffer_rsrc_t Vg,
+                                          int kt, int k_tile, int nkeys, int hw, int lane,
+                                          const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
+                                          const float (&nb)[C::QB], f32x16 (&S)[C::QB],
+                                          typename Mma<typename C::T>::frag (&P)[C::QB][C::PSTEPS],
+                                          f32x16 (&O)[2][C::QB], float (&l)[C::QB]) {
+  using T = typename C::T;
+  using MM = Mma<T>;
+  using Frag = typename MM::frag;
+  if constexpr (!LAST) load_run<C>(Kg, k_tile, hw, lane, k_load);
+  load_run<C>(Vg, kt, hw, lane, v_load);
+  Frag kf[C::KSTEPS], vf[2][C::PSTEPS];
+  as_frags<C>(k_next, v_prev, kf, vf);
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int ps = 0; ps < C::PSTEPS; ++ps) O[db][qb] = MM::mma(vf[db][ps], P[qb][ps], O[db][qb]);
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    Frag pn[C::PSTEPS];
+    softmax_block<T, RAGGED>(S[qb], nb[qb], l[qb], kt * C::KT, nkeys, lane, pn);
+    if constexpr (!LAST) S[qb] = s_block<C>(kf, qf[qb]);
+#pragma unroll
+    for (int ps = 0; ps < C::PSTEPS; ++ps) P[qb][ps] = pn[ps];
+  }
+  if constexpr (C::SCHED_ATT) {
+    // loads first; P.V of the previous tile beside the first softmax; S of the
+    // next tile beside the later ones
+    constexpr int NPV = 2 * C::PSTEPS * C::QB;
+    constexpr int NS = LAST ? 0 : C::KSTEPS * C::QB;
+    constexpr int NM = NPV + NS;
+    constexpr int VPM = (C::QB * 48 + NM - 1) / NM;
+    __builtin_amdgcn_sched_group_barrier(0x020, (LAST ? 1 : 2) * C::RUN_U4, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+    }
+  }
 }
 
 template <typename C, bool GATHER>
@@ -339,7 +433,8 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   using Frag = typename MM::frag;
   constexpr int KS = C::KSTEPS, PS = C::PSTEPS;
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int hw = wave % C::H, qg = wave / C::H;
   const int64_t nq = A.d_N ? (int64_t)*A.d_N : A.N;
   const int64_t n_tiles = A.items ? (A.d_n_items ? (int64_t)*A.d_n_items : A.n_tiles) : (nq + C::BQ - 1) / C::BQ;
@@ -415,37 +510,71 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     }
 
     if constexpr (!GATHER) {
-      // full 32-token tiles two at a time (ping-pong registers, one tile of
-      // prefetch), then the ragged tail tile, if any, with key masking
-      const int nfull = nkeys / C::KT;
-      uint4 ka[C::RUN_U4], va[C::RUN_U4], kb[C::RUN_U4], vb[C::RUN_U4];
-      load_run<C>(Kg, 0, hw, lane, ka);
-      load_run<C>(Vg, 0, hw, lane, va);
-      for (int kt = 0; kt < nfull; kt += 2) {
-        const int k1 = kt + 1 < nfull ? kt + 1 : kt;  // clamped: the last step reloads its own tile
-        load_run<C>(Kg, k1, hw, lane, kb);
-        load_run<C>(Vg, k1, hw, lane, vb);
-        {
-          Frag kf[KS], vf[2][PS];
-          as_frags<C>(ka, va, kf, vf);
-          tile_compute<C, false>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
-        }
-        if (kt + 1 < nfull) {
-          const int k2 = kt + 2 < nfull ? kt + 2 : kt + 1;
-          load_run<C>(Kg, k2, hw, lane, ka);
-          load_run<C>(Vg, k2, hw, lane, va);
-          Frag kf[KS], vf[2][PS];
-          as_frags<C>(kb, vb, kf, vf);
-          tile_compute<C, false>(kf, vf, qf, nb, O, l_run, kt + 1, nkeys, lane);
-        }
+      if (nkt == 0) goto attention_done;  // (no tokens: only reachable with M = 0, which the API rejects)
+      {
+      // Pipelined (see pipe_iter). Iteration k reads K(k+1) from kb[(k+1)&1] and
+      // V(k-1) from vb[(k+1)&1] and loads K(k+2) into kb[k&1], V(k) into vb[k&1];
+      // the loop runs the full iterations two at a time so buffers are static.
+      const int64_t packed_bytes = (int64_t)nkt * C::KT * C::D * C::SZ;
+      const __amdgpu_buffer_rsrc_t Kg = buffer_of(A.Kp, packed_bytes);
+      const __amdgpu_buffer_rsrc_t Vg = buffer_of(A.Vt, packed_bytes);
+      uint4 kb[2][C::RUN_U4], vb[2][C::RUN_U4];
+      f32x16 S[C::QB];
+      Frag P[C::QB][C::PSTEPS];
+#pragma unroll
+      for (int i = 0; i < C::RUN_U4; ++i) vb[1][i] = uint4{0, 0, 0, 0};
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+        for (int ps = 0; ps < C::PSTEPS; ++ps) P[qb][ps] = Frag{};
+      load_run<C>(Kg, 0, hw, lane, kb[0]);
+      load_run<C>(Kg, nkt > 1 ? 1 : 0, hw, lane, kb[1]);
+      {
+        Frag kf[KS], vf_unused[2][PS];
+        as_frags<C>(kb[0], vb[1], kf, vf_unused);
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) S[qb] = s_block<C>(kf, qf[qb]);
       }
-      if (nfull < nkt) {
-        load_run<C>(Kg, nfull, hw, lane, ka);
-        load_run<C>(Vg, nfull, hw, lane, va);
-        Frag kf[KS], vf[2][PS];
-        as_frags<C>(ka, va, kf, vf);
-        tile_compute<C, true>(kf, vf, qf, nb, O, l_run, nfull, nkeys, lane);
+      const bool ragged = nkeys % C::KT != 0;
+      int kt = 0;
+      for (; kt + 2 < nkt; kt += 2) {
+        pipe_iter<C, false, false>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, kt + 2, nkeys, hw, lane, qf, nb, S, P, O,
+                                   l_run);
+        const int k3 = kt + 3 < nkt ? kt + 3 : nkt - 1;
+        pipe_iter<C, false, false>(kb[0], vb[0], kb[1], vb[1], Kg, Vg, kt + 1, k3, nkeys, hw, lane, qf, nb, S, P, O,
+                                   l_run);
       }
+      if (kt + 1 < nkt) {  // one more full iteration (kt even)
+        pipe_iter<C, false, false>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, nkt - 1, nkeys, hw, lane, qf, nb, S, P, O,
+                                   l_run);
+        ++kt;
+      }
+      // the last tile: softmax (masked if partial) beside P.V of the previous one,
+      // then its own P.V
+      Frag vf_last[2][PS];
+      if (kt & 1) {
+        if (ragged)
+          pipe_iter<C, true, true>(kb[1], vb[0], kb[1], vb[1], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
+        else
+          pipe_iter<C, true, false>(kb[1], vb[0], kb[1], vb[1], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
+        Frag kf_unused[KS];
+        as_frags<C>(kb[0], vb[1], kf_unused, vf_last);
+      } else {
+        if (ragged)
+          pipe_iter<C, true, true>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
+        else
+          pipe_iter<C, true, false>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
+        Frag kf_unused[KS];
+        as_frags<C>(kb[0], vb[0], kf_unused, vf_last);
+      }
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int ps = 0; ps < PS; ++ps) O[db][qb] = MM::mma(vf_last[db][ps], P[qb][ps], O[db][qb]);
+      }
+    attention_done:;
     } else {
       uint4 rk[C::NCK], rv[C::NCK];
       tile_load<C, GATHER>(Kg, Vg, sel, nkeys, A.M, 0, tid, rk, rv);
@@ -488,52 +617,73 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     __syncthreads();
 
     // ---------------------------------------------------------------- a = Wo o  (kept in fp32 as y)
-    // this wave's epilogue tiles: weight row block rb0, column blocks cb0 .. cb0 + TPW - 1
-    const int rb0 = (wave * C::TPW) / C::CB, cb0 = (wave * C::TPW) % C::CB;
-    f32x16 Y[C::TPW];
+    // this wave's epilogue tiles: weight row blocks rb0 .. rb0 + RPW - 1, column
+    // blocks cb0 .. cb0 + CPW - 1
+    const int rb0 = C::TPW >= C::CB ? wave * C::RPW : (wave * C::TPW) / C::CB;
+    const int cb0 = C::TPW >= C::CB ? 0 : (wave * C::TPW) % C::CB;
+    f32x16 Y[C::RPW][C::CPW];
 #pragma unroll
-    for (int i = 0; i < C::TPW; ++i) Y[i] = zero16();
-    gemm_wrow<T, C::D / MM::KS, C::TPW>(Wo + (32 * rb0) * C::D, C::D, Ob, C::DPAD, cb0, Y, lane);
+    for (int r = 0; r < C::RPW; ++r)
+#pragma unroll
+      for (int i = 0; i < C::CPW; ++i) Y[r][i] = zero16();
+    gemm_rows<T, C::D / MM::KS, C::RPW, C::CPW>(Wo + (32 * rb0) * C::D, C::D, Ob, C::DPAD, cb0, Y, lane);
     T* Ab = reinterpret_cast<T*>(lds + C::ABUF);
 #pragma unroll
-    for (int i = 0; i < C::TPW; ++i) store_ct<T>(Ab + (32 * (cb0 + i)) * C::DPAD + 32 * rb0, C::DPAD, Y[i], lane);
+    for (int r = 0; r < C::RPW; ++r)
+#pragma unroll
+      for (int i = 0; i < C::CPW; ++i)
+        store_ct<T>(Ab + (32 * (cb0 + i)) * C::DPAD + 32 * (rb0 + r), C::DPAD, Y[r][i], lane);
     __syncthreads();
 
     // ---------------------------------------------------------------- y = a + W2 GELU(W1 a)
     T* Hb = reinterpret_cast<T*>(lds + C::OBUF);
-    const int rh0 = (wave * C::TPH) / C::CB, ch0 = (wave * C::TPH) % C::CB;
+    const int rh0 = C::TPH >= C::CB ? wave * C::RPH : (wave * C::TPH) / C::CB;
+    const int ch0 = C::TPH >= C::CB ? 0 : (wave * C::TPH) % C::CB;
     for (int f0 = 0; f0 < A.F; f0 += C::FC) {
-      f32x16 Hc[C::TPH];
+      f32x16 Hc[C::RPH][C::CPH];
 #pragma unroll
-      for (int j = 0; j < C::TPH; ++j) Hc[j] = zero16();
-      gemm_wrow<T, C::D / MM::KS, C::TPH>(W1 + (int64_t)(f0 + 32 * rh0) * C::D, C::D, Ab, C::DPAD, ch0, Hc, lane);
+      for (int r = 0; r < C::RPH; ++r)
 #pragma unroll
-      for (int j = 0; j < C::TPH; ++j) {
-        gelu_tile<C>(Hc[j], gtab);
-        store_ct<T>(Hb + (32 * (ch0 + j)) * C::HPAD + 32 * rh0, C::HPAD, Hc[j], lane);
-      }
+        for (int j = 0; j < C::CPH; ++j) Hc[r][j] = zero16();
+      gemm_rows<T, C::D / MM::KS, C::RPH, C::CPH>(W1 + (int64_t)(f0 + 32 * rh0) * C::D, C::D, Ab, C::DPAD, ch0, Hc,
+                                                  lane);
+#pragma unroll
+      for (int r = 0; r < C::RPH; ++r)
+#pragma unroll
+        for (int j = 0; j < C::CPH; ++j) {
+          gelu_tile<C>(Hc[r][j], gtab);
+          store_ct<T>(Hb + (32 * (ch0 + j)) * C::HPAD + 32 * (rh0 + r), C::HPAD, Hc[r][j], lane);
+        }
       __syncthreads();
-      gemm_wrow<T, C::FC / MM::KS, C::TPW>(W2 + (int64_t)(32 * rb0) * A.F + f0, A.F, Hb, C::HPAD, cb0, Y, lane);
+      gemm_rows<T, C::FC / MM::KS, C::RPW, C::CPW>(W2 + (int64_t)(32 * rb0) * A.F + f0, A.F, Hb, C::HPAD, cb0, Y,
+                                                   lane);
       __syncthreads();
     }
 
     // ---------------------------------------------------------------- net = w_head . y, SDF
     float* red = reinterpret_cast<float*>(lds + C::RED);
     {
-      float w[16];
+      float s[C::CPW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) w[r] = A.w_head[32 * rb0 + crow(r, lane)];
+      for (int i = 0; i < C::CPW; ++i) s[i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < C::TPW; ++i) {
-        float s = 0.f;
+      for (int r = 0; r < C::RPW; ++r) {
+        float w[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += w[r] * Y[i][r];
-        s += __shfl_xor(s, 32);
-        if (lane < 32) red[wave * C::BQ + 32 * (cb0 + i) + lane] = s;
+        for (int k = 0; k < 16; ++k) w[k] = A.w_head[32 * (rb0 + r) + crow(k, lane)];
+#pragma unroll
+        for (int i = 0; i < C::CPW; ++i)
+#pragma unroll
+          for (int k = 0; k < 16; ++k) s[i] += w[k] * Y[r][i][k];
+      }
+#pragma unroll
+      for (int i = 0; i < C::CPW; ++i) {
+        s[i] += __shfl_xor(s[i], 32);
+        if (lane < 32) red[wave * C::BQ + 32 * (cb0 + i) + lane] = s[i];
       }
       // column blocks this wave does not cover contribute zero
       for (int cb = 0; cb < C::CB; ++cb)
-        if ((cb < cb0 || cb >= cb0 + C::TPW) && lane < 32) red[wave * C::BQ + 32 * cb + lane] = 0.f;
+        if ((cb < cb0 || cb >= cb0 + C::CPW) && lane < 32) red[wave * C::BQ + 32 * cb + lane] = 0.f;
     }
     __syncthreads();
     for (int t = tid; t < C::BQ; t += C::NT) {
