@@ -63,6 +63,90 @@ def read_traffic():
         return None
 
 
+def mask_bytes(levels_stats, dilation):
+    """Algorithmic HBM bytes of each bookkeeping kernel of one hierarchical decode,
+    summed over levels (lower bounds: every byte a kernel must touch once)."""
+    b = dict(cell_test=0, dilate=0, mark=0, scan=0, emit=0, fill=0)
+    nb8 = lambda p: (p + 7) // 8
+    n = len(levels_stats)
+    for L, st in enumerate(levels_stats):
+        R = st["R"]
+        P = R + 1
+        b["cell_test"] += R ** 3 / 8 + (0 if L == 0 else (R // 2) ** 3 / 8) + 4 * max(st["tested"], st["queries"])
+        if L == n - 1:
+            break
+        Rn = 2 * R
+        Pn, NBn = Rn + 1, nb8(Rn + 1)
+        nx = levels_stats[L + 1]
+        b["dilate"] += dilation * 2 * R ** 3 / 8
+        b["mark"] += R ** 3 / 8 + (P ** 3 / 8 if L else 0) + 2 * Pn ** 3 / 8 + 4 * NBn ** 3
+        b["scan"] += 24 * NBn ** 3
+        b["emit"] += 20 * NBn ** 3 + Pn ** 3 / 8 + 4 * nx["queries"] + 16 * nx["items"] + 4 * nx["blocks"]
+        b["fill"] += 4 * P ** 3 + 4 * Pn ** 3
+    return b
+
+
+def mask_stress(steps: int):
+    """Bandwidth of the hierarchical bookkeeping kernels: the 75 -> 300 workload and
+    a scaled one (150 -> 300 -> 600, a 601^3 volume), warm and after a 1 GiB write
+    that evicts the caches (cold). One JSON line."""
+    import numpy as np
+    import torch
+
+    import shape_vae_decoding_amd as V
+    import vdm_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.make(1)
+    wt = {k: torch.from_numpy(v).to(dev) for k, v in w.weights.items()}
+    wt = {k: (v if k == "w_head" else v.to(torch.bfloat16)) for k, v in wt.items()}
+    dec = V.Decoder(wt, w.prims, w.net_scale)
+    Z = torch.from_numpy(w.Z).to(dev).to(torch.bfloat16)
+    K, Vv = torch.empty_like(Z), torch.empty_like(Z)
+    V.vdm_project_kv(dec, Z, K, Vv)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    kinds = ["cell_test", "dilate", "mark", "scan", "emit", "fill"]
+    out = {"metric": "hierarchical bookkeeping kernels: achieved HBM GB/s (algorithmic bytes / kernel time)",
+           "peak_hbm_gbs": PEAK_HBM_GBS, "workloads": {}}
+    for name, R0, tau in [("75->150->300", 75, float(np.float32(4 / 300))),
+                          ("150->300->600", 150, float(np.float32(4 / 600)))]:
+        p = V.hier_params(R0=R0, levels=3, tau=tau, dilation=1)
+        Pf = (R0 << 2) + 1
+        vol = torch.empty(Pf ** 3, dtype=torch.float32, device=dev)
+        st = torch.zeros(3 * V.STAT_FIELDS, dtype=torch.int64, device=dev)
+        ws = V.workspace(V.vdm_hier_workspace_size(dec, p, w.M), dev)
+        V.vdm_decode_hier(dec, p, K, Vv, vol, st, ws=ws)
+        torch.cuda.synchronize()
+        levels = V.stats_dict(st, 3)
+        alg = mask_bytes(levels, 1)
+        res = {"levels": levels}
+        for mode in ["warm", "cold"]:
+            V.vdm_timing(2)
+            for _ in range(steps):
+                if mode == "cold":
+                    flush.fill_(1.0)
+                V.vdm_timing(1)
+                V.vdm_decode_hier(dec, p, K, Vv, vol, st, ws=ws)
+                V.vdm_timing(0)
+            torch.cuda.synchronize()
+            per = {}
+            for kd in kinds:
+                n, ms = V.vdm_timing_read(kd)
+                t = ms / steps
+                gbs = alg[kd] / (t / 1e3) / 1e9 if t > 0 else None
+                per[kd] = {"launches_per_volume": n // steps, "ms_per_volume": round(t, 4),
+                           "algorithmic_MB": round(alg[kd] / 1e6, 3),
+                           "GB_per_s": round(gbs, 1) if gbs else None,
+                           "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4) if gbs else None}
+            res[mode] = per
+            V.vdm_timing(2)
+        out["workloads"][name] = res
+        del vol, ws
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -107,7 +191,13 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, copy 512 MiB device-to-device 3 times (a known-size kernel for "
                          "calibrating the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--mask-stress", action="store_true",
+                    help="instead of the step: bandwidth of the hierarchical bookkeeping kernels (75->300 and "
+                         "150->600), one JSON line")
     args = ap.parse_args()
+    if args.mask_stress:
+        mask_stress(max(args.steps // 4, 3))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decoder path here has no "
               f"multi-GPU part (queries would shard by independent z-slabs with K/V replicated per GPU)", file=sys.stderr)

@@ -244,8 +244,13 @@ enum {
   VDM_TIME_SELECT,          /* probe scoring, top-k and union (vdm_select_kv, hierarchical levels) */
   VDM_TIME_EMBED,           /* vdm_embed_queries */
   VDM_TIME_PROJECT_KV,      /* vdm_project_kv */
-  VDM_TIME_MASKS,           /* per-level bookkeeping of vdm_decode_hier: cell test, dilation,
-                               child marking, scan, list emission, ancestor fill */
+  /* per-level bookkeeping of vdm_decode_hier: */
+  VDM_TIME_CELL_TEST,       /* sign-change / band test of the tested cells */
+  VDM_TIME_DILATE,          /* 3x3x3 dilation of the active cells */
+  VDM_TIME_MARK,            /* candidate points of the next level, minus computed ones */
+  VDM_TIME_SCAN,            /* prefix sums of per-block counts (three launches per level) */
+  VDM_TIME_EMIT,            /* query list, work items and occupied blocks */
+  VDM_TIME_FILL,            /* nearest-ancestor fill of the next level's volume */
   VDM_TIME_KINDS
 };
 

@@ -35,7 +35,8 @@ EXPORTS = [
     "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_timing",
     "vdm_timing_read", "vdm_version", "vdm_last_error",
 ]
-TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "masks"]
+TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "cell_test", "dilate", "mark", "scan",
+              "emit", "fill"]
 
 
 class VdmError(RuntimeError):

@@ -58,57 +58,125 @@ hipError_t launch_stats_init(int64_t* stats, int levels, int R0, hipStream_t s) 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ counters
+// Per-workgroup counts are added to STAT_SLOTS spread-out partial counters (slot =
+// workgroup id mod STAT_SLOTS, 64 bytes apart) rather than to one address that
+// every workgroup would contend for; fold_kernel then adds the slots into the
+// level's stats and clears them for the next use.
+constexpr int STAT_SLOTS = 256;
+
+__global__ __launch_bounds__(STAT_SLOTS) void fold_kernel(int64_t* part, int f0, int nf, int64_t* dst0, int64_t* dst1) {
+  __shared__ int64_t red[STAT_SLOTS / 64];
+  const int t = threadIdx.x;
+  for (int f = 0; f < nf; ++f) {
+    const int64_t v = part[t * 8 + f0 + f];
+    part[t * 8 + f0 + f] = 0;
+    const int64_t sum = block_sum_i64(v, red, t, STAT_SLOTS);
+    if (t == 0) *(f == 0 ? dst0 : dst1) += sum;
+  }
+}
+
+static hipError_t launch_fold(int64_t* part, int f0, int nf, int64_t* dst0, int64_t* dst1, hipStream_t s) {
+  hipLaunchKernelGGL(fold_kernel, dim3(1), dim3(STAT_SLOTS), 0, s, part, f0, nf, dst0, dst1);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ cell test
 // Cell (i, j, k) of level L (R cells per axis) is tested when all 8 corners were
 // computed: every cell at level 0, the children of kept parents afterwards
 // (kept_prev = the previous level's kept cells; null at level 0). A tested cell
 // is active when its corner values include s < 0 and s >= 0, or min |s| < tau.
+// One workgroup per 2x2x2 group of 8x8x8 cell blocks (the children of one parent
+// block): the parent block's 8 words are read once, and a cell block none of whose
+// parents was kept (most of them above level 0) only writes its zero words.
+// For a tested block the 9x9x9 corner points are staged in LDS, each read once.
 __global__ __launch_bounds__(512) void cell_test_kernel(const float* __restrict__ vol, int R, int NB,
                                                         const uint64_t* __restrict__ kept_prev, int NBp,
-                                                        float tau, uint64_t* __restrict__ active,
-                                                        int64_t* stat_tested, int64_t* stat_active) {
-  __shared__ int64_t red[8];
-  const int64_t b = blockIdx.x;
-  const int bi = (int)(b / ((int64_t)NB * NB)), bj = (int)((b / NB) % NB), bk = (int)(b % NB);
+                                                        float tau, uint64_t* __restrict__ active, int64_t* part) {
+  __shared__ float cv[9 * 9 * 9];
+  __shared__ int cnt[2][8];
+  const int NG = (NB + 1) / 2;
+  const int64_t g = blockIdx.x;
+  const int gi = (int)(g / ((int64_t)NG * NG)), gj = (int)((g / NG) % NG), gk = (int)(g % NG);
   const int ii = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i = 8 * bi + ii, j = 8 * bj + (lane >> 3), k = 8 * bk + (lane & 7);
-  bool tested = i < R && j < R && k < R;
-  if (tested && kept_prev) tested = mask_bit(kept_prev, NBp, i >> 1, j >> 1, k >> 1);
-  bool act = false;
-  if (tested) {
-    const int64_t P = R + 1;
-    const float* v = vol + ((int64_t)i * P + j) * P + k;
-    bool neg = false, nonneg = false;
-    float mn = __builtin_inff();
+  uint64_t pw[8];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+  for (int r = 0; r < 8; ++r)
+    pw[r] = kept_prev ? kept_prev[(((int64_t)gi * NBp + gj) * NBp + gk) * 8 + r] : ~0ull;
+  int nt_w = 0, na_w = 0;  // this wave's counts (lane 0)
+  const int64_t P = R + 1;
+  for (int c = 0; c < 8; ++c) {
+    const int bi = 2 * gi + (c >> 2), bj = 2 * gj + ((c >> 1) & 1), bk = 2 * gk + (c & 1);
+    if (bi >= NB || bj >= NB || bk >= NB) continue;
+    const int64_t b = ((int64_t)bi * NB + bj) * NB + bk;
+    // parents of this block: rows 4(c>>2) .. +3 of the parent block, the 4x4 square
+    // (4bj .. 4bj+3) x (4bk .. 4bk+3) of each row's word
+    const uint64_t sq = 0x0f0f0f0full << (((4 * bj) & 7) * 8 + ((4 * bk) & 7));
+    const int r0 = 4 * (c >> 2);
+    if (((pw[r0] | pw[r0 + 1] | pw[r0 + 2] | pw[r0 + 3]) & sq) == 0ull) {  // uniform
+      if (lane == 0) active[b * 8 + ii] = 0ull;
+      continue;
+    }
+    for (int t = threadIdx.x; t < 9 * 9 * 9; t += 512) {
+      const int ci = t / 81, cj = (t / 9) % 9, ck = t % 9;
+      const int I = 8 * bi + ci, J = 8 * bj + cj, K = 8 * bk + ck;
+      cv[t] = (I <= R && J <= R && K <= R) ? vol[((int64_t)I * P + J) * P + K] : 0.f;
+    }
+    __syncthreads();
+    const int i = 8 * bi + ii, j = 8 * bj + (lane >> 3), k = 8 * bk + (lane & 7);
+    bool tested = i < R && j < R && k < R;
+    if (tested && kept_prev) tested = mask_bit(kept_prev, NBp, i >> 1, j >> 1, k >> 1);
+    bool act = false;
+    if (tested) {
+      const float* v = cv + (ii * 9 + (lane >> 3)) * 9 + (lane & 7);
+      bool neg = false, nonneg = false;
+      float mn = __builtin_inff();
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const float s = v[(a * P + c) * P + d];
-          neg |= s < 0.f;
-          nonneg |= s >= 0.f;
-          mn = fminf(mn, fabsf(s));
-        }
-    act = (neg && nonneg) || mn < tau;
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const float sv = v[(a * 9 + cc) * 9 + d];
+            neg |= sv < 0.f;
+            nonneg |= sv >= 0.f;
+            mn = fminf(mn, fabsf(sv));
+          }
+      act = (neg && nonneg) || mn < tau;
+    }
+    const uint64_t tw = __ballot(tested), aw = __ballot(act);
+    if (lane == 0) {
+      active[b * 8 + ii] = aw;
+      nt_w += __popcll(tw);
+      na_w += __popcll(aw);
+    }
+    __syncthreads();  // cv is reused by the next block
   }
-  const uint64_t word = __ballot(act);
-  if (lane == 0) active[b * 8 + ii] = word;
-  const int64_t nt = block_sum_i64(tested ? 1 : 0, red, threadIdx.x, 512);
-  const int64_t na = block_sum_i64(act ? 1 : 0, red, threadIdx.x, 512);
+  if (lane == 0) {
+    cnt[0][ii] = nt_w;
+    cnt[1][ii] = na_w;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    if (nt) atomicAdd((unsigned long long*)stat_tested, (unsigned long long)nt);
-    if (na) atomicAdd((unsigned long long*)stat_active, (unsigned long long)na);
+    int nt = 0, na = 0;
+    for (int w = 0; w < 8; ++w) {
+      nt += cnt[0][w];
+      na += cnt[1][w];
+    }
+    int64_t* slot = part + (g % STAT_SLOTS) * 8;
+    if (nt) atomicAdd((unsigned long long*)slot, (unsigned long long)nt);
+    if (na) atomicAdd((unsigned long long*)(slot + 1), (unsigned long long)na);
   }
 }
 
 hipError_t launch_cell_test(const float* vol, int R, const uint64_t* kept_prev, float tau, uint64_t* active,
-                            int64_t* stat_tested, int64_t* stat_active, hipStream_t s) {
-  const int NB = nblocks8(R + 1), NBp = nblocks8(R / 2 + 1);
-  hipLaunchKernelGGL(cell_test_kernel, dim3((unsigned)((int64_t)NB * NB * NB)), dim3(512), 0, s, vol, R, NB,
-                     kept_prev, NBp, tau, active, stat_tested, stat_active);
-  return hipGetLastError();
+                            int64_t* part, int64_t* stat_tested, int64_t* stat_active, hipStream_t s) {
+  const int NB = nblocks8(R + 1), NBp = nblocks8(R / 2 + 1), NG = (NB + 1) / 2;
+  hipLaunchKernelGGL(cell_test_kernel, dim3((unsigned)((int64_t)NG * NG * NG)), dim3(512), 0, s, vol, R, NB,
+                     kept_prev, NBp, tau, active, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_fold(part, 0, 2, stat_tested, stat_active, s);
 }
 
 // ------------------------------------------------------------------ dilation
@@ -124,7 +192,7 @@ __device__ __forceinline__ uint64_t dil_j(uint64_t t, uint64_t td, uint64_t tu) 
 }
 
 __global__ void dilate_kernel(const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int R, int NB,
-                              int identity, int64_t* stat) {
+                              int identity, int64_t* part) {
   __shared__ int64_t red[4];
   const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nw = (int64_t)NB * NB * NB * 8;
@@ -166,83 +234,139 @@ __global__ void dilate_kernel(const uint64_t* __restrict__ in, uint64_t* __restr
     }
     out[w] = res;
   }
-  if (stat) {
+  if (part) {
     const int64_t n = block_sum_i64(__popcll(res), red, threadIdx.x, 256);
-    if (threadIdx.x == 0 && n) atomicAdd((unsigned long long*)stat, (unsigned long long)n);
+    if (threadIdx.x == 0 && n) atomicAdd((unsigned long long*)(part + (blockIdx.x % STAT_SLOTS) * 8 + 2), (unsigned long long)n);
   }
 }
 
-hipError_t launch_dilate(const uint64_t* in, uint64_t* out, int R, int identity, int64_t* stat, hipStream_t s) {
+hipError_t launch_dilate(const uint64_t* in, uint64_t* out, int R, int identity, int64_t* part, int64_t* stat,
+                         hipStream_t s) {
   const int NB = nblocks8(R + 1);
   const int64_t nw = (int64_t)NB * NB * NB * 8;
   hipLaunchKernelGGL(dilate_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, in, out, R, NB, identity,
-                     stat);
-  return hipGetLastError();
+                     stat ? part : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !stat) return e;
+  return launch_fold(part, 2, 1, stat, stat, s);
 }
 
 // ------------------------------------------------------------------ child marking
 // Point (I, J, K) of level L+1 (Rn = 2R cells) is a candidate when it is a corner
-// of a child of a kept level-L cell: per axis, even I has parents I/2 - 1 and I/2,
-// odd I has parent (I-1)/2. It is new when it was not computed before: a point
+// of a child of a kept level-L cell: per axis, even X has parents X/2 - 1 and X/2,
+// odd X has parent (X-1)/2. It is new when it was not computed before: a point
 // with all-even indices was computed iff its level-L point (I/2, J/2, K/2) was
 // (every point at level 0). all_new: every in-range point is new (level 0 list).
-__global__ __launch_bounds__(512) void mark_kernel(const uint64_t* __restrict__ kept, int R,
+//
+// Bit-parallel: one thread per output word (the 8x8 (J, K) square of one I). For
+// a parent row a, the parent cells c = 4bj-1 .. 4bj+3, d = 4bk-1 .. 4bk+3 form a
+// 5x5 window (up to 4 words); "upsampling" it per axis with the parent rule gives
+// the candidate bits of the whole word.
+
+// 5-bit window (parents d = 4bk-1 .. 4bk+3 as bits 0..4) -> the 8 points K = 8bk .. 8bk+7:
+// odd K = 8bk+2m+1 has parent bit m+1, even K = 8bk+2m has parent bits m and m+1.
+__device__ __forceinline__ uint32_t up8(uint32_t w5) {
+  const uint32_t s = ((w5 >> 1) & 1u) << 1 | ((w5 >> 2) & 1u) << 3 | ((w5 >> 3) & 1u) << 5 | ((w5 >> 4) & 1u) << 7;
+  return (s | (((s >> 1) | (s << 1) | (w5 & 1u)) & 0x55u)) & 0xffu;
+}
+
+// Candidate word of level L+1 from kept parent row a (cells of level L; R cells, NB blocks).
+__device__ __forceinline__ uint64_t cand_from_row(const uint64_t* __restrict__ kept, int NB, int R, int a, int bj,
+                                                  int bk) {
+  if (a < 0 || a >= R) return 0ull;
+  const int Cm = bj >> 1, Ch = (4 * bj - 1) >> 3, Dm = bk >> 1, Dh = (4 * bk - 1) >> 3;
+  auto ld = [&](int C, int Dd) -> uint64_t {
+    return (C >= 0 && C < NB && Dd >= 0 && Dd < NB) ? kept[(((int64_t)(a >> 3) * NB + C) * NB + Dd) * 8 + (a & 7)]
+                                                    : 0ull;
+  };
+  const uint64_t Wmm = ld(Cm, Dm), Wmh = bk > 0 ? ld(Cm, Dh) : 0ull;
+  const uint64_t Whm = bj > 0 ? ld(Ch, Dm) : 0ull, Whh = (bj > 0 && bk > 0) ? ld(Ch, Dh) : 0ull;
+  uint32_t row[5];
+#pragma unroll
+  for (int r = 0; r < 5; ++r) {
+    const int c = 4 * bj - 1 + r;
+    const bool main_blk = (c >> 3) == Cm;
+    const uint64_t wm = main_blk ? Wmm : Whm, wh = main_blk ? Wmh : Whh;
+    const uint32_t lo = (uint32_t)((wm >> (((c & 7) << 3) + ((4 * bk) & 7))) & 0xfull) << 1;
+    const uint32_t hb = bk > 0 ? (uint32_t)((wh >> (((c & 7) << 3) + ((4 * bk - 1) & 7))) & 1ull) : 0u;
+    row[r] = (c >= 0 && c < R) ? (lo | hb) : 0u;
+  }
+  // the same rule along J on byte rows
+  uint64_t U = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) U |= (uint64_t)up8(row[m + 1]) << (8 * (2 * m + 1));
+  return U | (((U >> 8) | (U << 8) | (uint64_t)up8(row[0])) & 0x00ff00ff00ff00ffull);
+}
+
+__global__ __launch_bounds__(256) void mark_kernel(const uint64_t* __restrict__ kept, int R,
                                                    const uint64_t* __restrict__ comp_prev, int all_new,
                                                    int Rn, uint64_t* __restrict__ newmask,
                                                    uint64_t* __restrict__ comp_next, int32_t* __restrict__ counts) {
-  __shared__ int cnt[8];
   const int NBn = nblocks8(Rn + 1), NB = nblocks8(R + 1);
-  const int64_t b = blockIdx.x;
-  const int bi = (int)(b / ((int64_t)NBn * NBn)), bj = (int)((b / NBn) % NBn), bk = (int)(b % NBn);
-  const int ii = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int I = 8 * bi + ii, J = 8 * bj + (lane >> 3), K = 8 * bk + (lane & 7);
-  const bool in = I <= Rn && J <= Rn && K <= Rn;
-  bool isnew = false, prev = false;
-  if (in) {
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nw = (int64_t)NBn * NBn * NBn * 8;
+  uint64_t wn = 0ull;
+  if (w < nw) {
+    const int64_t b = w >> 3;
+    const int ii = (int)(w & 7);
+    const int bi = (int)(b / ((int64_t)NBn * NBn)), bj = (int)((b / NBn) % NBn), bk = (int)(b % NBn);
+    const int I = 8 * bi + ii;
+    // points inside [0, Rn]^3
+    const int nj = min(max(Rn + 1 - 8 * bj, 0), 8), nk = min(max(Rn + 1 - 8 * bk, 0), 8);
+    const uint64_t rowm = nk >= 8 ? 0xffull : ((1ull << nk) - 1ull);
+    uint64_t inr = 0ull;
+    for (int jj = 0; jj < nj; ++jj) inr |= rowm << (8 * jj);
+    if (I > Rn) inr = 0ull;
+    uint64_t wp = 0ull;
     if (all_new) {
-      isnew = true;
+      wn = inr;
     } else {
-      if (((I | J | K) & 1) == 0) prev = comp_prev ? mask_bit(comp_prev, NB, I >> 1, J >> 1, K >> 1) : true;
-      if (!prev) {
-        // parents along an axis: odd X -> X/2 only; even X -> X/2 - 1 and X/2
-        const int i1 = I >> 1, i0 = (I & 1) ? i1 : i1 - 1;
-        const int j1 = J >> 1, j0 = (J & 1) ? j1 : j1 - 1;
-        const int k1 = K >> 1, k0 = (K & 1) ? k1 : k1 - 1;
-        bool cand = false;
-        for (int a = max(i0, 0); a <= min(i1, R - 1) && !cand; ++a)
-          for (int c = max(j0, 0); c <= min(j1, R - 1) && !cand; ++c)
-            for (int d = max(k0, 0); d <= min(k1, R - 1) && !cand; ++d) cand = mask_bit(kept, NB, a, c, d);
-        isnew = cand;
+      // computed before: all-even points whose level-L point was computed
+      if ((I & 1) == 0) {
+        if (comp_prev) {
+          const int i2 = I >> 1;
+          const uint64_t pw =
+              comp_prev[(((int64_t)(i2 >> 3) * NB + (bj >> 1)) * NB + (bk >> 1)) * 8 + (i2 & 7)];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t q = (uint32_t)((pw >> ((((4 * bj) & 7) + r) * 8 + ((4 * bk) & 7))) & 0xfull);
+            const uint32_t e = (q & 1u) | (q & 2u) << 1 | (q & 4u) << 2 | (q & 8u) << 3;
+            wp |= (uint64_t)e << (16 * r);
+          }
+        } else {
+          wp = 0x0055005500550055ull;
+        }
       }
+      wp &= inr;
+      uint64_t cand = cand_from_row(kept, NB, R, (I & 1) ? (I - 1) >> 1 : (I >> 1) - 1, bj, bk);
+      if ((I & 1) == 0) cand |= cand_from_row(kept, NB, R, I >> 1, bj, bk);
+      wn = cand & ~wp & inr;
     }
+    newmask[w] = wn;
+    if (comp_next) comp_next[w] = wn | wp;
   }
-  const uint64_t wn = __ballot(isnew);
-  const uint64_t wp = __ballot(prev);
-  if (lane == 0) {
-    newmask[b * 8 + ii] = wn;
-    if (comp_next) comp_next[b * 8 + ii] = wn | wp;
-    cnt[ii] = __popcll(wn);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int c = 0;
-    for (int w = 0; w < 8; ++w) c += cnt[w];
-    counts[b] = c;
-  }
+  // per-block count: the 8 words of a block are 8 consecutive lanes
+  int c = __popcll(wn);
+  c += __shfl_xor(c, 1);
+  c += __shfl_xor(c, 2);
+  c += __shfl_xor(c, 4);
+  if (w < nw && (w & 7) == 0) counts[w >> 3] = c;
 }
 
 hipError_t launch_mark(const uint64_t* kept, int R, const uint64_t* comp_prev, int all_new, int Rn,
                        uint64_t* newmask, uint64_t* comp_next, int32_t* counts, hipStream_t s) {
   const int NBn = nblocks8(Rn + 1);
-  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((int64_t)NBn * NBn * NBn)), dim3(512), 0, s, kept, R, comp_prev,
-                     all_new, Rn, newmask, comp_next, counts);
+  const int64_t nw = (int64_t)NBn * NBn * NBn * 8;
+  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, kept, R, comp_prev, all_new,
+                     Rn, newmask, comp_next, counts);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ scan of per-block counts
 // For each block: queries q = counts[b], work items ceil(q / bq), occupied (q > 0).
 // Exclusive prefix sums give each block's offsets in the list, the item array and
-// the occupied-block array; totals go to tot[0..2] and to the level's stats.
+// the occupied-block array (which the last pass fills); totals go to tot[0..2]
+// and to the level's stats.
 constexpr int SCAN_NT = 256;
 constexpr int SCAN_PER = 8;
 constexpr int SCAN_CHUNK = SCAN_NT * SCAN_PER;
@@ -300,7 +424,7 @@ __global__ __launch_bounds__(SCAN_NT) void scan_top_kernel(int4* partial, int np
 }
 
 __global__ __launch_bounds__(SCAN_NT) void scan_apply_kernel(const int32_t* counts, int64_t n, int bq,
-                                                             const int4* partial, int4* offs) {
+                                                             const int4* partial, int4* offs, int32_t* occ) {
   __shared__ int4 sh[SCAN_NT];
   const int64_t base = (int64_t)blockIdx.x * SCAN_CHUNK + threadIdx.x * SCAN_PER;
   int4 v[SCAN_PER];
@@ -312,80 +436,119 @@ __global__ __launch_bounds__(SCAN_NT) void scan_apply_kernel(const int32_t* coun
   int4 tot;
   int4 run = add4(block_excl_scan(s, sh, threadIdx.x, &tot), partial[blockIdx.x]);
   for (int e = 0; e < SCAN_PER; ++e) {
-    if (base + e < n) offs[base + e] = run;
+    if (base + e < n) {
+      offs[base + e] = run;
+      if (v[e].z) occ[run.z] = (int32_t)(base + e);  // occupied blocks in block order
+    }
     run = add4(run, v[e]);
   }
 }
 
-hipError_t launch_scan(const int32_t* counts, int64_t n, int bq, int4* partial, int4* offs, int32_t* tot,
+hipError_t launch_scan(const int32_t* counts, int64_t n, int bq, int4* partial, int4* offs, int32_t* occ, int32_t* tot,
                        int64_t* stats_level, hipStream_t s) {
   const int np = (int)((n + SCAN_CHUNK - 1) / SCAN_CHUNK);
   hipLaunchKernelGGL(scan_reduce_kernel, dim3(np), dim3(SCAN_NT), 0, s, counts, n, bq, partial);
   hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(SCAN_NT), 0, s, partial, np, tot, stats_level);
-  hipLaunchKernelGGL(scan_apply_kernel, dim3(np), dim3(SCAN_NT), 0, s, counts, n, bq, (const int4*)partial, offs);
+  hipLaunchKernelGGL(scan_apply_kernel, dim3(np), dim3(SCAN_NT), 0, s, counts, n, bq, (const int4*)partial, offs,
+                     occ);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ emit lists
-// Block b writes its new points (row-major linear indices, in-block row-major
-// order) at its list offset, its work items (query chunks of at most bq, all
-// attending to occupied-block row occ) and its id in the occupied-block array.
-__global__ __launch_bounds__(512) void emit_kernel(const uint64_t* __restrict__ newmask, const int32_t* __restrict__ counts,
-                                                   const int4* __restrict__ offs, int Rn, int bq,
-                                                   int32_t* __restrict__ list, Item* __restrict__ items,
-                                                   int32_t* __restrict__ occ) {
-  __shared__ int pre[8];
-  const int64_t b = blockIdx.x;
-  const int c = counts[b];
-  if (c == 0) return;
+// One wave per occupied block (occ[0 .. tot[2]), grid-strided): the block writes
+// its new points (row-major linear indices, in-block row-major order) at its list
+// offset and its work items (query chunks of at most bq, all attending to
+// occupied-block row offs.z).
+constexpr int EMIT_NT = 256;
+
+__global__ __launch_bounds__(EMIT_NT) void emit_kernel(const uint64_t* __restrict__ newmask,
+                                                       const int32_t* __restrict__ counts,
+                                                       const int4* __restrict__ offs, const int32_t* __restrict__ occ,
+                                                       const int32_t* __restrict__ tot, int Rn, int bq,
+                                                       int32_t* __restrict__ list, Item* __restrict__ items) {
   const int NB = nblocks8(Rn + 1);
-  const int ii = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint64_t w = newmask[b * 8 + ii];
-  if (lane == 0) pre[ii] = __popcll(w);
-  __syncthreads();
-  int before = 0;
-  for (int x = 0; x < ii; ++x) before += pre[x];
-  const int4 o = offs[b];
-  if ((w >> lane) & 1ull) {
-    const int rank = before + __popcll(w & ((1ull << lane) - 1ull));
+  const int64_t P = Rn + 1;
+  const int lane = threadIdx.x & 63;
+  const int nocc = tot[2];
+  const int wpb = EMIT_NT / 64;
+  for (int o = blockIdx.x * wpb + (threadIdx.x >> 6); o < nocc; o += gridDim.x * wpb) {
+    const int64_t b = occ[o];
+    const int c = counts[b];
+    const int4 of = offs[b];
     const int bi = (int)(b / ((int64_t)NB * NB)), bj = (int)((b / NB) % NB), bk = (int)(b % NB);
-    const int64_t P = Rn + 1;
-    const int I = 8 * bi + ii, J = 8 * bj + (lane >> 3), K = 8 * bk + (lane & 7);
-    list[o.x + rank] = (int32_t)(((int64_t)I * P + J) * P + K);
+    const int J = 8 * bj + (lane >> 3), K = 8 * bk + (lane & 7);
+    int before = 0;
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const uint64_t w = newmask[b * 8 + ii];
+      if ((w >> lane) & 1ull) {
+        const int rank = before + __popcll(w & ((1ull << lane) - 1ull));
+        list[of.x + rank] = (int32_t)(((int64_t)(8 * bi + ii) * P + J) * P + K);
+      }
+      before += __popcll(w);
+    }
+    const int nchunks = (c + bq - 1) / bq;
+    for (int ch = lane; ch < nchunks; ch += 64) {
+      const int q0 = of.x + ch * bq;
+      items[of.y + ch] = Item{q0, min(q0 + bq, of.x + c), of.z, 0};
+    }
   }
-  const int nchunks = (c + bq - 1) / bq;
-  if ((int)threadIdx.x < nchunks) {
-    const int q0 = o.x + threadIdx.x * bq;
-    items[o.y + threadIdx.x] = Item{q0, min(q0 + bq, o.x + c), o.z, 0};
-  }
-  if (threadIdx.x == 0) occ[o.z] = (int32_t)b;
 }
 
-hipError_t launch_emit(const uint64_t* newmask, const int32_t* counts, const int4* offs, int Rn, int bq,
-                       int32_t* list, Item* items, int32_t* occ, hipStream_t s) {
+hipError_t launch_emit(const uint64_t* newmask, const int32_t* counts, const int4* offs, const int32_t* occ,
+                       const int32_t* tot, int Rn, int bq, int32_t* list, Item* items, hipStream_t s) {
   const int NB = nblocks8(Rn + 1);
-  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)((int64_t)NB * NB * NB)), dim3(512), 0, s, newmask, counts, offs, Rn,
-                     bq, list, items, occ);
+  const int64_t nb3 = (int64_t)NB * NB * NB;
+  int64_t g = (nb3 + EMIT_NT / 64 - 1) / (EMIT_NT / 64);
+  const int64_t cap = (int64_t)dev_info().cus * 8;
+  if (g > cap) g = cap;
+  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)g), dim3(EMIT_NT), 0, s, newmask, counts, offs, occ, tot, Rn, bq, list,
+                     items);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ nearest-ancestor fill
 // vol_next[I][J][K] = vol_prev[I/2][J/2][K/2] (integer division) for every point.
-__global__ void fill_kernel(const float* __restrict__ prev, int Pp, float* __restrict__ next, int Pn) {
-  const int64_t n = (int64_t)Pn * Pn * Pn;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
-    const int I = (int)(t / ((int64_t)Pn * Pn));
-    const int64_t r = t - (int64_t)I * Pn * Pn;
-    const int J = (int)(r / Pn), K = (int)(r - (int64_t)J * Pn);
-    next[t] = prev[((int64_t)(I >> 1) * Pp + (J >> 1)) * Pp + (K >> 1)];
+// One workgroup per 8 consecutive rows (I, J0 .. J0+7), J0 even: rows 2m and 2m+1
+// share source row J0/2 + m. Each thread loads all its source values first (up
+// to 4 rows x FILL_KI positions in flight), then stores them; threads run along K,
+// so every row is one contiguous store stream.
+constexpr int FILL_ROWS = 8;
+constexpr int FILL_NT = 256;
+constexpr int FILL_KI = 5;  // FILL_NT * FILL_KI >= 1201 points per row (finest grid at most 1200 cells)
+
+__global__ __launch_bounds__(FILL_NT) void fill_kernel(const float* __restrict__ prev, int Pp, float* __restrict__ next,
+                                                       int Pn) {
+  const int ng = (Pn + FILL_ROWS - 1) / FILL_ROWS;
+  const int I = blockIdx.x / ng, J0 = (blockIdx.x % ng) * FILL_ROWS;
+  float v[FILL_ROWS / 2][FILL_KI];
+#pragma unroll
+  for (int m = 0; m < FILL_ROWS / 2; ++m) {
+    const float* __restrict__ src = prev + ((int64_t)(I >> 1) * Pp + ((J0 >> 1) + m)) * Pp;
+    const bool row_ok = J0 + 2 * m < Pn;
+#pragma unroll
+    for (int t = 0; t < FILL_KI; ++t) {
+      const int K = threadIdx.x + FILL_NT * t;
+      v[m][t] = (row_ok && K < Pn) ? src[K >> 1] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < FILL_ROWS; ++r) {
+    const int J = J0 + r;
+    if (J >= Pn) break;
+    float* __restrict__ dst = next + ((int64_t)I * Pn + J) * Pn;
+#pragma unroll
+    for (int t = 0; t < FILL_KI; ++t) {
+      const int K = threadIdx.x + FILL_NT * t;
+      if (K < Pn) dst[K] = v[r >> 1][t];
+    }
   }
 }
 
 hipError_t launch_fill(const float* prev, int Pp, float* next, int Pn, hipStream_t s) {
-  const int64_t n = (int64_t)Pn * Pn * Pn;
-  int64_t g = (n + 255) / 256;
-  if (g > 8192) g = 8192;
-  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)g), dim3(256), 0, s, prev, Pp, next, Pn);
+  if (Pn > FILL_NT * FILL_KI) return hipErrorInvalidValue;
+  const int64_t g = (int64_t)Pn * ((Pn + FILL_ROWS - 1) / FILL_ROWS);
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)g), dim3(FILL_NT), 0, s, prev, Pp, next, Pn);
   return hipGetLastError();
 }
 

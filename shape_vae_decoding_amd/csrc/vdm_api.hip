@@ -230,6 +230,7 @@ struct HierWs {
   int32_t* sel_idx;
   int32_t* sel_cnt;
   int64_t* stats;
+  int64_t* part;  // spread partial counters of the mask stages
 };
 
 static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M, void* base, HierWs* w) {
@@ -267,6 +268,7 @@ static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M,
     x.sel_cnt = c.take<int32_t>((size_t)maxNB3 * 4);
   }
   x.stats = c.take<int64_t>((size_t)VDM_MAX_LEVELS * VDM_STAT_FIELDS * 8);
+  x.part = c.take<int64_t>((size_t)stat_part_words() * 8);
   if (w) *w = x;
   return c.off + 256;
 }
@@ -504,6 +506,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
   const bool kv = p->use_kvsel != 0;
 
   VDM_HIP(launch_stats_init(S, p->levels, p->R0, s), "stats init");
+  VDM_HIP(launch_zero(w.part, (size_t)stat_part_words() * 8, s), "zero launch");
   VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
   VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
   if (!kv) VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
@@ -560,16 +563,17 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
   {
     const int NB = nblocks8(p->R0 + 1);
     const int64_t nb3 = (int64_t)NB * NB * NB;
-    VDM_HIP_T(VDM_TIME_MASKS, s, launch_mark(nullptr, 1, nullptr, 1, p->R0, w.newmask, nullptr, w.counts, s), "mark launch");
-    VDM_HIP_T(VDM_TIME_MASKS, s, launch_scan(w.counts, nb3, bq, w.partial, w.offs, w.totals, S, s), "scan launch");
-    VDM_HIP_T(VDM_TIME_MASKS, s, launch_emit(w.newmask, w.counts, w.offs, p->R0, bq, w.list, w.items, w.occ, s), "emit launch");
+    VDM_HIP_T(VDM_TIME_MARK, s, launch_mark(nullptr, 1, nullptr, 1, p->R0, w.newmask, nullptr, w.counts, s), "mark launch");
+    VDM_HIP_T(VDM_TIME_SCAN, s, launch_scan(w.counts, nb3, bq, w.partial, w.offs, w.occ, w.totals, S, s), "scan launch");
+    VDM_HIP_T(VDM_TIME_EMIT, s, launch_emit(w.newmask, w.counts, w.offs, w.occ, w.totals, p->R0, bq, w.list, w.items, s),
+              "emit launch");
     st = decode_level(0);
     if (st != VDM_OK) return st;
   }
   for (int L = 0; L < p->levels; ++L) {
     const int R = p->R0 << L, P = R + 1, NB = nblocks8(P);
     int64_t* SL = S + L * VDM_STAT_FIELDS;
-    VDM_HIP_T(VDM_TIME_MASKS, s, launch_cell_test(vol_of(L), R, L ? w.kept[L - 1] : nullptr, p->tau, w.active[L], SL + VDM_STAT_TESTED,
+    VDM_HIP_T(VDM_TIME_CELL_TEST, s, launch_cell_test(vol_of(L), R, L ? w.kept[L - 1] : nullptr, p->tau, w.active[L], w.part, SL + VDM_STAT_TESTED,
                              SL + VDM_STAT_ACTIVE, s),
             "cell test launch");
     if (dbg) {
@@ -590,24 +594,26 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
     if (L == p->levels - 1) break;
     // kept = active dilated `dilation` times (ping-pong through tmp)
     if (p->dilation == 0) {
-      VDM_HIP_T(VDM_TIME_MASKS, s, launch_dilate(w.active[L], w.kept[L], R, 1, SL + VDM_STAT_KEPT, s), "copy launch");
+      VDM_HIP_T(VDM_TIME_DILATE, s, launch_dilate(w.active[L], w.kept[L], R, 1, w.part, SL + VDM_STAT_KEPT, s), "copy launch");
     } else {
       const uint64_t* src = w.active[L];
       for (int t = 0; t < p->dilation; ++t) {
         uint64_t* dst = ((p->dilation - 1 - t) % 2 == 0) ? w.kept[L] : w.tmp;
-        VDM_HIP_T(VDM_TIME_MASKS, s, launch_dilate(src, dst, R, 0, t == p->dilation - 1 ? SL + VDM_STAT_KEPT : nullptr, s), "dilate launch");
+        VDM_HIP_T(VDM_TIME_DILATE, s, launch_dilate(src, dst, R, 0, w.part, t == p->dilation - 1 ? SL + VDM_STAT_KEPT : nullptr, s), "dilate launch");
         src = dst;
       }
     }
     if (dbg && dbg->kept[L]) VDM_HIP(launch_bits_to_bytes(w.kept[L], R, NB, dbg->kept[L], s), "debug export");
     const int Rn = 2 * R, Pn = Rn + 1, NBn = nblocks8(Pn);
-    VDM_HIP_T(VDM_TIME_MASKS, s, launch_mark(w.kept[L], R, L ? w.comp[L] : nullptr, 0, Rn, w.newmask, w.comp[L + 1], w.counts, s),
+    VDM_HIP_T(VDM_TIME_MARK, s, launch_mark(w.kept[L], R, L ? w.comp[L] : nullptr, 0, Rn, w.newmask, w.comp[L + 1], w.counts, s),
             "mark launch");
-    VDM_HIP_T(VDM_TIME_MASKS, s, launch_scan(w.counts, (int64_t)NBn * NBn * NBn, bq, w.partial, w.offs, w.totals + 4 * (L + 1),
+    VDM_HIP_T(VDM_TIME_SCAN, s, launch_scan(w.counts, (int64_t)NBn * NBn * NBn, bq, w.partial, w.offs, w.occ, w.totals + 4 * (L + 1),
                         S + (L + 1) * VDM_STAT_FIELDS, s),
             "scan launch");
-    VDM_HIP_T(VDM_TIME_MASKS, s, launch_emit(w.newmask, w.counts, w.offs, Rn, bq, w.list, w.items, w.occ, s), "emit launch");
-    VDM_HIP_T(VDM_TIME_MASKS, s, launch_fill(vol_of(L), P, vol_of(L + 1), Pn, s), "fill launch");
+    VDM_HIP_T(VDM_TIME_EMIT, s,
+              launch_emit(w.newmask, w.counts, w.offs, w.occ, w.totals + 4 * (L + 1), Rn, bq, w.list, w.items, s),
+              "emit launch");
+    VDM_HIP_T(VDM_TIME_FILL, s, launch_fill(vol_of(L), P, vol_of(L + 1), Pn, s), "fill launch");
     st = decode_level(L + 1);
     if (st != VDM_OK) return st;
   }
