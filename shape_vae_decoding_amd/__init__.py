@@ -302,9 +302,10 @@ def vdm_select_kv(dec: Decoder, R: int, block: int, k: int, cap: int, K: torch.T
     elif nblk is None:
         nb = -(-(R + 1) // block)
         nblk = nb ** 3
+    if ws is None:
+        ws = workspace(vdm_select_workspace_size(dec, K.shape[0]), K.device)
     _check(_lib.vdm_select_kv(dec.ref, R, block, k, cap, K.data_ptr(), K.shape[0], _ptr(blocks), nblk,
-                              sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(),
-                              _stream(stream)))
+                              sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def hier_params(R0=75, levels=3, tau=2 * 2 / 300, dilation=1, kvsel: Optional[dict] = None) -> _HierParams:

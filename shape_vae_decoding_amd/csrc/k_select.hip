@@ -3,29 +3,32 @@
 // scoring tokens become the sub-volume's key/value set; techwalker article,
 // part 5, describes the same probe-then-reuse scheme).
 //
-// One workgroup per block: the block's 8 corner probes are embedded and
-// projected (same device routine as the decoder), then
-//   pass 1: per (probe, head) softmax max and sum over all tokens (MFMA logits),
-//   pass 2: score_j = mean over heads of the softmax probability, kept in LDS,
-//   top-k per probe by an exact 4-digit radix select on the float bits
-//   (equal scores: lower token index first), union in an LDS bitmap, optional
-//   cap by max-over-probes score, ascending compaction.
-// Each wave covers a quarter of the tokens for all heads; the per-wave partial
-// softmax statistics are merged in a fixed order, so results are reproducible.
+// One workgroup (8 waves) per group of up to 4 blocks: the 32 corner probes of
+// the group fill the 32 MFMA columns, so every K tile read serves 4 blocks.
+//   pass 1: per (probe, head) softmax max and sum over all tokens (MFMA logits);
+//   pass 2: score_j = mean over heads of the softmax probability, written to a
+//           per-workgroup scratch row in global memory (32 x M floats do not fit
+//           in LDS);
+//   top-k:  per probe, the k-th largest score by a bitwise search on the float
+//           bits held in registers (scores are >= 0, so unsigned order is float
+//           order), then every larger score and the lowest-index equal ones;
+//           the block's probes OR their sets into an LDS bitmap;
+//   cap:    if the union exceeds `cap`, the cap tokens of largest max-over-probes
+//           score (same search; members rank above non-members);
+//   output: ascending compaction of the bitmap.
+// Each wave covers 1/8 of the tokens in the passes; partial softmax statistics
+// are merged in a fixed order, so results are reproducible.
 #include "vdm_device.hpp"
 
 namespace vdm {
 
-constexpr int SEL_NT = 256;
+constexpr int SEL_NT = 512;
 constexpr int SEL_NW = SEL_NT / 64;
-constexpr int SEL_NP = 8;   // probes per block
-constexpr int SEL_BQ = 32;  // probe columns of the MFMA tile (8 used)
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+constexpr int SEL_NP = 8;                // probes per block
+constexpr int SEL_GB = 4;                // blocks per workgroup
+constexpr int SEL_BQ = SEL_NP * SEL_GB;  // probe columns of the MFMA tile
+constexpr int SEL_MAXV = 64;             // scores per lane in the search: M <= 64 * 64
+constexpr int SEL_GRID_MAX = 256;        // workgroups (scratch rows are per workgroup)
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -36,79 +39,71 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Mark in `bits` the k largest of the M values getu(i) (unsigned order; equal
-// values: lower index first). One wave; `hist` is 256 ints of this wave's LDS.
-template <typename GetU>
-__device__ void topk_mark(GetU getu, int M, int k, int* hist, unsigned* bits, int lane) {
-  unsigned prefix = 0, pmask = 0;
-  int need = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = lane; i < 256; i += 64) hist[i] = 0;
-    wave_sync();
-    for (int i = lane; i < M; i += 64) {
-      const unsigned u = getu(i);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
-    }
-    wave_sync();
-    // lane holds bins 255-4l .. 252-4l (descending digit order)
-    const int c0 = hist[255 - 4 * lane], c1 = hist[254 - 4 * lane], c2 = hist[253 - 4 * lane],
-              c3 = hist[252 - 4 * lane];
-    const int tot = c0 + c1 + c2 + c3;
-    const int incl = wave_incl_scan(tot, lane);
-    const int excl = incl - tot;
-    const bool mine = excl < need && need <= incl;
-    int digit = 0, before = 0;
-    if (mine) {
-      int c = excl;
-      if (c + c0 >= need) {
-        digit = 255 - 4 * lane;
-      } else if ((c += c0) + c1 >= need) {
-        digit = 254 - 4 * lane;
-      } else if ((c += c1) + c2 >= need) {
-        digit = 253 - 4 * lane;
-      } else {
-        c += c2;
-        digit = 252 - 4 * lane;
-      }
-      before = c;
-    }
-    const unsigned long long bal = __ballot(mine);
-    const int src = __ffsll((long long)bal) - 1;
-    digit = __shfl(digit, src);
-    before = __shfl(before, src);
-    need -= before;
-    prefix |= (unsigned)digit << shift;
-    pmask |= 255u << shift;
-    wave_sync();
-  }
-  // prefix is now the k-th largest value; `need` of its copies are taken, lowest index first
-  int taken = 0;
-  for (int base = 0; base < M; base += 64) {
-    const int i = base + lane;
-    const unsigned u = i < M ? getu(i) : 0u;
-    const bool eq = i < M && u == prefix;
-    const bool gt = i < M && u > prefix;
-    const unsigned long long be = __ballot(eq);
-    const int rank = __popcll(be & ((1ull << lane) - 1ull));
-    if (gt || (eq && taken + rank < need)) atomicOr(&bits[i >> 5], 1u << (i & 31));
-    taken += __popcll(be);
-  }
-  wave_sync();
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
+// Values u[i] stand for index i * 64 + lane (entries at or past n are 0 and never
+// taken). Sets in `bits` the k largest (unsigned order; equal values: lower index
+// first). One wave.
+__device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, int k, unsigned* bits, int lane) {
+  // (every loop is fully unrolled with constant indices, so u stays in registers)
+  // k-th largest: the largest p with #{u >= p} >= k, built bit by bit
+  unsigned p = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const unsigned cand = p | (1u << b);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_MAXV; ++i) c += (i * 64 + lane < n && u[i] >= cand) ? 1 : 0;
+    if (wave_sum(c) >= k) p = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_MAXV; ++i) gt += (i * 64 + lane < n && u[i] > p) ? 1 : 0;
+  const int need = k - wave_sum(gt);  // copies of p to take, lowest index first
+  int taken = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_MAXV; ++i) {
+    const int idx = i * 64 + lane;
+    const bool valid = idx < n;
+    const bool eq = valid && u[i] == p;
+    const unsigned long long be = __ballot(eq);
+    const int rank = taken + __popcll(be & ((1ull << lane) - 1ull));
+    if (valid && (u[i] > p || (eq && rank < need))) atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+    taken += __popcll(be);
+  }
+}
+
+// LDS: [embedding stage] | stats [NW][H][32] float2 | bits [GB][words] | bits2 [GB][words] | cnt [GB]
 template <typename T, int H>
 struct SelCfg {
   static constexpr int D = 64 * H;
   static constexpr int EMB_END = EmbedLds<T, SEL_BQ, D>::END;
-  __host__ __device__ static int base(int M) {
-    const int s = SEL_NP * M * 4;
-    return ((s > EMB_END ? s : EMB_END) + 15) & ~15;
-  }
+  static constexpr int STATS = (EMB_END + 15) & ~15;
+  static constexpr int BITS = STATS + SEL_NW * H * 32 * 8;
   __host__ __device__ static int total(int M) {
     const int words = (M + 31) / 32;
-    return base(M) + SEL_NW * H * 32 * 8 + SEL_NW * 256 * 4 + 2 * words * 4 + 16;
+    return BITS + 2 * SEL_GB * words * 4 + SEL_GB * 4 + 16;
   }
 };
+
+// per-workgroup scratch: SEL_BQ rows of Mpad scores
+__host__ __device__ inline int sel_mpad(int M) { return (M + 63) / 64 * 64; }
+
+// Scores row r, element i * 64 + lane, for i = 0 .. SEL_MAXV-1, as unsigned bits
+// (0 past M). Buffer loads: a scalar offset per i, so no per-element address
+// registers are kept live.
+__device__ __forceinline__ void load_scores(__amdgpu_buffer_rsrc_t buf, int row, int Mp, int M, int lane,
+                                            unsigned (&u)[SEL_MAXV]) {
+  const int voff = (row * Mp + lane) * 4;
+#pragma unroll
+  for (int i = 0; i < SEL_MAXV; ++i) {
+    const unsigned v = __builtin_amdgcn_raw_buffer_load_b32(buf, voff, i * 256, 0);
+    u[i] = i * 64 + lane < M ? v : 0u;
+  }
+}
 
 template <typename T, int H>
 __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
@@ -116,17 +111,21 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   using MM = Mma<T>;
   using Frag = typename MM::frag;
   using L = EmbedLds<T, SEL_BQ, 64 * H>;
+  using CF = SelCfg<T, H>;
   constexpr int D = 64 * H, KS_H = 64 / MM::KS;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int M = A.M;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = A.M, Mp = sel_mpad(M);
   const int nwords = (M + 31) / 32;
-  const int lbase = SelCfg<T, H>::base(M);
-  float* scores = reinterpret_cast<float*>(lds);                              // [8][M]
-  float2* stats = reinterpret_cast<float2*>(lds + lbase);                     // [NW][H][32]
-  int* hist = reinterpret_cast<int*>(lds + lbase + SEL_NW * H * 32 * 8);      // [NW][256]
-  unsigned* bits = reinterpret_cast<unsigned*>(hist + SEL_NW * 256);          // [nwords]
-  unsigned* bits2 = bits + nwords;                                            // [nwords]
+  float2* stats = reinterpret_cast<float2*>(lds + CF::STATS);     // [NW][H][32]
+  unsigned* bits = reinterpret_cast<unsigned*>(lds + CF::BITS);    // [GB][nwords]
+  unsigned* bits2 = bits + SEL_GB * nwords;                        // [GB][nwords]
+  int* ucount = reinterpret_cast<int*>(bits2 + SEL_GB * nwords);   // [GB]
+  float* scores = A.scores + (int64_t)blockIdx.x * SEL_BQ * Mp;    // [BQ][Mp], this workgroup's rows
+  const __amdgpu_buffer_rsrc_t sbuf =
+      __builtin_amdgcn_make_buffer_rsrc(scores, (short)0, SEL_BQ * Mp * 4, 0x00020000 /* raw buffer */);
   const int64_t nblk = A.d_n_blocks ? (int64_t)*A.d_n_blocks : A.n_blocks;
+  const int64_t ngroups = (nblk + SEL_GB - 1) / SEL_GB;
   const T* __restrict__ K = (const T*)A.K;
   QuerySrc qs;
   qs.mode = 3;
@@ -137,21 +136,14 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   const int nkb = (M + 31) / 32;
   const int per = (nkb + SEL_NW - 1) / SEL_NW;
   const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
-  const int col = lane & 31;
+  const int col = lane & 31;  // this lane's probe (MFMA column)
   const float NEG = -__builtin_inff();
 
-  for (int64_t row = blockIdx.x; row < nblk; row += gridDim.x) {
-    embed_qproj<T, SEL_BQ, D, SEL_NT>(qs, row * SEL_NP, row * SEL_NP + SEL_NP, (const T*)A.Wq, lds, tid);
-    Frag qf[H][KS_H];
-    {
-      const T* Qs = reinterpret_cast<const T*>(lds + L::QS);
-#pragma unroll
-      for (int h = 0; h < H; ++h)
-#pragma unroll
-        for (int ks = 0; ks < KS_H; ++ks) qf[h][ks] = load_frag<T>(Qs + 64 * h + ks * MM::KS, L::DPAD, lane);
-    }
-    __syncthreads();
-    for (int i = tid; i < 2 * nwords; i += SEL_NT) bits[i] = 0u;
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t row0 = grp * SEL_GB;
+    const int nb = (int)min<int64_t>(SEL_GB, nblk - row0);
+    embed_qproj<T, SEL_BQ, D, SEL_NT>(qs, row0 * SEL_NP, (row0 + nb) * SEL_NP, (const T*)A.Wq, lds, tid);
+    const T* qrow = reinterpret_cast<const T*>(lds + L::QS) + col * L::DPAD + MM::KW * (lane >> 5);
 
     // ---------------------------------------------------------------- pass 1: softmax statistics
     float m[H], l[H];
@@ -168,7 +160,8 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         f32x16 S = zero16();
 #pragma unroll
         for (int ks = 0; ks < KS_H; ++ks)
-          S = MM::mma(*reinterpret_cast<const Frag*>(krow + 64 * h + ks * MM::KS), qf[h][ks], S);
+          S = MM::mma(*reinterpret_cast<const Frag*>(krow + 64 * h + ks * MM::KS),
+                      *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
         float mx = NEG;
         float t[16];
 #pragma unroll
@@ -178,10 +171,10 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         }
         const float mnew = fmaxf(m[h], mx);
         if (mnew != NEG) {
-          float s = 0.f;
+          float sum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(t[r] - mnew);
-          l[h] = l[h] * __builtin_amdgcn_exp2f(m[h] - mnew) + s;
+          for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(t[r] - mnew);
+          l[h] = l[h] * __builtin_amdgcn_exp2f(m[h] - mnew) + sum;
           m[h] = mnew;
         }
       }
@@ -196,6 +189,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       }
       if (lane < 32) stats[(wave * H + h) * 32 + lane] = make_float2(m[h], l[h]);
     }
+    for (int i = tid; i < 2 * SEL_GB * nwords; i += SEL_NT) bits[i] = 0u;
     __syncthreads();
     float mf[H], linv[H];
 #pragma unroll
@@ -225,49 +219,58 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         f32x16 S = zero16();
 #pragma unroll
         for (int ks = 0; ks < KS_H; ++ks)
-          S = MM::mma(*reinterpret_cast<const Frag*>(krow + 64 * h + ks * MM::KS), qf[h][ks], S);
+          S = MM::mma(*reinterpret_cast<const Frag*>(krow + 64 * h + ks * MM::KS),
+                      *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           acc[r] += __builtin_amdgcn_exp2f(S[r] * 0.18033688011112042f - mf[h]) * linv[h];
       }
-      if (col < SEL_NP) {
+      if (col < nb * SEL_NP) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = kb * 32 + crow(r, lane);
-          if (j < M) scores[col * M + j] = acc[r] * (1.f / H);
+          if (j < M) scores[col * Mp + j] = acc[r] * (1.f / H);
         }
       }
     }
-    __syncthreads();
+    __syncthreads();  // the scores rows are complete and visible to the workgroup
 
-    // ---------------------------------------------------------------- top-k per probe, union
-    for (int p = wave; p < SEL_NP; p += SEL_NW) {
-      const float* sc = scores + p * M;
-      topk_mark([&](int i) { return __float_as_uint(sc[i]); }, M, A.k, hist + wave * 256, bits, lane);
+    // ---------------------------------------------------------------- top-k per probe, union per block
+    for (int p = wave; p < nb * SEL_NP; p += SEL_NW) {
+      unsigned u[SEL_MAXV];
+      load_scores(sbuf, p, Mp, M, lane, u);
+      topk_bits(u, M, A.k, bits + (p / SEL_NP) * nwords, lane);
     }
     __syncthreads();
-    int cnt = 0;
-    for (int i = lane; i < nwords; i += 64) cnt += __popc(bits[i]);
+
+    // ---------------------------------------------------------------- cap, compaction (one wave per block)
+    if (wave < nb) {
+      const int blk = wave;
+      unsigned* ub = bits + blk * nwords;
+      int cnt = 0;
+      for (int i = lane; i < nwords; i += 64) cnt += __popc(ub[i]);
+      cnt = wave_sum(cnt);
+      const unsigned* outbits = ub;
+      if (cnt > A.cap) {
+        // keep the cap tokens of largest max-over-probes score (members rank above non-members)
+        unsigned u[SEL_MAXV];
+        load_scores(sbuf, blk * SEL_NP, Mp, M, lane, u);
+        for (int q = 1; q < SEL_NP; ++q) {
+          const int voff = ((blk * SEL_NP + q) * Mp + lane) * 4;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
-    unsigned* outbits = bits;
-    if (cnt > A.cap) {
-      // keep the cap tokens of largest max-over-probes score (members rank above non-members)
-      if (wave == 0) {
-        auto getu = [&](int i) -> unsigned {
-          if (!((bits[i >> 5] >> (i & 31)) & 1u)) return 0u;
-          float mx = scores[i];
-          for (int p = 1; p < SEL_NP; ++p) mx = fmaxf(mx, scores[p * M + i]);
-          return __float_as_uint(mx) + 1u;
-        };
-        topk_mark(getu, M, A.cap, hist, bits2, lane);
+          for (int i = 0; i < SEL_MAXV; ++i)  // scores >= 0: bit order is float order
+            u[i] = max(u[i], __builtin_amdgcn_raw_buffer_load_b32(sbuf, voff, i * 256, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < SEL_MAXV; ++i) {
+          const int idx = i * 64 + lane;
+          const bool member = idx < M && ((ub[idx >> 5] >> (idx & 31)) & 1u);
+          u[i] = member ? u[i] + 1u : 0u;
+        }
+        topk_bits(u, M, A.cap, bits2 + blk * nwords, lane);
+        outbits = bits2 + blk * nwords;
       }
-      outbits = bits2;
-      __syncthreads();
-    }
-
-    // ---------------------------------------------------------------- ascending compaction
-    if (wave == 0) {
+      const int64_t row = row0 + blk;
       int32_t* out = A.sel_idx + row * (int64_t)A.cap;
       int base = 0;
       for (int w0 = 0; w0 < nwords; w0 += 64) {
@@ -286,10 +289,15 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       for (int i = base + lane; i < A.cap; i += 64) out[i] = -1;
       if (lane == 0) {
         A.sel_cnt[row] = base;
-        if (A.stat_selected) atomicAdd((unsigned long long*)A.stat_selected, (unsigned long long)base);
+        ucount[blk] = base;
       }
     }
     __syncthreads();
+    if (tid == 0 && A.stat_selected) {
+      int64_t t = 0;
+      for (int b = 0; b < nb; ++b) t += ucount[b];
+      atomicAdd((unsigned long long*)A.stat_selected, (unsigned long long)t);
+    }
   }
 }
 
@@ -299,23 +307,21 @@ static hipError_t run_select(const SelectArgs& a, hipStream_t s) {
   const void* fn = reinterpret_cast<const void*>(&select_kernel<T, H>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, select_kernel<T, H>, SEL_NT, lds);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) per_cu = 1;
-  int64_t grid = (int64_t)dev_info().cus * per_cu;
-  if (!a.d_n_blocks && a.n_blocks < grid) grid = a.n_blocks;
+  int64_t grid = dev_info().cus;
+  if (grid > SEL_GRID_MAX) grid = SEL_GRID_MAX;
+  if (!a.d_n_blocks) {
+    const int64_t groups = (a.n_blocks + SEL_GB - 1) / SEL_GB;
+    if (groups < grid) grid = groups;
+  }
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL((select_kernel<T, H>), dim3((unsigned)grid), dim3(SEL_NT), lds, s, a);
   return hipGetLastError();
 }
 
-size_t select_lds_bytes(int dtype, int D, int M) {
-  if (dtype == VDM_BF16) return D == 256 ? SelCfg<bf16, 4>::total(M) : SelCfg<bf16, 1>::total(M);
-  return SelCfg<float, 1>::total(M);
-}
+size_t select_scratch_bytes(int M) { return (size_t)SEL_GRID_MAX * SEL_BQ * sel_mpad(M) * sizeof(float); }
 
 hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s) {
+  if (a.M > SEL_MAXV * 64) return hipErrorInvalidValue;
   if (dtype == VDM_BF16) return a.D == 256 ? run_select<bf16, 4>(a, s) : run_select<bf16, 1>(a, s);
   return run_select<float, 1>(a, s);
 }

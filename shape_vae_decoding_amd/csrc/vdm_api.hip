@@ -229,6 +229,7 @@ struct HierWs {
   int32_t* occ;
   int32_t* sel_idx;
   int32_t* sel_cnt;
+  float* sel_scores;
   int64_t* stats;
   int64_t* part;  // spread partial counters of the mask stages
 };
@@ -266,6 +267,7 @@ static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M,
   if (p->use_kvsel) {
     x.sel_idx = c.take<int32_t>((size_t)maxNB3 * p->cap * 4);
     x.sel_cnt = c.take<int32_t>((size_t)maxNB3 * 4);
+    x.sel_scores = c.take<float>(select_scratch_bytes((int)M));
   }
   x.stats = c.take<int64_t>((size_t)VDM_MAX_LEVELS * VDM_STAT_FIELDS * 8);
   x.part = c.take<int64_t>((size_t)stat_part_words() * 8);
@@ -346,8 +348,11 @@ size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, in
 
 size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M) {
   if (check_decoder(dec) != VDM_OK) return 0;
-  (void)M;
-  return 256;
+  if (M < 1 || M > 4096) {
+    fail(VDM_ERR_INVALID_ARG, "M=%lld (1..4096)", (long long)M);
+    return 0;
+  }
+  return select_scratch_bytes((int)M) + 256;
 }
 
 size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M) {
@@ -450,8 +455,6 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
 vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, const void* K,
                          int64_t M, const int32_t* blocks, int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt, void* ws,
                          size_t ws_bytes, vdm_stream stream) {
-  (void)ws;
-  (void)ws_bytes;
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;
   if (R < 1 || R > 1200 || block < 1) return fail(VDM_ERR_INVALID_ARG, "R=%d block=%d", R, block);
@@ -462,6 +465,9 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
     return fail(VDM_ERR_INVALID_ARG, "nblk=%lld (all blocks: %lld)", (long long)nblk, (long long)(NB * NB * NB));
   if (nblk == 0) return VDM_OK;
   if (!K || !sel_idx || !sel_cnt || !aligned(K, 16)) return fail(VDM_ERR_INVALID_ARG, "K, sel_idx or sel_cnt NULL/misaligned");
+  const size_t need = select_scratch_bytes((int)M) + 256;
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(VDM_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes, need);
   SelectArgs a;
   memset(&a, 0, sizeof a);
   a.R = R;
@@ -477,6 +483,7 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
   a.n_blocks = nblk;
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
+  a.scores = (float*)ws;
   (void)hipGetLastError();
   VDM_HIP_T(VDM_TIME_SELECT, (hipStream_t)stream, launch_select(dec->dtype, a, (hipStream_t)stream), "select launch");
   return VDM_OK;
@@ -534,6 +541,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       sa.sel_idx = w.sel_idx;
       sa.sel_cnt = w.sel_cnt;
       sa.stat_selected = S + L * VDM_STAT_FIELDS + VDM_STAT_SELECTED;
+      sa.scores = w.sel_scores;
       VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, sa, s), "select launch");
     }
     DecodeArgs a = base_args(dec);

@@ -105,8 +105,9 @@ struct SelectArgs {
   int32_t* sel_idx;
   int32_t* sel_cnt;
   int64_t* stat_selected;  // optional: += sum of sel_cnt
+  float* scores;           // scratch of select_scratch_bytes(M)
 };
 hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s);
-size_t select_lds_bytes(int dtype, int D, int M);
+size_t select_scratch_bytes(int M);
 
 }  // namespace vdm

@@ -113,6 +113,11 @@ def test_select_and_hier_argument_checks():
     # blocks == NULL requires nblk = NB^3 (76 points per axis -> 10 blocks)
     assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0x1000, 3072, None, 999, 0x1000, 0x1000, None, 0,
                              None) == V.VDM_ERR_INVALID_ARG
+    # the score scratch is required and sized by vdm_select_workspace_size
+    need = lib.vdm_select_workspace_size(C.byref(d), 3072)
+    assert need >= 32 * 3072 * 4
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0x1000, 3072, None, 1000, 0x1000, 0x1000, 0x1000,
+                             need - 1, None) == V.VDM_ERR_WORKSPACE
     p = V.hier_params(R0=75, levels=3)
     assert lib.vdm_hier_workspace_size(C.byref(d), C.byref(p), 3072) > 27 * 10 ** 6 * 4
     bad = V.hier_params(R0=75, levels=7)
