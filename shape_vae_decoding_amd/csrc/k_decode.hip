@@ -378,7 +378,8 @@ __device__ __forceinline__ f32x16 s_block(const typename Mma<typename C::T>::fra
   return S;
 }
 
-// LAST: the final tile (no S of a next tile, no K load); RAGGED: it is partial.
+// LAST: the final tile (no S of a next tile, no K load; ends with its own P.V);
+// RAGGED: it is partial.
 template <typename C, bool LAST, bool RAGGED>
 __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], const uint4 (&v_prev)[C::RUN_U4],
                                           uint4 (&k_load)[C::RUN_U4], uint4 (&v_load)[C::RUN_U4],
@@ -423,6 +424,16 @@ __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], cons
       __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
     }
   }
+  if constexpr (LAST) {
+    Frag kf_unused[C::KSTEPS], vf_last[2][C::PSTEPS];
+    as_frags<C>(k_next, v_load, kf_unused, vf_last);
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int ps = 0; ps < C::PSTEPS; ++ps) O[db][qb] = MM::mma(vf_last[db][ps], P[qb][ps], O[db][qb]);
+  }
 }
 
 template <typename C, bool GATHER>
@@ -433,8 +444,8 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   using Frag = typename MM::frag;
   constexpr int KS = C::KSTEPS, PS = C::PSTEPS;
 
-  const int tid = threadIdx.x, lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
+  const int tid0 = threadIdx.x, lane0 = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // wave-uniform: scalar registers
   const int hw = wave % C::H, qg = wave / C::H;
   const int64_t nq = A.d_N ? (int64_t)*A.d_N : A.N;
   const int64_t n_tiles = A.items ? (A.d_n_items ? (int64_t)*A.d_n_items : A.n_tiles) : (nq + C::BQ - 1) / C::BQ;
@@ -446,24 +457,30 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   const float kmax = A.kmax[hw];
 
   const float2* gtab = reinterpret_cast<const float2*>(lds + C::GTAB);
-  if constexpr (C::GELU_TABLE) gelu_table_fill(reinterpret_cast<float2*>(lds + C::GTAB), tid, C::NT);
+  if constexpr (C::GELU_TABLE) gelu_table_fill(reinterpret_cast<float2*>(lds + C::GTAB), tid0, C::NT);
   // (the first barrier of the tile loop orders the fill before any lookup)
 
   int vpos[C::NCK] = {};
   if constexpr (GATHER) {
     constexpr int CPR = C::D / C::EPC;
 #pragma unroll
-    for (int i = 0; i < C::NCK; ++i) vpos[i] = key_pos<T>((tid + i * C::NT) / CPR);
+    for (int i = 0; i < C::NCK; ++i) vpos[i] = key_pos<T>((tid0 + i * C::NT) / CPR);
   }
 
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    // Thread and lane indices are re-derived opaquely in each phase, so that the
+    // address arithmetic of one phase is neither hoisted out of the tile loop
+    // nor shared with another phase: otherwise it stays live across the token
+    // loop, whose registers are all taken.
+    int tid = opaque(tid0), lane = opaque(lane0);
     int64_t q0, q1;
     int row = -1;
     if (A.items) {
+      // one item per workgroup: its fields are uniform (scalar registers)
       const Item it = A.items[tile];
-      q0 = it.q0;
-      q1 = it.q1;
-      row = it.row;
+      q0 = __builtin_amdgcn_readfirstlane(it.q0);
+      q1 = __builtin_amdgcn_readfirstlane(it.q1);
+      row = __builtin_amdgcn_readfirstlane(it.row);
     } else {
       q0 = tile * C::BQ;
       q1 = q0 + C::BQ < nq ? q0 + C::BQ : nq;
@@ -471,6 +488,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
 
     // ---------------------------------------------------------------- Q = Wq e(p)
     embed_qproj<T, C::BQ, C::D, C::NT>(A.qs, q0, q1, (const T*)A.Wq, lds, tid);
+    lane = opaque(lane);
     Frag qf[C::QB][KS];
     float nb[C::QB];  // -b, the fixed softmax shift of this lane's query, per block
     {
@@ -535,7 +553,6 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) S[qb] = s_block<C>(kf, qf[qb]);
       }
-      const bool ragged = nkeys % C::KT != 0;
       int kt = 0;
       for (; kt + 2 < nkt; kt += 2) {
         pipe_iter<C, false, false>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, kt + 2, nkeys, hw, lane, qf, nb, S, P, O,
@@ -549,30 +566,15 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
                                    l_run);
         ++kt;
       }
-      // the last tile: softmax (masked if partial) beside P.V of the previous one,
-      // then its own P.V
-      Frag vf_last[2][PS];
+      // the last tile: softmax (masked, in case it is partial) beside P.V of the
+      // previous one, then its own P.V. Its K was consumed by the previous step;
+      // V of the previous tile sits in vb[(kt+1)&1] and moves to vb[1] when kt
+      // is odd, so that a single instance of the step is emitted.
       if (kt & 1) {
-        if (ragged)
-          pipe_iter<C, true, true>(kb[1], vb[0], kb[1], vb[1], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
-        else
-          pipe_iter<C, true, false>(kb[1], vb[0], kb[1], vb[1], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
-        Frag kf_unused[KS];
-        as_frags<C>(kb[0], vb[1], kf_unused, vf_last);
-      } else {
-        if (ragged)
-          pipe_iter<C, true, true>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
-        else
-          pipe_iter<C, true, false>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
-        Frag kf_unused[KS];
-        as_frags<C>(kb[0], vb[0], kf_unused, vf_last);
+#pragma unroll
+        for (int i = 0; i < C::RUN_U4; ++i) vb[1][i] = vb[0][i];
       }
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int ps = 0; ps < PS; ++ps) O[db][qb] = MM::mma(vf_last[db][ps], P[qb][ps], O[db][qb]);
+      pipe_iter<C, true, true>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
       }
     attention_done:;
     } else {
@@ -604,6 +606,8 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     }
 
     // ---------------------------------------------------------------- o = sum p v / sum p
+    tid = opaque(tid);
+    lane = opaque(lane);
     T* Ob = reinterpret_cast<T*>(lds + C::OBUF);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {

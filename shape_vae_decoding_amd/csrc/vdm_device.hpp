@@ -54,6 +54,13 @@ struct Pad {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// x, hidden from the optimiser: values derived from it are recomputed where they
+// are used instead of being hoisted out of a loop and kept live across it.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ int crow(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 template <typename T>
@@ -296,9 +303,10 @@ __device__ void embed_qproj(const QuerySrc& qs, int64_t q0, int64_t q1, const T*
   T* e_hi = reinterpret_cast<T*>(lds + L::E_HI);
   T* e_lo = reinterpret_cast<T*>(lds + L::E_LO);
   T* Qs = reinterpret_cast<T*>(lds + L::QS);
-  const int lane = lane_id();
-  const int wave = tid >> 6;
   constexpr int NW = NT / 64;
+  static_assert((NW & (NW - 1)) == 0, "a power-of-two number of waves");
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & (NW - 1));
   constexpr int RB = D / 32, CB = BQ / 32, KS = 64 / MM::KS;
   // wave w owns row blocks w, w + NW, .. (RB > NW) or row block w % RB and every
   // (NW / RB)-th column block (RB <= NW); each of its Wq fragments is loaded once
