@@ -180,16 +180,19 @@ __device__ __forceinline__ void as_frags(const uint4 (&kr)[C::RUN_U4], const uin
     for (int ps = 0; ps < C::PSTEPS; ++ps) vf[db][ps] = vp[db * C::PSTEPS + ps];
 }
 
-// Softmax numerators of one 32x32 S^T block for this lane's query column:
-// p = exp2(s * scale - b), rounded to the operand type, packed as P^T fragments;
-// l accumulates the rounded p. Keys at or beyond `valid` (ragged last tile) give 0.
-template <typename T, bool RAGGED>
+// Softmax numerators of one 32x32 S^T block for this lane's query column. The
+// queries carry the logit scale log2(e)/sqrt(64), so S holds base-2 logits t and
+// p = exp2(t + nb) (SHIFT) or exp2(t) (no shift: every |t| of these queries is at
+// most SHIFT_FREE_MAX, so p can neither overflow nor underflow), rounded to the
+// operand type and packed as P^T fragments; l accumulates the rounded p. Keys at
+// or beyond `valid` (ragged last tile) give 0.
+template <typename T, bool RAGGED, bool SHIFT>
 __device__ __forceinline__ void softmax_block(const f32x16& S, float nb, float& l, int key0, int valid, int lane,
                                               typename Mma<T>::frag (&pf)[32 / Mma<T>::KS]) {
   using MM = Mma<T>;
   float p[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], SOFTMAX_SCALE_LOG2, nb));
+  for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(SHIFT ? S[r] + nb : S[r]);
   if constexpr (RAGGED) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
@@ -311,7 +314,7 @@ __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, cons
 // One 32-token tile for all of this wave's query blocks: S^T of the next query
 // block is issued before the softmax of the current one, so MFMA and VALU work
 // overlap. kf: K_h fragments (A operand), vf: V_h^T fragments.
-template <typename C, bool RAGGED>
+template <typename C, bool RAGGED, bool SHIFT>
 __device__ __forceinline__ void tile_compute(const typename Mma<typename C::T>::frag (&kf)[C::KSTEPS],
                                              const typename Mma<typename C::T>::frag (&vf)[2][C::PSTEPS],
                                              const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
@@ -334,7 +337,7 @@ __device__ __forceinline__ void tile_compute(const typename Mma<typename C::T>::
       for (int ks = 1; ks < C::KSTEPS; ++ks) S_next = MM::mma(kf[ks], qf[nq][ks], S_next);
     }
     Frag pf[C::PSTEPS];
-    softmax_block<T, RAGGED>(S, nb[qb], l[qb], kt * C::KT, nkeys, lane, pf);
+    softmax_block<T, RAGGED, SHIFT>(S, nb[qb], l[qb], kt * C::KT, nkeys, lane, pf);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -346,7 +349,7 @@ __device__ __forceinline__ void tile_compute(const typename Mma<typename C::T>::
     // wave keeps the matrix pipe fed while it computes exponentials; P.V of the
     // last block at the end.
     constexpr int NM = (2 * C::QB - 2) * C::KSTEPS;  // MFMAs that have softmax work beside them
-    constexpr int VPM = (C::QB * 48 + NM - 1) / NM;   // VALU instructions per such MFMA
+    constexpr int VPM = (C::QB * (SHIFT ? 48 : 32) + NM - 1) / NM;  // VALU instructions per such MFMA
     // the next tile's operand loads first, so they have the whole tile to land
     __builtin_amdgcn_sched_group_barrier(0x020, 2 * C::RUN_U4, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, C::KSTEPS, 0);
@@ -363,7 +366,7 @@ __device__ __forceinline__ void tile_compute(const typename Mma<typename C::T>::
 // Iteration k of the loop over 32-token tiles issues three independent pieces of
 // work so that the matrix pipe and the VALU run side by side:
 //   O += V(k-1) P(k-1)          P.V of the previous tile            (MFMA)
-//   P(k) = exp2(S(k) scale - b)  softmax numerators of this tile     (VALU)
+//   P(k) = exp2(S(k) [- b])      softmax numerators of this tile     (VALU)
 //   S(k+1) = K(k+1) Q^T          logits of the next tile             (MFMA)
 // and the loads of K(k+2) and V(k). Before the first tile P(-1) = 0 and V(-1) = 0.
 
@@ -379,8 +382,8 @@ __device__ __forceinline__ f32x16 s_block(const typename Mma<typename C::T>::fra
 }
 
 // LAST: the final tile (no S of a next tile, no K load; ends with its own P.V);
-// RAGGED: it is partial.
-template <typename C, bool LAST, bool RAGGED>
+// RAGGED: it is partial; SHIFT: see softmax_block.
+template <typename C, bool LAST, bool RAGGED, bool SHIFT>
 __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], const uint4 (&v_prev)[C::RUN_U4],
                                           uint4 (&k_load)[C::RUN_U4], uint4 (&v_load)[C::RUN_U4],
                                           __amdgpu_buffer_rsrc_t Kg, __amdgpu_buffer_rsrc_t Vg,
@@ -405,7 +408,7 @@ __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], cons
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     Frag pn[C::PSTEPS];
-    softmax_block<T, RAGGED>(S[qb], nb[qb], l[qb], kt * C::KT, nkeys, lane, pn);
+    softmax_block<T, RAGGED, SHIFT>(S[qb], nb[qb], l[qb], kt * C::KT, nkeys, lane, pn);
     if constexpr (!LAST) S[qb] = s_block<C>(kf, qf[qb]);
 #pragma unroll
     for (int ps = 0; ps < C::PSTEPS; ++ps) P[qb][ps] = pn[ps];
@@ -416,7 +419,7 @@ __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], cons
     constexpr int NPV = 2 * C::PSTEPS * C::QB;
     constexpr int NS = LAST ? 0 : C::KSTEPS * C::QB;
     constexpr int NM = NPV + NS;
-    constexpr int VPM = (C::QB * 48 + NM - 1) / NM;
+    constexpr int VPM = (C::QB * (SHIFT ? 48 : 32) + NM - 1) / NM;
     __builtin_amdgcn_sched_group_barrier(0x020, (LAST ? 1 : 2) * C::RUN_U4, 0);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -433,6 +436,119 @@ __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], cons
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int ps = 0; ps < C::PSTEPS; ++ps) O[db][qb] = MM::mma(vf_last[db][ps], P[qb][ps], O[db][qb]);
+  }
+}
+
+// Softmax shift. With |t| <= B for every base-2 logit t of a query (B from
+// Cauchy-Schwarz), p = exp2(t + nb) with nb = SHIFT_FREE_MAX - B lies in
+// [2^(64 - 2B), 2^64]: no overflow, and sums of up to 2^31 products p v stay far
+// inside the fp32 range. When B <= 64 for every query of a wave, nb = 0 is just as
+// safe (p in [2^-64, 2^64]) and the wave skips the addition.
+constexpr float SHIFT_FREE_MAX = 64.f;
+
+template <int N>
+__device__ __forceinline__ bool any_below(const float (&x)[N], float lim) {
+  bool r = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) r = r || x[i] < lim;
+  return r;
+}
+
+// Dense attention of this wave's QB query blocks over all M tokens: the
+// software-pipelined loop over 32-token tiles (see pipe_iter).
+template <typename C, bool SHIFT>
+__device__ __forceinline__ void dense_attention(const DecodeArgs& A, int nkeys, int hw, int lane,
+                                                const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
+                                                const float (&nb)[C::QB], f32x16 (&O)[2][C::QB],
+                                                float (&l_run)[C::QB]) {
+  using Frag = typename Mma<typename C::T>::frag;
+  const int nkt = (nkeys + C::KT - 1) / C::KT;
+  if (nkt == 0) return;  // (no tokens: only reachable with M = 0, which the API rejects)
+  // Iteration k reads K(k+1) from kb[(k+1)&1] and V(k-1) from vb[(k+1)&1] and
+  // loads K(k+2) into kb[k&1], V(k) into vb[k&1]; the loop runs the full
+  // iterations two at a time so buffers are static.
+  const int64_t packed_bytes = (int64_t)nkt * C::KT * C::D * C::SZ;
+  const __amdgpu_buffer_rsrc_t Kg = buffer_of(A.Kp, packed_bytes);
+  const __amdgpu_buffer_rsrc_t Vg = buffer_of(A.Vt, packed_bytes);
+  uint4 kb[2][C::RUN_U4], vb[2][C::RUN_U4];
+  f32x16 S[C::QB];
+  Frag P[C::QB][C::PSTEPS];
+#pragma unroll
+  for (int i = 0; i < C::RUN_U4; ++i) vb[1][i] = uint4{0, 0, 0, 0};
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int ps = 0; ps < C::PSTEPS; ++ps) P[qb][ps] = Frag{};
+  load_run<C>(Kg, 0, hw, lane, kb[0]);
+  load_run<C>(Kg, nkt > 1 ? 1 : 0, hw, lane, kb[1]);
+  {
+    Frag kf[C::KSTEPS], vf_unused[2][C::PSTEPS];
+    as_frags<C>(kb[0], vb[1], kf, vf_unused);
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) S[qb] = s_block<C>(kf, qf[qb]);
+  }
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {
+    pipe_iter<C, false, false, SHIFT>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, kt + 2, nkeys, hw, lane, qf, nb, S, P,
+                                      O, l_run);
+    const int k3 = kt + 3 < nkt ? kt + 3 : nkt - 1;
+    pipe_iter<C, false, false, SHIFT>(kb[0], vb[0], kb[1], vb[1], Kg, Vg, kt + 1, k3, nkeys, hw, lane, qf, nb, S, P,
+                                      O, l_run);
+  }
+  if (kt + 1 < nkt) {  // one more full iteration (kt even)
+    pipe_iter<C, false, false, SHIFT>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, nkt - 1, nkeys, hw, lane, qf, nb, S, P,
+                                      O, l_run);
+    ++kt;
+  }
+  // the last tile: softmax (masked, in case it is partial) beside P.V of the
+  // previous one, then its own P.V. Its K was consumed by the previous step;
+  // V of the previous tile sits in vb[(kt+1)&1] and moves to vb[1] when kt
+  // is odd, so that a single instance of the step is emitted.
+  if (kt & 1) {
+#pragma unroll
+    for (int i = 0; i < C::RUN_U4; ++i) vb[1][i] = vb[0][i];
+  }
+  pipe_iter<C, true, true, SHIFT>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
+}
+
+// Attention over one block's selected token set: 32-token tiles gathered into
+// an LDS double buffer (V transposed on the way in), one barrier per tile.
+template <typename C, bool SHIFT>
+__device__ __forceinline__ void gathered_attention(const typename C::T* __restrict__ Kg,
+                                                   const typename C::T* __restrict__ Vg, const int32_t* sel,
+                                                   int nkeys, int M, int tid, int lane, int hw, char* lds,
+                                                   const int (&vpos)[C::NCK],
+                                                   const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
+                                                   const float (&nb)[C::QB], f32x16 (&O)[2][C::QB],
+                                                   float (&l_run)[C::QB]) {
+  using T = typename C::T;
+  using MM = Mma<T>;
+  using Frag = typename MM::frag;
+  const int nkt = (nkeys + C::KT - 1) / C::KT;
+  uint4 rk[C::NCK], rv[C::NCK];
+  tile_load<C, true>(Kg, Vg, sel, nkeys, M, 0, tid, rk, rv);
+  tile_store<C, true>(lds, 0, tid, vpos, rk, rv);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    // prefetch the next tile (clamped: the last step reloads its own tile)
+    tile_load<C, true>(Kg, Vg, sel, nkeys, M, kt + 1 < nkt ? kt + 1 : kt, tid, rk, rv);
+    const T* Kb = reinterpret_cast<const T*>(lds + (kt & 1) * C::KBYTES);
+    const T* Vb = reinterpret_cast<const T*>(lds + 2 * C::KBYTES + (kt & 1) * C::VBYTES);
+    Frag kf[C::KSTEPS], vf[2][C::PSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = load_frag<T>(Kb + 64 * hw + ks * MM::KS, C::DPAD, lane);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int ps = 0; ps < C::PSTEPS; ++ps)
+        vf[db][ps] = load_frag<T>(Vb + (64 * hw + 32 * db) * C::VPAD + ps * MM::KS, C::VPAD, lane);
+    if ((kt + 1) * C::KT > nkeys)
+      tile_compute<C, true, SHIFT>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
+    else
+      tile_compute<C, false, SHIFT>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
+    // the other buffer was last read before the previous barrier
+    tile_store<C, true>(lds, (kt + 1) & 1, tid, vpos, rk, rv);
+    __syncthreads();
   }
 }
 
@@ -487,10 +603,11 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     }
 
     // ---------------------------------------------------------------- Q = Wq e(p)
-    embed_qproj<T, C::BQ, C::D, C::NT>(A.qs, q0, q1, (const T*)A.Wq, lds, tid);
+    // (scaled by log2(e)/sqrt(64) before the one rounding, so logits come out in base 2)
+    embed_qproj<T, C::BQ, C::D, C::NT>(A.qs, q0, q1, (const T*)A.Wq, lds, tid, SOFTMAX_SCALE_LOG2);
     lane = opaque(lane);
     Frag qf[C::QB][KS];
-    float nb[C::QB];  // -b, the fixed softmax shift of this lane's query, per block
+    float nb[C::QB];  // the fixed softmax shift of this lane's query (if one is needed), per block
     {
       const T* Qs = reinterpret_cast<const T*>(lds + EmbedLds<T, C::BQ, C::D>::QS);
 #pragma unroll
@@ -507,8 +624,9 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
           }
         }
         n2 += __shfl_xor(n2, 32);
-        // upper bound of s * scale over all tokens, inflated to cover fp32 rounding
-        nb[qb] = -(SOFTMAX_SCALE_LOG2 * 1.00390625f) * sqrtf(n2) * kmax;
+        // B: upper bound of the base-2 logit over all tokens (Cauchy-Schwarz with
+        // the head's largest key norm), inflated to cover fp32 rounding
+        nb[qb] = SHIFT_FREE_MAX - 1.00390625f * sqrtf(n2) * kmax;
       }
     }
     __syncthreads();
@@ -516,7 +634,6 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     // ---------------------------------------------------------------- attention
     const int nkeys = GATHER ? min(max(A.sel_cnt[row], 0), A.cap) : A.M;
     const int32_t* sel = GATHER ? A.sel_idx + (int64_t)row * A.cap : nullptr;
-    const int nkt = (nkeys + C::KT - 1) / C::KT;
 
     f32x16 O[2][C::QB];
     float l_run[C::QB];
@@ -527,82 +644,19 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       l_run[qb] = 0.f;
     }
 
+    // logits of every query of this wave within +-SHIFT_FREE_MAX: no shift
+    const bool shift = __builtin_amdgcn_ballot_w64(any_below(nb, 0.f)) != 0;
     if constexpr (!GATHER) {
-      if (nkt == 0) goto attention_done;  // (no tokens: only reachable with M = 0, which the API rejects)
-      {
-      // Pipelined (see pipe_iter). Iteration k reads K(k+1) from kb[(k+1)&1] and
-      // V(k-1) from vb[(k+1)&1] and loads K(k+2) into kb[k&1], V(k) into vb[k&1];
-      // the loop runs the full iterations two at a time so buffers are static.
-      const int64_t packed_bytes = (int64_t)nkt * C::KT * C::D * C::SZ;
-      const __amdgpu_buffer_rsrc_t Kg = buffer_of(A.Kp, packed_bytes);
-      const __amdgpu_buffer_rsrc_t Vg = buffer_of(A.Vt, packed_bytes);
-      uint4 kb[2][C::RUN_U4], vb[2][C::RUN_U4];
-      f32x16 S[C::QB];
-      Frag P[C::QB][C::PSTEPS];
-#pragma unroll
-      for (int i = 0; i < C::RUN_U4; ++i) vb[1][i] = uint4{0, 0, 0, 0};
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
-#pragma unroll
-        for (int ps = 0; ps < C::PSTEPS; ++ps) P[qb][ps] = Frag{};
-      load_run<C>(Kg, 0, hw, lane, kb[0]);
-      load_run<C>(Kg, nkt > 1 ? 1 : 0, hw, lane, kb[1]);
-      {
-        Frag kf[KS], vf_unused[2][PS];
-        as_frags<C>(kb[0], vb[1], kf, vf_unused);
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) S[qb] = s_block<C>(kf, qf[qb]);
-      }
-      int kt = 0;
-      for (; kt + 2 < nkt; kt += 2) {
-        pipe_iter<C, false, false>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, kt + 2, nkeys, hw, lane, qf, nb, S, P, O,
-                                   l_run);
-        const int k3 = kt + 3 < nkt ? kt + 3 : nkt - 1;
-        pipe_iter<C, false, false>(kb[0], vb[0], kb[1], vb[1], Kg, Vg, kt + 1, k3, nkeys, hw, lane, qf, nb, S, P, O,
-                                   l_run);
-      }
-      if (kt + 1 < nkt) {  // one more full iteration (kt even)
-        pipe_iter<C, false, false>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, nkt - 1, nkeys, hw, lane, qf, nb, S, P, O,
-                                   l_run);
-        ++kt;
-      }
-      // the last tile: softmax (masked, in case it is partial) beside P.V of the
-      // previous one, then its own P.V. Its K was consumed by the previous step;
-      // V of the previous tile sits in vb[(kt+1)&1] and moves to vb[1] when kt
-      // is odd, so that a single instance of the step is emitted.
-      if (kt & 1) {
-#pragma unroll
-        for (int i = 0; i < C::RUN_U4; ++i) vb[1][i] = vb[0][i];
-      }
-      pipe_iter<C, true, true>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
-      }
-    attention_done:;
+      if (shift)
+        dense_attention<C, true>(A, nkeys, hw, lane, qf, nb, O, l_run);
+      else
+        dense_attention<C, false>(A, nkeys, hw, lane, qf, nb, O, l_run);
     } else {
-      uint4 rk[C::NCK], rv[C::NCK];
-      tile_load<C, GATHER>(Kg, Vg, sel, nkeys, A.M, 0, tid, rk, rv);
-      tile_store<C, GATHER>(lds, 0, tid, vpos, rk, rv);
-      __syncthreads();
-      for (int kt = 0; kt < nkt; ++kt) {
-        // prefetch the next tile (clamped: the last step reloads its own tile)
-        tile_load<C, GATHER>(Kg, Vg, sel, nkeys, A.M, kt + 1 < nkt ? kt + 1 : kt, tid, rk, rv);
-        const T* Kb = reinterpret_cast<const T*>(lds + (kt & 1) * C::KBYTES);
-        const T* Vb = reinterpret_cast<const T*>(lds + 2 * C::KBYTES + (kt & 1) * C::VBYTES);
-        Frag kf[KS], vf[2][PS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(Kb + 64 * hw + ks * MM::KS, C::DPAD, lane);
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int ps = 0; ps < PS; ++ps)
-            vf[db][ps] = load_frag<T>(Vb + (64 * hw + 32 * db) * C::VPAD + ps * MM::KS, C::VPAD, lane);
-        if ((kt + 1) * C::KT > nkeys)
-          tile_compute<C, true>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
-        else
-          tile_compute<C, false>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
-        // the other buffer was last read before the previous barrier
-        tile_store<C, GATHER>(lds, (kt + 1) & 1, tid, vpos, rk, rv);
-        __syncthreads();
-      }
+      // (both variants pass the same barriers, so waves may take different ones)
+      if (shift)
+        gathered_attention<C, true>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, qf, nb, O, l_run);
+      else
+        gathered_attention<C, false>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, qf, nb, O, l_run);
     }
 
     // ---------------------------------------------------------------- o = sum p v / sum p

@@ -294,10 +294,10 @@ struct EmbedLds {
 // bf16: each feature is split into hi + lo bf16 parts and both are projected, so
 // the fp32 accumulator carries the product with near-fp32 accuracy before the
 // single rounding of Q to bf16.
-// Wq: [D][51]. Ends with a barrier.
+// Wq: [D][51]. Q is multiplied by qscale before its rounding. Ends with a barrier.
 template <typename T, int BQ, int D, int NT>
 __device__ void embed_qproj(const QuerySrc& qs, int64_t q0, int64_t q1, const T* __restrict__ Wq,
-                            char* lds, int tid) {
+                            char* lds, int tid, float qscale = 1.f) {
   using L = EmbedLds<T, BQ, D>;
   using MM = Mma<T>;
   T* e_hi = reinterpret_cast<T*>(lds + L::E_HI);
@@ -357,6 +357,7 @@ __device__ void embed_qproj(const QuerySrc& qs, int64_t q0, int64_t q1, const T*
         if constexpr (L::SPLIT)
           acc = MM::mma(wq[ks], load_frag<T>(e_lo + (32 * cb) * L::EPAD + ks * MM::KS, L::EPAD, lane), acc);
       }
+      acc *= qscale;
       store_ct<T>(Qs + (32 * cb) * L::DPAD + 32 * rb, L::DPAD, acc, lane);
     }
   }

@@ -197,3 +197,39 @@ def test_hier_with_selection_full_workload():
     union = np.sum((vol_np < 0) | (dense_np < 0))
     print(f"[akvs] vs dense at finest decoded points: max|dSDF| {dd.max():.3e} mean {dd.mean():.3e}; "
           f"sign flips over the volume {flips}; occupancy IoU {inter / union:.5f}", flush=True)
+
+
+def test_gathered_decode_mixed_softmax_paths():
+    # head 0 with 16x larger logits: its waves take the shifted softmax, the other
+    # heads' waves in the same workgroups do not, while all pass the per-tile
+    # barriers of the gathered loop together
+    w = W.make(1)
+    weights = dict(w.weights)
+    weights["Wq"] = (w.weights["Wq"] * np.repeat(np.float32([16, 1, 1, 1]), 64)[:, None]).astype(np.float32)
+    dec = gpu_decoder(w, weights=weights)
+    K, Vv = gpu_kv(dec, w)
+    R = 30
+    nb = hv.nblocks(R + 1)
+    sel_idx = torch.empty((nb ** 3, 512), dtype=torch.int32, device=dev())
+    sel_cnt = torch.empty(nb ** 3, dtype=torch.int32, device=dev())
+    V().vdm_select_kv(dec, R, 8, 64, 512, K, None, sel_idx, sel_cnt)
+    lst = hv.blocked_order(np.ones((R + 1,) * 3, bool)).astype(np.int32)
+    out = torch.empty(lst.size, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_list(R, torch.from_numpy(lst).to(dev())), K, Vv, out,
+                         sel=V().kvsel(8, 512, sel_idx, sel_cnt))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    si, sc = sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
+    od = oracle_decoder(w, weights=weights)
+    Kh, Vh = f64(K), f64(Vv)
+    blk = hv.block_of(lst, R + 1)
+    rng = np.random.default_rng(5)
+    worst = 0.0
+    for b in rng.choice(np.unique(blk), 12, replace=False):
+        m = np.nonzero(blk == b)[0][:40]
+        toks = si[b, : sc[b]]
+        ref = od.sdf(odec.grid_points(R, lst[m]), Kh[toks], Vh[toks])
+        worst = max(worst, np.abs(out[m].astype(np.float64) - ref).max())
+    assert np.all(np.isfinite(out))
+    report("gathered decode, mixed softmax paths", worst, TOL_BF16)
+    assert worst <= TOL_BF16

@@ -229,3 +229,47 @@ def test_large_token_set_sampled():
     err = np.abs(out[idx].astype(np.float64) - ref).max()
     report("200K x 40960 sampled", err, TOL_BF16)
     assert err <= TOL_BF16
+
+
+def _head_gain_weights(w, gains):
+    """Wq with the rows of head h multiplied by gains[h] (powers of two, so the
+    bf16 weights stay exact): larger logit bounds for chosen heads."""
+    weights = dict(w.weights)
+    weights["Wq"] = (w.weights["Wq"] * np.repeat(np.asarray(gains, np.float32), 64)[:, None]).astype(np.float32)
+    return weights
+
+
+def _logit_bounds(od, xyz, H):
+    """Per head and query: |q|_2 max_j |k_j|_2 log2(e)/sqrt(64), the bound of the
+    base-2 logits (oracle Q and K)."""
+    q = odec.qproj(odec.embed(xyz), od.W["Wq"], od.dtype)
+    c = np.log2(np.e) / 8
+    return np.stack([np.linalg.norm(q[:, 64 * h:64 * h + 64], axis=1)
+                     * np.linalg.norm(od.K[:, 64 * h:64 * h + 64], axis=1).max() * c for h in range(H)])
+
+
+@pytest.mark.parametrize("gains", [(8, 8, 8, 8), (16, 1, 1, 1)])
+def test_large_logits_shifted_softmax(gains):
+    # Logit bounds above 64 (base 2) make a wave shift its softmax. Gain 8 puts
+    # about a third of the queries of every head above the bound; gain 16 on head 0
+    # alone puts all of that head's waves on the shifted path beside unshifted
+    # waves of the other heads in every workgroup. The tolerance covers rounding q
+    # after the logit scale rather than before it (the oracle rounds q itself):
+    # that placement alone moves the SDF by up to 8.4e-4 at gain 16.
+    w = W.make(1)
+    weights = _head_gain_weights(w, gains)
+    dec = gpu_decoder(w, weights=weights)
+    K, Vv = gpu_kv(dec, w)
+    xyz = W.gen.random_points(11, 3000)
+    od = oracle_decoder(w, weights=weights)
+    B = _logit_bounds(od, xyz, w.H)
+    frac = (B > 64).mean(axis=1)
+    assert frac[0] > 0.2 and (gains[1] > 1 or frac[1:].max() == 0.0), frac
+    sdf = torch.empty(3000, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_points(torch.from_numpy(xyz).to(dev())), K, Vv, sdf)
+    torch.cuda.synchronize()
+    ref = od.sdf(xyz, f64(K), f64(Vv))
+    err = np.abs(f64(sdf) - ref).max()
+    report(f"logit gains {gains} (queries above the bound per head {np.round(frac, 2)})", err, TOL_BF16)
+    assert np.all(np.isfinite(f64(sdf)))
+    assert err <= TOL_BF16
