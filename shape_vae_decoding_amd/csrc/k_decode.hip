@@ -13,20 +13,21 @@
 // column and the P.V product takes P^T straight from the C registers; the
 // packed V^T operand stores tokens in the matching order (perm_key).
 //
-// Softmax with a fixed shift: for query q and head h,
-//   b = log2(e)/8 * ||q_h|| * max_j ||k_hj||  >=  every scaled logit (Cauchy-Schwarz),
-// and p_j = exp2(s_j * log2(e)/8 - b), o = sum_j p_j v_j / sum_j p_j: the softmax
-// is shift-invariant, so this equals the max-subtracted definition in exact
-// arithmetic; p_j <= 1 never overflows, and the shift stays within ~120 of the
-// true maximum for any decoder whose logit norm products stay below ~600, so no
-// significant p_j underflows. No running maximum, no rescaling of O. The row
-// sum is accumulated from the bf16-rounded p_j (dot2 with ones), the same
-// values the P.V product uses.
+// Softmax with a fixed shift: queries are scaled by log2(e)/8 before their
+// rounding, so S holds base-2 logits t. For query q and head h,
+//   B = ||q_h|| * max_j ||k_hj||  >=  |t_j| for every token (Cauchy-Schwarz),
+// and p_j = exp2(t_j + nb), o = sum_j p_j v_j / sum_j p_j with nb = 0 when every
+// query of the wave has B <= 64 (p_j in [2^-64, 2^64]: no overflow, no
+// underflow) and nb = 64 - B otherwise. The softmax is shift-invariant, so this
+// equals the max-subtracted definition in exact arithmetic. No running maximum,
+// no rescaling of O. The row sum is accumulated from the bf16-rounded p_j (dot2
+// with ones), the same values the P.V product uses.
 //
-// Token tiles are staged through LDS once per workgroup (all heads, double
-// buffered, one barrier per 32-token tile) so every K/V byte is fetched once per
-// BQ queries; dense mode copies pre-packed tiles (K rows, per-tile V^T), gathered
-// mode reads the selected tokens' rows and transposes V on the way into LDS.
+// Dense mode: each wave streams its head's pre-packed K and V^T operand runs
+// straight from L2 into registers (no LDS, no barriers in the token loop), in a
+// software pipeline that overlaps the loads, the P.V and S MFMAs and the softmax.
+// Gathered mode reads the selected tokens' rows into an LDS double buffer
+// (V transposed on the way in), one barrier per 32-token tile.
 // The epilogue streams each weight row once per workgroup from L2 with a 4-deep
 // register prefetch ring.
 #include "vdm_device.hpp"
@@ -152,15 +153,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, GFX9_RAW_BUFFER);
 }
 
-// One lane's operand run (32 elements) of packed tile `kt`, head h.
+// One lane's operand run (32 elements) of packed tile `kt`, head h: chunk i of
+// all lanes is a contiguous 1 KB, so each load reads 1 KB without gaps.
 template <typename C>
 __device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t buf, int kt, int h, int lane,
                                          uint4 (&r)[C::RUN_U4]) {
   const int soff = (kt * C::H + h) * 64 * 32 * C::SZ;
-  const int voff = lane * 32 * C::SZ;
+  const int voff = lane * 16;
 #pragma unroll
   for (int i = 0; i < C::RUN_U4; ++i) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(buf, voff + 16 * i, soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(buf, voff + 1024 * i, soff, 0);
     r[i] = uint4{v[0], v[1], v[2], v[3]};
   }
 }

@@ -10,25 +10,31 @@
 namespace vdm {
 
 // ------------------------------------------------------------------ K/V packing
-// The decoder's token loop reads, per 32-token tile t and head h, one contiguous
-// run of 32 elements per lane l (64 lanes): exactly the lane's MFMA operands.
+// The decoder's token loop reads, per 32-token tile t and head h, a run of 32
+// elements per lane l (64 lanes): exactly the lane's MFMA operands.
 //   K run, element e: A operand of S^T = K_h Q_h^T, step ks = e / KW, slot v = e % KW:
 //       K[32t + l%32][64h + KS*ks + KW*(l/32) + v]
 //   V run, element e: A operand of O^T += V_h^T P^T, row block db = e / 16, step
 //       ps = (e % 16) / KW, slot v = e % KW:
 //       V[32t + perm_key(KS*ps + KW*(l/32) + v)][64h + 32db + l%32]
-// Tokens past M are zero.
+// The runs are stored in 16-byte chunks, chunk-major: chunk c of all 64 lanes
+// is one contiguous 1 KB (lane l at byte 16 l), so each 16-byte-per-lane load
+// instruction of the decoder reads a contiguous 1 KB. A lane-major layout (each
+// lane's run contiguous) makes every such load touch 4 KB and halves the
+// vector-memory throughput. Tokens past M are zero.
 
 template <typename T>
 __global__ void pack_kv_kernel(const T* __restrict__ K, const T* __restrict__ V, int M, int D, int Mpad,
                                T* __restrict__ Kp, T* __restrict__ Vt) {
   using MM = Mma<T>;
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (int64_t)Mpad * D;
   if (i >= n) return;
   const int64_t t = i / (32 * D);
   const int rem = (int)(i - t * 32 * D);
-  const int h = rem / 2048, l = (rem % 2048) / 32, e = rem % 32;
+  const int h = rem / 2048, c = (rem % 2048) / (64 * EPC), l = (rem % (64 * EPC)) / EPC;
+  const int e = c * EPC + rem % EPC;
   const int r = l & 31, half = l >> 5;
   {
     const int ks = e / MM::KW, v = e % MM::KW;
