@@ -72,6 +72,8 @@ struct DecCfg {
   static constexpr int LDS_MAIN = LDS_PRE > ATT_END ? LDS_PRE : ATT_END;
   // bf16: GELU table (value, slope) per segment, resident for the whole kernel
   static constexpr bool GELU_TABLE = sizeof(T) == 2;
+  // bf16: Wo, W1, W2 arrive fragment-packed (one contiguous 1 KB per MFMA step)
+  static constexpr bool PACKED_W = sizeof(T) == 2;
   static constexpr int GTAB = LDS_MAIN;
   static constexpr int LDS = LDS_MAIN + (GELU_TABLE ? GELU_SEGS * 8 : 0);
   // epilogue tiling: wave w owns C tiles [w*TPW, (w+1)*TPW) of (D/32) x (BQ/32), rb-major:
@@ -279,17 +281,25 @@ __device__ __forceinline__ void tile_store(char* lds, int buf, int tid, const in
 // acc[r][i] += W[rows 32 r ..][..] x B[columns 32 (cb0 + i) ..]^T for NR consecutive
 // row blocks of W (global memory, each through a RING-deep register prefetch ring)
 // and NC column blocks of B (LDS, read one step ahead, each fragment used NR times).
-template <typename T, int NKS, int NR, int NC, int RING = 4>
+template <typename T, int NKS, int NR, int NC, bool PACKED, int RING = 4>
 __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, const T* B, int ldb, int cb0,
                                           f32x16 (&acc)[NR][NC], int lane) {
   using MM = Mma<T>;
   using Frag = typename MM::frag;
+  // A fragment of row block r, step ks. Row-major W: rows of ldw elements from the
+  // block's first row; packed W: 32 x KS blocks of ldw / KS steps per row block.
+  auto wfrag = [&](int r, int ks) -> Frag {
+    if constexpr (PACKED)
+      return *reinterpret_cast<const Frag*>(W + ((int64_t)r * (ldw / MM::KS) + ks) * (32 * MM::KS) + lane * MM::KW);
+    else
+      return load_frag<T>(W + (int64_t)(32 * r) * ldw + ks * MM::KS, ldw, lane);
+  };
   constexpr int PF = NKS < RING ? NKS : RING;
   Frag ring[NR][PF];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int p = 0; p < PF; ++p) ring[r][p] = load_frag<T>(W + (int64_t)(32 * r) * ldw + p * MM::KS, ldw, lane);
+    for (int p = 0; p < PF; ++p) ring[r][p] = wfrag(r, p);
   Frag b[2][NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) b[0][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb, ldb, lane);
@@ -299,7 +309,7 @@ __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, cons
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       a[r] = ring[r][ks % PF];
-      if (ks + PF < NKS) ring[r][ks % PF] = load_frag<T>(W + (int64_t)(32 * r) * ldw + (ks + PF) * MM::KS, ldw, lane);
+      if (ks + PF < NKS) ring[r][ks % PF] = wfrag(r, ks + PF);
     }
     if (ks + 1 < NKS) {
 #pragma unroll
@@ -311,6 +321,17 @@ __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, cons
 #pragma unroll
       for (int i = 0; i < NC; ++i) acc[r][i] = MM::mma(a[r], b[ks & 1][i], acc[r][i]);
   }
+}
+
+// Start of row block rb, k-step ks of an epilogue weight with rows of `cols`
+// elements, in the form gemm_rows<..., PACKED> reads.
+template <typename C>
+__device__ __forceinline__ const typename C::T* wblock(const typename C::T* W, int rb, int ks, int cols) {
+  constexpr int KS = Mma<typename C::T>::KS;
+  if constexpr (C::PACKED_W)
+    return W + ((int64_t)rb * (cols / KS) + ks) * (32 * KS);
+  else
+    return W + (int64_t)(32 * rb) * cols + ks * KS;
 }
 
 // One 32-token tile for all of this wave's query blocks: S^T of the next query
@@ -686,7 +707,8 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     for (int r = 0; r < C::RPW; ++r)
 #pragma unroll
       for (int i = 0; i < C::CPW; ++i) Y[r][i] = zero16();
-    gemm_rows<T, C::D / MM::KS, C::RPW, C::CPW>(Wo + (32 * rb0) * C::D, C::D, Ob, C::DPAD, cb0, Y, lane);
+    gemm_rows<T, C::D / MM::KS, C::RPW, C::CPW, C::PACKED_W>(wblock<C>(Wo, rb0, 0, C::D), C::D, Ob, C::DPAD, cb0, Y,
+                                                             lane);
     T* Ab = reinterpret_cast<T*>(lds + C::ABUF);
 #pragma unroll
     for (int r = 0; r < C::RPW; ++r)
@@ -705,8 +727,8 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       for (int r = 0; r < C::RPH; ++r)
 #pragma unroll
         for (int j = 0; j < C::CPH; ++j) Hc[r][j] = zero16();
-      gemm_rows<T, C::D / MM::KS, C::RPH, C::CPH>(W1 + (int64_t)(f0 + 32 * rh0) * C::D, C::D, Ab, C::DPAD, ch0, Hc,
-                                                  lane);
+      gemm_rows<T, C::D / MM::KS, C::RPH, C::CPH, C::PACKED_W>(wblock<C>(W1, f0 / 32 + rh0, 0, C::D), C::D, Ab,
+                                                               C::DPAD, ch0, Hc, lane);
 #pragma unroll
       for (int r = 0; r < C::RPH; ++r)
 #pragma unroll
@@ -715,8 +737,8 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
           store_ct<T>(Hb + (32 * (ch0 + j)) * C::HPAD + 32 * (rh0 + r), C::HPAD, Hc[r][j], lane);
         }
       __syncthreads();
-      gemm_rows<T, C::FC / MM::KS, C::RPW, C::CPW>(W2 + (int64_t)(32 * rb0) * A.F + f0, A.F, Hb, C::HPAD, cb0, Y,
-                                                   lane);
+      gemm_rows<T, C::FC / MM::KS, C::RPW, C::CPW, C::PACKED_W>(wblock<C>(W2, rb0, f0 / MM::KS, A.F), A.F, Hb,
+                                                                C::HPAD, cb0, Y, lane);
       __syncthreads();
     }
 

@@ -48,6 +48,29 @@ __global__ void pack_kv_kernel(const T* __restrict__ K, const T* __restrict__ V,
   }
 }
 
+// ------------------------------------------------------------------ weight packing
+// The decoder epilogue's A operands (rows of Wo, W1, W2) as contiguous 1 KB
+// fragment blocks: one 16-byte-per-lane load per MFMA step (bf16 only).
+__global__ void pack_w_kernel(const bf16* __restrict__ W, int rows, int cols, bf16* __restrict__ Wp) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 16-byte chunk
+  const int64_t n = (int64_t)rows * cols / 8;
+  if (c >= n) return;
+  const int nks = cols / 16;
+  const int l = (int)(c % 64);
+  const int64_t blk = c / 64;
+  const int rb = (int)(blk / nks), ks = (int)(blk % nks);
+  const int64_t src = (int64_t)(32 * rb + (l & 31)) * cols + 16 * ks + 8 * (l >> 5);
+  reinterpret_cast<uint4*>(Wp)[c] = *reinterpret_cast<const uint4*>(W + src);
+}
+
+hipError_t launch_pack_w(const void* W, int rows, int cols, void* Wp, hipStream_t s) {
+  const int64_t n = (int64_t)rows * cols / 8;
+  const int bs = 256;
+  hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)((n + bs - 1) / bs)), dim3(bs), 0, s, (const bf16*)W, rows, cols,
+                     (bf16*)Wp);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D, int Mpad, void* Kp,
                           void* Vt, hipStream_t s) {
   const int64_t n = (int64_t)Mpad * D;

@@ -187,10 +187,29 @@ static DecodeArgs base_args(const vdm_decoder* d) {
 
 static int64_t mpad(int64_t M) { return (M + 31) / 32 * 32; }
 
+// bf16 decoders stream Wo, W1, W2 in fragment-packed form from the workspace
+static size_t packed_w_bytes(const vdm_decoder* d) {
+  return d->dtype == VDM_BF16 ? ((size_t)d->D * d->D + 2 * (size_t)d->D * d->F) * 2 : 0;
+}
+
+static hipError_t pack_weights(const vdm_decoder* d, void* Wp, DecodeArgs& a, hipStream_t s) {
+  if (d->dtype != VDM_BF16) return hipSuccess;
+  char* p = static_cast<char*>(Wp);
+  const size_t DD = (size_t)d->D * d->D * 2, DF = (size_t)d->D * d->F * 2;
+  hipError_t e = launch_pack_w(d->Wo, d->D, d->D, p, s);
+  if (e == hipSuccess) e = launch_pack_w(d->W1, d->F, d->D, p + DD, s);
+  if (e == hipSuccess) e = launch_pack_w(d->W2, d->D, d->F, p + DD + DF, s);
+  a.Wo = p;
+  a.W1 = p + DD;
+  a.W2 = p + DD + DF;
+  return e;
+}
+
 // ------------------------------------------------------------------ dense workspace
 struct DenseWs {
   void* Kp;
   void* Vt;
+  void* Wp;
   float* kmax;
   Item* items;
   int32_t* n_items;
@@ -202,6 +221,7 @@ static size_t dense_ws(const vdm_decoder* d, int64_t M, int64_t N, bool sel, voi
   const size_t kv = (size_t)mpad(M) * d->D * esize(d->dtype);
   x.Kp = sel ? nullptr : c.take<char>(kv);
   x.Vt = sel ? nullptr : c.take<char>(kv);
+  x.Wp = c.take<char>(packed_w_bytes(d));
   x.kmax = c.take<float>(256);
   x.items = sel ? c.take<Item>((size_t)(N > 0 ? N : 1) * sizeof(Item)) : nullptr;
   x.n_items = sel ? c.take<int32_t>(256) : nullptr;
@@ -213,6 +233,7 @@ static size_t dense_ws(const vdm_decoder* d, int64_t M, int64_t N, bool sel, voi
 struct HierWs {
   void* Kp;
   void* Vt;
+  void* Wp;
   float* kmax;
   float* vol[VDM_MAX_LEVELS];
   uint64_t* active[VDM_MAX_LEVELS];
@@ -241,6 +262,7 @@ static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M,
   const size_t kv = (size_t)mpad(M) * d->D * esize(d->dtype);
   x.Kp = c.take<char>(kv);
   x.Vt = c.take<char>(kv);
+  x.Wp = c.take<char>(packed_w_bytes(d));
   x.kmax = c.take<float>(256);
   int64_t maxP3 = 0, maxNB3 = 0, maxWords = 0;
   for (int L = 0; L < p->levels; ++L) {
@@ -426,6 +448,7 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
   a.kmax = w.kmax;
   VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
   VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
+  VDM_HIP(pack_weights(dec, w.Wp, a, s), "weight packing launch");
   if (!sel) {
     VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
     a.Kp = w.Kp;
@@ -517,6 +540,8 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
   VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
   VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
   if (!kv) VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
+  DecodeArgs packed = base_args(dec);
+  VDM_HIP(pack_weights(dec, w.Wp, packed, s), "weight packing launch");
 
   auto vol_of = [&](int L) { return L == p->levels - 1 ? vol : w.vol[L]; };
   // list, items and occupied blocks of level L are in w.list / w.items / w.occ
@@ -544,7 +569,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       sa.scores = w.sel_scores;
       VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, sa, s), "select launch");
     }
-    DecodeArgs a = base_args(dec);
+    DecodeArgs a = packed;
     a.qs = QuerySrc{VDM_Q_GRID_LIST, R, nullptr, w.list, 0};
     a.kmax = w.kmax;
     a.out = vol_of(L);

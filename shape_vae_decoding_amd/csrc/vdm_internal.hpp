@@ -43,10 +43,11 @@ struct DecodeArgs {
   QuerySrc qs;
   int64_t N;            // number of queries (dense tiles)
   const void* Wq;       // [D][51]
-  const void* Kp;       // dense: packed K tiles [Mpad/32][H][64 lanes][32]; gathered: K [M][D]
-  const void* Vt;       // dense: packed V^T tiles [Mpad/32][H][64 lanes][32]; gathered: V [M][D]
+  const void* Kp;       // dense: packed K tiles [Mpad/32][H][chunk][64 lanes][16 B]; gathered: K [M][D]
+  const void* Vt;       // dense: packed V^T tiles [Mpad/32][H][chunk][64 lanes][16 B]; gathered: V [M][D]
   const float* kmax;    // [H] max over tokens of ||k_h|| (softmax shift bound)
   int M;                // tokens (dense)
+  // bf16: fragment-packed copies (launch_pack_w); fp32: the row-major weights
   const void* Wo;
   const void* W1;
   const void* W2;
@@ -78,9 +79,14 @@ DevInfo dev_info();
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 
-// K, V [M][D] -> per-(32-token tile, head) operand runs of 64 lanes x 32 elements (see k_prep.hip)
+// K, V [M][D] -> per-(32-token tile, head) operand runs of 64 lanes x 32 elements,
+// stored chunk-major (see k_prep.hip)
 hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D, int Mpad, void* Kp,
                           void* Vt, hipStream_t s);
+// bf16 W [rows][cols] -> MFMA A-operand fragments: block (rb, ks) of 32 rows x 16
+// columns is 64 lanes x 8 elements, lane l holding W[32rb + l%32][16ks + 8(l/32) + 0..7];
+// blocks in (rb, ks) order. rows % 32 == 0, cols % 16 == 0.
+hipError_t launch_pack_w(const void* W, int rows, int cols, void* Wp, hipStream_t s);
 // kmax[h] = max_m ||K[m][64h .. 64h+63]||_2 (kmax must be zeroed first)
 hipError_t launch_key_norms(int dtype, const void* K, int M, int H, float* kmax, hipStream_t s);
 // K = Z Wk^T, V = Z Wv^T
