@@ -41,7 +41,7 @@ __global__ void pack_kv_kernel(const T* __restrict__ K, const T* __restrict__ V,
     const int64_t m = 32 * t + r;
     Kp[i] = m < M ? K[m * D + 64 * h + MM::KS * ks + MM::KW * half + v] : to_t<T>(0.f);
   }
-  {
+  if (Vt) {
     const int db = e / 16, f = e % 16, ps = f / MM::KW, v = f % MM::KW;
     const int64_t m = 32 * t + perm_key<T>(MM::KS * ps + MM::KW * half + v);
     Vt[i] = m < M ? V[m * D + 64 * h + 32 * db + r] : to_t<T>(0.f);

@@ -105,6 +105,42 @@ __device__ __forceinline__ void load_scores(__amdgpu_buffer_rsrc_t buf, int row,
   }
 }
 
+// K fragments of key tile kb for every head (A operands of S^T = K Q^T). bf16:
+// from the packed tiles, each load one contiguous 1 KB (chunk ks of head h);
+// fp32: from the rows of K (keys past M clamped; their logits are masked).
+template <typename T, int H>
+struct KTile {
+  using Frag = typename Mma<T>::frag;
+  static constexpr int KS_H = 64 / Mma<T>::KS;
+  Frag f[H][KS_H];
+};
+
+template <typename T, int H>
+__device__ __forceinline__ void load_ktile(const SelectArgs& A, __amdgpu_buffer_rsrc_t kbuf, int kb, int lane,
+                                           KTile<T, H>& t) {
+  using MM = Mma<T>;
+  using Frag = typename MM::frag;
+  constexpr int KS_H = KTile<T, H>::KS_H;
+  if constexpr (sizeof(T) == 2) {
+    static_assert(KS_H * 16 == 32 * (int)sizeof(T), "one 16-byte chunk of the packed run per MFMA step");
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int ks = 0; ks < KS_H; ++ks) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(kbuf, lane * 16, ((kb * H + h) * KS_H + ks) * 1024, 0);
+        const uint4 u{v[0], v[1], v[2], v[3]};
+        t.f[h][ks] = *reinterpret_cast<const Frag*>(&u);
+      }
+  } else {
+    const int key = min(kb * 32 + (lane & 31), A.M - 1);
+    const T* krow = (const T*)A.K + (int64_t)key * (64 * H) + MM::KW * (lane >> 5);
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int ks = 0; ks < KS_H; ++ks) t.f[h][ks] = *reinterpret_cast<const Frag*>(krow + 64 * h + ks * MM::KS);
+  }
+}
+
 template <typename T, int H>
 __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   extern __shared__ __align__(16) char lds[];
@@ -113,8 +149,8 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   using L = EmbedLds<T, SEL_BQ, 64 * H>;
   using CF = SelCfg<T, H>;
   constexpr int D = 64 * H, KS_H = 64 / MM::KS;
-  const int tid = threadIdx.x, lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid0 = threadIdx.x, lane0 = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const int M = A.M, Mp = sel_mpad(M);
   const int nwords = (M + 31) / 32;
   float2* stats = reinterpret_cast<float2*>(lds + CF::STATS);     // [NW][H][32]
@@ -126,7 +162,9 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       __builtin_amdgcn_make_buffer_rsrc(scores, (short)0, SEL_BQ * Mp * 4, 0x00020000 /* raw buffer */);
   const int64_t nblk = A.d_n_blocks ? (int64_t)*A.d_n_blocks : A.n_blocks;
   const int64_t ngroups = (nblk + SEL_GB - 1) / SEL_GB;
-  const T* __restrict__ K = (const T*)A.K;
+  const __amdgpu_buffer_rsrc_t kbuf =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(A.Kp), (short)0, sizeof(T) == 2 ? (M + 31) / 32 * 32 * D * 2 : 0,
+                                        0x00020000 /* raw buffer */);
   QuerySrc qs;
   qs.mode = 3;
   qs.R = A.R;
@@ -136,14 +174,32 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   const int nkb = (M + 31) / 32;
   const int per = (nkb + SEL_NW - 1) / SEL_NW;
   const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
-  const int col = lane & 31;  // this lane's probe (MFMA column)
   const float NEG = -__builtin_inff();
 
   for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
     const int64_t row0 = grp * SEL_GB;
     const int nb = (int)min<int64_t>(SEL_GB, nblk - row0);
+    // thread and lane indices re-derived opaquely per phase, so the address
+    // arithmetic of a phase is not hoisted out of the group loop (and kept live
+    // across the other phases)
+    int tid = opaque(tid0), lane = opaque(lane0);
+    int col = lane & 31;  // this lane's probe (MFMA column)
     embed_qproj<T, SEL_BQ, D, SEL_NT>(qs, row0 * SEL_NP, (row0 + nb) * SEL_NP, (const T*)A.Wq, lds, tid);
     const T* qrow = reinterpret_cast<const T*>(lds + L::QS) + col * L::DPAD + MM::KW * (lane >> 5);
+    // this wave's key tiles kb0 .. kb1-1, two at a time with static fragment buffers
+    auto over_key_tiles = [&](auto&& work) {
+      if (kb0 >= kb1) return;
+      KTile<T, H> ta, tb;
+      load_ktile<T, H>(A, kbuf, kb0, lane, ta);
+      int kb = kb0;
+      for (; kb + 1 < kb1; kb += 2) {
+        load_ktile<T, H>(A, kbuf, kb + 1, lane, tb);
+        work(ta, kb);
+        load_ktile<T, H>(A, kbuf, kb + 2 < kb1 ? kb + 2 : kb1 - 1, lane, ta);
+        work(tb, kb + 1);
+      }
+      if (kb < kb1) work(ta, kb);
+    };
 
     // ---------------------------------------------------------------- pass 1: softmax statistics
     float m[H], l[H];
@@ -152,33 +208,32 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       m[h] = NEG;
       l[h] = 0.f;
     }
-    for (int kb = kb0; kb < kb1; ++kb) {
-      const int key = min(kb * 32 + (lane & 31), M - 1);
-      const T* krow = K + (int64_t)key * D + MM::KW * (lane >> 5);
+    // (key tiles in pairs, the next tile's fragments loaded beside the current one's work)
+    auto stats_tile = [&](const KTile<T, H>& t, int kb) {
 #pragma unroll
       for (int h = 0; h < H; ++h) {
         f32x16 S = zero16();
 #pragma unroll
         for (int ks = 0; ks < KS_H; ++ks)
-          S = MM::mma(*reinterpret_cast<const Frag*>(krow + 64 * h + ks * MM::KS),
-                      *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
+          S = MM::mma(t.f[h][ks], *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
         float mx = NEG;
-        float t[16];
+        float tt[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          t[r] = kb * 32 + crow(r, lane) < M ? S[r] * 0.18033688011112042f : NEG;
-          mx = fmaxf(mx, t[r]);
+          tt[r] = kb * 32 + crow(r, lane) < M ? S[r] * 0.18033688011112042f : NEG;
+          mx = fmaxf(mx, tt[r]);
         }
         const float mnew = fmaxf(m[h], mx);
         if (mnew != NEG) {
           float sum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(t[r] - mnew);
+          for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(tt[r] - mnew);
           l[h] = l[h] * __builtin_amdgcn_exp2f(m[h] - mnew) + sum;
           m[h] = mnew;
         }
       }
-    }
+    };
+    over_key_tiles(stats_tile);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       const float mo = __shfl_xor(m[h], 32), lo = __shfl_xor(l[h], 32);
@@ -208,9 +263,9 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
     }
 
     // ---------------------------------------------------------------- pass 2: head-mean probabilities
-    for (int kb = kb0; kb < kb1; ++kb) {
-      const int key = min(kb * 32 + (lane & 31), M - 1);
-      const T* krow = K + (int64_t)key * D + MM::KW * (lane >> 5);
+    lane = opaque(lane);
+    col = lane & 31;
+    auto score_tile = [&](const KTile<T, H>& t, int kb) {
       float acc[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -219,8 +274,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         f32x16 S = zero16();
 #pragma unroll
         for (int ks = 0; ks < KS_H; ++ks)
-          S = MM::mma(*reinterpret_cast<const Frag*>(krow + 64 * h + ks * MM::KS),
-                      *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
+          S = MM::mma(t.f[h][ks], *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           acc[r] += __builtin_amdgcn_exp2f(S[r] * 0.18033688011112042f - mf[h]) * linv[h];
@@ -232,10 +286,13 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
           if (j < M) scores[col * Mp + j] = acc[r] * (1.f / H);
         }
       }
-    }
+    };
+    over_key_tiles(score_tile);
     __syncthreads();  // the scores rows are complete and visible to the workgroup
 
     // ---------------------------------------------------------------- top-k per probe, union per block
+    tid = opaque(tid);
+    lane = opaque(lane);
     for (int p = wave; p < nb * SEL_NP; p += SEL_NW) {
       unsigned u[SEL_MAXV];
       load_scores(sbuf, p, Mp, M, lane, u);
@@ -244,6 +301,8 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
     __syncthreads();
 
     // ---------------------------------------------------------------- cap, compaction (one wave per block)
+    tid = opaque(tid);
+    lane = opaque(lane);
     if (wave < nb) {
       const int blk = wave;
       unsigned* ub = bits + blk * nwords;

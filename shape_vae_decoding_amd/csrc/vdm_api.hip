@@ -187,6 +187,12 @@ static DecodeArgs base_args(const vdm_decoder* d) {
 
 static int64_t mpad(int64_t M) { return (M + 31) / 32 * 32; }
 
+// KV selection scratch: per-workgroup score rows, then (bf16) the packed K
+static size_t select_ws_bytes(const vdm_decoder* d, int64_t M) {
+  const size_t kp = d->dtype == VDM_BF16 ? (size_t)mpad(M) * d->D * 2 : 0;
+  return (select_scratch_bytes((int)M) + 255) / 256 * 256 + kp + 256;
+}
+
 // bf16 decoders stream Wo, W1, W2 in fragment-packed form from the workspace
 static size_t packed_w_bytes(const vdm_decoder* d) {
   return d->dtype == VDM_BF16 ? ((size_t)d->D * d->D + 2 * (size_t)d->D * d->F) * 2 : 0;
@@ -374,7 +380,7 @@ size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M) {
     fail(VDM_ERR_INVALID_ARG, "M=%lld (1..4096)", (long long)M);
     return 0;
   }
-  return select_scratch_bytes((int)M) + 256;
+  return select_ws_bytes(dec, M);
 }
 
 size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M) {
@@ -488,9 +494,14 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
     return fail(VDM_ERR_INVALID_ARG, "nblk=%lld (all blocks: %lld)", (long long)nblk, (long long)(NB * NB * NB));
   if (nblk == 0) return VDM_OK;
   if (!K || !sel_idx || !sel_cnt || !aligned(K, 16)) return fail(VDM_ERR_INVALID_ARG, "K, sel_idx or sel_cnt NULL/misaligned");
-  const size_t need = select_scratch_bytes((int)M) + 256;
+  const size_t need = select_ws_bytes(dec, M);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(VDM_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  char* kp = static_cast<char*>(ws) + (select_scratch_bytes((int)M) + 255) / 256 * 256;
+  if (dec->dtype == VDM_BF16)
+    VDM_HIP(launch_pack_kv(dec->dtype, K, nullptr, (int)M, dec->D, (int)mpad(M), kp, nullptr, s), "pack K launch");
   SelectArgs a;
   memset(&a, 0, sizeof a);
   a.R = R;
@@ -502,13 +513,13 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
   a.D = dec->D;
   a.Wq = dec->Wq;
   a.K = K;
+  a.Kp = kp;
   a.blocks = blocks;
   a.n_blocks = nblk;
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
   a.scores = (float*)ws;
-  (void)hipGetLastError();
-  VDM_HIP_T(VDM_TIME_SELECT, (hipStream_t)stream, launch_select(dec->dtype, a, (hipStream_t)stream), "select launch");
+  VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, a, s), "select launch");
   return VDM_OK;
 }
 
@@ -539,7 +550,10 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
   VDM_HIP(launch_zero(w.part, (size_t)stat_part_words() * 8, s), "zero launch");
   VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
   VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
-  if (!kv) VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
+  if (!kv)
+    VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
+  else if (dec->dtype == VDM_BF16)  // the selection streams packed K
+    VDM_HIP(launch_pack_kv(dec->dtype, K, nullptr, (int)M, dec->D, (int)mpad(M), w.Kp, nullptr, s), "pack K launch");
   DecodeArgs packed = base_args(dec);
   VDM_HIP(pack_weights(dec, w.Wp, packed, s), "weight packing launch");
 
@@ -560,6 +574,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       sa.D = dec->D;
       sa.Wq = dec->Wq;
       sa.K = K;
+      sa.Kp = w.Kp;
       sa.blocks = w.occ;
       sa.n_blocks = 0;
       sa.d_n_blocks = tot + 2;

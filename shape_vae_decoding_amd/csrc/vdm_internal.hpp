@@ -80,7 +80,7 @@ DevInfo dev_info();
 // Each returns hipSuccess or the launch error.
 
 // K, V [M][D] -> per-(32-token tile, head) operand runs of 64 lanes x 32 elements,
-// stored chunk-major (see k_prep.hip)
+// stored chunk-major (see k_prep.hip); V and Vt may be null (K only)
 hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D, int Mpad, void* Kp,
                           void* Vt, hipStream_t s);
 // bf16 W [rows][cols] -> MFMA A-operand fragments: block (rb, ks) of 32 rows x 16
@@ -104,7 +104,8 @@ int decode_f_chunk(int dtype, int D);
 struct SelectArgs {
   int R, block, k, cap, M, H, D;
   const void* Wq;  // [D][51]
-  const void* K;  // [M][D]
+  const void* K;   // [M][D]
+  const void* Kp;  // bf16: K packed like the dense decoder's tiles (launch_pack_kv), else unused
   const int32_t* blocks;
   int64_t n_blocks;
   const int32_t* d_n_blocks;
