@@ -58,9 +58,13 @@ struct DecCfg {
   static constexpr int PSTEPS = KT / Mma<T>::KS;   // MFMA steps over one 32-token tile
   // per-lane operand run of one (tile, head): 32 elements of K and 32 of V^T
   static constexpr int RUN_U4 = 32 * SZ / 16;
-  // gathered-mode staging: two K tiles [KT][DPAD] and two V^T tiles [D][VPAD]
+  // gathered-mode staging: two K tiles [KT][DPAD] and two V tiles, row-major
+  // [KT][VROW] for 16-bit types (read transposed by ds_read_b64_tr_b16; rows of
+  // D + 32 elements put the 4 rows of one read 16 banks apart) or V^T [D][VPAD]
+  static constexpr bool TR_V = SZ == 2;
+  static constexpr int VROW = D + 32;
   static constexpr int KBYTES = KT * DPAD * SZ;
-  static constexpr int VBYTES = D * VPAD * SZ;
+  static constexpr int VBYTES = TR_V ? KT * VROW * SZ : D * VPAD * SZ;
   static constexpr int ATT_END = 2 * (KBYTES + VBYTES);
   // epilogue: O [BQ][DPAD] (later the GELU chunk [BQ][HPAD]), a [BQ][DPAD], reduction
   static constexpr int OBUF = 0;
@@ -252,7 +256,8 @@ __device__ __forceinline__ void tile_load(const typename C::T* __restrict__ Kg, 
   }
 }
 
-// Registers -> LDS buffer `buf`: K rows [KT][DPAD]; V^T [D][VPAD] in perm_key token
+// Registers -> LDS buffer `buf`: K rows [KT][DPAD]; gathered 16-bit V rows [KT][VROW];
+// otherwise V^T [D][VPAD] in perm_key token
 // order (dense: already packed that way; gathered: each thread's 16-byte run of
 // one token's V row goes to column vpos of V^T).
 template <typename C, bool GATHER>
@@ -269,6 +274,8 @@ __device__ __forceinline__ void tile_store(char* lds, int buf, int tid, const in
     *reinterpret_cast<uint4*>(Kb + (c / CPR) * C::DPAD + (c % CPR) * C::EPC) = rk[i];
     if constexpr (!GATHER) {
       *reinterpret_cast<uint4*>(Vb + (c / VCPR) * C::VPAD + (c % VCPR) * C::EPC) = rv[i];
+    } else if constexpr (C::TR_V) {
+      *reinterpret_cast<uint4*>(Vb + (c / CPR) * C::VROW + (c % CPR) * C::EPC) = rv[i];
     } else {
       const int e = (c % CPR) * C::EPC;
       const T* v = reinterpret_cast<const T*>(&rv[i]);
@@ -534,6 +541,29 @@ __device__ __forceinline__ void dense_attention(const DecodeArgs& A, int nkeys, 
   pipe_iter<C, true, true, SHIFT>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
 }
 
+// V^T fragment (A operand of O^T += V^T P^T) for dims d0 .. d0+31 and MFMA step
+// ps, read from row-major V [KT][VROW] in LDS with two transposing reads. Within
+// each 16-lane group, ds_read_b64_tr_b16 gives lane i element i%4 of the 8-byte
+// blocks of lanes i/4 + 4j (j = 0..3). Source lane s of group g points at row
+// t0 + s/4, columns d0 + 16(g%2) + 4(s%4) .. +3, so lane i of the group receives
+// V[t0 + j][d0 + 16(g%2) + i], j = 0..3: rows are dims, keys run along k. With
+// t0 = 16 ps + 4(g/2) (+8 for the second read) the k slots of lane l hold keys
+// 16 ps + 8(v/4) + 4(l/32) + v%4, the order in which the C layout of S^T hands
+// P^T to the B operand.
+template <typename C>
+__device__ __forceinline__ typename Mma<typename C::T>::frag vt_frag_tr(const typename C::T* Vb, int d0, int ps,
+                                                                        int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int g = lane >> 4, s = lane & 15;
+  const int t0 = 16 * ps + 4 * (g >> 1) + (s >> 2);
+  const typename C::T* p = Vb + t0 * C::VROW + d0 + 16 * (g & 1) + 4 * (s & 3);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 8 * C::VROW));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return *reinterpret_cast<const typename Mma<typename C::T>::frag*>(&ab);
+}
+
 // Attention over one block's selected token set: 32-token tiles gathered into
 // an LDS double buffer (V transposed on the way in), one barrier per tile.
 template <typename C, bool SHIFT>
@@ -563,8 +593,12 @@ __device__ __forceinline__ void gathered_attention(const typename C::T* __restri
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int ps = 0; ps < C::PSTEPS; ++ps)
-        vf[db][ps] = load_frag<T>(Vb + (64 * hw + 32 * db) * C::VPAD + ps * MM::KS, C::VPAD, lane);
+      for (int ps = 0; ps < C::PSTEPS; ++ps) {
+        if constexpr (C::TR_V)
+          vf[db][ps] = vt_frag_tr<C>(Vb, 64 * hw + 32 * db, ps, lane);
+        else
+          vf[db][ps] = load_frag<T>(Vb + (64 * hw + 32 * db) * C::VPAD + ps * MM::KS, C::VPAD, lane);
+      }
     if ((kt + 1) * C::KT > nkeys)
       tile_compute<C, true, SHIFT>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
     else
