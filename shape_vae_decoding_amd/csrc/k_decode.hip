@@ -109,35 +109,37 @@ struct DecCfg {
 // GELU by table for bf16 decoders: GELU_SEGS linear segments over [-GELU_LIM, GELU_LIM]
 // (width 1/128), each stored as (GELU(x_i), GELU(x_{i+1}) - GELU(x_i)); interpolation
 // error <= h^2/8 max|GELU''| < 7e-6, far below the bf16 rounding of the hidden
-// activations. Beyond the range GELU(x) = x (x > 8; the difference is below 1e-14)
-// or GELU(-8) (x < -8, |value| < 1e-14).
+// activations. The first segment is flat at GELU(-8) (|GELU| < 6e-15 there). Past
+// the range the end segments extrapolate: x > 8 continues the last segment, whose
+// slope is 1 to within 1e-14, so the value is x to within 1e-14 (as GELU is);
+// x < -8 stays at GELU(-8). NaN gives NaN; -inf gives NaN.
 
 __device__ __forceinline__ void gelu_table_fill(float2* tab, int tid, int nt) {
   for (int i = tid; i < GELU_SEGS; i += nt) {
     const float x0 = -GELU_LIM + (float)i / GELU_SCALE, x1 = -GELU_LIM + (float)(i + 1) / GELU_SCALE;
     const float g0 = gelu(x0);
-    tab[i] = make_float2(g0, gelu(x1) - g0);
+    tab[i] = make_float2(g0, i == 0 ? 0.f : gelu(x1) - g0);
   }
 }
 
-// GELU of the 16 values of one C tile; all 16 table reads are issued before the
-// first is used, so their LDS latency overlaps.
+// GELU of the 16 values of one C tile, branch-free: the segment index is clamped
+// into the table, the offset within it is not (so the end segments extrapolate).
+// All 16 table reads are issued before the first is used, so their LDS latency
+// overlaps.
 template <typename C>
 __device__ __forceinline__ void gelu_tile(f32x16& h, const float2* tab) {
   if constexpr (C::GELU_TABLE) {
     float t[16];
+    int seg[16];
     float2 e[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      t[r] = __builtin_amdgcn_fmed3f(__builtin_fmaf(h[r], GELU_SCALE, GELU_LIM * GELU_SCALE), 0.f,
-                                     (float)GELU_SEGS - 0.001f);
-      e[r] = tab[(int)t[r]];
+      t[r] = __builtin_fmaf(h[r], GELU_SCALE, GELU_LIM * GELU_SCALE);
+      seg[r] = (int)__builtin_amdgcn_fmed3f(t[r], 0.f, (float)GELU_SEGS - 0.5f);
+      e[r] = tab[seg[r]];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float g = __builtin_fmaf(e[r].y, t[r] - (float)(int)t[r], e[r].x);
-      h[r] = !(h[r] <= GELU_LIM) ? h[r] : g;  // also passes NaN through
-    }
+    for (int r = 0; r < 16; ++r) h[r] = __builtin_fmaf(e[r].y, t[r] - (float)seg[r], e[r].x);
   } else {
 #pragma unroll
     for (int r = 0; r < 16; ++r) h[r] = gelu(h[r]);
@@ -288,9 +290,14 @@ __device__ __forceinline__ void tile_store(char* lds, int buf, int tid, const in
 // acc[r][i] += W[rows 32 r ..][..] x B[columns 32 (cb0 + i) ..]^T for NR consecutive
 // row blocks of W (global memory, each through a RING-deep register prefetch ring)
 // and NC column blocks of B (LDS, read one step ahead, each fragment used NR times).
-template <typename T, int NKS, int NR, int NC, bool PACKED, int RING = 4>
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// (hook(ks) runs after the MFMAs of step ks: independent work to interleave)
+template <typename T, int NKS, int NR, int NC, bool PACKED, int RING = 4, typename Hook = NoHook>
 __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, const T* B, int ldb, int cb0,
-                                          f32x16 (&acc)[NR][NC], int lane) {
+                                          f32x16 (&acc)[NR][NC], int lane, Hook&& hook = Hook{}) {
   using MM = Mma<T>;
   using Frag = typename MM::frag;
   // A fragment of row block r, step ks. Row-major W: rows of ldw elements from the
@@ -327,6 +334,10 @@ __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, cons
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int i = 0; i < NC; ++i) acc[r][i] = MM::mma(a[r], b[ks & 1][i], acc[r][i]);
+    hook(ks);
+    // with a hook, keep each step's loads and hooked work in their step (bounds
+    // the live registers of the interleaved work)
+    if constexpr (!std::is_same<typename std::decay<Hook>::type, NoHook>::value) __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -87,19 +87,27 @@ hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D,
 
 // kmax[h] = max over tokens of the Euclidean norm of head h's 64 key columns
 // (float32; norms are non-negative, so their bit patterns order like integers).
+// Thread i takes token i / H, head i % H (16-byte loads); the lanes of a wave that
+// share a head reduce first, so each wave issues H atomics. H divides 64.
 template <typename T>
 __global__ void key_norms_kernel(const T* __restrict__ K, int M, int H, float* kmax) {
+  constexpr int EPC = 16 / (int)sizeof(T);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)M * H) return;
-  const int64_t m = i / H;
   const int h = (int)(i % H);
-  const T* k = K + m * 64 * H + 64 * h;
   float s = 0.f;
-  for (int d = 0; d < 64; ++d) {
-    const float x = to_f(k[d]);
-    s += x * x;
+  if (i < (int64_t)M * H) {
+    const uint4* k = reinterpret_cast<const uint4*>(K + (i / H) * 64 * H + 64 * h);
+#pragma unroll
+    for (int c = 0; c < 64 / EPC; ++c) {
+      const uint4 u = k[c];
+      const T* x = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) s += to_f(x[e]) * to_f(x[e]);
+    }
   }
-  atomicMax(reinterpret_cast<unsigned*>(kmax + h), __float_as_uint(sqrtf(s)));
+  float n = sqrtf(s);
+  for (int o = 32; o >= H; o >>= 1) n = fmaxf(n, __shfl_xor(n, o));
+  if ((threadIdx.x & 63) < H) atomicMax(reinterpret_cast<unsigned*>(kmax + h), __float_as_uint(n));
 }
 
 hipError_t launch_key_norms(int dtype, const void* K, int M, int H, float* kmax, hipStream_t s) {
