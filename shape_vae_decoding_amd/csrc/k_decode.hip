@@ -290,14 +290,9 @@ __device__ __forceinline__ void tile_store(char* lds, int buf, int tid, const in
 // acc[r][i] += W[rows 32 r ..][..] x B[columns 32 (cb0 + i) ..]^T for NR consecutive
 // row blocks of W (global memory, each through a RING-deep register prefetch ring)
 // and NC column blocks of B (LDS, read one step ahead, each fragment used NR times).
-struct NoHook {
-  __device__ __forceinline__ void operator()(int) const {}
-};
-
-// (hook(ks) runs after the MFMAs of step ks: independent work to interleave)
-template <typename T, int NKS, int NR, int NC, bool PACKED, int RING = 4, typename Hook = NoHook>
+template <typename T, int NKS, int NR, int NC, bool PACKED, int RING = 4>
 __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, const T* B, int ldb, int cb0,
-                                          f32x16 (&acc)[NR][NC], int lane, Hook&& hook = Hook{}) {
+                                          f32x16 (&acc)[NR][NC], int lane) {
   using MM = Mma<T>;
   using Frag = typename MM::frag;
   // A fragment of row block r, step ks. Row-major W: rows of ldw elements from the
@@ -334,10 +329,6 @@ __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, cons
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int i = 0; i < NC; ++i) acc[r][i] = MM::mma(a[r], b[ks & 1][i], acc[r][i]);
-    hook(ks);
-    // with a hook, keep each step's loads and hooked work in their step (bounds
-    // the live registers of the interleaved work)
-    if constexpr (!std::is_same<typename std::decay<Hook>::type, NoHook>::value) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
