@@ -29,6 +29,7 @@ constexpr int SEL_GB = 4;                // blocks per workgroup
 constexpr int SEL_BQ = SEL_NP * SEL_GB;  // probe columns of the MFMA tile
 constexpr int SEL_MAXV = 64;             // scores per lane in the search: M <= 64 * 64
 constexpr int SEL_GRID_MAX = 256;        // workgroups (scratch rows are per workgroup)
+constexpr int SEL_LIST = 256;            // per-wave candidate list of the top-k search (LDS)
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -47,42 +48,116 @@ __device__ __forceinline__ int wave_sum(int v) {
 
 // Values u[i] stand for index i * 64 + lane (entries at or past n are 0 and never
 // taken). Sets in `bits` the k largest (unsigned order; equal values: lower index
-// first). One wave.
-__device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, int k, unsigned* bits, int lane) {
+// first). One wave; `list` is its LDS scratch of SEL_LIST values.
+//
+// The k-th largest value p is the largest threshold with #{u >= p} >= k, built
+// bit by bit. For k <= 64 the smallest of the 64 lane maxima, lo, is a lower
+// bound of p (64 values are >= lo), so only the values >= lo (usually a few times
+// k) take part: they are compacted into `list` and the bit search runs over 4 per
+// lane instead of 64; for every threshold above lo the counts are the same, and
+// below it both exceed k. If more than SEL_LIST values qualify, or k > 64, the
+// search runs over all values. Thresholds are >= 1, so zero entries never count;
+// values are visited in chunks of 16 and a chunk past n is skipped.
+__device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, int k, unsigned* bits,
+                                          unsigned* list, int lane) {
   // (every loop is fully unrolled with constant indices, so u stays in registers)
-  // k-th largest: the largest p with #{u >= p} >= k, built bit by bit
-  unsigned p = 0u;
-  for (int b = 31; b >= 0; --b) {
-    const unsigned cand = p | (1u << b);
+  constexpr int CH = 16, LV = SEL_LIST / 64;
+  static_assert(SEL_MAXV % CH == 0, "whole chunks");
+  auto count_all = [&](unsigned thr) {
     int c = 0;
 #pragma unroll
-    for (int i = 0; i < SEL_MAXV; ++i) c += (i * 64 + lane < n && u[i] >= cand) ? 1 : 0;
-    if (wave_sum(c) >= k) p = cand;
-  }
-  int gt = 0;
+    for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
+      if (c0 * 64 < n) {
 #pragma unroll
-  for (int i = 0; i < SEL_MAXV; ++i) gt += (i * 64 + lane < n && u[i] > p) ? 1 : 0;
-  const int need = k - wave_sum(gt);  // copies of p to take, lowest index first
+        for (int i = c0; i < c0 + CH; ++i) c += u[i] >= thr ? 1 : 0;
+      }
+    }
+    return wave_sum(c);
+  };
+  unsigned p = 0u;
+  bool done = false;
+  if (k <= 64) {
+    unsigned mx = 0u;
+#pragma unroll
+    for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
+      if (c0 * 64 < n) {
+#pragma unroll
+        for (int i = c0; i < c0 + CH; ++i) mx = u[i] > mx ? u[i] : mx;
+      }
+    }
+    unsigned lo = mx;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const unsigned t = __shfl_xor(lo, o);
+      lo = t < lo ? t : lo;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
+      if (c0 * 64 < n) {
+#pragma unroll
+        for (int i = c0; i < c0 + CH; ++i) mine += (u[i] >= lo && u[i] > 0u) ? 1 : 0;
+      }
+    }
+    const int incl = wave_incl_scan(mine, lane);
+    const int total = __shfl(incl, 63);
+    if (lo > 0u && total <= SEL_LIST) {
+      int off = incl - mine;
+#pragma unroll
+      for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
+        if (c0 * 64 < n) {
+#pragma unroll
+          for (int i = c0; i < c0 + CH; ++i)
+            if (u[i] >= lo) list[off++] = u[i];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      unsigned v[LV];
+#pragma unroll
+      for (int j = 0; j < LV; ++j) v[j] = j * 64 + lane < total ? list[j * 64 + lane] : 0u;
+      for (int b = 31; b >= 0; --b) {
+        const unsigned cand = p | (1u << b);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < LV; ++j) c += v[j] >= cand ? 1 : 0;
+        if (wave_sum(c) >= k) p = cand;
+      }
+      __builtin_amdgcn_wave_barrier();  // the list is read before the next search writes it
+      done = true;
+    }
+  }
+  if (!done) {
+    for (int b = 31; b >= 0; --b) {
+      const unsigned cand = p | (1u << b);
+      if (count_all(cand) >= k) p = cand;
+    }
+  }
+  const int need = k - (p == 0xffffffffu ? 0 : count_all(p + 1u));  // copies of p to take, lowest index first
   int taken = 0;
 #pragma unroll
   for (int i = 0; i < SEL_MAXV; ++i) {
-    const int idx = i * 64 + lane;
-    const bool valid = idx < n;
-    const bool eq = valid && u[i] == p;
-    const unsigned long long be = __ballot(eq);
-    const int rank = taken + __popcll(be & ((1ull << lane) - 1ull));
-    if (valid && (u[i] > p || (eq && rank < need))) atomicOr(&bits[idx >> 5], 1u << (idx & 31));
-    taken += __popcll(be);
+    if (i * 64 < n) {
+      const int idx = i * 64 + lane;
+      const bool valid = idx < n;
+      const bool eq = valid && u[i] == p;
+      const unsigned long long be = __ballot(eq);
+      const int rank = taken + __popcll(be & ((1ull << lane) - 1ull));
+      if (valid && (u[i] > p || (eq && rank < need))) atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+      taken += __popcll(be);
+    }
   }
 }
 
-// LDS: [embedding stage] | stats [NW][H][32] float2 | bits [GB][words] | bits2 [GB][words] | cnt [GB]
+// LDS: [embedding stage] | stats [NW][H][32] float2 | lists [NW][SEL_LIST] | bits [GB][words] |
+//      bits2 [GB][words] | cnt [GB]
 template <typename T, int H>
 struct SelCfg {
   static constexpr int D = 64 * H;
   static constexpr int EMB_END = EmbedLds<T, SEL_BQ, D>::END;
   static constexpr int STATS = (EMB_END + 15) & ~15;
-  static constexpr int BITS = STATS + SEL_NW * H * 32 * 8;
+  static constexpr int LISTS = STATS + SEL_NW * H * 32 * 8;
+  static constexpr int BITS = LISTS + SEL_NW * SEL_LIST * 4;
   __host__ __device__ static int total(int M) {
     const int words = (M + 31) / 32;
     return BITS + 2 * SEL_GB * words * 4 + SEL_GB * 4 + 16;
@@ -158,6 +233,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   unsigned* bits2 = bits + SEL_GB * nwords;                        // [GB][nwords]
   int* ucount = reinterpret_cast<int*>(bits2 + SEL_GB * nwords);   // [GB]
   float* scores = A.scores + (int64_t)blockIdx.x * SEL_BQ * Mp;    // [BQ][Mp], this workgroup's rows
+  unsigned* wlist = reinterpret_cast<unsigned*>(lds + CF::LISTS) + wave * SEL_LIST;  // this wave's top-k list
   const __amdgpu_buffer_rsrc_t sbuf =
       __builtin_amdgcn_make_buffer_rsrc(scores, (short)0, SEL_BQ * Mp * 4, 0x00020000 /* raw buffer */);
   const int64_t nblk = A.d_n_blocks ? (int64_t)*A.d_n_blocks : A.n_blocks;
@@ -296,7 +372,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
     for (int p = wave; p < nb * SEL_NP; p += SEL_NW) {
       unsigned u[SEL_MAXV];
       load_scores(sbuf, p, Mp, M, lane, u);
-      topk_bits(u, M, A.k, bits + (p / SEL_NP) * nwords, lane);
+      topk_bits(u, M, A.k, bits + (p / SEL_NP) * nwords, wlist, lane);
     }
     __syncthreads();
 
@@ -326,7 +402,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
           const bool member = idx < M && ((ub[idx >> 5] >> (idx & 31)) & 1u);
           u[i] = member ? u[i] + 1u : 0u;
         }
-        topk_bits(u, M, A.cap, bits2 + blk * nwords, lane);
+        topk_bits(u, M, A.cap, bits2 + blk * nwords, wlist, lane);
         outbits = bits2 + blk * nwords;
       }
       const int64_t row = row0 + blk;

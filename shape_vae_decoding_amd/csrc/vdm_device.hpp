@@ -296,8 +296,8 @@ struct EmbedLds {
 // single rounding of Q to bf16.
 // Wq: [D][51]. Q is multiplied by qscale before its rounding. Ends with a barrier.
 template <typename T, int BQ, int D, int NT>
-__device__ void embed_qproj(const QuerySrc& qs, int64_t q0, int64_t q1, const T* __restrict__ Wq,
-                            char* lds, int tid, float qscale = 1.f) {
+__device__ __forceinline__ void embed_qproj(const QuerySrc& qs, int64_t q0, int64_t q1, const T* __restrict__ Wq,
+                                            char* lds, int tid, float qscale = 1.f) {
   using L = EmbedLds<T, BQ, D>;
   using MM = Mma<T>;
   T* e_hi = reinterpret_cast<T*>(lds + L::E_HI);
