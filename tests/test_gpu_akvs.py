@@ -233,3 +233,31 @@ def test_gathered_decode_mixed_softmax_paths():
     assert np.all(np.isfinite(out))
     report("gathered decode, mixed softmax paths", worst, TOL_BF16)
     assert worst <= TOL_BF16
+
+
+@pytest.mark.parametrize("repeat", [1, 3])
+def test_select_ties_go_to_the_lower_index(repeat):
+    # Keys made of `repeat` distinct rows, each repeated: whole groups of tokens
+    # share one score, so the k-th score has many copies and the set must take the
+    # lowest-indexed of them (exactly, no tie window). repeat = 1: every score is
+    # equal, so every value is a candidate of the threshold search (more than its
+    # candidate list holds); repeat = 3: three score levels.
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    K, _ = gpu_kv(dec, w)
+    M = w.M
+    rows = K[torch.arange(M, device=dev()) % repeat * 97].contiguous()
+    R, k, cap = 75, 64, 512
+    nb = hv.nblocks(R + 1)
+    blocks = np.array([0, 5, nb ** 3 // 2, nb ** 3 - 1])
+    sel_idx, sel_cnt = run_select(dec, w, rows, R, blocks, k, cap)
+    Qp = gpu_probe_q(dec, w, R, blocks)
+    Kh = f64(rows)
+    for r in range(len(blocks)):
+        sc = oak.probe_scores(Qp[r], Kh, w.H)
+        ref = oak.select(sc, k, cap)
+        got = sel_idx[r, : sel_cnt[r]]
+        assert np.array_equal(np.sort(ref), got), (blocks[r], ref[:8], got[:8])
+    if repeat == 1:
+        assert np.all(sel_cnt == k) and np.array_equal(sel_idx[:, :k], np.tile(np.arange(k), (len(blocks), 1)))
+    print(f"[parity] selection ties (repeat={repeat}): {len(blocks)} blocks exact", flush=True)
