@@ -289,8 +289,8 @@ __device__ __forceinline__ void tile_store(char* lds, int buf, int tid, const in
 
 // acc[r][i] += W[rows 32 r ..][..] x B[columns 32 (cb0 + i) ..]^T for NR consecutive
 // row blocks of W (global memory, each through a RING-deep register prefetch ring)
-// and NC column blocks of B (LDS, read one step ahead, each fragment used NR times).
-template <typename T, int NKS, int NR, int NC, bool PACKED, int RING = 4>
+// and NC column blocks of B (LDS, read BPF steps ahead, each fragment used NR times).
+template <typename T, int NKS, int NR, int NC, bool PACKED, int RING = 8, int BPF = 2>
 __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, const T* B, int ldb, int cb0,
                                           f32x16 (&acc)[NR][NC], int lane) {
   using MM = Mma<T>;
@@ -303,15 +303,19 @@ __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, cons
     else
       return load_frag<T>(W + (int64_t)(32 * r) * ldw + ks * MM::KS, ldw, lane);
   };
-  constexpr int PF = NKS < RING ? NKS : RING;
+  auto bfrag = [&](int i, int ks) -> Frag { return load_frag<T>(B + (32 * (cb0 + i)) * ldb + ks * MM::KS, ldb, lane); };
+  constexpr int PF = NKS < RING ? NKS : RING;        // weight steps in flight (global memory)
+  constexpr int BD = NKS < BPF + 1 ? NKS : BPF + 1;  // B steps held (LDS reads BD - 1 steps ahead)
   Frag ring[NR][PF];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int p = 0; p < PF; ++p) ring[r][p] = wfrag(r, p);
-  Frag b[2][NC];
+  Frag b[BD][NC];
 #pragma unroll
-  for (int i = 0; i < NC; ++i) b[0][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb, ldb, lane);
+  for (int d = 0; d < BD - 1; ++d)
+#pragma unroll
+    for (int i = 0; i < NC; ++i) b[d][i] = bfrag(i, d);
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     Frag a[NR];
@@ -320,15 +324,14 @@ __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, cons
       a[r] = ring[r][ks % PF];
       if (ks + PF < NKS) ring[r][ks % PF] = wfrag(r, ks + PF);
     }
-    if (ks + 1 < NKS) {
+    if (ks + BD - 1 < NKS) {
 #pragma unroll
-      for (int i = 0; i < NC; ++i)
-        b[(ks + 1) & 1][i] = load_frag<T>(B + (32 * (cb0 + i)) * ldb + (ks + 1) * MM::KS, ldb, lane);
+      for (int i = 0; i < NC; ++i) b[(ks + BD - 1) % BD][i] = bfrag(i, ks + BD - 1);
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int i = 0; i < NC; ++i) acc[r][i] = MM::mma(a[r], b[ks & 1][i], acc[r][i]);
+      for (int i = 0; i < NC; ++i) acc[r][i] = MM::mma(a[r], b[ks % BD][i], acc[r][i]);
   }
 }
 
