@@ -182,12 +182,67 @@ def cpu_baseline(w, target_s: float = 12.0):
     }
 
 
+def large_token_decode(V, W, dev, reps: int = 5):
+    """The 40,960-token workload: 200,000 query points (half uniform, half near the
+    surface) against the latent set of a 10-primitive shape. Returns the launch
+    time (HIP events in the library) and the MFMA rate of the fused decode."""
+    import numpy as np
+    import torch
+
+    w = W.make(4)
+    wt = {k: torch.from_numpy(v).to(dev) for k, v in w.weights.items()}
+    wt = {k: (v if k == "w_head" else v.to(torch.bfloat16)) for k, v in wt.items()}
+    dec = V.Decoder(wt, w.prims, w.net_scale)
+    Z = torch.from_numpy(w.Z).to(dev).to(torch.bfloat16)
+    K = torch.empty_like(Z)
+    Vv = torch.empty_like(Z)
+    V.vdm_project_kv(dec, Z, K, Vv)
+    xyz = torch.from_numpy(np.ascontiguousarray(w.query["xyz"], np.float32)).to(dev)
+    N = xyz.shape[0]
+    sdf = torch.empty(N, dtype=torch.float32, device=dev)
+    q = V.queries_points(xyz)
+    ws = V.workspace(V.vdm_dense_workspace_size(dec, w.M, N), dev)
+    V.vdm_decode_dense(dec, q, K, Vv, sdf, ws=ws)
+    torch.cuda.synchronize()
+    V.vdm_timing(2)
+    V.vdm_timing(1)
+    for _ in range(reps):
+        V.vdm_decode_dense(dec, q, K, Vv, sdf, ws=ws)
+    V.vdm_timing(0)
+    n, ms = V.vdm_timing_read("decode")
+    V.vdm_timing(2)
+    launch_ms = ms / n
+    tflops = flops_per_query(51, w.D, w.M, w.F) * N / (launch_ms / 1e3) / 1e12
+    return {"tokens": w.M, "query_points": N, "launch_ms": round(launch_ms, 4),
+            "query_points_per_s": round(N / (launch_ms / 1e3), 1), "tflops": round(tflops, 2),
+            "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
+def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 5):
+    """Achievable HBM bandwidth: a device-to-device copy (read + write bytes / time)."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return round(2 * nbytes / (ms / 1e3) / 1e9, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU baseline (profiling runs)")
+    ap.add_argument("--skip-cpu", action="store_true",
+                    help="omit the CPU baseline, the large-token workload and the copy bandwidth (profiling runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, copy 512 MiB device-to-device 3 times (a known-size kernel for "
                          "calibrating the FETCH_SIZE / WRITE_SIZE counters)")
@@ -344,6 +399,13 @@ def main():
         },
         "roofline": roofline,
     }
+    if not args.skip_cpu:
+        # outside the timed steps (and left out of profiling runs): the large-token
+        # workload and the machine's reference figures
+        out["breakdown"]["large_tokens_200k_points"] = large_token_decode(V, W, dev)
+        props = torch.cuda.get_device_properties(0)
+        out["breakdown"]["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
+                                      "copy_GB_per_s": copy_bandwidth(dev), "hbm_peak_GB_per_s": PEAK_HBM_GBS}
     if args.copy_calib:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
