@@ -575,7 +575,7 @@ template <typename C, bool SHIFT>
 __device__ __forceinline__ void gathered_attention(const typename C::T* __restrict__ Kg,
                                                    const typename C::T* __restrict__ Vg, const int32_t* sel,
                                                    int nkeys, int M, int tid, int lane, int hw, char* lds,
-                                                   const int (&vpos)[C::NCK],
+                                                   const int (&vpos)[C::NCK], bool active,
                                                    const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
                                                    const float (&nb)[C::QB], f32x16 (&O)[2][C::QB],
                                                    float (&l_run)[C::QB]) {
@@ -592,6 +592,7 @@ __device__ __forceinline__ void gathered_attention(const typename C::T* __restri
     tile_load<C, true>(Kg, Vg, sel, nkeys, M, kt + 1 < nkt ? kt + 1 : kt, tid, rk, rv);
     const T* Kb = reinterpret_cast<const T*>(lds + (kt & 1) * C::KBYTES);
     const T* Vb = reinterpret_cast<const T*>(lds + 2 * C::KBYTES + (kt & 1) * C::VBYTES);
+    if (active) {  // (a wave whose queries are all past the item's end only stages tiles)
     Frag kf[C::KSTEPS], vf[2][C::PSTEPS];
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = load_frag<T>(Kb + 64 * hw + ks * MM::KS, C::DPAD, lane);
@@ -608,6 +609,7 @@ __device__ __forceinline__ void gathered_attention(const typename C::T* __restri
       tile_compute<C, true, SHIFT>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
     else
       tile_compute<C, false, SHIFT>(kf, vf, qf, nb, O, l_run, kt, nkeys, lane);
+    }
     // the other buffer was last read before the previous barrier
     tile_store<C, true>(lds, (kt + 1) & 1, tid, vpos, rk, rv);
     __syncthreads();
@@ -708,17 +710,21 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
 
     // logits of every query of this wave within +-SHIFT_FREE_MAX: no shift
     const bool shift = __builtin_amdgcn_ballot_w64(any_below(nb, 0.f)) != 0;
+    const bool active = qg * C::QW < q1 - q0;  // this wave has queries in the tile
     if constexpr (!GATHER) {
-      if (shift)
+      if (!active) {
+        // (every query of this wave lies past the tile's end: nothing to attend)
+      } else if (shift) {
         dense_attention<C, true>(A, nkeys, hw, lane, qf, nb, O, l_run);
-      else
+      } else {
         dense_attention<C, false>(A, nkeys, hw, lane, qf, nb, O, l_run);
+      }
     } else {
       // (both variants pass the same barriers, so waves may take different ones)
       if (shift)
-        gathered_attention<C, true>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, qf, nb, O, l_run);
+        gathered_attention<C, true>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O, l_run);
       else
-        gathered_attention<C, false>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, qf, nb, O, l_run);
+        gathered_attention<C, false>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O, l_run);
     }
 
     // ---------------------------------------------------------------- o = sum p v / sum p
@@ -738,51 +744,56 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
 
     // ---------------------------------------------------------------- a = Wo o  (kept in fp32 as y)
     // this wave's epilogue tiles: weight row blocks rb0 .. rb0 + RPW - 1, column
-    // blocks cb0 .. cb0 + CPW - 1
+    // blocks cb0 .. cb0 + NCB - 1. In gathered mode, when every wave covers all
+    // column blocks, a work item with at most half a tile of queries computes only
+    // the first half of the column blocks.
     const int rb0 = C::TPW >= C::CB ? wave * C::RPW : (wave * C::TPW) / C::CB;
     const int cb0 = C::TPW >= C::CB ? 0 : (wave * C::TPW) % C::CB;
-    f32x16 Y[C::RPW][C::CPW];
-#pragma unroll
-    for (int r = 0; r < C::RPW; ++r)
-#pragma unroll
-      for (int i = 0; i < C::CPW; ++i) Y[r][i] = zero16();
-    gemm_rows<T, C::D / MM::KS, C::RPW, C::CPW, C::PACKED_W>(wblock<C>(Wo, rb0, 0, C::D), C::D, Ob, C::DPAD, cb0, Y,
-                                                             lane);
+    const int rh0 = C::TPH >= C::CB ? wave * C::RPH : (wave * C::TPH) / C::CB;
+    const int ch0 = C::TPH >= C::CB ? 0 : (wave * C::TPH) % C::CB;
     T* Ab = reinterpret_cast<T*>(lds + C::ABUF);
+    T* Hb = reinterpret_cast<T*>(lds + C::OBUF);
+    float* red = reinterpret_cast<float*>(lds + C::RED);
+    auto epilogue = [&](auto ncb_tag) {
+    constexpr int NCB = decltype(ncb_tag)::value;
+    constexpr int NCH = C::CPH == C::CB ? NCB : C::CPH;
+    f32x16 Y[C::RPW][NCB];
 #pragma unroll
     for (int r = 0; r < C::RPW; ++r)
 #pragma unroll
-      for (int i = 0; i < C::CPW; ++i)
+      for (int i = 0; i < NCB; ++i) Y[r][i] = zero16();
+    gemm_rows<T, C::D / MM::KS, C::RPW, NCB, C::PACKED_W>(wblock<C>(Wo, rb0, 0, C::D), C::D, Ob, C::DPAD, cb0,
+                                                          Y, lane);
+#pragma unroll
+    for (int r = 0; r < C::RPW; ++r)
+#pragma unroll
+      for (int i = 0; i < NCB; ++i)
         store_ct<T>(Ab + (32 * (cb0 + i)) * C::DPAD + 32 * (rb0 + r), C::DPAD, Y[r][i], lane);
     __syncthreads();
 
     // ---------------------------------------------------------------- y = a + W2 GELU(W1 a)
-    T* Hb = reinterpret_cast<T*>(lds + C::OBUF);
-    const int rh0 = C::TPH >= C::CB ? wave * C::RPH : (wave * C::TPH) / C::CB;
-    const int ch0 = C::TPH >= C::CB ? 0 : (wave * C::TPH) % C::CB;
     for (int f0 = 0; f0 < A.F; f0 += C::FC) {
-      f32x16 Hc[C::RPH][C::CPH];
+      f32x16 Hc[C::RPH][NCH];
 #pragma unroll
       for (int r = 0; r < C::RPH; ++r)
 #pragma unroll
-        for (int j = 0; j < C::CPH; ++j) Hc[r][j] = zero16();
-      gemm_rows<T, C::D / MM::KS, C::RPH, C::CPH, C::PACKED_W>(wblock<C>(W1, f0 / 32 + rh0, 0, C::D), C::D, Ab,
-                                                               C::DPAD, ch0, Hc, lane);
+        for (int j = 0; j < NCH; ++j) Hc[r][j] = zero16();
+      gemm_rows<T, C::D / MM::KS, C::RPH, NCH, C::PACKED_W>(wblock<C>(W1, f0 / 32 + rh0, 0, C::D), C::D, Ab, C::DPAD,
+                                                            ch0, Hc, lane);
 #pragma unroll
       for (int r = 0; r < C::RPH; ++r)
 #pragma unroll
-        for (int j = 0; j < C::CPH; ++j) {
+        for (int j = 0; j < NCH; ++j) {
           gelu_tile<C>(Hc[r][j], gtab);
           store_ct<T>(Hb + (32 * (ch0 + j)) * C::HPAD + 32 * (rh0 + r), C::HPAD, Hc[r][j], lane);
         }
       __syncthreads();
-      gemm_rows<T, C::FC / MM::KS, C::RPW, C::CPW, C::PACKED_W>(wblock<C>(W2, rb0, f0 / MM::KS, A.F), A.F, Hb,
-                                                                C::HPAD, cb0, Y, lane);
+      gemm_rows<T, C::FC / MM::KS, C::RPW, NCB, C::PACKED_W>(wblock<C>(W2, rb0, f0 / MM::KS, A.F), A.F, Hb, C::HPAD,
+                                                             cb0, Y, lane);
       __syncthreads();
     }
 
     // ---------------------------------------------------------------- net = w_head . y, SDF
-    float* red = reinterpret_cast<float*>(lds + C::RED);
     {
       float s[C::CPW];
 #pragma unroll
@@ -793,7 +804,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) w[k] = A.w_head[32 * (rb0 + r) + crow(k, lane)];
 #pragma unroll
-        for (int i = 0; i < C::CPW; ++i)
+        for (int i = 0; i < NCB; ++i)
 #pragma unroll
           for (int k = 0; k < 16; ++k) s[i] += w[k] * Y[r][i][k];
       }
@@ -805,6 +816,18 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       // column blocks this wave does not cover contribute zero
       for (int cb = 0; cb < C::CB; ++cb)
         if ((cb < cb0 || cb >= cb0 + C::CPW) && lane < 32) red[wave * C::BQ + 32 * cb + lane] = 0.f;
+    }
+    };
+    if constexpr (C::CPW == C::CB && GATHER) {
+      // (work items of a block's token set often end part-way through a tile;
+      // wave-uniform: the item's query count)
+      const int ncb = (int)((q1 - q0 + 31) / 32);
+      if (2 * ncb > C::CB)
+        epilogue(std::integral_constant<int, C::CB>{});
+      else
+        epilogue(std::integral_constant<int, C::CB / 2>{});
+    } else {
+      epilogue(std::integral_constant<int, C::CPW>{});
     }
     __syncthreads();
     for (int t = tid; t < C::BQ; t += C::NT) {
