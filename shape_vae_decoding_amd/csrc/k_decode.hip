@@ -58,14 +58,15 @@ struct DecCfg {
   static constexpr int PSTEPS = KT / Mma<T>::KS;   // MFMA steps over one 32-token tile
   // per-lane operand run of one (tile, head): 32 elements of K and 32 of V^T
   static constexpr int RUN_U4 = 32 * SZ / 16;
-  // gathered-mode staging: two K tiles [KT][DPAD] and two V tiles, row-major
+  // gathered-mode staging: two K tiles [KT][DPAD] and two (three for the
+  // software-pipelined 16-bit path) V tiles, row-major
   // [KT][VROW] for 16-bit types (read transposed by ds_read_b64_tr_b16; rows of
   // D + 32 elements put the 4 rows of one read 16 banks apart) or V^T [D][VPAD]
   static constexpr bool TR_V = SZ == 2;
   static constexpr int VROW = D + 32;
   static constexpr int KBYTES = KT * DPAD * SZ;
   static constexpr int VBYTES = TR_V ? KT * VROW * SZ : D * VPAD * SZ;
-  static constexpr int ATT_END = 2 * (KBYTES + VBYTES);
+  static constexpr int ATT_END = 2 * KBYTES + (TR_V ? 3 : 2) * VBYTES;
   // epilogue: O [BQ][DPAD] (later the GELU chunk [BQ][HPAD]), a [BQ][DPAD], reduction
   static constexpr int OBUF = 0;
   static constexpr int ABUF = BQ * DPAD * SZ;
@@ -418,11 +419,13 @@ __device__ __forceinline__ f32x16 s_block(const typename Mma<typename C::T>::fra
 
 // LAST: the final tile (no S of a next tile, no K load; ends with its own P.V);
 // RAGGED: it is partial; SHIFT: see softmax_block.
-template <typename C, bool LAST, bool RAGGED, bool SHIFT>
+// load_k(t, regs) / load_v(t, regs) fetch this wave's operand runs of tile t;
+// after_loads(kt) runs right after them (independent work to start early).
+template <typename C, bool LAST, bool RAGGED, bool SHIFT, typename LK, typename LV, typename AL>
 __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], const uint4 (&v_prev)[C::RUN_U4],
                                           uint4 (&k_load)[C::RUN_U4], uint4 (&v_load)[C::RUN_U4],
-                                          __amdgpu_buffer_rsrc_t Kg, __amdgpu_buffer_rsrc_t Vg,
-                                          int kt, int k_tile, int nkeys, int hw, int lane,
+                                          LK&& load_k, LV&& load_v, AL&& after_loads,
+                                          int kt, int k_tile, int nkeys, int lane,
                                           const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
                                           const float (&nb)[C::QB], f32x16 (&S)[C::QB],
                                           typename Mma<typename C::T>::frag (&P)[C::QB][C::PSTEPS],
@@ -430,8 +433,9 @@ __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], cons
   using T = typename C::T;
   using MM = Mma<T>;
   using Frag = typename MM::frag;
-  if constexpr (!LAST) load_run<C>(Kg, k_tile, hw, lane, k_load);
-  load_run<C>(Vg, kt, hw, lane, v_load);
+  if constexpr (!LAST) load_k(k_tile, k_load);
+  load_v(kt, v_load);
+  after_loads(kt);
   Frag kf[C::KSTEPS], vf[2][C::PSTEPS];
   as_frags<C>(k_next, v_prev, kf, vf);
 #pragma unroll
@@ -505,6 +509,9 @@ __device__ __forceinline__ void dense_attention(const DecodeArgs& A, int nkeys, 
   const int64_t packed_bytes = (int64_t)nkt * C::KT * C::D * C::SZ;
   const __amdgpu_buffer_rsrc_t Kg = buffer_of(A.Kp, packed_bytes);
   const __amdgpu_buffer_rsrc_t Vg = buffer_of(A.Vt, packed_bytes);
+  auto load_k = [&](int t, uint4 (&r)[C::RUN_U4]) { load_run<C>(Kg, t, hw, lane, r); };
+  auto load_v = [&](int t, uint4 (&r)[C::RUN_U4]) { load_run<C>(Vg, t, hw, lane, r); };
+  auto nothing = [](int) {};
   uint4 kb[2][C::RUN_U4], vb[2][C::RUN_U4];
   f32x16 S[C::QB];
   Frag P[C::QB][C::PSTEPS];
@@ -524,14 +531,14 @@ __device__ __forceinline__ void dense_attention(const DecodeArgs& A, int nkeys, 
   }
   int kt = 0;
   for (; kt + 2 < nkt; kt += 2) {
-    pipe_iter<C, false, false, SHIFT>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, kt + 2, nkeys, hw, lane, qf, nb, S, P,
+    pipe_iter<C, false, false, SHIFT>(kb[1], vb[1], kb[0], vb[0], load_k, load_v, nothing, kt, kt + 2, nkeys, lane, qf, nb, S, P,
                                       O, l_run);
     const int k3 = kt + 3 < nkt ? kt + 3 : nkt - 1;
-    pipe_iter<C, false, false, SHIFT>(kb[0], vb[0], kb[1], vb[1], Kg, Vg, kt + 1, k3, nkeys, hw, lane, qf, nb, S, P,
+    pipe_iter<C, false, false, SHIFT>(kb[0], vb[0], kb[1], vb[1], load_k, load_v, nothing, kt + 1, k3, nkeys, lane, qf, nb, S, P,
                                       O, l_run);
   }
   if (kt + 1 < nkt) {  // one more full iteration (kt even)
-    pipe_iter<C, false, false, SHIFT>(kb[1], vb[1], kb[0], vb[0], Kg, Vg, kt, nkt - 1, nkeys, hw, lane, qf, nb, S, P,
+    pipe_iter<C, false, false, SHIFT>(kb[1], vb[1], kb[0], vb[0], load_k, load_v, nothing, kt, nkt - 1, nkeys, lane, qf, nb, S, P,
                                       O, l_run);
     ++kt;
   }
@@ -543,7 +550,8 @@ __device__ __forceinline__ void dense_attention(const DecodeArgs& A, int nkeys, 
 #pragma unroll
     for (int i = 0; i < C::RUN_U4; ++i) vb[1][i] = vb[0][i];
   }
-  pipe_iter<C, true, true, SHIFT>(kb[0], vb[1], kb[0], vb[0], Kg, Vg, kt, 0, nkeys, hw, lane, qf, nb, S, P, O, l_run);
+  pipe_iter<C, true, true, SHIFT>(kb[0], vb[1], kb[0], vb[0], load_k, load_v, nothing, kt, 0, nkeys, lane, qf, nb, S, P, O,
+                                  l_run);
 }
 
 // V^T fragment (A operand of O^T += V^T P^T) for dims d0 .. d0+31 and MFMA step
@@ -567,6 +575,203 @@ __device__ __forceinline__ typename Mma<typename C::T>::frag vt_frag_tr(const ty
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return *reinterpret_cast<const typename Mma<typename C::T>::frag*>(&ab);
+}
+
+// Selected-token rows of a 32-token tile t for this thread's staging chunks: the
+// thread moves NCK 16-byte chunks per tile, chunk c = tid + i*NT holding elements
+// (c % CPR)*EPC .. +EPC-1 of row j = 32t + c / CPR; entry i is the token index of
+// that row (as stored: gather_rows clamps it to [0, M) when it is used, so that
+// nothing waits for these loads before then). Rows past the set repeat its last
+// token (finite values that the softmax of the last tile masks), so that no load
+// is conditional: a branch around a load would end the scheduling region and wait
+// for every load in flight. nkeys >= 1.
+template <typename C>
+__device__ __forceinline__ void tile_rows(const int32_t* sel, int nkeys, int t, int tid, int (&s)[C::NCK]) {
+  constexpr int CPR = C::D / C::EPC;
+#pragma unroll
+  for (int i = 0; i < C::NCK; ++i) {
+    const int j = t * C::KT + (tid + i * C::NT) / CPR;
+    s[i] = sel[min(j, nkeys - 1)];
+  }
+}
+
+// This thread's chunks of the rows s (tile_rows) of K or V ([M][D] behind the
+// buffer X), into registers ...
+template <typename C>
+__device__ __forceinline__ void gather_rows(__amdgpu_buffer_rsrc_t X, const int (&s)[C::NCK], int M, int tid,
+                                            uint4 (&r)[C::NCK]) {
+  constexpr int CPR = C::D / C::EPC;
+#pragma unroll
+  for (int i = 0; i < C::NCK; ++i) {
+    const int e = ((tid + i * C::NT) % CPR) * C::EPC;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(X, (tok_clamp(s[i], M) * C::D + e) * C::SZ, 0, 0);
+    r[i] = uint4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+// ... and from registers into a row-major LDS tile with rows of `ld` elements.
+template <typename C>
+__device__ __forceinline__ void put_rows(typename C::T* dst, int ld, int tid, const uint4 (&r)[C::NCK]) {
+  constexpr int CPR = C::D / C::EPC;
+#pragma unroll
+  for (int i = 0; i < C::NCK; ++i) {
+    const int c = tid + i * C::NT;
+    *reinterpret_cast<uint4*>(dst + (c / CPR) * ld + (c % CPR) * C::EPC) = r[i];
+  }
+}
+
+// Gathered attention for 16-bit types, software-pipelined. Iteration k computes
+// O += V(k-1) P(k-1), P(k) = softmax(S(k)) and S(k+1) = K(k+1) Q, reading this
+// wave's V(k-1) and K(k+1) operands from LDS at its start. The workgroup stages
+// the selected rows through two K tiles and three V tiles in LDS: during
+// iteration k every thread gathers its chunks of K tile k+2 and V tile k+1 from
+// global memory (the token indices of the next K tile are fetched one iteration
+// ahead), writes them into LDS at the end and the iteration closes with one
+// barrier. Stage hazards: K tile k+2 replaces tile k, read in iteration k-1; V
+// tile k+1 replaces tile k-2, read in iteration k-1 (iteration k reads V tile k-1,
+// hence three V stages). Rows past the set repeat its last token and are masked
+// in the last softmax.
+template <typename C, bool SHIFT>
+__device__ __forceinline__ void gathered_attention_pipe(
+    const typename C::T* __restrict__ Kg, const typename C::T* __restrict__ Vg, const int32_t* sel, int nkeys, int M,
+    int tid, int lane, int hw, char* lds, bool active,
+    const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS], const float (&nb)[C::QB],
+    f32x16 (&O)[2][C::QB], float (&l_run)[C::QB]) {
+  using T = typename C::T;
+  using MM = Mma<T>;
+  using Frag = typename MM::frag;
+  static_assert(C::TR_V && C::RUN_U4 == C::KSTEPS && C::RUN_U4 == 2 * C::PSTEPS, "one uint4 per fragment");
+  const int nkt = (nkeys + C::KT - 1) / C::KT;
+  if (nkt == 0) return;  // (an empty set: the API never forms work items for it)
+  const __amdgpu_buffer_rsrc_t Kb = buffer_of(Kg, (int64_t)M * C::D * C::SZ);
+  const __amdgpu_buffer_rsrc_t Vb = buffer_of(Vg, (int64_t)M * C::D * C::SZ);
+  T* Ks = reinterpret_cast<T*>(lds);                  // two K tiles [KT][DPAD]
+  T* Vs = reinterpret_cast<T*>(lds + 2 * C::KBYTES);  // three V tiles [KT][VROW]
+  auto kstage = [&](int t) { return Ks + (t & 1) * (C::KBYTES / C::SZ); };
+  auto vstage = [&](int t) { return Vs + ((t + 3) % 3) * (C::VBYTES / C::SZ); };  // t >= -1
+  auto read_k = [&](int t, Frag (&kf)[C::KSTEPS]) {
+    const T* src = kstage(t) + 64 * hw;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = load_frag<T>(src + ks * MM::KS, C::DPAD, lane);
+  };
+  auto read_v = [&](int t, Frag (&vf)[2][C::PSTEPS]) {
+    const T* src = vstage(t);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int ps = 0; ps < C::PSTEPS; ++ps) vf[db][ps] = vt_frag_tr<C>(src, 64 * hw + 32 * db, ps, lane);
+  };
+  auto pv = [&](const Frag (&vf)[2][C::PSTEPS], const Frag (&P)[C::QB][C::PSTEPS]) {
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int ps = 0; ps < C::PSTEPS; ++ps) O[db][qb] = MM::mma(vf[db][ps], P[qb][ps], O[db][qb]);
+  };
+
+  // prologue: S(0) from K tile 0 read straight from global memory (this wave's
+  // head); K tile 1 and V tile 0 staged; V stage "-1" zeroed (P(-1) = 0 must not
+  // meet stale bits that could be NaN)
+  int sa[C::NCK], sb[C::NCK];  // token rows of V tile k+1 and K tile k+2 in iteration k
+  uint4 gk[C::NCK], gv[C::NCK];
+  tile_rows<C>(sel, nkeys, 0, tid, sa);
+  tile_rows<C>(sel, nkeys, 1, tid, sb);
+  gather_rows<C>(Vb, sa, M, tid, gv);
+  gather_rows<C>(Kb, sb, M, tid, gk);
+  f32x16 S[C::QB];
+  if (active) {
+    Frag kf[C::KSTEPS];
+    const int row = tok_clamp(sel[min(lane & 31, nkeys - 1)], M);
+    const int off = (row * C::D + 64 * hw + MM::KW * (lane >> 5)) * C::SZ;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(Kb, off + ks * MM::KS * C::SZ, 0, 0);
+      const uint4 u{v[0], v[1], v[2], v[3]};
+      kf[ks] = *reinterpret_cast<const Frag*>(&u);
+    }
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) S[qb] = s_block<C>(kf, qf[qb]);
+  }
+  {
+    uint4 z[C::NCK];
+#pragma unroll
+    for (int i = 0; i < C::NCK; ++i) z[i] = uint4{0, 0, 0, 0};
+    put_rows<C>(vstage(-1), C::VROW, tid, z);
+  }
+  put_rows<C>(vstage(0), C::VROW, tid, gv);
+  put_rows<C>(kstage(1), C::DPAD, tid, gk);
+#pragma unroll
+  for (int i = 0; i < C::NCK; ++i) sa[i] = sb[i];
+  tile_rows<C>(sel, nkeys, 2, tid, sb);
+  __syncthreads();
+
+  // staging of one loop iteration k (every wave takes part)
+  auto stage_next = [&](int k, auto work) {
+    int sn[C::NCK];
+    gather_rows<C>(Vb, sa, M, tid, gv);
+    gather_rows<C>(Kb, sb, M, tid, gk);
+    tile_rows<C>(sel, nkeys, k + 3, tid, sn);
+    work();
+    put_rows<C>(kstage(k + 2), C::DPAD, tid, gk);
+    put_rows<C>(vstage(k + 1), C::VROW, tid, gv);
+#pragma unroll
+    for (int i = 0; i < C::NCK; ++i) {
+      sa[i] = sb[i];
+      sb[i] = sn[i];
+    }
+    __syncthreads();
+  };
+  if (!active) {
+    // (no queries in this wave: it only keeps the workgroup's staging and barriers)
+    for (int k = 0; k + 1 < nkt; ++k) stage_next(k, [] {});
+    __syncthreads();
+    return;
+  }
+  Frag P[C::QB][C::PSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int ps = 0; ps < C::PSTEPS; ++ps) P[qb][ps] = Frag{};
+  for (int k = 0; k + 1 < nkt; ++k) {
+    Frag vf[2][C::PSTEPS], kf[C::KSTEPS];
+    read_v(k - 1, vf);
+    read_k(k + 1, kf);
+    stage_next(k, [&] {
+      pv(vf, P);
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        softmax_block<T, false, SHIFT>(S[qb], nb[qb], l_run[qb], k * C::KT, nkeys, lane, P[qb]);
+        S[qb] = s_block<C>(kf, qf[qb]);
+      }
+      if constexpr (C::SCHED_ATT) {
+        // operand reads and gathers first, then P.V of the previous tile beside the
+        // first softmax and S of the next tile beside the later ones
+        constexpr int NM = (2 * C::PSTEPS + C::KSTEPS) * C::QB;
+        constexpr int VPM = (C::QB * (SHIFT ? 48 : 32) + NM - 1) / NM;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * C::PSTEPS + C::KSTEPS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 3 * C::NCK, 0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+        }
+      }
+    });
+  }
+  {
+    // last tile (ragged): P.V of the one before, its softmax and its own P.V
+    const int k = nkt - 1;
+    Frag vf[2][C::PSTEPS];
+    read_v(k - 1, vf);
+    pv(vf, P);
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+      softmax_block<T, true, SHIFT>(S[qb], nb[qb], l_run[qb], k * C::KT, nkeys, lane, P[qb]);
+    read_v(k, vf);
+    pv(vf, P);
+  }
+  __syncthreads();
 }
 
 // Attention over one block's selected token set: 32-token tiles gathered into
@@ -721,10 +926,17 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       }
     } else {
       // (both variants pass the same barriers, so waves may take different ones)
-      if (shift)
-        gathered_attention<C, true>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O, l_run);
-      else
-        gathered_attention<C, false>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O, l_run);
+      if constexpr (C::TR_V) {
+        if (shift)
+          gathered_attention_pipe<C, true>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, active, qf, nb, O, l_run);
+        else
+          gathered_attention_pipe<C, false>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, active, qf, nb, O, l_run);
+      } else {
+        if (shift)
+          gathered_attention<C, true>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O, l_run);
+        else
+          gathered_attention<C, false>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O, l_run);
+      }
     }
 
     // ---------------------------------------------------------------- o = sum p v / sum p
