@@ -24,6 +24,8 @@ Modules:
   akvs     adaptive KV selection: corner probes, head-mean scores, top-k,
            union and cap
   brute    pure-Python loop versions of all of the above for tiny inputs
+  surface  marching cubes at SDF = 0 on the decoded volume (the surface
+           extraction stage that follows decoding)
 
 Parity status: every function is pinned by a CPU test (closed forms,
 invariants, library routines or brute force on tiny inputs); see the
@@ -32,4 +34,4 @@ weights have no printed values on the pages; they are pinned through the
 brute-force loops and the closed-form special cases.
 """
 
-from . import bf16, decoder, hvd, akvs, brute  # noqa: F401
+from . import bf16, decoder, hvd, akvs, brute, surface  # noqa: F401
