@@ -228,12 +228,49 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* params
                            int64_t* stats, const vdm_hier_debug* dbg, void* ws, size_t ws_bytes,
                            vdm_stream stream);
 
+/* Surface extraction: the stage that follows VAE decoding in a vecset diffusion
+ * pipeline (techwalker article on FlashVDM, part 1, the four stages). The pages
+ * leave the method open; it is read here as marching cubes at SDF = 0 on the
+ * decoded grid.
+ * vol: [(R+1)^3] float32 values at the grid points x_i = -1 + 2 i / R, row-major
+ * (x slowest), as vdm_decode_hier writes them. cell_mask: optional [R^3] uint8,
+ * row-major cells (cell (i,j,k) has corners i..i+1, j..j+1, k..k+1); nonzero =
+ * extract the cell; NULL = every cell.
+ * - A point is inside when its value is < 0 (0 and NaN are outside).
+ * - Every grid edge whose end points differ in that test and that belongs to an
+ *   extracted cell carries one vertex, at the zero of the linear interpolant
+ *   along the edge (t = v0 / (v0 - v1) from the lower end point). Vertices are
+ *   numbered by ascending edge id a * (R+1)^3 + point index (a = 0, 1, 2 for
+ *   edges along x, y, z; point index = (i * (R+1) + j) * (R+1) + k).
+ * - A cell's surface is built face by face: a face with two crossing edges gets
+ *   one segment between them, a face with four (inside corners on a diagonal)
+ *   gets two segments that each cut off one inside corner. Segments are directed
+ *   so that the normal points from inside corners to outside ones, and chain
+ *   into loops. Each loop is split into a fan around the loop vertex of smallest
+ *   edge id among those that share no cube face with a loop vertex other than
+ *   their two loop neighbours; loops of a cell in order of their smallest edge
+ *   id; cells in row-major order.
+ * - Triangle normals (right-hand rule) point towards positive values; the mesh
+ *   is closed wherever the surface does not reach the volume's boundary or the
+ *   edge of the cell mask.
+ * Outputs (device): verts [max_verts][3] float32 world coordinates; tris
+ * [max_tris][3] int32 vertex ids; vert_edges [max_verts] int64 edge ids (may be
+ * NULL); counts [2] int64 = vertices and triangles of the whole mesh. Entries
+ * past max_verts / max_tris are not written: compare counts with the maxima
+ * once the stream has run (verts / tris may be NULL when their maximum is 0).
+ * Requires 1 <= R <= 893 (vertex ids fit int32). Workspace:
+ * vdm_surface_workspace_size(R). */
+vdm_status vdm_extract_surface(const float* vol, int32_t R, const uint8_t* cell_mask, float* verts,
+                               int64_t max_verts, int32_t* tris, int64_t max_tris, int64_t* vert_edges,
+                               int64_t* counts, void* ws, size_t ws_bytes, vdm_stream stream);
+
 /* ---------------------------------------------------------------- helpers */
 
 /* Workspace bytes for the calls above (0 with vdm_last_error set on bad args). */
 size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, int32_t with_sel);
 size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M);
 size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M);
+size_t vdm_surface_workspace_size(int32_t R);
 
 /* ---------------------------------------------------------------- kernel timing */
 
@@ -251,6 +288,7 @@ enum {
   VDM_TIME_SCAN,            /* prefix sums of per-block counts (three launches per level) */
   VDM_TIME_EMIT,            /* query list, work items and occupied blocks */
   VDM_TIME_FILL,            /* nearest-ancestor fill of the next level's volume */
+  VDM_TIME_SURFACE,         /* vdm_extract_surface (all of its launches) */
   VDM_TIME_KINDS
 };
 

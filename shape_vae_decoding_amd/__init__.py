@@ -33,10 +33,10 @@ STAT_NAMES = ["R", "tested", "active", "kept", "queries", "blocks", "items", "se
 EXPORTS = [
     "vdm_embed_queries", "vdm_project_kv", "vdm_decode_dense", "vdm_select_kv", "vdm_decode_hier",
     "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_timing",
-    "vdm_timing_read", "vdm_version", "vdm_last_error",
+    "vdm_timing_read", "vdm_version", "vdm_last_error", "vdm_extract_surface", "vdm_surface_workspace_size",
 ]
 TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "cell_test", "dilate", "mark", "scan",
-              "emit", "fill"]
+              "emit", "fill", "surface"]
 
 
 class VdmError(RuntimeError):
@@ -103,6 +103,11 @@ _lib.vdm_select_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64]
 _lib.vdm_select_workspace_size.restype = C.c_size_t
 _lib.vdm_hier_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int64]
 _lib.vdm_hier_workspace_size.restype = C.c_size_t
+_lib.vdm_extract_surface.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                                     C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.vdm_extract_surface.restype = _st
+_lib.vdm_surface_workspace_size.argtypes = [C.c_int32]
+_lib.vdm_surface_workspace_size.restype = C.c_size_t
 _lib.vdm_timing.argtypes = [C.c_int32]
 _lib.vdm_timing.restype = C.c_int
 _lib.vdm_timing_read.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
@@ -356,6 +361,40 @@ def vdm_decode_hier(dec: Decoder, params: _HierParams, K: torch.Tensor, V: torch
     _check(_lib.vdm_decode_hier(dec.ref, C.byref(params), K.data_ptr(), V.data_ptr(), M, vol.data_ptr(),
                                 vol.numel(), _ptr(stats), C.byref(dbg.struct) if dbg is not None else None,
                                 ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def vdm_surface_workspace_size(R: int) -> int:
+    n = _lib.vdm_surface_workspace_size(R)
+    if n == 0:
+        raise VdmError(-1, vdm_last_error())
+    return n
+
+
+def vdm_extract_surface(vol: torch.Tensor, R: int, verts: torch.Tensor, tris: torch.Tensor, counts: torch.Tensor,
+                        cell_mask: Optional[torch.Tensor] = None, vert_edges: Optional[torch.Tensor] = None,
+                        ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Marching cubes at SDF = 0 on the (R+1)^3 volume (see include/vdm.h).
+    verts [max_verts, 3] float32, tris [max_tris, 3] int32, counts [2] int64,
+    cell_mask [R^3] uint8 or None, vert_edges [max_verts] int64 or None."""
+    _dev(vol, torch.float32, "vol")
+    _dev(verts, torch.float32, "verts")
+    _dev(tris, torch.int32, "tris")
+    _dev(counts, torch.int64, "counts")
+    if vol.numel() < (R + 1) ** 3:
+        raise ValueError(f"vol holds {vol.numel()} values, (R+1)^3 = {(R + 1) ** 3} needed")
+    if cell_mask is not None:
+        _dev(cell_mask, torch.uint8, "cell_mask")
+        if cell_mask.numel() < R ** 3:
+            raise ValueError(f"cell_mask holds {cell_mask.numel()} cells, R^3 = {R ** 3} needed")
+    if vert_edges is not None:
+        _dev(vert_edges, torch.int64, "vert_edges")
+        if vert_edges.numel() < verts.numel() // 3:
+            raise ValueError("vert_edges must hold max_verts entries")
+    if ws is None:
+        ws = workspace(vdm_surface_workspace_size(R), vol.device)
+    _check(_lib.vdm_extract_surface(vol.data_ptr(), R, _ptr(cell_mask), verts.data_ptr(), verts.numel() // 3,
+                                    tris.data_ptr(), tris.numel() // 3, _ptr(vert_edges), counts.data_ptr(),
+                                    ws.data_ptr(), ws.numel(), _stream(stream)))
 
 
 def stats_dict(stats: torch.Tensor, levels: int):

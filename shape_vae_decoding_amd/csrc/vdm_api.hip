@@ -388,6 +388,39 @@ size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* pa
   return hier_ws(dec, params, M, nullptr, nullptr);
 }
 
+// ------------------------------------------------------------------ surface extraction
+static vdm_status check_surface(int32_t R) {
+  if (R < 1 || R > 893) return fail(VDM_ERR_INVALID_ARG, "R=%d (1 <= R <= 893)", R);
+  return VDM_OK;
+}
+
+size_t vdm_surface_workspace_size(int32_t R) {
+  if (check_surface(R) != VDM_OK) return 0;
+  return surface_ws_layout(R).bytes;
+}
+
+vdm_status vdm_extract_surface(const float* vol, int32_t R, const uint8_t* cell_mask, float* verts,
+                               int64_t max_verts, int32_t* tris, int64_t max_tris, int64_t* vert_edges,
+                               int64_t* counts, void* ws, size_t ws_bytes, vdm_stream stream) {
+  vdm_status st = check_surface(R);
+  if (st != VDM_OK) return st;
+  if (!vol || !counts) return fail(VDM_ERR_INVALID_ARG, "vol or counts is NULL");
+  if (max_verts < 0 || max_tris < 0) return fail(VDM_ERR_INVALID_ARG, "negative max_verts or max_tris");
+  if ((max_verts > 0 && !verts) || (max_tris > 0 && !tris))
+    return fail(VDM_ERR_INVALID_ARG, "verts or tris is NULL with a nonzero maximum");
+  if (!aligned(vol, 4) || !aligned(counts, 8) || !aligned(verts, 4) || !aligned(tris, 4) || !aligned(vert_edges, 8))
+    return fail(VDM_ERR_INVALID_ARG, "misaligned vol, verts, tris (4 bytes) or counts, vert_edges (8 bytes)");
+  const size_t need = surface_ws_layout(R).bytes;
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(VDM_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", need, ws_bytes);
+  (void)hipGetLastError();
+  VDM_HIP_T(VDM_TIME_SURFACE, (hipStream_t)stream,
+            launch_surface(vol, R, cell_mask, verts, max_verts, tris, max_tris, vert_edges, counts, (char*)ws,
+                           (hipStream_t)stream),
+            "surface launch");
+  return VDM_OK;
+}
+
 vdm_status vdm_embed_queries(const vdm_decoder* dec, const float* xyz, int64_t N, void* Q, vdm_stream stream) {
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;

@@ -147,3 +147,33 @@ def test_timing_api_without_launches():
     n, ms = C.c_int64(), C.c_double()
     assert V._lib.vdm_timing_read(len(V.TIME_KINDS), C.byref(n), C.byref(ms)) == V.VDM_ERR_INVALID_ARG
     assert V._lib.vdm_timing_read(0, None, C.byref(ms)) == V.VDM_ERR_INVALID_ARG
+
+
+def test_surface_extraction_argument_checks():
+    import shape_vae_decoding_amd as V
+
+    lib = V._lib
+    fake = 0x100000  # never dereferenced: every case fails validation first
+    assert lib.vdm_surface_workspace_size(0) == 0 and "R=0" in V.vdm_last_error()
+    assert lib.vdm_surface_workspace_size(894) == 0
+    n300 = lib.vdm_surface_workspace_size(300)
+    # two bit planes' worth per axis (bits + int32 prefixes) plus partial sums
+    words = 3 * ((301 ** 3 + 63) // 64)
+    assert 12 * words <= n300 <= 12 * words + 8 * (words // 2048 + 300 ** 3 // 2048 + 8) + 4 * 256
+    ok = dict(vol=fake, R=300, mask=None, verts=fake, mv=10, tris=fake, mt=10, edges=None, counts=fake,
+              ws=fake, wsb=n300)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.vdm_extract_surface(a["vol"], a["R"], a["mask"], a["verts"], a["mv"], a["tris"], a["mt"],
+                                       a["edges"], a["counts"], a["ws"], a["wsb"], None)
+
+    assert call(R=0) == V.VDM_ERR_INVALID_ARG
+    assert call(vol=None) == V.VDM_ERR_INVALID_ARG
+    assert call(counts=None) == V.VDM_ERR_INVALID_ARG
+    assert call(verts=None) == V.VDM_ERR_INVALID_ARG
+    assert call(mt=-1) == V.VDM_ERR_INVALID_ARG
+    assert call(vol=fake + 2) == V.VDM_ERR_INVALID_ARG and "misaligned" in V.vdm_last_error()
+    assert call(edges=fake + 4) == V.VDM_ERR_INVALID_ARG
+    assert call(wsb=n300 - 1) == V.VDM_ERR_WORKSPACE
+    assert call(ws=fake + 16) == V.VDM_ERR_WORKSPACE
