@@ -218,6 +218,37 @@ def large_token_decode(V, W, dev, reps: int = 5):
             "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
+def surface_extraction(V, vol, R: int, dev, reps: int = 10):
+    """Marching cubes at SDF = 0 on the hierarchical decode's (R+1)^3 volume
+    (outside the timed steps). Launch time from the library's HIP events around
+    the whole call; algorithmic bytes = the volume read once + the mesh written."""
+    import torch
+
+    counts = torch.zeros(2, dtype=torch.int64, device=dev)
+    ws = V.workspace(V.vdm_surface_workspace_size(R), dev)
+    none_f = torch.empty((0, 3), dtype=torch.float32, device=dev)
+    none_i = torch.empty((0, 3), dtype=torch.int32, device=dev)
+    V.vdm_extract_surface(vol, R, none_f, none_i, counts, ws=ws)  # sizes only
+    nv, nt = (int(x) for x in counts.cpu().tolist())
+    verts = torch.empty((nv, 3), dtype=torch.float32, device=dev)
+    tris = torch.empty((nt, 3), dtype=torch.int32, device=dev)
+    V.vdm_extract_surface(vol, R, verts, tris, counts, ws=ws)
+    torch.cuda.synchronize()
+    V.vdm_timing(2)
+    V.vdm_timing(1)
+    for _ in range(reps):
+        V.vdm_extract_surface(vol, R, verts, tris, counts, ws=ws)
+    V.vdm_timing(0)
+    n, ms = V.vdm_timing_read("surface")
+    V.vdm_timing(2)
+    launch_ms = ms / n
+    nbytes = 4 * (R + 1) ** 3 + 12 * nv + 12 * nt
+    gbs = nbytes / (launch_ms / 1e3) / 1e9
+    return {"R": R, "vertices": nv, "triangles": nt, "ms_per_call": round(launch_ms, 4),
+            "volume_points_per_s": round((R + 1) ** 3 / (launch_ms / 1e3), 1),
+            "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 5):
     """Achievable HBM bandwidth: a device-to-device copy (read + write bytes / time)."""
     import torch
@@ -399,6 +430,8 @@ def main():
         },
         "roofline": roofline,
     }
+    # outside the timed steps: surface extraction of the hierarchical volume
+    out["breakdown"]["surface_extraction_300cubed"] = surface_extraction(V, vol_h, Pf - 1, dev)
     if not args.skip_cpu:
         # outside the timed steps (and left out of profiling runs): the large-token
         # workload and the machine's reference figures

@@ -182,39 +182,48 @@ constexpr McTable build_table() {
 __constant__ McTable kTable = build_table();
 
 // ------------------------------------------------------------------ kernels
-constexpr int SF_NT = 256;         // threads per block
-constexpr int SF_CPT = 8;          // consecutive cells per thread
-constexpr int SF_CPB = SF_NT * SF_CPT;
-constexpr int SF_WPT = 8;          // edge words per thread in the word scan
+// Every index fits 32 bits: R <= 893 keeps 3 (R+1)^3 below 2^31.
+constexpr int SF_NT = 256;              // threads per block (4 waves)
+// Cells go by row pieces: a piece is 64 consecutive cells (i, j, 64 kc .. 64 kc + 63)
+// of one row, one per lane (the last piece of a row is ragged); a wave takes SF_IPW
+// consecutive pieces, a block SF_PPB.
+constexpr int SF_IPW = 8;
+constexpr int SF_PPB = SF_IPW * (SF_NT / 64);
+constexpr int SF_WPT = 8;               // edge words per thread in the word scan
 constexpr int SF_WPB = SF_NT * SF_WPT;
+constexpr int SF_PPT = 16;              // partial sums per thread in the one-block scan
 
 __device__ __forceinline__ bool inside(float v) { return v < 0.f; }
 
 __device__ __forceinline__ bool cell_listed(const uint8_t* mask, int R, int i, int j, int k) {
-  return i >= 0 && j >= 0 && k >= 0 && i < R && j < R && k < R && mask[((int64_t)i * R + j) * R + k] != 0;
+  return i >= 0 && j >= 0 && k >= 0 && i < R && j < R && k < R && mask[(i * R + j) * R + k] != 0;
 }
 
-// Crossing-edge bits: wave m covers points 64 m .. 64 m + 63; lane 0..2 writes the
-// wave's word of axis a at words[a * nwa + m]. With a cell mask, an edge counts
-// only when one of the (up to 4) cells around it is listed.
+// Crossing-edge bits and inside bits: wave m covers points 64 m .. 64 m + 63;
+// lanes 0..2 write the wave's word of each axis plane (words[a * nwa + m]),
+// lane 3 the inside bits (ins[m]). With a cell mask an edge counts only when one
+// of the (up to 4) cells around it is listed.
 __global__ __launch_bounds__(SF_NT) void sf_edges_kernel(const float* __restrict__ vol, int R,
                                                          const uint8_t* __restrict__ mask,
-                                                         uint64_t* __restrict__ words, int64_t nwa) {
-  const int P = R + 1;
-  const int64_t NP = (int64_t)P * P * P;
+                                                         uint64_t* __restrict__ words, uint64_t* __restrict__ ins,
+                                                         int nwa) {
+  const int P = R + 1, PP = P * P, NP = PP * P;
   const int lane = threadIdx.x & 63;
-  const int64_t waves = (int64_t)gridDim.x * (SF_NT / 64);
-  for (int64_t m = ((int64_t)blockIdx.x * SF_NT + threadIdx.x) / 64; m < nwa; m += waves) {
-    const int64_t p = 64 * m + lane;
-    bool f0 = false, f1 = false, f2 = false;
-    if (p < NP) {
-      const int i = (int)(p / ((int64_t)P * P));
-      const int r = (int)(p - (int64_t)i * P * P);
-      const int j = r / P, k = r - j * P;
-      const bool in = inside(vol[p]);
-      if (i < R) f0 = in != inside(vol[p + (int64_t)P * P]);
-      if (j < R) f1 = in != inside(vol[p + P]);
-      if (k < R) f2 = in != inside(vol[p + 1]);
+  const int waves = gridDim.x * (SF_NT / 64);
+  if (blockIdx.x == 0 && threadIdx.x == 0) ins[nwa] = 0;  // the spare word (read only for points past the grid)
+  for (int m = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6); m < nwa; m += waves) {
+    const int p = 64 * m + lane;
+    // all four loads unconditional (clamped addresses), so they are in flight together
+    const int pc = min(p, NP - 1);
+    const float v = vol[pc], vi = vol[min(pc + PP, NP - 1)], vj = vol[min(pc + P, NP - 1)], vk = vol[pc + (pc + 1 < NP)];
+    const int row = pc / P, k = pc - row * P;
+    const int i = row / P, j = row - i * P;
+    const bool ok = p < NP;
+    const bool in = ok && inside(v);
+    bool f0 = ok && i < R && inside(v) != inside(vi);
+    bool f1 = ok && j < R && inside(v) != inside(vj);
+    bool f2 = ok && k < R && inside(v) != inside(vk);
+    {
       if (mask) {
         // cells holding edge (p, a): lower corner p minus 0/1 along the other two axes
         if (f0) f0 = cell_listed(mask, R, i, j, k) || cell_listed(mask, R, i, j - 1, k) ||
@@ -225,8 +234,9 @@ __global__ __launch_bounds__(SF_NT) void sf_edges_kernel(const float* __restrict
                      cell_listed(mask, R, i, j - 1, k) || cell_listed(mask, R, i - 1, j - 1, k);
       }
     }
-    const uint64_t b0 = __ballot(f0), b1 = __ballot(f1), b2 = __ballot(f2);
+    const uint64_t b0 = __ballot(f0), b1 = __ballot(f1), b2 = __ballot(f2), bi = __ballot(in);
     if (lane < 3) words[lane * nwa + m] = lane == 0 ? b0 : (lane == 1 ? b1 : b2);
+    if (lane == 3) ins[m] = bi;
   }
 }
 
@@ -250,10 +260,10 @@ __device__ __forceinline__ int64_t block_exclusive(int64_t v, int64_t* red, int6
   return before + x - v;
 }
 
-__global__ __launch_bounds__(SF_NT) void sf_word_sums_kernel(const uint64_t* __restrict__ words, int64_t n,
+__global__ __launch_bounds__(SF_NT) void sf_word_sums_kernel(const uint64_t* __restrict__ words, int n,
                                                              int64_t* __restrict__ part) {
   __shared__ int64_t red[SF_NT / 64];
-  const int64_t base = (int64_t)blockIdx.x * SF_WPB + (int64_t)threadIdx.x * SF_WPT;
+  const int base = blockIdx.x * SF_WPB + threadIdx.x * SF_WPT;
   int64_t c = 0;
 #pragma unroll
   for (int q = 0; q < SF_WPT; ++q)
@@ -264,16 +274,26 @@ __global__ __launch_bounds__(SF_NT) void sf_word_sums_kernel(const uint64_t* __r
 }
 
 // In-place exclusive scan of part[0 .. nb) by one block; the total goes to *total.
-__global__ __launch_bounds__(SF_NT) void sf_scan_parts_kernel(int64_t* __restrict__ part, int64_t nb,
+__global__ __launch_bounds__(SF_NT) void sf_scan_parts_kernel(int64_t* __restrict__ part, int nb,
                                                               int64_t* __restrict__ total) {
   __shared__ int64_t red[SF_NT / 64];
   int64_t carry = 0;
-  for (int64_t b0 = 0; b0 < nb; b0 += SF_NT) {
-    const int64_t b = b0 + threadIdx.x;
-    const int64_t v = b < nb ? part[b] : 0;
+  for (int b0 = 0; b0 < nb; b0 += SF_NT * SF_PPT) {
+    const int base = b0 + threadIdx.x * SF_PPT;
+    int64_t v[SF_PPT], s = 0;
+#pragma unroll
+    for (int q = 0; q < SF_PPT; ++q) {
+      v[q] = base + q < nb ? part[base + q] : 0;
+      s += v[q];
+    }
     int64_t t;
-    const int64_t ex = block_exclusive(v, red, t);
-    if (b < nb) part[b] = carry + ex;
+    int64_t run = carry + block_exclusive(s, red, t);
+#pragma unroll
+    for (int q = 0; q < SF_PPT; ++q)
+      if (base + q < nb) {
+        part[base + q] = run;
+        run += v[q];
+      }
     carry += t;
     __syncthreads();
   }
@@ -281,11 +301,11 @@ __global__ __launch_bounds__(SF_NT) void sf_scan_parts_kernel(int64_t* __restric
 }
 
 // Per-word prefix (vertex id of the word's first set bit).
-__global__ __launch_bounds__(SF_NT) void sf_word_prefix_kernel(const uint64_t* __restrict__ words, int64_t n,
+__global__ __launch_bounds__(SF_NT) void sf_word_prefix_kernel(const uint64_t* __restrict__ words, int n,
                                                                const int64_t* __restrict__ part,
                                                                int32_t* __restrict__ prefix) {
   __shared__ int64_t red[SF_NT / 64];
-  const int64_t base = (int64_t)blockIdx.x * SF_WPB + (int64_t)threadIdx.x * SF_WPT;
+  const int base = blockIdx.x * SF_WPB + threadIdx.x * SF_WPT;
   int c[SF_WPT];
   int64_t s = 0;
 #pragma unroll
@@ -303,47 +323,61 @@ __global__ __launch_bounds__(SF_NT) void sf_word_prefix_kernel(const uint64_t* _
     }
 }
 
-__device__ __forceinline__ int cell_case(const float* __restrict__ vol, int P, int64_t p0) {
-  const int64_t PP = (int64_t)P * P;
+// One row piece (see SF_IPW): its cells' cases, triangle counts and lower corners.
+// The inside bits of the four corner rows come from two scalar word loads each
+// (the piece's 65 points of a row span at most two words); ins has one spare
+// word after the last one.
+struct Piece {
+  int cs, nt, p0;
+};
+__device__ __forceinline__ Piece piece_cell(const uint64_t* __restrict__ ins, int R, const uint8_t* __restrict__ mask,
+                                            const unsigned char* ntri, int piece, int lane) {
+  const int P = R + 1, KC = (R + 63) >> 6;
+  Piece out{0, 0, 0};
+  const int r = piece / KC, kc = piece - r * KC;  // wave-uniform
+  if (r >= R * R) return out;
+  const int i = r / R, j = r - i * R;
+  const int k = 64 * kc + lane;
   int cs = 0;
 #pragma unroll
   for (int di = 0; di < 2; ++di)
 #pragma unroll
-    for (int dj = 0; dj < 2; ++dj)
-#pragma unroll
-      for (int dk = 0; dk < 2; ++dk)
-        cs |= (int)inside(vol[p0 + di * PP + dj * P + dk]) << (4 * di + 2 * dj + dk);
-  return cs;
+    for (int dj = 0; dj < 2; ++dj) {
+      const int start = ((i + di) * P + (j + dj)) * P + 64 * kc;
+      const int w = start >> 6, sh = start & 63;
+      const uint64_t w0 = ins[w], w1 = ins[w + 1];
+      const uint64_t lo = sh ? (w0 >> sh) | (w1 << (64 - sh)) : w0;
+      const int b0 = (int)((lo >> lane) & 1ull);
+      const int b1 = lane < 63 ? (int)((lo >> (lane + 1)) & 1ull) : (int)((w1 >> sh) & 1ull);
+      cs |= b0 << (4 * di + 2 * dj) | b1 << (4 * di + 2 * dj + 1);
+    }
+  const int c = (i * R + j) * R + k;
+  const bool ok = k < R && (!mask || mask[min(c, R * R * R - 1)] != 0);
+  out.cs = cs;
+  out.nt = ok ? ntri[cs] : 0;
+  out.p0 = (i * P + j) * P + k;
+  return out;
 }
 
-// Triangle counts of cells c0 .. c0 + SF_CPT - 1 (0 outside the grid or the mask).
-__device__ __forceinline__ void run_counts(const float* __restrict__ vol, int R, const uint8_t* __restrict__ mask,
-                                           int64_t c0, int (&cs)[SF_CPT], int (&nt)[SF_CPT]) {
-  const int P = R + 1;
-  const int64_t NC = (int64_t)R * R * R;
-#pragma unroll
-  for (int q = 0; q < SF_CPT; ++q) {
-    const int64_t c = c0 + q;
-    cs[q] = 0;
-    nt[q] = 0;
-    if (c >= NC || (mask && !mask[c])) continue;
-    const int i = (int)(c / ((int64_t)R * R));
-    const int r = (int)(c - (int64_t)i * R * R);
-    const int j = r / R, k = r - j * R;
-    cs[q] = cell_case(vol, P, ((int64_t)i * P + j) * P + k);
-    nt[q] = kTable.c[cs[q]].ntri;
-  }
+__device__ __forceinline__ void load_ntri(unsigned char* ntri) {
+  for (int c = threadIdx.x; c < 256; c += SF_NT) ntri[c] = kTable.c[c].ntri;
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(SF_NT) void sf_cell_sums_kernel(const float* __restrict__ vol, int R,
+__device__ __forceinline__ int piece_of(int q) {
+  return __builtin_amdgcn_readfirstlane(blockIdx.x * SF_PPB + (threadIdx.x >> 6) * SF_IPW + q);
+}
+
+__global__ __launch_bounds__(SF_NT) void sf_cell_sums_kernel(const uint64_t* __restrict__ ins, int R,
                                                              const uint8_t* __restrict__ mask,
                                                              int64_t* __restrict__ part) {
   __shared__ int64_t red[SF_NT / 64];
-  int cs[SF_CPT], nt[SF_CPT];
-  run_counts(vol, R, mask, (int64_t)blockIdx.x * SF_CPB + (int64_t)threadIdx.x * SF_CPT, cs, nt);
+  __shared__ unsigned char ntri[256];
+  load_ntri(ntri);
+  const int lane = threadIdx.x & 63;
   int64_t s = 0;
 #pragma unroll
-  for (int q = 0; q < SF_CPT; ++q) s += nt[q];
+  for (int q = 0; q < SF_IPW; ++q) s += piece_cell(ins, R, mask, ntri, piece_of(q), lane).nt;
   int64_t total;
   block_exclusive(s, red, total);
   if (threadIdx.x == 0) part[blockIdx.x] = total;
@@ -351,48 +385,57 @@ __global__ __launch_bounds__(SF_NT) void sf_cell_sums_kernel(const float* __rest
 
 // Vertex id of global edge (axis a, point p): rank of its bit.
 __device__ __forceinline__ int32_t vertex_of(const uint64_t* __restrict__ words, const int32_t* __restrict__ prefix,
-                                            int64_t nwa, int a, int64_t p) {
-  const int64_t w = a * nwa + (p >> 6);
+                                            int nwa, int a, int p) {
+  const int w = a * nwa + (p >> 6);
   const uint64_t below = words[w] & ((1ull << (p & 63)) - 1ull);
   return prefix[w] + __popcll(below);
 }
 
-__global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(const float* __restrict__ vol, int R,
+__global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(const uint64_t* __restrict__ ins, int R,
                                                              const uint8_t* __restrict__ mask,
                                                              const uint64_t* __restrict__ words,
-                                                             const int32_t* __restrict__ prefix, int64_t nwa,
+                                                             const int32_t* __restrict__ prefix, int nwa,
                                                              const int64_t* __restrict__ part,
                                                              int32_t* __restrict__ tris, int64_t max_tris) {
   __shared__ int64_t red[SF_NT / 64];
-  const int P = R + 1;
-  const int64_t PP = (int64_t)P * P;
-  const int64_t c0 = (int64_t)blockIdx.x * SF_CPB + (int64_t)threadIdx.x * SF_CPT;
-  int cs[SF_CPT], nt[SF_CPT];
-  run_counts(vol, R, mask, c0, cs, nt);
+  __shared__ unsigned char ntri[256];
+  load_ntri(ntri);
+  const int P = R + 1, PP = P * P;
+  const int lane = threadIdx.x & 63;
+  Piece pc[SF_IPW];
   int64_t s = 0;
 #pragma unroll
-  for (int q = 0; q < SF_CPT; ++q) s += nt[q];
+  for (int q = 0; q < SF_IPW; ++q) {
+    pc[q] = piece_cell(ins, R, mask, ntri, piece_of(q), lane);
+    s += pc[q].nt;
+  }
+  // this wave's first triangle: block offset + the triangles of the waves before it
   int64_t total;
-  int64_t t = part[blockIdx.x] + block_exclusive(s, red, total);
-  for (int q = 0; q < SF_CPT; ++q) {
-    if (nt[q] == 0) continue;
-    const int64_t c = c0 + q;
-    const int i = (int)(c / ((int64_t)R * R));
-    const int r = (int)(c - (int64_t)i * R * R);
-    const int j = r / R, k = r - j * R;
-    const int64_t p0 = ((int64_t)i * P + j) * P + k;
-    const McCase& mc = kTable.c[cs[q]];
-    for (int m = 0; m < mc.ntri; ++m, ++t) {
-      if (t >= max_tris) continue;
+  const int64_t before = block_exclusive(s, red, total);
+  int64_t t = part[blockIdx.x] + __shfl(before, 0);
+#pragma unroll
+  for (int q = 0; q < SF_IPW; ++q) {
+    int x = pc[q].nt;  // inclusive scan over the piece's cells (lane order = cell order)
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    int64_t u = t + x - pc[q].nt;
+    t += __shfl(x, 63);
+    if (pc[q].nt == 0) continue;
+    const McCase& mc = kTable.c[pc[q].cs];
+    for (int m = 0; m < pc[q].nt; ++m, ++u) {
+      if (u >= max_tris) continue;
       int32_t v[3];
 #pragma unroll
-      for (int x = 0; x < 3; ++x) {
-        const int code = mc.e[m][x];
-        v[x] = vertex_of(words, prefix, nwa, code >> 3, p0 + ((code >> 2) & 1) * PP + ((code >> 1) & 1) * P + (code & 1));
+      for (int x3 = 0; x3 < 3; ++x3) {
+        const int code = mc.e[m][x3];
+        v[x3] = vertex_of(words, prefix, nwa, code >> 3,
+                          pc[q].p0 + ((code >> 2) & 1) * PP + ((code >> 1) & 1) * P + (code & 1));
       }
-      tris[3 * t + 0] = v[0];
-      tris[3 * t + 1] = v[1];
-      tris[3 * t + 2] = v[2];
+      tris[3 * u + 0] = v[0];
+      tris[3 * u + 1] = v[1];
+      tris[3 * u + 2] = v[2];
     }
   }
 }
@@ -400,45 +443,43 @@ __global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(const float* __rest
 // Vertex positions (and optionally edge ids), one thread per point.
 __global__ __launch_bounds__(SF_NT) void sf_vertices_kernel(const float* __restrict__ vol, int R,
                                                             const uint64_t* __restrict__ words,
-                                                            const int32_t* __restrict__ prefix, int64_t nwa,
+                                                            const int32_t* __restrict__ prefix, int nwa,
                                                             float* __restrict__ verts, int64_t max_verts,
                                                             int64_t* __restrict__ vert_edges) {
-  const int P = R + 1;
-  const int64_t PP = (int64_t)P * P, NP = PP * P;
+  const int P = R + 1, PP = P * P, NP = PP * P;
   const float h = 2.0f / (float)R;
-  const int64_t stride = (int64_t)gridDim.x * SF_NT;
-  for (int64_t p = (int64_t)blockIdx.x * SF_NT + threadIdx.x; p < 64 * nwa; p += stride) {
-    if (p >= NP) continue;
-    const int64_t m = p >> 6;
+  const int lane = threadIdx.x & 63;
+  const int waves = gridDim.x * (SF_NT / 64);
+  for (int m = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6); m < nwa; m += waves) {
+    const uint64_t w0 = words[m], w1 = words[nwa + m], w2 = words[2 * nwa + m];  // wave-uniform
+    if ((w0 | w1 | w2) == 0) continue;
+    const int p = 64 * m + lane;
+    if (!((w0 | w1 | w2) >> lane & 1ull) || p >= NP) continue;
     const uint64_t low = (1ull << (p & 63)) - 1ull;
+    const int row = p / P, k = p - row * P;
+    const int i = row / P, j = row - i * P;
+    const float v0 = vol[p];
+    const float bx = fmaf((float)i, h, -1.f), by = fmaf((float)j, h, -1.f), bz = fmaf((float)k, h, -1.f);
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-      const uint64_t w = words[a * nwa + m];
+      const uint64_t w = a == 0 ? w0 : (a == 1 ? w1 : w2);
       if (!((w >> (p & 63)) & 1ull)) continue;
       const int64_t vid = prefix[a * nwa + m] + __popcll(w & low);
       if (vid >= max_verts) continue;
-      const int i = (int)(p / PP);
-      const int r = (int)(p - (int64_t)i * PP);
-      const int j = r / P, k = r - j * P;
-      const int64_t step = a == 0 ? PP : (a == 1 ? (int64_t)P : 1);
-      const float v0 = vol[p], v1 = vol[p + step];
+      const float v1 = vol[p + (a == 0 ? PP : (a == 1 ? P : 1))];
       const float t = v0 / (v0 - v1);
-      float x = fmaf((float)i, h, -1.f), y = fmaf((float)j, h, -1.f), z = fmaf((float)k, h, -1.f);
-      if (a == 0) x = fmaf(t, h, x);
-      if (a == 1) y = fmaf(t, h, y);
-      if (a == 2) z = fmaf(t, h, z);
-      verts[3 * vid + 0] = x;
-      verts[3 * vid + 1] = y;
-      verts[3 * vid + 2] = z;
-      if (vert_edges) vert_edges[vid] = a * NP + p;
+      verts[3 * vid + 0] = a == 0 ? fmaf(t, h, bx) : bx;
+      verts[3 * vid + 1] = a == 1 ? fmaf(t, h, by) : by;
+      verts[3 * vid + 2] = a == 2 ? fmaf(t, h, bz) : bz;
+      if (vert_edges) vert_edges[vid] = (int64_t)a * NP + p;
     }
   }
 }
 
-int64_t grid_blocks(int64_t work, int64_t per_block, int64_t cap) {
+int grid_blocks(int64_t work, int64_t per_block, int64_t cap) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g > cap) g = cap;
-  return g < 1 ? 1 : g;
+  return g < 1 ? 1 : (int)g;
 }
 
 }  // namespace
@@ -449,7 +490,9 @@ SurfaceWs surface_ws_layout(int R) {
   w.nwa = (NP + 63) / 64;
   w.nwords = 3 * w.nwa;
   w.nwb = (w.nwords + SF_WPB - 1) / SF_WPB;
-  w.ncb = (NC + SF_CPB - 1) / SF_CPB;
+  const int64_t pieces = (int64_t)R * R * ((R + 63) / 64);
+  w.ncb = (pieces + SF_PPB - 1) / SF_PPB;
+  (void)NC;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -457,6 +500,7 @@ SurfaceWs surface_ws_layout(int R) {
     return o;
   };
   w.off_words = take(8 * w.nwords);
+  w.off_ins = take(8 * (w.nwa + 1));
   w.off_prefix = take(4 * w.nwords);
   w.off_wpart = take(8 * w.nwb);
   w.off_cpart = take(8 * w.ncb);
@@ -469,21 +513,23 @@ hipError_t launch_surface(const float* vol, int R, const uint8_t* mask, float* v
                           hipStream_t s) {
   const SurfaceWs w = surface_ws_layout(R);
   uint64_t* words = reinterpret_cast<uint64_t*>(ws + w.off_words);
+  uint64_t* ins = reinterpret_cast<uint64_t*>(ws + w.off_ins);
   int32_t* prefix = reinterpret_cast<int32_t*>(ws + w.off_prefix);
   int64_t* wpart = reinterpret_cast<int64_t*>(ws + w.off_wpart);
   int64_t* cpart = reinterpret_cast<int64_t*>(ws + w.off_cpart);
   const int64_t cus = dev_info().cus;
-  hipLaunchKernelGGL(sf_edges_kernel, dim3((unsigned)grid_blocks(w.nwa, SF_NT / 64, 64 * cus)), dim3(SF_NT), 0, s,
-                     vol, R, mask, words, w.nwa);
-  hipLaunchKernelGGL(sf_word_sums_kernel, dim3((unsigned)w.nwb), dim3(SF_NT), 0, s, words, w.nwords, wpart);
-  hipLaunchKernelGGL(sf_scan_parts_kernel, dim3(1), dim3(SF_NT), 0, s, wpart, w.nwb, counts);
-  hipLaunchKernelGGL(sf_word_prefix_kernel, dim3((unsigned)w.nwb), dim3(SF_NT), 0, s, words, w.nwords, wpart, prefix);
-  hipLaunchKernelGGL(sf_cell_sums_kernel, dim3((unsigned)w.ncb), dim3(SF_NT), 0, s, vol, R, mask, cpart);
-  hipLaunchKernelGGL(sf_scan_parts_kernel, dim3(1), dim3(SF_NT), 0, s, cpart, w.ncb, counts + 1);
-  hipLaunchKernelGGL(sf_triangles_kernel, dim3((unsigned)w.ncb), dim3(SF_NT), 0, s, vol, R, mask, words, prefix,
-                     w.nwa, cpart, tris, max_tris);
-  hipLaunchKernelGGL(sf_vertices_kernel, dim3((unsigned)grid_blocks(64 * w.nwa, SF_NT, 64 * cus)), dim3(SF_NT), 0, s,
-                     vol, R, words, prefix, w.nwa, verts, max_verts, vert_edges);
+  const int nwa = (int)w.nwa, nwords = (int)w.nwords, nwb = (int)w.nwb, ncb = (int)w.ncb;
+  hipLaunchKernelGGL(sf_edges_kernel, dim3(grid_blocks(w.nwa, SF_NT / 64, 64 * cus)), dim3(SF_NT), 0, s, vol, R,
+                     mask, words, ins, nwa);
+  hipLaunchKernelGGL(sf_word_sums_kernel, dim3(nwb), dim3(SF_NT), 0, s, words, nwords, wpart);
+  hipLaunchKernelGGL(sf_scan_parts_kernel, dim3(1), dim3(SF_NT), 0, s, wpart, nwb, counts);
+  hipLaunchKernelGGL(sf_word_prefix_kernel, dim3(nwb), dim3(SF_NT), 0, s, words, nwords, wpart, prefix);
+  hipLaunchKernelGGL(sf_cell_sums_kernel, dim3(ncb), dim3(SF_NT), 0, s, ins, R, mask, cpart);
+  hipLaunchKernelGGL(sf_scan_parts_kernel, dim3(1), dim3(SF_NT), 0, s, cpart, ncb, counts + 1);
+  hipLaunchKernelGGL(sf_triangles_kernel, dim3(ncb), dim3(SF_NT), 0, s, ins, R, mask, words, prefix, nwa, cpart, tris,
+                     max_tris);
+  hipLaunchKernelGGL(sf_vertices_kernel, dim3(grid_blocks(64 * w.nwa, SF_NT, 64 * cus)), dim3(SF_NT), 0, s, vol, R,
+                     words, prefix, nwa, verts, max_verts, vert_edges);
   return hipGetLastError();
 }
 
