@@ -17,10 +17,16 @@
 //     inner fan edge then lies in a face the next cell also triangulates); loops
 //     of a cell in order of their smallest edge id, cells in row-major order.
 //
-// GPU layout: one bit per grid edge, per axis a bit plane of ceil(P^3 / 64)
-// words (bit = point index); a vertex id is the rank of its bit, from per-word
-// prefix counts. Cells are processed in runs of SF_CPT consecutive cells per
-// thread; a cell's first triangle index comes from per-block prefix counts.
+// GPU layout: a point row (i, j) is cut into pieces of 63 points, k = 63 kc + l,
+// l < 63; one 64-bit word per piece holds one bit per point (bit 63 unused), so a
+// wave of 64 lanes reads a piece plus the next point and writes whole words.
+// Per axis a plane of such words marks the crossing edges (bit = lower end
+// point); a vertex id is the rank of its bit over the planes in order, from
+// per-word prefix counts. A fourth plane holds the inside bits (bit 63 = the
+// next piece's first point). One pass over the volume (each wave walks a column
+// of pieces along i, so every value is loaded about twice) writes the planes and
+// the triangle count of every piece; a cell's first triangle index comes from
+// the prefix of those counts.
 #include "vdm_internal.hpp"
 
 namespace vdm {
@@ -182,16 +188,14 @@ constexpr McTable build_table() {
 __constant__ McTable kTable = build_table();
 
 // ------------------------------------------------------------------ kernels
-// Every index fits 32 bits: R <= 893 keeps 3 (R+1)^3 below 2^31.
-constexpr int SF_NT = 256;              // threads per block (4 waves)
-// Cells go by row pieces: a piece is 64 consecutive cells (i, j, 64 kc .. 64 kc + 63)
-// of one row, one per lane (the last piece of a row is ragged); a wave takes SF_IPW
-// consecutive pieces, a block SF_PPB.
-constexpr int SF_IPW = 8;
-constexpr int SF_PPB = SF_IPW * (SF_NT / 64);
-constexpr int SF_WPT = 8;               // edge words per thread in the word scan
+// Point and vertex indices fit 32 bits: R <= 893 keeps 3 (R+1)^3 below 2^31.
+constexpr int SF_NT = 256;   // threads per block (4 waves)
+constexpr int SF_PW = 63;    // points per piece
+constexpr int SF_IC = 16;    // pieces along i per wave in the volume pass
+constexpr int SF_TPW = 8;    // pieces per wave in the triangle pass
+constexpr int SF_WPT = 8;    // values per thread in the block sums / prefixes
 constexpr int SF_WPB = SF_NT * SF_WPT;
-constexpr int SF_PPT = 16;              // partial sums per thread in the one-block scan
+constexpr int SF_PPT = 16;   // partial sums per thread in the one-block scan
 
 __device__ __forceinline__ bool inside(float v) { return v < 0.f; }
 
@@ -199,46 +203,101 @@ __device__ __forceinline__ bool cell_listed(const uint8_t* mask, int R, int i, i
   return i >= 0 && j >= 0 && k >= 0 && i < R && j < R && k < R && mask[(i * R + j) * R + k] != 0;
 }
 
-// Crossing-edge bits and inside bits: wave m covers points 64 m .. 64 m + 63;
-// lanes 0..2 write the wave's word of each axis plane (words[a * nwa + m]),
-// lane 3 the inside bits (ins[m]). With a cell mask an edge counts only when one
-// of the (up to 4) cells around it is listed.
-__global__ __launch_bounds__(SF_NT) void sf_edges_kernel(const float* __restrict__ vol, int R,
-                                                         const uint8_t* __restrict__ mask,
-                                                         uint64_t* __restrict__ words, uint64_t* __restrict__ ins,
-                                                         int nwa) {
-  const int P = R + 1, PP = P * P, NP = PP * P;
-  const int lane = threadIdx.x & 63;
-  const int waves = gridDim.x * (SF_NT / 64);
-  if (blockIdx.x == 0 && threadIdx.x == 0) ins[nwa] = 0;  // the spare word (read only for points past the grid)
-  for (int m = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6); m < nwa; m += waves) {
-    const int p = 64 * m + lane;
-    // all four loads unconditional (clamped addresses), so they are in flight together
-    const int pc = min(p, NP - 1);
-    const float v = vol[pc], vi = vol[min(pc + PP, NP - 1)], vj = vol[min(pc + P, NP - 1)], vk = vol[pc + (pc + 1 < NP)];
-    const int row = pc / P, k = pc - row * P;
-    const int i = row / P, j = row - i * P;
-    const bool ok = p < NP;
-    const bool in = ok && inside(v);
-    bool f0 = ok && i < R && inside(v) != inside(vi);
-    bool f1 = ok && j < R && inside(v) != inside(vj);
-    bool f2 = ok && k < R && inside(v) != inside(vk);
-    {
-      if (mask) {
-        // cells holding edge (p, a): lower corner p minus 0/1 along the other two axes
-        if (f0) f0 = cell_listed(mask, R, i, j, k) || cell_listed(mask, R, i, j - 1, k) ||
-                     cell_listed(mask, R, i, j, k - 1) || cell_listed(mask, R, i, j - 1, k - 1);
-        if (f1) f1 = cell_listed(mask, R, i, j, k) || cell_listed(mask, R, i - 1, j, k) ||
-                     cell_listed(mask, R, i, j, k - 1) || cell_listed(mask, R, i - 1, j, k - 1);
-        if (f2) f2 = cell_listed(mask, R, i, j, k) || cell_listed(mask, R, i - 1, j, k) ||
-                     cell_listed(mask, R, i, j - 1, k) || cell_listed(mask, R, i - 1, j - 1, k);
-      }
+__device__ __forceinline__ int pieces_per_row(int P) { return (P + SF_PW - 1) / SF_PW; }
+
+__device__ __forceinline__ void load_ntri(unsigned char* ntri) {
+  for (int c = threadIdx.x; c < 256; c += SF_NT) ntri[c] = kTable.c[c].ntri;
+  __syncthreads();
+}
+
+// Case of cell (i, j, k) of lane l < 63 from the inside words of its four corner
+// rows (bits l and l + 1).
+__device__ __forceinline__ int cell_case(uint64_t b00, uint64_t b01, uint64_t b10, uint64_t b11, int l) {
+  return (int)((b00 >> l) & 3ull) | (int)((b01 >> l) & 3ull) << 2 | (int)((b10 >> l) & 3ull) << 4 |
+         (int)((b11 >> l) & 3ull) << 6;
+}
+
+// The volume pass. Block b covers rows j = 4 jg + wave, piece column kc, and
+// pieces i = SF_IC ic .. SF_IC ic + SF_IC - 1 (b = (jg * KC + kc) * NIC + ic). Per
+// piece (i, j, kc): the crossing-edge words of the three axes (planes[a * nwp +
+// piece]), the inside word (ins[piece]) and the triangle count of its cells
+// (tcnt[piece]). With a cell mask an edge counts only when one of the (up to 4)
+// cells around it is listed, and only listed cells have triangles.
+template <bool MASKED>
+__global__ __launch_bounds__(SF_NT) void sf_points_kernel(const float* __restrict__ vol, int R,
+                                                          const uint8_t* __restrict__ mask,
+                                                          uint64_t* __restrict__ planes, uint64_t* __restrict__ ins,
+                                                          int32_t* __restrict__ tcnt) {
+  __shared__ unsigned char ntri[256];
+  load_ntri(ntri);
+  const int P = R + 1, KC = pieces_per_row(P), nwp = P * P * KC, NIC = (P + SF_IC - 1) / SF_IC;
+  const int l = threadIdx.x & 63;
+  const int ic = blockIdx.x % NIC, rest = blockIdx.x / NIC;
+  const int kc = rest % KC, jg = rest / KC;
+  const int j = __builtin_amdgcn_readfirstlane(4 * jg + (threadIdx.x >> 6));
+  if (j >= P) return;  // (no barrier follows)
+  const int i0 = ic * SF_IC;
+  const int k = SF_PW * kc + l;
+  const bool ok = k < P;
+  const int kk = min(k, R), j1 = min(j + 1, R);
+  // rows (i, j) and (i, j+1) for i = i0 .. i0 + SF_IC (clamped to the grid), all loads first
+  float a[SF_IC + 1], b[SF_IC + 1];
+#pragma unroll
+  for (int t = 0; t <= SF_IC; ++t) {
+    const int i = min(i0 + t, R);
+    a[t] = vol[(i * P + j) * P + kk];
+    b[t] = vol[(i * P + j1) * P + kk];
+  }
+  // lane t keeps the words of piece i0 + t and stores them after the walk (one
+  // store instruction per output instead of one per piece)
+  uint64_t ox = 0, oy = 0, oz = 0, oi = 0;
+  int ocnt = 0;
+#pragma unroll
+  for (int t = 0; t < SF_IC; ++t) {
+    const int i = i0 + t;  // (rows past R: clamped loads, nothing stored)
+    const bool in00 = ok && inside(a[t]), in01 = ok && inside(b[t]), in10 = ok && inside(a[t + 1]),
+               in11 = ok && inside(b[t + 1]);
+    const uint64_t b00 = __ballot(in00), b01 = __ballot(in01), b10 = __ballot(in10), b11 = __ballot(in11);
+    const bool own = ok && l < SF_PW;
+    bool fx = own && i < R && in00 != in10;
+    bool fy = own && j < R && in00 != in01;
+    bool fz = own && k < R && in00 != (bool)((b00 >> (l + 1)) & 1ull);
+    if constexpr (MASKED) {
+      // cells holding the edge: lower corner (i, j, k) minus 0/1 along the other two axes
+      if (fx) fx = cell_listed(mask, R, i, j, k) || cell_listed(mask, R, i, j - 1, k) ||
+                   cell_listed(mask, R, i, j, k - 1) || cell_listed(mask, R, i, j - 1, k - 1);
+      if (fy) fy = cell_listed(mask, R, i, j, k) || cell_listed(mask, R, i - 1, j, k) ||
+                   cell_listed(mask, R, i, j, k - 1) || cell_listed(mask, R, i - 1, j, k - 1);
+      if (fz) fz = cell_listed(mask, R, i, j, k) || cell_listed(mask, R, i - 1, j, k) ||
+                   cell_listed(mask, R, i, j - 1, k) || cell_listed(mask, R, i - 1, j - 1, k);
     }
-    const uint64_t b0 = __ballot(f0), b1 = __ballot(f1), b2 = __ballot(f2), bi = __ballot(in);
-    if (lane < 3) words[lane * nwa + m] = lane == 0 ? b0 : (lane == 1 ? b1 : b2);
-    if (lane == 3) ins[m] = bi;
+    const uint64_t bx = __ballot(fx), by = __ballot(fy), bz = __ballot(fz);
+    // cell (i, j, k): corners in rows (i|i+1, j|j+1), points k, k+1; at most 5
+    // triangles, so the piece's sum comes from three ballots of the count's bits
+    int nt = 0;
+    if (own && i < R && j < R && k < R && (!MASKED || mask[(i * R + j) * R + k] != 0))
+      nt = ntri[cell_case(b00, b01, b10, b11, l)];
+    const int sum = __popcll(__ballot(nt & 1)) + 2 * __popcll(__ballot(nt & 2)) + 4 * __popcll(__ballot(nt & 4));
+    if (l == t) {
+      ox = bx;
+      oy = by;
+      oz = bz;
+      oi = b00;
+      ocnt = sum;
+    }
+  }
+  if (l < SF_IC && i0 + l <= R) {
+    const int piece = ((i0 + l) * P + j) * KC + kc;
+    planes[piece] = ox;
+    planes[nwp + piece] = oy;
+    planes[2 * nwp + piece] = oz;
+    ins[piece] = oi;
+    tcnt[piece] = ocnt;
   }
 }
+
+__device__ __forceinline__ int64_t count_of(const uint64_t* x, int i) { return __popcll(x[i]); }
+__device__ __forceinline__ int64_t count_of(const int32_t* x, int i) { return x[i]; }
 
 // Exclusive prefix of v over the block's threads (thread order), plus the total.
 __device__ __forceinline__ int64_t block_exclusive(int64_t v, int64_t* red, int64_t& total) {
@@ -260,14 +319,16 @@ __device__ __forceinline__ int64_t block_exclusive(int64_t v, int64_t* red, int6
   return before + x - v;
 }
 
-__global__ __launch_bounds__(SF_NT) void sf_word_sums_kernel(const uint64_t* __restrict__ words, int n,
-                                                             int64_t* __restrict__ part) {
+// Per-block sums of count_of(x, i), i < n (blocks of SF_WPB entries).
+template <typename X>
+__global__ __launch_bounds__(SF_NT) void sf_block_sums_kernel(const X* __restrict__ x, int n,
+                                                              int64_t* __restrict__ part) {
   __shared__ int64_t red[SF_NT / 64];
   const int base = blockIdx.x * SF_WPB + threadIdx.x * SF_WPT;
   int64_t c = 0;
 #pragma unroll
   for (int q = 0; q < SF_WPT; ++q)
-    if (base + q < n) c += __popcll(words[base + q]);
+    if (base + q < n) c += count_of(x, base + q);
   int64_t total;
   block_exclusive(c, red, total);
   if (threadIdx.x == 0) part[blockIdx.x] = total;
@@ -300,17 +361,17 @@ __global__ __launch_bounds__(SF_NT) void sf_scan_parts_kernel(int64_t* __restric
   if (threadIdx.x == 0) *total = carry;
 }
 
-// Per-word prefix (vertex id of the word's first set bit).
-__global__ __launch_bounds__(SF_NT) void sf_word_prefix_kernel(const uint64_t* __restrict__ words, int n,
-                                                               const int64_t* __restrict__ part,
-                                                               int32_t* __restrict__ prefix) {
+// Exclusive prefix of count_of(x, i) (part: the scanned block sums).
+template <typename X, typename Y>
+__global__ __launch_bounds__(SF_NT) void sf_prefix_kernel(const X* __restrict__ x, int n,
+                                                          const int64_t* __restrict__ part, Y* __restrict__ prefix) {
   __shared__ int64_t red[SF_NT / 64];
   const int base = blockIdx.x * SF_WPB + threadIdx.x * SF_WPT;
-  int c[SF_WPT];
+  int64_t c[SF_WPT];
   int64_t s = 0;
 #pragma unroll
   for (int q = 0; q < SF_WPT; ++q) {
-    c[q] = base + q < n ? __popcll(words[base + q]) : 0;
+    c[q] = base + q < n ? count_of(x, base + q) : 0;
     s += c[q];
   }
   int64_t total;
@@ -318,160 +379,124 @@ __global__ __launch_bounds__(SF_NT) void sf_word_prefix_kernel(const uint64_t* _
 #pragma unroll
   for (int q = 0; q < SF_WPT; ++q)
     if (base + q < n) {
-      prefix[base + q] = (int32_t)off;
+      prefix[base + q] = (Y)off;
       off += c[q];
     }
 }
 
-// One row piece (see SF_IPW): its cells' cases, triangle counts and lower corners.
-// The inside bits of the four corner rows come from two scalar word loads each
-// (the piece's 65 points of a row span at most two words); ins has one spare
-// word after the last one.
-struct Piece {
-  int cs, nt, p0;
-};
-__device__ __forceinline__ Piece piece_cell(const uint64_t* __restrict__ ins, int R, const uint8_t* __restrict__ mask,
-                                            const unsigned char* ntri, int piece, int lane) {
-  const int P = R + 1, KC = (R + 63) >> 6;
-  Piece out{0, 0, 0};
-  const int r = piece / KC, kc = piece - r * KC;  // wave-uniform
-  if (r >= R * R) return out;
-  const int i = r / R, j = r - i * R;
-  const int k = 64 * kc + lane;
-  int cs = 0;
-#pragma unroll
-  for (int di = 0; di < 2; ++di)
-#pragma unroll
-    for (int dj = 0; dj < 2; ++dj) {
-      const int start = ((i + di) * P + (j + dj)) * P + 64 * kc;
-      const int w = start >> 6, sh = start & 63;
-      const uint64_t w0 = ins[w], w1 = ins[w + 1];
-      const uint64_t lo = sh ? (w0 >> sh) | (w1 << (64 - sh)) : w0;
-      const int b0 = (int)((lo >> lane) & 1ull);
-      const int b1 = lane < 63 ? (int)((lo >> (lane + 1)) & 1ull) : (int)((w1 >> sh) & 1ull);
-      cs |= b0 << (4 * di + 2 * dj) | b1 << (4 * di + 2 * dj + 1);
-    }
-  const int c = (i * R + j) * R + k;
-  const bool ok = k < R && (!mask || mask[min(c, R * R * R - 1)] != 0);
-  out.cs = cs;
-  out.nt = ok ? ntri[cs] : 0;
-  out.p0 = (i * P + j) * P + k;
-  return out;
+// Vertex id of the edge along axis a from point (row, k): rank of its bit.
+__device__ __forceinline__ int32_t vertex_of(const uint64_t* __restrict__ planes, const int32_t* __restrict__ vpre,
+                                            int nwp, int KC, int a, int row, int k) {
+  const int kc = k / SF_PW, l = k - kc * SF_PW;
+  const int w = a * nwp + row * KC + kc;
+  return vpre[w] + __popcll(planes[w] & ((1ull << l) - 1ull));
 }
 
-__device__ __forceinline__ void load_ntri(unsigned char* ntri) {
-  for (int c = threadIdx.x; c < 256; c += SF_NT) ntri[c] = kTable.c[c].ntri;
-  __syncthreads();
-}
-
-__device__ __forceinline__ int piece_of(int q) {
-  return __builtin_amdgcn_readfirstlane(blockIdx.x * SF_PPB + (threadIdx.x >> 6) * SF_IPW + q);
-}
-
-__global__ __launch_bounds__(SF_NT) void sf_cell_sums_kernel(const uint64_t* __restrict__ ins, int R,
-                                                             const uint8_t* __restrict__ mask,
-                                                             int64_t* __restrict__ part) {
-  __shared__ int64_t red[SF_NT / 64];
-  __shared__ unsigned char ntri[256];
-  load_ntri(ntri);
-  const int lane = threadIdx.x & 63;
-  int64_t s = 0;
-#pragma unroll
-  for (int q = 0; q < SF_IPW; ++q) s += piece_cell(ins, R, mask, ntri, piece_of(q), lane).nt;
-  int64_t total;
-  block_exclusive(s, red, total);
-  if (threadIdx.x == 0) part[blockIdx.x] = total;
-}
-
-// Vertex id of global edge (axis a, point p): rank of its bit.
-__device__ __forceinline__ int32_t vertex_of(const uint64_t* __restrict__ words, const int32_t* __restrict__ prefix,
-                                            int nwa, int a, int p) {
-  const int w = a * nwa + (p >> 6);
-  const uint64_t below = words[w] & ((1ull << (p & 63)) - 1ull);
-  return prefix[w] + __popcll(below);
-}
-
-__global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(const uint64_t* __restrict__ ins, int R,
-                                                             const uint8_t* __restrict__ mask,
-                                                             const uint64_t* __restrict__ words,
-                                                             const int32_t* __restrict__ prefix, int nwa,
-                                                             const int64_t* __restrict__ part,
+// Triangles: one wave per piece with triangles. A lane with triangles fetches the
+// vertex ids of all 12 edges of its cell (independent loads, in flight together),
+// keeps them in LDS and writes its triangles from the case table.
+template <bool MASKED>
+__global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(int R, const uint8_t* __restrict__ mask,
+                                                             const uint64_t* __restrict__ planes,
+                                                             const uint64_t* __restrict__ ins,
+                                                             const int32_t* __restrict__ vpre,
+                                                             const int32_t* __restrict__ tcnt,
+                                                             const int64_t* __restrict__ tpre,
                                                              int32_t* __restrict__ tris, int64_t max_tris) {
-  __shared__ int64_t red[SF_NT / 64];
   __shared__ unsigned char ntri[256];
+  __shared__ int32_t vid_lds[12][SF_NT];
   load_ntri(ntri);
-  const int P = R + 1, PP = P * P;
-  const int lane = threadIdx.x & 63;
-  Piece pc[SF_IPW];
-  int64_t s = 0;
+  const int P = R + 1, KC = pieces_per_row(P), nwp = P * P * KC;
+  const int l = threadIdx.x & 63;
+  const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6) * SF_TPW;
+  int32_t cnt[SF_TPW];
 #pragma unroll
-  for (int q = 0; q < SF_IPW; ++q) {
-    pc[q] = piece_cell(ins, R, mask, ntri, piece_of(q), lane);
-    s += pc[q].nt;
-  }
-  // this wave's first triangle: block offset + the triangles of the waves before it
-  int64_t total;
-  const int64_t before = block_exclusive(s, red, total);
-  int64_t t = part[blockIdx.x] + __shfl(before, 0);
-#pragma unroll
-  for (int q = 0; q < SF_IPW; ++q) {
-    int x = pc[q].nt;  // inclusive scan over the piece's cells (lane order = cell order)
+  for (int q = 0; q < SF_TPW; ++q) cnt[q] = tcnt[min(p0 + q, nwp - 1)];  // wave-uniform
+  for (int q = 0; q < SF_TPW; ++q) {
+    const int piece = p0 + q;
+    if (piece >= nwp || cnt[q] == 0) continue;  // (wave-uniform)
+    const int row = piece / KC, kc = piece - row * KC;
+    const int i = row / P, j = row - i * P;
+    const int k = SF_PW * kc + l;
+    const uint64_t b00 = ins[piece], b01 = ins[piece + KC], b10 = ins[piece + P * KC], b11 = ins[piece + P * KC + KC];
+    const int cs = cell_case(b00, b01, b10, b11, l);
+    const int nt = l < SF_PW && k < R && (!MASKED || mask[(i * R + j) * R + k] != 0) ? ntri[cs] : 0;
+    int x = nt;  // inclusive scan over the piece's cells (lane order = cell order)
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
+      if (l >= o) x += y;
     }
-    int64_t u = t + x - pc[q].nt;
-    t += __shfl(x, 63);
-    if (pc[q].nt == 0) continue;
-    const McCase& mc = kTable.c[pc[q].cs];
-    for (int m = 0; m < pc[q].nt; ++m, ++u) {
+    if (nt == 0) continue;
+    int64_t u = tpre[piece] + x - nt;
+    // vertex ids of the cell's 12 edges (edges that do not cross give unused values)
+#pragma unroll
+    for (int e = 0; e < 12; ++e) {
+      // edge e: axis a = e / 4, offsets o1, o2 along the other two axes (in axis order)
+      const int a = e >> 2, o1 = (e >> 1) & 1, o2 = e & 1;
+      const int di = a == 0 ? 0 : o1, dj = a == 0 ? o1 : (a == 1 ? 0 : o2), dk = a == 2 ? 0 : o2;
+      vid_lds[e][threadIdx.x] = vertex_of(planes, vpre, nwp, KC, a, row + di * P + dj, k + dk);
+    }
+    const McCase& mc = kTable.c[cs];
+    for (int m = 0; m < nt; ++m, ++u) {
       if (u >= max_tris) continue;
-      int32_t v[3];
 #pragma unroll
       for (int x3 = 0; x3 < 3; ++x3) {
-        const int code = mc.e[m][x3];
-        v[x3] = vertex_of(words, prefix, nwa, code >> 3,
-                          pc[q].p0 + ((code >> 2) & 1) * PP + ((code >> 1) & 1) * P + (code & 1));
+        const int code = mc.e[m][x3];  // axis << 3 | di << 2 | dj << 1 | dk
+        const int a = code >> 3;
+        const int o1 = a == 0 ? (code >> 1) & 1 : (code >> 2) & 1;
+        const int o2 = a == 2 ? (code >> 1) & 1 : code & 1;
+        tris[3 * u + x3] = vid_lds[4 * a + 2 * o1 + o2][threadIdx.x];
       }
-      tris[3 * u + 0] = v[0];
-      tris[3 * u + 1] = v[1];
-      tris[3 * u + 2] = v[2];
     }
   }
 }
 
-// Vertex positions (and optionally edge ids), one thread per point.
+// Vertex positions (and optionally edge ids): one wave per piece, all three axes.
 __global__ __launch_bounds__(SF_NT) void sf_vertices_kernel(const float* __restrict__ vol, int R,
-                                                            const uint64_t* __restrict__ words,
-                                                            const int32_t* __restrict__ prefix, int nwa,
+                                                            const uint64_t* __restrict__ planes,
+                                                            const int32_t* __restrict__ vpre,
                                                             float* __restrict__ verts, int64_t max_verts,
                                                             int64_t* __restrict__ vert_edges) {
-  const int P = R + 1, PP = P * P, NP = PP * P;
+  const int P = R + 1, PP = P * P, NP = PP * P, KC = pieces_per_row(P), nwp = PP * KC;
   const float h = 2.0f / (float)R;
-  const int lane = threadIdx.x & 63;
+  const int l = threadIdx.x & 63;
   const int waves = gridDim.x * (SF_NT / 64);
-  for (int m = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6); m < nwa; m += waves) {
-    const uint64_t w0 = words[m], w1 = words[nwa + m], w2 = words[2 * nwa + m];  // wave-uniform
-    if ((w0 | w1 | w2) == 0) continue;
-    const int p = 64 * m + lane;
-    if (!((w0 | w1 | w2) >> lane & 1ull) || p >= NP) continue;
-    const uint64_t low = (1ull << (p & 63)) - 1ull;
-    const int row = p / P, k = p - row * P;
-    const int i = row / P, j = row - i * P;
-    const float v0 = vol[p];
-    const float bx = fmaf((float)i, h, -1.f), by = fmaf((float)j, h, -1.f), bz = fmaf((float)k, h, -1.f);
+  constexpr int U = 4;  // pieces per iteration, their words fetched together
+  for (int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6) * U; p0 < nwp;
+       p0 += waves * U) {
+    uint64_t wa[U][3];
 #pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      const uint64_t w = a == 0 ? w0 : (a == 1 ? w1 : w2);
-      if (!((w >> (p & 63)) & 1ull)) continue;
-      const int64_t vid = prefix[a * nwa + m] + __popcll(w & low);
-      if (vid >= max_verts) continue;
-      const float v1 = vol[p + (a == 0 ? PP : (a == 1 ? P : 1))];
-      const float t = v0 / (v0 - v1);
-      verts[3 * vid + 0] = a == 0 ? fmaf(t, h, bx) : bx;
-      verts[3 * vid + 1] = a == 1 ? fmaf(t, h, by) : by;
-      verts[3 * vid + 2] = a == 2 ? fmaf(t, h, bz) : bz;
-      if (vert_edges) vert_edges[vid] = (int64_t)a * NP + p;
+    for (int u = 0; u < U; ++u) {
+      const int pc = min(p0 + u, nwp - 1);
+#pragma unroll
+      for (int a = 0; a < 3; ++a) wa[u][a] = p0 + u < nwp ? planes[a * nwp + pc] : 0ull;  // wave-uniform
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int piece = p0 + u;
+      const uint64_t w0 = wa[u][0], w1 = wa[u][1], w2 = wa[u][2];
+      if ((w0 | w1 | w2) == 0) continue;
+      if (!((w0 | w1 | w2) >> l & 1ull)) continue;
+      const int row = piece / KC, kc = piece - row * KC;
+      const int i = row / P, j = row - i * P;
+      const int k = SF_PW * kc + l;
+      const int p = row * P + k;
+      const uint64_t low = (1ull << l) - 1ull;
+      const float v0 = vol[p];
+      const float bx = fmaf((float)i, h, -1.f), by = fmaf((float)j, h, -1.f), bz = fmaf((float)k, h, -1.f);
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        const uint64_t w = a == 0 ? w0 : (a == 1 ? w1 : w2);
+        if (!((w >> l) & 1ull)) continue;
+        const int64_t vid = vpre[a * nwp + piece] + __popcll(w & low);
+        if (vid >= max_verts) continue;
+        const float v1 = vol[p + (a == 0 ? PP : (a == 1 ? P : 1))];
+        const float t = v0 / (v0 - v1);
+        verts[3 * vid + 0] = a == 0 ? fmaf(t, h, bx) : bx;
+        verts[3 * vid + 1] = a == 1 ? fmaf(t, h, by) : by;
+        verts[3 * vid + 2] = a == 2 ? fmaf(t, h, bz) : bz;
+        if (vert_edges) vert_edges[vid] = (int64_t)a * NP + p;
+      }
     }
   }
 }
@@ -485,14 +510,12 @@ int grid_blocks(int64_t work, int64_t per_block, int64_t cap) {
 }  // namespace
 
 SurfaceWs surface_ws_layout(int R) {
-  const int64_t P = R + 1, NP = P * P * P, NC = (int64_t)R * R * R;
+  const int64_t P = R + 1, KC = (P + SF_PW - 1) / SF_PW;
   SurfaceWs w{};
-  w.nwa = (NP + 63) / 64;
+  w.nwa = P * P * KC;  // words per plane (one per piece)
   w.nwords = 3 * w.nwa;
   w.nwb = (w.nwords + SF_WPB - 1) / SF_WPB;
-  const int64_t pieces = (int64_t)R * R * ((R + 63) / 64);
-  w.ncb = (pieces + SF_PPB - 1) / SF_PPB;
-  (void)NC;
+  w.ncb = (w.nwa + SF_WPB - 1) / SF_WPB;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -500,8 +523,10 @@ SurfaceWs surface_ws_layout(int R) {
     return o;
   };
   w.off_words = take(8 * w.nwords);
-  w.off_ins = take(8 * (w.nwa + 1));
+  w.off_ins = take(8 * w.nwa);
   w.off_prefix = take(4 * w.nwords);
+  w.off_tcnt = take(4 * w.nwa);
+  w.off_tpre = take(8 * w.nwa);
   w.off_wpart = take(8 * w.nwb);
   w.off_cpart = take(8 * w.ncb);
   w.bytes = off;
@@ -512,24 +537,36 @@ hipError_t launch_surface(const float* vol, int R, const uint8_t* mask, float* v
                           int32_t* tris, int64_t max_tris, int64_t* vert_edges, int64_t* counts, char* ws,
                           hipStream_t s) {
   const SurfaceWs w = surface_ws_layout(R);
-  uint64_t* words = reinterpret_cast<uint64_t*>(ws + w.off_words);
+  uint64_t* planes = reinterpret_cast<uint64_t*>(ws + w.off_words);
   uint64_t* ins = reinterpret_cast<uint64_t*>(ws + w.off_ins);
-  int32_t* prefix = reinterpret_cast<int32_t*>(ws + w.off_prefix);
+  int32_t* vpre = reinterpret_cast<int32_t*>(ws + w.off_prefix);
+  int32_t* tcnt = reinterpret_cast<int32_t*>(ws + w.off_tcnt);
+  int64_t* tpre = reinterpret_cast<int64_t*>(ws + w.off_tpre);
   int64_t* wpart = reinterpret_cast<int64_t*>(ws + w.off_wpart);
   int64_t* cpart = reinterpret_cast<int64_t*>(ws + w.off_cpart);
   const int64_t cus = dev_info().cus;
-  const int nwa = (int)w.nwa, nwords = (int)w.nwords, nwb = (int)w.nwb, ncb = (int)w.ncb;
-  hipLaunchKernelGGL(sf_edges_kernel, dim3(grid_blocks(w.nwa, SF_NT / 64, 64 * cus)), dim3(SF_NT), 0, s, vol, R,
-                     mask, words, ins, nwa);
-  hipLaunchKernelGGL(sf_word_sums_kernel, dim3(nwb), dim3(SF_NT), 0, s, words, nwords, wpart);
+  const int P = R + 1, KC = (P + SF_PW - 1) / SF_PW, NIC = (P + SF_IC - 1) / SF_IC;
+  const int nwp = (int)w.nwa, nwords = (int)w.nwords, nwb = (int)w.nwb, ncb = (int)w.ncb;
+  const int gp = ((P + 3) / 4) * KC * NIC;
+  if (mask)
+    hipLaunchKernelGGL(sf_points_kernel<true>, dim3(gp), dim3(SF_NT), 0, s, vol, R, mask, planes, ins, tcnt);
+  else
+    hipLaunchKernelGGL(sf_points_kernel<false>, dim3(gp), dim3(SF_NT), 0, s, vol, R, mask, planes, ins, tcnt);
+  hipLaunchKernelGGL(sf_block_sums_kernel<uint64_t>, dim3(nwb), dim3(SF_NT), 0, s, planes, nwords, wpart);
   hipLaunchKernelGGL(sf_scan_parts_kernel, dim3(1), dim3(SF_NT), 0, s, wpart, nwb, counts);
-  hipLaunchKernelGGL(sf_word_prefix_kernel, dim3(nwb), dim3(SF_NT), 0, s, words, nwords, wpart, prefix);
-  hipLaunchKernelGGL(sf_cell_sums_kernel, dim3(ncb), dim3(SF_NT), 0, s, ins, R, mask, cpart);
+  hipLaunchKernelGGL((sf_prefix_kernel<uint64_t, int32_t>), dim3(nwb), dim3(SF_NT), 0, s, planes, nwords, wpart, vpre);
+  hipLaunchKernelGGL(sf_block_sums_kernel<int32_t>, dim3(ncb), dim3(SF_NT), 0, s, tcnt, nwp, cpart);
   hipLaunchKernelGGL(sf_scan_parts_kernel, dim3(1), dim3(SF_NT), 0, s, cpart, ncb, counts + 1);
-  hipLaunchKernelGGL(sf_triangles_kernel, dim3(ncb), dim3(SF_NT), 0, s, ins, R, mask, words, prefix, nwa, cpart, tris,
-                     max_tris);
-  hipLaunchKernelGGL(sf_vertices_kernel, dim3(grid_blocks(64 * w.nwa, SF_NT, 64 * cus)), dim3(SF_NT), 0, s, vol, R,
-                     words, prefix, nwa, verts, max_verts, vert_edges);
+  hipLaunchKernelGGL((sf_prefix_kernel<int32_t, int64_t>), dim3(ncb), dim3(SF_NT), 0, s, tcnt, nwp, cpart, tpre);
+  const int gt = grid_blocks(nwp, SF_TPW * (SF_NT / 64), INT32_MAX);
+  if (mask)
+    hipLaunchKernelGGL(sf_triangles_kernel<true>, dim3(gt), dim3(SF_NT), 0, s, R, mask, planes, ins, vpre, tcnt, tpre,
+                       tris, max_tris);
+  else
+    hipLaunchKernelGGL(sf_triangles_kernel<false>, dim3(gt), dim3(SF_NT), 0, s, R, mask, planes, ins, vpre, tcnt, tpre,
+                       tris, max_tris);
+  hipLaunchKernelGGL(sf_vertices_kernel, dim3(grid_blocks(nwp, 4 * SF_NT / 64, 64 * cus)), dim3(SF_NT), 0, s, vol, R,
+                     planes, vpre, verts, max_verts, vert_edges);
   return hipGetLastError();
 }
 

@@ -118,13 +118,14 @@ hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s);
 size_t select_scratch_bytes(int M);
 
 // Surface extraction (marching cubes at SDF = 0) workspace: crossing-edge bit
-// planes, inside bits, per-word vertex prefixes, per-block partial sums.
+// planes, inside bits, per-word vertex prefixes, per-piece triangle counts and
+// their prefixes, per-block partial sums.
 struct SurfaceWs {
-  int64_t nwa;     // 64-bit words per axis plane
+  int64_t nwa;     // 64-bit words per plane (one per piece of 63 points of a row)
   int64_t nwords;  // 3 * nwa
   int64_t nwb;     // blocks of the word scan
-  int64_t ncb;     // blocks of the cell scan
-  size_t off_words, off_ins, off_prefix, off_wpart, off_cpart, bytes;
+  int64_t ncb;     // blocks of the triangle-count scan
+  size_t off_words, off_ins, off_prefix, off_tcnt, off_tpre, off_wpart, off_cpart, bytes;
 };
 SurfaceWs surface_ws_layout(int R);
 // counts[0] = vertices, counts[1] = triangles (device); entries past the maxima are not written

@@ -157,9 +157,10 @@ def test_surface_extraction_argument_checks():
     assert lib.vdm_surface_workspace_size(0) == 0 and "R=0" in V.vdm_last_error()
     assert lib.vdm_surface_workspace_size(894) == 0
     n300 = lib.vdm_surface_workspace_size(300)
-    # two bit planes' worth per axis (bits + int32 prefixes) plus partial sums
-    words = 3 * ((301 ** 3 + 63) // 64)
-    assert 12 * words <= n300 <= 12 * words + 8 * (words // 2048 + 300 ** 3 // 2048 + 8) + 4 * 256
+    # per axis one bit per point (8-byte words of 63 points) and an int32 prefix per
+    # word, one more bit plane for the inside test, and small partial sums
+    words = 301 * 301 * ((301 + 62) // 63)
+    assert 3 * 12 * words + 8 * words <= n300 <= 2 * (3 * 12 * words + 8 * words)
     ok = dict(vol=fake, R=300, mask=None, verts=fake, mv=10, tris=fake, mt=10, edges=None, counts=fake,
               ws=fake, wsb=n300)
 
