@@ -827,7 +827,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   using T = typename C::T;
   using MM = Mma<T>;
   using Frag = typename MM::frag;
-  constexpr int KS = C::KSTEPS, PS = C::PSTEPS;
+  constexpr int KS = C::KSTEPS;
 
   const int tid0 = threadIdx.x, lane0 = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // wave-uniform: scalar registers

@@ -192,7 +192,7 @@ __constant__ McTable kTable = build_table();
 constexpr int SF_NT = 256;   // threads per block (4 waves)
 constexpr int SF_PW = 63;    // points per piece
 constexpr int SF_IC = 16;    // pieces along i per wave in the volume pass
-constexpr int SF_TPW = 8;    // pieces per wave in the triangle pass
+constexpr int SF_TPW = 16;   // pieces per wave in the triangle and vertex passes
 constexpr int SF_WPT = 8;    // values per thread in the block sums / prefixes
 constexpr int SF_WPB = SF_NT * SF_WPT;
 constexpr int SF_PPT = 16;   // partial sums per thread in the one-block scan
@@ -201,6 +201,13 @@ __device__ __forceinline__ bool inside(float v) { return v < 0.f; }
 
 __device__ __forceinline__ bool cell_listed(const uint8_t* mask, int R, int i, int j, int k) {
   return i >= 0 && j >= 0 && k >= 0 && i < R && j < R && k < R && mask[(i * R + j) * R + k] != 0;
+}
+
+// (the readlane builtin moves 32 bits)
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+  return (uint64_t)hi << 32 | lo;
 }
 
 __device__ __forceinline__ int pieces_per_row(int P) { return (P + SF_PW - 1) / SF_PW; }
@@ -392,9 +399,10 @@ __device__ __forceinline__ int32_t vertex_of(const uint64_t* __restrict__ planes
   return vpre[w] + __popcll(planes[w] & ((1ull << l) - 1ull));
 }
 
-// Triangles: one wave per piece with triangles. A lane with triangles fetches the
-// vertex ids of all 12 edges of its cell (independent loads, in flight together),
-// keeps them in LDS and writes its triangles from the case table.
+// Triangles: a wave per SF_TPW pieces, skipping those without triangles. A lane
+// with triangles fetches the vertex ids of all 12 edges of its cell (independent
+// loads, in flight together), keeps them in LDS and writes its triangles from the
+// case table.
 template <bool MASKED>
 __global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(int R, const uint8_t* __restrict__ mask,
                                                              const uint64_t* __restrict__ planes,
@@ -403,24 +411,24 @@ __global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(int R, const uint8_
                                                              const int32_t* __restrict__ tcnt,
                                                              const int64_t* __restrict__ tpre,
                                                              int32_t* __restrict__ tris, int64_t max_tris) {
-  __shared__ unsigned char ntri[256];
+  __shared__ McCase tab[256];
   __shared__ int32_t vid_lds[12][SF_NT];
-  load_ntri(ntri);
+  for (int c = threadIdx.x; c < 256; c += SF_NT) tab[c] = kTable.c[c];
+  __syncthreads();
   const int P = R + 1, KC = pieces_per_row(P), nwp = P * P * KC;
   const int l = threadIdx.x & 63;
   const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6) * SF_TPW;
-  int32_t cnt[SF_TPW];
-#pragma unroll
-  for (int q = 0; q < SF_TPW; ++q) cnt[q] = tcnt[min(p0 + q, nwp - 1)];  // wave-uniform
+  // the triangle counts of the wave's pieces, one per lane, in one load
+  const int cnt_l = l < SF_TPW && p0 + l < nwp ? tcnt[p0 + l] : 0;
   for (int q = 0; q < SF_TPW; ++q) {
     const int piece = p0 + q;
-    if (piece >= nwp || cnt[q] == 0) continue;  // (wave-uniform)
+    if (__builtin_amdgcn_readlane(cnt_l, q) == 0) continue;  // (wave-uniform; 0 past the end)
     const int row = piece / KC, kc = piece - row * KC;
     const int i = row / P, j = row - i * P;
     const int k = SF_PW * kc + l;
     const uint64_t b00 = ins[piece], b01 = ins[piece + KC], b10 = ins[piece + P * KC], b11 = ins[piece + P * KC + KC];
     const int cs = cell_case(b00, b01, b10, b11, l);
-    const int nt = l < SF_PW && k < R && (!MASKED || mask[(i * R + j) * R + k] != 0) ? ntri[cs] : 0;
+    const int nt = l < SF_PW && k < R && (!MASKED || mask[(i * R + j) * R + k] != 0) ? tab[cs].ntri : 0;
     int x = nt;  // inclusive scan over the piece's cells (lane order = cell order)
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o);
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(int R, const uint8_
       const int di = a == 0 ? 0 : o1, dj = a == 0 ? o1 : (a == 1 ? 0 : o2), dk = a == 2 ? 0 : o2;
       vid_lds[e][threadIdx.x] = vertex_of(planes, vpre, nwp, KC, a, row + di * P + dj, k + dk);
     }
-    const McCase& mc = kTable.c[cs];
+    const McCase& mc = tab[cs];
     for (int m = 0; m < nt; ++m, ++u) {
       if (u >= max_tris) continue;
 #pragma unroll
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(SF_NT) void sf_triangles_kernel(int R, const uint8_
   }
 }
 
-// Vertex positions (and optionally edge ids): one wave per piece, all three axes.
+// Vertex positions (and optionally edge ids): a wave per SF_TPW pieces, all three axes.
 __global__ __launch_bounds__(SF_NT) void sf_vertices_kernel(const float* __restrict__ vol, int R,
                                                             const uint64_t* __restrict__ planes,
                                                             const int32_t* __restrict__ vpre,
@@ -460,43 +468,35 @@ __global__ __launch_bounds__(SF_NT) void sf_vertices_kernel(const float* __restr
   const int P = R + 1, PP = P * P, NP = PP * P, KC = pieces_per_row(P), nwp = PP * KC;
   const float h = 2.0f / (float)R;
   const int l = threadIdx.x & 63;
-  const int waves = gridDim.x * (SF_NT / 64);
-  constexpr int U = 4;  // pieces per iteration, their words fetched together
-  for (int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6) * U; p0 < nwp;
-       p0 += waves * U) {
-    uint64_t wa[U][3];
+  const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * SF_NT + threadIdx.x) >> 6) * SF_TPW;
+  // the three words of each of the wave's pieces, lane 3 u + a = axis a of piece p0 + u, in one load
+  const int pl = p0 + l / 3;
+  const uint64_t word_l = l < 3 * SF_TPW && pl < nwp ? planes[(l % 3) * nwp + pl] : 0ull;
+  for (int u = 0; u < SF_TPW; ++u) {
+    const int piece = p0 + u;
+    const uint64_t w0 = readlane64(word_l, 3 * u), w1 = readlane64(word_l, 3 * u + 1),
+                   w2 = readlane64(word_l, 3 * u + 2);  // wave-uniform (0 past the end)
+    if ((w0 | w1 | w2) == 0) continue;
+    if (!((w0 | w1 | w2) >> l & 1ull)) continue;
+    const int row = piece / KC, kc = piece - row * KC;
+    const int i = row / P, j = row - i * P;
+    const int k = SF_PW * kc + l;
+    const int p = row * P + k;
+    const uint64_t low = (1ull << l) - 1ull;
+    const float v0 = vol[p];
+    const float bx = fmaf((float)i, h, -1.f), by = fmaf((float)j, h, -1.f), bz = fmaf((float)k, h, -1.f);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int pc = min(p0 + u, nwp - 1);
-#pragma unroll
-      for (int a = 0; a < 3; ++a) wa[u][a] = p0 + u < nwp ? planes[a * nwp + pc] : 0ull;  // wave-uniform
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int piece = p0 + u;
-      const uint64_t w0 = wa[u][0], w1 = wa[u][1], w2 = wa[u][2];
-      if ((w0 | w1 | w2) == 0) continue;
-      if (!((w0 | w1 | w2) >> l & 1ull)) continue;
-      const int row = piece / KC, kc = piece - row * KC;
-      const int i = row / P, j = row - i * P;
-      const int k = SF_PW * kc + l;
-      const int p = row * P + k;
-      const uint64_t low = (1ull << l) - 1ull;
-      const float v0 = vol[p];
-      const float bx = fmaf((float)i, h, -1.f), by = fmaf((float)j, h, -1.f), bz = fmaf((float)k, h, -1.f);
-#pragma unroll
-      for (int a = 0; a < 3; ++a) {
-        const uint64_t w = a == 0 ? w0 : (a == 1 ? w1 : w2);
-        if (!((w >> l) & 1ull)) continue;
-        const int64_t vid = vpre[a * nwp + piece] + __popcll(w & low);
-        if (vid >= max_verts) continue;
-        const float v1 = vol[p + (a == 0 ? PP : (a == 1 ? P : 1))];
-        const float t = v0 / (v0 - v1);
-        verts[3 * vid + 0] = a == 0 ? fmaf(t, h, bx) : bx;
-        verts[3 * vid + 1] = a == 1 ? fmaf(t, h, by) : by;
-        verts[3 * vid + 2] = a == 2 ? fmaf(t, h, bz) : bz;
-        if (vert_edges) vert_edges[vid] = (int64_t)a * NP + p;
-      }
+    for (int a = 0; a < 3; ++a) {
+      const uint64_t w = a == 0 ? w0 : (a == 1 ? w1 : w2);
+      if (!((w >> l) & 1ull)) continue;
+      const int64_t vid = vpre[a * nwp + piece] + __popcll(w & low);
+      if (vid >= max_verts) continue;
+      const float v1 = vol[p + (a == 0 ? PP : (a == 1 ? P : 1))];
+      const float t = v0 / (v0 - v1);
+      verts[3 * vid + 0] = a == 0 ? fmaf(t, h, bx) : bx;
+      verts[3 * vid + 1] = a == 1 ? fmaf(t, h, by) : by;
+      verts[3 * vid + 2] = a == 2 ? fmaf(t, h, bz) : bz;
+      if (vert_edges) vert_edges[vid] = (int64_t)a * NP + p;
     }
   }
 }
@@ -544,7 +544,6 @@ hipError_t launch_surface(const float* vol, int R, const uint8_t* mask, float* v
   int64_t* tpre = reinterpret_cast<int64_t*>(ws + w.off_tpre);
   int64_t* wpart = reinterpret_cast<int64_t*>(ws + w.off_wpart);
   int64_t* cpart = reinterpret_cast<int64_t*>(ws + w.off_cpart);
-  const int64_t cus = dev_info().cus;
   const int P = R + 1, KC = (P + SF_PW - 1) / SF_PW, NIC = (P + SF_IC - 1) / SF_IC;
   const int nwp = (int)w.nwa, nwords = (int)w.nwords, nwb = (int)w.nwb, ncb = (int)w.ncb;
   const int gp = ((P + 3) / 4) * KC * NIC;
@@ -565,7 +564,8 @@ hipError_t launch_surface(const float* vol, int R, const uint8_t* mask, float* v
   else
     hipLaunchKernelGGL(sf_triangles_kernel<false>, dim3(gt), dim3(SF_NT), 0, s, R, mask, planes, ins, vpre, tcnt, tpre,
                        tris, max_tris);
-  hipLaunchKernelGGL(sf_vertices_kernel, dim3(grid_blocks(nwp, 4 * SF_NT / 64, 64 * cus)), dim3(SF_NT), 0, s, vol, R,
+  hipLaunchKernelGGL(sf_vertices_kernel, dim3(grid_blocks(nwp, SF_TPW * (SF_NT / 64), INT32_MAX)), dim3(SF_NT), 0, s,
+                     vol, R,
                      planes, vpre, verts, max_verts, vert_edges);
   return hipGetLastError();
 }

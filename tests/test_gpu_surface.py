@@ -88,6 +88,16 @@ def test_sphere(R):
     assert len(To) > 1000
 
 
+@pytest.mark.parametrize("R", [70, 126])
+def test_rows_longer_than_a_word(R):
+    # points k >= 32 and k >= 63 of a row (R = 126: rows of exactly two pieces of 63
+    # points and one of 1); an off-centre sphere reaching close to the boundary
+    X, Y, Z = grid(R)
+    v = (np.sqrt((X - 0.05) ** 2 + (Y + 0.03) ** 2 + (Z - 0.04) ** 2) - 0.93).astype(np.float32)
+    Vo, To = check_equal(v, R)
+    assert np.abs(S.extract(v, R)[2] % (R + 1) - 63).min() == 0  # a vertex at k = 63
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_random_fields(seed):
     rng = np.random.default_rng(seed)
