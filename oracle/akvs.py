@@ -9,8 +9,14 @@ article (part 5) describes the same probe-then-reuse scheme.
 Readings (the pages leave these open):
   * sub-volumes are blocks of 8x8x8 grid points of the current level (block
     b spans indices 8b .. min(8b+7, R) on each axis), at every level;
-  * the probes are the block's 8 corner points (the pages sample random
-    queries; corners make the selection deterministic);
+  * the probes are the block's 8 corner points (corners make the selection
+    independent of any random stream), or, as the pages describe, 8 random
+    points of the block: probe n of block b takes, along axis a, the grid
+    index lo_a + (u mod e_a), where lo_a is the block's first index, e_a its
+    number of points along a, and u the c-th output (c = (8 b + n) * 3 + a,
+    counted from 0) of the SplitMix64 stream seeded with the call's seed
+    (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+    2014; the mixing constants of Vigna's reference splitmix64.c);
   * a token's score for a probe is the head-mean of its softmax probability;
   * each probe keeps its top-k tokens (ties go to the lower token index); the
     block keeps the union; if the union exceeds ``cap`` tokens, those with the
@@ -41,6 +47,33 @@ def block_corner_indices(R: int, bijk: np.ndarray, block: int = 8) -> np.ndarray
         out[:, n, 0] = np.where(a, hi[:, 0], lo[:, 0])
         out[:, n, 1] = np.where(b, hi[:, 1], lo[:, 1])
         out[:, n, 2] = np.where(c, hi[:, 2], lo[:, 2])
+    return out
+
+
+MASK64 = (1 << 64) - 1
+GAMMA = 0x9E3779B97F4A7C15
+
+
+def splitmix64(seed: int, c: int) -> int:
+    """The c-th output (from 0) of the SplitMix64 stream seeded with ``seed``:
+    the state advances by the golden-ratio increment, then is mixed."""
+    z = (seed + (c + 1) * GAMMA) & MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+    return z ^ (z >> 31)
+
+
+def block_random_indices(R: int, blocks: np.ndarray, NB: int, seed: int, block: int = 8) -> np.ndarray:
+    """[nblk, 8, 3] grid indices of the 8 random probes of the given block ids."""
+    blocks = np.asarray(blocks, np.int64).reshape(-1)
+    bijk = block_ijk(blocks, NB)
+    out = np.empty((blocks.size, 8, 3), np.int64)
+    for r, b in enumerate(blocks.tolist()):
+        for n in range(8):
+            for a in range(3):
+                lo = int(bijk[r, a]) * block
+                ext = min(block, R + 1 - lo)
+                out[r, n, a] = lo + splitmix64(seed, (8 * b + n) * 3 + a) % ext
     return out
 
 
@@ -87,11 +120,15 @@ def near_tie_tokens(scores: np.ndarray, k: int, rel: float = 1e-4) -> np.ndarray
 
 
 def select_blocks(decoder: dec.Decoder, R: int, blocks: np.ndarray, k: int, cap: int,
-                  block: int = 8, Qfn=None) -> Dict[int, np.ndarray]:
+                  block: int = 8, Qfn=None, probes: str = "corners", seed: int = 0) -> Dict[int, np.ndarray]:
     """Token sets for the given block ids of the R-cell grid. ``Qfn`` maps
-    float32 probe points to projections (default: the oracle's own)."""
+    float32 probe points to projections (default: the oracle's own). ``probes``:
+    "corners" or "random" (SplitMix64 stream seeded with ``seed``)."""
     NB = hv.nblocks(R + 1, block)
-    idx = block_corner_indices(R, block_ijk(blocks, NB), block)
+    if probes == "random":
+        idx = block_random_indices(R, blocks, NB, seed, block)
+    else:
+        idx = block_corner_indices(R, block_ijk(blocks, NB), block)
     out = {}
     for n, b in enumerate(np.asarray(blocks, np.int64)):
         pts = dec.grid_coord(idx[n], R).astype(np.float32)
@@ -100,16 +137,18 @@ def select_blocks(decoder: dec.Decoder, R: int, blocks: np.ndarray, k: int, cap:
     return out
 
 
-def make_decode(decoder: dec.Decoder, k: int, cap: int, block: int = 8, record: Optional[dict] = None):
+def make_decode(decoder: dec.Decoder, k: int, cap: int, block: int = 8, record: Optional[dict] = None,
+                probes: str = "corners", seed: int = 0):
     """A ``decode(R, lin)`` for ``hvd.hvd`` that groups the queries by block,
-    selects each block's tokens with its corner probes, and decodes the
-    block's queries against those tokens only."""
+    selects each block's tokens with its probes (random probes: the level with
+    R cells uses the stream seeded with seed + R), and decodes the block's
+    queries against those tokens only."""
 
     def decode(R: int, lin: np.ndarray) -> np.ndarray:
         P = R + 1
         blk = hv.block_of(lin, P, block)
         ub = np.unique(blk)
-        sets = select_blocks(decoder, R, ub, k, cap, block)
+        sets = select_blocks(decoder, R, ub, k, cap, block, probes=probes, seed=(seed + R) & MASK64)
         if record is not None:
             record[R] = sets
         out = np.empty(lin.size, np.float64)

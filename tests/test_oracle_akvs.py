@@ -64,6 +64,34 @@ def test_corner_probes_of_ragged_blocks():
     assert np.all(idx == 8)
 
 
+def test_splitmix64_reference_outputs():
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "splitmix64.json")))
+    assert akvs.splitmix64(0, 0) == int(g["seed_0_first"], 16)
+    assert [akvs.splitmix64(1234567, c) for c in range(5)] == [int(x) for x in g["seed_1234567_first_5"]]
+
+
+def test_random_probes_stay_in_their_blocks_and_cover_them():
+    R, NB = 75, 10
+    blocks = np.arange(NB ** 3)
+    idx = akvs.block_random_indices(R, blocks, NB, seed=99)
+    bijk = akvs.block_ijk(blocks, NB)
+    lo = bijk[:, None, :] * 8
+    hi = np.minimum(lo + 7, R)
+    assert (idx >= lo).all() and (idx <= hi).all()
+    # deterministic in the seed, different across seeds and blocks
+    assert np.array_equal(idx, akvs.block_random_indices(R, blocks, NB, seed=99))
+    assert not np.array_equal(idx, akvs.block_random_indices(R, blocks, NB, seed=100))
+    # roughly uniform over the 8 offsets of a full block (8000 draws per axis)
+    full = (bijk < 9).all(axis=1)
+    off = (idx - lo)[full].reshape(-1)
+    counts = np.bincount(off, minlength=8)
+    assert counts.min() > 0.9 * counts.mean() and counts.max() < 1.1 * counts.mean()
+    # the single-point edge blocks of an R = 8 grid keep their one point
+    idx = akvs.block_random_indices(8, np.array([7]), 2, seed=5)
+    assert np.all(idx == 8)
+
+
 def test_scores_mean_over_heads_of_softmax():
     rng = np.random.default_rng(35)
     Qp, K = rng.standard_normal((3, 256)), rng.standard_normal((50, 256))
