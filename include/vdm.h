@@ -143,6 +143,8 @@ typedef struct {
   int32_t block;     /* KV selection block edge in points (8) */
   int32_t k;         /* tokens kept per probe (64) */
   int32_t cap;       /* token cap per block (512) */
+  int32_t probes;    /* 0: corner probes; 1: random probes (see vdm_select_kv), level L seeded with seed + R0 * 2^L */
+  uint64_t seed;     /* random probes: SplitMix64 seed */
 } vdm_hier_params;
 
 /* Per-level counters written by vdm_decode_hier to a DEVICE array of int64:
@@ -197,8 +199,14 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
                             size_t ws_bytes, vdm_stream stream);
 
 /* Adaptive KV selection (section 4.1 item 2) for blocks of an R-cell grid.
- * For each listed block: its 8 corner points (indices block*b and
- * min(block*b + block - 1, R) per axis) are probes; a token's score for a probe
+ * For each listed block 8 probe points: probes = 0, its 8 corners (indices
+ * block*b and min(block*b + block - 1, R) per axis); probes = 1, 8 random grid
+ * points of the block, as the pages sample them: probe n of block id b takes
+ * along axis a (0 = x) the index lo_a + (u mod e_a), where lo_a is the block's
+ * first index, e_a its number of points along a, and u the c-th output (counted
+ * from 0, c = (8 b + n) * 3 + a) of the SplitMix64 stream seeded with `seed`
+ * (Steele, Lea and Flood 2014: state += 0x9E3779B97F4A7C15, then the mix of
+ * Vigna's reference splitmix64.c). A token's score for a probe
  * is the head-mean softmax probability; each probe keeps its top-k tokens (equal
  * scores: lower index first); the block keeps their union, reduced to the `cap`
  * tokens of largest max-over-probes score when larger (ties: lower index).
@@ -207,9 +215,9 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
  * Requires 1 <= k <= M, k <= cap, M <= 4096. Workspace:
  * vdm_select_workspace_size(dec, M). */
 vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,
-                         const void* K, int64_t M, const int32_t* blocks, int64_t nblk,
-                         int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes,
-                         vdm_stream stream);
+                         int32_t probes, uint64_t seed, const void* K, int64_t M,
+                         const int32_t* blocks, int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt,
+                         void* ws, size_t ws_bytes, vdm_stream stream);
 
 /* Hierarchical volume decoding (section 4.1 item 1), optionally with adaptive KV
  * selection at every level (item 2). Writes the final (R0*2^(levels-1) + 1)^3

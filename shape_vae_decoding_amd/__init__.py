@@ -70,7 +70,8 @@ class _KvSel(C.Structure):
 
 class _HierParams(C.Structure):
     _fields_ = [("R0", C.c_int32), ("levels", C.c_int32), ("dilation", C.c_int32), ("tau", C.c_float),
-                ("use_kvsel", C.c_int32), ("block", C.c_int32), ("k", C.c_int32), ("cap", C.c_int32)]
+                ("use_kvsel", C.c_int32), ("block", C.c_int32), ("k", C.c_int32), ("cap", C.c_int32),
+                ("probes", C.c_int32), ("seed", C.c_uint64)]
 
 
 _PtrArr = C.c_void_p * MAX_LEVELS
@@ -89,9 +90,9 @@ _lib.vdm_project_kv.restype = _st
 _lib.vdm_decode_dense.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_void_p, C.c_void_p, C.c_int64,
                                   C.POINTER(_KvSel), C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.vdm_decode_dense.restype = _st
-_lib.vdm_select_kv.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
-                               C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
-                               C.c_void_p]
+_lib.vdm_select_kv.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                               C.c_uint64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                               C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.vdm_select_kv.restype = _st
 _lib.vdm_decode_hier.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_void_p, C.c_void_p, C.c_int64,
                                  C.c_void_p, C.c_int64, C.c_void_p, C.POINTER(_HierDebug), C.c_void_p, C.c_size_t,
@@ -295,9 +296,13 @@ def vdm_decode_dense(dec: Decoder, q: Queries, K: torch.Tensor, V: torch.Tensor,
                                  ws.numel(), _stream(stream)))
 
 
+PROBES = {"corners": 0, "random": 1}
+
+
 def vdm_select_kv(dec: Decoder, R: int, block: int, k: int, cap: int, K: torch.Tensor,
                   blocks: Optional[torch.Tensor], sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
-                  nblk: Optional[int] = None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+                  nblk: Optional[int] = None, ws: Optional[torch.Tensor] = None, stream=None,
+                  probes: str = "corners", seed: int = 0) -> None:
     _dev(K, dec.torch_dtype, "K")
     _dev(sel_idx, torch.int32, "sel_idx")
     _dev(sel_cnt, torch.int32, "sel_cnt")
@@ -309,14 +314,16 @@ def vdm_select_kv(dec: Decoder, R: int, block: int, k: int, cap: int, K: torch.T
         nblk = nb ** 3
     if ws is None:
         ws = workspace(vdm_select_workspace_size(dec, K.shape[0]), K.device)
-    _check(_lib.vdm_select_kv(dec.ref, R, block, k, cap, K.data_ptr(), K.shape[0], _ptr(blocks), nblk,
-                              sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(ws), ws.numel(), _stream(stream)))
+    _check(_lib.vdm_select_kv(dec.ref, R, block, k, cap, PROBES[probes], seed, K.data_ptr(), K.shape[0],
+                              _ptr(blocks), nblk, sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(ws), ws.numel(),
+                              _stream(stream)))
 
 
 def hier_params(R0=75, levels=3, tau=2 * 2 / 300, dilation=1, kvsel: Optional[dict] = None) -> _HierParams:
-    p = _HierParams(R0, levels, dilation, float(tau), 0, 8, 64, 512)
+    p = _HierParams(R0, levels, dilation, float(tau), 0, 8, 64, 512, 0, 0)
     if kvsel:
         p.use_kvsel, p.block, p.k, p.cap = 1, kvsel.get("block", 8), kvsel["k"], kvsel["cap"]
+        p.probes, p.seed = PROBES[kvsel.get("probes", "corners")], kvsel.get("seed", 0)
     return p
 
 

@@ -247,6 +247,8 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   qs.xyz = nullptr;
   qs.list = A.blocks;
   qs.block = A.block;
+  qs.probes = A.probes;
+  qs.seed = A.seed;
   const int nkb = (M + 31) / 32;
   const int per = (nkb + SEL_NW - 1) / SEL_NW;
   const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);

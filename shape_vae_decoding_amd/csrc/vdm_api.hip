@@ -316,6 +316,7 @@ static vdm_status check_hier(const vdm_decoder* d, const vdm_hier_params* p, int
     if (p->block != 8) return fail(VDM_ERR_UNSUPPORTED, "KV selection blocks must be 8 points per axis");
     if (p->k < 1 || p->k > M || p->cap < p->k) return fail(VDM_ERR_INVALID_ARG, "k=%d cap=%d M=%lld", p->k, p->cap, (long long)M);
     if (M > 4096) return fail(VDM_ERR_UNSUPPORTED, "KV selection supports M <= 4096");
+    if (p->probes != 0 && p->probes != 1) return fail(VDM_ERR_INVALID_ARG, "probes=%d (0: corners, 1: random)", p->probes);
   }
   (void)d;
   return VDM_OK;
@@ -514,14 +515,15 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
   return VDM_OK;
 }
 
-vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, const void* K,
-                         int64_t M, const int32_t* blocks, int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt, void* ws,
-                         size_t ws_bytes, vdm_stream stream) {
+vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, int32_t probes,
+                         uint64_t seed, const void* K, int64_t M, const int32_t* blocks, int64_t nblk, int32_t* sel_idx,
+                         int32_t* sel_cnt, void* ws, size_t ws_bytes, vdm_stream stream) {
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;
   if (R < 1 || R > 1200 || block < 1) return fail(VDM_ERR_INVALID_ARG, "R=%d block=%d", R, block);
   if (M < 1 || M > 4096) return fail(M < 1 ? VDM_ERR_INVALID_ARG : VDM_ERR_UNSUPPORTED, "M=%lld (1..4096)", (long long)M);
   if (k < 1 || k > M || cap < k) return fail(VDM_ERR_INVALID_ARG, "k=%d cap=%d M=%lld", k, cap, (long long)M);
+  if (probes != 0 && probes != 1) return fail(VDM_ERR_INVALID_ARG, "probes=%d (0: corners, 1: random)", probes);
   const int64_t NB = (R + block) / block;
   if (nblk < 0 || (!blocks && nblk != NB * NB * NB))
     return fail(VDM_ERR_INVALID_ARG, "nblk=%lld (all blocks: %lld)", (long long)nblk, (long long)(NB * NB * NB));
@@ -541,6 +543,8 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
   a.block = block;
   a.k = k;
   a.cap = cap;
+  a.probes = probes;
+  a.seed = seed;
   a.M = (int)M;
   a.H = dec->H;
   a.D = dec->D;
@@ -602,6 +606,8 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       sa.block = 8;
       sa.k = p->k;
       sa.cap = p->cap;
+      sa.probes = p->probes;
+      sa.seed = p->seed + (uint64_t)R;  // a different stream per level
       sa.M = (int)M;
       sa.H = dec->H;
       sa.D = dec->D;

@@ -181,12 +181,41 @@ __device__ __forceinline__ Coords block_corner(int64_t b, int n, int R, int bloc
                 grid_coord(pick(bk, n & 1), R)};
 }
 
+// The c-th output (from 0) of the SplitMix64 stream seeded with `seed` (Steele,
+// Lea and Flood 2014; the mixing constants of Vigna's reference splitmix64.c):
+// the state advances by the golden-ratio increment, then is mixed.
+__device__ __forceinline__ unsigned long long splitmix64(unsigned long long seed, unsigned long long c) {
+  unsigned long long z = seed + (c + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Random probe n of block b: along axis a the index lo_a + (u mod e_a), lo_a the
+// block's first index, e_a its points along a, u output (8 b + n) * 3 + a of the
+// stream.
+__device__ __forceinline__ Coords block_random(int64_t b, int n, int R, int block, unsigned long long seed) {
+  const int64_t NB = (R + block) / block;
+  const int bx[3] = {(int)(b / (NB * NB)), (int)((b / NB) % NB), (int)(b % NB)};
+  float c[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int lo = block * bx[a];
+    const int ext = min(block, R + 1 - lo);
+    const unsigned long long u = splitmix64(seed, (unsigned long long)((8 * b + n) * 3 + a));
+    c[a] = grid_coord(lo + (int)(u % (unsigned long long)ext), R);
+  }
+  return Coords{c[0], c[1], c[2]};
+}
+
 // Position of query q of a tile's source (points, full grid, grid list, probes).
 __device__ __forceinline__ Coords query_coords(const QuerySrc& qs, int64_t q) {
   if (qs.mode == 0) return Coords{qs.xyz[3 * q], qs.xyz[3 * q + 1], qs.xyz[3 * q + 2]};
   if (qs.mode == 3) {
     const int64_t row = q >> 3;
-    return block_corner(qs.list ? (int64_t)qs.list[row] : row, (int)(q & 7), qs.R, qs.block);
+    const int64_t b = qs.list ? (int64_t)qs.list[row] : row;
+    return qs.probes ? block_random(b, (int)(q & 7), qs.R, qs.block, qs.seed)
+                     : block_corner(b, (int)(q & 7), qs.R, qs.block);
   }
   const int64_t lin = qs.mode == 1 ? q : (int64_t)qs.list[q];
   return grid_point(lin, qs.R);

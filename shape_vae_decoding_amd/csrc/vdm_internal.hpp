@@ -31,6 +31,8 @@ struct QuerySrc {
   const float* xyz;
   const int32_t* list;
   int block;
+  int probes = 0;          // mode 3: 0 = corner probes, 1 = random probes (SplitMix64 stream of `seed`)
+  unsigned long long seed = 0;
 };
 
 // A decode work item: queries [q0, q1) of the query source, attending to token
@@ -103,6 +105,8 @@ int decode_f_chunk(int dtype, int D);
 // KV selection for blocks; blocks == null: block id = row. n_blocks from host or *d_n_blocks.
 struct SelectArgs {
   int R, block, k, cap, M, H, D;
+  int probes;          // 0: the 8 corners of a block; 1: 8 random points (SplitMix64 stream of seed)
+  unsigned long long seed;
   const void* Wq;  // [D][51]
   const void* K;   // [M][D]
   const void* Kp;  // bf16: K packed like the dense decoder's tiles (launch_pack_kv), else unused

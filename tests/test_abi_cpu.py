@@ -104,24 +104,30 @@ def test_select_and_hier_argument_checks():
     d = _decoder()
     lib = V._lib
     # k > M, cap < k, M beyond the selection limit
-    assert lib.vdm_select_kv(C.byref(d), 75, 8, 65, 512, 0x1000, 64, None, 1000, 0x1000, 0x1000, None, 0,
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 65, 512, 0, 0, 0x1000, 64, None, 1000, 0x1000, 0x1000, None, 0,
                              None) == V.VDM_ERR_INVALID_ARG
-    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 32, 0x1000, 3072, None, 1000, 0x1000, 0x1000, None, 0,
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 32, 0, 0, 0x1000, 3072, None, 1000, 0x1000, 0x1000, None, 0,
                              None) == V.VDM_ERR_INVALID_ARG
-    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0x1000, 40960, None, 1000, 0x1000, 0x1000, None, 0,
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0, 0, 0x1000, 40960, None, 1000, 0x1000, 0x1000, None, 0,
                              None) == V.VDM_ERR_UNSUPPORTED
     # blocks == NULL requires nblk = NB^3 (76 points per axis -> 10 blocks)
-    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0x1000, 3072, None, 999, 0x1000, 0x1000, None, 0,
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0, 0, 0x1000, 3072, None, 999, 0x1000, 0x1000, None, 0,
+                             None) == V.VDM_ERR_INVALID_ARG
+    # probes: 0 (corners) or 1 (random)
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 2, 0, 0x1000, 3072, None, 1000, 0x1000, 0x1000, None, 0,
                              None) == V.VDM_ERR_INVALID_ARG
     # the score scratch is required and sized by vdm_select_workspace_size
     need = lib.vdm_select_workspace_size(C.byref(d), 3072)
     assert need >= 32 * 3072 * 4
-    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0x1000, 3072, None, 1000, 0x1000, 0x1000, 0x1000,
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0, 0, 0x1000, 3072, None, 1000, 0x1000, 0x1000, 0x1000,
                              need - 1, None) == V.VDM_ERR_WORKSPACE
     p = V.hier_params(R0=75, levels=3)
     assert lib.vdm_hier_workspace_size(C.byref(d), C.byref(p), 3072) > 27 * 10 ** 6 * 4
     bad = V.hier_params(R0=75, levels=7)
     assert lib.vdm_hier_workspace_size(C.byref(d), C.byref(bad), 3072) == 0
+    bad = V.hier_params(kvsel={"k": 64, "cap": 512})
+    bad.probes = 3
+    assert lib.vdm_hier_workspace_size(C.byref(d), C.byref(bad), 3072) == 0 and "probes" in V.vdm_last_error()
     bad = V.hier_params(tau=float("nan"))
     assert lib.vdm_decode_hier(C.byref(d), C.byref(bad), 0x1000, 0x1000, 3072, 0x1000, 301 ** 3, None, None,
                                0x1000, 1 << 40, None) == V.VDM_ERR_INVALID_ARG

@@ -25,16 +25,20 @@ def V():
     return mod
 
 
-def gpu_probe_q(dec, w, R, blocks, block=8):
-    idx = oak.block_corner_indices(R, oak.block_ijk(blocks, hv.nblocks(R + 1, block)), block)
+def gpu_probe_q(dec, w, R, blocks, block=8, probes="corners", seed=0):
+    NB = hv.nblocks(R + 1, block)
+    if probes == "random":
+        idx = oak.block_random_indices(R, blocks, NB, seed, block)
+    else:
+        idx = oak.block_corner_indices(R, oak.block_ijk(blocks, NB), block)
     pts = odec.grid_coord(idx.reshape(-1, 3), R).astype(np.float32)
     Q = torch.empty((pts.shape[0], w.D), dtype=tdtype(w), device=dev())
     V().vdm_embed_queries(dec, torch.from_numpy(pts).to(dev()), Q)
     return f64(Q).reshape(len(blocks), 8, w.D)
 
 
-def compare_sets(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt, block=8):
-    Qp = gpu_probe_q(dec, w, R, blocks, block)
+def compare_sets(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt, block=8, probes="corners", seed=0):
+    Qp = gpu_probe_q(dec, w, R, blocks, block, probes, seed)
     Kh = f64(K)
     n_amb = 0
     for r, b in enumerate(blocks):
@@ -51,12 +55,12 @@ def compare_sets(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt, block=8):
           flush=True)
 
 
-def run_select(dec, w, K, R, blocks, k, cap, block=8):
+def run_select(dec, w, K, R, blocks, k, cap, block=8, probes="corners", seed=0):
     nb = len(blocks)
     sel_idx = torch.empty((nb, cap), dtype=torch.int32, device=dev())
     sel_cnt = torch.empty(nb, dtype=torch.int32, device=dev())
     bt = torch.from_numpy(np.asarray(blocks, np.int32)).to(dev())
-    V().vdm_select_kv(dec, R, block, k, cap, K, bt, sel_idx, sel_cnt)
+    V().vdm_select_kv(dec, R, block, k, cap, K, bt, sel_idx, sel_cnt, probes=probes, seed=seed)
     torch.cuda.synchronize()
     return sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
 
@@ -74,6 +78,22 @@ def test_select_matches_oracle(R, k, cap):
     if cap == 100:
         assert np.all(sel_cnt == 100)  # the cap binds: 8 probes x 64 exceed it
     compare_sets(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt)
+
+
+@pytest.mark.parametrize("R,seed", [(75, 0), (150, 0x0123456789ABCDEF)])
+def test_select_with_random_probes_matches_oracle(R, seed):
+    # the pages' own probes: 8 random points per block from the SplitMix64 stream
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    K, _ = gpu_kv(dec, w)
+    nb = hv.nblocks(R + 1)
+    blocks = np.sort(np.random.default_rng(R).choice(nb ** 3, 60, replace=False))
+    blocks = np.unique(np.concatenate([blocks, [0, nb ** 3 - 1]]))
+    sel_idx, sel_cnt = run_select(dec, w, K, R, blocks, 64, 512, probes="random", seed=seed)
+    compare_sets(dec, w, K, R, blocks, 64, 512, sel_idx, sel_cnt, probes="random", seed=seed)
+    # and the sets differ from the corner probes' (other probe points)
+    ci, cc = run_select(dec, w, K, R, blocks, 64, 512)
+    assert any(not np.array_equal(ci[r, : cc[r]], sel_idx[r, : sel_cnt[r]]) for r in range(len(blocks)))
 
 
 def test_select_all_blocks_ragged_token_count():
@@ -140,13 +160,16 @@ def test_gathered_decode_matches_restricted_attention():
     assert worst <= TOL_BF16
 
 
-def test_hier_with_selection_full_workload():
+@pytest.mark.parametrize("probes", ["corners", "random"])
+def test_hier_with_selection_full_workload(probes):
     # the 75 -> 150 -> 300 workload with adaptive KV selection at every level
+    # (random probes: level L draws from the stream seeded with seed + R_L)
     w = W.make(3)
     dec = gpu_decoder(w)
     K, Vv = gpu_kv(dec, w)
     q = w.query
-    kv = q["kvsel"]
+    seed = 20251203
+    kv = dict(q["kvsel"], probes=probes, seed=seed)
     params = V().hier_params(R0=q["R0"], levels=q["levels"], tau=q["tau"], dilation=q["dilation"], kvsel=kv)
     levels = params.levels
     vol = torch.empty(301 ** 3, dtype=torch.float32, device=dev())
@@ -175,7 +198,8 @@ def test_hier_with_selection_full_workload():
         lst = d["list"][: s["queries"]].cpu().numpy().astype(np.int64)
         np.testing.assert_array_equal(blocks, np.unique(hv.block_of(lst, R + 1)))
         pick = np.sort(rng.choice(nocc, min(nocc, 40), replace=False))
-        compare_sets(dec, w, K, R, blocks[pick], kv["k"], kv["cap"], idx[pick], cnt[pick])
+        compare_sets(dec, w, K, R, blocks[pick], kv["k"], kv["cap"], idx[pick], cnt[pick], probes=probes,
+                     seed=seed + R)
         # decoded values with each block's selected tokens (identical inputs)
         volL = d["vol"].cpu().numpy()
         blk = hv.block_of(lst, R + 1)
@@ -195,7 +219,7 @@ def test_hier_with_selection_full_workload():
     flips = int(np.sum((vol_np < 0) != (dense_np < 0)))
     inter = np.sum((vol_np < 0) & (dense_np < 0))
     union = np.sum((vol_np < 0) | (dense_np < 0))
-    print(f"[akvs] vs dense at finest decoded points: max|dSDF| {dd.max():.3e} mean {dd.mean():.3e}; "
+    print(f"[akvs] {probes} probes vs dense at finest decoded points: max|dSDF| {dd.max():.3e} mean {dd.mean():.3e}; "
           f"sign flips over the volume {flips}; occupancy IoU {inter / union:.5f}", flush=True)
 
 
