@@ -432,6 +432,23 @@ def main():
     }
     # outside the timed steps: surface extraction of the hierarchical volume
     out["breakdown"]["surface_extraction_300cubed"] = surface_extraction(V, vol_h, Pf - 1, dev)
+    # outside the timed steps: the KV-selection volume with random probes (the pages' probe choice)
+    p_r = V.hier_params(R0=aq["R0"], levels=aq["levels"], tau=aq["tau"], dilation=aq["dilation"],
+                        kvsel=dict(aq["kvsel"], probes="random", seed=1))
+    st_r = torch.zeros(aq["levels"] * V.STAT_FIELDS, dtype=torch.int64, device=dev)
+    V.vdm_decode_hier(dec, p_r, K, Vv, vol_a, st_r, ws=ws_a)
+    torch.cuda.synchronize()
+    ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ra.record()
+    for _ in range(3):
+        V.vdm_decode_hier(dec, p_r, K, Vv, vol_a, st_r, ws=ws_a)
+    rb.record()
+    torch.cuda.synchronize()
+    sr = V.stats_dict(st_r, aq["levels"])
+    out["breakdown"]["akvs_random_probes"] = {
+        "ms_per_300cubed_volume": round(ra.elapsed_time(rb) / 3, 4),
+        "decoded_points": sum(x["queries"] for x in sr),
+        "mean_selected_tokens": round(sum(x["selected"] for x in sr) / max(sum(x["blocks"] for x in sr), 1), 1)}
     if not args.skip_cpu:
         # outside the timed steps (and left out of profiling runs): the large-token
         # workload and the machine's reference figures
