@@ -432,6 +432,26 @@ def main():
     }
     # outside the timed steps: surface extraction of the hierarchical volume
     out["breakdown"]["surface_extraction_300cubed"] = surface_extraction(V, vol_h, Pf - 1, dev)
+    # outside the timed steps: the pages' 384^3 resolution example (96 -> 192 -> 384, band of two fine widths)
+    p_384 = V.hier_params(R0=96, levels=3, tau=2 * 2 / 384, dilation=1)
+    vol_384 = torch.empty(385 ** 3, dtype=torch.float32, device=dev)
+    st_384 = torch.zeros(3 * V.STAT_FIELDS, dtype=torch.int64, device=dev)
+    ws_384 = V.workspace(V.vdm_hier_workspace_size(dec, p_384, w.M), dev)
+    V.vdm_decode_hier(dec, p_384, K, Vv, vol_384, st_384, ws=ws_384)
+    torch.cuda.synchronize()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for _ in range(3):
+        V.vdm_decode_hier(dec, p_384, K, Vv, vol_384, st_384, ws=ws_384)
+    eb.record()
+    torch.cuda.synchronize()
+    s384 = V.stats_dict(st_384, 3)
+    q384 = sum(x["queries"] for x in s384)
+    ms384 = ea.elapsed_time(eb) / 3
+    out["breakdown"]["hier_384cubed"] = {"ms_per_volume": round(ms384, 4), "decoded_points": q384,
+                                         "decoded_fraction": round(q384 / 385 ** 3, 5),
+                                         "volume_points_per_s": round(385 ** 3 / (ms384 / 1e3), 1)}
+    del vol_384, ws_384
     # outside the timed steps: the KV-selection volume with random probes (the pages' probe choice)
     p_r = V.hier_params(R0=aq["R0"], levels=aq["levels"], tau=aq["tau"], dilation=aq["dilation"],
                         kvsel=dict(aq["kvsel"], probes="random", seed=1))

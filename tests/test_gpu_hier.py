@@ -163,6 +163,21 @@ def test_hier_full_workload_lockstep():
     lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=600)
 
 
+def test_hier_384_target_lockstep():
+    # the pages' own resolution example: 96 -> 192 -> 384 (385^3 points), band of
+    # two fine widths
+    w = W.make(2)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    params = V().hier_params(R0=96, levels=3, tau=2 * 2 / 384, dilation=1)
+    vol, stats, dbg = run_hier(dec, params, K, Vv)
+    total = sum(s["queries"] for s in stats)
+    print(f"[hier] 384: decoded {total} of 385^3 points ({total / 385 ** 3:.2%})", flush=True)
+    od = oracle_decoder(w)
+    od.K, od.V = f64(K), f64(Vv)
+    lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=300)
+
+
 def test_hier_computed_points_equal_dense_decode():
     # hierarchical decoding without selection equals dense decoding: bitwise at
     # every decoded point; inherited points keep the dense sign (counted)
