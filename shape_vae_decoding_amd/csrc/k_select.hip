@@ -116,12 +116,14 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
       unsigned v[LV];
 #pragma unroll
       for (int j = 0; j < LV; ++j) v[j] = j * 64 + lane < total ? list[j * 64 + lane] : 0u;
+      // (counts by ballot and popcount: a short scalar chain per bit instead of a
+      // cross-lane reduction)
       for (int b = 31; b >= 0; --b) {
         const unsigned cand = p | (1u << b);
         int c = 0;
 #pragma unroll
-        for (int j = 0; j < LV; ++j) c += v[j] >= cand ? 1 : 0;
-        if (wave_sum(c) >= k) p = cand;
+        for (int j = 0; j < LV; ++j) c += __popcll(__ballot(v[j] >= cand));
+        if (c >= k) p = cand;
       }
       __builtin_amdgcn_wave_barrier();  // the list is read before the next search writes it
       done = true;
