@@ -14,7 +14,8 @@ Definition (all of it is restated from the geometry, no case table is copied):
   at the zero of the linear interpolant along the edge:
   t = v0 / (v0 - v1) from the lower end point, world coordinate -1 + 2 (i + t) / R
   on the edge's axis. Vertices are numbered by ascending edge id
-  3 * ((i * P + j) * P + k) + axis, P = R + 1, over the edges of processed cells.
+  axis * P^3 + (i * P + j) * P + k (all x edges, then y, then z; P = R + 1),
+  over the crossing edges of processed cells.
 * Each cell's surface is found face by face. On a cube face with two crossing
   edges one segment joins them; on a face with four (two inside corners on a
   diagonal) each inside corner is cut off by its own segment, so inside corners
@@ -139,7 +140,7 @@ def fan_apex(loop) -> List[int]:
 
 
 def edge_id(i: int, j: int, k: int, a: int, P: int) -> int:
-    return 3 * ((i * P + j) * P + k) + a
+    return a * P ** 3 + (i * P + j) * P + k
 
 
 def crossing_edges(vol3: np.ndarray) -> np.ndarray:
@@ -153,7 +154,7 @@ def crossing_edges(vol3: np.ndarray) -> np.ndarray:
         lo[a] = slice(0, P - 1)
         hi[a] = slice(1, P)
         x = np.argwhere(ins[tuple(lo)] != ins[tuple(hi)])
-        ids.append(3 * ((x[:, 0] * P + x[:, 1]) * P + x[:, 2]) + a)
+        ids.append(a * P ** 3 + (x[:, 0] * P + x[:, 1]) * P + x[:, 2])
     return np.sort(np.concatenate(ids)).astype(np.int64)
 
 
@@ -196,8 +197,8 @@ def vertex_positions(vol3: np.ndarray, edges: np.ndarray, R: int) -> np.ndarray:
     """World coordinates (float64) of the vertices on the given edge ids."""
     P = R + 1
     v = vol3.astype(np.float64).reshape(-1)
-    a = edges % 3
-    p = edges // 3
+    a = edges // P ** 3
+    p = edges % P ** 3
     step = np.array([P * P, P, 1], dtype=np.int64)[a]
     v0, v1 = v[p], v[p + step]
     t = v0 / (v0 - v1)

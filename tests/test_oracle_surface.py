@@ -84,7 +84,7 @@ def test_plane_lies_on_the_zero_set_and_faces_the_positive_side():
     v = (X - 0.13).astype(np.float32)
     V, T, E = S.extract(v, R)
     assert np.abs(V[:, 0] - 0.13).max() < 1e-6
-    assert set(np.unique(E % 3)) == {0}  # only x edges cross
+    assert set(np.unique(E // (R + 1) ** 3)) == {0}  # only x edges cross
     assert len(V) == (R + 1) ** 2
     n, _ = normals(V, T)
     area = 0.5 * np.linalg.norm(n, axis=1)
