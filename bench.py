@@ -249,6 +249,60 @@ def surface_extraction(V, vol, R: int, dev, reps: int = 10):
             "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def akvs_block_sweep(V, dec, K, Vv, vol, R: int, dev, reps: int = 3):
+    """KV selection with sub-volumes of 4^3, 8^3 and 16^3 points (the pages' size
+    trade-off) on the near-surface points of a decoded volume (|SDF| < 0.02): per
+    block size the selection and the gathered decode times, the mean set size and
+    the error against full attention at the same points."""
+    import torch
+
+    P = R + 1
+    lin = torch.nonzero(vol.abs() < 0.02).squeeze(1)
+    N = lin.numel()
+    ref = torch.empty(N, dtype=torch.float32, device=dev)
+    M = K.shape[0]
+    ws = V.workspace(V.vdm_dense_workspace_size(dec, M, N, True), dev)
+    V.vdm_decode_dense(dec, V.queries_list(R, lin.int()), K, Vv, ref, ws=ws)
+    i, j, k = lin // (P * P), (lin // P) % P, lin % P
+    out = {"points": N}
+    ws_sel = V.workspace(V.vdm_select_workspace_size(dec, M), dev)
+    for block in (4, 8, 16):
+        NB = -(-P // block)
+        bid = ((i // block) * NB + j // block) * NB + k // block
+        key = bid * block ** 3 + ((i % block) * block + j % block) * block + k % block
+        order = torch.argsort(key)
+        lst = lin[order].int().contiguous()
+        occ = torch.unique(bid).int().contiguous()
+        row = torch.full((NB ** 3,), -1, dtype=torch.int32, device=dev)
+        row[occ.long()] = torch.arange(occ.numel(), dtype=torch.int32, device=dev)
+        sel_idx = torch.empty((occ.numel(), 512), dtype=torch.int32, device=dev)
+        sel_cnt = torch.empty(occ.numel(), dtype=torch.int32, device=dev)
+        got = torch.empty(N, dtype=torch.float32, device=dev)
+        q = V.queries_list(R, lst)
+        sel = V.kvsel(block, 512, sel_idx, sel_cnt, row)
+
+        def run():
+            V.vdm_select_kv(dec, R, block, 64, 512, K, occ, sel_idx, sel_cnt, ws=ws_sel)
+            V.vdm_decode_dense(dec, q, K, Vv, got, sel=sel, ws=ws)
+        run()
+        torch.cuda.synchronize()
+        V.vdm_timing(2)
+        V.vdm_timing(1)
+        for _ in range(reps):
+            run()
+        V.vdm_timing(0)
+        ns, ms_s = V.vdm_timing_read("select")
+        nd, ms_d = V.vdm_timing_read("decode_gathered")
+        V.vdm_timing(2)
+        d = (got - ref[order]).abs()
+        flips = int(((got < 0) != (ref[order] < 0)).sum())
+        out[f"block_{block}"] = {"blocks": occ.numel(), "mean_selected": round(float(sel_cnt.float().mean()), 1),
+                                 "select_ms": round(ms_s / ns, 4), "gathered_decode_ms": round(ms_d / nd, 4),
+                                 "max_abs_dsdf": round(float(d.max()), 5), "mean_abs_dsdf": round(float(d.mean()), 6),
+                                 "sign_flips": flips}
+    return out
+
+
 def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 5):
     """Achievable HBM bandwidth: a device-to-device copy (read + write bytes / time)."""
     import torch
@@ -452,6 +506,8 @@ def main():
                                          "decoded_fraction": round(q384 / 385 ** 3, 5),
                                          "volume_points_per_s": round(385 ** 3 / (ms384 / 1e3), 1)}
     del vol_384, ws_384
+    # outside the timed steps: selection with 4^3, 8^3 and 16^3 sub-volumes on the near-surface points
+    out["breakdown"]["akvs_block_sweep"] = akvs_block_sweep(V, dec, K, Vv, vol_h, Pf - 1, dev)
     # outside the timed steps: the KV-selection volume with random probes (the pages' probe choice)
     p_r = V.hier_params(R0=aq["R0"], levels=aq["levels"], tau=aq["tau"], dilation=aq["dilation"],
                         kvsel=dict(aq["kvsel"], probes="random", seed=1))

@@ -65,19 +65,20 @@ def run_select(dec, w, K, R, blocks, k, cap, block=8, probes="corners", seed=0):
     return sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
 
 
-@pytest.mark.parametrize("R,k,cap", [(75, 64, 512), (75, 64, 100), (150, 32, 512)])
-def test_select_matches_oracle(R, k, cap):
+@pytest.mark.parametrize("R,k,cap,block", [(75, 64, 512, 8), (75, 64, 100, 8), (150, 32, 512, 8), (75, 64, 512, 16),
+                                           (150, 64, 512, 4)])
+def test_select_matches_oracle(R, k, cap, block):
     w = W.make(1)
     dec = gpu_decoder(w)
     K, _ = gpu_kv(dec, w)
-    nb = hv.nblocks(R + 1)
+    nb = hv.nblocks(R + 1, block)
     blocks = np.sort(np.random.default_rng(R + k + cap).choice(nb ** 3, 60, replace=False))
     blocks = np.unique(np.concatenate([blocks, [0, nb ** 3 - 1]]))  # include the ragged corner block
-    sel_idx, sel_cnt = run_select(dec, w, K, R, blocks, k, cap)
+    sel_idx, sel_cnt = run_select(dec, w, K, R, blocks, k, cap, block)
     assert np.all(sel_cnt <= cap) and np.all(sel_cnt >= k)
     if cap == 100:
         assert np.all(sel_cnt == 100)  # the cap binds: 8 probes x 64 exceed it
-    compare_sets(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt)
+    compare_sets(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt, block)
 
 
 @pytest.mark.parametrize("R,seed", [(75, 0), (150, 0x0123456789ABCDEF)])
@@ -130,33 +131,38 @@ def test_k_equal_all_tokens_is_full_attention():
     assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
 
 
-def test_gathered_decode_matches_restricted_attention():
+@pytest.mark.parametrize("block", [8, 4, 16])
+def test_gathered_decode_matches_restricted_attention(block):
+    # sub-volumes of block^3 points (the pages' size trade-off); the list in the
+    # blocked order of that block size
     w = W.make(1)
     dec = gpu_decoder(w)
     K, Vv = gpu_kv(dec, w)
     R = 30
-    nb = hv.nblocks(R + 1)
+    nb = hv.nblocks(R + 1, block)
     sel_idx = torch.empty((nb ** 3, 512), dtype=torch.int32, device=dev())
     sel_cnt = torch.empty(nb ** 3, dtype=torch.int32, device=dev())
-    V().vdm_select_kv(dec, R, 8, 64, 512, K, None, sel_idx, sel_cnt)
-    lst = hv.blocked_order(np.ones((R + 1,) * 3, bool)).astype(np.int32)
+    V().vdm_select_kv(dec, R, block, 64, 512, K, None, sel_idx, sel_cnt)
+    lin = np.arange((R + 1) ** 3)
+    lst = lin[np.argsort(hv.blocked_key(lin, R + 1, block), kind="stable")].astype(np.int32)
     out = torch.empty(lst.size, dtype=torch.float32, device=dev())
     V().vdm_decode_dense(dec, V().queries_list(R, torch.from_numpy(lst).to(dev())), K, Vv, out,
-                         sel=V().kvsel(8, 512, sel_idx, sel_cnt))
+                         sel=V().kvsel(block, 512, sel_idx, sel_cnt))
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     si, sc = sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
     od = oracle_decoder(w)
     Kh, Vh = f64(K), f64(Vv)
-    blk = hv.block_of(lst, R + 1)
+    blk = hv.block_of(lst, R + 1, block)
     rng = np.random.default_rng(4)
     worst = 0.0
-    for b in rng.choice(np.unique(blk), 12, replace=False):
+    ub = np.unique(blk)
+    for b in rng.choice(ub, min(12, ub.size), replace=False):
         m = np.nonzero(blk == b)[0][:40]
         toks = si[b, : sc[b]]
         ref = od.sdf(odec.grid_points(R, lst[m]), Kh[toks], Vh[toks])
         worst = max(worst, np.abs(out[m].astype(np.float64) - ref).max())
-    report("gathered decode vs restricted attention", worst, TOL_BF16)
+    report(f"gathered decode vs restricted attention (blocks of {block}^3)", worst, TOL_BF16)
     assert worst <= TOL_BF16
 
 
@@ -249,7 +255,8 @@ def test_gathered_decode_mixed_softmax_paths():
     blk = hv.block_of(lst, R + 1)
     rng = np.random.default_rng(5)
     worst = 0.0
-    for b in rng.choice(np.unique(blk), 12, replace=False):
+    ub = np.unique(blk)
+    for b in rng.choice(ub, min(12, ub.size), replace=False):
         m = np.nonzero(blk == b)[0][:40]
         toks = si[b, : sc[b]]
         ref = od.sdf(odec.grid_points(R, lst[m]), Kh[toks], Vh[toks])
