@@ -303,6 +303,51 @@ def akvs_block_sweep(V, dec, K, Vv, vol, R: int, dev, reps: int = 3):
     return out
 
 
+def batched_decode(V, W, dec, dev, B: int = 4, R: int = 32, reps: int = 5):
+    """B vecsets at the same (R+1)^3 grid: one batched decode launch against B
+    single-shape calls (launch time from the library's HIP events)."""
+    import numpy as np
+    import torch
+
+    w = W.make(1)
+    rng = np.random.default_rng(3)
+    Ks, Vs = [], []
+    for b in range(B):
+        Z = w.Z if b == 0 else w.Z * np.float32(0.8) + np.float32(0.2) * rng.standard_normal(w.Z.shape).astype(np.float32)
+        Zt = torch.from_numpy(np.ascontiguousarray(Z, np.float32)).to(dev).to(torch.bfloat16)
+        k, v = torch.empty_like(Zt), torch.empty_like(Zt)
+        V.vdm_project_kv(dec, Zt, k, v)
+        Ks.append(k)
+        Vs.append(v)
+    K, Vv = torch.stack(Ks).contiguous(), torch.stack(Vs).contiguous()
+    q = V.queries_grid(R)
+    N = (R + 1) ** 3
+    out = torch.empty((B, N), dtype=torch.float32, device=dev)
+    ws_b = V.workspace(V.vdm_dense_batch_workspace_size(dec, B, w.M), dev)
+    ws_1 = V.workspace(V.vdm_dense_workspace_size(dec, w.M, N), dev)
+    one = torch.empty(N, dtype=torch.float32, device=dev)
+    V.vdm_decode_dense_batch(dec, q, K, Vv, out, ws=ws_b)
+    torch.cuda.synchronize()
+    res = {"shapes": B, "grid_points": N}
+    for name, fn in (("batched", lambda: V.vdm_decode_dense_batch(dec, q, K, Vv, out, ws=ws_b)),
+                     ("single_calls", lambda: [V.vdm_decode_dense(dec, q, K[b], Vv[b], one, ws=ws_1) for b in range(B)])):
+        fn()
+        torch.cuda.synchronize()
+        V.vdm_timing(2)
+        V.vdm_timing(1)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        V.vdm_timing(0)
+        torch.cuda.synchronize()
+        n, ms = V.vdm_timing_read("decode")
+        V.vdm_timing(2)
+        res[name] = {"decode_launch_ms_per_batch": round(ms / reps, 4), "call_ms_per_batch": round(a.elapsed_time(e) / reps, 4)}
+    return res
+
+
 def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 5):
     """Achievable HBM bandwidth: a device-to-device copy (read + write bytes / time)."""
     import torch
@@ -506,6 +551,8 @@ def main():
                                          "decoded_fraction": round(q384 / 385 ** 3, 5),
                                          "volume_points_per_s": round(385 ** 3 / (ms384 / 1e3), 1)}
     del vol_384, ws_384
+    # outside the timed steps: a batch of 4 vecsets at a 33^3 grid in one decode launch vs 4 calls
+    out["breakdown"]["batched_decode_4x33cubed"] = batched_decode(V, W, dec, dev)
     # outside the timed steps: selection with 4^3, 8^3 and 16^3 sub-volumes on the near-surface points
     out["breakdown"]["akvs_block_sweep"] = akvs_block_sweep(V, dec, K, Vv, vol_h, Pf - 1, dev)
     # outside the timed steps: the KV-selection volume with random probes (the pages' probe choice)

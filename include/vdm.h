@@ -198,6 +198,17 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
                             const void* V, int64_t M, const vdm_kvsel* sel, float* sdf, void* ws,
                             size_t ws_bytes, vdm_stream stream);
 
+/* Dense decoding of a batch of B vecsets (shapes) at the same N query points:
+ * one decode launch for the whole batch (the packing of each shape's K/V is one
+ * launch per shape). K, V: [B, M, D] in dtype, shape b at byte offset
+ * b * M * D * element size (which must keep 16-byte alignment); sdf: [B, N]
+ * float32. Shape b's results equal, bit for bit, those of vdm_decode_dense on
+ * that shape alone. No token selection. Requires 1 <= B <= 4096. Workspace:
+ * vdm_dense_batch_workspace_size(dec, B, M). */
+vdm_status vdm_decode_dense_batch(const vdm_decoder* dec, const vdm_queries* q, int32_t B,
+                                  const void* K, const void* V, int64_t M, float* sdf, void* ws,
+                                  size_t ws_bytes, vdm_stream stream);
+
 /* Adaptive KV selection (section 4.1 item 2) for blocks of an R-cell grid.
  * For each listed block 8 probe points: probes = 0, its 8 corners (indices
  * block*b and min(block*b + block - 1, R) per axis); probes = 1, 8 random grid
@@ -279,6 +290,7 @@ size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, in
 size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M);
 size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M);
 size_t vdm_surface_workspace_size(int32_t R);
+size_t vdm_dense_batch_workspace_size(const vdm_decoder* dec, int32_t B, int64_t M);
 
 /* ---------------------------------------------------------------- kernel timing */
 

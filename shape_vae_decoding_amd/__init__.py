@@ -34,6 +34,7 @@ EXPORTS = [
     "vdm_embed_queries", "vdm_project_kv", "vdm_decode_dense", "vdm_select_kv", "vdm_decode_hier",
     "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_timing",
     "vdm_timing_read", "vdm_version", "vdm_last_error", "vdm_extract_surface", "vdm_surface_workspace_size",
+    "vdm_decode_dense_batch", "vdm_dense_batch_workspace_size",
 ]
 TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "cell_test", "dilate", "mark", "scan",
               "emit", "fill", "surface"]
@@ -109,6 +110,11 @@ _lib.vdm_extract_surface.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void
 _lib.vdm_extract_surface.restype = _st
 _lib.vdm_surface_workspace_size.argtypes = [C.c_int32]
 _lib.vdm_surface_workspace_size.restype = C.c_size_t
+_lib.vdm_decode_dense_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_int32, C.c_void_p, C.c_void_p,
+                                        C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.vdm_decode_dense_batch.restype = _st
+_lib.vdm_dense_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int64]
+_lib.vdm_dense_batch_workspace_size.restype = C.c_size_t
 _lib.vdm_timing.argtypes = [C.c_int32]
 _lib.vdm_timing.restype = C.c_int
 _lib.vdm_timing_read.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
@@ -270,6 +276,30 @@ def vdm_dense_workspace_size(dec: Decoder, M: int, N: int, with_sel: bool = Fals
     if n == 0:
         raise VdmError(VDM_ERR_INVALID_ARG, vdm_last_error())
     return n
+
+
+def vdm_dense_batch_workspace_size(dec: Decoder, B: int, M: int) -> int:
+    n = _lib.vdm_dense_batch_workspace_size(dec.ref, B, M)
+    if n == 0:
+        raise VdmError(-1, vdm_last_error())
+    return n
+
+
+def vdm_decode_dense_batch(dec: Decoder, q: Queries, K: torch.Tensor, V: torch.Tensor, sdf: torch.Tensor,
+                           ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """K, V [B, M, D] in the decoder dtype, sdf [B, N] float32 (see include/vdm.h)."""
+    _dev(K, dec.torch_dtype, "K")
+    _dev(V, dec.torch_dtype, "V")
+    _dev(sdf, torch.float32, "sdf")
+    if K.dim() != 3 or V.shape != K.shape or sdf.dim() != 2 or sdf.shape[0] != K.shape[0] or sdf.shape[1] < q.N:
+        raise ValueError("K, V must be [B, M, D] and sdf [B, N]")
+    if sdf.shape[1] != q.N:
+        raise ValueError("sdf rows must hold exactly N values (the batch stride is N)")
+    B, M = K.shape[0], K.shape[1]
+    if ws is None:
+        ws = workspace(vdm_dense_batch_workspace_size(dec, B, M), sdf.device)
+    _check(_lib.vdm_decode_dense_batch(dec.ref, C.byref(q.struct), B, K.data_ptr(), V.data_ptr(), M, sdf.data_ptr(),
+                                       ws.data_ptr(), ws.numel(), _stream(stream)))
 
 
 def vdm_select_workspace_size(dec: Decoder, M: int) -> int:

@@ -496,7 +496,7 @@ __device__ __forceinline__ bool any_below(const float (&x)[N], float lim) {
 // Dense attention of this wave's QB query blocks over all M tokens: the
 // software-pipelined loop over 32-token tiles (see pipe_iter).
 template <typename C, bool SHIFT>
-__device__ __forceinline__ void dense_attention(const DecodeArgs& A, int nkeys, int hw, int lane,
+__device__ __forceinline__ void dense_attention(const DecodeArgs& A, int shape, int nkeys, int hw, int lane,
                                                 const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
                                                 const float (&nb)[C::QB], f32x16 (&O)[2][C::QB],
                                                 float (&l_run)[C::QB]) {
@@ -507,8 +507,8 @@ __device__ __forceinline__ void dense_attention(const DecodeArgs& A, int nkeys, 
   // loads K(k+2) into kb[k&1], V(k) into vb[k&1]; the loop runs the full
   // iterations two at a time so buffers are static.
   const int64_t packed_bytes = (int64_t)nkt * C::KT * C::D * C::SZ;
-  const __amdgpu_buffer_rsrc_t Kg = buffer_of(A.Kp, packed_bytes);
-  const __amdgpu_buffer_rsrc_t Vg = buffer_of(A.Vt, packed_bytes);
+  const __amdgpu_buffer_rsrc_t Kg = buffer_of((const char*)A.Kp + shape * A.kv_stride, packed_bytes);
+  const __amdgpu_buffer_rsrc_t Vg = buffer_of((const char*)A.Vt + shape * A.kv_stride, packed_bytes);
   auto load_k = [&](int t, uint4 (&r)[C::RUN_U4]) { load_run<C>(Kg, t, hw, lane, r); };
   auto load_v = [&](int t, uint4 (&r)[C::RUN_U4]) { load_run<C>(Vg, t, hw, lane, r); };
   auto nothing = [](int) {};
@@ -833,13 +833,14 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // wave-uniform: scalar registers
   const int hw = wave % C::H, qg = wave / C::H;
   const int64_t nq = A.d_N ? (int64_t)*A.d_N : A.N;
-  const int64_t n_tiles = A.items ? (A.d_n_items ? (int64_t)*A.d_n_items : A.n_tiles) : (nq + C::BQ - 1) / C::BQ;
+  const int nbatch = A.batch > 1 ? A.batch : 1;
+  const int64_t tps = (nq + C::BQ - 1) / C::BQ;  // dense tiles per shape
+  const int64_t n_tiles = A.items ? (A.d_n_items ? (int64_t)*A.d_n_items : A.n_tiles) : tps * nbatch;
   const T* __restrict__ Kg = (const T*)A.Kp;
   const T* __restrict__ Vg = (const T*)A.Vt;
   const T* __restrict__ Wo = (const T*)A.Wo;
   const T* __restrict__ W1 = (const T*)A.W1;
   const T* __restrict__ W2 = (const T*)A.W2;
-  const float kmax = A.kmax[hw];
 
   const float2* gtab = reinterpret_cast<const float2*>(lds + C::GTAB);
   if constexpr (C::GELU_TABLE) gelu_table_fill(reinterpret_cast<float2*>(lds + C::GTAB), tid0, C::NT);
@@ -859,7 +860,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     // loop, whose registers are all taken.
     int tid = opaque(tid0), lane = opaque(lane0);
     int64_t q0, q1;
-    int row = -1;
+    int row = -1, shape = 0;
     if (A.items) {
       // one item per workgroup: its fields are uniform (scalar registers)
       const Item it = A.items[tile];
@@ -867,9 +868,15 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       q1 = __builtin_amdgcn_readfirstlane(it.q1);
       row = __builtin_amdgcn_readfirstlane(it.row);
     } else {
-      q0 = tile * C::BQ;
+      int64_t lt = tile;
+      if (nbatch > 1) {
+        shape = (int)(tile / tps);
+        lt = tile - (int64_t)shape * tps;
+      }
+      q0 = lt * C::BQ;
       q1 = q0 + C::BQ < nq ? q0 + C::BQ : nq;
     }
+    const float kmax = A.kmax[shape * C::H + hw];
 
     // ---------------------------------------------------------------- Q = Wq e(p)
     // (scaled by log2(e)/sqrt(64) before the one rounding, so logits come out in base 2)
@@ -920,9 +927,9 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       if (!active) {
         // (every query of this wave lies past the tile's end: nothing to attend)
       } else if (shift) {
-        dense_attention<C, true>(A, nkeys, hw, lane, qf, nb, O, l_run);
+        dense_attention<C, true>(A, shape, nkeys, hw, lane, qf, nb, O, l_run);
       } else {
-        dense_attention<C, false>(A, nkeys, hw, lane, qf, nb, O, l_run);
+        dense_attention<C, false>(A, shape, nkeys, hw, lane, qf, nb, O, l_run);
       }
     } else {
       // (both variants pass the same barriers, so waves may take different ones)
@@ -1052,7 +1059,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
         const float sdf = analytic_sdf(p, A.prims) + A.net_scale * net;
         int64_t o = q;
         if (A.scatter) o = A.qs.mode == 1 ? q : (int64_t)A.qs.list[q];
-        A.out[o] = sdf;
+        A.out[o + shape * A.out_stride] = sdf;
       }
     }
     __syncthreads();
@@ -1079,7 +1086,7 @@ static hipError_t run(const DecodeArgs& a, hipStream_t s) {
   if (per_cu < 1) per_cu = 1;
   int64_t grid = (int64_t)dev_info().cus * per_cu;
   if (!a.d_N && !a.d_n_items) {
-    const int64_t host_tiles = a.items ? a.n_tiles : (a.N + C::BQ - 1) / C::BQ;
+    const int64_t host_tiles = a.items ? a.n_tiles : (a.N + C::BQ - 1) / C::BQ * (a.batch > 1 ? a.batch : 1);
     if (host_tiles < grid) grid = host_tiles;
   }
   if (grid < 1) return hipSuccess;

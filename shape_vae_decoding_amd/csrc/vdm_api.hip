@@ -235,6 +235,27 @@ static size_t dense_ws(const vdm_decoder* d, int64_t M, int64_t N, bool sel, voi
   return c.off + 256;
 }
 
+// batch of B vecsets: packed K/V per shape, kmax [B][H]
+struct BatchWs {
+  char* Kp;
+  char* Vt;
+  void* Wp;
+  float* kmax;
+  size_t kv;  // packed bytes per shape (K or V)
+};
+
+static size_t batch_ws(const vdm_decoder* d, int64_t B, int64_t M, void* base, BatchWs* w) {
+  Carve c(base);
+  BatchWs x;
+  x.kv = ((size_t)mpad(M) * d->D * esize(d->dtype) + 255) / 256 * 256;
+  x.Kp = c.take<char>(x.kv * B);
+  x.Vt = c.take<char>(x.kv * B);
+  x.Wp = c.take<char>(packed_w_bytes(d));
+  x.kmax = c.take<float>((size_t)B * d->H * 4);
+  if (w) *w = x;
+  return c.off + 256;
+}
+
 // ------------------------------------------------------------------ hierarchical workspace
 struct HierWs {
   void* Kp;
@@ -512,6 +533,72 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
     a.cap = sel->cap;
     VDM_HIP_T(VDM_TIME_DECODE_GATHERED, s, launch_decode(dec->dtype, dec->D, true, a, s), "gathered decode launch");
   }
+  return VDM_OK;
+}
+
+size_t vdm_dense_batch_workspace_size(const vdm_decoder* dec, int32_t B, int64_t M) {
+  if (check_decoder(dec) != VDM_OK) return 0;
+  if (B < 1 || B > 4096 || M < 1 || M >= (1ll << 31) / dec->D) {
+    fail(VDM_ERR_INVALID_ARG, "B=%d M=%lld", B, (long long)M);
+    return 0;
+  }
+  return batch_ws(dec, B, M, nullptr, nullptr);
+}
+
+vdm_status vdm_decode_dense_batch(const vdm_decoder* dec, const vdm_queries* q, int32_t B, const void* K,
+                                  const void* V, int64_t M, float* sdf, void* ws, size_t ws_bytes,
+                                  vdm_stream stream) {
+  vdm_status st = check_decoder(dec);
+  if (st != VDM_OK) return st;
+  if (B < 1 || B > 4096) return fail(VDM_ERR_INVALID_ARG, "B=%d (1..4096)", B);
+  if (!q) return fail(VDM_ERR_INVALID_ARG, "queries is NULL");
+  if (q->N < 0 || q->N >= (1ll << 31)) return fail(VDM_ERR_INVALID_ARG, "N=%lld", (long long)q->N);
+  if (q->mode < VDM_Q_POINTS || q->mode > VDM_Q_GRID_LIST) return fail(VDM_ERR_INVALID_ARG, "query mode %d", q->mode);
+  if (q->mode != VDM_Q_POINTS) {
+    if (q->R < 1 || q->R > 1200) return fail(VDM_ERR_INVALID_ARG, "grid R=%d outside 1..1200", q->R);
+    const int64_t P = q->R + 1;
+    if (q->mode == VDM_Q_GRID && q->N != P * P * P)
+      return fail(VDM_ERR_INVALID_ARG, "grid mode needs N=(R+1)^3=%lld (got %lld)", (long long)(P * P * P), (long long)q->N);
+  }
+  if (q->N == 0) return VDM_OK;
+  if (M < 1 || M >= (1ll << 31) / dec->D) return fail(VDM_ERR_INVALID_ARG, "M=%lld", (long long)M);
+  if (!K || !V || !sdf) return fail(VDM_ERR_INVALID_ARG, "K, V or sdf is NULL");
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(sdf, 4)) return fail(VDM_ERR_INVALID_ARG, "misaligned K, V or sdf");
+  if ((M * dec->D * (int64_t)esize(dec->dtype)) % 16 != 0)
+    return fail(VDM_ERR_INVALID_ARG, "each shape's K/V must start 16-byte aligned (M * D * element size)");
+  if (q->mode == VDM_Q_POINTS && (!q->xyz || !aligned(q->xyz, 4))) return fail(VDM_ERR_INVALID_ARG, "xyz NULL or misaligned");
+  if (q->mode == VDM_Q_GRID_LIST && (!q->list || !aligned(q->list, 4)))
+    return fail(VDM_ERR_INVALID_ARG, "list NULL or misaligned");
+  const size_t need = batch_ws(dec, B, M, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(VDM_ERR_WORKSPACE, "workspace needs %zu bytes, 256-aligned (got %zu)", need, ws_bytes);
+  BatchWs w;
+  batch_ws(dec, B, M, ws, &w);
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  DecodeArgs a = base_args(dec);
+  a.qs = QuerySrc{q->mode, q->R, q->xyz, q->list, 0};
+  a.N = q->N;
+  a.out = sdf;
+  a.scatter = 0;
+  a.kmax = w.kmax;
+  const size_t shape_bytes = (size_t)M * dec->D * esize(dec->dtype);
+  VDM_HIP(launch_zero(w.kmax, ((size_t)B * dec->H * 4 + 7) / 8 * 8, s), "zero launch");  // (within its 256-byte slot)
+  VDM_HIP(pack_weights(dec, w.Wp, a, s), "weight packing launch");
+  for (int b = 0; b < B; ++b) {
+    const char* Kb = (const char*)K + b * shape_bytes;
+    const char* Vb = (const char*)V + b * shape_bytes;
+    VDM_HIP(launch_key_norms(dec->dtype, Kb, (int)M, dec->H, w.kmax + (size_t)b * dec->H, s), "key norms launch");
+    VDM_HIP(launch_pack_kv(dec->dtype, Kb, Vb, (int)M, dec->D, (int)mpad(M), w.Kp + b * w.kv, w.Vt + b * w.kv, s),
+            "pack_kv launch");
+  }
+  a.Kp = w.Kp;
+  a.Vt = w.Vt;
+  a.M = (int)M;
+  a.batch = B;
+  a.kv_stride = (int64_t)w.kv;
+  a.out_stride = q->N;
+  VDM_HIP_T(VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, false, a, s), "batched decode launch");
   return VDM_OK;
 }
 

@@ -69,6 +69,12 @@ struct DecodeArgs {
   const int32_t* sel_idx;
   const int32_t* sel_cnt;
   int cap;
+  // dense batch of vecsets (0 or 1: one): tile t belongs to shape t / tiles-per-shape,
+  // whose packed K/V start kv_stride bytes after the previous shape's, kmax at
+  // [shape][H], and outputs at out + shape * out_stride
+  int batch;
+  int64_t kv_stride;
+  int64_t out_stride;
 };
 
 struct DevInfo {

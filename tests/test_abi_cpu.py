@@ -184,3 +184,21 @@ def test_surface_extraction_argument_checks():
     assert call(edges=fake + 4) == V.VDM_ERR_INVALID_ARG
     assert call(wsb=n300 - 1) == V.VDM_ERR_WORKSPACE
     assert call(ws=fake + 16) == V.VDM_ERR_WORKSPACE
+
+
+def test_batched_decode_argument_checks():
+    import shape_vae_decoding_amd as V
+
+    lib = V._lib
+    d = _decoder()
+    q = V._Queries(V.VDM_Q_GRID, 16, 17 ** 3, None, None)
+    assert lib.vdm_dense_batch_workspace_size(C.byref(d), 0, 3072) == 0
+    need = lib.vdm_dense_batch_workspace_size(C.byref(d), 4, 3072)
+    one = lib.vdm_dense_batch_workspace_size(C.byref(d), 1, 3072)
+    assert need > 3 * (one - 2 * 256)  # per-shape packed K/V dominate
+    assert lib.vdm_decode_dense_batch(C.byref(d), C.byref(q), 0, 0x1000, 0x1000, 3072, 0x1000, 0x1000, need,
+                                      None) == V.VDM_ERR_INVALID_ARG
+    assert lib.vdm_decode_dense_batch(C.byref(d), C.byref(q), 4, None, 0x1000, 3072, 0x1000, 0x1000, need,
+                                      None) == V.VDM_ERR_INVALID_ARG
+    assert lib.vdm_decode_dense_batch(C.byref(d), C.byref(q), 4, 0x1000, 0x1000, 3072, 0x1000, 0x1000, need - 1,
+                                      None) == V.VDM_ERR_WORKSPACE

@@ -273,3 +273,43 @@ def test_large_logits_shifted_softmax(gains):
     report(f"logit gains {gains} (queries above the bound per head {np.round(frac, 2)})", err, TOL_BF16)
     assert np.all(np.isfinite(f64(sdf)))
     assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("mode", ["grid", "points"])
+def test_batched_decode_equals_single_shape_calls_bitwise(mode):
+    # B vecsets in one decode launch: every shape's SDF equals its own vdm_decode_dense
+    # call bit for bit; shape 0 against the oracle on a sample
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    rng = np.random.default_rng(21)
+    Zs = [w.Z] + [w.Z * np.float32(0.8) + np.float32(0.2) * rng.standard_normal(w.Z.shape).astype(np.float32)
+                  for _ in range(2)]
+    KV = [gpu_kv(dec, w, Z) for Z in Zs]
+    K = torch.stack([k for k, _ in KV]).contiguous()
+    Vv = torch.stack([v for _, v in KV]).contiguous()
+    if mode == "grid":
+        R = 24
+        q = V().queries_grid(R)
+    else:
+        xyz = torch.from_numpy(rng.uniform(-1, 1, (1001, 3)).astype(np.float32)).to(dev())
+        q = V().queries_points(xyz)
+    print(f"[batch] {mode}: B={len(Zs)} N={q.N}", flush=True)
+    out = torch.empty((len(Zs), q.N), dtype=torch.float32, device=dev())
+    V().vdm_decode_dense_batch(dec, q, K, Vv, out)
+    for b in range(len(Zs)):
+        one = torch.empty(q.N, dtype=torch.float32, device=dev())
+        V().vdm_decode_dense(dec, q, K[b], Vv[b], one)
+        torch.cuda.synchronize()
+        assert torch.equal(out[b], one), b
+    # a batch of one is the single call
+    one = torch.empty((1, q.N), dtype=torch.float32, device=dev())
+    V().vdm_decode_dense_batch(dec, q, K[1:2].contiguous(), Vv[1:2].contiguous(), one)
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], out[1])
+    od = oracle_decoder(w)
+    od.K, od.V = f64(K[0]), f64(Vv[0])
+    pick = np.sort(rng.choice(q.N, 200, replace=False))
+    ref = od.sdf_grid(R, pick) if mode == "grid" else od.sdf(f64(xyz)[pick])
+    err = np.abs(out[0].cpu().numpy()[pick].astype(np.float64) - ref).max()
+    report(f"batched decode ({mode}), shape 0 vs oracle", err, TOL_BF16)
+    assert err <= TOL_BF16
