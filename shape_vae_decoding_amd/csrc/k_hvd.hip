@@ -87,48 +87,100 @@ static hipError_t launch_fold(int64_t* part, int f0, int nf, int64_t* dst0, int6
 // (kept_prev = the previous level's kept cells; null at level 0). A tested cell
 // is active when its corner values include s < 0 and s >= 0, or min |s| < tau.
 // One workgroup per 2x2x2 group of 8x8x8 cell blocks (the children of one parent
-// block): the parent block's 8 words are read once, and a cell block none of whose
-// parents was kept (most of them above level 0) only writes its zero words.
-// For a tested block the 9x9x9 corner points are staged in LDS, each read once.
+// block). The parent block's 8 words are read once (scalar loads) and decide which
+// child blocks hold a child of a kept parent; a group with none (most of them above
+// level 0) only writes its zero words. For the others the 9x9x9 corner points of
+// every such child block are loaded together (two loads per thread and block, all
+// in flight, indexes clamped into the volume: clamped points belong only to cells
+// that are not tested) and staged in LDS, then each block is tested with one lane
+// per cell; a cell's parent bit comes from the parent words already in registers.
+__device__ __forceinline__ bool child_block(int NB, int gi, int gj, int gk, int c, int& bi, int& bj, int& bk) {
+  bi = 2 * gi + (c >> 2);
+  bj = 2 * gj + ((c >> 1) & 1);
+  bk = 2 * gk + (c & 1);
+  return bi < NB && bj < NB && bk < NB;
+}
+
 __global__ __launch_bounds__(512) void cell_test_kernel(const float* __restrict__ vol, int R, int NB,
                                                         const uint64_t* __restrict__ kept_prev, int NBp,
                                                         float tau, uint64_t* __restrict__ active, int64_t* part) {
-  __shared__ float cv[9 * 9 * 9];
+  constexpr int NP = 9 * 9 * 9;
+  __shared__ float cv[8][NP];
   __shared__ int cnt[2][8];
   const int NG = (NB + 1) / 2;
-  const int64_t g = blockIdx.x;
-  const int gi = (int)(g / ((int64_t)NG * NG)), gj = (int)((g / NG) % NG), gk = (int)(g % NG);
-  const int ii = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.x;  // NG^3 <= 76^3
+  const int gi = g / (NG * NG), gj = (g / NG) % NG, gk = g % NG;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ii = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint64_t pw[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r)
     pw[r] = kept_prev ? kept_prev[(((int64_t)gi * NBp + gj) * NBp + gk) * 8 + r] : ~0ull;
-  int nt_w = 0, na_w = 0;  // this wave's counts (lane 0)
-  const int64_t P = R + 1;
+  // child block c (of the group) is tested when it exists and one of its parents was
+  // kept: rows 4(c>>2) .. +3 of the parent block, the 4x4 square (4bj .. 4bj+3) x
+  // (4bk .. 4bk+3) of each row's word
+  int exists = 0, tmask = 0;
+#pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const int bi = 2 * gi + (c >> 2), bj = 2 * gj + ((c >> 1) & 1), bk = 2 * gk + (c & 1);
-    if (bi >= NB || bj >= NB || bk >= NB) continue;
-    const int64_t b = ((int64_t)bi * NB + bj) * NB + bk;
-    // parents of this block: rows 4(c>>2) .. +3 of the parent block, the 4x4 square
-    // (4bj .. 4bj+3) x (4bk .. 4bk+3) of each row's word
-    const uint64_t sq = 0x0f0f0f0full << (((4 * bj) & 7) * 8 + ((4 * bk) & 7));
+    int bi, bj, bk;
+    if (!child_block(NB, gi, gj, gk, c, bi, bj, bk)) continue;
+    exists |= 1 << c;
+    const uint64_t sq = 0x0f0f0f0full << (((c >> 1) & 1) * 32 + (c & 1) * 4);
     const int r0 = 4 * (c >> 2);
-    if (((pw[r0] | pw[r0 + 1] | pw[r0 + 2] | pw[r0 + 3]) & sq) == 0ull) {  // uniform
+    if ((pw[r0] | pw[r0 + 1] | pw[r0 + 2] | pw[r0 + 3]) & sq) tmask |= 1 << c;
+  }
+  if (tmask == 0) {  // no tested cell: 64 zero words (one per thread of the first wave)
+    int bi, bj, bk;
+    if (tid < 64 && child_block(NB, gi, gj, gk, tid >> 3, bi, bj, bk))
+      active[(((int64_t)bi * NB + bj) * NB + bk) * 8 + (tid & 7)] = 0ull;
+    return;
+  }
+  // corner points t0 = tid and t1 = tid + 512 (t1 < NP for tid < 217) of each tested block
+  const int64_t P = R + 1;
+  const int t1 = min(tid + 512, NP - 1);
+  const int c0i = tid / 81, c0j = (tid / 9) % 9, c0k = tid % 9;
+  const int c1i = t1 / 81, c1j = (t1 / 9) % 9, c1k = t1 % 9;
+  float x0[8], x1[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    x0[c] = x1[c] = 0.f;
+    if (tmask >> c & 1) {
+      const int I0 = 16 * gi + 8 * (c >> 2), J0 = 16 * gj + 8 * ((c >> 1) & 1), K0 = 16 * gk + 8 * (c & 1);
+      x0[c] = vol[((int64_t)min(I0 + c0i, R) * P + min(J0 + c0j, R)) * P + min(K0 + c0k, R)];
+      x1[c] = vol[((int64_t)min(I0 + c1i, R) * P + min(J0 + c1j, R)) * P + min(K0 + c1k, R)];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    if (tmask >> c & 1) {
+      cv[c][tid] = x0[c];
+      if (tid + 512 < NP) cv[c][t1] = x1[c];
+    }
+  __syncthreads();
+  int nt_w = 0, na_w = 0;  // this wave's counts (lane 0)
+  const int jj = lane >> 3, kk = lane & 7;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if (!(exists >> c & 1)) continue;
+    const int bi = 2 * gi + (c >> 2), bj = 2 * gj + ((c >> 1) & 1), bk = 2 * gk + (c & 1);
+    const int64_t b = ((int64_t)bi * NB + bj) * NB + bk;
+    if (!(tmask >> c & 1)) {
       if (lane == 0) active[b * 8 + ii] = 0ull;
       continue;
     }
-    for (int t = threadIdx.x; t < 9 * 9 * 9; t += 512) {
-      const int ci = t / 81, cj = (t / 9) % 9, ck = t % 9;
-      const int I = 8 * bi + ci, J = 8 * bj + cj, K = 8 * bk + ck;
-      cv[t] = (I <= R && J <= R && K <= R) ? vol[((int64_t)I * P + J) * P + K] : 0.f;
-    }
-    __syncthreads();
-    const int i = 8 * bi + ii, j = 8 * bj + (lane >> 3), k = 8 * bk + (lane & 7);
+    const int i = 8 * bi + ii, j = 8 * bj + jj, k = 8 * bk + kk;
     bool tested = i < R && j < R && k < R;
-    if (tested && kept_prev) tested = mask_bit(kept_prev, NBp, i >> 1, j >> 1, k >> 1);
+    if (kept_prev) {
+      // parent cell (i/2, j/2, k/2) lies in the group's parent block: row 4(c>>2) + ii/2,
+      // bit (4((c>>1)&1) + jj/2) * 8 + 4(c&1) + kk/2
+      const int r = 4 * (c >> 2) + (ii >> 1);
+      const uint64_t row = r == 0 ? pw[0] : r == 1 ? pw[1] : r == 2 ? pw[2] : r == 3 ? pw[3]
+                         : r == 4 ? pw[4] : r == 5 ? pw[5] : r == 6 ? pw[6] : pw[7];
+      tested = tested && ((row >> ((4 * ((c >> 1) & 1) + (jj >> 1)) * 8 + 4 * (c & 1) + (kk >> 1))) & 1ull);
+    }
     bool act = false;
     if (tested) {
-      const float* v = cv + (ii * 9 + (lane >> 3)) * 9 + (lane & 7);
+      const float* v = &cv[c][(ii * 9 + jj) * 9 + kk];
       bool neg = false, nonneg = false;
       float mn = __builtin_inff();
 #pragma unroll
@@ -150,14 +202,13 @@ __global__ __launch_bounds__(512) void cell_test_kernel(const float* __restrict_
       nt_w += __popcll(tw);
       na_w += __popcll(aw);
     }
-    __syncthreads();  // cv is reused by the next block
   }
   if (lane == 0) {
     cnt[0][ii] = nt_w;
     cnt[1][ii] = na_w;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int nt = 0, na = 0;
     for (int w = 0; w < 8; ++w) {
       nt += cnt[0][w];
