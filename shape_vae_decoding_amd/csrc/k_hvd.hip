@@ -86,14 +86,15 @@ static hipError_t launch_fold(int64_t* part, int f0, int nf, int64_t* dst0, int6
 // computed: every cell at level 0, the children of kept parents afterwards
 // (kept_prev = the previous level's kept cells; null at level 0). A tested cell
 // is active when its corner values include s < 0 and s >= 0, or min |s| < tau.
-// One workgroup per 2x2x2 group of 8x8x8 cell blocks (the children of one parent
-// block). The parent block's 8 words are read once (scalar loads) and decide which
-// child blocks hold a child of a kept parent; a group with none (most of them above
-// level 0) only writes its zero words. For the others the 9x9x9 corner points of
-// every such child block are loaded together (two loads per thread and block, all
-// in flight, indexes clamped into the volume: clamped points belong only to cells
-// that are not tested) and staged in LDS, then each block is tested with one lane
-// per cell; a cell's parent bit comes from the parent words already in registers.
+// One wave tests one 8x8x8 cell block: lane (jj, kk) holds the 9 x 2 x 2 corner
+// values of its column of cells (i = 8bi .. 8bi+7), 36 loads in flight at once
+// (indexes clamped into the volume: clamped points belong only to cells that are
+// not tested), and each of the 8 cell rows gives one ballot word. Level 0 has one
+// wave per cell block. Above it one wave takes the 2x2x2 child blocks of one parent
+// block: the parent block's 8 words (scalar loads) decide which child blocks hold a
+// child of a kept parent, the others only get their zero words, and a cell's parent
+// bit comes from the same registers. (Loading two tested blocks at a time measured
+// slower: the registers it takes cost more occupancy than the overlap gains.)
 __device__ __forceinline__ bool child_block(int NB, int gi, int gj, int gk, int c, int& bi, int& bj, int& bk) {
   bi = 2 * gi + (c >> 2);
   bj = 2 * gj + ((c >> 1) & 1);
@@ -101,120 +102,101 @@ __device__ __forceinline__ bool child_block(int NB, int gi, int gj, int gk, int 
   return bi < NB && bj < NB && bk < NB;
 }
 
-__global__ __launch_bounds__(512) void cell_test_kernel(const float* __restrict__ vol, int R, int NB,
-                                                        const uint64_t* __restrict__ kept_prev, int NBp,
-                                                        float tau, uint64_t* __restrict__ active, int64_t* part) {
-  constexpr int NP = 9 * 9 * 9;
-  __shared__ float cv[8][NP];
-  __shared__ int cnt[2][8];
-  const int NG = (NB + 1) / 2;
-  const int g = blockIdx.x;  // NG^3 <= 76^3
-  const int gi = g / (NG * NG), gj = (g / NG) % NG, gk = g % NG;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int ii = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint64_t pw[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-    pw[r] = kept_prev ? kept_prev[(((int64_t)gi * NBp + gj) * NBp + gk) * 8 + r] : ~0ull;
-  // child block c (of the group) is tested when it exists and one of its parents was
-  // kept: rows 4(c>>2) .. +3 of the parent block, the 4x4 square (4bj .. 4bj+3) x
-  // (4bk .. 4bk+3) of each row's word
-  int exists = 0, tmask = 0;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    int bi, bj, bk;
-    if (!child_block(NB, gi, gj, gk, c, bi, bj, bk)) continue;
-    exists |= 1 << c;
-    const uint64_t sq = 0x0f0f0f0full << (((c >> 1) & 1) * 32 + (c & 1) * 4);
-    const int r0 = 4 * (c >> 2);
-    if ((pw[r0] | pw[r0 + 1] | pw[r0 + 2] | pw[r0 + 3]) & sq) tmask |= 1 << c;
-  }
-  if (tmask == 0) {  // no tested cell: 64 zero words (one per thread of the first wave)
-    int bi, bj, bk;
-    if (tid < 64 && child_block(NB, gi, gj, gk, tid >> 3, bi, bj, bk))
-      active[(((int64_t)bi * NB + bj) * NB + bk) * 8 + (tid & 7)] = 0ull;
-    return;
-  }
-  // corner points t0 = tid and t1 = tid + 512 (t1 < NP for tid < 217) of each tested block
+// Corner values of the column of cells (i = 8bi .. 8bi+7, j = 8bj + lane/8,
+// k = 8bk + lane%8): v[a][e] = point (8bi + a, j + e/2, k + e%2), clamped into the volume.
+__device__ __forceinline__ void load_cell_block(const float* __restrict__ vol, int R, int bi, int bj, int bk, int lane,
+                                                float (&v)[9][4]) {
   const int64_t P = R + 1;
-  const int t1 = min(tid + 512, NP - 1);
-  const int c0i = tid / 81, c0j = (tid / 9) % 9, c0k = tid % 9;
-  const int c1i = t1 / 81, c1j = (t1 / 9) % 9, c1k = t1 % 9;
-  float x0[8], x1[8];
+  const int J = 8 * bj + (lane >> 3), K = 8 * bk + (lane & 7);
+  const int64_t Ja = min(J, R) * P, Jb = min(J + 1, R) * P;
+  const int Ka = min(K, R), Kb = min(K + 1, R);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    x0[c] = x1[c] = 0.f;
-    if (tmask >> c & 1) {
-      const int I0 = 16 * gi + 8 * (c >> 2), J0 = 16 * gj + 8 * ((c >> 1) & 1), K0 = 16 * gk + 8 * (c & 1);
-      x0[c] = vol[((int64_t)min(I0 + c0i, R) * P + min(J0 + c0j, R)) * P + min(K0 + c0k, R)];
-      x1[c] = vol[((int64_t)min(I0 + c1i, R) * P + min(J0 + c1j, R)) * P + min(K0 + c1k, R)];
-    }
+  for (int a = 0; a < 9; ++a) {
+    const float* row = vol + (int64_t)min(8 * bi + a, R) * P * P;
+    v[a][0] = row[Ja + Ka];
+    v[a][1] = row[Ja + Kb];
+    v[a][2] = row[Jb + Ka];
+    v[a][3] = row[Jb + Kb];
   }
+}
+
+// Test the block's 512 cells, write its 8 active words, add to the wave's counts.
+// SPARSE: the parent bit of cell row ii is pw[r0 + ii/2] >> psh.
+template <bool SPARSE>
+__device__ __forceinline__ void test_cell_block(const float (&v)[9][4], int R, int NB, int bi, int bj, int bk,
+                                                int lane, const uint64_t (&pw)[8], int r0, int psh, float tau,
+                                                uint64_t* __restrict__ active, int& nt, int& na) {
+  const bool in_jk = 8 * bj + (lane >> 3) < R && 8 * bk + (lane & 7) < R;
+  uint64_t mine = 0;
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    if (tmask >> c & 1) {
-      cv[c][tid] = x0[c];
-      if (tid + 512 < NP) cv[c][t1] = x1[c];
-    }
-  __syncthreads();
-  int nt_w = 0, na_w = 0;  // this wave's counts (lane 0)
-  const int jj = lane >> 3, kk = lane & 7;
+  for (int ii = 0; ii < 8; ++ii) {
+    bool tested = in_jk && 8 * bi + ii < R;
+    if (SPARSE) tested = tested && ((pw[r0 + (ii >> 1)] >> psh) & 1ull);
+    bool neg = false, nonneg = false;
+    float mn = __builtin_inff();
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    if (!(exists >> c & 1)) continue;
-    const int bi = 2 * gi + (c >> 2), bj = 2 * gj + ((c >> 1) & 1), bk = 2 * gk + (c & 1);
-    const int64_t b = ((int64_t)bi * NB + bj) * NB + bk;
-    if (!(tmask >> c & 1)) {
-      if (lane == 0) active[b * 8 + ii] = 0ull;
-      continue;
-    }
-    const int i = 8 * bi + ii, j = 8 * bj + jj, k = 8 * bk + kk;
-    bool tested = i < R && j < R && k < R;
-    if (kept_prev) {
-      // parent cell (i/2, j/2, k/2) lies in the group's parent block: row 4(c>>2) + ii/2,
-      // bit (4((c>>1)&1) + jj/2) * 8 + 4(c&1) + kk/2
-      const int r = 4 * (c >> 2) + (ii >> 1);
-      const uint64_t row = r == 0 ? pw[0] : r == 1 ? pw[1] : r == 2 ? pw[2] : r == 3 ? pw[3]
-                         : r == 4 ? pw[4] : r == 5 ? pw[5] : r == 6 ? pw[6] : pw[7];
-      tested = tested && ((row >> ((4 * ((c >> 1) & 1) + (jj >> 1)) * 8 + 4 * (c & 1) + (kk >> 1))) & 1ull);
-    }
-    bool act = false;
-    if (tested) {
-      const float* v = &cv[c][(ii * 9 + jj) * 9 + kk];
-      bool neg = false, nonneg = false;
-      float mn = __builtin_inff();
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const float sv = v[(a * 9 + cc) * 9 + d];
-            neg |= sv < 0.f;
-            nonneg |= sv >= 0.f;
-            mn = fminf(mn, fabsf(sv));
-          }
-      act = (neg && nonneg) || mn < tau;
-    }
+      for (int e = 0; e < 4; ++e) {
+        const float sv = v[ii + a][e];
+        neg |= sv < 0.f;
+        nonneg |= sv >= 0.f;
+        mn = fminf(mn, fabsf(sv));
+      }
+    const bool act = tested && ((neg && nonneg) || mn < tau);
     const uint64_t tw = __ballot(tested), aw = __ballot(act);
-    if (lane == 0) {
-      active[b * 8 + ii] = aw;
-      nt_w += __popcll(tw);
-      na_w += __popcll(aw);
+    nt += __popcll(tw);
+    na += __popcll(aw);
+    if (lane == ii) mine = aw;
+  }
+  if (lane < 8) active[(((int64_t)bi * NB + bj) * NB + bk) * 8 + lane] = mine;
+}
+
+template <bool SPARSE>
+__global__ __launch_bounds__(256) void cell_test_kernel(const float* __restrict__ vol, int R, int NB,
+                                                        const uint64_t* __restrict__ kept_prev, int NBp,
+                                                        float tau, uint64_t* __restrict__ active, int64_t* part,
+                                                        int nunits) {
+  const int lane = threadIdx.x & 63;
+  const int u = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+  if (u >= nunits) return;
+  int nt = 0, na = 0;
+  uint64_t pw[8];
+  if (!SPARSE) {  // unit = one cell block
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pw[r] = ~0ull;
+    const int bi = u / (NB * NB), bj = (u / NB) % NB, bk = u % NB;
+    float v[9][4];
+    load_cell_block(vol, R, bi, bj, bk, lane, v);
+    test_cell_block<false>(v, R, NB, bi, bj, bk, lane, pw, 0, 0, tau, active, nt, na);
+  } else {  // unit = the 2x2x2 child blocks of parent block u
+    const int NG = (NB + 1) / 2;
+    const int gi = u / (NG * NG), gj = (u / NG) % NG, gk = u % NG;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pw[r] = kept_prev[(((int64_t)gi * NBp + gj) * NBp + gk) * 8 + r];
+    const int jj = lane >> 3, kk = lane & 7;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      int bi, bj, bk;
+      if (!child_block(NB, gi, gj, gk, c, bi, bj, bk)) continue;
+      // parents of child block c: rows 4(c>>2) .. +3 of the parent block, the 4x4
+      // square (4bj .. 4bj+3) x (4bk .. 4bk+3) of each row's word
+      const int r0 = 4 * (c >> 2);
+      const uint64_t sq = 0x0f0f0f0full << (((c >> 1) & 1) * 32 + (c & 1) * 4);
+      if (((pw[r0] | pw[r0 + 1] | pw[r0 + 2] | pw[r0 + 3]) & sq) == 0ull) {
+        if (lane < 8) active[(((int64_t)bi * NB + bj) * NB + bk) * 8 + lane] = 0ull;
+        continue;
+      }
+      // parent of cell (i, j, k) = (i/2, j/2, k/2): row r0 + ii/2, bit
+      // (4((c>>1)&1) + jj/2) * 8 + 4(c&1) + kk/2
+      const int psh = (4 * ((c >> 1) & 1) + (jj >> 1)) * 8 + 4 * (c & 1) + (kk >> 1);
+      float v[9][4];
+      load_cell_block(vol, R, bi, bj, bk, lane, v);
+      test_cell_block<true>(v, R, NB, bi, bj, bk, lane, pw, r0, psh, tau, active, nt, na);
     }
   }
-  if (lane == 0) {
-    cnt[0][ii] = nt_w;
-    cnt[1][ii] = na_w;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int nt = 0, na = 0;
-    for (int w = 0; w < 8; ++w) {
-      nt += cnt[0][w];
-      na += cnt[1][w];
-    }
-    int64_t* slot = part + (g % STAT_SLOTS) * 8;
+  if (lane == 0 && (nt | na)) {
+    int64_t* slot = part + (u % STAT_SLOTS) * 8;
     if (nt) atomicAdd((unsigned long long*)slot, (unsigned long long)nt);
     if (na) atomicAdd((unsigned long long*)(slot + 1), (unsigned long long)na);
   }
@@ -223,8 +205,14 @@ __global__ __launch_bounds__(512) void cell_test_kernel(const float* __restrict_
 hipError_t launch_cell_test(const float* vol, int R, const uint64_t* kept_prev, float tau, uint64_t* active,
                             int64_t* part, int64_t* stat_tested, int64_t* stat_active, hipStream_t s) {
   const int NB = nblocks8(R + 1), NBp = nblocks8(R / 2 + 1), NG = (NB + 1) / 2;
-  hipLaunchKernelGGL(cell_test_kernel, dim3((unsigned)((int64_t)NG * NG * NG)), dim3(512), 0, s, vol, R, NB,
-                     kept_prev, NBp, tau, active, part);
+  const int nunits = kept_prev ? NG * NG * NG : NB * NB * NB;
+  const dim3 grid((unsigned)((nunits + 3) / 4));
+  if (kept_prev)
+    hipLaunchKernelGGL(cell_test_kernel<true>, grid, dim3(256), 0, s, vol, R, NB, kept_prev, NBp, tau, active, part,
+                       nunits);
+  else
+    hipLaunchKernelGGL(cell_test_kernel<false>, grid, dim3(256), 0, s, vol, R, NB, kept_prev, NBp, tau, active,
+                       part, nunits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_fold(part, 0, 2, stat_tested, stat_active, s);
