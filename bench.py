@@ -348,6 +348,51 @@ def batched_decode(V, W, dec, dev, B: int = 4, R: int = 32, reps: int = 5):
     return res
 
 
+def batched_hier(V, W, dec, dev, params_of, B: int = 4, reps: int = 3):
+    """B vecsets through the hierarchical decode: one vdm_decode_hier_batch call
+    (the shapes on up to four streams at once) against B single-shape calls, for
+    plain HVD and HVD with KV selection (call time, HIP events on the stream)."""
+    import numpy as np
+    import torch
+
+    w = W.make(1)
+    rng = np.random.default_rng(5)
+    Ks, Vs = [], []
+    for b in range(B):
+        Z = w.Z if b == 0 else w.Z * np.float32(0.8) + np.float32(0.2) * rng.standard_normal(w.Z.shape).astype(np.float32)
+        Zt = torch.from_numpy(np.ascontiguousarray(Z, np.float32)).to(dev).to(torch.bfloat16)
+        k, v = torch.empty_like(Zt), torch.empty_like(Zt)
+        V.vdm_project_kv(dec, Zt, k, v)
+        Ks.append(k)
+        Vs.append(v)
+    K, Vv = torch.stack(Ks).contiguous(), torch.stack(Vs).contiguous()
+    res = {"shapes": B}
+    for mode in ("hvd", "hvd_akvs"):
+        params = params_of(mode == "hvd_akvs")
+        P3 = ((params.R0 << (params.levels - 1)) + 1) ** 3
+        vol = torch.empty((B, P3), dtype=torch.float32, device=dev)
+        ws_b = V.workspace(V.vdm_hier_batch_workspace_size(dec, params, B, w.M), dev)
+        ws_1 = V.workspace(V.vdm_hier_workspace_size(dec, params, w.M), dev)
+        r = {}
+        for name, fn in (("batched", lambda: V.vdm_decode_hier_batch(dec, params, K, Vv, vol, ws=ws_b)),
+                         ("single_calls", lambda: [V.vdm_decode_hier(dec, params, K[b], Vv[b], vol[b], ws=ws_1)
+                                                   for b in range(B)])):
+            fn()
+            torch.cuda.synchronize()
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            r[name] = round(a.elapsed_time(e) / reps, 3)
+        r["ms_per_volume_batched"] = round(r["batched"] / B, 3)
+        r["ms_per_volume_single"] = round(r["single_calls"] / B, 3)
+        res[mode] = {"ms_per_batch": r, "speedup": round(r["single_calls"] / r["batched"], 3)}
+        del vol, ws_b, ws_1
+    return res
+
+
 def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 5):
     """Achievable HBM bandwidth: a device-to-device copy (read + write bytes / time)."""
     import torch
@@ -553,6 +598,7 @@ def main():
     del vol_384, ws_384
     # outside the timed steps: a batch of 4 vecsets at a 33^3 grid in one decode launch vs 4 calls
     out["breakdown"]["batched_decode_4x33cubed"] = batched_decode(V, W, dec, dev)
+    out["breakdown"]["batched_hier_4x301cubed"] = batched_hier(V, W, dec, dev, lambda kv: p_a if kv else p_h)
     # outside the timed steps: selection with 4^3, 8^3 and 16^3 sub-volumes on the near-surface points
     out["breakdown"]["akvs_block_sweep"] = akvs_block_sweep(V, dec, K, Vv, vol_h, Pf - 1, dev)
     # outside the timed steps: the KV-selection volume with random probes (the pages' probe choice)

@@ -247,6 +247,23 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* params
                            int64_t* stats, const vdm_hier_debug* dbg, void* ws, size_t ws_bytes,
                            vdm_stream stream);
 
+/* Hierarchical decoding of a batch of B vecsets (shapes) with the same params:
+ * shape b runs vdm_decode_hier on K, V at byte offset b * M * D * element size
+ * (which must keep 16-byte alignment), writes vol + b * (R+1)^3 (R the finest
+ * grid; vol_elems covers all B volumes) and, when stats is not NULL, stats +
+ * b * levels * VDM_STAT_FIELDS, with workspace slice b of
+ * vdm_hier_batch_workspace_size(dec, params, B, M) / B bytes. The shapes run on up
+ * to four streams at once (the call's stream and three side streams that the
+ * library creates on first use per device, ordered after the call's stream by an
+ * event and joined back into it by events), so the small bookkeeping launches of
+ * different shapes overlap; the whole batch is ordered on `stream` as one call.
+ * Shape b's volume and counters equal, bit for bit, those of vdm_decode_hier on
+ * that shape alone. No inspection outputs. Requires 1 <= B <= 4096. Batched calls
+ * on one device from several host threads run one after the other. */
+vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* params, int32_t B,
+                                 const void* K, const void* V, int64_t M, float* vol, int64_t vol_elems,
+                                 int64_t* stats, void* ws, size_t ws_bytes, vdm_stream stream);
+
 /* Surface extraction: the stage that follows VAE decoding in a vecset diffusion
  * pipeline (techwalker article on FlashVDM, part 1, the four stages). The pages
  * leave the method open; it is read here as marching cubes at SDF = 0 on the
@@ -291,6 +308,8 @@ size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M);
 size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M);
 size_t vdm_surface_workspace_size(int32_t R);
 size_t vdm_dense_batch_workspace_size(const vdm_decoder* dec, int32_t B, int64_t M);
+size_t vdm_hier_batch_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int32_t B,
+                                     int64_t M);
 
 /* ---------------------------------------------------------------- kernel timing */
 

@@ -34,7 +34,8 @@ EXPORTS = [
     "vdm_embed_queries", "vdm_project_kv", "vdm_decode_dense", "vdm_select_kv", "vdm_decode_hier",
     "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_timing",
     "vdm_timing_read", "vdm_version", "vdm_last_error", "vdm_extract_surface", "vdm_surface_workspace_size",
-    "vdm_decode_dense_batch", "vdm_dense_batch_workspace_size",
+    "vdm_decode_dense_batch", "vdm_dense_batch_workspace_size", "vdm_decode_hier_batch",
+    "vdm_hier_batch_workspace_size",
 ]
 TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "cell_test", "dilate", "mark", "scan",
               "emit", "fill", "surface"]
@@ -115,6 +116,12 @@ _lib.vdm_decode_dense_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries)
 _lib.vdm_decode_dense_batch.restype = _st
 _lib.vdm_dense_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int64]
 _lib.vdm_dense_batch_workspace_size.restype = C.c_size_t
+_lib.vdm_decode_hier_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_void_p,
+                                       C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                       C.c_size_t, C.c_void_p]
+_lib.vdm_decode_hier_batch.restype = _st
+_lib.vdm_hier_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_int64]
+_lib.vdm_hier_batch_workspace_size.restype = C.c_size_t
 _lib.vdm_timing.argtypes = [C.c_int32]
 _lib.vdm_timing.restype = C.c_int
 _lib.vdm_timing_read.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
@@ -398,6 +405,37 @@ def vdm_decode_hier(dec: Decoder, params: _HierParams, K: torch.Tensor, V: torch
     _check(_lib.vdm_decode_hier(dec.ref, C.byref(params), K.data_ptr(), V.data_ptr(), M, vol.data_ptr(),
                                 vol.numel(), _ptr(stats), C.byref(dbg.struct) if dbg is not None else None,
                                 ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def vdm_hier_batch_workspace_size(dec: Decoder, params: _HierParams, B: int, M: int) -> int:
+    n = int(_lib.vdm_hier_batch_workspace_size(dec.ref, C.byref(params), B, M))
+    if n == 0:
+        raise VdmError(VDM_ERR_INVALID_ARG, vdm_last_error())
+    return n
+
+
+def vdm_decode_hier_batch(dec: Decoder, params: _HierParams, K: torch.Tensor, V: torch.Tensor, vol: torch.Tensor,
+                          stats: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                          stream=None) -> None:
+    """K, V [B, M, D] in the decoder dtype, vol [B, (R+1)^3] float32, stats
+    [B, levels * VDM_STAT_FIELDS] int64 or None (see include/vdm.h)."""
+    _dev(K, dec.torch_dtype, "K")
+    _dev(V, dec.torch_dtype, "V")
+    _dev(vol, torch.float32, "vol")
+    if K.dim() != 3 or V.shape != K.shape or vol.dim() != 2 or vol.shape[0] != K.shape[0]:
+        raise ValueError("K, V must be [B, M, D] and vol [B, (R+1)^3]")
+    P = (params.R0 << (params.levels - 1)) + 1
+    if vol.shape[1] != P ** 3:
+        raise ValueError(f"vol rows must hold exactly (R+1)^3 = {P ** 3} values (the batch stride)")
+    B, M = K.shape[0], K.shape[1]
+    if stats is not None:
+        _dev(stats, torch.int64, "stats")
+        if stats.shape != (B, params.levels * STAT_FIELDS):
+            raise ValueError("stats must be [B, levels * STAT_FIELDS]")
+    if ws is None:
+        ws = workspace(vdm_hier_batch_workspace_size(dec, params, B, M), vol.device)
+    _check(_lib.vdm_decode_hier_batch(dec.ref, C.byref(params), B, K.data_ptr(), V.data_ptr(), M, vol.data_ptr(),
+                                      vol.numel(), _ptr(stats), ws.data_ptr(), ws.numel(), _stream(stream)))
 
 
 def vdm_surface_workspace_size(R: int) -> int:

@@ -410,6 +410,95 @@ size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* pa
   return hier_ws(dec, params, M, nullptr, nullptr);
 }
 
+// ------------------------------------------------------------------ batched hierarchical decoding
+// B shapes through the hierarchical pipeline on up to four streams of the device
+// at once: the caller's stream and three side streams forked from it with an event
+// and joined back. The per-level bookkeeping launches of one shape are too small to
+// fill the chip; those of different shapes run side by side. No host
+// synchronisation (the fork and join are stream-ordered events).
+namespace {
+constexpr int HB_SIDE = 3;  // side streams (four with the caller's: HIP's default number of hardware queues)
+constexpr int HB_MAX_DEV = 64;
+struct HierFork {
+  std::mutex mu;  // one batched call per device at a time records and waits on these events
+  bool ready = false;
+  hipStream_t side[HB_SIDE];
+  hipEvent_t fork, join[HB_SIDE];
+};
+HierFork g_fork[HB_MAX_DEV];
+
+vdm_status hier_fork_init(HierFork& f) {
+  if (f.ready) return VDM_OK;
+  for (int i = 0; i < HB_SIDE; ++i) {
+    VDM_HIP(hipStreamCreateWithFlags(&f.side[i], hipStreamNonBlocking), "side stream");
+    VDM_HIP(hipEventCreateWithFlags(&f.join[i], hipEventDisableTiming), "join event");
+  }
+  VDM_HIP(hipEventCreateWithFlags(&f.fork, hipEventDisableTiming), "fork event");
+  f.ready = true;
+  return VDM_OK;
+}
+
+size_t hier_batch_stride(const vdm_decoder* dec, const vdm_hier_params* p, int64_t M) {
+  return (hier_ws(dec, p, M, nullptr, nullptr) + 255) / 256 * 256;
+}
+}  // namespace
+
+size_t vdm_hier_batch_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int32_t B, int64_t M) {
+  if (B < 1 || B > 4096) {
+    fail(VDM_ERR_INVALID_ARG, "B=%d (1..4096)", B);
+    return 0;
+  }
+  if (check_decoder(dec) != VDM_OK || check_hier(dec, params, M) != VDM_OK) return 0;
+  return hier_batch_stride(dec, params, M) * (size_t)B;
+}
+
+vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* p, int32_t B, const void* K,
+                                 const void* V, int64_t M, float* vol, int64_t vol_elems, int64_t* stats, void* ws,
+                                 size_t ws_bytes, vdm_stream stream) {
+  vdm_status st = check_decoder(dec);
+  if (st != VDM_OK) return st;
+  if (B < 1 || B > 4096) return fail(VDM_ERR_INVALID_ARG, "B=%d (1..4096)", B);
+  st = check_hier(dec, p, M);
+  if (st != VDM_OK) return st;
+  const int64_t Pf = ((int64_t)p->R0 << (p->levels - 1)) + 1, P3 = Pf * Pf * Pf;
+  if (!vol || vol_elems / B < P3) return fail(VDM_ERR_INVALID_ARG, "vol needs %d x %lld floats", B, (long long)P3);
+  const size_t kv_bytes = (size_t)M * dec->D * esize(dec->dtype);
+  if (!K || !V || !aligned(K, 16) || !aligned(V, 16) || kv_bytes % 16 != 0 || !aligned(vol, 4))
+    return fail(VDM_ERR_INVALID_ARG, "K, V or vol NULL/misaligned (each shape's K/V must start 16-byte aligned)");
+  const size_t stride = hier_batch_stride(dec, p, M);
+  if (!ws || ws_bytes / (size_t)B < stride || !aligned(ws, 256))
+    return fail(VDM_ERR_WORKSPACE, "workspace needs %d x %zu bytes, 256-aligned (got %zu)", B, stride, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  auto shape = [&](int b, hipStream_t sb) {
+    return vdm_decode_hier(dec, p, (const char*)K + b * kv_bytes, (const char*)V + b * kv_bytes, M, vol + b * P3, P3,
+                           stats ? stats + (int64_t)b * p->levels * VDM_STAT_FIELDS : nullptr, nullptr,
+                           (char*)ws + b * stride, stride, (vdm_stream)sb);
+  };
+  if (B == 1) return shape(0, s);
+  int dev = 0;
+  VDM_HIP(hipGetDevice(&dev), "device query");
+  if (dev < 0 || dev >= HB_MAX_DEV) return fail(VDM_ERR_UNSUPPORTED, "device %d", dev);
+  HierFork& f = g_fork[dev];
+  std::lock_guard<std::mutex> lock(f.mu);
+  st = hier_fork_init(f);
+  if (st != VDM_OK) return st;
+  const int nside = B - 1 < HB_SIDE ? B - 1 : HB_SIDE;
+  VDM_HIP(hipEventRecord(f.fork, s), "fork record");
+  for (int i = 0; i < nside; ++i) VDM_HIP(hipStreamWaitEvent(f.side[i], f.fork, 0), "fork wait");
+  vdm_status first = VDM_OK;
+  for (int b = 0; b < B && first == VDM_OK; ++b) {
+    const int q = b % (nside + 1);
+    first = shape(b, q == 0 ? s : f.side[q - 1]);
+  }
+  // join every side stream, also after an error, so that nothing of this call is
+  // left running unordered with the caller's stream
+  for (int i = 0; i < nside; ++i) {
+    VDM_HIP(hipEventRecord(f.join[i], f.side[i]), "join record");
+    VDM_HIP(hipStreamWaitEvent(s, f.join[i], 0), "join wait");
+  }
+  return first;
+}
+
 // ------------------------------------------------------------------ surface extraction
 static vdm_status check_surface(int32_t R) {
   if (R < 1 || R > 893) return fail(VDM_ERR_INVALID_ARG, "R=%d (1 <= R <= 893)", R);

@@ -202,3 +202,30 @@ def test_batched_decode_argument_checks():
                                       None) == V.VDM_ERR_INVALID_ARG
     assert lib.vdm_decode_dense_batch(C.byref(d), C.byref(q), 4, 0x1000, 0x1000, 3072, 0x1000, 0x1000, need - 1,
                                       None) == V.VDM_ERR_WORKSPACE
+
+
+def test_batched_hier_argument_checks():
+    import shape_vae_decoding_amd as V
+
+    lib = V._lib
+    d = _decoder()
+    p = V.hier_params(R0=75, levels=3)
+    assert lib.vdm_hier_batch_workspace_size(C.byref(d), C.byref(p), 0, 3072) == 0
+    one = lib.vdm_hier_workspace_size(C.byref(d), C.byref(p), 3072)
+    need = lib.vdm_hier_batch_workspace_size(C.byref(d), C.byref(p), 4, 3072)
+    assert need % 4 == 0 and need // 4 >= one and need // 4 % 256 == 0 and need // 4 - one < 256
+    P3 = 301 ** 3
+
+    def call(B=4, K=0x1000, vol_elems=4 * P3, wsb=need, ws=0x1000, params=p):
+        return lib.vdm_decode_hier_batch(C.byref(d), C.byref(params), B, K, 0x1000, 3072, 0x1000, vol_elems, None,
+                                         ws, wsb, None)
+
+    assert call(B=0) == V.VDM_ERR_INVALID_ARG
+    assert call(B=4097) == V.VDM_ERR_INVALID_ARG
+    assert call(K=None) == V.VDM_ERR_INVALID_ARG
+    assert call(K=0x1008) == V.VDM_ERR_INVALID_ARG
+    assert call(vol_elems=4 * P3 - 1) == V.VDM_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == V.VDM_ERR_WORKSPACE
+    assert call(ws=0x1010) == V.VDM_ERR_WORKSPACE
+    bad = V.hier_params(R0=75, levels=7)
+    assert call(params=bad) == V.VDM_ERR_INVALID_ARG

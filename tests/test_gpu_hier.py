@@ -206,3 +206,41 @@ def test_hier_computed_points_equal_dense_decode():
     print(f"[hier] {int(computed.sum())} decoded points equal dense bitwise; {flips} of {int(inh.sum())} "
           f"inherited points have a sign different from dense", flush=True)
     assert flips <= 1e-4 * inh.sum()
+
+
+@pytest.mark.parametrize("kvsel", [False, True])
+def test_hier_batch_equals_single_shape_calls_bitwise(kvsel):
+    # B vecsets through vdm_decode_hier_batch (up to four streams at once, B = 5 wraps
+    # round the streams): each shape's volume and counters equal its own
+    # vdm_decode_hier call bit for bit; shape 0 also passes the lockstep check
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    rng = np.random.default_rng(23)
+    Zs = [w.Z] + [w.Z * np.float32(0.8) + np.float32(0.2) * rng.standard_normal(w.Z.shape).astype(np.float32)
+                  for _ in range(4)]
+    KV = [gpu_kv(dec, w, Z) for Z in Zs]
+    K = torch.stack([k for k, _ in KV]).contiguous()
+    Vv = torch.stack([v for _, v in KV]).contiguous()
+    params = V().hier_params(R0=24, levels=3, tau=2 * 2 / 96, dilation=1,
+                             kvsel=dict(k=32, cap=256) if kvsel else None)
+    B, P3 = len(Zs), 97 ** 3
+    print(f"[hier batch] B={B} kvsel={kvsel} R0=24 levels=3", flush=True)
+    vol = torch.full((B, P3), float("nan"), dtype=torch.float32, device=dev())
+    stats = torch.zeros((B, 3 * V().STAT_FIELDS), dtype=torch.int64, device=dev())
+    V().vdm_decode_hier_batch(dec, params, K, Vv, vol, stats)
+    torch.cuda.synchronize()
+    for b in range(B):
+        one = torch.empty(P3, dtype=torch.float32, device=dev())
+        st = torch.zeros(3 * V().STAT_FIELDS, dtype=torch.int64, device=dev())
+        V().vdm_decode_hier(dec, params, K[b], Vv[b], one, st)
+        torch.cuda.synchronize()
+        assert torch.equal(vol[b], one), b
+        assert torch.equal(stats[b], st), b
+    # the shapes differ (no shape reused another's buffers)
+    assert not torch.equal(vol[0], vol[1])
+    if not kvsel:
+        v0, s0, dbg = run_hier(dec, params, K[0], Vv[0])
+        assert np.array_equal(v0, vol[0].cpu().numpy())
+        od = oracle_decoder(w)
+        od.K, od.V = f64(K[0]), f64(Vv[0])
+        lockstep(params, v0, s0, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=400)
