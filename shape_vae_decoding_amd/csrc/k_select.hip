@@ -18,6 +18,8 @@
 //   output: ascending compaction of the bitmap.
 // Each wave covers 1/8 of the tokens in the passes; partial softmax statistics
 // are merged in a fixed order, so results are reproducible.
+#include <type_traits>
+
 #include "vdm_device.hpp"
 
 namespace vdm {
@@ -29,7 +31,7 @@ constexpr int SEL_GB = 4;                // blocks per workgroup
 constexpr int SEL_BQ = SEL_NP * SEL_GB;  // probe columns of the MFMA tile
 constexpr int SEL_MAXV = 64;             // scores per lane in the search: M <= 64 * 64
 constexpr int SEL_GRID_MAX = 256;        // workgroups (scratch rows are per workgroup)
-constexpr int SEL_LIST = 256;            // per-wave candidate list of the top-k search (LDS)
+constexpr int SEL_LIST = 1024;           // per-wave candidate list of the top-k search (LDS)
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -51,13 +53,16 @@ __device__ __forceinline__ int wave_sum(int v) {
 // first). One wave; `list` is its LDS scratch of SEL_LIST values.
 //
 // The k-th largest value p is the largest threshold with #{u >= p} >= k, built
-// bit by bit. For k <= 64 the smallest of the 64 lane maxima, lo, is a lower
-// bound of p (64 values are >= lo), so only the values >= lo (usually a few times
-// k) take part: they are compacted into `list` and the bit search runs over 4 per
-// lane instead of 64; for every threshold above lo the counts are the same, and
-// below it both exceed k. If more than SEL_LIST values qualify, or k > 64, the
-// search runs over all values. Thresholds are >= 1, so zero entries never count;
-// values are visited in chunks of 16 and a chunk past n is skipped.
+// bit by bit. For k <= 64 the 64th largest of the lanes' two largest values, lo,
+// is a lower bound of p (64 values are >= lo), so only the values >= lo (usually
+// a small multiple of k) take part: they are compacted into `list` and the bit
+// search runs over 4 (or, for a long list, 16) per lane instead of 48-64; for
+// every threshold above lo the counts are the same, and below it both exceed k.
+// If more than SEL_LIST values qualify, or k > 64, the search runs over all
+// values (3-4 times the work: with the smallest lane maximum as the bound and a
+// 256-entry list this path ran for most probes). Thresholds are >= 1, so zero
+// entries never count; values are visited in chunks of 16 and a chunk past n is
+// skipped.
 __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, int k, unsigned* bits,
                                           unsigned* list, int lane) {
   // (every loop is fully unrolled with constant indices, so u stays in registers)
@@ -77,19 +82,25 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
   unsigned p = 0u;
   bool done = false;
   if (k <= 64) {
-    unsigned mx = 0u;
+    // lo = the 64th largest of the 128 values {largest, second largest of each
+    // lane}: at least 64 >= k values are >= lo, and it is tighter than the smallest
+    // lane maximum (which is <= lo)
+    unsigned m1 = 0u, m2 = 0u;
 #pragma unroll
     for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
       if (c0 * 64 < n) {
 #pragma unroll
-        for (int i = c0; i < c0 + CH; ++i) mx = u[i] > mx ? u[i] : mx;
+        for (int i = c0; i < c0 + CH; ++i) {
+          const unsigned x = u[i];
+          m2 = max(m2, min(m1, x));
+          m1 = max(m1, x);
+        }
       }
     }
-    unsigned lo = mx;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const unsigned t = __shfl_xor(lo, o);
-      lo = t < lo ? t : lo;
+    unsigned lo = 0u;
+    for (int b = 31; b >= 0; --b) {
+      const unsigned cand = lo | (1u << b);
+      if (__popcll(__ballot(m1 >= cand)) + __popcll(__ballot(m2 >= cand)) >= 64) lo = cand;
     }
     int mine = 0;
 #pragma unroll
@@ -113,18 +124,25 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      unsigned v[LV];
-#pragma unroll
-      for (int j = 0; j < LV; ++j) v[j] = j * 64 + lane < total ? list[j * 64 + lane] : 0u;
       // (counts by ballot and popcount: a short scalar chain per bit instead of a
-      // cross-lane reduction)
-      for (int b = 31; b >= 0; --b) {
-        const unsigned cand = p | (1u << b);
-        int c = 0;
+      // cross-lane reduction; a short list is searched over its first 4 slots per lane)
+      auto search = [&](auto lv) {
+        constexpr int NV = decltype(lv)::value;
+        unsigned v[NV];
 #pragma unroll
-        for (int j = 0; j < LV; ++j) c += __popcll(__ballot(v[j] >= cand));
-        if (c >= k) p = cand;
-      }
+        for (int j = 0; j < NV; ++j) v[j] = j * 64 + lane < total ? list[j * 64 + lane] : 0u;
+        for (int b = 31; b >= 0; --b) {
+          const unsigned cand = p | (1u << b);
+          int c = 0;
+#pragma unroll
+          for (int j = 0; j < NV; ++j) c += __popcll(__ballot(v[j] >= cand));
+          if (c >= k) p = cand;
+        }
+      };
+      if (total <= 256)
+        search(std::integral_constant<int, 4>());
+      else
+        search(std::integral_constant<int, LV>());
       __builtin_amdgcn_wave_barrier();  // the list is read before the next search writes it
       done = true;
     }
