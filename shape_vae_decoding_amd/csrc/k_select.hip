@@ -81,6 +81,7 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
   };
   unsigned p = 0u;
   bool done = false;
+  int greater = 0;  // number of values > p (fast path)
   if (k <= 64) {
     // lo = the 64th largest of the 128 values {largest, second largest of each
     // lane}: at least 64 >= k values are >= lo, and it is tighter than the smallest
@@ -138,11 +139,13 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
           for (int j = 0; j < NV; ++j) c += __popcll(__ballot(v[j] >= cand));
           if (c >= k) p = cand;
         }
+        // values > p (all of them are in the list: p >= lo)
+        int g = 0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) g += __popcll(__ballot(v[j] > p));
+        return g;
       };
-      if (total <= 256)
-        search(std::integral_constant<int, 4>());
-      else
-        search(std::integral_constant<int, LV>());
+      greater = total <= 256 ? search(std::integral_constant<int, 4>()) : search(std::integral_constant<int, LV>());
       __builtin_amdgcn_wave_barrier();  // the list is read before the next search writes it
       done = true;
     }
@@ -153,7 +156,8 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
       if (count_all(cand) >= k) p = cand;
     }
   }
-  const int need = k - (p == 0xffffffffu ? 0 : count_all(p + 1u));  // copies of p to take, lowest index first
+  // copies of p to take, lowest index first
+  const int need = k - (done ? greater : (p == 0xffffffffu ? 0 : count_all(p + 1u)));
   int taken = 0;
 #pragma unroll
   for (int i = 0; i < SEL_MAXV; ++i) {
