@@ -238,6 +238,11 @@ def test_hier_batch_equals_single_shape_calls_bitwise(kvsel):
         assert torch.equal(stats[b], st), b
     # the shapes differ (no shape reused another's buffers)
     assert not torch.equal(vol[0], vol[1])
+    # a batch of one (the caller's stream only), without counters
+    one = torch.empty((1, P3), dtype=torch.float32, device=dev())
+    V().vdm_decode_hier_batch(dec, params, K[2:3].contiguous(), Vv[2:3].contiguous(), one)
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], vol[2])
     if not kvsel:
         v0, s0, dbg = run_hier(dec, params, K[0], Vv[0])
         assert np.array_equal(v0, vol[0].cpu().numpy())
