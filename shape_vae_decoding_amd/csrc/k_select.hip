@@ -321,10 +321,13 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         float mx = NEG;
         float tt[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          tt[r] = kb * 32 + crow(r, lane) < M ? S[r] * 0.18033688011112042f : NEG;
-          mx = fmaxf(mx, tt[r]);
+        for (int r = 0; r < 16; ++r) tt[r] = S[r] * 0.18033688011112042f;
+        if (kb * 32 + 32 > M) {  // (uniform) the last, partial tile: keys past M do not count
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tt[r] = kb * 32 + crow(r, lane) < M ? tt[r] : NEG;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, tt[r]);
         const float mnew = fmaxf(m[h], mx);
         if (mnew != NEG) {
           float sum = 0.f;
@@ -382,10 +385,11 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
           acc[r] += __builtin_amdgcn_exp2f(S[r] * 0.18033688011112042f - mf[h]) * linv[h];
       }
       if (col < nb * SEL_NP) {
+        const bool full = kb * 32 + 32 <= M;  // (uniform)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = kb * 32 + crow(r, lane);
-          if (j < M) scores[col * Mp + j] = acc[r] * (1.f / H);
+          if (full || j < M) scores[col * Mp + j] = acc[r] * (1.f / H);
         }
       }
     };
