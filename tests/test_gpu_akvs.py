@@ -292,3 +292,22 @@ def test_select_ties_go_to_the_lower_index(repeat):
     if repeat == 1:
         assert np.all(sel_cnt == k) and np.array_equal(sel_idx[:, :k], np.tile(np.arange(k), (len(blocks), 1)))
     print(f"[parity] selection ties (repeat={repeat}): {len(blocks)} blocks exact", flush=True)
+
+
+@pytest.mark.parametrize("M", [1000, 33])
+def test_select_ragged_token_count_full_width(M):
+    # the 4-head, 256-wide decoder with a token count that leaves a partial last key
+    # tile (1000 = 31 tiles + 8 keys; 33 = 1 tile + 1 key): only that tile is masked
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    K, _ = gpu_kv(dec, w)
+    K = K[:M].contiguous()
+    R = 75
+    nb = hv.nblocks(R + 1)
+    blocks = np.sort(np.random.default_rng(M).choice(nb ** 3, 40, replace=False))
+    blocks = np.unique(np.concatenate([blocks, [0, nb ** 3 - 1]]))
+    k = min(64, M)
+    print(f"[select] ragged M={M} k={k}", flush=True)
+    sel_idx, sel_cnt = run_select(dec, w, K, R, blocks, k, 512)
+    assert np.all(sel_cnt >= k) and np.all(sel_cnt <= min(512, M))
+    compare_sets(dec, w, K, R, blocks, k, 512, sel_idx, sel_cnt)
