@@ -249,3 +249,35 @@ def test_hier_batch_equals_single_shape_calls_bitwise(kvsel):
         od = oracle_decoder(w)
         od.K, od.V = f64(K[0]), f64(Vv[0])
         lockstep(params, v0, s0, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=400)
+
+
+def test_hier_batch_fp32_and_timing_across_streams():
+    # the float32 decoder through the batched call (B = 3) equals single calls bit for
+    # bit, and launch timing records every shape's launches although they run on
+    # several streams (levels x B decode launches, B x (levels - 1) fills)
+    w = W.make(0)
+    dec = gpu_decoder(w)
+    rng = np.random.default_rng(29)
+    Zs = [w.Z] + [w.Z * np.float32(0.8) + np.float32(0.2) * rng.standard_normal(w.Z.shape).astype(np.float32)
+                  for _ in range(2)]
+    KV = [gpu_kv(dec, w, Z) for Z in Zs]
+    K = torch.stack([k for k, _ in KV]).contiguous()
+    Vv = torch.stack([v for _, v in KV]).contiguous()
+    params = V().hier_params(R0=8, levels=3, tau=2 * 2 / 32, dilation=1)
+    B, P3 = len(Zs), 33 ** 3
+    print(f"[hier batch] fp32 B={B} R0=8 levels=3", flush=True)
+    vol = torch.empty((B, P3), dtype=torch.float32, device=dev())
+    V().vdm_timing(2)
+    V().vdm_timing(1)
+    V().vdm_decode_hier_batch(dec, params, K, Vv, vol)
+    V().vdm_timing(0)
+    torch.cuda.synchronize()
+    n_dec, ms_dec = V().vdm_timing_read("decode")
+    n_fill, _ = V().vdm_timing_read("fill")
+    V().vdm_timing(2)
+    assert n_dec == 3 * B and n_fill == 2 * B and ms_dec > 0
+    for b in range(B):
+        one = torch.empty(P3, dtype=torch.float32, device=dev())
+        V().vdm_decode_hier(dec, params, K[b], Vv[b], one)
+        torch.cuda.synchronize()
+        assert torch.equal(vol[b], one), b
