@@ -107,15 +107,30 @@ def select(scores: np.ndarray, k: int, cap: int) -> np.ndarray:
     return union
 
 
-def near_tie_tokens(scores: np.ndarray, k: int, rel: float = 1e-4) -> np.ndarray:
-    """Tokens whose score, for some probe, lies within ``rel`` (relative) of
-    that probe's k-th largest score: their membership can flip under a
-    perturbation of that size."""
+def near_tie_tokens(scores: np.ndarray, k: int, cap: Optional[int] = None, rel: float = 1e-4) -> np.ndarray:
+    """Tokens whose membership in the block's set can flip under a relative
+    perturbation ``rel`` of the scores [n_probe, M] (the tie window of the
+    selection):
+
+    * top-k stage: tokens whose score, for some probe, lies within ``rel`` of
+      that probe's k-th largest score;
+    * cap stage (``cap`` given and the union of the probes' top-k sets, as
+      ``select`` forms it, larger than ``cap``): union tokens whose
+      max-over-probes score lies within ``rel`` of the cap-th largest such
+      score, the cutoff of the cap.
+    """
     s = np.asarray(scores, np.float64)
     amb = np.zeros(s.shape[1], bool)
     for row in s:
         kth = np.sort(row)[::-1][k - 1]
         amb |= np.abs(row - kth) <= rel * abs(kth)
+    if cap is not None:
+        s32 = s.astype(np.float32)
+        union = np.unique(np.concatenate([topk_ids(r, k) for r in s32]))
+        if union.size > cap:
+            key = s[:, union].max(axis=0)
+            cut = np.sort(key)[::-1][cap - 1]
+            amb[union[np.abs(key - cut) <= rel * abs(cut)]] = True
     return np.flatnonzero(amb)
 
 

@@ -48,7 +48,7 @@ def compare_sets(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt, block=8, probes
         assert np.all(np.diff(got) > 0) and np.all(sel_idx[r, sel_cnt[r]:] == -1)
         sym = np.setxor1d(ref, got)
         if sym.size:
-            amb = oak.near_tie_tokens(sc, k)
+            amb = oak.near_tie_tokens(sc, k, cap)
             n_amb += sym.size
             assert np.all(np.isin(sym, amb)), (b, sym, got.size, ref.size)
     print(f"[parity] selection R={R} k={k} cap={cap}: {len(blocks)} blocks, {n_amb} near-tie tokens differ",
