@@ -129,7 +129,7 @@ typedef struct {
   int32_t block;            /* block edge in grid points (8) */
   int32_t cap;              /* row stride of sel_idx */
   const int32_t* sel_idx;   /* [rows, cap] ascending token ids (first sel_cnt valid) */
-  const int32_t* sel_cnt;   /* [rows], 1 .. cap */
+  const int32_t* sel_cnt;   /* [rows], 1 .. cap (0 gives a zero attention output) */
   const int32_t* block_row; /* [NB^3] block id -> row of sel_idx, or NULL (row = block id) */
 } vdm_kvsel;
 
@@ -193,7 +193,14 @@ vdm_status vdm_project_kv(const vdm_decoder* dec, const void* Z, int64_t M, void
  * n-th query. sel: NULL = full attention; otherwise queries must be
  * VDM_Q_GRID_LIST entries sorted by blocked key (block id, then row-major inside
  * the block; as vdm_decode_hier produces) and each query attends to its block's
- * token set. Workspace: vdm_dense_workspace_size(dec, M, N, sel != NULL). */
+ * token set. Preconditions with sel: list entries are unique grid points; for
+ * every block holding a query, block_row (or the block id) names a row of
+ * sel_idx / sel_cnt; sel_cnt of that row lies in 1 .. cap. Outside them the
+ * results are defined but not meaningful: an entry outside [0, (R+1)^3) gets
+ * sdf = NaN, a repeated entry is decoded once per occurrence, token ids are
+ * clamped into [0, M), sel_cnt is clamped into [0, cap], and an empty set
+ * (sel_cnt = 0) gives a zero attention output. Workspace:
+ * vdm_dense_workspace_size(dec, M, N, sel != NULL). */
 vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K,
                             const void* V, int64_t M, const vdm_kvsel* sel, float* sdf, void* ws,
                             size_t ws_bytes, vdm_stream stream);

@@ -16,12 +16,17 @@
 // Softmax with a fixed shift: queries are scaled by log2(e)/8 before their
 // rounding, so S holds base-2 logits t. For query q and head h,
 //   B = ||q_h|| * max_j ||k_hj||  >=  |t_j| for every token (Cauchy-Schwarz),
-// and p_j = exp2(t_j + nb), o = sum_j p_j v_j / sum_j p_j with nb = 0 when every
-// query of the wave has B <= 64 (p_j in [2^-64, 2^64]: no overflow, no
-// underflow) and nb = 64 - B otherwise. The softmax is shift-invariant, so this
-// equals the max-subtracted definition in exact arithmetic. No running maximum,
-// no rescaling of O. The row sum is accumulated from the bf16-rounded p_j (dot2
-// with ones), the same values the P.V product uses.
+// and p_j = exp2(t_j + nb), o = sum_j p_j v_j / sum_j p_j. When every query of
+// the wave has B <= 64, nb = 0 (p_j in [2^-64, 2^64]: no overflow, no
+// underflow). Otherwise the wave first takes each query's true maximum logit
+// t_max over the tokens (a pass of the same S products, so the same values) and
+// uses nb = 64 - t_max: p_j <= 2^64 and the largest p_j is 2^64, so the row sum
+// cannot vanish however loose B is (a key with a large component that no query
+// sees, e.g. outside the span of the head's Wq rows, makes B large without
+// raising any logit). The softmax is shift-invariant, so both equal the
+// max-subtracted definition in exact arithmetic. No running maximum in the main
+// pass, no rescaling of O. The row sum is accumulated from the bf16-rounded p_j
+// (dot2 with ones), the same values the P.V product uses.
 //
 // Dense mode: each wave streams its head's pre-packed K and V^T operand runs
 // straight from L2 into registers (no LDS, no barriers in the token loop), in a
@@ -478,11 +483,12 @@ __device__ __forceinline__ void pipe_iter(const uint4 (&k_next)[C::RUN_U4], cons
   }
 }
 
-// Softmax shift. With |t| <= B for every base-2 logit t of a query (B from
-// Cauchy-Schwarz), p = exp2(t + nb) with nb = SHIFT_FREE_MAX - B lies in
-// [2^(64 - 2B), 2^64]: no overflow, and sums of up to 2^31 products p v stay far
-// inside the fp32 range. When B <= 64 for every query of a wave, nb = 0 is just as
-// safe (p in [2^-64, 2^64]) and the wave skips the addition.
+// Softmax shift. When B <= 64 bounds every base-2 logit of every query of a wave
+// (B from Cauchy-Schwarz), p = exp2(t) lies in [2^-64, 2^64] and the wave skips
+// the shift. Otherwise p = exp2(t + nb) with nb = SHIFT_FREE_MAX - t_max, t_max
+// the query's largest logit (max_logits): p <= 2^64 with equality at the maximum,
+// so no overflow, no vanishing row sum, and sums of up to 2^31 products p v stay
+// far inside the fp32 range.
 constexpr float SHIFT_FREE_MAX = 64.f;
 
 template <int N>
@@ -491,6 +497,72 @@ __device__ __forceinline__ bool any_below(const float (&x)[N], float lim) {
 #pragma unroll
   for (int i = 0; i < N; ++i) r = r || x[i] < lim;
   return r;
+}
+
+// m[qb] = max(m[qb], logits of the valid keys (index < nkeys) of one S^T block).
+template <typename C>
+__device__ __forceinline__ void block_max(const f32x16 (&S)[C::QB], int key0, int nkeys, int lane,
+                                          float (&m)[C::QB]) {
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (key0 + crow(r, lane) < nkeys) m[qb] = fmaxf(m[qb], S[qb][r]);
+}
+
+// nb[qb] = SHIFT_FREE_MAX - (largest logit of this lane's query over the tokens),
+// from the S^T products of every tile (the values the attention pass recomputes
+// bit for bit). kfrags(t, kf) fetches this wave's K_h fragments of tile t; the
+// next tile's are fetched while the current one is multiplied.
+template <typename C, typename KF>
+__device__ __forceinline__ void max_logits(KF&& kfrags, int nkeys, int lane,
+                                           const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
+                                           float (&nb)[C::QB]) {
+  using Frag = typename Mma<typename C::T>::frag;
+  const int nkt = (nkeys + C::KT - 1) / C::KT;
+  float m[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) m[qb] = -__builtin_inff();
+  Frag kf[C::KSTEPS], kn[C::KSTEPS];
+  kfrags(0, kf);
+  for (int kt = 0; kt < nkt; ++kt) {
+    kfrags(kt + 1 < nkt ? kt + 1 : kt, kn);
+    f32x16 S[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) S[qb] = s_block<C>(kf, qf[qb]);
+    block_max<C>(S, kt * C::KT, nkeys, lane, m);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = kn[ks];
+  }
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) nb[qb] = SHIFT_FREE_MAX - fmaxf(m[qb], __shfl_xor(m[qb], 32));
+}
+
+// This wave's K_h fragments of packed tile t (dense mode).
+template <typename C>
+__device__ __forceinline__ void packed_kfrags(__amdgpu_buffer_rsrc_t Kg, int t, int hw, int lane,
+                                              typename Mma<typename C::T>::frag (&kf)[C::KSTEPS]) {
+  using Frag = typename Mma<typename C::T>::frag;
+  uint4 r[C::RUN_U4];
+  load_run<C>(Kg, t, hw, lane, r);
+  const Frag* kp = reinterpret_cast<const Frag*>(r);
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = kp[ks];
+}
+
+// This wave's K_h fragments of tile t of a selected token set, read straight from
+// K [M][D]: lane l takes row sel[32t + l % 32] (the last token past the set's
+// end; those keys are masked by block_max).
+template <typename C>
+__device__ __forceinline__ void gathered_kfrags(const typename C::T* __restrict__ Kg, const int32_t* sel, int nkeys,
+                                                int M, int t, int hw, int lane,
+                                                typename Mma<typename C::T>::frag (&kf)[C::KSTEPS]) {
+  using MM = Mma<typename C::T>;
+  const int row = tok_clamp(sel[min(t * C::KT + (lane & 31), nkeys - 1)], M);
+  const typename C::T* p = Kg + (int64_t)row * C::D + 64 * hw + MM::KW * (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks)
+    kf[ks] = *reinterpret_cast<const typename MM::frag*>(p + ks * MM::KS);
 }
 
 // Dense attention of this wave's QB query blocks over all M tokens: the
@@ -920,9 +992,20 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       l_run[qb] = 0.f;
     }
 
-    // logits of every query of this wave within +-SHIFT_FREE_MAX: no shift
+    // logits of every query of this wave within +-SHIFT_FREE_MAX: no shift;
+    // otherwise the shift comes from each query's largest logit
     const bool shift = __builtin_amdgcn_ballot_w64(any_below(nb, 0.f)) != 0;
     const bool active = qg * C::QW < q1 - q0;  // this wave has queries in the tile
+    if (shift && active && nkeys > 0) {
+      if constexpr (!GATHER) {
+        const int64_t packed_bytes = (int64_t)((nkeys + C::KT - 1) / C::KT) * C::KT * C::D * C::SZ;
+        const __amdgpu_buffer_rsrc_t Kb = buffer_of((const char*)A.Kp + shape * A.kv_stride, packed_bytes);
+        max_logits<C>([&](int t, Frag(&kf)[KS]) { packed_kfrags<C>(Kb, t, hw, lane, kf); }, nkeys, lane, qf, nb);
+      } else {
+        max_logits<C>([&](int t, Frag(&kf)[KS]) { gathered_kfrags<C>(Kg, sel, nkeys, A.M, t, hw, lane, kf); },
+                      nkeys, lane, qf, nb);
+      }
+    }
     if constexpr (!GATHER) {
       if (!active) {
         // (every query of this wave lies past the tile's end: nothing to attend)
@@ -952,7 +1035,9 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     T* Ob = reinterpret_cast<T*>(lds + C::OBUF);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
-      const float inv = 1.f / (l_run[qb] + __shfl_xor(l_run[qb], 32));
+      // (an empty token set, sel_cnt = 0, has l = 0 and gives o = 0)
+      const float lsum = l_run[qb] + __shfl_xor(l_run[qb], 32);
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         O[db][qb] *= inv;

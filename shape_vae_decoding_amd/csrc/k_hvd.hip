@@ -613,27 +613,33 @@ hipError_t launch_bits_to_bytes(const uint64_t* m, int n, int NB, uint8_t* out, 
 
 // ------------------------------------------------------------------ work items from a query list
 // For a grid-list decode with per-block token sets: every maximal run of list
-// entries in one block (at most block^3 entries are scanned) is cut into chunks
-// of at most bq queries; n_items counts them (the order of items does not affect
-// any result, each query's value depends only on its own block's token set).
+// entries in one block is cut into chunks of at most bq queries; n_items counts
+// them (the order of items does not affect any result, each query's value depends
+// only on its own block's token set). A run of a valid list (unique entries) holds
+// at most block^3 entries. An entry outside [0, (R+1)^3) belongs to no block: it
+// gets no item, ends the run it interrupts, and its output is set to NaN here.
 __global__ void items_from_list_kernel(const int32_t* __restrict__ list, int64_t N, int R, int block,
                                        const int32_t* __restrict__ block_row, int bq, Item* __restrict__ items,
-                                       int32_t* n_items) {
+                                       int32_t* n_items, float* __restrict__ out) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= N) return;
   const int64_t P = R + 1;
   const int NB = (R + block) / block;
-  auto blk = [&](int64_t lin) -> int64_t {
+  auto blk = [&](int64_t lin) -> int64_t {  // -1: not a grid point
+    if (lin < 0 || lin >= P * P * P) return -1;
     const int i = (int)(lin / (P * P));
     const int64_t r = lin - (int64_t)i * P * P;
     const int j = (int)(r / P), k = (int)(r - (int64_t)j * P);
     return ((int64_t)(i / block) * NB + j / block) * NB + k / block;
   };
   const int64_t b = blk(list[q]);
+  if (b < 0) {
+    out[q] = __builtin_nanf("");
+    return;
+  }
   if (q > 0 && blk(list[q - 1]) == b) return;
-  const int64_t lim = (int64_t)block * block * block;
   int64_t e = q + 1;
-  while (e < N && e - q < lim && blk(list[e]) == b) ++e;
+  while (e < N && blk(list[e]) == b) ++e;
   const int nch = (int)((e - q + bq - 1) / bq);
   const int at = atomicAdd(n_items, nch);
   const int row = block_row ? block_row[b] : (int)b;
@@ -644,9 +650,9 @@ __global__ void items_from_list_kernel(const int32_t* __restrict__ list, int64_t
 }
 
 hipError_t launch_items_from_list(const int32_t* list, int64_t N, int R, int block, const int32_t* block_row, int bq,
-                                  Item* items, int32_t* n_items, hipStream_t s) {
+                                  Item* items, int32_t* n_items, float* out, hipStream_t s) {
   hipLaunchKernelGGL(items_from_list_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, list, N, R, block,
-                     block_row, bq, items, n_items);
+                     block_row, bq, items, n_items, out);
   return hipGetLastError();
 }
 

@@ -558,8 +558,11 @@ vdm_status vdm_project_kv(const vdm_decoder* dec, const void* Z, int64_t M, void
   return VDM_OK;
 }
 
-vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V, int64_t M,
-                            const vdm_kvsel* sel, float* sdf, void* ws, size_t ws_bytes, vdm_stream stream) {
+// Checks shared by the dense decode calls (decoder, queries, K/V, output).
+// *done = true when there is nothing to do (N = 0).
+static vdm_status check_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V, int64_t M,
+                              const float* sdf, bool* done) {
+  *done = false;
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;
   if (!q) return fail(VDM_ERR_INVALID_ARG, "queries is NULL");
@@ -571,13 +574,50 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
     if (q->mode == VDM_Q_GRID && q->N != P * P * P)
       return fail(VDM_ERR_INVALID_ARG, "grid mode needs N=(R+1)^3=%lld (got %lld)", (long long)(P * P * P), (long long)q->N);
   }
-  if (q->N == 0) return VDM_OK;
+  if (q->N == 0) {
+    *done = true;
+    return VDM_OK;
+  }
   if (M < 1 || M >= (1ll << 31) / dec->D) return fail(VDM_ERR_INVALID_ARG, "M=%lld", (long long)M);
   if (!K || !V || !sdf) return fail(VDM_ERR_INVALID_ARG, "K, V or sdf is NULL");
   if (!aligned(K, 16) || !aligned(V, 16) || !aligned(sdf, 4)) return fail(VDM_ERR_INVALID_ARG, "misaligned K, V or sdf");
   if (q->mode == VDM_Q_POINTS && (!q->xyz || !aligned(q->xyz, 4))) return fail(VDM_ERR_INVALID_ARG, "xyz NULL or misaligned");
   if (q->mode == VDM_Q_GRID_LIST && (!q->list || !aligned(q->list, 4)))
     return fail(VDM_ERR_INVALID_ARG, "list NULL or misaligned");
+  return VDM_OK;
+}
+
+// Full-attention decode over a carved dense workspace: key norms, packed
+// weights, packed K/V, then the decode launch. timed: record the decode launch
+// for vdm_timing.
+static vdm_status dense_full(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V, int64_t M,
+                             float* sdf, const DenseWs& w, hipStream_t s, bool timed) {
+  DecodeArgs a = base_args(dec);
+  a.qs = QuerySrc{q->mode, q->R, q->xyz, q->list, 0};
+  a.N = q->N;
+  a.out = sdf;
+  a.scatter = 0;
+  a.kmax = w.kmax;
+  VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
+  VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
+  VDM_HIP(pack_weights(dec, w.Wp, a, s), "weight packing launch");
+  VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
+  a.Kp = w.Kp;
+  a.Vt = w.Vt;
+  a.M = (int)M;
+  a.n_tiles = (q->N + decode_tile_queries(dec->dtype, dec->D) - 1) / decode_tile_queries(dec->dtype, dec->D);
+  if (timed)
+    VDM_HIP_T(VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, false, a, s), "decode launch");
+  else
+    VDM_HIP(launch_decode(dec->dtype, dec->D, false, a, s), "decode launch");
+  return VDM_OK;
+}
+
+vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V, int64_t M,
+                            const vdm_kvsel* sel, float* sdf, void* ws, size_t ws_bytes, vdm_stream stream) {
+  bool done = false;
+  vdm_status st = check_dense(dec, q, K, V, M, sdf, &done);
+  if (st != VDM_OK || done) return st;
   if (sel) {
     if (q->mode != VDM_Q_GRID_LIST) return fail(VDM_ERR_INVALID_ARG, "token selection needs grid-list queries");
     if (sel->block < 1 || sel->cap < 1 || !sel->sel_idx || !sel->sel_cnt)
@@ -590,26 +630,20 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
   dense_ws(dec, M, q->N, sel != nullptr, ws, &w);
   (void)hipGetLastError();
   hipStream_t s = (hipStream_t)stream;
-  DecodeArgs a = base_args(dec);
-  a.qs = QuerySrc{q->mode, q->R, q->xyz, q->list, 0};
-  a.N = q->N;
-  a.out = sdf;
-  a.scatter = 0;
-  a.kmax = w.kmax;
-  VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
-  VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
-  VDM_HIP(pack_weights(dec, w.Wp, a, s), "weight packing launch");
-  if (!sel) {
-    VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
-    a.Kp = w.Kp;
-    a.Vt = w.Vt;
-    a.M = (int)M;
-    a.n_tiles = (q->N + decode_tile_queries(dec->dtype, dec->D) - 1) / decode_tile_queries(dec->dtype, dec->D);
-    VDM_HIP_T(VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, false, a, s), "decode launch");
-  } else {
+  if (!sel) return dense_full(dec, q, K, V, M, sdf, w, s, true);
+  {
+    DecodeArgs a = base_args(dec);
+    a.qs = QuerySrc{q->mode, q->R, q->xyz, q->list, 0};
+    a.N = q->N;
+    a.out = sdf;
+    a.scatter = 0;
+    a.kmax = w.kmax;
+    VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
+    VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
+    VDM_HIP(pack_weights(dec, w.Wp, a, s), "weight packing launch");
     const int bq = decode_tile_queries(dec->dtype, dec->D);
     VDM_HIP(launch_zero(w.n_items, 256, s), "zero launch");
-    VDM_HIP(launch_items_from_list(q->list, q->N, q->R, sel->block, sel->block_row, bq, w.items, w.n_items, s),
+    VDM_HIP(launch_items_from_list(q->list, q->N, q->R, sel->block, sel->block_row, bq, w.items, w.n_items, sdf, s),
             "items launch");
     a.Kp = K;
     a.Vt = V;

@@ -33,6 +33,6 @@ hipError_t launch_emit(const uint64_t* newmask, const int32_t* counts, const int
 hipError_t launch_fill(const float* prev, int Pp, float* next, int Pn, hipStream_t s);
 hipError_t launch_bits_to_bytes(const uint64_t* m, int n, int NB, uint8_t* out, hipStream_t s);
 hipError_t launch_items_from_list(const int32_t* list, int64_t N, int R, int block, const int32_t* block_row, int bq,
-                                  Item* items, int32_t* n_items, hipStream_t s);
+                                  Item* items, int32_t* n_items, float* out, hipStream_t s);
 
 }  // namespace vdm

@@ -10,6 +10,7 @@ from oracle import decoder as odec
 
 TOL_BF16 = 2e-3  # max |dSDF| for bf16 decoders
 TOL_F32 = 1e-5   # max |dSDF| for fp32 decoders
+DECODE_TILE = 128  # queries per decode work item, for every supported decoder
 
 
 def dev():
@@ -70,3 +71,10 @@ def bf16_close(g: np.ndarray, r: np.ndarray, abs_terms: np.ndarray, n_terms: int
 
 def report(name, err, tol):
     print(f"[parity] {name}: max|d| = {err:.3e} (tol {tol:.1e})", flush=True)
+
+
+def tile_sample(n, bq):
+    """One index in each bq-query tile of [0, n): tile t takes lane (37 t) mod bq,
+    the last tile its last query if that lane lies past n."""
+    t = np.arange(-(-n // bq), dtype=np.int64)
+    return np.minimum(bq * t + (37 * t) % bq, n - 1)

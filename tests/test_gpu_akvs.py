@@ -14,7 +14,8 @@ import vdm_workloads as W
 from oracle import akvs as oak
 from oracle import decoder as odec
 from oracle import hvd as hv
-from tests.helpers import TOL_BF16, dev, f64, gpu_decoder, gpu_kv, oracle_decoder, report, tdtype
+from tests.helpers import (DECODE_TILE, TOL_BF16, dev, f64, gpu_decoder, gpu_kv, oracle_decoder, report, tdtype,
+                           tile_sample)
 
 pytestmark = pytest.mark.gpu
 
@@ -206,16 +207,22 @@ def test_hier_with_selection_full_workload(probes):
         pick = np.sort(rng.choice(nocc, min(nocc, 40), replace=False))
         compare_sets(dec, w, K, R, blocks[pick], kv["k"], kv["cap"], idx[pick], cnt[pick], probes=probes,
                      seed=seed + R)
-        # decoded values with each block's selected tokens (identical inputs)
+        # decoded values with each block's selected tokens (identical inputs): one
+        # point of every work item (an occupied block's queries, in list order, cut
+        # into DECODE_TILE-query items), the lane offset rotating with the item
         volL = d["vol"].cpu().numpy()
         blk = hv.block_of(lst, R + 1)
-        worst = 0.0
-        for r in pick[:15]:
-            m = lst[blk == blocks[r]][:30]
+        starts = np.searchsorted(blk, blocks)
+        ends = np.searchsorted(blk, blocks, side="right")
+        worst, n_items = 0.0, 0
+        for r in range(nocc):
+            m = lst[starts[r]:ends[r]][tile_sample(ends[r] - starts[r], DECODE_TILE)]
+            n_items += m.size
             toks = idx[r, : cnt[r]]
             ref = od.sdf(odec.grid_points(R, m), Kh[toks], Vh[toks])
             worst = max(worst, np.abs(volL[m].astype(np.float64) - ref).max())
-        report(f"selection level {L}: decoded points vs restricted attention", worst, TOL_BF16)
+        assert n_items == s["items"]
+        report(f"selection level {L}: one point per work item ({n_items}) vs restricted attention", worst, TOL_BF16)
         assert worst <= TOL_BF16
     # quality against dense decoding (reported, as on the pages: not a parity bound)
     comp = np.zeros(301 ** 3, bool)
@@ -311,3 +318,85 @@ def test_select_ragged_token_count_full_width(M):
     sel_idx, sel_cnt = run_select(dec, w, K, R, blocks, k, 512)
     assert np.all(sel_cnt >= k) and np.all(sel_cnt <= min(512, M))
     compare_sets(dec, w, K, R, blocks, k, 512, sel_idx, sel_cnt)
+
+
+def test_gathered_decode_key_outside_query_span():
+    # One key with a large component outside every head's query span: its norm
+    # sets the softmax bound of every block whose set holds it, far above any
+    # logit (see test_gpu_dense.py::test_dense_key_outside_query_span). The
+    # gathered decode must stay finite and match attention restricted to each
+    # block's set on the same K.
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    R = 30
+    nb = hv.nblocks(R + 1)
+    sel_idx = torch.empty((nb ** 3, 512), dtype=torch.int32, device=dev())
+    sel_cnt = torch.empty(nb ** 3, dtype=torch.int32, device=dev())
+    # the token: the first of block 0's set (its logits barely move, so it stays selected)
+    V().vdm_select_kv(dec, R, 8, 64, 512, K, None, sel_idx, sel_cnt)
+    tok = int(sel_idx[0, 0].item())
+    K2 = torch.from_numpy(W.with_unseen_key(f64(K), w.weights["Wq"], w.H, tok, 400.0)).to(dev()).to(tdtype(w))
+    V().vdm_select_kv(dec, R, 8, 64, 512, K2, None, sel_idx, sel_cnt)
+    lst = hv.blocked_order(np.ones((R + 1,) * 3, bool)).astype(np.int32)
+    out = torch.empty(lst.size, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_list(R, torch.from_numpy(lst).to(dev())), K2, Vv, out,
+                         sel=V().kvsel(8, 512, sel_idx, sel_cnt))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    si, sc = sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
+    od = oracle_decoder(w)
+    Kh, Vh = f64(K2), f64(Vv)
+    blk = hv.block_of(lst, R + 1)
+    # blocks whose set holds the token and blocks whose set does not
+    has7 = np.array([tok in si[b, : sc[b]] for b in range(nb ** 3)])
+    assert has7.any()
+    worst = 0.0
+    rng = np.random.default_rng(6)
+    for b in np.concatenate([rng.choice(np.flatnonzero(has7), min(10, has7.sum()), replace=False),
+                             rng.choice(np.flatnonzero(~has7), min(4, (~has7).sum()), replace=False)]):
+        m = np.nonzero(blk == b)[0][:40]
+        toks = si[b, : sc[b]]
+        ref = od.sdf(odec.grid_points(R, lst[m]), Kh[toks], Vh[toks])
+        worst = max(worst, np.abs(out[m].astype(np.float64) - ref).max())
+    report(f"gathered decode, key outside the query span ({int(has7.sum())} sets hold it)", worst, TOL_BF16)
+    assert worst <= TOL_BF16
+
+
+def test_gathered_decode_list_outside_preconditions():
+    # Lists outside the documented preconditions stay defined: an entry outside
+    # the grid gets NaN and no work item, a run of one block longer than block^3
+    # (repeated entries) is decoded in full, each copy equal to the point's value
+    # in a valid list, and an empty token set gives a finite value.
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    R = 30
+    P = R + 1
+    nb = hv.nblocks(P)
+    sel_idx = torch.empty((nb ** 3, 512), dtype=torch.int32, device=dev())
+    sel_cnt = torch.empty(nb ** 3, dtype=torch.int32, device=dev())
+    V().vdm_select_kv(dec, R, 8, 64, 512, K, None, sel_idx, sel_cnt)
+    valid = hv.blocked_order(np.ones((P,) * 3, bool)).astype(np.int32)
+    ref = torch.empty(valid.size, dtype=torch.float32, device=dev())
+    sel = V().kvsel(8, 512, sel_idx, sel_cnt)
+    V().vdm_decode_dense(dec, V().queries_list(R, torch.from_numpy(valid).to(dev())), K, Vv, ref, sel=sel)
+    p0 = int(valid[3])  # a point of block 0
+    lst = np.concatenate([valid[:100], [-5, P ** 3 + 3], np.full(700, p0), valid[100:300]]).astype(np.int32)
+    out = torch.zeros(lst.size, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_list(R, torch.from_numpy(lst).to(dev())), K, Vv, out, sel=sel)
+    # an empty set for block 0
+    cnt0 = sel_cnt.clone()
+    cnt0[0] = 0
+    out0 = torch.zeros(64, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_list(R, torch.from_numpy(valid[:64].copy()).to(dev())), K, Vv, out0,
+                         sel=V().kvsel(8, 512, sel_idx, cnt0))
+    torch.cuda.synchronize()
+    out, ref, out0 = out.cpu().numpy(), ref.cpu().numpy(), out0.cpu().numpy()
+    assert np.isnan(out[100]) and np.isnan(out[101])
+    assert np.array_equal(out[:100], ref[:100])
+    assert np.array_equal(out[102:802], np.full(700, ref[3], np.float32))
+    assert np.array_equal(out[802:], ref[100:300])
+    assert np.all(np.isfinite(out0))
+    print("[guard] out-of-grid entries NaN, 700 repeated entries decoded, empty set finite", flush=True)

@@ -10,7 +10,7 @@ import torch
 import vdm_workloads as W
 from oracle import decoder as odec
 from oracle.bf16 import round_bf16
-from tests.helpers import (TOL_BF16, TOL_F32, bf16_close, dev, f64, gpu_decoder, gpu_kv, oracle_decoder,
+from tests.helpers import (DECODE_TILE, TOL_BF16, TOL_F32, bf16_close, tile_sample, dev, f64, gpu_decoder, gpu_kv, oracle_decoder,
                            report, tdtype)
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +22,7 @@ def V():
     return mod
 
 
-@pytest.mark.parametrize("cid", [0, 1])
+@pytest.mark.parametrize("cid", [0, 1, 4])
 def test_kv_projection(cid):
     w = W.make(cid)
     dec = gpu_decoder(w)
@@ -193,42 +193,92 @@ def test_token_permutation_invariance():
     assert err <= TOL_BF16
 
 
-def test_dense_full_grid_129_sampled():
-    # the 129^3 dense workload, in the launch configuration the benchmark times
+def test_dense_full_grid_129_one_query_per_tile():
+    # the 129^3 dense workload, in the launch configuration the benchmark times:
+    # one query of every 128-query tile (16,771 tiles; the lane offset rotates
+    # from tile to tile), plus the first 200 points and the last one
     w = W.make(1)
     dec = gpu_decoder(w)
     K, Vv = gpu_kv(dec, w)
     R = w.query["R"]
-    sdf = torch.empty((R + 1) ** 3, dtype=torch.float32, device=dev())
+    n = (R + 1) ** 3
+    sdf = torch.empty(n, dtype=torch.float32, device=dev())
     V().vdm_decode_dense(dec, V().queries_grid(R), K, Vv, sdf)
     torch.cuda.synchronize()
     out = sdf.cpu().numpy()
-    rng = np.random.default_rng(12)
-    lin = np.unique(np.concatenate([rng.integers(0, (R + 1) ** 3, 1500), np.arange(0, 200), [(R + 1) ** 3 - 1]]))
+    bq = DECODE_TILE
+    lin = np.unique(np.concatenate([tile_sample(n, bq), np.arange(0, 200), [n - 1]]))
+    assert np.unique(lin // bq).size == -(-n // bq)
     od = _bf16_identical_inputs(w, K, Vv)
     ref = od.sdf(odec.grid_points(R, lin))
     err = np.abs(out[lin].astype(np.float64) - ref).max()
-    report("129^3 sampled", err, TOL_BF16)
+    report(f"129^3, one query per tile ({lin.size} points)", err, TOL_BF16)
     assert err <= TOL_BF16
     assert np.all(np.isfinite(out))
 
 
-def test_large_token_set_sampled():
-    # the 40,960-token x 200K-query workload, sampled
+def test_large_token_set_one_query_per_tile():
+    # the 40,960-token x 200K-query workload: one query of every 128-query tile
     w = W.make(4)
     dec = gpu_decoder(w)
     K, Vv = gpu_kv(dec, w)
     xyz = w.query["xyz"]
-    sdf = torch.empty(xyz.shape[0], dtype=torch.float32, device=dev())
+    n = xyz.shape[0]
+    sdf = torch.empty(n, dtype=torch.float32, device=dev())
     V().vdm_decode_dense(dec, V().queries_points(torch.from_numpy(xyz).to(dev())), K, Vv, sdf)
     torch.cuda.synchronize()
     out = sdf.cpu().numpy()
-    idx = np.unique(np.random.default_rng(13).integers(0, xyz.shape[0], 300))
+    assert np.all(np.isfinite(out))
+    idx = tile_sample(n, DECODE_TILE)
     od = _bf16_identical_inputs(w, K, Vv)
     ref = od.sdf(xyz[idx], chunk=64)
     err = np.abs(out[idx].astype(np.float64) - ref).max()
-    report("200K x 40960 sampled", err, TOL_BF16)
+    report(f"200K x 40960, one query per tile ({idx.size} points)", err, TOL_BF16)
     assert err <= TOL_BF16
+
+
+def _unseen_key_inputs(w, dec, K, norm=400.0, token=7):
+    """The GPU's K with one token given a large component outside every head's
+    query span (vdm_workloads.with_unseen_key), on the device, and the oracle
+    decoder fed the same K and V."""
+    K2 = W.with_unseen_key(f64(K), w.weights["Wq"], w.H, token, norm, w.dtype)
+    return torch.from_numpy(K2).to(dev()).to(tdtype(w))
+
+
+@pytest.mark.parametrize("cid", [1, 0])
+def test_dense_key_outside_query_span(cid):
+    # One key with a large component that no query sees makes the Cauchy-Schwarz
+    # logit bound B exceed the true maximum logit by more than 213 (base 2) for
+    # every query here (checked below with the oracle's numbers): a softmax
+    # shifted by the bound alone would underflow to an all-zero row sum. The
+    # decode must stay finite and within tolerance of the oracle on the same K.
+    w = W.make(cid)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    K2 = _unseen_key_inputs(w, dec, K)
+    n = 4097 if cid == 1 else 1000  # ragged last tile
+    xyz = W.gen.random_points(300 + cid, n, -1.05, 1.05)
+    od = oracle_decoder(w)
+    od.K, od.V = f64(K2), f64(Vv)
+    q = odec.qproj(odec.embed(xyz), od.W["Wq"], od.dtype) * (np.log2(np.e) / 8)
+    gaps = []
+    for h in range(w.H):
+        c = slice(64 * h, 64 * h + 64)
+        B = 1.00390625 * np.linalg.norm(q[:, c], axis=1) * np.linalg.norm(od.K[:, c], axis=1).max()
+        gaps.append(B - (q[:, c] @ od.K[:, c].T).max(axis=1))
+    gap = np.min(gaps, axis=0)
+    print(f"[unseen key] c{cid}: bound minus max logit, min {gap.min():.1f}, median {np.median(gap):.1f}",
+          flush=True)
+    assert np.mean(gap > 213) > 0.9
+    sdf = torch.empty(n, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_points(torch.from_numpy(xyz).to(dev())), K2, Vv, sdf)
+    torch.cuda.synchronize()
+    out = f64(sdf)
+    assert np.all(np.isfinite(out))
+    tol = TOL_BF16 if w.dtype == "bf16" else TOL_F32
+    err = np.abs(out - od.sdf(xyz)).max()
+    report(f"key outside the query span, c{cid}", err, tol)
+    assert err <= tol
 
 
 def _head_gain_weights(w, gains):

@@ -15,7 +15,8 @@ import torch
 import vdm_workloads as W
 from oracle import decoder as odec
 from oracle import hvd as hv
-from tests.helpers import TOL_BF16, TOL_F32, dev, f64, gpu_decoder, gpu_kv, oracle_decoder, report
+from tests.helpers import (DECODE_TILE, TOL_BF16, TOL_F32, dev, f64, gpu_decoder, gpu_kv, oracle_decoder, report,
+                           tile_sample)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +38,7 @@ def run_hier(dec, params, K, Vv, with_sel=False):
     return vol.cpu().numpy(), V().stats_dict(stats, levels), dbg
 
 
-def lockstep(params, vol, stats, dbg, decode_ref=None, sample=1500, tol=TOL_BF16, bq=128):
+def lockstep(params, vol, stats, dbg, decode_ref=None, sample=1500, tol=TOL_BF16, bq=DECODE_TILE):
     """Check every level's GPU outputs against the oracle steps applied to the
     GPU's own data. decode_ref(R, lin) -> oracle SDF at those grid points."""
     rng = np.random.default_rng(5)
@@ -67,9 +68,13 @@ def lockstep(params, vol, stats, dbg, decode_ref=None, sample=1500, tol=TOL_BF16
         blk = hv.block_of(lst, P)
         ub, cnt = np.unique(blk, return_counts=True)
         assert st["blocks"] == ub.size and st["items"] == int(np.sum((cnt + bq - 1) // bq))
-        # decoded values at the listed points
+        # decoded values at the listed points: a random sample, or (sample="tiles")
+        # one point of every bq-query decode tile of the list
         if decode_ref is not None and n:
-            pick = lst if n <= sample else np.sort(rng.choice(lst, sample, replace=False))
+            if sample == "tiles":
+                pick = np.sort(lst[tile_sample(n, bq)])
+            else:
+                pick = lst if n <= sample else np.sort(rng.choice(lst, sample, replace=False))
             ref = decode_ref(R, pick)
             err = np.abs(vol_L.reshape(-1)[pick].astype(np.float64) - ref).max()
             worst = max(worst, err)
@@ -160,7 +165,7 @@ def test_hier_full_workload_lockstep():
     print(f"[hier] decoded {total} of 301^3 points ({total / 301 ** 3:.2%})", flush=True)
     od = oracle_decoder(w)
     od.K, od.V = f64(K), f64(Vv)
-    lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=600)
+    lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample="tiles")
 
 
 def test_hier_384_target_lockstep():
@@ -175,7 +180,7 @@ def test_hier_384_target_lockstep():
     print(f"[hier] 384: decoded {total} of 385^3 points ({total / 385 ** 3:.2%})", flush=True)
     od = oracle_decoder(w)
     od.K, od.V = f64(K), f64(Vv)
-    lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=300)
+    lockstep(params, vol, stats, dbg, lambda R, lin: od.sdf_grid(R, lin), sample="tiles")
 
 
 def test_hier_computed_points_equal_dense_decode():

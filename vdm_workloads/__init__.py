@@ -21,4 +21,5 @@ from .gen import (  # noqa: F401
     make,
     CONFIG_NAMES,
     round_bf16_values,
+    with_unseen_key,
 )

@@ -295,3 +295,28 @@ def small_decoder(seed: int, D: int, F: int, M: int, dtype: str = "bf16", n_sph:
         weights, Z = _bf16_all(weights, Z)
     return Workload(-1, f"small_D{D}_F{F}_M{M}_{dtype}", dtype, D, D // 64, F, M, weights, Z,
                     prims, 0.05, {"kind": "none"}, src, seed)
+
+
+def unseen_key_directions(Wq: np.ndarray, H: int) -> np.ndarray:
+    """[H, 64] unit vectors, one per head h, orthogonal to every column of the
+    head's query weights Wq[64h:64h+64, :] (a head's queries span at most 51 of
+    its 64 dimensions; the rest is the left null space of those rows). A key
+    component along such a direction changes no logit of an exactly projected
+    query, but raises the key's norm (test input construction)."""
+    Wq = np.asarray(Wq, np.float64)
+    out = np.empty((H, 64))
+    for h in range(H):
+        U, _, _ = np.linalg.svd(Wq[64 * h:64 * h + 64, :])
+        u = U[:, Wq.shape[1]:].sum(axis=1)
+        out[h] = u / np.linalg.norm(u)
+    return out
+
+
+def with_unseen_key(K: np.ndarray, Wq: np.ndarray, H: int, token: int, norm: float,
+                    dtype: str = "bf16") -> np.ndarray:
+    """K [M, 64 H] with ``norm`` times each head's unseen direction added to row
+    ``token`` (rounded to bf16 for bf16 decoders)."""
+    K = np.array(K, np.float64)
+    K[token] += norm * unseen_key_directions(Wq, H).reshape(-1)
+    K = K.astype(np.float32)
+    return round_bf16_values(K) if dtype == "bf16" else K
