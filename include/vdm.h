@@ -205,6 +205,25 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
                             const void* V, int64_t M, const vdm_kvsel* sel, float* sdf, void* ws,
                             size_t ws_bytes, vdm_stream stream);
 
+/* Bytes of the device scratch array that vdm_decode_dense_noalloc uses on each
+ * GPU (48 MiB): enough for the 1024-wide bf16 decoder up to about 47,000 tokens. */
+#define VDM_NOALLOC_SCRATCH_BYTES (48u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): vdm_decode_dense with
+ * full attention (sel = NULL) and no workspace argument. The packed K/V, packed
+ * epilogue weights and key norms live in a library-owned device array of
+ * VDM_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; the call
+ * allocates nothing. It needs vdm_dense_workspace_size(dec, M, N, 0) bytes of
+ * that array and returns VDM_ERR_WORKSPACE (launching nothing) when that exceeds
+ * VDM_NOALLOC_SCRATCH_BYTES. Results equal vdm_decode_dense's bit for bit. Every
+ * call on one GPU shares that GPU's array (the key norms are cleared on each
+ * call; the rest is overwritten): calls that overlap on one GPU, on different
+ * streams or host threads, race and must be ordered by the caller. The first
+ * call on a device looks up the array's address on that device. */
+vdm_status vdm_decode_dense_noalloc(const vdm_decoder* dec, const vdm_queries* q, const void* K,
+                                    const void* V, int64_t M, float* sdf, vdm_stream stream);
+
 /* Dense decoding of a batch of B vecsets (shapes) at the same N query points:
  * one decode launch for the whole batch (the packing of each shape's K/V is one
  * launch per shape). K, V: [B, M, D] in dtype, shape b at byte offset

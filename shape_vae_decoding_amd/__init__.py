@@ -35,7 +35,7 @@ EXPORTS = [
     "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_timing",
     "vdm_timing_read", "vdm_version", "vdm_last_error", "vdm_extract_surface", "vdm_surface_workspace_size",
     "vdm_decode_dense_batch", "vdm_dense_batch_workspace_size", "vdm_decode_hier_batch",
-    "vdm_hier_batch_workspace_size",
+    "vdm_hier_batch_workspace_size", "vdm_decode_dense_noalloc",
 ]
 TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "cell_test", "dilate", "mark", "scan",
               "emit", "fill", "surface"]
@@ -92,6 +92,9 @@ _lib.vdm_project_kv.restype = _st
 _lib.vdm_decode_dense.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_void_p, C.c_void_p, C.c_int64,
                                   C.POINTER(_KvSel), C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.vdm_decode_dense.restype = _st
+_lib.vdm_decode_dense_noalloc.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_void_p, C.c_void_p,
+                                          C.c_int64, C.c_void_p, C.c_void_p]
+_lib.vdm_decode_dense_noalloc.restype = _st
 _lib.vdm_select_kv.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                C.c_uint64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
                                C.c_void_p, C.c_size_t, C.c_void_p]
@@ -331,6 +334,20 @@ def vdm_decode_dense(dec: Decoder, q: Queries, K: torch.Tensor, V: torch.Tensor,
     _check(_lib.vdm_decode_dense(dec.ref, C.byref(q.struct), K.data_ptr(), V.data_ptr(), M,
                                  C.byref(sel.struct) if sel is not None else None, sdf.data_ptr(), ws.data_ptr(),
                                  ws.numel(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def vdm_decode_dense_noalloc(dec: Decoder, q: Queries, K: torch.Tensor, V: torch.Tensor, sdf: torch.Tensor,
+                             stream=None) -> None:
+    """vdm_decode_dense with full attention and no workspace: the library's
+    per-GPU scratch array stands in for it (nothing is allocated)."""
+    _dev(K, dec.torch_dtype, "K")
+    _dev(V, dec.torch_dtype, "V")
+    _dev(sdf, torch.float32, "sdf")
+    _check(_lib.vdm_decode_dense_noalloc(dec.ref, C.byref(q.struct), K.data_ptr(), V.data_ptr(), K.shape[0],
+                                         sdf.data_ptr(), _stream(stream)))
 
 
 PROBES = {"corners": 0, "random": 1}

@@ -613,6 +613,33 @@ static vdm_status dense_full(const vdm_decoder* dec, const vdm_queries* q, const
   return VDM_OK;
 }
 
+// ------------------------------------------------------------------ no-allocation scratch
+// The scratch of vdm_decode_dense_noalloc: one array per GPU, held until the
+// process ends. Host code uses only its device address from hipGetSymbolAddress
+// (per device, taken once with that device current), never the array's name.
+static __device__ __align__(256) char scratch[VDM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NA_MAX_DEV = 64;
+std::mutex g_na_mu;
+void* g_na_ptr[NA_MAX_DEV];
+}  // namespace
+
+static vdm_status noalloc_scratch(void** out) {
+  int dev = 0;
+  VDM_HIP(hipGetDevice(&dev), "device query");
+  if (dev < 0 || dev >= NA_MAX_DEV) return fail(VDM_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> g(g_na_mu);
+  if (!g_na_ptr[dev]) {
+    void* p = nullptr;
+    VDM_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch symbol address");
+    if (!p) return fail(VDM_ERR_HIP, "scratch symbol address is NULL");
+    g_na_ptr[dev] = p;
+  }
+  *out = g_na_ptr[dev];
+  return VDM_OK;
+}
+
 vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V, int64_t M,
                             const vdm_kvsel* sel, float* sdf, void* ws, size_t ws_bytes, vdm_stream stream) {
   bool done = false;
@@ -657,6 +684,24 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
     VDM_HIP_T(VDM_TIME_DECODE_GATHERED, s, launch_decode(dec->dtype, dec->D, true, a, s), "gathered decode launch");
   }
   return VDM_OK;
+}
+
+vdm_status vdm_decode_dense_noalloc(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V,
+                                    int64_t M, float* sdf, vdm_stream stream) {
+  bool done = false;
+  vdm_status st = check_dense(dec, q, K, V, M, sdf, &done);
+  if (st != VDM_OK || done) return st;
+  const size_t need = dense_ws(dec, M, q->N, false, nullptr, nullptr);
+  if (need > (size_t)VDM_NOALLOC_SCRATCH_BYTES)
+    return fail(VDM_ERR_WORKSPACE, "M=%lld needs %zu bytes of scratch; the no-allocation decode holds %zu",
+                (long long)M, need, (size_t)VDM_NOALLOC_SCRATCH_BYTES);
+  void* base = nullptr;
+  st = noalloc_scratch(&base);
+  if (st != VDM_OK) return st;
+  DenseWs w;
+  dense_ws(dec, M, q->N, false, base, &w);
+  (void)hipGetLastError();
+  return dense_full(dec, q, K, V, M, sdf, w, (hipStream_t)stream, false);
 }
 
 size_t vdm_dense_batch_workspace_size(const vdm_decoder* dec, int32_t B, int64_t M) {

@@ -98,6 +98,25 @@ def test_decode_argument_checks():
     assert need >= 2 * 3072 * 256 * 2
 
 
+def test_noalloc_decode_argument_checks():
+    # the no-allocation decode validates before touching a GPU: zero queries are a
+    # no-op, a token count whose scratch exceeds the fixed array is refused
+    import shape_vae_decoding_amd as V
+
+    d = _decoder()
+    lib = V._lib
+    q0 = V._Queries(V.VDM_Q_POINTS, 0, 0, None, None)
+    assert lib.vdm_decode_dense_noalloc(C.byref(d), C.byref(q0), None, None, 1, None, None) == V.VDM_OK
+    q = V._Queries(V.VDM_Q_GRID, 16, 17 ** 3, None, None)
+    assert lib.vdm_decode_dense_noalloc(C.byref(d), C.byref(q), 0x1000, 0x1000, 0, 0x1000, None) == V.VDM_ERR_INVALID_ARG
+    assert lib.vdm_decode_dense_noalloc(C.byref(d), C.byref(q), None, 0x1000, 10, 0x1000, None) == V.VDM_ERR_INVALID_ARG
+    big = 60000  # 2 x 60000 x 256 x 2 bytes of packed K/V alone exceed 48 MiB
+    assert lib.vdm_dense_workspace_size(C.byref(d), big, q.N, 0) > V.NOALLOC_SCRATCH_BYTES
+    assert lib.vdm_decode_dense_noalloc(C.byref(d), C.byref(q), 0x1000, 0x1000, big, 0x1000, None) == V.VDM_ERR_WORKSPACE
+    assert "scratch" in V.vdm_last_error()
+    assert lib.vdm_dense_workspace_size(C.byref(d), 40960, q.N, 0) <= V.NOALLOC_SCRATCH_BYTES
+
+
 def test_select_and_hier_argument_checks():
     import shape_vae_decoding_amd as V
 
