@@ -10,7 +10,10 @@ its two accelerations compute, written from the pages:
   Selection, efficient decoder design);
 * the techwalker article on FlashVDM, parts 2 and 5 (sign test between
   neighbouring voxels, truncated-SDF band, dilation; probe queries per
-  sub-volume).
+  sub-volume);
+* the MSVS-VAE page (kwkr.cn), sections 1.1 and 3.3 (a local decoder: each
+  query fuses the features of its K nearest supports with offset-dependent
+  weights and a mean-pool residual).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The GPU library shares no code with it.
@@ -26,6 +29,8 @@ Modules:
   brute    pure-Python loop versions of all of the above for tiny inputs
   surface  marching cubes at SDF = 0 on the decoded volume (the surface
            extraction stage that follows decoding)
+  local    the local KNN decoder (AVS-Conv): float32 neighbour decision,
+           offset MLP, weighted sum with mean residual, head
 
 Parity status: every function is pinned by a CPU test (closed forms,
 invariants, library routines or brute force on tiny inputs); see the
@@ -34,4 +39,4 @@ weights have no printed values on the pages; they are pinned through the
 brute-force loops and the closed-form special cases.
 """
 
-from . import bf16, decoder, hvd, akvs, brute, surface  # noqa: F401
+from . import bf16, decoder, hvd, akvs, brute, surface, local  # noqa: F401

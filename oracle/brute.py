@@ -235,3 +235,46 @@ def select(sc: List[List[float]], k: int, cap: int) -> List[int]:
         best = {j: max(row[j] for row in s32) for j in union}
         union = sorted(sorted(union, key=lambda j: (-best[j], j))[:cap])
     return union
+
+
+# ---------------------------------------------------------------- local KNN decoder (AVS-Conv)
+
+def local_neighbours(P, x, K: int) -> List[int]:
+    """K nearest supports of point x: float32 squared distances from exact
+    rational arithmetic rounded at each step (difference, square, x + y, + z),
+    sorted as (distance, index) tuples."""
+    def d2(p):
+        dx = [f32(Fraction(float(p[a])) - Fraction(float(x[a]))) for a in range(3)]
+        sq = [f32(Fraction(v) * Fraction(v)) for v in dx]
+        return f32(Fraction(f32(Fraction(sq[0]) + Fraction(sq[1]))) + Fraction(sq[2]))
+
+    keyed = sorted((d2(P[j]), j) for j in range(len(P)))
+    return [j for _, j in keyed[:K]]
+
+
+def local_point(P, Fe, x, W: Dict, K: int, prims, net_scale: float) -> float:
+    """SDF of the local decoder at one point, with explicit loops."""
+    nb = local_neighbours(P, x, K)
+    A, a, B = W["A"], W["a"], W["B"]
+    C = len(Fe[0])
+    Hw = len(a)
+    gelu = lambda u: 0.5 * u * (1.0 + math.erf(u / math.sqrt(2.0)))  # noqa: E731
+    h = [0.0] * C
+    for j in nb:
+        delta = [f32(Fraction(float(P[j][t])) - Fraction(float(x[t]))) for t in range(3)]
+        g = []
+        for m in range(Hw):
+            u = float(a[m])
+            for t in range(3):
+                u += float(A[m][t]) * delta[t]
+            g.append(gelu(u))
+        for c in range(C):
+            wc = 0.0
+            for m in range(Hw):
+                wc += float(B[c][m]) * g[m]
+            h[c] += wc * float(Fe[j][c]) + float(Fe[j][c]) / K
+    W1, W2, wh = W["W1"], W["W2"], W["w_head"]
+    hid = [gelu(sum(float(W1[f][c]) * h[c] for c in range(C))) for f in range(len(W1))]
+    y = [h[c] + sum(float(W2[c][f]) * hid[f] for f in range(len(hid))) for c in range(C)]
+    net = sum(float(wh[c]) * y[c] for c in range(C))
+    return analytic([float(v) for v in x], prims) + f32(net_scale) * net

@@ -3,7 +3,8 @@
 This module builds *data*: decoder weights, latent vecsets, analytic shape
 primitives and query point sets, for the five workloads (tiny fp32 dense,
 dense 129^3 grid, hierarchical 75->150->300, hierarchical with KV
-selection, 40,960-token x 200K-query dense). It holds none of the decoder's
+selection, 40,960-token x 200K-query dense) and for the local KNN decoder
+(AVS-Conv of the MSVS-VAE page) at that 200K x 40,960 shape. It holds none of the decoder's
 arithmetic: no embedding of queries, no projection, no attention, no MLP,
 no SDF evaluation and no voxel selection. Both the oracle (``oracle/``) and
 the GPU path consume what it returns; neither is imported here.
@@ -22,4 +23,7 @@ from .gen import (  # noqa: F401
     CONFIG_NAMES,
     round_bf16_values,
     with_unseen_key,
+    make_local,
+    small_local,
+    LocalWorkload,
 )

@@ -320,3 +320,79 @@ def with_unseen_key(K: np.ndarray, Wq: np.ndarray, H: int, token: int, norm: flo
     K[token] += norm * unseen_key_directions(Wq, H).reshape(-1)
     K = K.astype(np.float32)
     return round_bf16_values(K) if dtype == "bf16" else K
+
+
+# ---------------------------------------------------------------- local KNN decoder workload
+
+_S_LOCAL = 50
+LOCAL_K = 16       # neighbours per query
+LOCAL_HIDDEN = 32  # width of the offset MLP
+LOCAL_OFFSET_SCALE = 0.05  # offsets of this length reach the offset MLP's hidden units at unit scale
+
+
+@dataclasses.dataclass
+class LocalWorkload:
+    """Inputs of the local KNN decoder (AVS-Conv) at the 200K-query x 40,960-token
+    shape: supports (anchor positions and their latent features), offset-MLP and
+    head weights, query points, analytic prior."""
+
+    name: str
+    K: int
+    xyz: np.ndarray       # float32 [M, 3] support positions
+    feats: np.ndarray     # float32 [M, C] support features (bf16 values)
+    weights: Dict[str, np.ndarray]  # A [Hw,3], a [Hw] (float32); B [C,Hw], W1 [F,C], W2 [C,F] (bf16 values); w_head [C]
+    queries: np.ndarray   # float32 [N, 3]
+    prims: List[Prim]
+    net_scale: float
+
+    @property
+    def M(self) -> int:
+        return int(self.xyz.shape[0])
+
+    @property
+    def C(self) -> int:
+        return int(self.feats.shape[1])
+
+    @property
+    def F(self) -> int:
+        return int(self.weights["W1"].shape[0])
+
+
+def _local_weights(rng: np.random.Generator, C: int, Hw: int) -> Dict[str, np.ndarray]:
+    # A ~ N(0, 1/3) / LOCAL_OFFSET_SCALE, a ~ N(0, 1), B ~ N(0, 1/Hw)
+    A = (rng.standard_normal((Hw, 3)) / np.sqrt(3.0) / LOCAL_OFFSET_SCALE).astype(np.float32)
+    a = rng.standard_normal(Hw).astype(np.float32)
+    B = round_bf16_values((rng.standard_normal((C, Hw)) / np.sqrt(Hw)).astype(np.float32))
+    return {"A": A, "a": a, "B": B}
+
+
+def make_local(seed: int = 0, *, M: Optional[int] = None, n_queries: Optional[int] = None) -> LocalWorkload:
+    """The local decoder at the MSVS-VAE page's decode-speed shape: the
+    40,960-token shape's latents as supports at the surface points they were
+    drawn from, the 200,000 query points of that workload, the 1024-wide head
+    of the vecset decoder (W1, W2, w_head) and a fresh offset MLP."""
+    base = make(4, seed, M=M)
+    lw = _local_weights(_rng(seed, _S_LOCAL), base.D, LOCAL_HIDDEN)
+    weights = dict(lw, W1=base.weights["W1"], W2=base.weights["W2"], w_head=base.weights["w_head"])
+    q = base.query["xyz"] if n_queries is None else base.query["xyz"][:n_queries]
+    return LocalWorkload(f"local_knn_{q.shape[0]}q_M{base.M}", LOCAL_K, base.source_points.astype(np.float32),
+                         base.Z, weights, np.ascontiguousarray(q), base.prims, 0.05)
+
+
+def small_local(seed: int, M: int, C: int, F: int, n_queries: int, K: int = LOCAL_K,
+                hidden: int = LOCAL_HIDDEN) -> LocalWorkload:
+    """A scaled-down local decoder with the same recipe (supports on a union of
+    primitives, features = latents of those points, uniform and near-surface
+    queries)."""
+    rng = _rng(seed, 78)
+    prims = _random_prims(rng, 2, 1)
+    src = sample_union_surface(rng, prims, M)
+    Z = round_bf16_values(_latents(rng, src, C))
+    head = _decoder_weights(rng, C, F)
+    lw = _local_weights(rng, C, hidden)
+    weights = dict(lw, W1=round_bf16_values(head["W1"]), W2=round_bf16_values(head["W2"]), w_head=head["w_head"])
+    half = n_queries // 2
+    uni = rng.uniform(-1.0, 1.0, (half, 3))
+    near = sample_union_surface(rng, prims, n_queries - half) + rng.normal(0.0, 0.01, (n_queries - half, 3))
+    q = np.concatenate([uni, near]).astype(np.float32)
+    return LocalWorkload(f"small_local_M{M}_C{C}", K, src.astype(np.float32), Z, weights, q, prims, 0.05)
