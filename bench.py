@@ -218,6 +218,53 @@ def large_token_decode(V, W, dev, reps: int = 5):
             "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
+def local_knn_decode(V, W, dev, reps: int = 5):
+    """The local KNN decoder (AVS-Conv of the MSVS-VAE page) at its speed-test
+    shape: 200,000 queries against 40,960 supports. Returns the call time (HIP
+    events around the call) and each stage's launch time from the library's
+    timing events, with the head's MFMA rate."""
+    import numpy as np
+    import torch
+
+    w = W.make_local()
+    wt = {k: torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev) for k, v in w.weights.items()}
+    for k in ("B", "W1", "W2"):
+        wt[k] = wt[k].to(torch.bfloat16)
+    dec = V.LocalDecoder(wt, w.prims, w.K, w.net_scale)
+    P = torch.from_numpy(np.ascontiguousarray(w.xyz, np.float32)).to(dev)
+    Fe = torch.from_numpy(np.ascontiguousarray(w.feats, np.float32)).to(dev).to(torch.bfloat16)
+    X = torch.from_numpy(np.ascontiguousarray(w.queries, np.float32)).to(dev)
+    N = X.shape[0]
+    sdf = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = V.workspace(V.vdm_local_workspace_size(dec, w.M, N), dev)
+    V.vdm_decode_local(dec, P, Fe, X, sdf, ws=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        V.vdm_decode_local(dec, P, Fe, X, sdf, ws=ws)
+    b.record()
+    torch.cuda.synchronize()
+    call_ms = a.elapsed_time(b) / reps
+    V.vdm_timing(2)
+    V.vdm_timing(1)
+    for _ in range(reps):
+        V.vdm_decode_local(dec, P, Fe, X, sdf, ws=ws)
+    V.vdm_timing(0)
+    stages = {}
+    for kind in ("local_grid", "local_knn", "local_fuse", "local_head"):
+        n, ms = V.vdm_timing_read(kind)
+        stages[kind[6:] + "_ms"] = round(ms / max(n, 1), 4)
+    V.vdm_timing(2)
+    head_flop = 2 * (2 * w.C * w.F + w.C) * N  # W1, W2 and the head per query
+    fuse_flop = 2 * w.K * w.C * 32 * N          # dynamic weights G B^T
+    return {"supports": w.M, "query_points": N, "neighbours": w.K, "call_ms": round(call_ms, 4),
+            "query_points_per_s": round(N / (call_ms / 1e3), 1), "stages": stages,
+            "head_tflops": round(head_flop / (stages["head_ms"] / 1e3) / 1e12, 2),
+            "fuse_mfma_tflops": round(fuse_flop / (stages["fuse_ms"] / 1e3) / 1e12, 2),
+            "vs_dense_200k_x_40960": None}
+
+
 def surface_extraction(V, vol, R: int, dev, reps: int = 10):
     """Marching cubes at SDF = 0 on the hierarchical decode's (R+1)^3 volume
     (outside the timed steps). Launch time from the library's HIP events around
@@ -421,6 +468,9 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, copy 512 MiB device-to-device 3 times (a known-size kernel for "
                          "calibrating the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the warmup and the timed steps and their JSON line, with no work outside them "
+                         "(profiler passes)")
     ap.add_argument("--mask-stress", action="store_true",
                     help="instead of the step: bandwidth of the hierarchical bookkeeping kernels (75->300 and "
                          "150->600), one JSON line")
@@ -574,6 +624,9 @@ def main():
         },
         "roofline": roofline,
     }
+    if args.step_only:
+        print(json.dumps(out), flush=True)
+        return
     # outside the timed steps: surface extraction of the hierarchical volume
     out["breakdown"]["surface_extraction_300cubed"] = surface_extraction(V, vol_h, Pf - 1, dev)
     # outside the timed steps: the pages' 384^3 resolution example (96 -> 192 -> 384, band of two fine widths)
@@ -622,6 +675,9 @@ def main():
         # outside the timed steps (and left out of profiling runs): the large-token
         # workload and the machine's reference figures
         out["breakdown"]["large_tokens_200k_points"] = large_token_decode(V, W, dev)
+        loc = local_knn_decode(V, W, dev)
+        loc["vs_dense_200k_x_40960"] = round(out["breakdown"]["large_tokens_200k_points"]["launch_ms"] / loc["call_ms"], 2)
+        out["breakdown"]["local_knn_200k_points"] = loc
         props = torch.cuda.get_device_properties(0)
         out["breakdown"]["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
                                       "copy_GB_per_s": copy_bandwidth(dev), "hbm_peak_GB_per_s": PEAK_HBM_GBS}
