@@ -328,6 +328,49 @@ vdm_status vdm_extract_surface(const float* vol, int32_t R, const uint8_t* cell_
 
 /* ---------------------------------------------------------------- helpers */
 
+/* ---------------------------------------------------------------- local KNN decoder */
+
+/* A local (K-nearest-neighbour) decoder: the AVS-Conv operator of the MSVS-VAE
+ * page (kwkr.cn), section 1.1, followed by the slim head of the vecset decoder.
+ * For a query x, its K nearest supports j (support positions p_j, features f_j)
+ * give offsets delta_j = p_j - x, dynamic weights w_j = B GELU(A delta_j + a)
+ * (one per feature channel, exact-erf GELU) and the fused feature
+ *   h = (1/K) sum_j w_j * f_j + (1/K) sum_j f_j    (weighted mean + mean-pool residual);
+ * then y = h + W2 GELU(W1 h), net = w_head . y, SDF = analytic(x) + net_scale * net.
+ * Neighbours: the K supports of smallest float32 squared distance
+ * fl(fl(fl(dx*dx) + fl(dy*dy)) + fl(dz*dz)), dx = fl(p_jx - x_x) etc. (no fused
+ * multiply-add), equal distances to the lower support index.
+ * Supported: C = 256, K = 16, hidden = 32, bf16 features and B, W1, W2;
+ * F a multiple of 256 up to 4096. Device pointers, row-major [out, in]. */
+typedef struct {
+  int32_t C;           /* feature width */
+  int32_t F;           /* head MLP width */
+  int32_t K;           /* neighbours per query */
+  int32_t hidden;      /* width of the offset MLP */
+  float net_scale;     /* SDF = analytic + net_scale * net */
+  const float* A;      /* [hidden, 3] float32 */
+  const float* a;      /* [hidden] float32 */
+  const void* B;       /* [C, hidden] bf16 */
+  const void* W1;      /* [F, C] bf16 */
+  const void* W2;      /* [C, F] bf16 */
+  const float* w_head; /* [C] float32 */
+  int32_t n_prims;     /* 1 .. VDM_MAX_PRIMS */
+  vdm_prim prims[VDM_MAX_PRIMS];
+} vdm_local_decoder;
+
+/* SDF of the local decoder at N query points (MSVS-VAE page section 1.1; the
+ * 200K-query batch of its section 3.3). sup_xyz: [M, 3] float32 support
+ * positions; feats: [M, C] bf16 support features; xyz: [N, 3] float32 queries;
+ * sdf: [N] float32. nbr: optional [N, K] int32 output, each query's neighbours
+ * nearest first (NULL: not written). The supports are bucketed into a 32^3 grid
+ * of cells over [-1, 1]^3 (positions outside are bucketed into the border cells
+ * and still found). A query with a NaN coordinate has no neighbours (its nbr
+ * entries are 2^31 - 1) and a NaN SDF. Requires K <= M. Workspace:
+ * vdm_local_workspace_size(dec, M, N). */
+vdm_status vdm_decode_local(const vdm_local_decoder* dec, const float* sup_xyz, const void* feats, int64_t M,
+                            const float* xyz, int64_t N, float* sdf, int32_t* nbr, void* ws, size_t ws_bytes,
+                            vdm_stream stream);
+
 /* Workspace bytes for the calls above (0 with vdm_last_error set on bad args). */
 size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, int32_t with_sel);
 size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M);
@@ -336,6 +379,7 @@ size_t vdm_surface_workspace_size(int32_t R);
 size_t vdm_dense_batch_workspace_size(const vdm_decoder* dec, int32_t B, int64_t M);
 size_t vdm_hier_batch_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int32_t B,
                                      int64_t M);
+size_t vdm_local_workspace_size(const vdm_local_decoder* dec, int64_t M, int64_t N);
 
 /* ---------------------------------------------------------------- kernel timing */
 
@@ -354,6 +398,11 @@ enum {
   VDM_TIME_EMIT,            /* query list, work items and occupied blocks */
   VDM_TIME_FILL,            /* nearest-ancestor fill of the next level's volume */
   VDM_TIME_SURFACE,         /* vdm_extract_surface (all of its launches) */
+  /* vdm_decode_local: */
+  VDM_TIME_LOCAL_GRID,      /* bucketing of the supports into cells (count, scan, scatter) */
+  VDM_TIME_LOCAL_KNN,       /* K nearest supports of every query */
+  VDM_TIME_LOCAL_FUSE,      /* offset MLP, dynamic weights, weighted sum and mean residual */
+  VDM_TIME_LOCAL_HEAD,      /* head MLP, SDF */
   VDM_TIME_KINDS
 };
 

@@ -272,7 +272,7 @@ def local_point(P, Fe, x, W: Dict, K: int, prims, net_scale: float) -> float:
             wc = 0.0
             for m in range(Hw):
                 wc += float(B[c][m]) * g[m]
-            h[c] += wc * float(Fe[j][c]) + float(Fe[j][c]) / K
+            h[c] += (wc * float(Fe[j][c]) + float(Fe[j][c])) / K
     W1, W2, wh = W["W1"], W["W2"], W["w_head"]
     hid = [gelu(sum(float(W1[f][c]) * h[c] for c in range(C))) for f in range(len(W1))]
     y = [h[c] + sum(float(W2[c][f]) * hid[f] for f in range(len(hid))) for c in range(C)]

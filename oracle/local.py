@@ -20,8 +20,9 @@ Readings (the page leaves these open; the plainest reading is taken):
   * offset delta_j = p_j - x (the float32 differences above);
   * dynamic weights w_j = B GELU(A delta_j + a): A [Hw, 3], a [Hw], B [C, Hw],
     exact-erf GELU, one weight per feature channel;
-  * fusion h = sum_j w_j * f_j + (1/K) sum_j f_j over the K neighbours
-    (weighted sum plus the mean-pool residual);
+  * fusion h = (1/K) sum_j w_j * f_j + (1/K) sum_j f_j over the K neighbours
+    (the weighted fusion as a weighted mean, beside the mean-pool residual:
+    h does not grow with K);
   * head (the light network): y = h + W2 GELU(W1 h), net = w_head . y,
     SDF = analytic(x) + net_scale * net -- the slim head of the vecset
     decoder, so the two decoders differ only in how a query gathers its
@@ -73,7 +74,7 @@ def offset_weights(delta: np.ndarray, W: dict) -> np.ndarray:
 
 
 def fuse(P: np.ndarray, Fe: np.ndarray, X: np.ndarray, nbr: np.ndarray, W: dict) -> np.ndarray:
-    """h [N, C] = sum_j w_j * f_j + mean_j f_j over each query's neighbours."""
+    """h [N, C] = mean_j w_j * f_j + mean_j f_j over each query's neighbours."""
     P32 = np.asarray(P, np.float32)
     X32 = np.asarray(X, np.float32)
     Fe = np.asarray(Fe, np.float64)
@@ -81,7 +82,7 @@ def fuse(P: np.ndarray, Fe: np.ndarray, X: np.ndarray, nbr: np.ndarray, W: dict)
     delta = (P32[nbr] - X32[:, None, :]).astype(np.float64)  # float32 differences, [N, K, 3]
     w = offset_weights(delta, W)                             # [N, K, C]
     f = Fe[nbr]                                              # [N, K, C]
-    return (w * f).sum(axis=1) + f.sum(axis=1) / K
+    return (w * f).sum(axis=1) / K + f.sum(axis=1) / K
 
 
 def head(h: np.ndarray, W: dict) -> np.ndarray:

@@ -35,10 +35,10 @@ EXPORTS = [
     "vdm_dense_workspace_size", "vdm_select_workspace_size", "vdm_hier_workspace_size", "vdm_timing",
     "vdm_timing_read", "vdm_version", "vdm_last_error", "vdm_extract_surface", "vdm_surface_workspace_size",
     "vdm_decode_dense_batch", "vdm_dense_batch_workspace_size", "vdm_decode_hier_batch",
-    "vdm_hier_batch_workspace_size", "vdm_decode_dense_noalloc",
+    "vdm_hier_batch_workspace_size", "vdm_decode_dense_noalloc", "vdm_decode_local", "vdm_local_workspace_size",
 ]
 TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "cell_test", "dilate", "mark", "scan",
-              "emit", "fill", "surface"]
+              "emit", "fill", "surface", "local_grid", "local_knn", "local_fuse", "local_head"]
 
 
 class VdmError(RuntimeError):
@@ -74,6 +74,14 @@ class _HierParams(C.Structure):
     _fields_ = [("R0", C.c_int32), ("levels", C.c_int32), ("dilation", C.c_int32), ("tau", C.c_float),
                 ("use_kvsel", C.c_int32), ("block", C.c_int32), ("k", C.c_int32), ("cap", C.c_int32),
                 ("probes", C.c_int32), ("seed", C.c_uint64)]
+
+
+class _LocalDecoder(C.Structure):
+    _fields_ = [
+        ("C", C.c_int32), ("F", C.c_int32), ("K", C.c_int32), ("hidden", C.c_int32), ("net_scale", C.c_float),
+        ("A", C.c_void_p), ("a", C.c_void_p), ("B", C.c_void_p), ("W1", C.c_void_p), ("W2", C.c_void_p),
+        ("w_head", C.c_void_p), ("n_prims", C.c_int32), ("prims", _Prim * MAX_PRIMS),
+    ]
 
 
 _PtrArr = C.c_void_p * MAX_LEVELS
@@ -125,6 +133,11 @@ _lib.vdm_decode_hier_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParam
 _lib.vdm_decode_hier_batch.restype = _st
 _lib.vdm_hier_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_int64]
 _lib.vdm_hier_batch_workspace_size.restype = C.c_size_t
+_lib.vdm_decode_local.argtypes = [C.POINTER(_LocalDecoder), C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                                  C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.vdm_decode_local.restype = _st
+_lib.vdm_local_workspace_size.argtypes = [C.POINTER(_LocalDecoder), C.c_int64, C.c_int64]
+_lib.vdm_local_workspace_size.restype = C.c_size_t
 _lib.vdm_timing.argtypes = [C.c_int32]
 _lib.vdm_timing.restype = C.c_int
 _lib.vdm_timing_read.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
@@ -214,6 +227,64 @@ class Decoder:
     @property
     def ref(self):
         return C.byref(self.struct)
+
+
+class LocalDecoder:
+    """A vdm_local_decoder plus the device tensors it points to.
+
+    weights: A [hidden,3], a [hidden] float32; B [C,hidden], W1 [F,C], W2 [C,F]
+    bf16; w_head [C] float32 (device tensors). K: neighbours per query."""
+
+    def __init__(self, weights: Dict[str, torch.Tensor], prims: Sequence, K: int = 16, net_scale: float = 0.05):
+        self.tensors = {}
+        for k in ("A", "a", "w_head"):
+            self.tensors[k] = _dev(weights[k], torch.float32, k)
+        for k in ("B", "W1", "W2"):
+            self.tensors[k] = _dev(weights[k], torch.bfloat16, k)
+        s = _LocalDecoder()
+        s.C, s.hidden = self.tensors["B"].shape
+        s.F = self.tensors["W1"].shape[0]
+        s.K = int(K)
+        s.net_scale = float(net_scale)
+        for k, t in self.tensors.items():
+            setattr(s, k, t.data_ptr())
+        if len(prims) > MAX_PRIMS:
+            raise ValueError("too many primitives")
+        s.n_prims = len(prims)
+        for i, p in enumerate(prims):
+            s.prims[i].kind = int(p.kind)
+            for c in range(3):
+                s.prims[i].centre[c] = float(p.centre[c])
+                s.prims[i].size[c] = float(p.size[c])
+        self.struct = s
+        self.C, self.F, self.K = s.C, s.F, s.K
+
+    @property
+    def ref(self):
+        return C.byref(self.struct)
+
+
+def vdm_local_workspace_size(dec: LocalDecoder, M: int, N: int) -> int:
+    n = int(_lib.vdm_local_workspace_size(dec.ref, M, N))
+    if n == 0:
+        raise VdmError(VDM_ERR_INVALID_ARG, vdm_last_error())
+    return n
+
+
+def vdm_decode_local(dec: LocalDecoder, sup_xyz: torch.Tensor, feats: torch.Tensor, xyz: torch.Tensor,
+                     sdf: torch.Tensor, nbr: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    _dev(sup_xyz, torch.float32, "sup_xyz")
+    _dev(feats, torch.bfloat16, "feats")
+    _dev(xyz, torch.float32, "xyz")
+    _dev(sdf, torch.float32, "sdf")
+    if nbr is not None:
+        _dev(nbr, torch.int32, "nbr")
+    M, N = sup_xyz.shape[0], xyz.shape[0]
+    if ws is None:
+        ws = workspace(vdm_local_workspace_size(dec, M, N), sdf.device)
+    _check(_lib.vdm_decode_local(dec.ref, sup_xyz.data_ptr(), feats.data_ptr(), M, xyz.data_ptr(), N,
+                                 sdf.data_ptr(), _ptr(nbr), ws.data_ptr(), ws.numel(), _stream(stream)))
 
 
 def workspace(nbytes: int, device=None) -> torch.Tensor:

@@ -1185,6 +1185,130 @@ hipError_t launch_decode(int dtype, int D, bool gathered, const DecodeArgs& a, h
   return gathered ? run<CfgF64, true>(a, s) : run<CfgF64, false>(a, s);
 }
 
+// ---------------------------------------------------------------- head of the local decoder
+// y = h + W2 GELU(W1 h), net = w_head . y, SDF = analytic + net_scale net for
+// fused features h [N][256] (bf16) of the local KNN decoder: the epilogue of
+// decode_kernel with h in place of Wo o, one 128-query tile per workgroup
+// iteration, the weights streamed once per tile.
+template <typename C>
+__global__ __launch_bounds__(C::NT) void local_head_kernel(HeadArgs A) {
+  extern __shared__ __align__(16) char lds[];
+  using T = typename C::T;
+  using MM = Mma<T>;
+  static_assert(C::D == 256 && C::PACKED_W && C::GELU_TABLE && C::CPW == C::CB, "the 256-wide bf16 head");
+  const int tid0 = threadIdx.x, lane0 = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+  const T* __restrict__ W1 = (const T*)A.W1;
+  const T* __restrict__ W2 = (const T*)A.W2;
+  const T* __restrict__ Hg = (const T*)A.h;
+  const float2* gtab = reinterpret_cast<const float2*>(lds + C::GTAB);
+  gelu_table_fill(reinterpret_cast<float2*>(lds + C::GTAB), tid0, C::NT);
+  T* Ab = reinterpret_cast<T*>(lds + C::ABUF);
+  T* Hb = reinterpret_cast<T*>(lds + C::OBUF);
+  float* red = reinterpret_cast<float*>(lds + C::RED);
+  const int64_t n_tiles = (A.N + C::BQ - 1) / C::BQ;
+  constexpr int NCB = C::CB, NCH = C::CPH;
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    int tid = opaque(tid0), lane = opaque(lane0);
+    const int64_t q0 = tile * C::BQ;
+    const int64_t q1 = q0 + C::BQ < A.N ? q0 + C::BQ : A.N;
+    // h rows of the tile into Ab [BQ][DPAD] (rows past the end: zero)
+    constexpr int CPR = C::D * C::SZ / 16;
+    for (int c = tid; c < C::BQ * CPR; c += C::NT) {
+      const int r = c / CPR, e = (c % CPR) * (16 / C::SZ);
+      const uint4 v = q0 + r < q1 ? *reinterpret_cast<const uint4*>(Hg + (q0 + r) * C::D + e) : uint4{0, 0, 0, 0};
+      *reinterpret_cast<uint4*>(Ab + r * C::DPAD + e) = v;
+    }
+    __syncthreads();
+    lane = opaque(lane);
+    const int rb0 = wave * C::RPW, rh0 = wave * C::RPH;
+    // y = h (C layout: rows = channels, columns = queries)
+    f32x16 Y[C::RPW][NCB];
+#pragma unroll
+    for (int r = 0; r < C::RPW; ++r)
+#pragma unroll
+      for (int i = 0; i < NCB; ++i)
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          Y[r][i][k] = (float)Ab[(32 * i + (lane & 31)) * C::DPAD + 32 * (rb0 + r) + crow(k, lane)];
+    for (int f0 = 0; f0 < A.F; f0 += C::FC) {
+      f32x16 Hc[C::RPH][NCH];
+#pragma unroll
+      for (int r = 0; r < C::RPH; ++r)
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) Hc[r][j] = zero16();
+      gemm_rows<T, C::D / MM::KS, C::RPH, NCH, true>(wblock<C>(W1, f0 / 32 + rh0, 0, C::D), C::D, Ab, C::DPAD, 0, Hc,
+                                                     lane);
+#pragma unroll
+      for (int r = 0; r < C::RPH; ++r)
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          gelu_tile<C>(Hc[r][j], gtab);
+          store_ct<T>(Hb + (32 * j) * C::HPAD + 32 * (rh0 + r), C::HPAD, Hc[r][j], lane);
+        }
+      __syncthreads();
+      gemm_rows<T, C::FC / MM::KS, C::RPW, NCB, true>(wblock<C>(W2, rb0, f0 / MM::KS, A.F), A.F, Hb, C::HPAD, 0, Y,
+                                                      lane);
+      __syncthreads();
+    }
+    {
+      float s[NCB];
+#pragma unroll
+      for (int i = 0; i < NCB; ++i) s[i] = 0.f;
+#pragma unroll
+      for (int r = 0; r < C::RPW; ++r) {
+        float w[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) w[k] = A.w_head[32 * (rb0 + r) + crow(k, lane)];
+#pragma unroll
+        for (int i = 0; i < NCB; ++i)
+#pragma unroll
+          for (int k = 0; k < 16; ++k) s[i] += w[k] * Y[r][i][k];
+      }
+#pragma unroll
+      for (int i = 0; i < NCB; ++i) {
+        s[i] += __shfl_xor(s[i], 32);
+        if (lane < 32) red[wave * C::BQ + 32 * i + lane] = s[i];
+      }
+    }
+    __syncthreads();
+    tid = opaque(tid);
+    for (int t = tid; t < C::BQ; t += C::NT) {
+      const int64_t q = q0 + t;
+      if (q < q1) {
+        float net = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) net += red[w * C::BQ + t];
+        const Coords p{A.xyz[3 * q], A.xyz[3 * q + 1], A.xyz[3 * q + 2]};
+        A.out[q] = analytic_sdf(p, A.prims) + A.net_scale * net;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_local_head(const HeadArgs& a, hipStream_t s) {
+  using C = CfgB256;
+  if (a.N <= 0) return hipSuccess;
+  constexpr int lds = C::LDS;
+  static bool attr = false;
+  const void* fn = reinterpret_cast<const void*>(&local_head_kernel<C>);
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, local_head_kernel<C>, C::NT, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  int64_t grid = (int64_t)dev_info().cus * per_cu;
+  const int64_t tiles = (a.N + C::BQ - 1) / C::BQ;
+  if (tiles < grid) grid = tiles;
+  hipLaunchKernelGGL((local_head_kernel<C>), dim3((unsigned)grid), dim3(C::NT), lds, s, a);
+  return hipGetLastError();
+}
+
 int decode_tile_queries(int dtype, int D) {
   if (dtype == VDM_BF16 && D == 256) return CfgB256::BQ;
   if (dtype == VDM_BF16) return CfgB64::BQ;

@@ -962,4 +962,153 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
   return VDM_OK;
 }
 
+// ------------------------------------------------------------------ local KNN decoder
+}  // extern "C"
+
+namespace vdm {
+
+struct LocalWs {
+  int32_t* counts;   // support buckets
+  int32_t* fill;
+  int32_t* starts;
+  int32_t* cell_of;
+  uint32_t* occ;
+  float4* spos;
+  int32_t* qcounts;  // query buckets (processing order)
+  int32_t* qfill;
+  int32_t* qstarts;
+  int32_t* qcell;
+  int32_t* order;
+  int32_t* nbr;
+  void* h;
+  void* Wp;
+};
+
+static size_t local_ws(const vdm_local_decoder* d, int64_t M, int64_t N, void* base, LocalWs* w) {
+  Carve c(base);
+  LocalWs x;
+  constexpr size_t NC = (size_t)LOCAL_G * LOCAL_G * LOCAL_G;
+  const size_t n1 = (size_t)(N > 0 ? N : 1);
+  x.counts = c.take<int32_t>(NC * 4);
+  x.fill = c.take<int32_t>(NC * 4);
+  x.starts = c.take<int32_t>((NC + 1) * 4);
+  x.cell_of = c.take<int32_t>((size_t)M * 4);
+  x.occ = c.take<uint32_t>((size_t)LOCAL_G * LOCAL_G * 4);
+  x.spos = c.take<float4>((size_t)M * 16);
+  x.qcounts = c.take<int32_t>(NC * 4);
+  x.qfill = c.take<int32_t>(NC * 4);
+  x.qstarts = c.take<int32_t>((NC + 1) * 4);
+  x.qcell = c.take<int32_t>(n1 * 4);
+  x.order = c.take<int32_t>(n1 * 4);
+  x.nbr = c.take<int32_t>((size_t)(N > 0 ? N : 1) * LOCAL_K * 4);
+  x.h = c.take<char>((size_t)(N > 0 ? N : 1) * LOCAL_C * 2);
+  x.Wp = c.take<char>((size_t)2 * d->C * d->F * 2);
+  if (w) *w = x;
+  return c.off + 256;
+}
+
+static vdm_status check_local(const vdm_local_decoder* d) {
+  if (!d) return fail(VDM_ERR_INVALID_ARG, "local decoder is NULL");
+  if (d->C != LOCAL_C || d->K != LOCAL_K || d->hidden != LOCAL_HIDDEN)
+    return fail(VDM_ERR_UNSUPPORTED, "local decoder needs C=%d K=%d hidden=%d (got %d, %d, %d)", LOCAL_C, LOCAL_K,
+                LOCAL_HIDDEN, d->C, d->K, d->hidden);
+  if (d->F < 256 || d->F > 4096 || d->F % 256)
+    return fail(VDM_ERR_UNSUPPORTED, "F=%d must be a multiple of 256 in [256, 4096]", d->F);
+  if (!d->A || !d->a || !d->B || !d->W1 || !d->W2 || !d->w_head)
+    return fail(VDM_ERR_INVALID_ARG, "a local decoder weight pointer is NULL");
+  if (!aligned(d->A, 4) || !aligned(d->a, 4) || !aligned(d->w_head, 4) || !aligned(d->B, 16) || !aligned(d->W1, 16) ||
+      !aligned(d->W2, 16))
+    return fail(VDM_ERR_INVALID_ARG, "misaligned local decoder weights (A, a, w_head: 4 bytes; B, W1, W2: 16)");
+  if (d->n_prims < 1 || d->n_prims > VDM_MAX_PRIMS) return fail(VDM_ERR_INVALID_ARG, "n_prims=%d", d->n_prims);
+  for (int i = 0; i < d->n_prims; ++i)
+    if (d->prims[i].kind != VDM_PRIM_SPHERE && d->prims[i].kind != VDM_PRIM_BOX)
+      return fail(VDM_ERR_INVALID_ARG, "primitive %d has kind %d", i, d->prims[i].kind);
+  if (!isfinite(d->net_scale)) return fail(VDM_ERR_INVALID_ARG, "net_scale is not finite");
+  return VDM_OK;
+}
+
+}  // namespace vdm
+
+extern "C" {
+
+size_t vdm_local_workspace_size(const vdm_local_decoder* dec, int64_t M, int64_t N) {
+  if (check_local(dec) != VDM_OK) return 0;
+  if (M < 1 || M >= (1ll << 31) / LOCAL_C || N < 0 || N >= (1ll << 31) / LOCAL_C) {
+    fail(VDM_ERR_INVALID_ARG, "M=%lld N=%lld", (long long)M, (long long)N);
+    return 0;
+  }
+  return local_ws(dec, M, N, nullptr, nullptr);
+}
+
+vdm_status vdm_decode_local(const vdm_local_decoder* dec, const float* sup_xyz, const void* feats, int64_t M,
+                            const float* xyz, int64_t N, float* sdf, int32_t* nbr, void* ws, size_t ws_bytes,
+                            vdm_stream stream) {
+  vdm_status st = check_local(dec);
+  if (st != VDM_OK) return st;
+  if (N < 0 || N >= (1ll << 31) / LOCAL_C) return fail(VDM_ERR_INVALID_ARG, "N=%lld", (long long)N);
+  if (N == 0) return VDM_OK;
+  if (M < dec->K || M >= (1ll << 31) / LOCAL_C)
+    return fail(VDM_ERR_INVALID_ARG, "M=%lld (K=%d <= M < %lld)", (long long)M, dec->K, (1ll << 31) / LOCAL_C);
+  if (!sup_xyz || !feats || !xyz || !sdf) return fail(VDM_ERR_INVALID_ARG, "sup_xyz, feats, xyz or sdf is NULL");
+  if (!aligned(sup_xyz, 4) || !aligned(feats, 16) || !aligned(xyz, 4) || !aligned(sdf, 4) || !aligned(nbr, 4))
+    return fail(VDM_ERR_INVALID_ARG, "misaligned sup_xyz, xyz, sdf, nbr (4 bytes) or feats (16 bytes)");
+  const size_t need = local_ws(dec, M, N, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(VDM_ERR_WORKSPACE, "workspace needs %zu bytes, 256-aligned (got %zu)", need, ws_bytes);
+  LocalWs w;
+  local_ws(dec, M, N, ws, &w);
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* nb = nbr ? nbr : w.nbr;
+  constexpr size_t NC = (size_t)LOCAL_G * LOCAL_G * LOCAL_G;
+  VDM_HIP(launch_zero(w.counts, NC * 4, s), "zero launch");
+  VDM_HIP(launch_zero(w.fill, NC * 4, s), "zero launch");
+  VDM_HIP(launch_zero(w.qcounts, NC * 4, s), "zero launch");
+  VDM_HIP(launch_zero(w.qfill, NC * 4, s), "zero launch");
+  VDM_HIP_T(VDM_TIME_LOCAL_GRID, s,
+            launch_local_grid(sup_xyz, M, w.counts, w.starts, w.fill, w.cell_of, w.spos, nullptr, w.occ, s),
+            "support grid launch");
+  VDM_HIP_T(VDM_TIME_LOCAL_GRID, s,
+            launch_local_grid(xyz, N, w.qcounts, w.qstarts, w.qfill, w.qcell, nullptr, w.order, nullptr, s),
+            "query order launch");
+  VDM_HIP_T(VDM_TIME_LOCAL_KNN, s, launch_local_knn(xyz, N, w.order, w.starts, w.occ, w.spos, nb, s), "knn launch");
+  LocalFuseArgs fa;
+  fa.sup_xyz = sup_xyz;
+  fa.feats = feats;
+  fa.M = (int)M;
+  fa.xyz = xyz;
+  fa.N = N;
+  fa.nbr = nb;
+  fa.A = dec->A;
+  fa.a = dec->a;
+  fa.B = dec->B;
+  fa.h = w.h;
+  VDM_HIP_T(VDM_TIME_LOCAL_FUSE, s, launch_local_fuse(fa, s), "fuse launch");
+  const size_t CF = (size_t)dec->C * dec->F * 2;
+  char* wp = static_cast<char*>(w.Wp);
+  VDM_HIP(launch_pack_w(dec->W1, dec->F, dec->C, wp, s), "weight packing launch");
+  VDM_HIP(launch_pack_w(dec->W2, dec->C, dec->F, wp + CF, s), "weight packing launch");
+  HeadArgs ha;
+  memset(&ha, 0, sizeof ha);
+  ha.xyz = xyz;
+  ha.N = N;
+  ha.h = w.h;
+  ha.W1 = wp;
+  ha.W2 = wp + CF;
+  ha.w_head = dec->w_head;
+  ha.F = dec->F;
+  ha.net_scale = dec->net_scale;
+  ha.prims.n = dec->n_prims;
+  for (int i = 0; i < dec->n_prims; ++i) {
+    ha.prims.p[i].kind = dec->prims[i].kind;
+    for (int c = 0; c < 3; ++c) {
+      ha.prims.p[i].c[c] = dec->prims[i].centre[c];
+      ha.prims.p[i].s[c] = dec->prims[i].size[c];
+    }
+  }
+  ha.out = sdf;
+  VDM_HIP_T(VDM_TIME_LOCAL_HEAD, s, launch_local_head(ha, s), "head launch");
+  return VDM_OK;
+}
+
 }  // extern "C"

@@ -127,6 +127,53 @@ struct SelectArgs {
 hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s);
 size_t select_scratch_bytes(int M);
 
+// ------------------------------------------------------------------ local KNN decoder
+// Supports are bucketed into LOCAL_G^3 cells over [-1, 1]^3.
+constexpr int LOCAL_G = 32;
+constexpr int LOCAL_K = 16;
+constexpr int LOCAL_HIDDEN = 32;
+constexpr int LOCAL_C = 256;
+
+// Bucketing of n points into the cells: counts (zeroed by the caller), starts
+// [LOCAL_G^3 + 1], fill (zeroed), cell_of [n]; then, in cell order, spos (x, y, z,
+// index bits) and/or order (index) when not null; occ [LOCAL_G^2] occupancy words
+// (bit k of word i * LOCAL_G + j: cell (i, j, k) holds a point) when not null.
+hipError_t launch_local_grid(const float* xyz, int64_t n, int32_t* counts, int32_t* starts, int32_t* fill,
+                             int32_t* cell_of, float4* spos, int32_t* order, uint32_t* occ, hipStream_t s);
+// nbr [N][LOCAL_K]: each query's nearest supports, nearest first; queries taken
+// in the given order (a permutation of 0 .. N-1)
+hipError_t launch_local_knn(const float* xyz, int64_t N, const int32_t* order, const int32_t* starts,
+                            const uint32_t* occ, const float4* spos, int32_t* nbr, hipStream_t s);
+
+struct LocalFuseArgs {
+  const float* sup_xyz;   // [M][3]
+  const void* feats;      // [M][C] bf16
+  int M;
+  const float* xyz;       // [N][3]
+  int64_t N;
+  const int32_t* nbr;     // [N][K]
+  const float* A;         // [hidden][3]
+  const float* a;         // [hidden]
+  const void* B;          // [C][hidden] bf16
+  void* h;                // [N][C] bf16 out
+};
+hipError_t launch_local_fuse(const LocalFuseArgs& a, hipStream_t s);
+
+// y = h + W2 GELU(W1 h), net = w_head . y, out[q] = analytic(x_q) + net_scale net
+struct HeadArgs {
+  const float* xyz;    // [N][3]
+  int64_t N;
+  const void* h;       // [N][256] bf16
+  const void* W1;      // fragment-packed (launch_pack_w)
+  const void* W2;      // fragment-packed
+  const float* w_head; // [256]
+  int F;
+  float net_scale;
+  PrimSet prims;
+  float* out;
+};
+hipError_t launch_local_head(const HeadArgs& a, hipStream_t s);
+
 // Surface extraction (marching cubes at SDF = 0) workspace: crossing-edge bit
 // planes, inside bits, per-word vertex prefixes, per-piece triangle counts and
 // their prefixes, per-block partial sums.

@@ -117,6 +117,34 @@ def test_noalloc_decode_argument_checks():
     assert lib.vdm_dense_workspace_size(C.byref(d), 40960, q.N, 0) <= V.NOALLOC_SCRATCH_BYTES
 
 
+def test_local_decoder_argument_checks():
+    import shape_vae_decoding_amd as V
+
+    lib = V._lib
+    d = V._LocalDecoder()
+    d.C, d.F, d.K, d.hidden, d.net_scale = 256, 1024, 16, 32, 0.05
+    for k in ("A", "a", "B", "W1", "W2", "w_head"):
+        setattr(d, k, 0x100000)  # never dereferenced: every case fails validation first or does nothing
+    d.n_prims = 1
+    args = (0x1000, 0x1000, 100, 0x1000, 50, 0x1000, None, 0x1000, 1 << 30, None)
+    assert lib.vdm_decode_local(None, *args) == V.VDM_ERR_INVALID_ARG
+    assert lib.vdm_decode_local(C.byref(d), 0x1000, 0x1000, 100, 0x1000, 0, None, None, None, 0, None) == V.VDM_OK
+    d.K = 8
+    assert lib.vdm_decode_local(C.byref(d), *args) == V.VDM_ERR_UNSUPPORTED
+    d.K = 16
+    d.F = 1000
+    assert lib.vdm_decode_local(C.byref(d), *args) == V.VDM_ERR_UNSUPPORTED
+    d.F = 1024
+    assert lib.vdm_decode_local(C.byref(d), 0x1000, 0x1000, 15, 0x1000, 50, 0x1000, None, 0x1000, 1 << 30,
+                                None) == V.VDM_ERR_INVALID_ARG  # M < K
+    assert lib.vdm_decode_local(C.byref(d), 0x1000, 0x1008, 100, 0x1000, 50, 0x1000, None, 0x1000, 1 << 30,
+                                None) == V.VDM_ERR_INVALID_ARG  # feats misaligned
+    assert lib.vdm_decode_local(C.byref(d), 0x1000, 0x1000, 100, 0x1000, 50, 0x1000, None, 0x1000, 64,
+                                None) == V.VDM_ERR_WORKSPACE
+    need = lib.vdm_local_workspace_size(C.byref(d), 40960, 200000)
+    assert need >= 200000 * 256 * 2 + 200000 * 16 * 4
+
+
 def test_select_and_hier_argument_checks():
     import shape_vae_decoding_amd as V
 

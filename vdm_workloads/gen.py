@@ -327,7 +327,7 @@ def with_unseen_key(K: np.ndarray, Wq: np.ndarray, H: int, token: int, norm: flo
 _S_LOCAL = 50
 LOCAL_K = 16       # neighbours per query
 LOCAL_HIDDEN = 32  # width of the offset MLP
-LOCAL_OFFSET_SCALE = 0.05  # offsets of this length reach the offset MLP's hidden units at unit scale
+LOCAL_OFFSET_SCALE = 0.25  # offsets of this length reach the offset MLP's hidden units at unit scale
 
 
 @dataclasses.dataclass
