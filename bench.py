@@ -93,8 +93,12 @@ def mask_stress(steps: int):
     import numpy as np
     import torch
 
-    import shape_vae_decoding_amd as V
     import vdm_workloads as W
+
+    # the CPU baseline first: its worker processes fork before this process touches the GPU
+    cpu_cfg = None if args.skip_cpu else cpu_baseline(W)
+
+    import shape_vae_decoding_amd as V
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -151,35 +155,77 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, target_s: float = 12.0):
-    """The oracle, as it stands, on a bounded sample of the dense 129^3 workload."""
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+
+_CPU = {}  # per worker process: the workloads and oracle decoders (set before the pool forks)
+
+
+def _cpu_init():
+    from threadpoolctl import threadpool_limits
+
+    threadpool_limits(1)  # one BLAS thread per worker process
+
+
+def _cpu_chunk(task):
+    """Decode one chunk of a workload's queries with the oracle; returns (points, seconds)."""
     import numpy as np
 
-    from oracle import decoder as odec
+    from oracle import local as olo
+
+    cfg, seed, n = task
+    rng = np.random.default_rng(seed)
+    t0 = time.perf_counter()
+    if cfg in ("c0", "c1"):
+        R = _CPU[cfg].query["R"]
+        _CPU["dec"][cfg].sdf_grid(R, rng.integers(0, (R + 1) ** 3, n), chunk=n)
+    elif cfg == "c4":
+        xyz = _CPU[cfg].query["xyz"]
+        _CPU["dec"][cfg].sdf(xyz[rng.integers(0, xyz.shape[0], n)], chunk=n)
+    else:  # the local KNN decoder
+        w = _CPU[cfg]
+        olo.sdf_of(w, w.queries[rng.integers(0, w.queries.shape[0], n)])
+    return n, time.perf_counter() - t0
+
+
+def cpu_baseline(W, budget_s: float = 24.0):
+    """The oracle, as it stands, timed on the host's cores: a process pool (one BLAS
+    thread per worker, workers = the cores this process may use, at most 16) decodes
+    chunks of random query points of each workload for a bounded wall time. Points
+    per second per workload, and the ms one whole workload would take at that rate
+    (c2 / c3: their decoded-point counts at the dense 129^3 rate of the same decoder;
+    the oracle's bookkeeping is negligible next to its decode)."""
+    import multiprocessing as mp
 
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = sorted({f"{i.get('internal_api')} ({i.get('prefix')})" for i in threadpool_info()
+                       if i.get("user_api") == "blas"})
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    od = odec.Decoder.from_workload(w)
-    R = w.query["R"]
-    rng = np.random.default_rng(0)
-    n_done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < target_s:
-        lin = rng.integers(0, (R + 1) ** 3, 512)
-        od.sdf_grid(R, lin)
-        n_done += lin.size
-    dt = time.perf_counter() - t0
-    return {
-        "value": n_done / dt,
-        "unit": "query points/s",
-        "cores": int(cores),
-        "kind": "oracle",
-        "sample": f"{n_done} random points of the 129^3 grid decoded by the float64 oracle "
-                  f"(M=3072, D=256, F=1024) in {dt:.1f} s",
-    }
+        blas = ["unknown"]
+    from oracle import decoder as odec
+
+    _CPU.update({"c0": W.make(0), "c1": W.make(1), "c4": W.make(4), "local": W.make_local()})
+    _CPU["dec"] = {c: odec.Decoder.from_workload(_CPU[c]) for c in ("c0", "c1", "c4")}
+    workers = max(1, min(len(os.sched_getaffinity(0)), 16))
+    # seconds of wall time per workload, and points per chunk
+    plan = {"c0": (2.0, 1024), "c1": (9.0, 256), "c4": (7.0, 32), "local": (6.0, 64)}
+    out = {}
+    with mp.get_context("fork").Pool(workers, initializer=_cpu_init) as pool:
+        for cfg, (secs, chunk) in plan.items():
+            t0 = time.perf_counter()
+            n = 0
+            seed = 0
+            while time.perf_counter() - t0 < secs:
+                for done, _ in pool.imap_unordered(_cpu_chunk, [(cfg, seed + i, chunk) for i in range(workers)]):
+                    n += done
+                seed += workers
+            dt = time.perf_counter() - t0
+            out[cfg] = {"points": n, "seconds": round(dt, 2), "query_points_per_s": round(n / dt, 1)}
+    sizes = {"c0": 17 ** 3, "c1": 129 ** 3, "c4": 200_000, "local": 200_000}
+    for cfg, n in sizes.items():
+        out[cfg]["ms_per_workload"] = round(n / out[cfg]["query_points_per_s"] * 1e3, 1)
+    return out, workers, blas
 
 
 def large_token_decode(V, W, dev, reps: int = 5):
@@ -263,6 +309,42 @@ def local_knn_decode(V, W, dev, reps: int = 5):
             "head_tflops": round(head_flop / (stages["head_ms"] / 1e3) / 1e12, 2),
             "fuse_mfma_tflops": round(fuse_flop / (stages["fuse_ms"] / 1e3) / 1e12, 2),
             "vs_dense_200k_x_40960": None}
+
+
+def quality_vs_dense(V, dec, K, Vv, p_h, p_a, Pf: int, dev):
+    """Hierarchical decoding (without and with KV selection) against the dense
+    decode of every point of the same grid: at the points the finest level
+    decodes, max / mean |dSDF|; over the whole volume, sign flips (inside is
+    SDF < 0) and the IoU of the occupancies."""
+    import numpy as np
+    import torch
+
+    dense = torch.empty(Pf ** 3, dtype=torch.float32, device=dev)
+    V.vdm_decode_dense(dec, V.queries_grid(Pf - 1), K, Vv, dense)
+    res = {}
+    for name, p in (("hier", p_h), ("hier_akvs", p_a)):
+        vol = torch.empty(Pf ** 3, dtype=torch.float32, device=dev)
+        st = torch.zeros(p.levels * V.STAT_FIELDS, dtype=torch.int64, device=dev)
+        dbg = V.HierDebug(p, dev)
+        V.vdm_decode_hier(dec, p, K, Vv, vol, st, dbg)
+        torch.cuda.synchronize()
+        n_last = V.stats_dict(st, p.levels)[-1]["queries"]
+        lst = dbg.levels[p.levels - 1]["list"][:n_last].long()
+        d = (vol[lst] - dense[lst]).abs().double()
+        inside_h, inside_d = vol < 0, dense < 0
+        inter = int((inside_h & inside_d).sum().item())
+        union = int((inside_h | inside_d).sum().item())
+        res[name] = {
+            "finest_decoded_points": int(n_last),
+            "max_abs_dsdf": round(float(d.max().item()), 6),
+            "mean_abs_dsdf": round(float(d.mean().item()), 7),
+            "sign_flips": int((inside_h != inside_d).sum().item()),
+            "volume_points": Pf ** 3,
+            "occupancy_iou": round(inter / max(union, 1), 6),
+        }
+        del vol, dbg
+    del dense
+    return res
 
 
 def surface_extraction(V, vol, R: int, dev, reps: int = 10):
@@ -627,6 +709,10 @@ def main():
     if args.step_only:
         print(json.dumps(out), flush=True)
         return
+    # outside the timed steps: quality of the hierarchical volumes against a dense
+    # 301^3 decode (the hierarchical-with-selection workload asks for dSDF and sign
+    # flips; occupancy IoU as on the pages)
+    out["breakdown"]["quality_vs_dense_301cubed"] = quality_vs_dense(V, dec, K, Vv, p_h, p_a, Pf, dev)
     # outside the timed steps: surface extraction of the hierarchical volume
     out["breakdown"]["surface_extraction_300cubed"] = surface_extraction(V, vol_h, Pf - 1, dev)
     # outside the timed steps: the pages' 384^3 resolution example (96 -> 192 -> 384, band of two fine widths)
@@ -690,7 +776,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.skip_cpu:
-        out["cpu_baseline"] = cpu_baseline(w)
+        per, workers, blas = cpu_cfg
+        hv_rate = per["c1"]["query_points_per_s"]
+        per["c2"] = {"ms_per_workload": round(q_h / hv_rate * 1e3, 1), "from": "c1 rate x decoded points"}
+        per["c3"] = {"ms_per_workload": round(q_a / hv_rate * 1e3, 1), "from": "c1 rate x decoded points"}
+        out["cpu_baseline"] = {
+            "value": per["c1"]["query_points_per_s"],
+            "unit": "query points/s",
+            "cores": workers,
+            "kind": "oracle",
+            "sample": (f"float64 oracle in a pool of {workers} processes (one BLAS thread each; BLAS: "
+                       f"{', '.join(blas)}), random points of each workload for a bounded time: "
+                       + "; ".join(f"{k} {v['points']} points in {v['seconds']} s" for k, v in per.items()
+                                   if "points" in v)
+                       + "; value = the dense 129^3 workload's rate"),
+            "per_config": per,
+        }
     print(json.dumps(out), flush=True)
 
 
