@@ -93,12 +93,8 @@ def mask_stress(steps: int):
     import numpy as np
     import torch
 
-    import vdm_workloads as W
-
-    # the CPU baseline first: its worker processes fork before this process touches the GPU
-    cpu_cfg = None if args.skip_cpu else cpu_baseline(W)
-
     import shape_vae_decoding_amd as V
+    import vdm_workloads as W
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -568,8 +564,12 @@ def main():
     import numpy as np
     import torch
 
-    import shape_vae_decoding_amd as V
     import vdm_workloads as W
+
+    # the CPU baseline first: its worker processes fork before this process touches the GPU
+    cpu_cfg = None if args.skip_cpu else cpu_baseline(W)
+
+    import shape_vae_decoding_amd as V
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
