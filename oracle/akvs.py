@@ -22,7 +22,10 @@ Readings (the pages leave these open):
     block keeps the union; if the union exceeds ``cap`` tokens, those with the
     largest max-over-probes score are kept (ties to the lower index);
   * the kept set is stored in ascending token order;
-  * ranking uses float32 scores (the precision a GPU kernel ranks in).
+  * ranking uses float32 scores (the precision a GPU kernel ranks in);
+  * per-head sets (the alternative reading of the multi-head score): head h
+    ranks tokens by its own softmax probability and keeps its own union and cap,
+    and its attention in the sub-volume runs over that set only.
 """
 
 from __future__ import annotations
@@ -89,6 +92,33 @@ def probe_scores(Qp: np.ndarray, K: np.ndarray, H: int) -> np.ndarray:
     return dec.attention_probs(np.asarray(Qp, np.float64), np.asarray(K, np.float64), H).mean(axis=0)
 
 
+def probe_scores_per_head(Qp: np.ndarray, K: np.ndarray, H: int) -> np.ndarray:
+    """[H, n_probe, M]: each head's softmax probability for each probe."""
+    return dec.attention_probs(np.asarray(Qp, np.float64), np.asarray(K, np.float64), H)
+
+
+def attention_per_head_sets(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, sets) -> np.ndarray:
+    """Attention of queries Q [N, D] where head h attends only to tokens sets[h]
+    (columns 64h .. 64h+63 of K and V)."""
+    Q = np.asarray(Q, np.float64)
+    out = np.empty_like(Q)
+    for h in range(H):
+        c = slice(dec.HEAD_DIM * h, dec.HEAD_DIM * (h + 1))
+        t = np.asarray(sets[h])
+        s_ = (Q[:, c] @ np.asarray(K, np.float64)[t][:, c].T) / np.sqrt(dec.HEAD_DIM)
+        out[:, c] = dec.softmax_rows(s_) @ np.asarray(V, np.float64)[t][:, c]
+    return out
+
+
+def sdf_per_head_sets(decoder: dec.Decoder, xyz: np.ndarray, sets, K=None, V=None) -> np.ndarray:
+    """SDF at float32 points with head h attending only to sets[h]."""
+    K = decoder.K if K is None else K
+    V = decoder.V if V is None else V
+    xyz = np.asarray(xyz, np.float32)
+    O = attention_per_head_sets(decoder.q(xyz), K, V, decoder.H, sets)
+    return dec.analytic_sdf(xyz, decoder.prims) + decoder.net_scale * dec.mlp_head(O, decoder.W)
+
+
 def topk_ids(score: np.ndarray, k: int) -> np.ndarray:
     """Indices of the k largest scores; equal scores go to the lower index."""
     M = score.shape[0]
@@ -135,10 +165,12 @@ def near_tie_tokens(scores: np.ndarray, k: int, cap: Optional[int] = None, rel: 
 
 
 def select_blocks(decoder: dec.Decoder, R: int, blocks: np.ndarray, k: int, cap: int,
-                  block: int = 8, Qfn=None, probes: str = "corners", seed: int = 0) -> Dict[int, np.ndarray]:
+                  block: int = 8, Qfn=None, probes: str = "corners", seed: int = 0,
+                  heads: bool = False) -> Dict[int, np.ndarray]:
     """Token sets for the given block ids of the R-cell grid. ``Qfn`` maps
     float32 probe points to projections (default: the oracle's own). ``probes``:
-    "corners" or "random" (SplitMix64 stream seeded with ``seed``)."""
+    "corners" or "random" (SplitMix64 stream seeded with ``seed``). ``heads``:
+    one set per head (a list of H arrays per block) instead of one per block."""
     NB = hv.nblocks(R + 1, block)
     if probes == "random":
         idx = block_random_indices(R, blocks, NB, seed, block)
@@ -148,12 +180,16 @@ def select_blocks(decoder: dec.Decoder, R: int, blocks: np.ndarray, k: int, cap:
     for n, b in enumerate(np.asarray(blocks, np.int64)):
         pts = dec.grid_coord(idx[n], R).astype(np.float32)
         Qp = decoder.q(pts) if Qfn is None else Qfn(pts)
-        out[int(b)] = select(probe_scores(Qp, decoder.K, decoder.H), k, cap)
+        if heads:
+            sc = probe_scores_per_head(Qp, decoder.K, decoder.H)
+            out[int(b)] = [select(sc[h], k, cap) for h in range(decoder.H)]
+        else:
+            out[int(b)] = select(probe_scores(Qp, decoder.K, decoder.H), k, cap)
     return out
 
 
 def make_decode(decoder: dec.Decoder, k: int, cap: int, block: int = 8, record: Optional[dict] = None,
-                probes: str = "corners", seed: int = 0):
+                probes: str = "corners", seed: int = 0, heads: bool = False):
     """A ``decode(R, lin)`` for ``hvd.hvd`` that groups the queries by block,
     selects each block's tokens with its probes (random probes: the level with
     R cells uses the stream seeded with seed + R), and decodes the block's
@@ -163,7 +199,7 @@ def make_decode(decoder: dec.Decoder, k: int, cap: int, block: int = 8, record: 
         P = R + 1
         blk = hv.block_of(lin, P, block)
         ub = np.unique(blk)
-        sets = select_blocks(decoder, R, ub, k, cap, block, probes=probes, seed=(seed + R) & MASK64)
+        sets = select_blocks(decoder, R, ub, k, cap, block, probes=probes, seed=(seed + R) & MASK64, heads=heads)
         if record is not None:
             record[R] = sets
         out = np.empty(lin.size, np.float64)
@@ -171,7 +207,10 @@ def make_decode(decoder: dec.Decoder, k: int, cap: int, block: int = 8, record: 
         for b in ub:
             m = blk == b
             sel = sets[int(b)]
-            out[m] = decoder.sdf(pts[m], decoder.K[sel], decoder.V[sel])
+            if heads:
+                out[m] = sdf_per_head_sets(decoder, pts[m], sel)
+            else:
+                out[m] = decoder.sdf(pts[m], decoder.K[sel], decoder.V[sel])
         return out
 
     return decode

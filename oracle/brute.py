@@ -80,13 +80,17 @@ def matvec(W, x) -> List[float]:
 
 
 def decode_point(p, W: Dict, K: List[List[float]], V: List[List[float]], H: int,
-                 prims, net_scale: float, dtype: str, tokens=None) -> float:
+                 prims, net_scale: float, dtype: str, tokens=None, head_tokens=None) -> float:
+    """tokens: one token subset for every head; head_tokens: a subset per head."""
     q = matvec(W["Wq"], embed(p))
     if dtype == "bf16":
         q = [bf16(v) for v in q]
-    toks = range(len(K)) if tokens is None else tokens
     o = []
     for h in range(H):
+        if head_tokens is not None:
+            toks = head_tokens[h]
+        else:
+            toks = range(len(K)) if tokens is None else tokens
         cols = range(64 * h, 64 * h + 64)
         logits = []
         for j in toks:
@@ -221,6 +225,21 @@ def scores(qs, K, H: int) -> List[List[float]]:
             for j in range(M):
                 acc[j] += ex[j] / tot / H
         out.append(acc)
+    return out
+
+
+def scores_per_head(qs, K, H: int) -> List[List[List[float]]]:
+    """[H][probe][token]: each head's softmax probability."""
+    M = len(K)
+    out = [[] for _ in range(H)]
+    for q in qs:
+        for h in range(H):
+            cols = range(64 * h, 64 * h + 64)
+            lg = [sum(q[c] * K[j][c] for c in cols) / 8.0 for j in range(M)]
+            mx = max(lg)
+            ex = [math.exp(v - mx) for v in lg]
+            tot = sum(ex)
+            out[h].append([e / tot for e in ex])
     return out
 
 

@@ -134,3 +134,48 @@ def test_hvd_with_selection_vs_brute():
     P = R0 * 2 ** (levels - 1) + 1
     ref = np.array([bvol[t] for t in itertools.product(range(P), repeat=3)]).reshape(P, P, P)
     np.testing.assert_allclose(res["vol"], ref, atol=1e-12, rtol=0)
+
+
+def test_per_head_scores_and_sets_vs_brute():
+    rng = np.random.default_rng(35)
+    Qp = rng.standard_normal((8, 128)) * 2
+    K = rng.standard_normal((24, 128))
+    got = akvs.probe_scores_per_head(Qp, K, 2)
+    ref = brute.scores_per_head(Qp.tolist(), K.tolist(), 2)
+    np.testing.assert_allclose(got, ref, atol=1e-15, rtol=0)
+    # the head-mean score is the mean of the per-head scores
+    np.testing.assert_allclose(got.mean(axis=0), akvs.probe_scores(Qp, K, 2), atol=1e-16, rtol=0)
+    for h in range(2):
+        assert list(akvs.select(got[h], 3, 10)) == brute.select(ref[h], 3, 10)
+    # the heads rank differently: their sets differ
+    assert not np.array_equal(akvs.select(got[0], 3, 24), akvs.select(got[1], 3, 24))
+
+
+def test_per_head_sets_decode_vs_brute_and_special_cases():
+    w = W.gen.small_decoder(36, 128, 128, 20, "f32")
+    od = dec.Decoder.from_workload(w)
+    pts = W.gen.random_points(37, 5)
+    sets = [np.array([0, 3, 4, 9, 17]), np.array([1, 2, 3, 12, 13, 19])]
+    got = akvs.sdf_per_head_sets(od, pts, sets)
+    W64 = {k: v.astype(np.float64).tolist() for k, v in w.weights.items()}
+    for n in range(pts.shape[0]):
+        ref = brute.decode_point(pts[n].tolist(), W64, od.K.tolist(), od.V.tolist(), 2, w.prims, w.net_scale, "f32",
+                                 head_tokens=[s.tolist() for s in sets])
+        assert abs(got[n] - ref) < 1e-12
+    # every head on the same set: attention restricted to that set
+    same = [sets[0], sets[0]]
+    np.testing.assert_allclose(akvs.sdf_per_head_sets(od, pts, same),
+                               od.sdf(pts, od.K[sets[0]], od.V[sets[0]]), atol=1e-13, rtol=0)
+    # every head on all tokens: full attention
+    allt = [np.arange(w.M)] * 2
+    np.testing.assert_allclose(akvs.sdf_per_head_sets(od, pts, allt), od.sdf(pts), atol=1e-13, rtol=0)
+
+
+def test_per_head_selection_with_one_head_equals_head_mean():
+    w = W.gen.small_decoder(38, 64, 128, 50, "bf16")
+    od = dec.Decoder.from_workload(w)
+    blocks = np.array([0, 2, 5])
+    a = akvs.select_blocks(od, 12, blocks, 7, 30)
+    b = akvs.select_blocks(od, 12, blocks, 7, 30, heads=True)
+    for blk in blocks:
+        np.testing.assert_array_equal(a[int(blk)], b[int(blk)][0])
