@@ -307,7 +307,7 @@ def local_knn_decode(V, W, dev, reps: int = 5):
             "vs_dense_200k_x_40960": None}
 
 
-def quality_vs_dense(V, dec, K, Vv, p_h, p_a, Pf: int, dev):
+def quality_vs_dense(V, dec, K, Vv, p_h, p_a, Pf: int, dev, p_ph=None):
     """Hierarchical decoding (without and with KV selection) against the dense
     decode of every point of the same grid: at the points the finest level
     decodes, max / mean |dSDF|; over the whole volume, sign flips (inside is
@@ -318,7 +318,8 @@ def quality_vs_dense(V, dec, K, Vv, p_h, p_a, Pf: int, dev):
     dense = torch.empty(Pf ** 3, dtype=torch.float32, device=dev)
     V.vdm_decode_dense(dec, V.queries_grid(Pf - 1), K, Vv, dense)
     res = {}
-    for name, p in (("hier", p_h), ("hier_akvs", p_a)):
+    runs = [("hier", p_h), ("hier_akvs", p_a)] + ([("hier_akvs_per_head", p_ph)] if p_ph is not None else [])
+    for name, p in runs:
         vol = torch.empty(Pf ** 3, dtype=torch.float32, device=dev)
         st = torch.zeros(p.levels * V.STAT_FIELDS, dtype=torch.int64, device=dev)
         dbg = V.HierDebug(p, dev)
@@ -712,7 +713,9 @@ def main():
     # outside the timed steps: quality of the hierarchical volumes against a dense
     # 301^3 decode (the hierarchical-with-selection workload asks for dSDF and sign
     # flips; occupancy IoU as on the pages)
-    out["breakdown"]["quality_vs_dense_301cubed"] = quality_vs_dense(V, dec, K, Vv, p_h, p_a, Pf, dev)
+    p_q = V.hier_params(R0=aq["R0"], levels=aq["levels"], tau=aq["tau"], dilation=aq["dilation"],
+                        kvsel=dict(aq["kvsel"], heads=True))
+    out["breakdown"]["quality_vs_dense_301cubed"] = quality_vs_dense(V, dec, K, Vv, p_h, p_a, Pf, dev, p_q)
     # outside the timed steps: surface extraction of the hierarchical volume
     out["breakdown"]["surface_extraction_300cubed"] = surface_extraction(V, vol_h, Pf - 1, dev)
     # outside the timed steps: the pages' 384^3 resolution example (96 -> 192 -> 384, band of two fine widths)
@@ -757,6 +760,26 @@ def main():
         "ms_per_300cubed_volume": round(ra.elapsed_time(rb) / 3, 4),
         "decoded_points": sum(x["queries"] for x in sr),
         "mean_selected_tokens": round(sum(x["selected"] for x in sr) / max(sum(x["blocks"] for x in sr), 1), 1)}
+    # outside the timed steps: the KV-selection volume with one token set per (block, head)
+    p_ph = V.hier_params(R0=aq["R0"], levels=aq["levels"], tau=aq["tau"], dilation=aq["dilation"],
+                         kvsel=dict(aq["kvsel"], heads=True))
+    st_ph = torch.zeros(aq["levels"] * V.STAT_FIELDS, dtype=torch.int64, device=dev)
+    ws_ph = V.workspace(V.vdm_hier_workspace_size(dec, p_ph, w.M), dev)
+    V.vdm_decode_hier(dec, p_ph, K, Vv, vol_a, st_ph, ws=ws_ph)
+    torch.cuda.synchronize()
+    ha, hb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ha.record()
+    for _ in range(3):
+        V.vdm_decode_hier(dec, p_ph, K, Vv, vol_a, st_ph, ws=ws_ph)
+    hb.record()
+    torch.cuda.synchronize()
+    sph = V.stats_dict(st_ph, aq["levels"])
+    out["breakdown"]["akvs_per_head_sets"] = {
+        "ms_per_300cubed_volume": round(ha.elapsed_time(hb) / 3, 4),
+        "decoded_points": sum(x["queries"] for x in sph),
+        "mean_selected_tokens_per_head": round(sum(x["selected"] for x in sph)
+                                               / max(w.H * sum(x["blocks"] for x in sph), 1), 1)}
+    del ws_ph
     if not args.skip_cpu:
         # outside the timed steps (and left out of profiling runs): the large-token
         # workload and the machine's reference figures

@@ -131,6 +131,8 @@ typedef struct {
   const int32_t* sel_idx;   /* [rows, cap] ascending token ids (first sel_cnt valid) */
   const int32_t* sel_cnt;   /* [rows], 1 .. cap (0 gives a zero attention output) */
   const int32_t* block_row; /* [NB^3] block id -> row of sel_idx, or NULL (row = block id) */
+  int32_t heads;            /* 0: one set per row; 1: per-head sets (vdm_select_kv_heads): head h of
+                               row r attends to set r * H + h of sel_idx / sel_cnt */
 } vdm_kvsel;
 
 /* Hierarchical decoding parameters. Level L has R0 * 2^L cells per axis. */
@@ -145,6 +147,7 @@ typedef struct {
   int32_t cap;       /* token cap per block (512) */
   int32_t probes;    /* 0: corner probes; 1: random probes (see vdm_select_kv), level L seeded with seed + R0 * 2^L */
   uint64_t seed;     /* random probes: SplitMix64 seed */
+  int32_t heads;     /* KV selection: 0 = one token set per block; 1 = one per (block, head) */
 } vdm_hier_params;
 
 /* Per-level counters written by vdm_decode_hier to a DEVICE array of int64:
@@ -255,6 +258,18 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
                          int32_t probes, uint64_t seed, const void* K, int64_t M,
                          const int32_t* blocks, int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt,
                          void* ws, size_t ws_bytes, vdm_stream stream);
+
+/* Adaptive KV selection with one token set per (block, head): the alternative
+ * reading of the multi-head score in section 4.1 item 2. Head h ranks the tokens
+ * by its own softmax probability (not the head mean); each head keeps its own
+ * union of the probes' top-k and its own cap (by the head's max-over-probes
+ * probability). Arguments as vdm_select_kv; output rows are [nblk][H]: set h of
+ * block row r is sel_idx[(r * H + h) * cap ..], sel_cnt[r * H + h]. Workspace:
+ * vdm_select_heads_workspace_size(dec, M). Decode with a vdm_kvsel whose heads = 1. */
+vdm_status vdm_select_kv_heads(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,
+                               int32_t probes, uint64_t seed, const void* K, int64_t M,
+                               const int32_t* blocks, int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt,
+                               void* ws, size_t ws_bytes, vdm_stream stream);
 
 /* Hierarchical volume decoding (section 4.1 item 1), optionally with adaptive KV
  * selection at every level (item 2). Writes the final (R0*2^(levels-1) + 1)^3
@@ -375,6 +390,7 @@ vdm_status vdm_decode_local(const vdm_local_decoder* dec, const float* sup_xyz, 
 /* Workspace bytes for the calls above (0 with vdm_last_error set on bad args). */
 size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, int32_t with_sel);
 size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M);
+size_t vdm_select_heads_workspace_size(const vdm_decoder* dec, int64_t M);
 size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M);
 size_t vdm_surface_workspace_size(int32_t R);
 size_t vdm_dense_batch_workspace_size(const vdm_decoder* dec, int32_t B, int64_t M);

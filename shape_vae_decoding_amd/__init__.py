@@ -36,6 +36,7 @@ EXPORTS = [
     "vdm_timing_read", "vdm_version", "vdm_last_error", "vdm_extract_surface", "vdm_surface_workspace_size",
     "vdm_decode_dense_batch", "vdm_dense_batch_workspace_size", "vdm_decode_hier_batch",
     "vdm_hier_batch_workspace_size", "vdm_decode_dense_noalloc", "vdm_decode_local", "vdm_local_workspace_size",
+    "vdm_select_kv_heads", "vdm_select_heads_workspace_size",
 ]
 TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "cell_test", "dilate", "mark", "scan",
               "emit", "fill", "surface", "local_grid", "local_knn", "local_fuse", "local_head"]
@@ -67,13 +68,13 @@ class _Queries(C.Structure):
 
 class _KvSel(C.Structure):
     _fields_ = [("block", C.c_int32), ("cap", C.c_int32), ("sel_idx", C.c_void_p), ("sel_cnt", C.c_void_p),
-                ("block_row", C.c_void_p)]
+                ("block_row", C.c_void_p), ("heads", C.c_int32)]
 
 
 class _HierParams(C.Structure):
     _fields_ = [("R0", C.c_int32), ("levels", C.c_int32), ("dilation", C.c_int32), ("tau", C.c_float),
                 ("use_kvsel", C.c_int32), ("block", C.c_int32), ("k", C.c_int32), ("cap", C.c_int32),
-                ("probes", C.c_int32), ("seed", C.c_uint64)]
+                ("probes", C.c_int32), ("seed", C.c_uint64), ("heads", C.c_int32)]
 
 
 class _LocalDecoder(C.Structure):
@@ -107,6 +108,10 @@ _lib.vdm_select_kv.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int32, C.c_in
                                C.c_uint64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
                                C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.vdm_select_kv.restype = _st
+_lib.vdm_select_kv_heads.argtypes = _lib.vdm_select_kv.argtypes
+_lib.vdm_select_kv_heads.restype = _st
+_lib.vdm_select_heads_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64]
+_lib.vdm_select_heads_workspace_size.restype = C.c_size_t
 _lib.vdm_decode_hier.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_void_p, C.c_void_p, C.c_int64,
                                  C.c_void_p, C.c_int64, C.c_void_p, C.POINTER(_HierDebug), C.c_void_p, C.c_size_t,
                                  C.c_void_p]
@@ -342,14 +347,15 @@ class KvSel:
 
 
 def kvsel(block: int, cap: int, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
-          block_row: Optional[torch.Tensor] = None) -> KvSel:
+          block_row: Optional[torch.Tensor] = None, heads: bool = False) -> KvSel:
+    """heads: the sets come from vdm_select_kv_heads (rows [block][H])."""
     _dev(sel_idx, torch.int32, "sel_idx")
     _dev(sel_cnt, torch.int32, "sel_cnt")
     keep = [sel_idx, sel_cnt]
     if block_row is not None:
         _dev(block_row, torch.int32, "block_row")
         keep.append(block_row)
-    return KvSel(_KvSel(block, cap, sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(block_row)), *keep)
+    return KvSel(_KvSel(block, cap, sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(block_row), int(heads)), *keep)
 
 
 def vdm_dense_workspace_size(dec: Decoder, M: int, N: int, with_sel: bool = False) -> int:
@@ -427,7 +433,8 @@ PROBES = {"corners": 0, "random": 1}
 def vdm_select_kv(dec: Decoder, R: int, block: int, k: int, cap: int, K: torch.Tensor,
                   blocks: Optional[torch.Tensor], sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
                   nblk: Optional[int] = None, ws: Optional[torch.Tensor] = None, stream=None,
-                  probes: str = "corners", seed: int = 0) -> None:
+                  probes: str = "corners", seed: int = 0, heads: bool = False) -> None:
+    """heads: one set per (block, head) (vdm_select_kv_heads): sel_idx [nblk, H, cap], sel_cnt [nblk, H]."""
     _dev(K, dec.torch_dtype, "K")
     _dev(sel_idx, torch.int32, "sel_idx")
     _dev(sel_cnt, torch.int32, "sel_cnt")
@@ -438,25 +445,29 @@ def vdm_select_kv(dec: Decoder, R: int, block: int, k: int, cap: int, K: torch.T
         nb = -(-(R + 1) // block)
         nblk = nb ** 3
     if ws is None:
-        ws = workspace(vdm_select_workspace_size(dec, K.shape[0]), K.device)
-    _check(_lib.vdm_select_kv(dec.ref, R, block, k, cap, PROBES[probes], seed, K.data_ptr(), K.shape[0],
-                              _ptr(blocks), nblk, sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(ws), ws.numel(),
-                              _stream(stream)))
+        size = _lib.vdm_select_heads_workspace_size if heads else _lib.vdm_select_workspace_size
+        ws = workspace(int(size(dec.ref, K.shape[0])), K.device)
+    fn = _lib.vdm_select_kv_heads if heads else _lib.vdm_select_kv
+    _check(fn(dec.ref, R, block, k, cap, PROBES[probes], seed, K.data_ptr(), K.shape[0], _ptr(blocks), nblk,
+              sel_idx.data_ptr(), sel_cnt.data_ptr(), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def hier_params(R0=75, levels=3, tau=2 * 2 / 300, dilation=1, kvsel: Optional[dict] = None) -> _HierParams:
-    p = _HierParams(R0, levels, dilation, float(tau), 0, 8, 64, 512, 0, 0)
+    p = _HierParams(R0, levels, dilation, float(tau), 0, 8, 64, 512, 0, 0, 0)
     if kvsel:
         p.use_kvsel, p.block, p.k, p.cap = 1, kvsel.get("block", 8), kvsel["k"], kvsel["cap"]
         p.probes, p.seed = PROBES[kvsel.get("probes", "corners")], kvsel.get("seed", 0)
+        p.heads = int(bool(kvsel.get("heads", False)))
     return p
 
 
 class HierDebug:
     """Device buffers for the inspection outputs of vdm_decode_hier."""
 
-    def __init__(self, params: _HierParams, device=None, with_sel: bool = False):
+    def __init__(self, params: _HierParams, device=None, with_sel: bool = False, H: int = 4):
+        """H: heads of the decoder (per-head sets hold H rows per block)."""
         dev = device or "cuda"
+        ns = H if params.heads else 1
         self.levels = []
         s = _HierDebug()
         for L in range(params.levels):
@@ -471,8 +482,8 @@ class HierDebug:
             }
             if with_sel:
                 d["sel_blocks"] = torch.empty(nb ** 3, dtype=torch.int32, device=dev)
-                d["sel_cnt"] = torch.empty(nb ** 3, dtype=torch.int32, device=dev)
-                d["sel_idx"] = torch.empty(nb ** 3 * params.cap, dtype=torch.int32, device=dev)
+                d["sel_cnt"] = torch.empty(nb ** 3 * ns, dtype=torch.int32, device=dev)
+                d["sel_idx"] = torch.empty(nb ** 3 * ns * params.cap, dtype=torch.int32, device=dev)
             for k, t in d.items():
                 getattr(s, k)[L] = t.data_ptr()
             self.levels.append(d)

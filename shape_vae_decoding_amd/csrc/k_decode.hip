@@ -239,7 +239,9 @@ __device__ __forceinline__ void softmax_block(const f32x16& S, float nb, float& 
 
 // ---------------------------------------------------------------- token-tile staging (LDS)
 // Global -> registers for tile kt. Dense: 32 rows of packed K and the packed V^T
-// tile, both contiguous. Gathered: rows sel[32kt + j] of K and V (zero past nkeys).
+// tile, both contiguous. Gathered: rows sel[32kt + j] of K and V (zero past nkeys;
+// with per-head sets, sel and nkeys are those of the head whose columns this
+// thread stages).
 template <typename C, bool GATHER>
 __device__ __forceinline__ void tile_load(const typename C::T* __restrict__ Kg, const typename C::T* __restrict__ Vg,
                                           const int32_t* sel, int nkeys, int M, int kt, int tid, uint4 (&rk)[C::NCK],
@@ -848,25 +850,27 @@ __device__ __forceinline__ void gathered_attention_pipe(
 
 // Attention over one block's selected token set: 32-token tiles gathered into
 // an LDS double buffer (V transposed on the way in), one barrier per tile.
+// sel_st / nk_st: the token set this thread stages (its head's with per-head
+// sets); nkeys: this wave's count (its softmax masks keys past it); nkt: tiles
+// of the largest set of the workgroup (every wave runs them for the barriers).
 template <typename C, bool SHIFT>
 __device__ __forceinline__ void gathered_attention(const typename C::T* __restrict__ Kg,
-                                                   const typename C::T* __restrict__ Vg, const int32_t* sel,
-                                                   int nkeys, int M, int tid, int lane, int hw, char* lds,
-                                                   const int (&vpos)[C::NCK], bool active,
+                                                   const typename C::T* __restrict__ Vg, const int32_t* sel_st,
+                                                   int nk_st, int nkeys, int nkt, int M, int tid, int lane, int hw,
+                                                   char* lds, const int (&vpos)[C::NCK], bool active,
                                                    const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
                                                    const float (&nb)[C::QB], f32x16 (&O)[2][C::QB],
                                                    float (&l_run)[C::QB]) {
   using T = typename C::T;
   using MM = Mma<T>;
   using Frag = typename MM::frag;
-  const int nkt = (nkeys + C::KT - 1) / C::KT;
   uint4 rk[C::NCK], rv[C::NCK];
-  tile_load<C, true>(Kg, Vg, sel, nkeys, M, 0, tid, rk, rv);
+  tile_load<C, true>(Kg, Vg, sel_st, nk_st, M, 0, tid, rk, rv);
   tile_store<C, true>(lds, 0, tid, vpos, rk, rv);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     // prefetch the next tile (clamped: the last step reloads its own tile)
-    tile_load<C, true>(Kg, Vg, sel, nkeys, M, kt + 1 < nkt ? kt + 1 : kt, tid, rk, rv);
+    tile_load<C, true>(Kg, Vg, sel_st, nk_st, M, kt + 1 < nkt ? kt + 1 : kt, tid, rk, rv);
     const T* Kb = reinterpret_cast<const T*>(lds + (kt & 1) * C::KBYTES);
     const T* Vb = reinterpret_cast<const T*>(lds + 2 * C::KBYTES + (kt & 1) * C::VBYTES);
     if (active) {  // (a wave whose queries are all past the item's end only stages tiles)
@@ -980,8 +984,10 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     __syncthreads();
 
     // ---------------------------------------------------------------- attention
-    const int nkeys = GATHER ? min(max(A.sel_cnt[row], 0), A.cap) : A.M;
-    const int32_t* sel = GATHER ? A.sel_idx + (int64_t)row * A.cap : nullptr;
+    // gathered: this wave's token set (per-head sets: selection row row * H + head)
+    const int64_t srow = GATHER ? (A.heads ? (int64_t)row * C::H + hw : row) : 0;
+    const int nkeys = GATHER ? min(max(A.sel_cnt[srow], 0), A.cap) : A.M;
+    const int32_t* sel = GATHER ? A.sel_idx + srow * A.cap : nullptr;
 
     f32x16 O[2][C::QB];
     float l_run[C::QB];
@@ -1016,16 +1022,37 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       }
     } else {
       // (both variants pass the same barriers, so waves may take different ones)
-      if constexpr (C::TR_V) {
+      if (A.heads) {
+        // per-head sets: this thread stages the columns of head hs (the same head
+        // for all of its chunks), with that head's set; tiles of the largest set
+        constexpr int CPR = C::D / C::EPC;
+        const int hs = ((tid % CPR) * C::EPC) / 64;
+        const int64_t st_row = (int64_t)row * C::H + hs;
+        const int nk_st = min(max(A.sel_cnt[st_row], 0), A.cap);
+        int nmax = 0;
+#pragma unroll
+        for (int h = 0; h < C::H; ++h) nmax = max(nmax, min(max(A.sel_cnt[(int64_t)row * C::H + h], 0), A.cap));
+        const int nkt = (nmax + C::KT - 1) / C::KT;
+        const int32_t* sel_st = A.sel_idx + st_row * A.cap;
+        if (shift)
+          gathered_attention<C, true>(Kg, Vg, sel_st, nk_st, nkeys, nkt, A.M, tid, lane, hw, lds, vpos, active, qf, nb,
+                                      O, l_run);
+        else
+          gathered_attention<C, false>(Kg, Vg, sel_st, nk_st, nkeys, nkt, A.M, tid, lane, hw, lds, vpos, active, qf,
+                                       nb, O, l_run);
+      } else if constexpr (C::TR_V) {
         if (shift)
           gathered_attention_pipe<C, true>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, active, qf, nb, O, l_run);
         else
           gathered_attention_pipe<C, false>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, active, qf, nb, O, l_run);
       } else {
+        const int nkt = (nkeys + C::KT - 1) / C::KT;
         if (shift)
-          gathered_attention<C, true>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O, l_run);
+          gathered_attention<C, true>(Kg, Vg, sel, nkeys, nkeys, nkt, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O,
+                                      l_run);
         else
-          gathered_attention<C, false>(Kg, Vg, sel, nkeys, A.M, tid, lane, hw, lds, vpos, active, qf, nb, O, l_run);
+          gathered_attention<C, false>(Kg, Vg, sel, nkeys, nkeys, nkt, A.M, tid, lane, hw, lds, vpos, active, qf, nb,
+                                       O, l_run);
       }
     }
 

@@ -16,6 +16,8 @@
 //   cap:    if the union exceeds `cap`, the cap tokens of largest max-over-probes
 //           score (same search; members rank above non-members);
 //   output: ascending compaction of the bitmap.
+// Per-head sets (PH): pass 2 keeps each head's probability as its own score row,
+// and top-k, union, cap and output run per (block, head).
 // Each wave covers 1/8 of the tokens in the passes; partial softmax statistics
 // are merged in a fixed order, so results are reproducible.
 #include <type_traits>
@@ -173,9 +175,9 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
   }
 }
 
-// LDS: [embedding stage] | stats [NW][H][32] float2 | lists [NW][SEL_LIST] | bits [GB][words] |
-//      bits2 [GB][words] | cnt [GB]
-template <typename T, int H>
+// LDS: [embedding stage] | stats [NW][H][32] float2 | lists [NW][SEL_LIST] | bits [GB*NS][words] |
+//      bits2 [GB*NS][words] | cnt [GB*NS]   (NS sets per block: H with per-head sets, else 1)
+template <typename T, int H, int NS>
 struct SelCfg {
   static constexpr int D = 64 * H;
   static constexpr int EMB_END = EmbedLds<T, SEL_BQ, D>::END;
@@ -184,7 +186,7 @@ struct SelCfg {
   static constexpr int BITS = LISTS + SEL_NW * SEL_LIST * 4;
   __host__ __device__ static int total(int M) {
     const int words = (M + 31) / 32;
-    return BITS + 2 * SEL_GB * words * 4 + SEL_GB * 4 + 16;
+    return BITS + 2 * SEL_GB * NS * words * 4 + SEL_GB * NS * 4 + 16;
   }
 };
 
@@ -240,26 +242,27 @@ __device__ __forceinline__ void load_ktile(const SelectArgs& A, __amdgpu_buffer_
   }
 }
 
-template <typename T, int H>
+template <typename T, int H, bool PH>
 __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   extern __shared__ __align__(16) char lds[];
   using MM = Mma<T>;
   using Frag = typename MM::frag;
   using L = EmbedLds<T, SEL_BQ, 64 * H>;
-  using CF = SelCfg<T, H>;
+  constexpr int NS = PH ? H : 1;  // token sets (and score rows per probe) per block
+  using CF = SelCfg<T, H, NS>;
   constexpr int D = 64 * H, KS_H = 64 / MM::KS;
   const int tid0 = threadIdx.x, lane0 = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const int M = A.M, Mp = sel_mpad(M);
   const int nwords = (M + 31) / 32;
   float2* stats = reinterpret_cast<float2*>(lds + CF::STATS);     // [NW][H][32]
-  unsigned* bits = reinterpret_cast<unsigned*>(lds + CF::BITS);    // [GB][nwords]
-  unsigned* bits2 = bits + SEL_GB * nwords;                        // [GB][nwords]
-  int* ucount = reinterpret_cast<int*>(bits2 + SEL_GB * nwords);   // [GB]
-  float* scores = A.scores + (int64_t)blockIdx.x * SEL_BQ * Mp;    // [BQ][Mp], this workgroup's rows
+  unsigned* bits = reinterpret_cast<unsigned*>(lds + CF::BITS);        // [GB][NS][nwords]
+  unsigned* bits2 = bits + SEL_GB * NS * nwords;                       // [GB][NS][nwords]
+  int* ucount = reinterpret_cast<int*>(bits2 + SEL_GB * NS * nwords);  // [GB][NS]
+  float* scores = A.scores + (int64_t)blockIdx.x * SEL_BQ * NS * Mp;   // [BQ][NS][Mp], this workgroup's rows
   unsigned* wlist = reinterpret_cast<unsigned*>(lds + CF::LISTS) + wave * SEL_LIST;  // this wave's top-k list
   const __amdgpu_buffer_rsrc_t sbuf =
-      __builtin_amdgcn_make_buffer_rsrc(scores, (short)0, SEL_BQ * Mp * 4, 0x00020000 /* raw buffer */);
+      __builtin_amdgcn_make_buffer_rsrc(scores, (short)0, SEL_BQ * NS * Mp * 4, 0x00020000 /* raw buffer */);
   const int64_t nblk = A.d_n_blocks ? (int64_t)*A.d_n_blocks : A.n_blocks;
   const int64_t ngroups = (nblk + SEL_GB - 1) / SEL_GB;
   const __amdgpu_buffer_rsrc_t kbuf =
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       }
       if (lane < 32) stats[(wave * H + h) * 32 + lane] = make_float2(m[h], l[h]);
     }
-    for (int i = tid; i < 2 * SEL_GB * nwords; i += SEL_NT) bits[i] = 0u;
+    for (int i = tid; i < 2 * SEL_GB * NS * nwords; i += SEL_NT) bits[i] = 0u;
     __syncthreads();
     float mf[H], linv[H];
 #pragma unroll
@@ -367,51 +370,66 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       linv[h] = 1.f / ll;
     }
 
-    // ---------------------------------------------------------------- pass 2: head-mean probabilities
+    // ---------------------------------------------------------------- pass 2: head-mean (or per-head) probabilities
     lane = opaque(lane);
     col = lane & 31;
     auto score_tile = [&](const KTile<T, H>& t, int kb) {
       float acc[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      const bool full = kb * 32 + 32 <= M;  // (uniform)
 #pragma unroll
       for (int h = 0; h < H; ++h) {
         f32x16 S = zero16();
 #pragma unroll
         for (int ks = 0; ks < KS_H; ++ks)
           S = MM::mma(t.f[h][ks], *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
+        if constexpr (PH) {
+          // this head's probability is the score row (probe col, head h)
+          if (col < nb * SEL_NP) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[r] += __builtin_amdgcn_exp2f(S[r] * 0.18033688011112042f - mf[h]) * linv[h];
+            for (int r = 0; r < 16; ++r) {
+              const int j = kb * 32 + crow(r, lane);
+              if (full || j < M)
+                scores[(col * NS + h) * Mp + j] = __builtin_amdgcn_exp2f(S[r] * 0.18033688011112042f - mf[h]) * linv[h];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[r] += __builtin_amdgcn_exp2f(S[r] * 0.18033688011112042f - mf[h]) * linv[h];
+        }
       }
-      if (col < nb * SEL_NP) {
-        const bool full = kb * 32 + 32 <= M;  // (uniform)
+      if constexpr (!PH) {
+        if (col < nb * SEL_NP) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kb * 32 + crow(r, lane);
-          if (full || j < M) scores[col * Mp + j] = acc[r] * (1.f / H);
+          for (int r = 0; r < 16; ++r) {
+            const int j = kb * 32 + crow(r, lane);
+            if (full || j < M) scores[col * Mp + j] = acc[r] * (1.f / H);
+          }
         }
       }
     };
     over_key_tiles(score_tile);
     __syncthreads();  // the scores rows are complete and visible to the workgroup
 
-    // ---------------------------------------------------------------- top-k per probe, union per block
+    // ---------------------------------------------------------------- top-k per probe (and head), union per set
     tid = opaque(tid);
     lane = opaque(lane);
-    for (int p = wave; p < nb * SEL_NP; p += SEL_NW) {
+    for (int p = wave; p < nb * SEL_NP * NS; p += SEL_NW) {
+      // score row p = probe * NS + head; set (probe / NP) * NS + head
       unsigned u[SEL_MAXV];
       load_scores(sbuf, p, Mp, M, lane, u);
-      topk_bits(u, M, A.k, bits + (p / SEL_NP) * nwords, wlist, lane);
+      topk_bits(u, M, A.k, bits + ((p / NS) / SEL_NP * NS + p % NS) * nwords, wlist, lane);
     }
     __syncthreads();
 
-    // ---------------------------------------------------------------- cap, compaction (one wave per block)
+    // ---------------------------------------------------------------- cap, compaction (one wave per set)
     tid = opaque(tid);
     lane = opaque(lane);
-    if (wave < nb) {
-      const int blk = wave;
-      unsigned* ub = bits + blk * nwords;
+    for (int set = wave; set < nb * NS; set += SEL_NW) {
+      const int blk = set / NS, hs = set % NS;
+      unsigned* ub = bits + set * nwords;
       int cnt = 0;
       for (int i = lane; i < nwords; i += 64) cnt += __popc(ub[i]);
       cnt = wave_sum(cnt);
@@ -419,9 +437,9 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       if (cnt > A.cap) {
         // keep the cap tokens of largest max-over-probes score (members rank above non-members)
         unsigned u[SEL_MAXV];
-        load_scores(sbuf, blk * SEL_NP, Mp, M, lane, u);
+        load_scores(sbuf, (blk * SEL_NP) * NS + hs, Mp, M, lane, u);
         for (int q = 1; q < SEL_NP; ++q) {
-          const int voff = ((blk * SEL_NP + q) * Mp + lane) * 4;
+          const int voff = (((blk * SEL_NP + q) * NS + hs) * Mp + lane) * 4;
 #pragma unroll
           for (int i = 0; i < SEL_MAXV; ++i)  // scores >= 0: bit order is float order
             u[i] = max(u[i], __builtin_amdgcn_raw_buffer_load_b32(sbuf, voff, i * 256, 0));
@@ -432,10 +450,10 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
           const bool member = idx < M && ((ub[idx >> 5] >> (idx & 31)) & 1u);
           u[i] = member ? u[i] + 1u : 0u;
         }
-        topk_bits(u, M, A.cap, bits2 + blk * nwords, wlist, lane);
-        outbits = bits2 + blk * nwords;
+        topk_bits(u, M, A.cap, bits2 + set * nwords, wlist, lane);
+        outbits = bits2 + set * nwords;
       }
-      const int64_t row = row0 + blk;
+      const int64_t row = (row0 + blk) * NS + hs;  // output row: [block][head] with per-head sets
       int32_t* out = A.sel_idx + row * (int64_t)A.cap;
       int base = 0;
       for (int w0 = 0; w0 < nwords; w0 += 64) {
@@ -454,22 +472,22 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       for (int i = base + lane; i < A.cap; i += 64) out[i] = -1;
       if (lane == 0) {
         A.sel_cnt[row] = base;
-        ucount[blk] = base;
+        ucount[set] = base;
       }
     }
     __syncthreads();
     if (tid == 0 && A.stat_selected) {
       int64_t t = 0;
-      for (int b = 0; b < nb; ++b) t += ucount[b];
+      for (int b = 0; b < nb * NS; ++b) t += ucount[b];
       atomicAdd((unsigned long long*)A.stat_selected, (unsigned long long)t);
     }
   }
 }
 
-template <typename T, int H>
+template <typename T, int H, bool PH>
 static hipError_t run_select(const SelectArgs& a, hipStream_t s) {
-  const int lds = SelCfg<T, H>::total(a.M);
-  const void* fn = reinterpret_cast<const void*>(&select_kernel<T, H>);
+  const int lds = SelCfg<T, H, PH ? H : 1>::total(a.M);
+  const void* fn = reinterpret_cast<const void*>(&select_kernel<T, H, PH>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   int64_t grid = dev_info().cus;
@@ -479,16 +497,20 @@ static hipError_t run_select(const SelectArgs& a, hipStream_t s) {
     if (groups < grid) grid = groups;
   }
   if (grid < 1) return hipSuccess;
-  hipLaunchKernelGGL((select_kernel<T, H>), dim3((unsigned)grid), dim3(SEL_NT), lds, s, a);
+  hipLaunchKernelGGL((select_kernel<T, H, PH>), dim3((unsigned)grid), dim3(SEL_NT), lds, s, a);
   return hipGetLastError();
 }
 
-size_t select_scratch_bytes(int M) { return (size_t)SEL_GRID_MAX * SEL_BQ * sel_mpad(M) * sizeof(float); }
+size_t select_scratch_bytes(int M, int sets) {
+  return (size_t)SEL_GRID_MAX * SEL_BQ * sets * sel_mpad(M) * sizeof(float);
+}
 
 hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s) {
   if (a.M > SEL_MAXV * 64) return hipErrorInvalidValue;
-  if (dtype == VDM_BF16) return a.D == 256 ? run_select<bf16, 4>(a, s) : run_select<bf16, 1>(a, s);
-  return run_select<float, 1>(a, s);
+  if (dtype == VDM_BF16 && a.D == 256) return a.per_head ? run_select<bf16, 4, true>(a, s) : run_select<bf16, 4, false>(a, s);
+  // (one head: its per-head set is the head-mean set)
+  if (dtype == VDM_BF16) return run_select<bf16, 1, false>(a, s);
+  return run_select<float, 1, false>(a, s);
 }
 
 }  // namespace vdm

@@ -187,10 +187,12 @@ static DecodeArgs base_args(const vdm_decoder* d) {
 
 static int64_t mpad(int64_t M) { return (M + 31) / 32 * 32; }
 
-// KV selection scratch: per-workgroup score rows, then (bf16) the packed K
-static size_t select_ws_bytes(const vdm_decoder* d, int64_t M) {
+// KV selection scratch: per-workgroup score rows (H rows per probe with per-head
+// sets), then (bf16) the packed K
+static int sel_sets(const vdm_decoder* d, bool heads) { return heads ? d->H : 1; }
+static size_t select_ws_bytes(const vdm_decoder* d, int64_t M, bool heads = false) {
   const size_t kp = d->dtype == VDM_BF16 ? (size_t)mpad(M) * d->D * 2 : 0;
-  return (select_scratch_bytes((int)M) + 255) / 256 * 256 + kp + 256;
+  return (select_scratch_bytes((int)M, sel_sets(d, heads)) + 255) / 256 * 256 + kp + 256;
 }
 
 // bf16 decoders stream Wo, W1, W2 in fragment-packed form from the workspace
@@ -314,9 +316,10 @@ static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M,
   x.items = c.take<Item>((size_t)maxNB3 * ((512 + bq - 1) / bq) * sizeof(Item));
   x.occ = c.take<int32_t>((size_t)maxNB3 * 4);
   if (p->use_kvsel) {
-    x.sel_idx = c.take<int32_t>((size_t)maxNB3 * p->cap * 4);
-    x.sel_cnt = c.take<int32_t>((size_t)maxNB3 * 4);
-    x.sel_scores = c.take<float>(select_scratch_bytes((int)M));
+    const int ns = sel_sets(d, p->heads != 0);
+    x.sel_idx = c.take<int32_t>((size_t)maxNB3 * ns * p->cap * 4);
+    x.sel_cnt = c.take<int32_t>((size_t)maxNB3 * ns * 4);
+    x.sel_scores = c.take<float>(select_scratch_bytes((int)M, ns));
   }
   x.stats = c.take<int64_t>((size_t)VDM_MAX_LEVELS * VDM_STAT_FIELDS * 8);
   x.part = c.take<int64_t>((size_t)stat_part_words() * 8);
@@ -338,6 +341,7 @@ static vdm_status check_hier(const vdm_decoder* d, const vdm_hier_params* p, int
     if (p->k < 1 || p->k > M || p->cap < p->k) return fail(VDM_ERR_INVALID_ARG, "k=%d cap=%d M=%lld", p->k, p->cap, (long long)M);
     if (M > 4096) return fail(VDM_ERR_UNSUPPORTED, "KV selection supports M <= 4096");
     if (p->probes != 0 && p->probes != 1) return fail(VDM_ERR_INVALID_ARG, "probes=%d (0: corners, 1: random)", p->probes);
+    if (p->heads != 0 && p->heads != 1) return fail(VDM_ERR_INVALID_ARG, "heads=%d (0: one set per block, 1: per head)", p->heads);
   }
   (void)d;
   return VDM_OK;
@@ -403,6 +407,15 @@ size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M) {
     return 0;
   }
   return select_ws_bytes(dec, M);
+}
+
+size_t vdm_select_heads_workspace_size(const vdm_decoder* dec, int64_t M) {
+  if (check_decoder(dec) != VDM_OK) return 0;
+  if (M < 1 || M > 4096) {
+    fail(VDM_ERR_INVALID_ARG, "M=%lld (1..4096)", (long long)M);
+    return 0;
+  }
+  return select_ws_bytes(dec, M, true);
 }
 
 size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* params, int64_t M) {
@@ -605,8 +618,8 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
   if (st != VDM_OK || done) return st;
   if (sel) {
     if (q->mode != VDM_Q_GRID_LIST) return fail(VDM_ERR_INVALID_ARG, "token selection needs grid-list queries");
-    if (sel->block < 1 || sel->cap < 1 || !sel->sel_idx || !sel->sel_cnt)
-      return fail(VDM_ERR_INVALID_ARG, "bad kvsel (block=%d cap=%d)", sel->block, sel->cap);
+    if (sel->block < 1 || sel->cap < 1 || !sel->sel_idx || !sel->sel_cnt || (sel->heads != 0 && sel->heads != 1))
+      return fail(VDM_ERR_INVALID_ARG, "bad kvsel (block=%d cap=%d heads=%d)", sel->block, sel->cap, sel->heads);
   }
   const size_t need = dense_ws(dec, M, q->N, sel != nullptr, nullptr, nullptr);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
@@ -639,6 +652,7 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
     a.sel_idx = sel->sel_idx;
     a.sel_cnt = sel->sel_cnt;
     a.cap = sel->cap;
+    a.heads = sel->heads;
     VDM_HIP_T(VDM_TIME_DECODE_GATHERED, s, launch_decode(dec->dtype, dec->D, true, a, s), "gathered decode launch");
   }
   return VDM_OK;
@@ -728,9 +742,12 @@ vdm_status vdm_decode_dense_batch(const vdm_decoder* dec, const vdm_queries* q, 
   return VDM_OK;
 }
 
-vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, int32_t probes,
-                         uint64_t seed, const void* K, int64_t M, const int32_t* blocks, int64_t nblk, int32_t* sel_idx,
-                         int32_t* sel_cnt, void* ws, size_t ws_bytes, vdm_stream stream) {
+}  // extern "C"
+
+static vdm_status select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, int32_t probes,
+                            uint64_t seed, const void* K, int64_t M, const int32_t* blocks, int64_t nblk,
+                            int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes, vdm_stream stream,
+                            bool heads) {
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;
   if (R < 1 || R > 1200 || block < 1) return fail(VDM_ERR_INVALID_ARG, "R=%d block=%d", R, block);
@@ -742,12 +759,12 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
     return fail(VDM_ERR_INVALID_ARG, "nblk=%lld (all blocks: %lld)", (long long)nblk, (long long)(NB * NB * NB));
   if (nblk == 0) return VDM_OK;
   if (!K || !sel_idx || !sel_cnt || !aligned(K, 16)) return fail(VDM_ERR_INVALID_ARG, "K, sel_idx or sel_cnt NULL/misaligned");
-  const size_t need = select_ws_bytes(dec, M);
+  const size_t need = select_ws_bytes(dec, M, heads);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(VDM_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  char* kp = static_cast<char*>(ws) + (select_scratch_bytes((int)M) + 255) / 256 * 256;
+  char* kp = static_cast<char*>(ws) + (select_scratch_bytes((int)M, sel_sets(dec, heads)) + 255) / 256 * 256;
   if (dec->dtype == VDM_BF16)
     VDM_HIP(launch_pack_kv(dec->dtype, K, nullptr, (int)M, dec->D, (int)mpad(M), kp, nullptr, s), "pack K launch");
   SelectArgs a;
@@ -769,9 +786,28 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
   a.scores = (float*)ws;
+  a.per_head = heads ? 1 : 0;
   VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, a, s), "select launch");
   return VDM_OK;
 }
+
+extern "C" {
+
+vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, int32_t probes,
+                         uint64_t seed, const void* K, int64_t M, const int32_t* blocks, int64_t nblk, int32_t* sel_idx,
+                         int32_t* sel_cnt, void* ws, size_t ws_bytes, vdm_stream stream) {
+  return select_kv(dec, R, block, k, cap, probes, seed, K, M, blocks, nblk, sel_idx, sel_cnt, ws, ws_bytes, stream,
+                   false);
+}
+
+vdm_status vdm_select_kv_heads(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,
+                               int32_t probes, uint64_t seed, const void* K, int64_t M, const int32_t* blocks,
+                               int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes,
+                               vdm_stream stream) {
+  return select_kv(dec, R, block, k, cap, probes, seed, K, M, blocks, nblk, sel_idx, sel_cnt, ws, ws_bytes, stream,
+                   true);
+}
+
 
 vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, const void* K, const void* V, int64_t M,
                            float* vol, int64_t vol_elems, int64_t* stats, const vdm_hier_debug* dbg, void* ws,
@@ -834,6 +870,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       sa.sel_cnt = w.sel_cnt;
       sa.stat_selected = S + L * VDM_STAT_FIELDS + VDM_STAT_SELECTED;
       sa.scores = w.sel_scores;
+      sa.per_head = p->heads;
       VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, sa, s), "select launch");
     }
     DecodeArgs a = packed;
@@ -850,6 +887,7 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       a.sel_idx = w.sel_idx;
       a.sel_cnt = w.sel_cnt;
       a.cap = p->cap;
+      a.heads = p->heads;
     } else {
       a.Kp = w.Kp;
       a.Vt = w.Vt;
@@ -886,10 +924,12 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
       if (dbg->list[L]) VDM_HIP(hipMemcpyAsync(dbg->list[L], w.list, p3 * 4, hipMemcpyDeviceToDevice, s), "debug copy");
       if (kv && dbg->sel_blocks[L])
         VDM_HIP(hipMemcpyAsync(dbg->sel_blocks[L], w.occ, nb3 * 4, hipMemcpyDeviceToDevice, s), "debug copy");
+      const int64_t ns = kv && p->heads ? dec->H : 1;
       if (kv && dbg->sel_cnt[L])
-        VDM_HIP(hipMemcpyAsync(dbg->sel_cnt[L], w.sel_cnt, nb3 * 4, hipMemcpyDeviceToDevice, s), "debug copy");
+        VDM_HIP(hipMemcpyAsync(dbg->sel_cnt[L], w.sel_cnt, nb3 * ns * 4, hipMemcpyDeviceToDevice, s), "debug copy");
       if (kv && dbg->sel_idx[L])
-        VDM_HIP(hipMemcpyAsync(dbg->sel_idx[L], w.sel_idx, nb3 * p->cap * 4, hipMemcpyDeviceToDevice, s), "debug copy");
+        VDM_HIP(hipMemcpyAsync(dbg->sel_idx[L], w.sel_idx, nb3 * ns * p->cap * 4, hipMemcpyDeviceToDevice, s),
+                "debug copy");
     }
     if (L == p->levels - 1) break;
     // kept = active dilated `dilation` times (ping-pong through tmp)

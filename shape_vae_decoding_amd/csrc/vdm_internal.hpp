@@ -69,6 +69,7 @@ struct DecodeArgs {
   const int32_t* sel_idx;
   const int32_t* sel_cnt;
   int cap;
+  int heads;  // gathered: 1 = per-head sets (row r's set for head h is selection row r * H + h)
   // dense batch of vecsets (0 or 1: one): tile t belongs to shape t / tiles-per-shape,
   // whose packed K/V start kv_stride bytes after the previous shape's, kmax at
   // [shape][H], and outputs at out + shape * out_stride
@@ -122,10 +123,11 @@ struct SelectArgs {
   int32_t* sel_idx;
   int32_t* sel_cnt;
   int64_t* stat_selected;  // optional: += sum of sel_cnt
-  float* scores;           // scratch of select_scratch_bytes(M)
+  float* scores;           // scratch of select_scratch_bytes(M, per_head ? H : 1)
+  int per_head;            // 1: one set per (block, head), rows [block][H]; 0: one per block
 };
 hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s);
-size_t select_scratch_bytes(int M);
+size_t select_scratch_bytes(int M, int sets);
 
 // ------------------------------------------------------------------ local KNN decoder
 // Supports are bucketed into LOCAL_G^3 cells over [-1, 1]^3.

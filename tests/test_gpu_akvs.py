@@ -400,3 +400,137 @@ def test_gathered_decode_list_outside_preconditions():
     assert np.array_equal(out[802:], ref[100:300])
     assert np.all(np.isfinite(out0))
     print("[guard] out-of-grid entries NaN, 700 repeated entries decoded, empty set finite", flush=True)
+
+
+# ---------------------------------------------------------------- per-head token sets
+
+def run_select_heads(dec, w, K, R, blocks, k, cap, block=8):
+    nb = len(blocks)
+    sel_idx = torch.empty((nb, w.H, cap), dtype=torch.int32, device=dev())
+    sel_cnt = torch.empty((nb, w.H), dtype=torch.int32, device=dev())
+    bt = torch.from_numpy(np.asarray(blocks, np.int32)).to(dev())
+    V().vdm_select_kv(dec, R, block, k, cap, K, bt, sel_idx, sel_cnt, heads=True)
+    torch.cuda.synchronize()
+    return sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
+
+
+def compare_sets_heads(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt, block=8):
+    Qp = gpu_probe_q(dec, w, R, blocks, block)
+    Kh = f64(K)
+    n_amb, differ = 0, 0
+    for r, b in enumerate(blocks):
+        sc = oak.probe_scores_per_head(Qp[r], Kh, w.H)
+        ref_sets = [oak.select(sc[h], k, cap) for h in range(w.H)]
+        for h in range(w.H):
+            got = sel_idx[r, h, : sel_cnt[r, h]]
+            assert np.all(np.diff(got) > 0) and np.all(sel_idx[r, h, sel_cnt[r, h]:] == -1)
+            sym = np.setxor1d(ref_sets[h], got)
+            if sym.size:
+                amb = oak.near_tie_tokens(sc[h], k, cap)
+                n_amb += sym.size
+                assert np.all(np.isin(sym, amb)), (b, h, sym)
+        differ += any(not np.array_equal(ref_sets[0], ref_sets[h]) for h in range(1, w.H))
+    print(f"[parity] per-head selection R={R} k={k} cap={cap}: {len(blocks)} blocks x {w.H} heads, "
+          f"{n_amb} near-tie tokens differ; heads' sets differ in {differ} blocks", flush=True)
+    return differ
+
+
+@pytest.mark.parametrize("R,k,cap", [(75, 64, 512), (75, 64, 100), (150, 32, 512)])
+def test_select_per_head_matches_oracle(R, k, cap):
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    K, _ = gpu_kv(dec, w)
+    nb = hv.nblocks(R + 1)
+    blocks = np.sort(np.random.default_rng(R + k + cap + 7).choice(nb ** 3, 40, replace=False))
+    blocks = np.unique(np.concatenate([blocks, [0, nb ** 3 - 1]]))
+    sel_idx, sel_cnt = run_select_heads(dec, w, K, R, blocks, k, cap)
+    assert np.all(sel_cnt <= cap) and np.all(sel_cnt >= k)
+    if cap == 100:
+        assert np.all(sel_cnt == 100)
+    assert compare_sets_heads(dec, w, K, R, blocks, k, cap, sel_idx, sel_cnt) > 0
+
+
+def test_gathered_decode_per_head_sets():
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    R = 30
+    nb = hv.nblocks(R + 1)
+    sel_idx = torch.empty((nb ** 3, w.H, 512), dtype=torch.int32, device=dev())
+    sel_cnt = torch.empty((nb ** 3, w.H), dtype=torch.int32, device=dev())
+    V().vdm_select_kv(dec, R, 8, 64, 512, K, None, sel_idx, sel_cnt, heads=True)
+    lst = hv.blocked_order(np.ones((R + 1,) * 3, bool)).astype(np.int32)
+    out = torch.empty(lst.size, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_list(R, torch.from_numpy(lst).to(dev())), K, Vv, out,
+                         sel=V().kvsel(8, 512, sel_idx, sel_cnt, heads=True))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    si, sc = sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
+    od = oracle_decoder(w)
+    Kh, Vh = f64(K), f64(Vv)
+    blk = hv.block_of(lst, R + 1)
+    worst = 0.0
+    for b in range(nb ** 3):
+        m = np.nonzero(blk == b)[0]
+        m = m[tile_sample(m.size, DECODE_TILE)]
+        sets = [si[b, h, : sc[b, h]] for h in range(w.H)]
+        ref = oak.sdf_per_head_sets(od, odec.grid_points(R, lst[m]), sets, Kh, Vh)
+        worst = max(worst, np.abs(out[m].astype(np.float64) - ref).max())
+    report("gathered decode with per-head sets vs per-head restricted attention (every work item)", worst, TOL_BF16)
+    assert worst <= TOL_BF16
+
+
+def test_hier_with_per_head_sets_full_workload():
+    # the 75 -> 150 -> 300 workload with one token set per (block, head) at every level
+    w = W.make(3)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    q = w.query
+    kv = dict(q["kvsel"], heads=True)
+    params = V().hier_params(R0=q["R0"], levels=q["levels"], tau=q["tau"], dilation=q["dilation"], kvsel=kv)
+    levels = params.levels
+    vol = torch.empty(301 ** 3, dtype=torch.float32, device=dev())
+    stats = torch.zeros(levels * V().STAT_FIELDS, dtype=torch.int64, device=dev())
+    dbg = V().HierDebug(params, with_sel=True, H=w.H)
+    V().vdm_decode_hier(dec, params, K, Vv, vol, stats, dbg)
+    dense = torch.empty(301 ** 3, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_grid(300), K, Vv, dense)
+    torch.cuda.synchronize()
+    st = V().stats_dict(stats, levels)
+    od = oracle_decoder(w)
+    Kh, Vh = f64(K), f64(Vv)
+    rng = np.random.default_rng(9)
+    cap = kv["cap"]
+    for L in range(levels):
+        R = 75 << L
+        s = st[L]
+        d = dbg.levels[L]
+        nocc = s["blocks"]
+        blocks = d["sel_blocks"][:nocc].cpu().numpy()
+        cnt = d["sel_cnt"][: nocc * w.H].cpu().numpy().reshape(nocc, w.H)
+        idx = d["sel_idx"][: nocc * w.H * cap].cpu().numpy().reshape(nocc, w.H, cap)
+        assert s["selected"] == int(cnt.sum())
+        print(f"[akvs heads] R={R}: {nocc} blocks, mean selected per head {cnt.mean():.1f} tokens", flush=True)
+        pick = np.sort(rng.choice(nocc, min(nocc, 20), replace=False))
+        compare_sets_heads(dec, w, K, R, blocks[pick], kv["k"], cap, idx[pick], cnt[pick])
+        lst = d["list"][: s["queries"]].cpu().numpy().astype(np.int64)
+        volL = d["vol"].cpu().numpy()
+        blk = hv.block_of(lst, R + 1)
+        starts = np.searchsorted(blk, blocks)
+        ends = np.searchsorted(blk, blocks, side="right")
+        worst, n_items = 0.0, 0
+        for r in range(nocc):
+            m = lst[starts[r]:ends[r]][tile_sample(ends[r] - starts[r], DECODE_TILE)]
+            n_items += m.size
+            sets = [idx[r, h, : cnt[r, h]] for h in range(w.H)]
+            ref = oak.sdf_per_head_sets(od, odec.grid_points(R, m), sets, Kh, Vh)
+            worst = max(worst, np.abs(volL[m].astype(np.float64) - ref).max())
+        assert n_items == s["items"]
+        report(f"per-head selection level {L}: one point per work item ({n_items})", worst, TOL_BF16)
+        assert worst <= TOL_BF16
+    vol_np, dense_np = vol.cpu().numpy(), dense.cpu().numpy()
+    flips = int(np.sum((vol_np < 0) != (dense_np < 0)))
+    inter = np.sum((vol_np < 0) & (dense_np < 0))
+    union = np.sum((vol_np < 0) | (dense_np < 0))
+    print(f"[akvs heads] per-head sets vs dense: sign flips {flips}; occupancy IoU {inter / union:.5f}", flush=True)
