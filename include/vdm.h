@@ -289,22 +289,19 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* params
                            vdm_stream stream);
 
 /* Hierarchical decoding of a batch of B vecsets (shapes) with the same params:
- * shape b runs vdm_decode_hier on K, V at byte offset b * M * D * element size
- * (which must keep 16-byte alignment), writes vol + b * (R+1)^3 (R the finest
- * grid; vol_elems covers all B volumes) and, when stats is not NULL, stats +
- * b * levels * VDM_STAT_FIELDS, with workspace slice b of
- * vdm_hier_batch_workspace_size(dec, params, B, M) / B bytes. Shape b is
- * enqueued on streams[b % n_streams] (1 <= n_streams <= 64), so the small
- * bookkeeping launches of shapes on different streams overlap. The library
- * creates no streams or events: the caller orders its streams around the call
- * (everything the batch reads must be ready on every stream it names, and the
- * results are complete once every named stream has finished its part).
- * Shape b's volume and counters equal, bit for bit, those of vdm_decode_hier on
- * that shape alone. No inspection outputs. Requires 1 <= B <= 4096. */
+ * shape b runs the level loop of vdm_decode_hier on K, V at byte offset
+ * b * M * D * element size (which must keep 16-byte alignment), writes
+ * vol + b * (R+1)^3 (R the finest grid; vol_elems covers all B volumes) and, when
+ * stats is not NULL, stats + b * levels * VDM_STAT_FIELDS, with workspace slice b
+ * of vdm_hier_batch_workspace_size(dec, params, B, M) / B bytes. Every mask stage
+ * of a level (cell test, dilation, marking, scans, list emission, fill) is one
+ * launch for all B shapes; each level's decode (and KV selection) is one launch
+ * per shape. Shape b's volume and counters equal, bit for bit, those of
+ * vdm_decode_hier on that shape alone. No inspection outputs. Requires
+ * 1 <= B <= 4096. */
 vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* params, int32_t B,
                                  const void* K, const void* V, int64_t M, float* vol, int64_t vol_elems,
-                                 int64_t* stats, void* ws, size_t ws_bytes, const vdm_stream* streams,
-                                 int32_t n_streams);
+                                 int64_t* stats, void* ws, size_t ws_bytes, vdm_stream stream);
 
 /* Surface extraction: the stage that follows VAE decoding in a vecset diffusion
  * pipeline (techwalker article on FlashVDM, part 1, the four stages). The pages

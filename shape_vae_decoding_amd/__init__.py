@@ -134,7 +134,7 @@ _lib.vdm_dense_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int32, 
 _lib.vdm_dense_batch_workspace_size.restype = C.c_size_t
 _lib.vdm_decode_hier_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_void_p,
                                        C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
-                                       C.c_size_t, C.POINTER(C.c_void_p), C.c_int32]
+                                       C.c_size_t, C.c_void_p]
 _lib.vdm_decode_hier_batch.restype = _st
 _lib.vdm_hier_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_int64]
 _lib.vdm_hier_batch_workspace_size.restype = C.c_size_t
@@ -513,25 +513,11 @@ def vdm_hier_batch_workspace_size(dec: Decoder, params: _HierParams, B: int, M: 
     return n
 
 
-_SIDE_STREAMS: Dict[int, list] = {}
-
-
-def _side_streams(device: torch.device, n: int) -> list:
-    """n streams of the device (default priority), created once and reused."""
-    idx = device.index if device.index is not None else torch.cuda.current_device()
-    have = _SIDE_STREAMS.setdefault(idx, [])
-    while len(have) < n:
-        have.append(torch.cuda.Stream(device=idx))
-    return have[:n]
-
-
 def vdm_decode_hier_batch(dec: Decoder, params: _HierParams, K: torch.Tensor, V: torch.Tensor, vol: torch.Tensor,
                           stats: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                          stream=None, side_streams: int = 3) -> None:
+                          stream=None) -> None:
     """K, V [B, M, D] in the decoder dtype, vol [B, (R+1)^3] float32, stats
-    [B, levels * VDM_STAT_FIELDS] int64 or None (see include/vdm.h). The shapes
-    run on the call's stream and up to `side_streams` more, forked from it and
-    joined back into it with events, so the whole call is ordered on `stream`."""
+    [B, levels * VDM_STAT_FIELDS] int64 or None (see include/vdm.h)."""
     _dev(K, dec.torch_dtype, "K")
     _dev(V, dec.torch_dtype, "V")
     _dev(vol, torch.float32, "vol")
@@ -547,21 +533,8 @@ def vdm_decode_hier_batch(dec: Decoder, params: _HierParams, K: torch.Tensor, V:
             raise ValueError("stats must be [B, levels * STAT_FIELDS]")
     if ws is None:
         ws = workspace(vdm_hier_batch_workspace_size(dec, params, B, M), vol.device)
-    main = stream if stream is not None else torch.cuda.current_stream(vol.device)
-    side = _side_streams(vol.device, max(0, min(side_streams, B - 1)))
-    fork = torch.cuda.Event()
-    fork.record(main)
-    for s in side:
-        s.wait_event(fork)
-    arr = (C.c_void_p * (1 + len(side)))(*[x.cuda_stream for x in [main] + side])
-    try:
-        _check(_lib.vdm_decode_hier_batch(dec.ref, C.byref(params), B, K.data_ptr(), V.data_ptr(), M, vol.data_ptr(),
-                                          vol.numel(), _ptr(stats), ws.data_ptr(), ws.numel(), arr, len(arr)))
-    finally:
-        for s in side:  # join every side stream, also after an error
-            j = torch.cuda.Event()
-            j.record(s)
-            main.wait_event(j)
+    _check(_lib.vdm_decode_hier_batch(dec.ref, C.byref(params), B, K.data_ptr(), V.data_ptr(), M, vol.data_ptr(),
+                                      vol.numel(), _ptr(stats), ws.data_ptr(), ws.numel(), _stream(stream)))
 
 
 def vdm_surface_workspace_size(R: int) -> int:

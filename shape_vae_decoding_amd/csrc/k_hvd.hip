@@ -34,27 +34,33 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* red, int ti
   return s;
 }
 
-__global__ void zero_u64_kernel(uint64_t* p, int64_t n) {
+__global__ void zero_u64_kernel(BP<uint64_t> pb, int64_t n) {
+  uint64_t* p = pb.at();
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0ull;
 }
 
-hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+hipError_t launch_zero_b(BP<void> p, size_t bytes, int B, hipStream_t s) {
   const int64_t n = (int64_t)(bytes / 8);
   if (n <= 0) return hipSuccess;
   int64_t g = (n + 255) / 256;
   if (g > 65536) g = 65536;
-  hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)g), dim3(256), 0, s, (uint64_t*)p, n);
+  hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)g, (unsigned)B), dim3(256), 0, s,
+                     BP<uint64_t>{(uint64_t*)p.p, p.stride}, n);
   return hipGetLastError();
 }
 
-__global__ void stats_init_kernel(int64_t* stats, int levels, int R0) {
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) { return launch_zero_b(bp(p), bytes, 1, s); }
+
+__global__ void stats_init_kernel(BP<int64_t> sb, int levels, int R0) {
+  int64_t* stats = sb.at();
   const int i = threadIdx.x;
   if (i < levels * VDM_STAT_FIELDS) stats[i] = (i % VDM_STAT_FIELDS) == VDM_STAT_R ? (int64_t)R0 << (i / VDM_STAT_FIELDS) : 0;
 }
 
-hipError_t launch_stats_init(int64_t* stats, int levels, int R0, hipStream_t s) {
-  hipLaunchKernelGGL(stats_init_kernel, dim3(1), dim3(VDM_MAX_LEVELS * VDM_STAT_FIELDS), 0, s, stats, levels, R0);
+hipError_t launch_stats_init(BP<int64_t> stats, int levels, int R0, int B, hipStream_t s) {
+  hipLaunchKernelGGL(stats_init_kernel, dim3(1, (unsigned)B), dim3(VDM_MAX_LEVELS * VDM_STAT_FIELDS), 0, s, stats,
+                     levels, R0);
   return hipGetLastError();
 }
 
@@ -65,8 +71,12 @@ hipError_t launch_stats_init(int64_t* stats, int levels, int R0, hipStream_t s) 
 // level's stats and clears them for the next use.
 constexpr int STAT_SLOTS = 256;
 
-__global__ __launch_bounds__(STAT_SLOTS) void fold_kernel(int64_t* part, int f0, int nf, int64_t* dst0, int64_t* dst1) {
+__global__ __launch_bounds__(STAT_SLOTS) void fold_kernel(BP<int64_t> pb, int f0, int nf, BP<int64_t> d0,
+                                                          BP<int64_t> d1) {
   __shared__ int64_t red[STAT_SLOTS / 64];
+  int64_t* part = pb.at();
+  int64_t* dst0 = d0.at();
+  int64_t* dst1 = d1.at();
   const int t = threadIdx.x;
   for (int f = 0; f < nf; ++f) {
     const int64_t v = part[t * 8 + f0 + f];
@@ -76,8 +86,9 @@ __global__ __launch_bounds__(STAT_SLOTS) void fold_kernel(int64_t* part, int f0,
   }
 }
 
-static hipError_t launch_fold(int64_t* part, int f0, int nf, int64_t* dst0, int64_t* dst1, hipStream_t s) {
-  hipLaunchKernelGGL(fold_kernel, dim3(1), dim3(STAT_SLOTS), 0, s, part, f0, nf, dst0, dst1);
+static hipError_t launch_fold(BP<int64_t> part, int f0, int nf, BP<int64_t> dst0, BP<int64_t> dst1, int B,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(fold_kernel, dim3(1, (unsigned)B), dim3(STAT_SLOTS), 0, s, part, f0, nf, dst0, dst1);
   return hipGetLastError();
 }
 
@@ -153,10 +164,13 @@ __device__ __forceinline__ void test_cell_block(const float (&v)[9][4], int R, i
 }
 
 template <bool SPARSE>
-__global__ __launch_bounds__(256) void cell_test_kernel(const float* __restrict__ vol, int R, int NB,
-                                                        const uint64_t* __restrict__ kept_prev, int NBp,
-                                                        float tau, uint64_t* __restrict__ active, int64_t* part,
+__global__ __launch_bounds__(256) void cell_test_kernel(BP<const float> vb, int R, int NB, BP<const uint64_t> kb,
+                                                        int NBp, float tau, BP<uint64_t> ab, BP<int64_t> pb,
                                                         int nunits) {
+  const float* __restrict__ vol = vb.at();
+  const uint64_t* __restrict__ kept_prev = kb.at();
+  uint64_t* __restrict__ active = ab.at();
+  int64_t* part = pb.at();
   const int lane = threadIdx.x & 63;
   const int u = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (u >= nunits) return;
@@ -202,12 +216,12 @@ __global__ __launch_bounds__(256) void cell_test_kernel(const float* __restrict_
   }
 }
 
-hipError_t launch_cell_test(const float* vol, int R, const uint64_t* kept_prev, float tau, uint64_t* active,
-                            int64_t* part, int64_t* stat_tested, int64_t* stat_active, hipStream_t s) {
+hipError_t launch_cell_test(BP<const float> vol, int R, BP<const uint64_t> kept_prev, float tau, BP<uint64_t> active,
+                            BP<int64_t> part, BP<int64_t> stat_tested, BP<int64_t> stat_active, int B, hipStream_t s) {
   const int NB = nblocks8(R + 1), NBp = nblocks8(R / 2 + 1), NG = (NB + 1) / 2;
-  const int nunits = kept_prev ? NG * NG * NG : NB * NB * NB;
-  const dim3 grid((unsigned)((nunits + 3) / 4));
-  if (kept_prev)
+  const int nunits = kept_prev.p ? NG * NG * NG : NB * NB * NB;
+  const dim3 grid((unsigned)((nunits + 3) / 4), (unsigned)B);
+  if (kept_prev.p)
     hipLaunchKernelGGL(cell_test_kernel<true>, grid, dim3(256), 0, s, vol, R, NB, kept_prev, NBp, tau, active, part,
                        nunits);
   else
@@ -215,7 +229,7 @@ hipError_t launch_cell_test(const float* vol, int R, const uint64_t* kept_prev, 
                        part, nunits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_fold(part, 0, 2, stat_tested, stat_active, s);
+  return launch_fold(part, 0, 2, stat_tested, stat_active, B, s);
 }
 
 // ------------------------------------------------------------------ dilation
@@ -230,9 +244,11 @@ __device__ __forceinline__ uint64_t dil_j(uint64_t t, uint64_t td, uint64_t tu) 
   return t | (t << 8) | (td >> 56) | (t >> 8) | (tu << 56);
 }
 
-__global__ void dilate_kernel(const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int R, int NB,
-                              int identity, int64_t* part) {
+__global__ void dilate_kernel(BP<const uint64_t> ib, BP<uint64_t> ob, int R, int NB, int identity, BP<int64_t> pb) {
   __shared__ int64_t red[4];
+  const uint64_t* __restrict__ in = ib.at();
+  uint64_t* __restrict__ out = ob.at();
+  int64_t* part = pb.p ? pb.at() : nullptr;
   const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nw = (int64_t)NB * NB * NB * 8;
   uint64_t res = 0;
@@ -279,15 +295,15 @@ __global__ void dilate_kernel(const uint64_t* __restrict__ in, uint64_t* __restr
   }
 }
 
-hipError_t launch_dilate(const uint64_t* in, uint64_t* out, int R, int identity, int64_t* part, int64_t* stat,
-                         hipStream_t s) {
+hipError_t launch_dilate(BP<const uint64_t> in, BP<uint64_t> out, int R, int identity, BP<int64_t> part,
+                         BP<int64_t> stat, int B, hipStream_t s) {
   const int NB = nblocks8(R + 1);
   const int64_t nw = (int64_t)NB * NB * NB * 8;
-  hipLaunchKernelGGL(dilate_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, in, out, R, NB, identity,
-                     stat ? part : nullptr);
+  hipLaunchKernelGGL(dilate_kernel, dim3((unsigned)((nw + 255) / 256), (unsigned)B), dim3(256), 0, s, in, out, R, NB,
+                     identity, stat.p ? part : BP<int64_t>{nullptr, 0});
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !stat) return e;
-  return launch_fold(part, 2, 1, stat, stat, s);
+  if (e != hipSuccess || !stat.p) return e;
+  return launch_fold(part, 2, 1, stat, stat, B, s);
 }
 
 // ------------------------------------------------------------------ child marking
@@ -337,10 +353,13 @@ __device__ __forceinline__ uint64_t cand_from_row(const uint64_t* __restrict__ k
   return U | (((U >> 8) | (U << 8) | (uint64_t)up8(row[0])) & 0x00ff00ff00ff00ffull);
 }
 
-__global__ __launch_bounds__(256) void mark_kernel(const uint64_t* __restrict__ kept, int R,
-                                                   const uint64_t* __restrict__ comp_prev, int all_new,
-                                                   int Rn, uint64_t* __restrict__ newmask,
-                                                   uint64_t* __restrict__ comp_next, int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(256) void mark_kernel(BP<const uint64_t> kb, int R, BP<const uint64_t> cpb, int all_new,
+                                                   int Rn, BP<uint64_t> nmb, BP<uint64_t> cnb, BP<int32_t> cb) {
+  const uint64_t* __restrict__ kept = kb.at();
+  const uint64_t* __restrict__ comp_prev = cpb.p ? cpb.at() : nullptr;
+  uint64_t* __restrict__ newmask = nmb.at();
+  uint64_t* __restrict__ comp_next = cnb.p ? cnb.at() : nullptr;
+  int32_t* __restrict__ counts = cb.at();
   const int NBn = nblocks8(Rn + 1), NB = nblocks8(R + 1);
   const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nw = (int64_t)NBn * NBn * NBn * 8;
@@ -392,12 +411,12 @@ __global__ __launch_bounds__(256) void mark_kernel(const uint64_t* __restrict__ 
   if (w < nw && (w & 7) == 0) counts[w >> 3] = c;
 }
 
-hipError_t launch_mark(const uint64_t* kept, int R, const uint64_t* comp_prev, int all_new, int Rn,
-                       uint64_t* newmask, uint64_t* comp_next, int32_t* counts, hipStream_t s) {
+hipError_t launch_mark(BP<const uint64_t> kept, int R, BP<const uint64_t> comp_prev, int all_new, int Rn,
+                       BP<uint64_t> newmask, BP<uint64_t> comp_next, BP<int32_t> counts, int B, hipStream_t s) {
   const int NBn = nblocks8(Rn + 1);
   const int64_t nw = (int64_t)NBn * NBn * NBn * 8;
-  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, kept, R, comp_prev, all_new,
-                     Rn, newmask, comp_next, counts);
+  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((nw + 255) / 256), (unsigned)B), dim3(256), 0, s, kept, R,
+                     comp_prev, all_new, Rn, newmask, comp_next, counts);
   return hipGetLastError();
 }
 
@@ -428,8 +447,10 @@ __device__ int4 block_excl_scan(int4 v, int4* sh, int tid, int4* total) {
   return make_int4(incl.x - v.x, incl.y - v.y, incl.z - v.z, 0);
 }
 
-__global__ __launch_bounds__(SCAN_NT) void scan_reduce_kernel(const int32_t* counts, int64_t n, int bq, int4* partial) {
+__global__ __launch_bounds__(SCAN_NT) void scan_reduce_kernel(BP<const int32_t> cb, int64_t n, int bq, BP<int4> pb) {
   __shared__ int4 sh[SCAN_NT];
+  const int32_t* counts = cb.at();
+  int4* partial = pb.at();
   const int64_t base = (int64_t)blockIdx.x * SCAN_CHUNK + threadIdx.x * SCAN_PER;
   int4 s = make_int4(0, 0, 0, 0);
   for (int e = 0; e < SCAN_PER; ++e)
@@ -439,8 +460,11 @@ __global__ __launch_bounds__(SCAN_NT) void scan_reduce_kernel(const int32_t* cou
   if (threadIdx.x == 0) partial[blockIdx.x] = tot;
 }
 
-__global__ __launch_bounds__(SCAN_NT) void scan_top_kernel(int4* partial, int np, int32_t* tot, int64_t* stats_level) {
+__global__ __launch_bounds__(SCAN_NT) void scan_top_kernel(BP<int4> pb, int np, BP<int32_t> tb, BP<int64_t> sb) {
   __shared__ int4 sh[SCAN_NT];
+  int4* partial = pb.at();
+  int32_t* tot = tb.at();
+  int64_t* stats_level = sb.p ? sb.at() : nullptr;
   int4 carry = make_int4(0, 0, 0, 0);
   for (int base = 0; base < np; base += SCAN_NT) {
     const int i = base + threadIdx.x;
@@ -462,9 +486,13 @@ __global__ __launch_bounds__(SCAN_NT) void scan_top_kernel(int4* partial, int np
   }
 }
 
-__global__ __launch_bounds__(SCAN_NT) void scan_apply_kernel(const int32_t* counts, int64_t n, int bq,
-                                                             const int4* partial, int4* offs, int32_t* occ) {
+__global__ __launch_bounds__(SCAN_NT) void scan_apply_kernel(BP<const int32_t> cb, int64_t n, int bq,
+                                                             BP<const int4> pb, BP<int4> ob, BP<int32_t> occb) {
   __shared__ int4 sh[SCAN_NT];
+  const int32_t* counts = cb.at();
+  const int4* partial = pb.at();
+  int4* offs = ob.at();
+  int32_t* occ = occb.at();
   const int64_t base = (int64_t)blockIdx.x * SCAN_CHUNK + threadIdx.x * SCAN_PER;
   int4 v[SCAN_PER];
   int4 s = make_int4(0, 0, 0, 0);
@@ -483,13 +511,13 @@ __global__ __launch_bounds__(SCAN_NT) void scan_apply_kernel(const int32_t* coun
   }
 }
 
-hipError_t launch_scan(const int32_t* counts, int64_t n, int bq, int4* partial, int4* offs, int32_t* occ, int32_t* tot,
-                       int64_t* stats_level, hipStream_t s) {
+hipError_t launch_scan(BP<const int32_t> counts, int64_t n, int bq, BP<int4> partial, BP<int4> offs, BP<int32_t> occ,
+                       BP<int32_t> tot, BP<int64_t> stats_level, int B, hipStream_t s) {
   const int np = (int)((n + SCAN_CHUNK - 1) / SCAN_CHUNK);
-  hipLaunchKernelGGL(scan_reduce_kernel, dim3(np), dim3(SCAN_NT), 0, s, counts, n, bq, partial);
-  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(SCAN_NT), 0, s, partial, np, tot, stats_level);
-  hipLaunchKernelGGL(scan_apply_kernel, dim3(np), dim3(SCAN_NT), 0, s, counts, n, bq, (const int4*)partial, offs,
-                     occ);
+  hipLaunchKernelGGL(scan_reduce_kernel, dim3(np, (unsigned)B), dim3(SCAN_NT), 0, s, counts, n, bq, partial);
+  hipLaunchKernelGGL(scan_top_kernel, dim3(1, (unsigned)B), dim3(SCAN_NT), 0, s, partial, np, tot, stats_level);
+  hipLaunchKernelGGL(scan_apply_kernel, dim3(np, (unsigned)B), dim3(SCAN_NT), 0, s, counts, n, bq,
+                     BP<const int4>{partial.p, partial.stride}, offs, occ);
   return hipGetLastError();
 }
 
@@ -500,11 +528,17 @@ hipError_t launch_scan(const int32_t* counts, int64_t n, int bq, int4* partial, 
 // occupied-block row offs.z).
 constexpr int EMIT_NT = 256;
 
-__global__ __launch_bounds__(EMIT_NT) void emit_kernel(const uint64_t* __restrict__ newmask,
-                                                       const int32_t* __restrict__ counts,
-                                                       const int4* __restrict__ offs, const int32_t* __restrict__ occ,
-                                                       const int32_t* __restrict__ tot, int Rn, int bq,
-                                                       int32_t* __restrict__ list, Item* __restrict__ items) {
+__global__ __launch_bounds__(EMIT_NT) void emit_kernel(BP<const uint64_t> nmb, BP<const int32_t> cb,
+                                                       BP<const int4> ob, BP<const int32_t> occb,
+                                                       BP<const int32_t> tb, int Rn, int bq, BP<int32_t> lb,
+                                                       BP<Item> ib) {
+  const uint64_t* __restrict__ newmask = nmb.at();
+  const int32_t* __restrict__ counts = cb.at();
+  const int4* __restrict__ offs = ob.at();
+  const int32_t* __restrict__ occ = occb.at();
+  const int32_t* __restrict__ tot = tb.at();
+  int32_t* __restrict__ list = lb.at();
+  Item* __restrict__ items = ib.at();
   const int NB = nblocks8(Rn + 1);
   const int64_t P = Rn + 1;
   const int lane = threadIdx.x & 63;
@@ -534,15 +568,17 @@ __global__ __launch_bounds__(EMIT_NT) void emit_kernel(const uint64_t* __restric
   }
 }
 
-hipError_t launch_emit(const uint64_t* newmask, const int32_t* counts, const int4* offs, const int32_t* occ,
-                       const int32_t* tot, int Rn, int bq, int32_t* list, Item* items, hipStream_t s) {
+hipError_t launch_emit(BP<const uint64_t> newmask, BP<const int32_t> counts, BP<const int4> offs,
+                       BP<const int32_t> occ, BP<const int32_t> tot, int Rn, int bq, BP<int32_t> list,
+                       BP<Item> items, int B, hipStream_t s) {
   const int NB = nblocks8(Rn + 1);
   const int64_t nb3 = (int64_t)NB * NB * NB;
   int64_t g = (nb3 + EMIT_NT / 64 - 1) / (EMIT_NT / 64);
-  const int64_t cap = (int64_t)dev_info().cus * 8;
+  const int64_t cap = ((int64_t)dev_info().cus * 8 + B - 1) / B;
   if (g > cap) g = cap;
-  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)g), dim3(EMIT_NT), 0, s, newmask, counts, offs, occ, tot, Rn, bq, list,
-                     items);
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)g, (unsigned)B), dim3(EMIT_NT), 0, s, newmask, counts, offs, occ, tot,
+                     Rn, bq, list, items);
   return hipGetLastError();
 }
 
@@ -556,8 +592,9 @@ constexpr int FILL_ROWS = 8;
 constexpr int FILL_NT = 256;
 constexpr int FILL_KI = 5;  // FILL_NT * FILL_KI >= 1201 points per row (finest grid at most 1200 cells)
 
-__global__ __launch_bounds__(FILL_NT) void fill_kernel(const float* __restrict__ prev, int Pp, float* __restrict__ next,
-                                                       int Pn) {
+__global__ __launch_bounds__(FILL_NT) void fill_kernel(BP<const float> pb, int Pp, BP<float> nb, int Pn) {
+  const float* __restrict__ prev = pb.at();
+  float* __restrict__ next = nb.at();
   const int ng = (Pn + FILL_ROWS - 1) / FILL_ROWS;
   const int I = blockIdx.x / ng, J0 = (blockIdx.x % ng) * FILL_ROWS;
   float v[FILL_ROWS / 2][FILL_KI];
@@ -584,10 +621,10 @@ __global__ __launch_bounds__(FILL_NT) void fill_kernel(const float* __restrict__
   }
 }
 
-hipError_t launch_fill(const float* prev, int Pp, float* next, int Pn, hipStream_t s) {
+hipError_t launch_fill(BP<const float> prev, int Pp, BP<float> next, int Pn, int B, hipStream_t s) {
   if (Pn > FILL_NT * FILL_KI) return hipErrorInvalidValue;
   const int64_t g = (int64_t)Pn * ((Pn + FILL_ROWS - 1) / FILL_ROWS);
-  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)g), dim3(FILL_NT), 0, s, prev, Pp, next, Pn);
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)g, (unsigned)B), dim3(FILL_NT), 0, s, prev, Pp, next, Pn);
   return hipGetLastError();
 }
 

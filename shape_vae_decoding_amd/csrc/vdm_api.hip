@@ -423,11 +423,14 @@ size_t vdm_hier_workspace_size(const vdm_decoder* dec, const vdm_hier_params* pa
   return hier_ws(dec, params, M, nullptr, nullptr);
 }
 
+static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int B, const void* K, const void* V,
+                           int64_t M, size_t kv_bytes, float* vol, int64_t vol_stride, int64_t* S, int64_t st_stride,
+                           const vdm_hier_debug* dbg, void* ws, size_t ws_stride, hipStream_t s);
+
 // ------------------------------------------------------------------ batched hierarchical decoding
-// B shapes through the hierarchical pipeline, shape b on the caller's stream
-// b % n_streams: the per-level bookkeeping launches of one shape are too small to
-// fill the chip, those of shapes on different streams run side by side. No host
-// synchronisation, no library-owned streams or events.
+// B shapes through the hierarchical pipeline on one stream: every mask stage of a
+// level is one launch for all B shapes (hier_run), so the small per-level
+// bookkeeping launches are shared instead of repeated per shape.
 namespace {
 size_t hier_batch_stride(const vdm_decoder* dec, const vdm_hier_params* p, int64_t M) {
   return (hier_ws(dec, p, M, nullptr, nullptr) + 255) / 256 * 256;
@@ -445,12 +448,10 @@ size_t vdm_hier_batch_workspace_size(const vdm_decoder* dec, const vdm_hier_para
 
 vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* p, int32_t B, const void* K,
                                  const void* V, int64_t M, float* vol, int64_t vol_elems, int64_t* stats, void* ws,
-                                 size_t ws_bytes, const vdm_stream* streams, int32_t n_streams) {
+                                 size_t ws_bytes, vdm_stream stream) {
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;
   if (B < 1 || B > 4096) return fail(VDM_ERR_INVALID_ARG, "B=%d (1..4096)", B);
-  if (!streams || n_streams < 1 || n_streams > 64)
-    return fail(VDM_ERR_INVALID_ARG, "streams NULL or n_streams=%d outside 1..64", n_streams);
   st = check_hier(dec, p, M);
   if (st != VDM_OK) return st;
   const int64_t Pf = ((int64_t)p->R0 << (p->levels - 1)) + 1, P3 = Pf * Pf * Pf;
@@ -461,13 +462,13 @@ vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* 
   const size_t stride = hier_batch_stride(dec, p, M);
   if (!ws || ws_bytes / (size_t)B < stride || !aligned(ws, 256))
     return fail(VDM_ERR_WORKSPACE, "workspace needs %d x %zu bytes, 256-aligned (got %zu)", B, stride, ws_bytes);
-  for (int b = 0; b < B; ++b) {
-    st = vdm_decode_hier(dec, p, (const char*)K + b * kv_bytes, (const char*)V + b * kv_bytes, M, vol + b * P3, P3,
-                         stats ? stats + (int64_t)b * p->levels * VDM_STAT_FIELDS : nullptr, nullptr,
-                         (char*)ws + b * stride, stride, streams[b % n_streams]);
-    if (st != VDM_OK) return st;
-  }
-  return VDM_OK;
+  (void)hipGetLastError();
+  // counters: the caller's [B][levels][fields], or each slice's own
+  HierWs w;
+  hier_ws(dec, p, M, ws, &w);
+  int64_t* S = stats ? stats : w.stats;
+  const int64_t sst = stats ? (int64_t)p->levels * VDM_STAT_FIELDS : (int64_t)(stride / 8);
+  return hier_run(dec, p, B, K, V, M, kv_bytes, vol, P3, S, sst, nullptr, ws, stride, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ surface extraction
@@ -809,111 +810,132 @@ vdm_status vdm_select_kv_heads(const vdm_decoder* dec, int32_t R, int32_t block,
 }
 
 
-vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, const void* K, const void* V, int64_t M,
-                           float* vol, int64_t vol_elems, int64_t* stats, const vdm_hier_debug* dbg, void* ws,
-                           size_t ws_bytes, vdm_stream stream) {
-  vdm_status st = check_decoder(dec);
-  if (st != VDM_OK) return st;
-  st = check_hier(dec, p, M);
-  if (st != VDM_OK) return st;
-  const int64_t Rf = (int64_t)p->R0 << (p->levels - 1), Pf = Rf + 1;
-  if (!vol || vol_elems < Pf * Pf * Pf)
-    return fail(VDM_ERR_INVALID_ARG, "vol needs %lld floats", (long long)(Pf * Pf * Pf));
-  if (!K || !V || !aligned(K, 16) || !aligned(V, 16) || !aligned(vol, 4))
-    return fail(VDM_ERR_INVALID_ARG, "K, V or vol NULL/misaligned");
-  const size_t need = hier_ws(dec, p, M, nullptr, nullptr);
-  if (!ws || ws_bytes < need || !aligned(ws, 256))
-    return fail(VDM_ERR_WORKSPACE, "workspace needs %zu bytes, 256-aligned (got %zu)", need, ws_bytes);
+}  // extern "C"
+
+// The hierarchical level loop for B shapes at once: shape b uses K, V at byte
+// offset b * kv_bytes, its volume at vol + b * vol_stride floats, its counters at
+// S + b * st_stride int64 and workspace slice ws + b * ws_stride bytes (each
+// slice laid out by hier_ws). Every mask stage is one launch for all B shapes
+// (gridDim.y = B); the decode (and selection) of a level is one launch per
+// shape. The packed epilogue weights of slice 0 serve every shape. dbg: B = 1 only.
+static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int B, const void* K, const void* V,
+                           int64_t M, size_t kv_bytes, float* vol, int64_t vol_stride, int64_t* S, int64_t st_stride,
+                           const vdm_hier_debug* dbg, void* ws, size_t ws_stride, hipStream_t s) {
   HierWs w;
   hier_ws(dec, p, M, ws, &w);
-  (void)hipGetLastError();
-  hipStream_t s = (hipStream_t)stream;
-  int64_t* S = stats ? stats : w.stats;
   const int bq = decode_tile_queries(dec->dtype, dec->D);
   const bool kv = p->use_kvsel != 0;
+  const int64_t wst = (int64_t)ws_stride, sst = st_stride * 8, vst = vol_stride * 4;
+  auto off = [](const void* q, int64_t bytes) { return (const char*)q + bytes; };
+  auto shape_of = [&](auto* q, int b) { return (decltype(q))((char*)q + (int64_t)b * wst); };
 
-  VDM_HIP(launch_stats_init(S, p->levels, p->R0, s), "stats init");
-  VDM_HIP(launch_zero(w.part, (size_t)stat_part_words() * 8, s), "zero launch");
-  VDM_HIP(launch_zero(w.kmax, 256, s), "zero launch");
-  VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s), "key norms launch");
-  if (!kv)
-    VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s), "pack_kv launch");
-  else if (dec->dtype == VDM_BF16)  // the selection streams packed K
-    VDM_HIP(launch_pack_kv(dec->dtype, K, nullptr, (int)M, dec->D, (int)mpad(M), w.Kp, nullptr, s), "pack K launch");
+  VDM_HIP(launch_stats_init(bp(S, sst), p->levels, p->R0, B, s), "stats init");
+  VDM_HIP(launch_zero_b(BP<void>{w.part, wst}, (size_t)stat_part_words() * 8, B, s), "zero launch");
+  VDM_HIP(launch_zero_b(BP<void>{w.kmax, wst}, 256, B, s), "zero launch");
+  for (int b = 0; b < B; ++b) {
+    const void* Kb = off(K, (int64_t)b * kv_bytes);
+    const void* Vb = off(V, (int64_t)b * kv_bytes);
+    VDM_HIP(launch_key_norms(dec->dtype, Kb, (int)M, dec->H, shape_of(w.kmax, b), s), "key norms launch");
+    if (!kv)
+      VDM_HIP(launch_pack_kv(dec->dtype, Kb, Vb, (int)M, dec->D, (int)mpad(M), shape_of(w.Kp, b), shape_of(w.Vt, b), s),
+              "pack_kv launch");
+    else if (dec->dtype == VDM_BF16)  // the selection streams packed K
+      VDM_HIP(launch_pack_kv(dec->dtype, Kb, nullptr, (int)M, dec->D, (int)mpad(M), shape_of(w.Kp, b), nullptr, s),
+              "pack K launch");
+  }
   DecodeArgs packed = base_args(dec);
   VDM_HIP(pack_weights(dec, w.Wp, packed, s), "weight packing launch");
 
+  // the level's volume of shape 0 and its stride (the last level is the caller's)
   auto vol_of = [&](int L) { return L == p->levels - 1 ? vol : w.vol[L]; };
+  auto vstride = [&](int L) { return L == p->levels - 1 ? vst : wst; };
   // list, items and occupied blocks of level L are in w.list / w.items / w.occ
   auto decode_level = [&](int L) -> vdm_status {
     const int R = p->R0 << L;
-    int32_t* tot = w.totals + 4 * L;
-    if (kv) {
-      SelectArgs sa;
-      memset(&sa, 0, sizeof sa);
-      sa.R = R;
-      sa.block = 8;
-      sa.k = p->k;
-      sa.cap = p->cap;
-      sa.probes = p->probes;
-      sa.seed = p->seed + (uint64_t)R;  // a different stream per level
-      sa.M = (int)M;
-      sa.H = dec->H;
-      sa.D = dec->D;
-      sa.Wq = dec->Wq;
-      sa.K = K;
-      sa.Kp = w.Kp;
-      sa.blocks = w.occ;
-      sa.n_blocks = 0;
-      sa.d_n_blocks = tot + 2;
-      sa.sel_idx = w.sel_idx;
-      sa.sel_cnt = w.sel_cnt;
-      sa.stat_selected = S + L * VDM_STAT_FIELDS + VDM_STAT_SELECTED;
-      sa.scores = w.sel_scores;
-      sa.per_head = p->heads;
-      VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, sa, s), "select launch");
+    for (int b = 0; b < B; ++b) {
+      int32_t* tot = shape_of(w.totals, b) + 4 * L;
+      const void* Kb = off(K, (int64_t)b * kv_bytes);
+      const void* Vb = off(V, (int64_t)b * kv_bytes);
+      if (kv) {
+        SelectArgs sa;
+        memset(&sa, 0, sizeof sa);
+        sa.R = R;
+        sa.block = 8;
+        sa.k = p->k;
+        sa.cap = p->cap;
+        sa.probes = p->probes;
+        sa.seed = p->seed + (uint64_t)R;  // a different stream per level
+        sa.M = (int)M;
+        sa.H = dec->H;
+        sa.D = dec->D;
+        sa.Wq = dec->Wq;
+        sa.K = Kb;
+        sa.Kp = shape_of(w.Kp, b);
+        sa.blocks = shape_of(w.occ, b);
+        sa.n_blocks = 0;
+        sa.d_n_blocks = tot + 2;
+        sa.sel_idx = shape_of(w.sel_idx, b);
+        sa.sel_cnt = shape_of(w.sel_cnt, b);
+        sa.stat_selected = S + (int64_t)b * st_stride + L * VDM_STAT_FIELDS + VDM_STAT_SELECTED;
+        sa.scores = shape_of(w.sel_scores, b);
+        sa.per_head = p->heads;
+        VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, sa, s), "select launch");
+      }
+      DecodeArgs a = packed;
+      a.qs = QuerySrc{VDM_Q_GRID_LIST, R, nullptr, shape_of(w.list, b), 0};
+      a.kmax = shape_of(w.kmax, b);
+      a.out = (float*)((char*)vol_of(L) + (int64_t)b * vstride(L));
+      a.scatter = 1;
+      a.M = (int)M;
+      if (kv) {
+        a.Kp = Kb;
+        a.Vt = Vb;
+        a.items = shape_of(w.items, b);
+        a.d_n_items = tot + 1;
+        a.sel_idx = shape_of(w.sel_idx, b);
+        a.sel_cnt = shape_of(w.sel_cnt, b);
+        a.cap = p->cap;
+        a.heads = p->heads;
+      } else {
+        a.Kp = shape_of(w.Kp, b);
+        a.Vt = shape_of(w.Vt, b);
+        a.d_N = tot;
+      }
+      VDM_HIP_T(kv ? VDM_TIME_DECODE_GATHERED : VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, kv, a, s),
+                "decode launch");
     }
-    DecodeArgs a = packed;
-    a.qs = QuerySrc{VDM_Q_GRID_LIST, R, nullptr, w.list, 0};
-    a.kmax = w.kmax;
-    a.out = vol_of(L);
-    a.scatter = 1;
-    a.M = (int)M;
-    if (kv) {
-      a.Kp = K;
-      a.Vt = V;
-      a.items = w.items;
-      a.d_n_items = tot + 1;
-      a.sel_idx = w.sel_idx;
-      a.sel_cnt = w.sel_cnt;
-      a.cap = p->cap;
-      a.heads = p->heads;
-    } else {
-      a.Kp = w.Kp;
-      a.Vt = w.Vt;
-      a.d_N = tot;
-    }
-    VDM_HIP_T(kv ? VDM_TIME_DECODE_GATHERED : VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, kv, a, s), "decode launch");
     return VDM_OK;
   };
 
+  auto BPt = [&](auto* q) { return bp(q, wst); };
   // level 0: every point, in blocked order
   {
     const int NB = nblocks8(p->R0 + 1);
     const int64_t nb3 = (int64_t)NB * NB * NB;
-    VDM_HIP_T(VDM_TIME_MARK, s, launch_mark(nullptr, 1, nullptr, 1, p->R0, w.newmask, nullptr, w.counts, s), "mark launch");
-    VDM_HIP_T(VDM_TIME_SCAN, s, launch_scan(w.counts, nb3, bq, w.partial, w.offs, w.occ, w.totals, S, s), "scan launch");
-    VDM_HIP_T(VDM_TIME_EMIT, s, launch_emit(w.newmask, w.counts, w.offs, w.occ, w.totals, p->R0, bq, w.list, w.items, s),
+    VDM_HIP_T(VDM_TIME_MARK, s,
+              launch_mark(BP<const uint64_t>{nullptr, 0}, 1, BP<const uint64_t>{nullptr, 0}, 1, p->R0, BPt(w.newmask),
+                          BP<uint64_t>{nullptr, 0}, BPt(w.counts), B, s),
+              "mark launch");
+    VDM_HIP_T(VDM_TIME_SCAN, s,
+              launch_scan(bp((const int32_t*)w.counts, wst), nb3, bq, BPt(w.partial), BPt(w.offs), BPt(w.occ),
+                          BPt(w.totals), bp(S, sst), B, s),
+              "scan launch");
+    VDM_HIP_T(VDM_TIME_EMIT, s,
+              launch_emit(bp((const uint64_t*)w.newmask, wst), bp((const int32_t*)w.counts, wst),
+                          bp((const int4*)w.offs, wst), bp((const int32_t*)w.occ, wst),
+                          bp((const int32_t*)w.totals, wst), p->R0, bq, BPt(w.list), BPt(w.items), B, s),
               "emit launch");
-    st = decode_level(0);
+    vdm_status st = decode_level(0);
     if (st != VDM_OK) return st;
   }
   for (int L = 0; L < p->levels; ++L) {
     const int R = p->R0 << L, P = R + 1, NB = nblocks8(P);
     int64_t* SL = S + L * VDM_STAT_FIELDS;
-    VDM_HIP_T(VDM_TIME_CELL_TEST, s, launch_cell_test(vol_of(L), R, L ? w.kept[L - 1] : nullptr, p->tau, w.active[L], w.part, SL + VDM_STAT_TESTED,
-                             SL + VDM_STAT_ACTIVE, s),
-            "cell test launch");
+    VDM_HIP_T(VDM_TIME_CELL_TEST, s,
+              launch_cell_test(bp((const float*)vol_of(L), vstride(L)), R,
+                               bp((const uint64_t*)(L ? w.kept[L - 1] : nullptr), wst), p->tau, BPt(w.active[L]),
+                               BPt(w.part), bp(SL + VDM_STAT_TESTED, sst), bp(SL + VDM_STAT_ACTIVE, sst), B, s),
+              "cell test launch");
     if (dbg) {
       const int64_t p3 = (int64_t)P * P * P, nb3 = (int64_t)NB * NB * NB;
       if (dbg->vol[L] && L < p->levels - 1)
@@ -934,30 +956,67 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
     if (L == p->levels - 1) break;
     // kept = active dilated `dilation` times (ping-pong through tmp)
     if (p->dilation == 0) {
-      VDM_HIP_T(VDM_TIME_DILATE, s, launch_dilate(w.active[L], w.kept[L], R, 1, w.part, SL + VDM_STAT_KEPT, s), "copy launch");
+      VDM_HIP_T(VDM_TIME_DILATE, s,
+                launch_dilate(bp((const uint64_t*)w.active[L], wst), BPt(w.kept[L]), R, 1, BPt(w.part),
+                              bp(SL + VDM_STAT_KEPT, sst), B, s),
+                "copy launch");
     } else {
       const uint64_t* src = w.active[L];
       for (int t = 0; t < p->dilation; ++t) {
         uint64_t* dst = ((p->dilation - 1 - t) % 2 == 0) ? w.kept[L] : w.tmp;
-        VDM_HIP_T(VDM_TIME_DILATE, s, launch_dilate(src, dst, R, 0, w.part, t == p->dilation - 1 ? SL + VDM_STAT_KEPT : nullptr, s), "dilate launch");
+        VDM_HIP_T(VDM_TIME_DILATE, s,
+                  launch_dilate(bp(src, wst), BPt(dst), R, 0, BPt(w.part),
+                                t == p->dilation - 1 ? bp(SL + VDM_STAT_KEPT, sst) : BP<int64_t>{nullptr, 0}, B, s),
+                  "dilate launch");
         src = dst;
       }
     }
     if (dbg && dbg->kept[L]) VDM_HIP(launch_bits_to_bytes(w.kept[L], R, NB, dbg->kept[L], s), "debug export");
     const int Rn = 2 * R, Pn = Rn + 1, NBn = nblocks8(Pn);
-    VDM_HIP_T(VDM_TIME_MARK, s, launch_mark(w.kept[L], R, L ? w.comp[L] : nullptr, 0, Rn, w.newmask, w.comp[L + 1], w.counts, s),
-            "mark launch");
-    VDM_HIP_T(VDM_TIME_SCAN, s, launch_scan(w.counts, (int64_t)NBn * NBn * NBn, bq, w.partial, w.offs, w.occ, w.totals + 4 * (L + 1),
-                        S + (L + 1) * VDM_STAT_FIELDS, s),
-            "scan launch");
+    VDM_HIP_T(VDM_TIME_MARK, s,
+              launch_mark(bp((const uint64_t*)w.kept[L], wst), R, bp((const uint64_t*)(L ? w.comp[L] : nullptr), wst), 0,
+                          Rn, BPt(w.newmask), BPt(w.comp[L + 1]), BPt(w.counts), B, s),
+              "mark launch");
+    VDM_HIP_T(VDM_TIME_SCAN, s,
+              launch_scan(bp((const int32_t*)w.counts, wst), (int64_t)NBn * NBn * NBn, bq, BPt(w.partial), BPt(w.offs),
+                          BPt(w.occ), BPt(w.totals + 4 * (L + 1)), bp(S + (L + 1) * VDM_STAT_FIELDS, sst), B, s),
+              "scan launch");
     VDM_HIP_T(VDM_TIME_EMIT, s,
-              launch_emit(w.newmask, w.counts, w.offs, w.occ, w.totals + 4 * (L + 1), Rn, bq, w.list, w.items, s),
+              launch_emit(bp((const uint64_t*)w.newmask, wst), bp((const int32_t*)w.counts, wst),
+                          bp((const int4*)w.offs, wst), bp((const int32_t*)w.occ, wst),
+                          bp((const int32_t*)(w.totals + 4 * (L + 1)), wst), Rn, bq, BPt(w.list), BPt(w.items), B, s),
               "emit launch");
-    VDM_HIP_T(VDM_TIME_FILL, s, launch_fill(vol_of(L), P, vol_of(L + 1), Pn, s), "fill launch");
-    st = decode_level(L + 1);
+    VDM_HIP_T(VDM_TIME_FILL, s,
+              launch_fill(bp((const float*)vol_of(L), vstride(L)), P, bp(vol_of(L + 1), vstride(L + 1)), Pn, B, s),
+              "fill launch");
+    vdm_status st = decode_level(L + 1);
     if (st != VDM_OK) return st;
   }
   return VDM_OK;
+}
+
+extern "C" {
+
+vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, const void* K, const void* V, int64_t M,
+                           float* vol, int64_t vol_elems, int64_t* stats, const vdm_hier_debug* dbg, void* ws,
+                           size_t ws_bytes, vdm_stream stream) {
+  vdm_status st = check_decoder(dec);
+  if (st != VDM_OK) return st;
+  st = check_hier(dec, p, M);
+  if (st != VDM_OK) return st;
+  const int64_t Rf = (int64_t)p->R0 << (p->levels - 1), Pf = Rf + 1;
+  if (!vol || vol_elems < Pf * Pf * Pf)
+    return fail(VDM_ERR_INVALID_ARG, "vol needs %lld floats", (long long)(Pf * Pf * Pf));
+  if (!K || !V || !aligned(K, 16) || !aligned(V, 16) || !aligned(vol, 4))
+    return fail(VDM_ERR_INVALID_ARG, "K, V or vol NULL/misaligned");
+  const size_t need = hier_ws(dec, p, M, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(VDM_ERR_WORKSPACE, "workspace needs %zu bytes, 256-aligned (got %zu)", need, ws_bytes);
+  HierWs w;
+  hier_ws(dec, p, M, ws, &w);
+  (void)hipGetLastError();
+  int64_t* S = stats ? stats : w.stats;
+  return hier_run(dec, p, 1, K, V, M, 0, vol, 0, S, 0, dbg, ws, 0, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ local KNN decoder

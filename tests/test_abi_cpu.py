@@ -263,15 +263,9 @@ def test_batched_hier_argument_checks():
     assert need % 4 == 0 and need // 4 >= one and need // 4 % 256 == 0 and need // 4 - one < 256
     P3 = 301 ** 3
 
-    streams = (C.c_void_p * 2)(None, None)
-
-    def call(B=4, K=0x1000, vol_elems=4 * P3, wsb=need, ws=0x1000, params=p, st=streams, ns=2):
+    def call(B=4, K=0x1000, vol_elems=4 * P3, wsb=need, ws=0x1000, params=p):
         return lib.vdm_decode_hier_batch(C.byref(d), C.byref(params), B, K, 0x1000, 3072, 0x1000, vol_elems, None,
-                                         ws, wsb, st, ns)
-
-    assert call(st=None) == V.VDM_ERR_INVALID_ARG
-    assert call(ns=0) == V.VDM_ERR_INVALID_ARG
-    assert call(ns=65) == V.VDM_ERR_INVALID_ARG
+                                         ws, wsb, None)
 
     assert call(B=0) == V.VDM_ERR_INVALID_ARG
     assert call(B=4097) == V.VDM_ERR_INVALID_ARG

@@ -215,8 +215,8 @@ def test_hier_computed_points_equal_dense_decode():
 
 @pytest.mark.parametrize("kvsel", [False, True])
 def test_hier_batch_equals_single_shape_calls_bitwise(kvsel):
-    # B vecsets through vdm_decode_hier_batch (up to four streams at once, B = 5 wraps
-    # round the streams): each shape's volume and counters equal its own
+    # B = 5 vecsets through vdm_decode_hier_batch (every mask stage one launch for
+    # the five shapes): each shape's volume and counters equal its own
     # vdm_decode_hier call bit for bit; shape 0 also passes the lockstep check
     w = W.make(1)
     dec = gpu_decoder(w)
@@ -256,10 +256,10 @@ def test_hier_batch_equals_single_shape_calls_bitwise(kvsel):
         lockstep(params, v0, s0, dbg, lambda R, lin: od.sdf_grid(R, lin), sample=400)
 
 
-def test_hier_batch_fp32_and_timing_across_streams():
+def test_hier_batch_fp32_and_one_launch_per_mask_stage():
     # the float32 decoder through the batched call (B = 3) equals single calls bit for
-    # bit, and launch timing records every shape's launches although they run on
-    # several streams (levels x B decode launches, B x (levels - 1) fills)
+    # bit; launch timing shows one launch per mask stage for the whole batch
+    # (levels - 1 fills, levels cell tests) and one decode launch per shape and level
     w = W.make(0)
     dec = gpu_decoder(w)
     rng = np.random.default_rng(29)
@@ -279,8 +279,11 @@ def test_hier_batch_fp32_and_timing_across_streams():
     torch.cuda.synchronize()
     n_dec, ms_dec = V().vdm_timing_read("decode")
     n_fill, _ = V().vdm_timing_read("fill")
+    n_test, _ = V().vdm_timing_read("cell_test")
+    n_emit, _ = V().vdm_timing_read("emit")
     V().vdm_timing(2)
-    assert n_dec == 3 * B and n_fill == 2 * B and ms_dec > 0
+    assert n_dec == 3 * B and ms_dec > 0
+    assert n_fill == 2 and n_test == 3 and n_emit == 3
     for b in range(B):
         one = torch.empty(P3, dtype=torch.float32, device=dev())
         V().vdm_decode_hier(dec, params, K[b], Vv[b], one)
