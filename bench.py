@@ -144,6 +144,56 @@ def mask_stress(steps: int):
         out["workloads"][name] = res
         del vol, ws
         torch.cuda.empty_cache()
+    # a batch of 8 shapes at 150 -> 300 -> 600 through vdm_decode_hier_batch: every
+    # bookkeeping launch covers the 8 volumes (8 perturbed latent sets)
+    B = 8
+    rng = np.random.default_rng(5)
+    Ks, Vs = [], []
+    for b in range(B):
+        Zb = w.Z if b == 0 else w.Z * np.float32(0.8) + np.float32(0.2) * rng.standard_normal(w.Z.shape).astype(np.float32)
+        Zt = torch.from_numpy(np.ascontiguousarray(Zb, np.float32)).to(dev).to(torch.bfloat16)
+        k, v = torch.empty_like(Zt), torch.empty_like(Zt)
+        V.vdm_project_kv(dec, Zt, k, v)
+        Ks.append(k)
+        Vs.append(v)
+    KB, VB = torch.stack(Ks).contiguous(), torch.stack(Vs).contiguous()
+    del Ks, Vs
+    R0, tau = 150, float(np.float32(4 / 600))
+    p = V.hier_params(R0=R0, levels=3, tau=tau, dilation=1)
+    Pf = (R0 << 2) + 1
+    vol = torch.empty((B, Pf ** 3), dtype=torch.float32, device=dev)
+    st = torch.zeros((B, 3 * V.STAT_FIELDS), dtype=torch.int64, device=dev)
+    ws = V.workspace(V.vdm_hier_batch_workspace_size(dec, p, B, w.M), dev)
+    V.vdm_decode_hier_batch(dec, p, KB, VB, vol, st, ws=ws)
+    torch.cuda.synchronize()
+    per_shape = [V.stats_dict(st[b], 3) for b in range(B)]
+    algs = [mask_bytes(lv, 1) for lv in per_shape]
+    alg = {kd: sum(a[kd] for a in algs) for kd in kinds}
+    res = {"shapes": B, "levels_shape0": per_shape[0]}
+    for mode in ["warm", "cold"]:
+        V.vdm_timing(2)
+        for _ in range(max(steps // 4, 2)):
+            if mode == "cold":
+                flush.fill_(1.0)
+            V.vdm_timing(1)
+            V.vdm_decode_hier_batch(dec, p, KB, VB, vol, st, ws=ws)
+            V.vdm_timing(0)
+        torch.cuda.synchronize()
+        nrep = max(steps // 4, 2)
+        per = {}
+        for kd in kinds:
+            n, ms = V.vdm_timing_read(kd)
+            t = ms / nrep
+            gbs = alg[kd] / (t / 1e3) / 1e9 if t > 0 else None
+            per[kd] = {"launches_per_batch": n // nrep, "ms_per_batch": round(t, 4),
+                       "algorithmic_MB": round(alg[kd] / 1e6, 3),
+                       "GB_per_s": round(gbs, 1) if gbs else None,
+                       "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4) if gbs else None}
+        res[mode] = per
+        V.vdm_timing(2)
+    out["workloads"]["8 x 150->300->600 (one launch per stage)"] = res
+    del vol, ws, KB, VB
+    torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

@@ -233,9 +233,11 @@ hipError_t launch_cell_test(BP<const float> vol, int R, BP<const uint64_t> kept_
 }
 
 // ------------------------------------------------------------------ dilation
-// One thread per word: OR over the 3x3x3 neighbourhood, separably along k
-// (bit shifts inside each 8-bit row), j (shifts by 8) and i (neighbour words),
-// with neighbour blocks supplying the halo. Cells outside [0, R)^3 stay clear.
+// One thread per 8x8x8 cell block: OR over the 3x3x3 neighbourhood, separably
+// along k (bit shifts inside each 8-bit row), j (shifts by 8) and i (neighbouring
+// rows). The thread forms the (j, k)-dilated word of each row 8bi-1 .. 8bi+8 once
+// (neighbour blocks supply the halo) and ORs three of them per output row. Cells
+// outside [0, R)^3 stay clear.
 __device__ __forceinline__ uint64_t dil_k(uint64_t w, uint64_t wl, uint64_t wr) {
   const uint64_t C0 = 0x0101010101010101ull, C7 = 0x8080808080808080ull;
   return w | ((w << 1) & ~C0) | ((wl >> 7) & C0) | ((w >> 1) & ~C7) | ((wr << 7) & C7);
@@ -244,53 +246,70 @@ __device__ __forceinline__ uint64_t dil_j(uint64_t t, uint64_t td, uint64_t tu) 
   return t | (t << 8) | (td >> 56) | (t >> 8) | (tu << 56);
 }
 
-__global__ void dilate_kernel(BP<const uint64_t> ib, BP<uint64_t> ob, int R, int NB, int identity, BP<int64_t> pb) {
+// Bits of the 8x8 (j, k) cells of block (bj, bk) that lie inside [0, R)^2.
+__device__ __forceinline__ uint64_t inside_jk(int lim, int bj, int bk) {
+  const int nj = min(max(lim - 8 * bj, 0), 8), nk = min(max(lim - 8 * bk, 0), 8);
+  const uint64_t rows = nj >= 8 ? ~0ull : ((1ull << (8 * nj)) - 1ull);
+  return (nk >= 8 ? ~0ull : ((1ull << nk) - 1ull) * 0x0101010101010101ull) & rows;
+}
+
+// The 8 words of a block as four 16-byte stores (block words are 64-byte aligned).
+__device__ __forceinline__ void store_block(uint64_t* __restrict__ dst, const uint64_t (&w)[8]) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    reinterpret_cast<uint4*>(dst)[h] =
+        make_uint4((uint32_t)w[2 * h], (uint32_t)(w[2 * h] >> 32), (uint32_t)w[2 * h + 1], (uint32_t)(w[2 * h + 1] >> 32));
+}
+
+__global__ __launch_bounds__(256) void dilate_kernel(BP<const uint64_t> ib, BP<uint64_t> ob, int R, int NB, int identity,
+                                                     BP<int64_t> pb) {
   __shared__ int64_t red[4];
   const uint64_t* __restrict__ in = ib.at();
   uint64_t* __restrict__ out = ob.at();
   int64_t* part = pb.p ? pb.at() : nullptr;
-  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nw = (int64_t)NB * NB * NB * 8;
-  uint64_t res = 0;
-  if (w < nw) {
-    const int64_t b = w >> 3;
-    const int ii = (int)(w & 7);
-    const int bi = (int)(b / ((int64_t)NB * NB)), bj = (int)((b / NB) % NB), bk = (int)(b % NB);
-    const int i = 8 * bi + ii;
-    if (i < R && identity) {
-      res = in[w];
-    } else if (i < R) {
-      for (int di = -1; di <= 1; ++di) {
-        const int i2 = i + di;
-        if (i2 < 0 || i2 >= R) continue;
-        const int bi2 = i2 >> 3, ii2 = i2 & 7;
+  const int b = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  int cnt = 0;
+  if (b < NB * NB * NB) {
+    const int bi = b / (NB * NB), r2 = b - bi * NB * NB, bj = r2 / NB, bk = r2 - bj * NB;
+    const uint64_t m = inside_jk(R, bj, bk);
+    uint64_t res[8];
+    if (identity) {
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) res[ii] = in[(int64_t)b * 8 + ii];
+    } else {
+      // (j, k)-dilated word of cell row i (0 outside [0, R))
+      auto row = [&](int i) -> uint64_t {
+        if (i < 0 || i >= R) return 0ull;
+        const int64_t base = (int64_t)(i >> 3) * NB;
         uint64_t W[3][3];
 #pragma unroll
         for (int a = 0; a < 3; ++a)
 #pragma unroll
           for (int c = 0; c < 3; ++c) {
             const int bj2 = bj + a - 1, bk2 = bk + c - 1;
-            W[a][c] = (bj2 >= 0 && bj2 < NB && bk2 >= 0 && bk2 < NB)
-                          ? in[(((int64_t)bi2 * NB + bj2) * NB + bk2) * 8 + ii2]
-                          : 0ull;
+            W[a][c] = (bj2 >= 0 && bj2 < NB && bk2 >= 0 && bk2 < NB) ? in[((base + bj2) * NB + bk2) * 8 + (i & 7)] : 0ull;
           }
-        const uint64_t t0 = dil_k(W[0][1], W[0][0], W[0][2]);
-        const uint64_t t1 = dil_k(W[1][1], W[1][0], W[1][2]);
-        const uint64_t t2 = dil_k(W[2][1], W[2][0], W[2][2]);
-        res |= dil_j(t1, t0, t2);
+        return dil_j(dil_k(W[1][1], W[1][0], W[1][2]), dil_k(W[0][1], W[0][0], W[0][2]),
+                     dil_k(W[2][1], W[2][0], W[2][2]));
+      };
+      uint64_t tp = row(8 * bi - 1), tc = row(8 * bi);
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const uint64_t tn = row(8 * bi + ii + 1);
+        res[ii] = tp | tc | tn;
+        tp = tc;
+        tc = tn;
       }
     }
-    if (i < R) {  // clip to cells inside the grid
-      const int nj = min(max(R - 8 * bj, 0), 8), nk = min(max(R - 8 * bk, 0), 8);
-      const uint64_t row = nk >= 8 ? 0xffull : ((1ull << nk) - 1ull);
-      uint64_t m = 0;
-      for (int jj = 0; jj < nj; ++jj) m |= row << (8 * jj);
-      res &= m;
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {  // clip to cells inside the grid
+      res[ii] &= 8 * bi + ii < R ? m : 0ull;
+      cnt += __popcll(res[ii]);
     }
-    out[w] = res;
+    store_block(out + (int64_t)b * 8, res);
   }
   if (part) {
-    const int64_t n = block_sum_i64(__popcll(res), red, threadIdx.x, 256);
+    const int64_t n = block_sum_i64(cnt, red, threadIdx.x, 256);
     if (threadIdx.x == 0 && n) atomicAdd((unsigned long long*)(part + (blockIdx.x % STAT_SLOTS) * 8 + 2), (unsigned long long)n);
   }
 }
@@ -298,8 +317,8 @@ __global__ void dilate_kernel(BP<const uint64_t> ib, BP<uint64_t> ob, int R, int
 hipError_t launch_dilate(BP<const uint64_t> in, BP<uint64_t> out, int R, int identity, BP<int64_t> part,
                          BP<int64_t> stat, int B, hipStream_t s) {
   const int NB = nblocks8(R + 1);
-  const int64_t nw = (int64_t)NB * NB * NB * 8;
-  hipLaunchKernelGGL(dilate_kernel, dim3((unsigned)((nw + 255) / 256), (unsigned)B), dim3(256), 0, s, in, out, R, NB,
+  const int64_t nb3 = (int64_t)NB * NB * NB;
+  hipLaunchKernelGGL(dilate_kernel, dim3((unsigned)((nb3 + 255) / 256), (unsigned)B), dim3(256), 0, s, in, out, R, NB,
                      identity, stat.p ? part : BP<int64_t>{nullptr, 0});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !stat.p) return e;
@@ -313,109 +332,107 @@ hipError_t launch_dilate(BP<const uint64_t> in, BP<uint64_t> out, int R, int ide
 // with all-even indices was computed iff its level-L point (I/2, J/2, K/2) was
 // (every point at level 0). all_new: every in-range point is new (level 0 list).
 //
-// Bit-parallel: one thread per output word (the 8x8 (J, K) square of one I). For
-// a parent row a, the parent cells c = 4bj-1 .. 4bj+3, d = 4bk-1 .. 4bk+3 form a
-// 5x5 window (up to 4 words); "upsampling" it per axis with the parent rule gives
-// the candidate bits of the whole word.
+// Bit-parallel, one thread per 8x8x8 point block (bi, bj, bk). Its points have
+// parent cells in rows a = 4bi-1 .. 4bi+3, and in each row the 5x5 window
+// c = 4bj-1 .. 4bj+3, d = 4bk-1 .. 4bk+3 (up to 4 words: the main quadrant and the
+// j-, k- and corner halos). Each row's window, packed as 5 bytes of 5 bits, is
+// "upsampled" by the parent rule along k (bits) and j (bytes) with spread
+// operations on the whole word; output row I takes the rows of its parents.
 
-// 5-bit window (parents d = 4bk-1 .. 4bk+3 as bits 0..4) -> the 8 points K = 8bk .. 8bk+7:
-// odd K = 8bk+2m+1 has parent bit m+1, even K = 8bk+2m has parent bits m and m+1.
-__device__ __forceinline__ uint32_t up8(uint32_t w5) {
-  const uint32_t s = ((w5 >> 1) & 1u) << 1 | ((w5 >> 2) & 1u) << 3 | ((w5 >> 3) & 1u) << 5 | ((w5 >> 4) & 1u) << 7;
-  return (s | (((s >> 1) | (s << 1) | (w5 & 1u)) & 0x55u)) & 0xffu;
+// The low 4 bits of every byte to bits 0, 2, 4, 6 of that byte.
+__device__ __forceinline__ uint64_t spread_bits(uint64_t t) {
+  t = (t | (t << 2)) & 0x3333333333333333ull;
+  return (t | (t << 1)) & 0x5555555555555555ull;
+}
+// The low 4 bytes of a word to bytes 0, 2, 4, 6.
+__device__ __forceinline__ uint64_t spread_bytes(uint64_t t) {
+  t = (t | (t << 16)) & 0x0000ffff0000ffffull;
+  return (t | (t << 8)) & 0x00ff00ff00ff00ffull;
+}
+// 5x5 window X (byte r = parent row 4bj-1+r, bit c = parent column 4bk-1+c) to
+// the 8x8 candidate word: point 2m+1 has parent m+1 of the window, point 2m
+// parents m and m+1, along each axis.
+__device__ __forceinline__ uint64_t upsample_window(uint64_t X) {
+  const uint64_t E = spread_bits((X >> 1) & 0x0f0f0f0f0full);
+  const uint64_t Y = spread_bits(X & 0x0f0f0f0f0full) | E | (E << 1);
+  const uint64_t H = spread_bytes((Y >> 8) & 0xffffffffull);
+  return spread_bytes(Y & 0xffffffffull) | H | (H << 8);
 }
 
-// Candidate word of level L+1 from kept parent row a (cells of level L; R cells, NB blocks).
-__device__ __forceinline__ uint64_t cand_from_row(const uint64_t* __restrict__ kept, int NB, int R, int a, int bj,
-                                                  int bk) {
+// Candidate word of point block (., bj, bk) of level L+1 from kept parent row a
+// (kept: level-L cell mask, R cells, NB blocks; bits outside [0, R)^3 are clear).
+__device__ __forceinline__ uint64_t cand_row(const uint64_t* __restrict__ kept, int NB, int R, int a, int bj, int bk) {
   if (a < 0 || a >= R) return 0ull;
-  const int Cm = bj >> 1, Ch = (4 * bj - 1) >> 3, Dm = bk >> 1, Dh = (4 * bk - 1) >> 3;
-  auto ld = [&](int C, int Dd) -> uint64_t {
-    return (C >= 0 && C < NB && Dd >= 0 && Dd < NB) ? kept[(((int64_t)(a >> 3) * NB + C) * NB + Dd) * 8 + (a & 7)]
-                                                    : 0ull;
-  };
-  const uint64_t Wmm = ld(Cm, Dm), Wmh = bk > 0 ? ld(Cm, Dh) : 0ull;
-  const uint64_t Whm = bj > 0 ? ld(Ch, Dm) : 0ull, Whh = (bj > 0 && bk > 0) ? ld(Ch, Dh) : 0ull;
-  uint32_t row[5];
-#pragma unroll
-  for (int r = 0; r < 5; ++r) {
-    const int c = 4 * bj - 1 + r;
-    const bool main_blk = (c >> 3) == Cm;
-    const uint64_t wm = main_blk ? Wmm : Whm, wh = main_blk ? Wmh : Whh;
-    const uint32_t lo = (uint32_t)((wm >> (((c & 7) << 3) + ((4 * bk) & 7))) & 0xfull) << 1;
-    const uint32_t hb = bk > 0 ? (uint32_t)((wh >> (((c & 7) << 3) + ((4 * bk - 1) & 7))) & 1ull) : 0u;
-    row[r] = (c >= 0 && c < R) ? (lo | hb) : 0u;
-  }
-  // the same rule along J on byte rows
-  uint64_t U = 0;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) U |= (uint64_t)up8(row[m + 1]) << (8 * (2 * m + 1));
-  return U | (((U >> 8) | (U << 8) | (uint64_t)up8(row[0])) & 0x00ff00ff00ff00ffull);
+  const int64_t rb = (int64_t)(a >> 3) * NB;
+  const int Cm = bj >> 1, Dm = bk >> 1, jo = bj & 1, ko = bk & 1;
+  auto ld = [&](int C, int Dd) { return kept[((rb + C) * NB + Dd) * 8 + (a & 7)]; };
+  const uint64_t Wm = ld(Cm, Dm);
+  const uint64_t Wj = jo ? Wm : (bj > 0 ? ld(Cm - 1, Dm) : 0ull);  // holds parent row 4bj-1
+  const uint64_t Wk = ko ? Wm : (bk > 0 ? ld(Cm, Dm - 1) : 0ull);  // holds parent column 4bk-1
+  const uint64_t Wc = jo ? Wk : (ko ? Wj : ((bj > 0 && bk > 0) ? ld(Cm - 1, Dm - 1) : 0ull));
+  const int hr = jo ? 3 : 7, hc = ko ? 3 : 7;  // (4bj-1) & 7 and (4bk-1) & 7
+  uint64_t X = ((Wm >> (32 * jo + 4 * ko)) & 0x0f0f0f0full) << 9;
+  X |= ((Wk >> (32 * jo + hc)) & 0x01010101ull) << 8;
+  X |= ((Wj >> (8 * hr + 4 * ko)) & 0xfull) << 1;
+  X |= (Wc >> (8 * hr + hc)) & 1ull;
+  return upsample_window(X);
 }
 
 __global__ __launch_bounds__(256) void mark_kernel(BP<const uint64_t> kb, int R, BP<const uint64_t> cpb, int all_new,
                                                    int Rn, BP<uint64_t> nmb, BP<uint64_t> cnb, BP<int32_t> cb) {
-  const uint64_t* __restrict__ kept = kb.at();
+  const uint64_t* __restrict__ kept = kb.p ? kb.at() : nullptr;
   const uint64_t* __restrict__ comp_prev = cpb.p ? cpb.at() : nullptr;
   uint64_t* __restrict__ newmask = nmb.at();
   uint64_t* __restrict__ comp_next = cnb.p ? cnb.at() : nullptr;
   int32_t* __restrict__ counts = cb.at();
   const int NBn = nblocks8(Rn + 1), NB = nblocks8(R + 1);
-  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nw = (int64_t)NBn * NBn * NBn * 8;
-  uint64_t wn = 0ull;
-  if (w < nw) {
-    const int64_t b = w >> 3;
-    const int ii = (int)(w & 7);
-    const int bi = (int)(b / ((int64_t)NBn * NBn)), bj = (int)((b / NBn) % NBn), bk = (int)(b % NBn);
-    const int I = 8 * bi + ii;
-    // points inside [0, Rn]^3
-    const int nj = min(max(Rn + 1 - 8 * bj, 0), 8), nk = min(max(Rn + 1 - 8 * bk, 0), 8);
-    const uint64_t rowm = nk >= 8 ? 0xffull : ((1ull << nk) - 1ull);
-    uint64_t inr = 0ull;
-    for (int jj = 0; jj < nj; ++jj) inr |= rowm << (8 * jj);
-    if (I > Rn) inr = 0ull;
-    uint64_t wp = 0ull;
-    if (all_new) {
-      wn = inr;
-    } else {
-      // computed before: all-even points whose level-L point was computed
-      if ((I & 1) == 0) {
+  const int b = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (b >= NBn * NBn * NBn) return;
+  const int bi = b / (NBn * NBn), r2 = b - bi * NBn * NBn, bj = r2 / NBn, bk = r2 - bj * NBn;
+  const uint64_t inr = inside_jk(Rn + 1, bj, bk);  // points inside [0, Rn]^2
+  uint64_t wn[8], wc[8];
+  if (all_new) {
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) wn[ii] = wc[ii] = 8 * bi + ii <= Rn ? inr : 0ull;
+  } else {
+    uint64_t C[5];
+#pragma unroll
+    for (int r = 0; r < 5; ++r) C[r] = cand_row(kept, NB, R, 4 * bi - 1 + r, bj, bk);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // even row I = 8bi+2m: parents 4bi+m-1 and 4bi+m; computed before where all-even
+      const int I = 8 * bi + 2 * m;
+      const uint64_t in_e = I <= Rn ? inr : 0ull;
+      uint64_t wp = 0ull;
+      if (I <= Rn) {
         if (comp_prev) {
           const int i2 = I >> 1;
-          const uint64_t pw =
-              comp_prev[(((int64_t)(i2 >> 3) * NB + (bj >> 1)) * NB + (bk >> 1)) * 8 + (i2 & 7)];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t q = (uint32_t)((pw >> ((((4 * bj) & 7) + r) * 8 + ((4 * bk) & 7))) & 0xfull);
-            const uint32_t e = (q & 1u) | (q & 2u) << 1 | (q & 4u) << 2 | (q & 8u) << 3;
-            wp |= (uint64_t)e << (16 * r);
-          }
+          const uint64_t pw = comp_prev[(((int64_t)(i2 >> 3) * NB + (bj >> 1)) * NB + (bk >> 1)) * 8 + (i2 & 7)];
+          wp = spread_bytes(spread_bits((pw >> (32 * (bj & 1) + 4 * (bk & 1))) & 0x0f0f0f0full));
         } else {
           wp = 0x0055005500550055ull;
         }
+        wp &= in_e;
       }
-      wp &= inr;
-      uint64_t cand = cand_from_row(kept, NB, R, (I & 1) ? (I - 1) >> 1 : (I >> 1) - 1, bj, bk);
-      if ((I & 1) == 0) cand |= cand_from_row(kept, NB, R, I >> 1, bj, bk);
-      wn = cand & ~wp & inr;
+      wn[2 * m] = (C[m] | C[m + 1]) & ~wp & in_e;
+      wc[2 * m] = wn[2 * m] | wp;
+      // odd row I + 1: parent 4bi+m
+      wn[2 * m + 1] = wc[2 * m + 1] = C[m + 1] & (I + 1 <= Rn ? inr : 0ull);
     }
-    newmask[w] = wn;
-    if (comp_next) comp_next[w] = wn | wp;
   }
-  // per-block count: the 8 words of a block are 8 consecutive lanes
-  int c = __popcll(wn);
-  c += __shfl_xor(c, 1);
-  c += __shfl_xor(c, 2);
-  c += __shfl_xor(c, 4);
-  if (w < nw && (w & 7) == 0) counts[w >> 3] = c;
+  int c = 0;
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) c += __popcll(wn[ii]);
+  store_block(newmask + (int64_t)b * 8, wn);
+  if (comp_next) store_block(comp_next + (int64_t)b * 8, wc);
+  counts[b] = c;
 }
 
 hipError_t launch_mark(BP<const uint64_t> kept, int R, BP<const uint64_t> comp_prev, int all_new, int Rn,
                        BP<uint64_t> newmask, BP<uint64_t> comp_next, BP<int32_t> counts, int B, hipStream_t s) {
   const int NBn = nblocks8(Rn + 1);
-  const int64_t nw = (int64_t)NBn * NBn * NBn * 8;
-  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((nw + 255) / 256), (unsigned)B), dim3(256), 0, s, kept, R,
+  const int64_t nb3 = (int64_t)NBn * NBn * NBn;
+  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((nb3 + 255) / 256), (unsigned)B), dim3(256), 0, s, kept, R,
                      comp_prev, all_new, Rn, newmask, comp_next, counts);
   return hipGetLastError();
 }
@@ -584,47 +601,106 @@ hipError_t launch_emit(BP<const uint64_t> newmask, BP<const int32_t> counts, BP<
 
 // ------------------------------------------------------------------ nearest-ancestor fill
 // vol_next[I][J][K] = vol_prev[I/2][J/2][K/2] (integer division) for every point.
-// One workgroup per 8 consecutive rows (I, J0 .. J0+7), J0 even: rows 2m and 2m+1
-// share source row J0/2 + m. Each thread loads all its source values first (up
-// to 4 rows x FILL_KI positions in flight), then stores them; threads run along K,
-// so every row is one contiguous store stream.
-constexpr int FILL_ROWS = 8;
+// The output is one flat array cut into groups of 4 consecutive values, aligned
+// so that each group is one 16-byte store (the few values before the first
+// aligned address and after the last whole group are written one by one). A
+// workgroup writes FILL_U x 256 consecutive groups: all their source loads are
+// issued before the first store. A group's (I, J, K) comes from a division (a
+// double-precision reciprocal estimate, corrected exactly); inside one output row
+// its 4 values need 2 or 3 consecutive source values. The output is not read back
+// by this kernel and is larger than the caches, so it is stored non-temporally.
+// Flat offsets are 32-bit: the finest volume holds at most 1201^3 < 2^32 points.
 constexpr int FILL_NT = 256;
-constexpr int FILL_KI = 5;  // FILL_NT * FILL_KI >= 1201 points per row (finest grid at most 1200 cells)
+constexpr int FILL_U = 2;
 
-__global__ __launch_bounds__(FILL_NT) void fill_kernel(BP<const float> pb, int Pp, BP<float> nb, int Pn) {
-  const float* __restrict__ prev = pb.at();
-  float* __restrict__ next = nb.at();
-  const int ng = (Pn + FILL_ROWS - 1) / FILL_ROWS;
-  const int I = blockIdx.x / ng, J0 = (blockIdx.x % ng) * FILL_ROWS;
-  float v[FILL_ROWS / 2][FILL_KI];
+struct Div32 {
+  uint32_t d;
+  double inv;
+};
+
+// floor(n / d): n * (1/d) in double is within one of the quotient for n < 2^32,
+// then one exact correction.
+__device__ __forceinline__ uint32_t div32(uint32_t n, const Div32& dv) {
+  uint32_t q = (uint32_t)((double)n * dv.inv);
+  const uint32_t qd = q * dv.d;
+  if (qd > n)
+    --q;
+  else if (n - qd >= dv.d)
+    ++q;
+  return q;
+}
+
+__device__ __forceinline__ float fill_value(const float* __restrict__ prev, int Pp, int I, int J, int K) {
+  return prev[((size_t)(I >> 1) * Pp + (J >> 1)) * Pp + (K >> 1)];
+}
+
+// the 4 values of the group that starts at flat offset o
+__device__ __forceinline__ float4 fill_group(const float* __restrict__ prev, int Pp, int Pn, uint32_t o,
+                                             const Div32& d2, const Div32& d1) {
+  const uint32_t I = div32(o, d2), rem = o - I * d2.d;
+  const uint32_t J = div32(rem, d1);
+  uint32_t K = rem - J * d1.d;
+  if (K + 3 < (uint32_t)Pn) {  // one output row: sources K/2 .. (K+3)/2
+    const float* __restrict__ src = prev + ((size_t)(I >> 1) * Pp + (J >> 1)) * Pp + (K >> 1);
+    const float a = src[0], b = src[1];
+    if (K & 1) return make_float4(a, b, b, src[2]);
+    return make_float4(a, a, b, b);
+  }
+  float v[4];
+  uint32_t Ii = I, Jj = J;
 #pragma unroll
-  for (int m = 0; m < FILL_ROWS / 2; ++m) {
-    const float* __restrict__ src = prev + ((int64_t)(I >> 1) * Pp + ((J0 >> 1) + m)) * Pp;
-    const bool row_ok = J0 + 2 * m < Pn;
-#pragma unroll
-    for (int t = 0; t < FILL_KI; ++t) {
-      const int K = threadIdx.x + FILL_NT * t;
-      v[m][t] = (row_ok && K < Pn) ? src[K >> 1] : 0.f;
+  for (int t = 0; t < 4; ++t) {
+    v[t] = fill_value(prev, Pp, (int)Ii, (int)Jj, (int)K);
+    if (++K == (uint32_t)Pn) {
+      K = 0;
+      if (++Jj == (uint32_t)Pn) {
+        Jj = 0;
+        ++Ii;
+      }
     }
   }
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+typedef float fill_f4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(FILL_NT) void fill_kernel(BP<const float> pb, int Pp, BP<float> nb, int Pn, Div32 d2,
+                                                       Div32 d1) {
+  const float* __restrict__ prev = pb.at();
+  float* __restrict__ next = nb.at();
+  const uint32_t n = (uint32_t)Pn * Pn * Pn;
+  // values before the first 16-byte aligned address, then whole groups of 4
+  const uint32_t head = min((uint32_t)(((16 - ((uintptr_t)next & 15)) & 15) / 4), n);
+  const uint32_t ngroups = (n - head) / 4;
+  const uint32_t g0 = blockIdx.x * (FILL_NT * FILL_U) + threadIdx.x;
+  float4 v[FILL_U];
 #pragma unroll
-  for (int r = 0; r < FILL_ROWS; ++r) {
-    const int J = J0 + r;
-    if (J >= Pn) break;
-    float* __restrict__ dst = next + ((int64_t)I * Pn + J) * Pn;
+  for (int u = 0; u < FILL_U; ++u) {
+    const uint32_t g = g0 + u * FILL_NT;
+    if (g < ngroups) v[u] = fill_group(prev, Pp, Pn, head + 4 * g, d2, d1);
+  }
 #pragma unroll
-    for (int t = 0; t < FILL_KI; ++t) {
-      const int K = threadIdx.x + FILL_NT * t;
-      if (K < Pn) dst[K] = v[r >> 1][t];
+  for (int u = 0; u < FILL_U; ++u) {
+    const uint32_t g = g0 + u * FILL_NT;
+    if (g < ngroups) {
+      const fill_f4 x = {v[u].x, v[u].y, v[u].z, v[u].w};
+      __builtin_nontemporal_store(x, reinterpret_cast<fill_f4*>(next + head + 4 * g));
     }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < head + ((n - head) & 3)) {
+    const uint32_t o = threadIdx.x < head ? threadIdx.x : head + 4 * ngroups + (threadIdx.x - head);
+    const uint32_t I = div32(o, d2), rem = o - I * d2.d;
+    const uint32_t J = div32(rem, d1);
+    next[o] = fill_value(prev, Pp, (int)I, (int)J, (int)(rem - J * d1.d));
   }
 }
 
 hipError_t launch_fill(BP<const float> prev, int Pp, BP<float> next, int Pn, int B, hipStream_t s) {
-  if (Pn > FILL_NT * FILL_KI) return hipErrorInvalidValue;
-  const int64_t g = (int64_t)Pn * ((Pn + FILL_ROWS - 1) / FILL_ROWS);
-  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)g, (unsigned)B), dim3(FILL_NT), 0, s, prev, Pp, next, Pn);
+  if (Pn < 1 || Pn > 1201) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)Pn * Pn * Pn;
+  const int64_t g = n / 4 / (FILL_NT * FILL_U) + 1;
+  const Div32 d2{(uint32_t)(Pn * Pn), 1.0 / ((double)Pn * Pn)}, d1{(uint32_t)Pn, 1.0 / (double)Pn};
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)g, (unsigned)B), dim3(FILL_NT), 0, s, prev, Pp, next, Pn, d2, d1);
   return hipGetLastError();
 }
 
