@@ -5,14 +5,18 @@
 //
 // One workgroup (8 waves) per group of up to 4 blocks: the 32 corner probes of
 // the group fill the 32 MFMA columns, so every K tile read serves 4 blocks.
-//   pass 1: per (probe, head) softmax max and sum over all tokens (MFMA logits);
-//   pass 2: score_j = mean over heads of the softmax probability, written to a
-//           per-workgroup scratch row in global memory (32 x M floats do not fit
-//           in LDS);
+//   pass 1: per (probe, head) softmax max and sum over all tokens (MFMA logits
+//           as K Q^T: one probe per lane, so the statistics are per-lane sums);
+//   pass 2: score_j = mean over heads of the softmax probability, 1/sum folded
+//           into the exponent; the logits are formed as Q K^T (16 probes and one
+//           token per lane), so each store writes 32 consecutive tokens of a
+//           probe's row in the per-workgroup scratch (32 x M floats do not fit in
+//           LDS);
 //   top-k:  per probe, the k-th largest score by a bitwise search on the float
 //           bits held in registers (scores are >= 0, so unsigned order is float
-//           order), then every larger score and the lowest-index equal ones;
-//           the block's probes OR their sets into an LDS bitmap;
+//           order), then every larger score and the lowest-index equal ones, as a
+//           per-lane mask; a wave ORs the masks of its probes of one block and
+//           adds them to the block's LDS bitmap with one ballot per mask bit;
 //   cap:    if the union exceeds `cap`, the cap tokens of largest max-over-probes
 //           score (same search; members rank above non-members);
 //   output: ascending compaction of the bitmap.
@@ -51,8 +55,9 @@ __device__ __forceinline__ int wave_sum(int v) {
 }
 
 // Values u[i] stand for index i * 64 + lane (entries at or past n are 0 and never
-// taken). Sets in `bits` the k largest (unsigned order; equal values: lower index
-// first). One wave; `list` is its LDS scratch of SEL_LIST values.
+// taken). Returns the lane's mask of the k largest (bit i: value i of this lane;
+// unsigned order; equal values: lower index first). One wave; `list` is its LDS
+// scratch of SEL_LIST values.
 //
 // The k-th largest value p is the largest threshold with #{u >= p} >= k, built
 // bit by bit. For k <= 64 the 64th largest of the lanes' two largest values, lo,
@@ -65,8 +70,7 @@ __device__ __forceinline__ int wave_sum(int v) {
 // 256-entry list this path ran for most probes). Thresholds are >= 1, so zero
 // entries never count; values are visited in chunks of 16 and a chunk past n is
 // skipped.
-__device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, int k, unsigned* bits,
-                                          unsigned* list, int lane) {
+__device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[SEL_MAXV], int n, int k, unsigned* list, int lane) {
   // (every loop is fully unrolled with constant indices, so u stays in registers)
   constexpr int CH = 16, LV = SEL_LIST / 64;
   static_assert(SEL_MAXV % CH == 0, "whole chunks");
@@ -83,7 +87,7 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
   };
   unsigned p = 0u;
   bool done = false;
-  int greater = 0;  // number of values > p (fast path)
+  int greater = 0, equal = 0;  // numbers of values > p and == p (fast path)
   if (k <= 64) {
     // lo = the 64th largest of the 128 values {largest, second largest of each
     // lane}: at least 64 >= k values are >= lo, and it is tighter than the smallest
@@ -141,13 +145,18 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
           for (int j = 0; j < NV; ++j) c += __popcll(__ballot(v[j] >= cand));
           if (c >= k) p = cand;
         }
-        // values > p (all of them are in the list: p >= lo)
-        int g = 0;
+        // values > p and == p (all of them are in the list: p >= lo)
+        int g = 0, e = 0;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) g += __popcll(__ballot(v[j] > p));
-        return g;
+        for (int j = 0; j < NV; ++j) {
+          g += __popcll(__ballot(v[j] > p));
+          e += __popcll(__ballot(v[j] == p));
+        }
+        return make_int2(g, e);
       };
-      greater = total <= 256 ? search(std::integral_constant<int, 4>()) : search(std::integral_constant<int, LV>());
+      const int2 ge = total <= 256 ? search(std::integral_constant<int, 4>()) : search(std::integral_constant<int, LV>());
+      greater = ge.x;
+      equal = ge.y;
       __builtin_amdgcn_wave_barrier();  // the list is read before the next search writes it
       done = true;
     }
@@ -158,35 +167,64 @@ __device__ __forceinline__ void topk_bits(const unsigned (&u)[SEL_MAXV], int n, 
       if (count_all(cand) >= k) p = cand;
     }
   }
-  // copies of p to take, lowest index first
-  const int need = k - (done ? greater : (p == 0xffffffffu ? 0 : count_all(p + 1u)));
+  if (!done) {
+    greater = p == 0xffffffffu ? 0 : count_all(p + 1u);
+    equal = count_all(p) - greater;
+  }
+  // copies of p to take, lowest index first; usually every copy (no tie at the cut)
+  const int need = k - greater;
+  uint64_t sel = 0ull;
+  if (p > 0u && equal == need) {
+#pragma unroll
+    for (int i = 0; i < SEL_MAXV; ++i)
+      if (i * 64 < n) sel |= (uint64_t)(u[i] >= p) << i;  // (entries past n are 0 < p)
+    return sel;
+  }
   int taken = 0;
 #pragma unroll
   for (int i = 0; i < SEL_MAXV; ++i) {
     if (i * 64 < n) {
-      const int idx = i * 64 + lane;
-      const bool valid = idx < n;
+      const bool valid = i * 64 + lane < n;
       const bool eq = valid && u[i] == p;
       const unsigned long long be = __ballot(eq);
       const int rank = taken + __popcll(be & ((1ull << lane) - 1ull));
-      if (valid && (u[i] > p || (eq && rank < need))) atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+      sel |= (uint64_t)(valid && (u[i] > p || (eq && rank < need))) << i;
       taken += __popcll(be);
+    }
+  }
+  return sel;
+}
+
+// Adds a wave's selection masks (bit i of lane l: token i * 64 + l) to a bitmap of
+// 32-bit words (token t: bit t % 32 of word t / 32; 8-byte aligned): the ballot of
+// bit i is words 2i and 2i+1.
+__device__ __forceinline__ void add_to_bitmap(uint64_t sel, int n, unsigned* words, int lane) {
+#pragma unroll
+  for (int i = 0; i < SEL_MAXV; ++i) {
+    if (i * 64 < n) {
+      const unsigned long long b = __ballot((sel >> i) & 1ull);
+      if (b != 0ull && lane == 0) atomicOr(reinterpret_cast<unsigned long long*>(words + 2 * i), b);
     }
   }
 }
 
-// LDS: [embedding stage] | stats [NW][H][32] float2 | lists [NW][SEL_LIST] | bits [GB*NS][words] |
-//      bits2 [GB*NS][words] | cnt [GB*NS]   (NS sets per block: H with per-head sets, else 1)
+// LDS: [embedding stage] | stats [NW][H][32] float2 | fin [H][32] | lists [NW][SEL_LIST] |
+//      bits [GB*NS][wst] | bits2 [GB*NS][wst] | cnt [GB*NS]   (NS sets per block: H with
+//      per-head sets, else 1; wst = sel_wstride(M) words per set, an even number)
+__host__ __device__ inline int sel_wstride(int M) { return 2 * ((M + 63) / 64); }
+
 template <typename T, int H, int NS>
 struct SelCfg {
   static constexpr int D = 64 * H;
   static constexpr int EMB_END = EmbedLds<T, SEL_BQ, D>::END;
   static constexpr int STATS = (EMB_END + 15) & ~15;
-  static constexpr int LISTS = STATS + SEL_NW * H * 32 * 8;
+  static constexpr int FIN = STATS + SEL_NW * H * 32 * 8;
+  static constexpr int LISTS = FIN + H * 32 * 4;
   static constexpr int BITS = LISTS + SEL_NW * SEL_LIST * 4;
+  static_assert(BITS % 16 == 0, "16-byte aligned bitmaps");
+  static_assert(SEL_LIST >= 32 * 32, "a wave's list holds its 32 x 32 transposition tile in pass 2");
   __host__ __device__ static int total(int M) {
-    const int words = (M + 31) / 32;
-    return BITS + 2 * SEL_GB * NS * words * 4 + SEL_GB * NS * 4 + 16;
+    return BITS + 2 * SEL_GB * NS * sel_wstride(M) * 4 + SEL_GB * NS * 4 + 16;
   }
 };
 
@@ -254,11 +292,12 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   const int tid0 = threadIdx.x, lane0 = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const int M = A.M, Mp = sel_mpad(M);
-  const int nwords = (M + 31) / 32;
-  float2* stats = reinterpret_cast<float2*>(lds + CF::STATS);     // [NW][H][32]
-  unsigned* bits = reinterpret_cast<unsigned*>(lds + CF::BITS);        // [GB][NS][nwords]
-  unsigned* bits2 = bits + SEL_GB * NS * nwords;                       // [GB][NS][nwords]
-  int* ucount = reinterpret_cast<int*>(bits2 + SEL_GB * NS * nwords);  // [GB][NS]
+  const int nwords = (M + 31) / 32, wst = sel_wstride(M);
+  float2* stats = reinterpret_cast<float2*>(lds + CF::STATS);       // [NW][H][32]
+  float* fin = reinterpret_cast<float*>(lds + CF::FIN);             // [H][32]
+  unsigned* bits = reinterpret_cast<unsigned*>(lds + CF::BITS);     // [GB][NS][wst]
+  unsigned* bits2 = bits + SEL_GB * NS * wst;                       // [GB][NS][wst]
+  int* ucount = reinterpret_cast<int*>(bits2 + SEL_GB * NS * wst);  // [GB][NS]
   float* scores = A.scores + (int64_t)blockIdx.x * SEL_BQ * NS * Mp;   // [BQ][NS][Mp], this workgroup's rows
   unsigned* wlist = reinterpret_cast<unsigned*>(lds + CF::LISTS) + wave * SEL_LIST;  // this wave's top-k list
   const __amdgpu_buffer_rsrc_t sbuf =
@@ -321,21 +360,20 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
 #pragma unroll
         for (int ks = 0; ks < KS_H; ++ks)
           S = MM::mma(t.f[h][ks], *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
-        float mx = NEG;
-        float tt[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tt[r] = S[r] * 0.18033688011112042f;
+        // logits in base 2: t = S * log2(e) / 8 (the scale is positive, so the
+        // largest S gives the largest t)
         if (kb * 32 + 32 > M) {  // (uniform) the last, partial tile: keys past M do not count
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tt[r] = kb * 32 + crow(r, lane) < M ? tt[r] : NEG;
+          for (int r = 0; r < 16; ++r) S[r] = kb * 32 + crow(r, lane) < M ? S[r] : NEG;
         }
+        float mx = S[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, tt[r]);
-        const float mnew = fmaxf(m[h], mx);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        const float mnew = fmaxf(m[h], mx * 0.18033688011112042f);
         if (mnew != NEG) {
           float sum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(tt[r] - mnew);
+          for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], 0.18033688011112042f, -mnew));
           l[h] = l[h] * __builtin_amdgcn_exp2f(m[h] - mnew) + sum;
           m[h] = mnew;
         }
@@ -352,32 +390,56 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       }
       if (lane < 32) stats[(wave * H + h) * 32 + lane] = make_float2(m[h], l[h]);
     }
-    for (int i = tid; i < 2 * SEL_GB * NS * nwords; i += SEL_NT) bits[i] = 0u;
+    for (int i = tid; i < 2 * SEL_GB * NS * wst; i += SEL_NT) bits[i] = 0u;
     __syncthreads();
-    float mf[H], linv[H];
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
+    // per (head, probe): max + log2(sum) over all tokens, so p = exp2(t - fin)
+    if (tid < H * 32) {
+      const int h = tid >> 5, c = tid & 31;
       float mm = NEG, ll = 0.f;
       for (int w = 0; w < SEL_NW; ++w) {
-        const float2 st = stats[(w * H + h) * 32 + col];
+        const float2 st = stats[(w * H + h) * 32 + c];
         const float mn = fmaxf(mm, st.x);
         if (mn != NEG) {
           ll = ll * __builtin_amdgcn_exp2f(mm - mn) + st.y * __builtin_amdgcn_exp2f(st.x - mn);
           mm = mn;
         }
       }
-      mf[h] = mm;
-      linv[h] = 1.f / ll;
+      fin[tid] = mm + __builtin_amdgcn_logf(ll);
     }
+    __syncthreads();
 
     // ---------------------------------------------------------------- pass 2: head-mean (or per-head) probabilities
+    // K Q^T as in pass 1 (register r: token kb*32 + crow(r, lane), probe lane%32),
+    // p = exp2(t - fin). Each wave transposes its 32 x 32 tile through its 4 KB of
+    // the (not yet used) list region, so that every store writes 32 consecutive
+    // tokens of one probe's row; rows are XOR-swizzled by the probe, which keeps
+    // both the column writes and the row reads free of bank conflicts. (Rows of
+    // probes past the group and tokens past M are written too: the scratch rows
+    // hold Mp >= 32 * ceil(M / 32) values and the search reads only rows of the
+    // group's probes and tokens below M.)
     lane = opaque(lane);
     col = lane & 31;
+    float kcol[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) kcol[h] = fin[h * 32 + col];
+    float* tb = reinterpret_cast<float*>(lds + CF::LISTS) + wave * 1024;  // [32 probes][32 tokens], swizzled
+    const int rr = lane >> 5, kk = lane & 31;
+    auto transpose_store = [&](const float (&v)[16], float* dst0, int rstride) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tb[col * 32 + (crow(r, lane) ^ col)] = v[r];
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int pr = 2 * i + rr;
+        dst0[pr * rstride + kk] = tb[pr * 32 + (kk ^ pr)];
+      }
+      __builtin_amdgcn_wave_barrier();  // the tile is read before the next one is written
+    };
     auto score_tile = [&](const KTile<T, H>& t, int kb) {
       float acc[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      const bool full = kb * 32 + 32 <= M;  // (uniform)
 #pragma unroll
       for (int h = 0; h < H; ++h) {
         f32x16 S = zero16();
@@ -385,42 +447,48 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         for (int ks = 0; ks < KS_H; ++ks)
           S = MM::mma(t.f[h][ks], *reinterpret_cast<const Frag*>(qrow + 64 * h + ks * MM::KS), S);
         if constexpr (PH) {
-          // this head's probability is the score row (probe col, head h)
-          if (col < nb * SEL_NP) {
+          // this head's probability is the score row (probe, head h)
+          float pr[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int j = kb * 32 + crow(r, lane);
-              if (full || j < M)
-                scores[(col * NS + h) * Mp + j] = __builtin_amdgcn_exp2f(S[r] * 0.18033688011112042f - mf[h]) * linv[h];
-            }
-          }
+          for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], 0.18033688011112042f, -kcol[h]));
+          transpose_store(pr, scores + h * Mp + kb * 32, NS * Mp);
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc[r] += __builtin_amdgcn_exp2f(S[r] * 0.18033688011112042f - mf[h]) * linv[h];
+          for (int r = 0; r < 16; ++r) acc[r] += __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], 0.18033688011112042f, -kcol[h]));
         }
       }
       if constexpr (!PH) {
-        if (col < nb * SEL_NP) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = kb * 32 + crow(r, lane);
-            if (full || j < M) scores[col * Mp + j] = acc[r] * (1.f / H);
-          }
-        }
+        for (int r = 0; r < 16; ++r) acc[r] *= 1.f / H;
+        transpose_store(acc, scores + kb * 32, Mp);
       }
     };
     over_key_tiles(score_tile);
     __syncthreads();  // the scores rows are complete and visible to the workgroup
 
     // ---------------------------------------------------------------- top-k per probe (and head), union per set
+    // items (set, probe) in set order, a contiguous run per wave: a wave ORs the
+    // masks of its probes of one set and adds them to the set's bitmap once
     tid = opaque(tid);
     lane = opaque(lane);
-    for (int p = wave; p < nb * SEL_NP * NS; p += SEL_NW) {
-      // score row p = probe * NS + head; set (probe / NP) * NS + head
-      unsigned u[SEL_MAXV];
-      load_scores(sbuf, p, Mp, M, lane, u);
-      topk_bits(u, M, A.k, bits + ((p / NS) / SEL_NP * NS + p % NS) * nwords, wlist, lane);
+    {
+      const int nit = nb * SEL_NP * NS, per = (nit + SEL_NW - 1) / SEL_NW;
+      const int it1 = min(nit, (wave + 1) * per);
+      uint64_t acc = 0ull;
+      int cur = -1;
+      for (int it = wave * per; it < it1; ++it) {
+        const int set = it / SEL_NP, pr = it % SEL_NP;
+        if (set != cur) {
+          if (cur >= 0) add_to_bitmap(acc, M, bits + cur * wst, lane);
+          acc = 0ull;
+          cur = set;
+        }
+        // score row (probe, head): probe = block * NP + pr, head = set % NS
+        unsigned u[SEL_MAXV];
+        load_scores(sbuf, ((set / NS) * SEL_NP + pr) * NS + set % NS, Mp, M, lane, u);
+        acc |= topk_mask(u, M, A.k, wlist, lane);
+      }
+      if (cur >= 0) add_to_bitmap(acc, M, bits + cur * wst, lane);
     }
     __syncthreads();
 
@@ -429,7 +497,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
     lane = opaque(lane);
     for (int set = wave; set < nb * NS; set += SEL_NW) {
       const int blk = set / NS, hs = set % NS;
-      unsigned* ub = bits + set * nwords;
+      unsigned* ub = bits + set * wst;
       int cnt = 0;
       for (int i = lane; i < nwords; i += 64) cnt += __popc(ub[i]);
       cnt = wave_sum(cnt);
@@ -450,8 +518,8 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
           const bool member = idx < M && ((ub[idx >> 5] >> (idx & 31)) & 1u);
           u[i] = member ? u[i] + 1u : 0u;
         }
-        topk_bits(u, M, A.cap, bits2 + set * nwords, wlist, lane);
-        outbits = bits2 + set * nwords;
+        add_to_bitmap(topk_mask(u, M, A.cap, wlist, lane), M, bits2 + set * wst, lane);
+        outbits = bits2 + set * wst;
       }
       const int64_t row = (row0 + blk) * NS + hs;  // output row: [block][head] with per-head sets
       int32_t* out = A.sel_idx + row * (int64_t)A.cap;
