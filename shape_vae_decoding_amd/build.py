@@ -2,6 +2,10 @@
 object under _build/, then linked into shape_vae_decoding_amd/libvdm.so.
 
     python shape_vae_decoding_amd/build.py
+
+build_sanitized(out_dir) builds the same library with AddressSanitizer and
+UndefinedBehaviorSanitizer on its host code (device code is compiled as usual)
+into out_dir/libvdm_asan.so, for host-side checks of the C ABI.
 """
 
 from __future__ import annotations
@@ -32,9 +36,14 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+# host code only (device code cannot take them): every sanitizer flag follows -Xarch_host
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
@@ -58,6 +67,20 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
     return LIB
+
+
+def build_sanitized(out_dir: str) -> str:
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    extra = ["-g", *SAN_HOST]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda f: _compile(f, out_dir, extra), srcs))
+    lib = os.path.join(out_dir, "libvdm_asan.so")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", *SAN_HOST, "-o", lib, *objs], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return lib
 
 
 if __name__ == "__main__":
