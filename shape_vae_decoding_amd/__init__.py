@@ -94,61 +94,82 @@ class _HierDebug(C.Structure):
 
 
 _st = C.c_int32
-_lib.vdm_embed_queries.argtypes = [C.POINTER(_Decoder), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
-_lib.vdm_embed_queries.restype = _st
-_lib.vdm_project_kv.argtypes = [C.POINTER(_Decoder), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]
-_lib.vdm_project_kv.restype = _st
-_lib.vdm_decode_dense.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_void_p, C.c_void_p, C.c_int64,
-                                  C.POINTER(_KvSel), C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
-_lib.vdm_decode_dense.restype = _st
-_lib.vdm_decode_dense_noalloc.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_void_p, C.c_void_p,
-                                          C.c_int64, C.c_void_p, C.c_void_p]
-_lib.vdm_decode_dense_noalloc.restype = _st
-_lib.vdm_select_kv.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                               C.c_uint64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
-                               C.c_void_p, C.c_size_t, C.c_void_p]
-_lib.vdm_select_kv.restype = _st
-_lib.vdm_select_kv_heads.argtypes = _lib.vdm_select_kv.argtypes
-_lib.vdm_select_kv_heads.restype = _st
-_lib.vdm_select_heads_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64]
-_lib.vdm_select_heads_workspace_size.restype = C.c_size_t
-_lib.vdm_decode_hier.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_void_p, C.c_void_p, C.c_int64,
-                                 C.c_void_p, C.c_int64, C.c_void_p, C.POINTER(_HierDebug), C.c_void_p, C.c_size_t,
-                                 C.c_void_p]
-_lib.vdm_decode_hier.restype = _st
-_lib.vdm_dense_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64, C.c_int64, C.c_int32]
-_lib.vdm_dense_workspace_size.restype = C.c_size_t
-_lib.vdm_select_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64]
-_lib.vdm_select_workspace_size.restype = C.c_size_t
-_lib.vdm_hier_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int64]
-_lib.vdm_hier_workspace_size.restype = C.c_size_t
-_lib.vdm_extract_surface.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
-                                     C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
-_lib.vdm_extract_surface.restype = _st
-_lib.vdm_surface_workspace_size.argtypes = [C.c_int32]
-_lib.vdm_surface_workspace_size.restype = C.c_size_t
-_lib.vdm_decode_dense_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_int32, C.c_void_p, C.c_void_p,
-                                        C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
-_lib.vdm_decode_dense_batch.restype = _st
-_lib.vdm_dense_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int64]
-_lib.vdm_dense_batch_workspace_size.restype = C.c_size_t
-_lib.vdm_decode_hier_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_void_p,
-                                       C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
-                                       C.c_size_t, C.c_void_p]
-_lib.vdm_decode_hier_batch.restype = _st
-_lib.vdm_hier_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_int64]
-_lib.vdm_hier_batch_workspace_size.restype = C.c_size_t
-_lib.vdm_decode_local.argtypes = [C.POINTER(_LocalDecoder), C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
-                                  C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
-_lib.vdm_decode_local.restype = _st
-_lib.vdm_local_workspace_size.argtypes = [C.POINTER(_LocalDecoder), C.c_int64, C.c_int64]
-_lib.vdm_local_workspace_size.restype = C.c_size_t
-_lib.vdm_timing.argtypes = [C.c_int32]
-_lib.vdm_timing.restype = C.c_int
-_lib.vdm_timing_read.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
-_lib.vdm_timing_read.restype = C.c_int
-_lib.vdm_version.restype = C.c_int32
-_lib.vdm_last_error.restype = C.c_char_p
+
+
+def _bind(lib) -> None:
+    """Argument and result types of every entry point of a build of the library."""
+    lib.vdm_embed_queries.argtypes = [C.POINTER(_Decoder), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+    lib.vdm_embed_queries.restype = _st
+    lib.vdm_project_kv.argtypes = [C.POINTER(_Decoder), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.vdm_project_kv.restype = _st
+    lib.vdm_decode_dense.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_void_p, C.c_void_p, C.c_int64,
+                                      C.POINTER(_KvSel), C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.vdm_decode_dense.restype = _st
+    lib.vdm_decode_dense_noalloc.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_void_p, C.c_void_p,
+                                              C.c_int64, C.c_void_p, C.c_void_p]
+    lib.vdm_decode_dense_noalloc.restype = _st
+    lib.vdm_select_kv.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                   C.c_uint64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.vdm_select_kv.restype = _st
+    lib.vdm_select_kv_heads.argtypes = lib.vdm_select_kv.argtypes
+    lib.vdm_select_kv_heads.restype = _st
+    lib.vdm_select_heads_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64]
+    lib.vdm_select_heads_workspace_size.restype = C.c_size_t
+    lib.vdm_decode_hier.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_void_p, C.c_void_p, C.c_int64,
+                                     C.c_void_p, C.c_int64, C.c_void_p, C.POINTER(_HierDebug), C.c_void_p, C.c_size_t,
+                                     C.c_void_p]
+    lib.vdm_decode_hier.restype = _st
+    lib.vdm_dense_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64, C.c_int64, C.c_int32]
+    lib.vdm_dense_workspace_size.restype = C.c_size_t
+    lib.vdm_select_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int64]
+    lib.vdm_select_workspace_size.restype = C.c_size_t
+    lib.vdm_hier_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int64]
+    lib.vdm_hier_workspace_size.restype = C.c_size_t
+    lib.vdm_extract_surface.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                                         C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.vdm_extract_surface.restype = _st
+    lib.vdm_surface_workspace_size.argtypes = [C.c_int32]
+    lib.vdm_surface_workspace_size.restype = C.c_size_t
+    lib.vdm_decode_dense_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_Queries), C.c_int32, C.c_void_p, C.c_void_p,
+                                            C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.vdm_decode_dense_batch.restype = _st
+    lib.vdm_dense_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.c_int32, C.c_int64]
+    lib.vdm_dense_batch_workspace_size.restype = C.c_size_t
+    lib.vdm_decode_hier_batch.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_void_p,
+                                           C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                           C.c_size_t, C.c_void_p]
+    lib.vdm_decode_hier_batch.restype = _st
+    lib.vdm_hier_batch_workspace_size.argtypes = [C.POINTER(_Decoder), C.POINTER(_HierParams), C.c_int32, C.c_int64]
+    lib.vdm_hier_batch_workspace_size.restype = C.c_size_t
+    lib.vdm_decode_local.argtypes = [C.POINTER(_LocalDecoder), C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                                      C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.vdm_decode_local.restype = _st
+    lib.vdm_local_workspace_size.argtypes = [C.POINTER(_LocalDecoder), C.c_int64, C.c_int64]
+    lib.vdm_local_workspace_size.restype = C.c_size_t
+    lib.vdm_timing.argtypes = [C.c_int32]
+    lib.vdm_timing.restype = C.c_int
+    lib.vdm_timing_read.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
+    lib.vdm_timing_read.restype = C.c_int
+    lib.vdm_version.restype = C.c_int32
+    lib.vdm_last_error.restype = C.c_char_p
+
+
+_bind(_lib)
+
+# the bounds-checked build (VDM_DEBUG): every data-dependent index in the kernels
+# is checked and each call reports the first failed check (see debug_library)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libvdm_debug.so")
+
+
+def debug_library():
+    """The bounds-checked build of the library, bound like the default one.
+    Assigning it to this module's ``_lib`` routes every wrapper through it."""
+    if not os.path.exists(DEBUG_LIB_PATH):
+        raise ImportError(f"{DEBUG_LIB_PATH} is not built; run `python shape_vae_decoding_amd/build.py`")
+    lib = C.CDLL(DEBUG_LIB_PATH)
+    _bind(lib)
+    return lib
 
 
 def vdm_version() -> int:

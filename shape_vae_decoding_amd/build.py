@@ -1,5 +1,6 @@
 """Build libvdm.so (HIP for gfx950) in-tree: every csrc/*.hip compiled to an
-object under _build/, then linked into shape_vae_decoding_amd/libvdm.so.
+object under _build/, then linked into shape_vae_decoding_amd/libvdm.so; then the
+bounds-checked build (-DVDM_DEBUG=1) into shape_vae_decoding_amd/libvdm_debug.so.
 
     python shape_vae_decoding_amd/build.py
 
@@ -21,6 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvdm.so")
+LIB_DEBUG = os.path.join(PKG, "libvdm_debug.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -54,18 +56,25 @@ def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def _build_lib(lib: str, out_dir: str, extra=(), verbose: bool = True) -> str:
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, out_dir, extra), srcs))
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-o", tmp, *objs], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {lib} from {len(srcs)} sources")
+    return lib
+
+
+def build(verbose: bool = True) -> str:
+    """The library, then its bounds-checked build (libvdm_debug.so: -DVDM_DEBUG=1)."""
+    _build_lib(LIB, BUILD, verbose=verbose)
+    _build_lib(LIB_DEBUG, os.path.join(BUILD, "debug"), ["-DVDM_DEBUG=1"], verbose=verbose)
     return LIB
 
 

@@ -156,7 +156,10 @@ __device__ __forceinline__ void gelu_tile(f32x16& h, const float2* tab) {
 constexpr float SOFTMAX_SCALE_LOG2 = 0.18033688011112042f;
 
 // token ids of a selection are clamped into [0, M) so that no input can index past K/V
-__device__ __forceinline__ int tok_clamp(int t, int M) { return t < 0 ? 0 : (t >= M ? M - 1 : t); }
+__device__ __forceinline__ int tok_clamp(int t, int M) {
+  (void)VDM_BOUND(t >= 0 && t < M, BC_DECODE_TOKEN);
+  return t < 0 ? 0 : (t >= M ? M - 1 : t);
+}
 
 // Packed K/V operands are read with buffer loads: the tile/head base is a scalar
 // offset, the lane's run a fixed vector offset; reads past the buffer's size
@@ -943,6 +946,9 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       q0 = __builtin_amdgcn_readfirstlane(it.q0);
       q1 = __builtin_amdgcn_readfirstlane(it.q1);
       row = __builtin_amdgcn_readfirstlane(it.row);
+      // (uniform: the whole workgroup skips a malformed item, before any barrier)
+      if (!VDM_BOUND(q0 >= 0 && q0 <= q1 && q1 <= nq && q1 - q0 <= C::BQ, BC_DECODE_ITEM)) continue;
+      if (!VDM_BOUND(!GATHER || row >= 0, BC_DECODE_ROW)) continue;
     } else {
       int64_t lt = tile;
       if (nbatch > 1) {
@@ -987,6 +993,7 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     // gathered: this wave's token set (per-head sets: selection row row * H + head)
     const int64_t srow = GATHER ? (A.heads ? (int64_t)row * C::H + hw : row) : 0;
     const int nkeys = GATHER ? min(max(A.sel_cnt[srow], 0), A.cap) : A.M;
+    if (GATHER) (void)VDM_BOUND(A.sel_cnt[srow] >= 0 && A.sel_cnt[srow] <= A.cap, BC_DECODE_SET);
     const int32_t* sel = GATHER ? A.sel_idx + srow * A.cap : nullptr;
 
     f32x16 O[2][C::QB];
@@ -1347,5 +1354,7 @@ int decode_f_chunk(int dtype, int D) {
   if (dtype == VDM_BF16) return CfgB64::FC;
   return CfgF64::FC;
 }
+
+VDM_DEBUG_READER(debug_take_decode)
 
 }  // namespace vdm

@@ -233,11 +233,11 @@ hipError_t launch_cell_test(BP<const float> vol, int R, BP<const uint64_t> kept_
 }
 
 // ------------------------------------------------------------------ dilation
-// One thread per 8x8x8 cell block: OR over the 3x3x3 neighbourhood, separably
-// along k (bit shifts inside each 8-bit row), j (shifts by 8) and i (neighbouring
-// rows). The thread forms the (j, k)-dilated word of each row 8bi-1 .. 8bi+8 once
-// (neighbour blocks supply the halo) and ORs three of them per output row. Cells
-// outside [0, R)^3 stay clear.
+// One thread per word (8 consecutive lanes: the 8 rows of one block, so every
+// load of a wave reads whole 64-byte blocks): OR over the 3x3x3 neighbourhood,
+// separably along k (bit shifts inside each 8-bit row), j (shifts by 8) and i
+// (neighbouring rows), with neighbour blocks supplying the halo. Cells outside
+// [0, R)^3 stay clear.
 __device__ __forceinline__ uint64_t dil_k(uint64_t w, uint64_t wl, uint64_t wr) {
   const uint64_t C0 = 0x0101010101010101ull, C7 = 0x8080808080808080ull;
   return w | ((w << 1) & ~C0) | ((wl >> 7) & C0) | ((w >> 1) & ~C7) | ((wr << 7) & C7);
@@ -246,7 +246,7 @@ __device__ __forceinline__ uint64_t dil_j(uint64_t t, uint64_t td, uint64_t tu) 
   return t | (t << 8) | (td >> 56) | (t >> 8) | (tu << 56);
 }
 
-// Bits of the 8x8 (j, k) cells of block (bj, bk) that lie inside [0, R)^2.
+// Bits of the 8x8 (j, k) cells of block (bj, bk) that lie inside [0, lim)^2.
 __device__ __forceinline__ uint64_t inside_jk(int lim, int bj, int bk) {
   const int nj = min(max(lim - 8 * bj, 0), 8), nk = min(max(lim - 8 * bk, 0), 8);
   const uint64_t rows = nj >= 8 ? ~0ull : ((1ull << (8 * nj)) - 1ull);
@@ -267,49 +267,36 @@ __global__ __launch_bounds__(256) void dilate_kernel(BP<const uint64_t> ib, BP<u
   const uint64_t* __restrict__ in = ib.at();
   uint64_t* __restrict__ out = ob.at();
   int64_t* part = pb.p ? pb.at() : nullptr;
-  const int b = (int)blockIdx.x * 256 + (int)threadIdx.x;
-  int cnt = 0;
-  if (b < NB * NB * NB) {
+  const int w = (int)blockIdx.x * 256 + (int)threadIdx.x;  // word; NB^3 * 8 < 2^31 (R <= 1200)
+  uint64_t res = 0;
+  if (w < NB * NB * NB * 8) {
+    const int b = w >> 3, ii = w & 7;
     const int bi = b / (NB * NB), r2 = b - bi * NB * NB, bj = r2 / NB, bk = r2 - bj * NB;
-    const uint64_t m = inside_jk(R, bj, bk);
-    uint64_t res[8];
-    if (identity) {
+    const int i = 8 * bi + ii;
+    if (i < R && identity) {
+      res = in[w];
+    } else if (i < R) {
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) res[ii] = in[(int64_t)b * 8 + ii];
-    } else {
-      // (j, k)-dilated word of cell row i (0 outside [0, R))
-      auto row = [&](int i) -> uint64_t {
-        if (i < 0 || i >= R) return 0ull;
-        const int64_t base = (int64_t)(i >> 3) * NB;
+      for (int di = -1; di <= 1; ++di) {
+        const int i2 = i + di;
+        if (i2 < 0 || i2 >= R) continue;
+        const int64_t base = (int64_t)(i2 >> 3) * NB;
         uint64_t W[3][3];
 #pragma unroll
         for (int a = 0; a < 3; ++a)
 #pragma unroll
           for (int c = 0; c < 3; ++c) {
             const int bj2 = bj + a - 1, bk2 = bk + c - 1;
-            W[a][c] = (bj2 >= 0 && bj2 < NB && bk2 >= 0 && bk2 < NB) ? in[((base + bj2) * NB + bk2) * 8 + (i & 7)] : 0ull;
+            W[a][c] = (bj2 >= 0 && bj2 < NB && bk2 >= 0 && bk2 < NB) ? in[((base + bj2) * NB + bk2) * 8 + (i2 & 7)] : 0ull;
           }
-        return dil_j(dil_k(W[1][1], W[1][0], W[1][2]), dil_k(W[0][1], W[0][0], W[0][2]),
-                     dil_k(W[2][1], W[2][0], W[2][2]));
-      };
-      uint64_t tp = row(8 * bi - 1), tc = row(8 * bi);
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const uint64_t tn = row(8 * bi + ii + 1);
-        res[ii] = tp | tc | tn;
-        tp = tc;
-        tc = tn;
+        res |= dil_j(dil_k(W[1][1], W[1][0], W[1][2]), dil_k(W[0][1], W[0][0], W[0][2]), dil_k(W[2][1], W[2][0], W[2][2]));
       }
     }
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {  // clip to cells inside the grid
-      res[ii] &= 8 * bi + ii < R ? m : 0ull;
-      cnt += __popcll(res[ii]);
-    }
-    store_block(out + (int64_t)b * 8, res);
+    res &= i < R ? inside_jk(R, bj, bk) : 0ull;  // clip to cells inside the grid
+    out[w] = res;
   }
   if (part) {
-    const int64_t n = block_sum_i64(cnt, red, threadIdx.x, 256);
+    const int64_t n = block_sum_i64(__popcll(res), red, threadIdx.x, 256);
     if (threadIdx.x == 0 && n) atomicAdd((unsigned long long*)(part + (blockIdx.x % STAT_SLOTS) * 8 + 2), (unsigned long long)n);
   }
 }
@@ -317,8 +304,8 @@ __global__ __launch_bounds__(256) void dilate_kernel(BP<const uint64_t> ib, BP<u
 hipError_t launch_dilate(BP<const uint64_t> in, BP<uint64_t> out, int R, int identity, BP<int64_t> part,
                          BP<int64_t> stat, int B, hipStream_t s) {
   const int NB = nblocks8(R + 1);
-  const int64_t nb3 = (int64_t)NB * NB * NB;
-  hipLaunchKernelGGL(dilate_kernel, dim3((unsigned)((nb3 + 255) / 256), (unsigned)B), dim3(256), 0, s, in, out, R, NB,
+  const int64_t nw = (int64_t)NB * NB * NB * 8;
+  hipLaunchKernelGGL(dilate_kernel, dim3((unsigned)((nw + 255) / 256), (unsigned)B), dim3(256), 0, s, in, out, R, NB,
                      identity, stat.p ? part : BP<int64_t>{nullptr, 0});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !stat.p) return e;
@@ -522,7 +509,7 @@ __global__ __launch_bounds__(SCAN_NT) void scan_apply_kernel(BP<const int32_t> c
   for (int e = 0; e < SCAN_PER; ++e) {
     if (base + e < n) {
       offs[base + e] = run;
-      if (v[e].z) occ[run.z] = (int32_t)(base + e);  // occupied blocks in block order
+      if (v[e].z && VDM_BOUND(run.z < n, BC_SCAN_OCC)) occ[run.z] = (int32_t)(base + e);  // occupied blocks in block order
     }
     run = add4(run, v[e]);
   }
@@ -548,7 +535,7 @@ constexpr int EMIT_NT = 256;
 __global__ __launch_bounds__(EMIT_NT) void emit_kernel(BP<const uint64_t> nmb, BP<const int32_t> cb,
                                                        BP<const int4> ob, BP<const int32_t> occb,
                                                        BP<const int32_t> tb, int Rn, int bq, BP<int32_t> lb,
-                                                       BP<Item> ib) {
+                                                       BP<Item> ib, int64_t list_cap, int64_t item_cap) {
   const uint64_t* __restrict__ newmask = nmb.at();
   const int32_t* __restrict__ counts = cb.at();
   const int4* __restrict__ offs = ob.at();
@@ -573,21 +560,22 @@ __global__ __launch_bounds__(EMIT_NT) void emit_kernel(BP<const uint64_t> nmb, B
       const uint64_t w = newmask[b * 8 + ii];
       if ((w >> lane) & 1ull) {
         const int rank = before + __popcll(w & ((1ull << lane) - 1ull));
-        list[of.x + rank] = (int32_t)(((int64_t)(8 * bi + ii) * P + J) * P + K);
+        if (VDM_BOUND((int64_t)of.x + rank < list_cap, BC_EMIT_LIST))
+          list[of.x + rank] = (int32_t)(((int64_t)(8 * bi + ii) * P + J) * P + K);
       }
       before += __popcll(w);
     }
     const int nchunks = (c + bq - 1) / bq;
     for (int ch = lane; ch < nchunks; ch += 64) {
       const int q0 = of.x + ch * bq;
-      items[of.y + ch] = Item{q0, min(q0 + bq, of.x + c), of.z, 0};
+      if (VDM_BOUND((int64_t)of.y + ch < item_cap, BC_EMIT_ITEM)) items[of.y + ch] = Item{q0, min(q0 + bq, of.x + c), of.z, 0};
     }
   }
 }
 
 hipError_t launch_emit(BP<const uint64_t> newmask, BP<const int32_t> counts, BP<const int4> offs,
                        BP<const int32_t> occ, BP<const int32_t> tot, int Rn, int bq, BP<int32_t> list,
-                       BP<Item> items, int B, hipStream_t s) {
+                       int64_t list_cap, BP<Item> items, int64_t item_cap, int B, hipStream_t s) {
   const int NB = nblocks8(Rn + 1);
   const int64_t nb3 = (int64_t)NB * NB * NB;
   int64_t g = (nb3 + EMIT_NT / 64 - 1) / (EMIT_NT / 64);
@@ -595,7 +583,7 @@ hipError_t launch_emit(BP<const uint64_t> newmask, BP<const int32_t> counts, BP<
   if (g > cap) g = cap;
   if (g < 1) g = 1;
   hipLaunchKernelGGL(emit_kernel, dim3((unsigned)g, (unsigned)B), dim3(EMIT_NT), 0, s, newmask, counts, offs, occ, tot,
-                     Rn, bq, list, items);
+                     Rn, bq, list, items, list_cap, item_cap);
   return hipGetLastError();
 }
 
@@ -756,6 +744,7 @@ __global__ void items_from_list_kernel(const int32_t* __restrict__ list, int64_t
   const int nch = (int)((e - q + bq - 1) / bq);
   const int at = atomicAdd(n_items, nch);
   const int row = block_row ? block_row[b] : (int)b;
+  (void)VDM_BOUND(row >= 0, BC_LIST_ROW);
   for (int c = 0; c < nch; ++c) {
     const int64_t q0 = q + (int64_t)c * bq;
     items[at + c] = Item{(int32_t)q0, (int32_t)min(q0 + bq, e), row, 0};
@@ -768,5 +757,7 @@ hipError_t launch_items_from_list(const int32_t* list, int64_t N, int R, int blo
                      block_row, bq, items, n_items, out);
   return hipGetLastError();
 }
+
+VDM_DEBUG_READER(debug_take_hvd)
 
 }  // namespace vdm

@@ -95,6 +95,7 @@ __global__ void local_scatter_kernel(const float* __restrict__ xyz, int64_t n, c
   if (j >= n) return;
   const int c = cell_of[j];
   const int at = starts[c] + atomicAdd(&fill[c], 1);
+  if (!VDM_BOUND(at >= 0 && at < n, BC_LOCAL_SCATTER)) return;
   if (spos) spos[at] = make_float4(xyz[3 * j], xyz[3 * j + 1], xyz[3 * j + 2], __int_as_float((int)j));
   if (order) order[at] = (int32_t)j;
 }
@@ -150,6 +151,8 @@ __global__ __launch_bounds__(KNN_THREADS) void local_knn_kernel(const float* __r
   const int64_t t = (int64_t)blockIdx.x * KNN_THREADS + threadIdx.x;
   if (t >= N) return;
   const int64_t q = order[t];
+  if (!VDM_BOUND(q >= 0 && q < N, BC_LOCAL_QUERY)) return;
+  [[maybe_unused]] const int mtot = VDM_DEBUG ? starts[LOCAL_NC] : 0;  // the support count (bounds-checked builds)
   const float x = xyz[3 * q], y = xyz[3 * q + 1], z = xyz[3 * q + 2];
   const int c[3] = {local_cell(x), local_cell(y), local_cell(z)};
   const float xv[3] = {x, y, z};
@@ -188,6 +191,7 @@ __global__ __launch_bounds__(KNN_THREADS) void local_knn_kernel(const float* __r
   };
   // the supports spos[lo .. hi), four loads in flight at a time
   auto visit = [&](int lo, int hi) {
+    if (!VDM_BOUND(lo >= 0 && lo <= hi && (!VDM_DEBUG || hi <= mtot), BC_LOCAL_RANGE)) return;
     int u = lo;
     for (; u + 4 <= hi; u += 4) {
       const float4 p0 = spos[u], p1 = spos[u + 1], p2 = spos[u + 2], p3 = spos[u + 3];
@@ -382,5 +386,7 @@ hipError_t launch_local_fuse(const LocalFuseArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(local_fuse_kernel, dim3((unsigned)grid), dim3(64 * FUSE_WAVES), lds, s, a);
   return hipGetLastError();
 }
+
+VDM_DEBUG_READER(debug_take_local)
 
 }  // namespace vdm

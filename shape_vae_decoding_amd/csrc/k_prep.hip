@@ -200,4 +200,6 @@ hipError_t launch_embed(int dtype, int D, const QuerySrc& qs, int64_t N, const v
   return embed_t<float, 64>(qs, N, Wq, Q, s);
 }
 
+VDM_DEBUG_READER(debug_take_prep)
+
 }  // namespace vdm

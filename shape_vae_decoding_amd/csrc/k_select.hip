@@ -522,6 +522,13 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         outbits = bits2 + set * wst;
       }
       const int64_t row = (row0 + blk) * NS + hs;  // output row: [block][head] with per-head sets
+#if VDM_DEBUG
+      if (lane == 0) {
+        const int NBs = (A.R + A.block) / A.block;
+        const int64_t bid = A.blocks ? A.blocks[row0 + blk] : row0 + blk;
+        (void)VDM_BOUND(bid >= 0 && bid < (int64_t)NBs * NBs * NBs, BC_SELECT_BLOCK);
+      }
+#endif
       int32_t* out = A.sel_idx + row * (int64_t)A.cap;
       int base = 0;
       for (int w0 = 0; w0 < nwords; w0 += 64) {
@@ -532,7 +539,8 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         int off = base + incl - c;
         while (word) {
           const int b = __ffs(word) - 1;
-          out[off++] = wi * 32 + b;
+          if (VDM_BOUND(off < A.cap, BC_SELECT_OUT)) out[off] = wi * 32 + b;
+          ++off;
           word &= word - 1u;
         }
         base += __shfl(incl, 63);
@@ -580,5 +588,7 @@ hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s) {
   if (dtype == VDM_BF16) return run_select<bf16, 1, false>(a, s);
   return run_select<float, 1, false>(a, s);
 }
+
+VDM_DEBUG_READER(debug_take_select)
 
 }  // namespace vdm

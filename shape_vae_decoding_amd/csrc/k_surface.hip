@@ -570,4 +570,6 @@ hipError_t launch_surface(const float* vol, int R, const uint8_t* mask, float* v
   return hipGetLastError();
 }
 
+VDM_DEBUG_READER(debug_take_surface)
+
 }  // namespace vdm

@@ -276,6 +276,7 @@ struct HierWs {
   int32_t* totals;  // [levels][4]: queries, items, occupied blocks
   int32_t* list;
   Item* items;
+  int64_t list_cap, item_cap;  // entries of list and items
   int32_t* occ;
   int32_t* sel_idx;
   int32_t* sel_cnt;
@@ -312,8 +313,10 @@ static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M,
   x.offs = c.take<int4>((size_t)maxNB3 * 16);
   x.partial = c.take<int4>((size_t)scan_partials(maxNB3) * 16);
   x.totals = c.take<int32_t>((size_t)VDM_MAX_LEVELS * 4 * 4);
-  x.list = c.take<int32_t>((size_t)maxP3 * 4);
-  x.items = c.take<Item>((size_t)maxNB3 * ((512 + bq - 1) / bq) * sizeof(Item));
+  x.list_cap = maxP3;
+  x.item_cap = maxNB3 * ((512 + bq - 1) / bq);
+  x.list = c.take<int32_t>((size_t)x.list_cap * 4);
+  x.items = c.take<Item>((size_t)x.item_cap * sizeof(Item));
   x.occ = c.take<int32_t>((size_t)maxNB3 * 4);
   if (p->use_kvsel) {
     const int ns = sel_sets(d, p->heads != 0);
@@ -350,6 +353,47 @@ static vdm_status check_hier(const vdm_decoder* d, const vdm_hier_params* p, int
 }  // namespace vdm
 
 using namespace vdm;
+
+
+// Bounds-checked builds: after a call's launches, wait for them and report the
+// first failed device bounds check of any kernel file (VDM_BOUND). Release builds
+// return the status unchanged.
+static vdm_status debug_checked(vdm_status st, vdm_stream stream) {
+#if VDM_DEBUG
+  if (st != VDM_OK) return st;
+  static const char* const what[BC_CHECKS] = {
+      "",
+      "work item query range",
+      "work item selection row",
+      "selection row count",
+      "selected token id",
+      "block selection row",
+      "selection block id",
+      "selection output slot",
+      "query list slot",
+      "work item slot",
+      "occupied block slot",
+      "support slot",
+      "cell support range",
+      "query index in cell order"};
+  hipError_t (*const take[])(unsigned*) = {debug_take_decode, debug_take_select, debug_take_hvd,
+                                            debug_take_local,  debug_take_prep,   debug_take_surface};
+  static const char* const file[] = {"decode", "select", "hvd", "local", "prep", "surface"};
+  VDM_HIP(hipStreamSynchronize((hipStream_t)stream), "bounds-check synchronize");
+  vdm_status out = VDM_OK;
+  for (int f = 0; f < 6; ++f) {
+    unsigned w = 0;
+    VDM_HIP(take[f](&w), "bounds-check read");
+    if (w != 0 && out == VDM_OK)
+      out = fail(VDM_ERR_HIP, "bounds check failed in the %s kernels: %s (check %u)", file[f],
+                 w < BC_CHECKS ? what[w] : "?", w);
+  }
+  return out;
+#else
+  (void)stream;
+  return st;
+#endif
+}
 
 extern "C" {
 
@@ -446,7 +490,7 @@ size_t vdm_hier_batch_workspace_size(const vdm_decoder* dec, const vdm_hier_para
   return hier_batch_stride(dec, params, M) * (size_t)B;
 }
 
-vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* p, int32_t B, const void* K,
+static vdm_status decode_hier_batch_body(const vdm_decoder* dec, const vdm_hier_params* p, int32_t B, const void* K,
                                  const void* V, int64_t M, float* vol, int64_t vol_elems, int64_t* stats, void* ws,
                                  size_t ws_bytes, vdm_stream stream) {
   vdm_status st = check_decoder(dec);
@@ -471,6 +515,12 @@ vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* 
   return hier_run(dec, p, B, K, V, M, kv_bytes, vol, P3, S, sst, nullptr, ws, stride, (hipStream_t)stream);
 }
 
+vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* p, int32_t B, const void* K,
+                                 const void* V, int64_t M, float* vol, int64_t vol_elems, int64_t* stats, void* ws,
+                                 size_t ws_bytes, vdm_stream stream) {
+  return debug_checked(decode_hier_batch_body(dec, p, B, K, V, M, vol, vol_elems, stats, ws, ws_bytes, stream), stream);
+}
+
 // ------------------------------------------------------------------ surface extraction
 static vdm_status check_surface(int32_t R) {
   if (R < 1 || R > 893) return fail(VDM_ERR_INVALID_ARG, "R=%d (1 <= R <= 893)", R);
@@ -482,7 +532,7 @@ size_t vdm_surface_workspace_size(int32_t R) {
   return surface_ws_layout(R).bytes;
 }
 
-vdm_status vdm_extract_surface(const float* vol, int32_t R, const uint8_t* cell_mask, float* verts,
+static vdm_status extract_surface_body(const float* vol, int32_t R, const uint8_t* cell_mask, float* verts,
                                int64_t max_verts, int32_t* tris, int64_t max_tris, int64_t* vert_edges,
                                int64_t* counts, void* ws, size_t ws_bytes, vdm_stream stream) {
   vdm_status st = check_surface(R);
@@ -504,7 +554,14 @@ vdm_status vdm_extract_surface(const float* vol, int32_t R, const uint8_t* cell_
   return VDM_OK;
 }
 
-vdm_status vdm_embed_queries(const vdm_decoder* dec, const float* xyz, int64_t N, void* Q, vdm_stream stream) {
+vdm_status vdm_extract_surface(const float* vol, int32_t R, const uint8_t* cell_mask, float* verts,
+                               int64_t max_verts, int32_t* tris, int64_t max_tris, int64_t* vert_edges,
+                               int64_t* counts, void* ws, size_t ws_bytes, vdm_stream stream) {
+  return debug_checked(extract_surface_body(vol, R, cell_mask, verts, max_verts, tris, max_tris, vert_edges, counts,
+                                            ws, ws_bytes, stream), stream);
+}
+
+static vdm_status embed_queries_body(const vdm_decoder* dec, const float* xyz, int64_t N, void* Q, vdm_stream stream) {
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;
   if (N < 0 || N >= (1ll << 31)) return fail(VDM_ERR_INVALID_ARG, "N=%lld", (long long)N);
@@ -517,7 +574,11 @@ vdm_status vdm_embed_queries(const vdm_decoder* dec, const float* xyz, int64_t N
   return VDM_OK;
 }
 
-vdm_status vdm_project_kv(const vdm_decoder* dec, const void* Z, int64_t M, void* K, void* V, vdm_stream stream) {
+vdm_status vdm_embed_queries(const vdm_decoder* dec, const float* xyz, int64_t N, void* Q, vdm_stream stream) {
+  return debug_checked(embed_queries_body(dec, xyz, N, Q, stream), stream);
+}
+
+static vdm_status project_kv_body(const vdm_decoder* dec, const void* Z, int64_t M, void* K, void* V, vdm_stream stream) {
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;
   if (M < 0 || M >= (1ll << 31) / dec->D) return fail(VDM_ERR_INVALID_ARG, "M=%lld", (long long)M);
@@ -528,6 +589,10 @@ vdm_status vdm_project_kv(const vdm_decoder* dec, const void* Z, int64_t M, void
   VDM_HIP_T(VDM_TIME_PROJECT_KV, (hipStream_t)stream, launch_project_kv(dec->dtype, Z, dec->Wk, dec->Wv, (int)M, dec->D, K, V, (hipStream_t)stream),
           "project_kv launch");
   return VDM_OK;
+}
+
+vdm_status vdm_project_kv(const vdm_decoder* dec, const void* Z, int64_t M, void* K, void* V, vdm_stream stream) {
+  return debug_checked(project_kv_body(dec, Z, M, K, V, stream), stream);
 }
 
 // Checks shared by the dense decode calls (decoder, queries, K/V, output).
@@ -612,7 +677,7 @@ static vdm_status noalloc_scratch(void** out) {
   return VDM_OK;
 }
 
-vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V, int64_t M,
+static vdm_status decode_dense_body(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V, int64_t M,
                             const vdm_kvsel* sel, float* sdf, void* ws, size_t ws_bytes, vdm_stream stream) {
   bool done = false;
   vdm_status st = check_dense(dec, q, K, V, M, sdf, &done);
@@ -659,7 +724,12 @@ vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const 
   return VDM_OK;
 }
 
-vdm_status vdm_decode_dense_noalloc(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V,
+vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V, int64_t M,
+                            const vdm_kvsel* sel, float* sdf, void* ws, size_t ws_bytes, vdm_stream stream) {
+  return debug_checked(decode_dense_body(dec, q, K, V, M, sel, sdf, ws, ws_bytes, stream), stream);
+}
+
+static vdm_status decode_dense_noalloc_body(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V,
                                     int64_t M, float* sdf, vdm_stream stream) {
   bool done = false;
   vdm_status st = check_dense(dec, q, K, V, M, sdf, &done);
@@ -677,6 +747,11 @@ vdm_status vdm_decode_dense_noalloc(const vdm_decoder* dec, const vdm_queries* q
   return dense_full(dec, q, K, V, M, sdf, w, (hipStream_t)stream, false);
 }
 
+vdm_status vdm_decode_dense_noalloc(const vdm_decoder* dec, const vdm_queries* q, const void* K, const void* V,
+                                    int64_t M, float* sdf, vdm_stream stream) {
+  return debug_checked(decode_dense_noalloc_body(dec, q, K, V, M, sdf, stream), stream);
+}
+
 size_t vdm_dense_batch_workspace_size(const vdm_decoder* dec, int32_t B, int64_t M) {
   if (check_decoder(dec) != VDM_OK) return 0;
   if (B < 1 || B > 4096 || M < 1 || M >= (1ll << 31) / dec->D) {
@@ -686,7 +761,7 @@ size_t vdm_dense_batch_workspace_size(const vdm_decoder* dec, int32_t B, int64_t
   return batch_ws(dec, B, M, nullptr, nullptr);
 }
 
-vdm_status vdm_decode_dense_batch(const vdm_decoder* dec, const vdm_queries* q, int32_t B, const void* K,
+static vdm_status decode_dense_batch_body(const vdm_decoder* dec, const vdm_queries* q, int32_t B, const void* K,
                                   const void* V, int64_t M, float* sdf, void* ws, size_t ws_bytes,
                                   vdm_stream stream) {
   vdm_status st = check_decoder(dec);
@@ -743,6 +818,12 @@ vdm_status vdm_decode_dense_batch(const vdm_decoder* dec, const vdm_queries* q, 
   return VDM_OK;
 }
 
+vdm_status vdm_decode_dense_batch(const vdm_decoder* dec, const vdm_queries* q, int32_t B, const void* K,
+                                  const void* V, int64_t M, float* sdf, void* ws, size_t ws_bytes,
+                                  vdm_stream stream) {
+  return debug_checked(decode_dense_batch_body(dec, q, B, K, V, M, sdf, ws, ws_bytes, stream), stream);
+}
+
 }  // extern "C"
 
 static vdm_status select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, int32_t probes,
@@ -794,19 +875,34 @@ static vdm_status select_kv(const vdm_decoder* dec, int32_t R, int32_t block, in
 
 extern "C" {
 
-vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, int32_t probes,
+static vdm_status select_kv_body(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, int32_t probes,
                          uint64_t seed, const void* K, int64_t M, const int32_t* blocks, int64_t nblk, int32_t* sel_idx,
                          int32_t* sel_cnt, void* ws, size_t ws_bytes, vdm_stream stream) {
   return select_kv(dec, R, block, k, cap, probes, seed, K, M, blocks, nblk, sel_idx, sel_cnt, ws, ws_bytes, stream,
                    false);
 }
 
-vdm_status vdm_select_kv_heads(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,
+vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap, int32_t probes,
+                         uint64_t seed, const void* K, int64_t M, const int32_t* blocks, int64_t nblk, int32_t* sel_idx,
+                         int32_t* sel_cnt, void* ws, size_t ws_bytes, vdm_stream stream) {
+  return debug_checked(select_kv_body(dec, R, block, k, cap, probes, seed, K, M, blocks, nblk, sel_idx, sel_cnt, ws,
+                                      ws_bytes, stream), stream);
+}
+
+static vdm_status select_kv_heads_body(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,
                                int32_t probes, uint64_t seed, const void* K, int64_t M, const int32_t* blocks,
                                int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes,
                                vdm_stream stream) {
   return select_kv(dec, R, block, k, cap, probes, seed, K, M, blocks, nblk, sel_idx, sel_cnt, ws, ws_bytes, stream,
                    true);
+}
+
+vdm_status vdm_select_kv_heads(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,
+                               int32_t probes, uint64_t seed, const void* K, int64_t M, const int32_t* blocks,
+                               int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes,
+                               vdm_stream stream) {
+  return debug_checked(select_kv_heads_body(dec, R, block, k, cap, probes, seed, K, M, blocks, nblk, sel_idx,
+                                            sel_cnt, ws, ws_bytes, stream), stream);
 }
 
 
@@ -887,6 +983,7 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
       a.out = (float*)((char*)vol_of(L) + (int64_t)b * vstride(L));
       a.scatter = 1;
       a.M = (int)M;
+      a.d_N = tot;  // the level's query count (the list length)
       if (kv) {
         a.Kp = Kb;
         a.Vt = Vb;
@@ -899,7 +996,6 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
       } else {
         a.Kp = shape_of(w.Kp, b);
         a.Vt = shape_of(w.Vt, b);
-        a.d_N = tot;
       }
       VDM_HIP_T(kv ? VDM_TIME_DECODE_GATHERED : VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, kv, a, s),
                 "decode launch");
@@ -923,7 +1019,8 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
     VDM_HIP_T(VDM_TIME_EMIT, s,
               launch_emit(bp((const uint64_t*)w.newmask, wst), bp((const int32_t*)w.counts, wst),
                           bp((const int4*)w.offs, wst), bp((const int32_t*)w.occ, wst),
-                          bp((const int32_t*)w.totals, wst), p->R0, bq, BPt(w.list), BPt(w.items), B, s),
+                          bp((const int32_t*)w.totals, wst), p->R0, bq, BPt(w.list), w.list_cap, BPt(w.items),
+                          w.item_cap, B, s),
               "emit launch");
     vdm_status st = decode_level(0);
     if (st != VDM_OK) return st;
@@ -984,7 +1081,8 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
     VDM_HIP_T(VDM_TIME_EMIT, s,
               launch_emit(bp((const uint64_t*)w.newmask, wst), bp((const int32_t*)w.counts, wst),
                           bp((const int4*)w.offs, wst), bp((const int32_t*)w.occ, wst),
-                          bp((const int32_t*)(w.totals + 4 * (L + 1)), wst), Rn, bq, BPt(w.list), BPt(w.items), B, s),
+                          bp((const int32_t*)(w.totals + 4 * (L + 1)), wst), Rn, bq, BPt(w.list), w.list_cap,
+                          BPt(w.items), w.item_cap, B, s),
               "emit launch");
     VDM_HIP_T(VDM_TIME_FILL, s,
               launch_fill(bp((const float*)vol_of(L), vstride(L)), P, bp(vol_of(L + 1), vstride(L + 1)), Pn, B, s),
@@ -997,7 +1095,7 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
 
 extern "C" {
 
-vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, const void* K, const void* V, int64_t M,
+static vdm_status decode_hier_body(const vdm_decoder* dec, const vdm_hier_params* p, const void* K, const void* V, int64_t M,
                            float* vol, int64_t vol_elems, int64_t* stats, const vdm_hier_debug* dbg, void* ws,
                            size_t ws_bytes, vdm_stream stream) {
   vdm_status st = check_decoder(dec);
@@ -1017,6 +1115,12 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, con
   (void)hipGetLastError();
   int64_t* S = stats ? stats : w.stats;
   return hier_run(dec, p, 1, K, V, M, 0, vol, 0, S, 0, dbg, ws, 0, (hipStream_t)stream);
+}
+
+vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* p, const void* K, const void* V, int64_t M,
+                           float* vol, int64_t vol_elems, int64_t* stats, const vdm_hier_debug* dbg, void* ws,
+                           size_t ws_bytes, vdm_stream stream) {
+  return debug_checked(decode_hier_body(dec, p, K, V, M, vol, vol_elems, stats, dbg, ws, ws_bytes, stream), stream);
 }
 
 // ------------------------------------------------------------------ local KNN decoder
@@ -1097,7 +1201,7 @@ size_t vdm_local_workspace_size(const vdm_local_decoder* dec, int64_t M, int64_t
   return local_ws(dec, M, N, nullptr, nullptr);
 }
 
-vdm_status vdm_decode_local(const vdm_local_decoder* dec, const float* sup_xyz, const void* feats, int64_t M,
+static vdm_status decode_local_body(const vdm_local_decoder* dec, const float* sup_xyz, const void* feats, int64_t M,
                             const float* xyz, int64_t N, float* sdf, int32_t* nbr, void* ws, size_t ws_bytes,
                             vdm_stream stream) {
   vdm_status st = check_local(dec);
@@ -1166,6 +1270,12 @@ vdm_status vdm_decode_local(const vdm_local_decoder* dec, const float* sup_xyz, 
   ha.out = sdf;
   VDM_HIP_T(VDM_TIME_LOCAL_HEAD, s, launch_local_head(ha, s), "head launch");
   return VDM_OK;
+}
+
+vdm_status vdm_decode_local(const vdm_local_decoder* dec, const float* sup_xyz, const void* feats, int64_t M,
+                            const float* xyz, int64_t N, float* sdf, int32_t* nbr, void* ws, size_t ws_bytes,
+                            vdm_stream stream) {
+  return debug_checked(decode_local_body(dec, sup_xyz, feats, M, xyz, N, sdf, nbr, ws, ws_bytes, stream), stream);
 }
 
 }  // extern "C"

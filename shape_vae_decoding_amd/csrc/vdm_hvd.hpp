@@ -49,9 +49,11 @@ hipError_t launch_scan(BP<const int32_t> counts, int64_t n, int bq, BP<int4> par
                        BP<int32_t> tot, BP<int64_t> stats_level, int B, hipStream_t s);
 inline int64_t scan_partials(int64_t n) { return (n + 2047) / 2048; }
 // reads the occupied-block list and its count tot[2] written by launch_scan
+// list_cap, item_cap: capacities of one shape's list and item array (checked in
+// bounds-checked builds)
 hipError_t launch_emit(BP<const uint64_t> newmask, BP<const int32_t> counts, BP<const int4> offs,
                        BP<const int32_t> occ, BP<const int32_t> tot, int Rn, int bq, BP<int32_t> list,
-                       BP<Item> items, int B, hipStream_t s);
+                       int64_t list_cap, BP<Item> items, int64_t item_cap, int B, hipStream_t s);
 hipError_t launch_fill(BP<const float> prev, int Pp, BP<float> next, int Pn, int B, hipStream_t s);
 hipError_t launch_bits_to_bytes(const uint64_t* m, int n, int NB, uint8_t* out, hipStream_t s);
 hipError_t launch_items_from_list(const int32_t* list, int64_t N, int R, int block, const int32_t* block_row, int bq,

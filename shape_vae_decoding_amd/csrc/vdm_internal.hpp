@@ -10,6 +10,67 @@
 
 namespace vdm {
 
+// ------------------------------------------------------------------ bounds-checked builds
+// Built with -DVDM_DEBUG=1, the kernels check every data-dependent index
+// (token ids, selection rows, work items, block ids, list and item slots,
+// support indices) with VDM_BOUND(cond, id): a false condition records `id` in
+// its source file's debug word (the first failure is kept) and the guarded
+// access is skipped or clamped. Every entry point of such a build synchronises
+// its stream, reads and clears the words, and fails with VDM_ERR_HIP naming the
+// check. Release builds compile VDM_BOUND to `true`.
+#ifndef VDM_DEBUG
+#define VDM_DEBUG 0
+#endif
+
+enum BoundCheck : unsigned {
+  BC_DECODE_ITEM = 1,  // a work item's queries [q0, q1): 0 <= q0 <= q1 <= N, at most one tile
+  BC_DECODE_ROW,       // a work item's selection row >= 0
+  BC_DECODE_SET,       // a selection row's count within [0, cap]
+  BC_DECODE_TOKEN,     // a selected token id within [0, M)
+  BC_LIST_ROW,         // a block's selection row (block_row) >= 0
+  BC_SELECT_BLOCK,     // a block id of the selection within [0, NB^3)
+  BC_SELECT_OUT,       // a compacted token set within its cap
+  BC_EMIT_LIST,        // a list slot within the list's capacity
+  BC_EMIT_ITEM,        // a work-item slot within the item array's capacity
+  BC_SCAN_OCC,         // an occupied-block slot within the block count
+  BC_LOCAL_SCATTER,    // a support's slot in cell order within [0, M)
+  BC_LOCAL_RANGE,      // a cell's support range within [0, M]
+  BC_LOCAL_QUERY,      // a query index in cell order within [0, N)
+  BC_CHECKS
+};
+
+#if VDM_DEBUG
+// one per source file (static): each file reads its own with debug_take_word
+static __device__ unsigned debug_word;
+__device__ __forceinline__ bool bound_ok(bool ok, unsigned id) {
+  if (!ok) atomicCAS(&debug_word, 0u, id);
+  return ok;
+}
+#define VDM_BOUND(cond, id) ::vdm::bound_ok((cond), (id))
+// this file's debug word, cleared; defines the file's reader `fn`
+#define VDM_DEBUG_READER(fn)                                                        \
+  hipError_t fn(unsigned* w) {                                                      \
+    hipError_t e = hipMemcpyFromSymbol(w, HIP_SYMBOL(debug_word), sizeof(unsigned)); \
+    if (e != hipSuccess) return e;                                                  \
+    const unsigned z = 0;                                                           \
+    return hipMemcpyToSymbol(HIP_SYMBOL(debug_word), &z, sizeof(unsigned));         \
+  }
+#else
+#define VDM_BOUND(cond, id) true
+#define VDM_DEBUG_READER(fn) \
+  hipError_t fn(unsigned* w) {   \
+    *w = 0;                      \
+    return hipSuccess;           \
+  }
+#endif
+// the readers of the kernel files
+hipError_t debug_take_decode(unsigned* w);
+hipError_t debug_take_select(unsigned* w);
+hipError_t debug_take_hvd(unsigned* w);
+hipError_t debug_take_local(unsigned* w);
+hipError_t debug_take_prep(unsigned* w);
+hipError_t debug_take_surface(unsigned* w);
+
 struct PrimDev {
   int kind;
   float c[3];
