@@ -570,10 +570,11 @@ __device__ __forceinline__ void gathered_kfrags(const typename C::T* __restrict_
     kf[ks] = *reinterpret_cast<const typename MM::frag*>(p + ks * MM::KS);
 }
 
-// Dense attention of this wave's QB query blocks over all M tokens: the
+// Dense attention of this wave's QB query blocks over nkeys tokens starting at
+// token tile kt0 (all M tokens, or one range of a split tile): the
 // software-pipelined loop over 32-token tiles (see pipe_iter).
 template <typename C, bool SHIFT>
-__device__ __forceinline__ void dense_attention(const DecodeArgs& A, int shape, int nkeys, int hw, int lane,
+__device__ __forceinline__ void dense_attention(const DecodeArgs& A, int shape, int kt0, int nkeys, int hw, int lane,
                                                 const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
                                                 const float (&nb)[C::QB], f32x16 (&O)[2][C::QB],
                                                 float (&l_run)[C::QB]) {
@@ -584,8 +585,9 @@ __device__ __forceinline__ void dense_attention(const DecodeArgs& A, int shape, 
   // loads K(k+2) into kb[k&1], V(k) into vb[k&1]; the loop runs the full
   // iterations two at a time so buffers are static.
   const int64_t packed_bytes = (int64_t)nkt * C::KT * C::D * C::SZ;
-  const __amdgpu_buffer_rsrc_t Kg = buffer_of((const char*)A.Kp + shape * A.kv_stride, packed_bytes);
-  const __amdgpu_buffer_rsrc_t Vg = buffer_of((const char*)A.Vt + shape * A.kv_stride, packed_bytes);
+  const int64_t first = shape * A.kv_stride + (int64_t)kt0 * C::KT * C::D * C::SZ;
+  const __amdgpu_buffer_rsrc_t Kg = buffer_of((const char*)A.Kp + first, packed_bytes);
+  const __amdgpu_buffer_rsrc_t Vg = buffer_of((const char*)A.Vt + first, packed_bytes);
   auto load_k = [&](int t, uint4 (&r)[C::RUN_U4]) { load_run<C>(Kg, t, hw, lane, r); };
   auto load_v = [&](int t, uint4 (&r)[C::RUN_U4]) { load_run<C>(Vg, t, hw, lane, r); };
   auto nothing = [](int) {};
@@ -932,7 +934,17 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     for (int i = 0; i < C::NCK; ++i) vpos[i] = key_pos<T>((tid0 + i * C::NT) / CPR);
   }
 
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  // work units: whole tiles, then (dense tail split) split_tiles tiles of `split`
+  // token ranges each, a tile's ranges on consecutive units
+  const int64_t n_whole = n_tiles - A.split_tiles;
+  const int64_t n_units = n_whole + A.split_tiles * A.split;
+  for (int64_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    int64_t tile = unit;
+    int part = -1;  // this unit's token range of a split tile, or -1
+    if (!GATHER && unit >= n_whole) {
+      tile = n_whole + (unit - n_whole) / A.split;
+      part = (int)((unit - n_whole) % A.split);
+    }
     // Thread and lane indices are re-derived opaquely in each phase, so that the
     // address arithmetic of one phase is neither hoisted out of the tile loop
     // nor shared with another phase: otherwise it stays live across the token
@@ -1020,12 +1032,61 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       }
     }
     if constexpr (!GATHER) {
+      // a split tile's range: token tiles [kt0, kt0 + per) (the shift above came
+      // from every token, so all ranges share it and their sums add plainly)
+      int kt0 = 0, nk = nkeys;
+      if (part >= 0) {
+        const int nkt = (nkeys + C::KT - 1) / C::KT, per = (nkt + A.split - 1) / A.split;
+        kt0 = min(part * per, nkt);
+        nk = max(min(nkeys, (kt0 + per) * C::KT) - kt0 * C::KT, 0);
+      }
       if (!active) {
         // (every query of this wave lies past the tile's end: nothing to attend)
       } else if (shift) {
-        dense_attention<C, true>(A, shape, nkeys, hw, lane, qf, nb, O, l_run);
+        dense_attention<C, true>(A, shape, kt0, nk, hw, lane, qf, nb, O, l_run);
       } else {
-        dense_attention<C, false>(A, shape, nkeys, hw, lane, qf, nb, O, l_run);
+        dense_attention<C, false>(A, shape, kt0, nk, hw, lane, qf, nb, O, l_run);
+      }
+      if (part >= 0) {
+        // partial O and row sums to this range's slot; the last range to arrive
+        // adds all of them in range order (the same sums whichever arrives last)
+        constexpr int NCOMP = 2 * C::QB * 16 + C::QB;
+        const int64_t tslot = (tile - n_whole) * A.split;
+        float* mine = A.part + ((tslot + part) * C::NW + wave) * NCOMP * 64 + lane;
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) {
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mine[((qb * 2 + db) * 16 + r) * 64] = O[db][qb][r];
+          mine[(2 * C::QB * 16 + qb) * 64] = l_run[qb];
+        }
+        __threadfence();  // release: the partials before the arrival count
+        __syncthreads();
+        int* flag = reinterpret_cast<int*>(lds + C::RED);
+        if (tid == 0) *flag = atomicAdd(&A.part_cnt[tile - n_whole], 1) == A.split - 1;
+        __syncthreads();
+        const bool last = *flag != 0;
+        __syncthreads();  // (the flag's word is reused by the head)
+        if (!last) continue;  // (uniform) another range finishes this tile
+        __threadfence();      // acquire: the other ranges' partials
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) {
+          O[0][qb] = zero16();
+          O[1][qb] = zero16();
+          l_run[qb] = 0.f;
+        }
+        for (int pr = 0; pr < A.split; ++pr) {
+          const float* src = A.part + ((tslot + pr) * C::NW + wave) * NCOMP * 64 + lane;
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) {
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) O[db][qb][r] += src[((qb * 2 + db) * 16 + r) * 64];
+            l_run[qb] += src[(2 * C::QB * 16 + qb) * 64];
+          }
+        }
       }
     } else {
       // (both variants pass the same barriers, so waves may take different ones)
@@ -1189,8 +1250,9 @@ typedef DecCfg<bf16, 4, 8, 64, 256> CfgB256;
 typedef DecCfg<bf16, 1, 4, 32, 64> CfgB64;
 typedef DecCfg<float, 1, 4, 32, 64> CfgF64;
 
+// workgroups of the persistent decode grid
 template <typename C, bool GATHER>
-static hipError_t run(const DecodeArgs& a, hipStream_t s) {
+static hipError_t decode_grid(int64_t* grid) {
   constexpr int lds = C::LDS;
   static bool attr = false;
   const void* fn = reinterpret_cast<const void*>(&decode_kernel<C, GATHER>);
@@ -1203,14 +1265,44 @@ static hipError_t run(const DecodeArgs& a, hipStream_t s) {
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<C, GATHER>, C::NT, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  int64_t grid = (int64_t)dev_info().cus * per_cu;
+  *grid = (int64_t)dev_info().cus * per_cu;
+  return hipSuccess;
+}
+
+template <typename C, bool GATHER>
+static hipError_t run(const DecodeArgs& a, hipStream_t s) {
+  constexpr int lds = C::LDS;
+  int64_t grid = 0;
+  hipError_t e = decode_grid<C, GATHER>(&grid);
+  if (e != hipSuccess) return e;
   if (!a.d_N && !a.d_n_items) {
     const int64_t host_tiles = a.items ? a.n_tiles : (a.N + C::BQ - 1) / C::BQ * (a.batch > 1 ? a.batch : 1);
-    if (host_tiles < grid) grid = host_tiles;
+    const int64_t host_units = host_tiles + a.split_tiles * (a.split - 1);
+    if (host_units < grid) grid = host_units;
   }
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL((decode_kernel<C, GATHER>), dim3((unsigned)grid), dim3(C::NT), lds, s, a);
   return hipGetLastError();
+}
+
+SplitPlan decode_split_plan(int dtype, int D, int64_t M, int64_t n_tiles) {
+  SplitPlan p;
+  if (dtype != VDM_BF16 || D != 256 || M < 8192 || n_tiles < 1) return p;
+  int64_t G = 0;
+  if (decode_grid<CfgB256, false>(&G) != hipSuccess || G < 2) return p;
+  const int64_t tail = n_tiles % G;  // the last round's tiles (all of them when fewer than G)
+  if (tail == 0 || 2 * tail > G) return p;
+  const int64_t nkt = (M + CfgB256::KT - 1) / CfgB256::KT;
+  int64_t parts = G / tail;
+  if (parts > nkt / 16) parts = nkt / 16;  // ranges of at least 16 token tiles
+  if (parts > 16) parts = 16;
+  if (parts < 2) return p;
+  constexpr int NCOMP = 2 * CfgB256::QB * 16 + CfgB256::QB;
+  p.parts = (int)parts;
+  p.tiles = tail;
+  p.part_bytes = (size_t)tail * parts * CfgB256::NW * NCOMP * 64 * sizeof(float);
+  p.cnt_bytes = ((size_t)tail * sizeof(int32_t) + 255) / 256 * 256;
+  return p;
 }
 
 hipError_t launch_decode(int dtype, int D, bool gathered, const DecodeArgs& a, hipStream_t s) {

@@ -221,9 +221,14 @@ struct DenseWs {
   float* kmax;
   Item* items;
   int32_t* n_items;
+  SplitPlan split;  // tail split of the full-attention launch (parts = 1: none)
+  float* part;
+  int32_t* part_cnt;
 };
 
-static size_t dense_ws(const vdm_decoder* d, int64_t M, int64_t N, bool sel, void* base, DenseWs* w) {
+// split: plan a tail split of the full-attention decode (decode_split_plan)
+static size_t dense_ws(const vdm_decoder* d, int64_t M, int64_t N, bool sel, void* base, DenseWs* w,
+                       bool split = true) {
   Carve c(base);
   DenseWs x;
   const size_t kv = (size_t)mpad(M) * d->D * esize(d->dtype);
@@ -233,6 +238,10 @@ static size_t dense_ws(const vdm_decoder* d, int64_t M, int64_t N, bool sel, voi
   x.kmax = c.take<float>(256);
   x.items = sel ? c.take<Item>((size_t)(N > 0 ? N : 1) * sizeof(Item)) : nullptr;
   x.n_items = sel ? c.take<int32_t>(256) : nullptr;
+  const int bq = decode_tile_queries(d->dtype, d->D);
+  if (!sel && split) x.split = decode_split_plan(d->dtype, d->D, M, (N + bq - 1) / bq);
+  x.part = x.split.parts > 1 ? c.take<float>(x.split.part_bytes) : nullptr;
+  x.part_cnt = x.split.parts > 1 ? c.take<int32_t>(x.split.cnt_bytes) : nullptr;
   if (w) *w = x;
   return c.off + 256;
 }
@@ -643,6 +652,13 @@ static vdm_status dense_full(const vdm_decoder* dec, const vdm_queries* q, const
   a.Vt = w.Vt;
   a.M = (int)M;
   a.n_tiles = (q->N + decode_tile_queries(dec->dtype, dec->D) - 1) / decode_tile_queries(dec->dtype, dec->D);
+  if (w.split.parts > 1) {
+    a.split = w.split.parts;
+    a.split_tiles = w.split.tiles;
+    a.part = w.part;
+    a.part_cnt = w.part_cnt;
+    VDM_HIP(launch_zero(w.part_cnt, w.split.cnt_bytes, s), "zero launch");
+  }
   if (timed)
     VDM_HIP_T(VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, false, a, s), "decode launch");
   else
@@ -734,7 +750,7 @@ static vdm_status decode_dense_noalloc_body(const vdm_decoder* dec, const vdm_qu
   bool done = false;
   vdm_status st = check_dense(dec, q, K, V, M, sdf, &done);
   if (st != VDM_OK || done) return st;
-  const size_t need = dense_ws(dec, M, q->N, false, nullptr, nullptr);
+  const size_t need = dense_ws(dec, M, q->N, false, nullptr, nullptr, false);
   if (need > (size_t)VDM_NOALLOC_SCRATCH_BYTES)
     return fail(VDM_ERR_WORKSPACE, "M=%lld needs %zu bytes of scratch; the no-allocation decode holds %zu",
                 (long long)M, need, (size_t)VDM_NOALLOC_SCRATCH_BYTES);
@@ -742,7 +758,7 @@ static vdm_status decode_dense_noalloc_body(const vdm_decoder* dec, const vdm_qu
   st = noalloc_scratch(&base);
   if (st != VDM_OK) return st;
   DenseWs w;
-  dense_ws(dec, M, q->N, false, base, &w);
+  dense_ws(dec, M, q->N, false, base, &w, false);
   (void)hipGetLastError();
   return dense_full(dec, q, K, V, M, sdf, w, (hipStream_t)stream, false);
 }

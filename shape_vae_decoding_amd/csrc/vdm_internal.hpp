@@ -137,7 +137,28 @@ struct DecodeArgs {
   int batch;
   int64_t kv_stride;
   int64_t out_stride;
+  // dense split of the tail (decode_split_plan): the last split_tiles tiles are each
+  // cut into `split` ranges of token tiles, one work unit per range; each unit
+  // writes its partial O and row sums to part, and the unit that arrives last at a
+  // tile (part_cnt, zeroed before the launch) adds them in range order and runs the
+  // epilogue. split = 1: no split.
+  int split = 1;
+  int64_t split_tiles = 0;
+  float* part = nullptr;
+  int32_t* part_cnt = nullptr;
 };
+
+// The tail split of a dense full-attention launch of n_tiles tiles over M tokens:
+// when the last round of the persistent grid would be at most half full and the
+// token set is long (M >= 8192), the leftover tiles are split into `parts` token
+// ranges (of at least 512 tokens) so that the last round is filled. parts = 1: no
+// split. part_bytes / cnt_bytes: the scratch the split needs.
+struct SplitPlan {
+  int parts = 1;
+  int64_t tiles = 0;
+  size_t part_bytes = 0, cnt_bytes = 0;
+};
+SplitPlan decode_split_plan(int dtype, int D, int64_t M, int64_t n_tiles);
 
 struct DevInfo {
   int cus;
