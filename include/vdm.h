@@ -203,7 +203,13 @@ vdm_status vdm_project_kv(const vdm_decoder* dec, const void* Z, int64_t M, void
  * sdf = NaN, a repeated entry is decoded once per occurrence, token ids are
  * clamped into [0, M), sel_cnt is clamped into [0, cap], and an empty set
  * (sel_cnt = 0) gives a zero attention output. Workspace:
- * vdm_dense_workspace_size(dec, M, N, sel != NULL). */
+ * vdm_dense_workspace_size(dec, M, N, sel != NULL), asked with the device that
+ * runs the call current: with full attention over M >= 8192 tokens (bf16, D = 256)
+ * the tiles of a last round of the decode grid that would be at most half full
+ * are split over token ranges (split-KV), and the size includes the partial
+ * results of that split, planned for the current device's compute units. The
+ * split changes only the fp32 order of the attention sums; results stay the same
+ * from run to run. */
 vdm_status vdm_decode_dense(const vdm_decoder* dec, const vdm_queries* q, const void* K,
                             const void* V, int64_t M, const vdm_kvsel* sel, float* sdf, void* ws,
                             size_t ws_bytes, vdm_stream stream);
