@@ -258,8 +258,13 @@ vdm_status vdm_decode_dense_batch(const vdm_decoder* dec, const vdm_queries* q, 
  * tokens of largest max-over-probes score when larger (ties: lower index).
  * Output row r (for blocks[r], or block r when blocks == NULL and
  * nblk = NB^3): sel_idx[r, 0 .. sel_cnt[r]) ascending, rest -1.
- * Requires 1 <= k <= M, k <= cap, M <= 4096. Workspace:
- * vdm_select_workspace_size(dec, M). */
+ * Requires 1 <= k <= M, k <= cap and M <= 65536 (VDM_ERR_UNSUPPORTED beyond).
+ * Rows of more than 4096 tokens are searched in 4096-token chunks, which keep
+ * up to 1024 candidates per probe and 1024 union members per block, so there
+ * k * ceil(M / 4096) <= 1024 and, unless cap >= 8 k, 8 k <= 1024 (else
+ * VDM_ERR_UNSUPPORTED); the result is the same top-k. Workspace:
+ * vdm_select_workspace_size(dec, M): 32 score rows of M floats for each of up
+ * to 256 workgroups (1 GiB at M = 32768), plus a packed copy of K. */
 vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,
                          int32_t probes, uint64_t seed, const void* K, int64_t M,
                          const int32_t* blocks, int64_t nblk, int32_t* sel_idx, int32_t* sel_cnt,
@@ -269,7 +274,8 @@ vdm_status vdm_select_kv(const vdm_decoder* dec, int32_t R, int32_t block, int32
  * reading of the multi-head score in section 4.1 item 2. Head h ranks the tokens
  * by its own softmax probability (not the head mean); each head keeps its own
  * union of the probes' top-k and its own cap (by the head's max-over-probes
- * probability). Arguments as vdm_select_kv; output rows are [nblk][H]: set h of
+ * probability). Arguments and limits as vdm_select_kv, except M <= 16384 (the
+ * workspace holds H score rows per probe); output rows are [nblk][H]: set h of
  * block row r is sel_idx[(r * H + h) * cap ..], sel_cnt[r * H + h]. Workspace:
  * vdm_select_heads_workspace_size(dec, M). Decode with a vdm_kvsel whose heads = 1. */
 vdm_status vdm_select_kv_heads(const vdm_decoder* dec, int32_t R, int32_t block, int32_t k, int32_t cap,

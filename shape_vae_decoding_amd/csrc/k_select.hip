@@ -38,6 +38,10 @@ constexpr int SEL_BQ = SEL_NP * SEL_GB;  // probe columns of the MFMA tile
 constexpr int SEL_MAXV = 64;             // scores per lane in the search: M <= 64 * 64
 constexpr int SEL_GRID_MAX = 256;        // workgroups (scratch rows are per workgroup)
 constexpr int SEL_LIST = 1024;           // per-wave candidate list of the top-k search (LDS)
+constexpr int SEL_MAX_M = 65536;         // tokens of a selection (one set per block)
+constexpr int SEL_MAX_M_PH = 16384;      // tokens of a per-head selection (4 score rows per probe)
+constexpr int SEL_CHUNK = SEL_MAXV * 64; // tokens per search of a chunked row
+constexpr int SEL_CV = SEL_LIST / 64;    // list entries per lane
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -70,14 +74,15 @@ __device__ __forceinline__ int wave_sum(int v) {
 // 256-entry list this path ran for most probes). Thresholds are >= 1, so zero
 // entries never count; values are visited in chunks of 16 and a chunk past n is
 // skipped.
-__device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[SEL_MAXV], int n, int k, unsigned* list, int lane) {
+template <int NU>
+__device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[NU], int n, int k, unsigned* list, int lane) {
   // (every loop is fully unrolled with constant indices, so u stays in registers)
   constexpr int CH = 16, LV = SEL_LIST / 64;
-  static_assert(SEL_MAXV % CH == 0, "whole chunks");
+  static_assert(NU % CH == 0, "whole chunks");
   auto count_all = [&](unsigned thr) {
     int c = 0;
 #pragma unroll
-    for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
+    for (int c0 = 0; c0 < NU; c0 += CH) {
       if (c0 * 64 < n) {
 #pragma unroll
         for (int i = c0; i < c0 + CH; ++i) c += u[i] >= thr ? 1 : 0;
@@ -94,7 +99,7 @@ __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[SEL_MAXV], int
     // lane maximum (which is <= lo)
     unsigned m1 = 0u, m2 = 0u;
 #pragma unroll
-    for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
+    for (int c0 = 0; c0 < NU; c0 += CH) {
       if (c0 * 64 < n) {
 #pragma unroll
         for (int i = c0; i < c0 + CH; ++i) {
@@ -111,7 +116,7 @@ __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[SEL_MAXV], int
     }
     int mine = 0;
 #pragma unroll
-    for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
+    for (int c0 = 0; c0 < NU; c0 += CH) {
       if (c0 * 64 < n) {
 #pragma unroll
         for (int i = c0; i < c0 + CH; ++i) mine += (u[i] >= lo && u[i] > 0u) ? 1 : 0;
@@ -122,7 +127,7 @@ __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[SEL_MAXV], int
     if (lo > 0u && total <= SEL_LIST) {
       int off = incl - mine;
 #pragma unroll
-      for (int c0 = 0; c0 < SEL_MAXV; c0 += CH) {
+      for (int c0 = 0; c0 < NU; c0 += CH) {
         if (c0 * 64 < n) {
 #pragma unroll
           for (int i = c0; i < c0 + CH; ++i)
@@ -176,13 +181,13 @@ __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[SEL_MAXV], int
   uint64_t sel = 0ull;
   if (p > 0u && equal == need) {
 #pragma unroll
-    for (int i = 0; i < SEL_MAXV; ++i)
+    for (int i = 0; i < NU; ++i)
       if (i * 64 < n) sel |= (uint64_t)(u[i] >= p) << i;  // (entries past n are 0 < p)
     return sel;
   }
   int taken = 0;
 #pragma unroll
-  for (int i = 0; i < SEL_MAXV; ++i) {
+  for (int i = 0; i < NU; ++i) {
     if (i * 64 < n) {
       const bool valid = i * 64 + lane < n;
       const bool eq = valid && u[i] == p;
@@ -209,9 +214,12 @@ __device__ __forceinline__ void add_to_bitmap(uint64_t sel, int n, unsigned* wor
 }
 
 // LDS: [embedding stage] | stats [NW][H][32] float2 | fin [H][32] | lists [NW][SEL_LIST] |
-//      bits [GB*NS][wst] | bits2 [GB*NS][wst] | cnt [GB*NS]   (NS sets per block: H with
-//      per-head sets, else 1; wst = sel_wstride(M) words per set, an even number)
-__host__ __device__ inline int sel_wstride(int M) { return 2 * ((M + 63) / 64); }
+//      bits [GB*NS][wst] | bits2 [GB*NS][wst] | cnt [GB*NS] | (cand [NW][SEL_LIST])
+//      (NS sets per block: H with per-head sets, else 1; wst = sel_wstride(M) words
+//      per set, an even number). Chunked rows (M > SEL_CHUNK) keep each wave's token
+//      list in `cand`: over the embedding stage and stats, which are dead once pass 2
+//      has ended, where they are large enough, else past the counts.
+__host__ __device__ constexpr int sel_wstride(int M) { return 2 * ((M + 63) / 64); }
 
 template <typename T, int H, int NS>
 struct SelCfg {
@@ -221,27 +229,71 @@ struct SelCfg {
   static constexpr int FIN = STATS + SEL_NW * H * 32 * 8;
   static constexpr int LISTS = FIN + H * 32 * 4;
   static constexpr int BITS = LISTS + SEL_NW * SEL_LIST * 4;
+  static constexpr int CAND_BYTES = SEL_NW * SEL_LIST * 4;
+  static constexpr bool CAND_LOW = FIN >= CAND_BYTES;
   static_assert(BITS % 16 == 0, "16-byte aligned bitmaps");
   static_assert(SEL_LIST >= 32 * 32, "a wave's list holds its 32 x 32 transposition tile in pass 2");
-  __host__ __device__ static int total(int M) {
+  __host__ __device__ static constexpr int bits_end(int M) {
     return BITS + 2 * SEL_GB * NS * sel_wstride(M) * 4 + SEL_GB * NS * 4 + 16;
   }
+  __host__ __device__ static constexpr int cand(int M) { return CAND_LOW ? 0 : (bits_end(M) + 15) & ~15; }
+  __host__ __device__ static constexpr int total(int M) {
+    return M > SEL_CHUNK && !CAND_LOW ? cand(M) + CAND_BYTES : bits_end(M);
+  }
 };
+
+constexpr int SEL_LDS_MAX = 160 * 1024;
+static_assert(SelCfg<bf16, 4, 1>::total(SEL_MAX_M) <= SEL_LDS_MAX && SelCfg<bf16, 4, 4>::total(SEL_MAX_M_PH) <= SEL_LDS_MAX &&
+                  SelCfg<bf16, 1, 1>::total(SEL_MAX_M) <= SEL_LDS_MAX && SelCfg<float, 1, 1>::total(SEL_MAX_M) <= SEL_LDS_MAX,
+              "the largest selections fit the LDS of a workgroup");
 
 // per-workgroup scratch: SEL_BQ rows of Mpad scores
 __host__ __device__ inline int sel_mpad(int M) { return (M + 63) / 64 * 64; }
 
-// Scores row r, element i * 64 + lane, for i = 0 .. SEL_MAXV-1, as unsigned bits
-// (0 past M). Buffer loads: a scalar offset per i, so no per-element address
+// Scores row r, element c0 + i * 64 + lane, for i = 0 .. SEL_MAXV-1, as unsigned
+// bits (0 past M). Buffer loads: a scalar offset per i, so no per-element address
 // registers are kept live.
 __device__ __forceinline__ void load_scores(__amdgpu_buffer_rsrc_t buf, int row, int Mp, int M, int lane,
-                                            unsigned (&u)[SEL_MAXV]) {
-  const int voff = (row * Mp + lane) * 4;
+                                            unsigned (&u)[SEL_MAXV], int c0 = 0) {
+  const int voff = (row * Mp + c0 + lane) * 4;
 #pragma unroll
   for (int i = 0; i < SEL_MAXV; ++i) {
     const unsigned v = __builtin_amdgcn_raw_buffer_load_b32(buf, voff, i * 256, 0);
-    u[i] = i * 64 + lane < M ? v : 0u;
+    u[i] = c0 + i * 64 + lane < M ? v : 0u;
   }
+}
+
+// Rows of more than SEL_MAXV * 64 tokens are searched in chunks of that many. A
+// token among the k largest of the row (equal scores: lower index first) is among
+// the k largest of its chunk by the same order, so the chunks' winners, kept in
+// ascending token order, hold the row's k largest with the same tie order; a
+// second search over them (at most SEL_LIST, so NV = 16 per lane) picks those.
+
+// Appends the tokens of a chunk's mask (bit i of lane l: token c0 + i * 64 + l) to
+// a wave's list in ascending order; returns the new length.
+__device__ __forceinline__ int append_tokens(uint64_t sel, int c0, int n, int* list, int len, int lane) {
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int i = 0; i < SEL_MAXV; ++i) {
+    if (i * 64 < n) {
+      const bool on = (sel >> i) & 1ull;
+      const unsigned long long b = __ballot(on);
+      const int slot = len + __popcll(b & below);
+      if (on && VDM_BOUND(slot < SEL_LIST, BC_SELECT_CAND)) list[slot] = c0 + i * 64 + lane;
+      len += __popcll(b);
+    }
+  }
+  return len;
+}
+
+// Sets the bits of the tokens list[j * 64 + lane] whose bit j of `sel` is set.
+__device__ __forceinline__ void mark_listed(uint64_t sel, const int* list, unsigned* words, int lane) {
+#pragma unroll
+  for (int j = 0; j < SEL_CV; ++j)
+    if ((sel >> j) & 1ull) {
+      const int t = list[j * 64 + lane];
+      atomicOr(words + (t >> 5), 1u << (t & 31));
+    }
 }
 
 // K fragments of key tile kb for every head (A operands of S^T = K Q^T). bf16:
@@ -280,7 +332,7 @@ __device__ __forceinline__ void load_ktile(const SelectArgs& A, __amdgpu_buffer_
   }
 }
 
-template <typename T, int H, bool PH>
+template <typename T, int H, bool PH, bool BIG>
 __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   extern __shared__ __align__(16) char lds[];
   using MM = Mma<T>;
@@ -300,6 +352,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   int* ucount = reinterpret_cast<int*>(bits2 + SEL_GB * NS * wst);  // [GB][NS]
   float* scores = A.scores + (int64_t)blockIdx.x * SEL_BQ * NS * Mp;   // [BQ][NS][Mp], this workgroup's rows
   unsigned* wlist = reinterpret_cast<unsigned*>(lds + CF::LISTS) + wave * SEL_LIST;  // this wave's top-k list
+  int* cand = reinterpret_cast<int*>(lds + CF::cand(M)) + wave * SEL_LIST;          // chunked rows: token list
   const __amdgpu_buffer_rsrc_t sbuf =
       __builtin_amdgcn_make_buffer_rsrc(scores, (short)0, SEL_BQ * NS * Mp * 4, 0x00020000 /* raw buffer */);
   const int64_t nblk = A.d_n_blocks ? (int64_t)*A.d_n_blocks : A.n_blocks;
@@ -484,11 +537,36 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
           cur = set;
         }
         // score row (probe, head): probe = block * NP + pr, head = set % NS
-        unsigned u[SEL_MAXV];
-        load_scores(sbuf, ((set / NS) * SEL_NP + pr) * NS + set % NS, Mp, M, lane, u);
-        acc |= topk_mask(u, M, A.k, wlist, lane);
+        const int srow = ((set / NS) * SEL_NP + pr) * NS + set % NS;
+        if constexpr (!BIG) {
+          unsigned u[SEL_MAXV];
+          load_scores(sbuf, srow, Mp, M, lane, u);
+          acc |= topk_mask(u, M, A.k, wlist, lane);
+        } else {
+          // each chunk's k largest, then the k largest of those (token order kept)
+          int nc = 0;
+          for (int c0 = 0; c0 < M; c0 += SEL_CHUNK) {
+            unsigned u[SEL_MAXV];
+            load_scores(sbuf, srow, Mp, M, lane, u, c0);
+            const int n = min(SEL_CHUNK, M - c0);
+            nc = append_tokens(topk_mask(u, n, A.k, wlist, lane), c0, n, cand, nc, lane);
+          }
+          nc = min(nc, SEL_LIST);
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          unsigned v[SEL_CV];
+#pragma unroll
+          for (int j = 0; j < SEL_CV; ++j) {
+            const int t = j * 64 + lane < nc ? cand[j * 64 + lane] : 0;
+            const unsigned x = __builtin_amdgcn_raw_buffer_load_b32(sbuf, (srow * Mp + t) * 4, 0, 0);
+            v[j] = j * 64 + lane < nc ? x : 0u;
+          }
+          mark_listed(topk_mask(v, nc, A.k, wlist, lane), cand, bits + set * wst, lane);
+          __builtin_amdgcn_wave_barrier();  // the list is read before the next item writes it
+        }
       }
-      if (cur >= 0) add_to_bitmap(acc, M, bits + cur * wst, lane);
+      if constexpr (!BIG)
+        if (cur >= 0) add_to_bitmap(acc, M, bits + cur * wst, lane);
     }
     __syncthreads();
 
@@ -502,7 +580,43 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       for (int i = lane; i < nwords; i += 64) cnt += __popc(ub[i]);
       cnt = wave_sum(cnt);
       const unsigned* outbits = ub;
-      if (cnt > A.cap) {
+      if (BIG && cnt > A.cap) {
+        // the same ranking over the union's members only (at most 8 k <= SEL_LIST),
+        // listed in ascending token order, so equal scores keep their index order
+        int base = 0;
+        for (int w0 = 0; w0 < nwords; w0 += 64) {
+          const int wi = w0 + lane;
+          unsigned word = wi < nwords ? ub[wi] : 0u;
+          const int c = __popc(word);
+          const int incl = wave_incl_scan(c, lane);
+          int off = base + incl - c;
+          while (word) {
+            const int b = __ffs(word) - 1;
+            if (VDM_BOUND(off < SEL_LIST, BC_SELECT_CAND)) cand[off] = wi * 32 + b;
+            ++off;
+            word &= word - 1u;
+          }
+          base += __shfl(incl, 63);
+        }
+        const int nm = min(base, SEL_LIST);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        unsigned v[SEL_CV];
+#pragma unroll
+        for (int j = 0; j < SEL_CV; ++j) {
+          const bool in = j * 64 + lane < nm;
+          const int t = in ? cand[j * 64 + lane] : 0;
+          unsigned x = 0u;
+#pragma unroll
+          for (int q = 0; q < SEL_NP; ++q)
+            x = max(x, __builtin_amdgcn_raw_buffer_load_b32(sbuf, ((((blk * SEL_NP + q) * NS + hs) * Mp) + t) * 4, 0, 0));
+          v[j] = in ? x + 1u : 0u;
+        }
+        mark_listed(topk_mask(v, nm, A.cap, wlist, lane), cand, bits2 + set * wst, lane);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        outbits = bits2 + set * wst;
+      } else if (!BIG && cnt > A.cap) {
         // keep the cap tokens of largest max-over-probes score (members rank above non-members)
         unsigned u[SEL_MAXV];
         load_scores(sbuf, (blk * SEL_NP) * NS + hs, Mp, M, lane, u);
@@ -560,10 +674,10 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   }
 }
 
-template <typename T, int H, bool PH>
+template <typename T, int H, bool PH, bool BIG>
 static hipError_t run_select(const SelectArgs& a, hipStream_t s) {
   const int lds = SelCfg<T, H, PH ? H : 1>::total(a.M);
-  const void* fn = reinterpret_cast<const void*>(&select_kernel<T, H, PH>);
+  const void* fn = reinterpret_cast<const void*>(&select_kernel<T, H, PH, BIG>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   int64_t grid = dev_info().cus;
@@ -573,7 +687,7 @@ static hipError_t run_select(const SelectArgs& a, hipStream_t s) {
     if (groups < grid) grid = groups;
   }
   if (grid < 1) return hipSuccess;
-  hipLaunchKernelGGL((select_kernel<T, H, PH>), dim3((unsigned)grid), dim3(SEL_NT), lds, s, a);
+  hipLaunchKernelGGL((select_kernel<T, H, PH, BIG>), dim3((unsigned)grid), dim3(SEL_NT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -581,12 +695,28 @@ size_t select_scratch_bytes(int M, int sets) {
   return (size_t)SEL_GRID_MAX * SEL_BQ * sets * sel_mpad(M) * sizeof(float);
 }
 
+int select_max_tokens(bool per_head) { return per_head ? SEL_MAX_M_PH : SEL_MAX_M; }
+
+bool select_fits(int64_t M, int k, int cap, bool per_head) {
+  if (M < 1 || M > select_max_tokens(per_head) || k < 1) return false;
+  if (M <= SEL_CHUNK) return true;
+  // chunk winners and the union's members fit a wave's list
+  const int64_t chunks = (M + SEL_CHUNK - 1) / SEL_CHUNK;
+  return (int64_t)k * chunks <= SEL_LIST && (cap >= SEL_NP * k || SEL_NP * k <= SEL_LIST);
+}
+
+template <typename T, int H, bool PH>
+static hipError_t run_select_m(const SelectArgs& a, hipStream_t s) {
+  return a.M > SEL_CHUNK ? run_select<T, H, PH, true>(a, s) : run_select<T, H, PH, false>(a, s);
+}
+
 hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s) {
-  if (a.M > SEL_MAXV * 64) return hipErrorInvalidValue;
-  if (dtype == VDM_BF16 && a.D == 256) return a.per_head ? run_select<bf16, 4, true>(a, s) : run_select<bf16, 4, false>(a, s);
+  if (!select_fits(a.M, a.k, a.cap, a.per_head != 0)) return hipErrorInvalidValue;
+  if (dtype == VDM_BF16 && a.D == 256)
+    return a.per_head ? run_select_m<bf16, 4, true>(a, s) : run_select_m<bf16, 4, false>(a, s);
   // (one head: its per-head set is the head-mean set)
-  if (dtype == VDM_BF16) return run_select<bf16, 1, false>(a, s);
-  return run_select<float, 1, false>(a, s);
+  if (dtype == VDM_BF16) return run_select_m<bf16, 1, false>(a, s);
+  return run_select_m<float, 1, false>(a, s);
 }
 
 VDM_DEBUG_READER(debug_take_select)

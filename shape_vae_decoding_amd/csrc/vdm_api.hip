@@ -351,7 +351,9 @@ static vdm_status check_hier(const vdm_decoder* d, const vdm_hier_params* p, int
   if (p->use_kvsel) {
     if (p->block != 8) return fail(VDM_ERR_UNSUPPORTED, "KV selection blocks must be 8 points per axis");
     if (p->k < 1 || p->k > M || p->cap < p->k) return fail(VDM_ERR_INVALID_ARG, "k=%d cap=%d M=%lld", p->k, p->cap, (long long)M);
-    if (M > 4096) return fail(VDM_ERR_UNSUPPORTED, "KV selection supports M <= 4096");
+    if (!select_fits(M, p->k, p->cap, p->heads == 1))
+      return fail(VDM_ERR_UNSUPPORTED, "KV selection: M=%lld (at most %d) with k=%d cap=%d", (long long)M,
+                  select_max_tokens(p->heads == 1), p->k, p->cap);
     if (p->probes != 0 && p->probes != 1) return fail(VDM_ERR_INVALID_ARG, "probes=%d (0: corners, 1: random)", p->probes);
     if (p->heads != 0 && p->heads != 1) return fail(VDM_ERR_INVALID_ARG, "heads=%d (0: one set per block, 1: per head)", p->heads);
   }
@@ -384,7 +386,8 @@ static vdm_status debug_checked(vdm_status st, vdm_stream stream) {
       "occupied block slot",
       "support slot",
       "cell support range",
-      "query index in cell order"};
+      "query index in cell order",
+      "selection candidate slot"};
   hipError_t (*const take[])(unsigned*) = {debug_take_decode, debug_take_select, debug_take_hvd,
                                             debug_take_local,  debug_take_prep,   debug_take_surface};
   static const char* const file[] = {"decode", "select", "hvd", "local", "prep", "surface"};
@@ -455,8 +458,8 @@ size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, in
 
 size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M) {
   if (check_decoder(dec) != VDM_OK) return 0;
-  if (M < 1 || M > 4096) {
-    fail(VDM_ERR_INVALID_ARG, "M=%lld (1..4096)", (long long)M);
+  if (M < 1 || M > select_max_tokens(false)) {
+    fail(VDM_ERR_INVALID_ARG, "M=%lld (1..%d)", (long long)M, select_max_tokens(false));
     return 0;
   }
   return select_ws_bytes(dec, M);
@@ -464,8 +467,8 @@ size_t vdm_select_workspace_size(const vdm_decoder* dec, int64_t M) {
 
 size_t vdm_select_heads_workspace_size(const vdm_decoder* dec, int64_t M) {
   if (check_decoder(dec) != VDM_OK) return 0;
-  if (M < 1 || M > 4096) {
-    fail(VDM_ERR_INVALID_ARG, "M=%lld (1..4096)", (long long)M);
+  if (M < 1 || M > select_max_tokens(true)) {
+    fail(VDM_ERR_INVALID_ARG, "M=%lld (1..%d)", (long long)M, select_max_tokens(true));
     return 0;
   }
   return select_ws_bytes(dec, M, true);
@@ -849,8 +852,12 @@ static vdm_status select_kv(const vdm_decoder* dec, int32_t R, int32_t block, in
   vdm_status st = check_decoder(dec);
   if (st != VDM_OK) return st;
   if (R < 1 || R > 1200 || block < 1) return fail(VDM_ERR_INVALID_ARG, "R=%d block=%d", R, block);
-  if (M < 1 || M > 4096) return fail(M < 1 ? VDM_ERR_INVALID_ARG : VDM_ERR_UNSUPPORTED, "M=%lld (1..4096)", (long long)M);
+  if (M < 1 || M > select_max_tokens(heads))
+    return fail(M < 1 ? VDM_ERR_INVALID_ARG : VDM_ERR_UNSUPPORTED, "M=%lld (1..%d)", (long long)M, select_max_tokens(heads));
   if (k < 1 || k > M || cap < k) return fail(VDM_ERR_INVALID_ARG, "k=%d cap=%d M=%lld", k, cap, (long long)M);
+  if (!select_fits(M, k, cap, heads))
+    return fail(VDM_ERR_UNSUPPORTED, "k=%d cap=%d with M=%lld: k * ceil(M / 4096) must be <= 1024, and 8 k <= 1024 unless cap >= 8 k",
+                k, cap, (long long)M);
   if (probes != 0 && probes != 1) return fail(VDM_ERR_INVALID_ARG, "probes=%d (0: corners, 1: random)", probes);
   const int64_t NB = (R + block) / block;
   if (nblk < 0 || (!blocks && nblk != NB * NB * NB))

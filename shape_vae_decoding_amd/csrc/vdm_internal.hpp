@@ -36,6 +36,7 @@ enum BoundCheck : unsigned {
   BC_LOCAL_SCATTER,    // a support's slot in cell order within [0, M)
   BC_LOCAL_RANGE,      // a cell's support range within [0, M]
   BC_LOCAL_QUERY,      // a query index in cell order within [0, N)
+  BC_SELECT_CAND,      // a chunk winner's slot within a wave's candidate list
   BC_CHECKS
 };
 
@@ -210,6 +211,9 @@ struct SelectArgs {
 };
 hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s);
 size_t select_scratch_bytes(int M, int sets);
+// largest token count of a selection; whether (M, k, cap) fits the kernel's lists
+int select_max_tokens(bool per_head);
+bool select_fits(int64_t M, int k, int cap, bool per_head);
 
 // ------------------------------------------------------------------ local KNN decoder
 // Supports are bucketed into LOCAL_G^3 cells over [-1, 1]^3.

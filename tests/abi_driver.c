@@ -125,7 +125,13 @@ static void select_and_hier(void) {
   int32_t* I = (int32_t*)FAKE;
   CHECK(vdm_select_kv(&d, 75, 8, 65, 512, 0, 0, FAKE, 64, NULL, 1000, I, I, NULL, 0, NULL) == VDM_ERR_INVALID_ARG);
   CHECK(vdm_select_kv(&d, 75, 8, 64, 32, 0, 0, FAKE, 3072, NULL, 1000, I, I, NULL, 0, NULL) == VDM_ERR_INVALID_ARG);
+  CHECK(vdm_select_kv(&d, 75, 8, 64, 512, 0, 0, FAKE, 65537, NULL, 1000, I, I, NULL, 0, NULL) ==
+        VDM_ERR_UNSUPPORTED);
+  CHECK(vdm_select_kv(&d, 75, 8, 103, 1024, 0, 0, FAKE, 40960, NULL, 1000, I, I, NULL, 0, NULL) ==
+        VDM_ERR_UNSUPPORTED);
   CHECK(vdm_select_kv(&d, 75, 8, 64, 512, 0, 0, FAKE, 40960, NULL, 1000, I, I, NULL, 0, NULL) ==
+        VDM_ERR_WORKSPACE);
+  CHECK(vdm_select_kv_heads(&d, 75, 8, 64, 512, 0, 0, FAKE, 16385, NULL, 1000, I, I, NULL, 0, NULL) ==
         VDM_ERR_UNSUPPORTED);
   CHECK(vdm_select_kv(&d, 75, 8, 64, 512, 2, 0, FAKE, 3072, NULL, 1000, I, I, NULL, 0, NULL) == VDM_ERR_INVALID_ARG);
   CHECK(vdm_select_kv(&d, 75, 8, 64, 512, 0, 0, FAKE, 3072, NULL, 999, I, I, NULL, 0, NULL) == VDM_ERR_INVALID_ARG);

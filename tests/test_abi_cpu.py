@@ -155,8 +155,23 @@ def test_select_and_hier_argument_checks():
                              None) == V.VDM_ERR_INVALID_ARG
     assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 32, 0, 0, 0x1000, 3072, None, 1000, 0x1000, 0x1000, None, 0,
                              None) == V.VDM_ERR_INVALID_ARG
-    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0, 0, 0x1000, 40960, None, 1000, 0x1000, 0x1000, None, 0,
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0, 0, 0x1000, 65537, None, 1000, 0x1000, 0x1000, None, 0,
                              None) == V.VDM_ERR_UNSUPPORTED
+    # chunked rows: k * ceil(M / 4096) <= 1024, and 8 k <= 1024 unless cap >= 8 k
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 103, 1024, 0, 0, 0x1000, 40960, None, 1000, 0x1000, 0x1000, None, 0,
+                             None) == V.VDM_ERR_UNSUPPORTED
+    assert lib.vdm_select_kv(C.byref(d), 75, 8, 129, 1000, 0, 0, 0x1000, 8192, None, 1000, 0x1000, 0x1000, None, 0,
+                             None) == V.VDM_ERR_UNSUPPORTED
+    for k, cap in ((102, 1024), (129, 1032), (64, 512)):  # within the limits: only the workspace is missing
+        assert lib.vdm_select_kv(C.byref(d), 75, 8, k, cap, 0, 0, 0x1000, 40960 if k != 129 else 8192, None, 1000,
+                                 0x1000, 0x1000, None, 0, None) == V.VDM_ERR_WORKSPACE
+    assert lib.vdm_select_kv_heads(C.byref(d), 75, 8, 64, 512, 0, 0, 0x1000, 16385, None, 1000, 0x1000, 0x1000,
+                                   None, 0, None) == V.VDM_ERR_UNSUPPORTED
+    assert lib.vdm_select_kv_heads(C.byref(d), 75, 8, 64, 512, 0, 0, 0x1000, 16384, None, 1000, 0x1000, 0x1000,
+                                   None, 0, None) == V.VDM_ERR_WORKSPACE
+    assert lib.vdm_select_workspace_size(C.byref(d), 65536) > 0 and lib.vdm_select_workspace_size(C.byref(d), 65537) == 0
+    assert lib.vdm_select_heads_workspace_size(C.byref(d), 16384) > 0
+    assert lib.vdm_select_heads_workspace_size(C.byref(d), 16385) == 0
     # blocks == NULL requires nblk = NB^3 (76 points per axis -> 10 blocks)
     assert lib.vdm_select_kv(C.byref(d), 75, 8, 64, 512, 0, 0, 0x1000, 3072, None, 999, 0x1000, 0x1000, None, 0,
                              None) == V.VDM_ERR_INVALID_ARG

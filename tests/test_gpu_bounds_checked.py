@@ -146,6 +146,28 @@ def test_selection_and_gathered_decode_equal_default_build(V, libs):
     same(*both(V, libs, run))
 
 
+@pytest.mark.parametrize("heads", [False, True])
+def test_chunked_selection_equals_default_build(V, libs, heads):
+    # 9,000 tokens: rows searched in 4,096-token chunks; a cap of 100 binds, so the
+    # cap ranking over the union's members runs too
+    w = W.make(4)
+    dec = gpu_decoder(w)
+    K, _ = gpu_kv(dec, w, Z=w.Z[:9000])
+    R = 37
+    nb = -(-(R + 1) // 8)
+    ns = w.H if heads else 1
+
+    def run():
+        sel_idx = torch.empty((nb ** 3 * ns, 100), dtype=torch.int32, device=dev())
+        sel_cnt = torch.empty(nb ** 3 * ns, dtype=torch.int32, device=dev())
+        V.vdm_select_kv(dec, R, 8, 64, 100, K, None, sel_idx, sel_cnt, heads=heads)
+        return sel_idx, sel_cnt
+
+    a, b = both(V, libs, run)
+    same(a, b)
+    assert torch.all(a[1] == 100)
+
+
 def test_local_decoder_equals_default_build(V, libs):
     w = W.small_local(seed=3, M=700, C=256, F=1024, n_queries=999)
     d = dev()

@@ -94,6 +94,21 @@ def test_selection_and_gathered_decode():
     g.check()
 
 
+def test_chunked_selection():
+    # 9,000 tokens (4,096-token chunks), the cap binding, one set per block and per head
+    g = Guarded()
+    w = W.make(4)
+    dec = gpu_decoder(w)
+    K, _ = gpu_kv(dec, w, Z=w.Z[:9000])
+    R = 30
+    nb = -(-(R + 1) // 8)
+    sel_idx, sel_cnt = g((nb ** 3, 100), torch.int32), g((nb ** 3,), torch.int32)
+    V().vdm_select_kv(dec, R, 8, 64, 100, K, None, sel_idx, sel_cnt)
+    hs_idx, hs_cnt = g((nb ** 3, w.H, 100), torch.int32), g((nb ** 3, w.H), torch.int32)
+    V().vdm_select_kv(dec, R, 8, 64, 100, K, None, hs_idx, hs_cnt, heads=True)
+    g.check()
+
+
 @pytest.mark.parametrize("kvsel", [None, dict(k=64, cap=512)])
 def test_hierarchical_decode_and_exports(kvsel):
     g = Guarded()

@@ -1,0 +1,147 @@
+"""GPU parity of adaptive KV selection over more than 4,096 tokens, through the C
+ABI. Such rows are searched in 4,096-token chunks: each chunk's k largest scores
+(equal scores: lower index first), kept in ascending token order, then the k
+largest of those; when the cap binds, the cap ranking runs over the union's
+members only. The sets must be the oracle's top-k (which sorts whole rows), up to
+tokens within a relative 1e-4 of a probe's k-th score, as for shorter rows.
+
+- 40,960 tokens (the 200K-point workload's vecset), cap free and binding, corner
+  and random probes; 9,000 tokens (a partial last chunk); k > 64 (the search
+  that does not use the candidate bound); ties across chunk boundaries (exact);
+  per-head sets at 16,384 and 9,000 tokens; the hierarchical decode with
+  selection at every level over 40,960 tokens."""
+
+import numpy as np
+import pytest
+import torch
+
+import vdm_workloads as W
+from oracle import akvs as oak
+from oracle import decoder as odec
+from oracle import hvd as hv
+from tests.helpers import DECODE_TILE, TOL_BF16, dev, f64, gpu_decoder, gpu_kv, oracle_decoder, report, tile_sample
+from tests.test_gpu_akvs import compare_sets, compare_sets_heads, gpu_probe_q, run_select, run_select_heads
+
+pytestmark = pytest.mark.gpu
+
+
+def V():
+    import shape_vae_decoding_amd as mod
+
+    return mod
+
+
+@pytest.fixture(scope="module")
+def big():
+    w = W.make(4)
+    assert w.M == 40960
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    return w, dec, K, Vv
+
+
+def _blocks(R, n, seed):
+    nb = hv.nblocks(R + 1)
+    b = np.sort(np.random.default_rng(seed).choice(nb ** 3, n, replace=False))
+    return np.unique(np.concatenate([b, [0, nb ** 3 - 1]]))  # with the ragged corner block
+
+
+@pytest.mark.parametrize("M,k,cap", [(40960, 64, 512), (40960, 64, 100), (9000, 64, 512), (9000, 100, 1000),
+                                     (9000, 100, 300)])
+def test_select_many_tokens_matches_oracle(big, M, k, cap):
+    w, dec, K, _ = big
+    Km = K[:M].contiguous()
+    R = 75
+    blocks = _blocks(R, 24, M + k + cap)
+    print(f"[select] chunked M={M} k={k} cap={cap}", flush=True)
+    sel_idx, sel_cnt = run_select(dec, w, Km, R, blocks, k, cap)
+    assert np.all(sel_cnt <= cap) and np.all(sel_cnt >= k)
+    if cap == 100:
+        assert np.all(sel_cnt == 100)  # the cap binds: 8 probes x 64 exceed it
+    if cap == 300:
+        assert np.any(sel_cnt == 300)  # the cap binds in some blocks (8 x 100 candidates)
+    compare_sets(dec, w, Km, R, blocks, k, cap, sel_idx, sel_cnt)
+
+
+def test_select_many_tokens_random_probes(big):
+    w, dec, K, _ = big
+    R, seed = 150, 0x5EED
+    blocks = _blocks(R, 20, 3)
+    sel_idx, sel_cnt = run_select(dec, w, K, R, blocks, 64, 512, probes="random", seed=seed)
+    compare_sets(dec, w, K, R, blocks, 64, 512, sel_idx, sel_cnt, probes="random", seed=seed)
+
+
+@pytest.mark.parametrize("repeat", [1, 3])
+def test_select_many_tokens_ties_go_to_the_lower_index(big, repeat):
+    # 9,000 tokens made of `repeat` distinct keys: every chunk holds copies of the
+    # k-th score, and the set must be its lowest-indexed copies over the whole row
+    # (repeat = 1: exactly tokens 0 .. k-1, all from the first chunk)
+    w, dec, K, _ = big
+    M = 9000
+    rows = K[torch.arange(M, device=dev()) % repeat * 97].contiguous()
+    R, k, cap = 75, 64, 512
+    nb = hv.nblocks(R + 1)
+    blocks = np.array([0, 5, nb ** 3 // 2, nb ** 3 - 1])
+    sel_idx, sel_cnt = run_select(dec, w, rows, R, blocks, k, cap)
+    Qp = gpu_probe_q(dec, w, R, blocks)
+    Kh = f64(rows)
+    for r in range(len(blocks)):
+        sc = oak.probe_scores(Qp[r], Kh, w.H)
+        ref = oak.select(sc, k, cap)
+        got = sel_idx[r, : sel_cnt[r]]
+        assert np.array_equal(np.sort(ref), got), (blocks[r], ref[:8], got[:8])
+    if repeat == 1:
+        assert np.all(sel_cnt == k) and np.array_equal(sel_idx[:, :k], np.tile(np.arange(k), (len(blocks), 1)))
+    print(f"[parity] chunked selection ties (repeat={repeat}): {len(blocks)} blocks exact", flush=True)
+
+
+@pytest.mark.parametrize("M,cap", [(16384, 512), (9000, 100)])
+def test_select_per_head_many_tokens(big, M, cap):
+    w, dec, K, _ = big
+    Km = K[:M].contiguous()
+    R = 75
+    blocks = _blocks(R, 16, M + cap)
+    sel_idx, sel_cnt = run_select_heads(dec, w, Km, R, blocks, 64, cap)
+    assert np.all(sel_cnt <= cap) and np.all(sel_cnt >= 64)
+    compare_sets_heads(dec, w, Km, R, blocks, 64, cap, sel_idx, sel_cnt)
+
+
+def test_hier_with_selection_many_tokens(big):
+    # 30 -> 60 with selection at both levels over the 40,960-token vecset: the
+    # selected sets against the oracle's top-k, and one point per work item
+    # against attention restricted to its block's set
+    w, dec, K, Vv = big
+    kv = dict(k=64, cap=512)
+    params = V().hier_params(R0=30, levels=2, tau=float(np.float32(4 / 60)), dilation=1, kvsel=kv)
+    vol = torch.empty(61 ** 3, dtype=torch.float32, device=dev())
+    stats = torch.zeros(2 * V().STAT_FIELDS, dtype=torch.int64, device=dev())
+    dbg = V().HierDebug(params, with_sel=True)
+    V().vdm_decode_hier(dec, params, K, Vv, vol, stats, dbg)
+    torch.cuda.synchronize()
+    st = V().stats_dict(stats, 2)
+    od = oracle_decoder(w)
+    Kh, Vh = f64(K), f64(Vv)
+    rng = np.random.default_rng(9)
+    for L in range(2):
+        R = 30 << L
+        s, d = st[L], dbg.levels[L]
+        nocc = s["blocks"]
+        blocks = d["sel_blocks"][:nocc].cpu().numpy()
+        cnt = d["sel_cnt"][:nocc].cpu().numpy()
+        idx = d["sel_idx"][: nocc * kv["cap"]].cpu().numpy().reshape(nocc, kv["cap"])
+        assert s["selected"] == int(cnt.sum())
+        pick = np.sort(rng.choice(nocc, min(nocc, 12), replace=False))
+        compare_sets(dec, w, K, R, blocks[pick], kv["k"], kv["cap"], idx[pick], cnt[pick])
+        lst = d["list"][: s["queries"]].cpu().numpy().astype(np.int64)
+        volL = d["vol"].cpu().numpy()
+        blk = hv.block_of(lst, R + 1)
+        starts = np.searchsorted(blk, blocks)
+        ends = np.searchsorted(blk, blocks, side="right")
+        worst = 0.0
+        for r in pick:
+            m = lst[starts[r]:ends[r]][tile_sample(ends[r] - starts[r], DECODE_TILE)]
+            toks = idx[r, : cnt[r]]
+            ref = od.sdf(odec.grid_points(R, m), Kh[toks], Vh[toks])
+            worst = max(worst, np.abs(volL[m].astype(np.float64) - ref).max())
+        report(f"40,960-token selection, level {L}: sampled work items vs restricted attention", worst, TOL_BF16)
+        assert worst <= TOL_BF16
