@@ -38,6 +38,7 @@ constexpr int SEL_BQ = SEL_NP * SEL_GB;  // probe columns of the MFMA tile
 constexpr int SEL_MAXV = 64;             // scores per lane in the search: M <= 64 * 64
 constexpr int SEL_GRID_MAX = 256;        // workgroups (scratch rows are per workgroup)
 constexpr int SEL_LIST = 1024;           // per-wave candidate list of the top-k search (LDS)
+constexpr int SEL_LSTRIDE = SEL_LIST + 64;  // ... and one discard slot per lane after it
 constexpr int SEL_MAX_M = 65536;         // tokens of a selection (one set per block)
 constexpr int SEL_MAX_M_PH = 16384;      // tokens of a per-head selection (4 score rows per probe)
 constexpr int SEL_CHUNK = SEL_MAXV * 64; // tokens per search of a chunked row
@@ -61,7 +62,7 @@ __device__ __forceinline__ int wave_sum(int v) {
 // Values u[i] stand for index i * 64 + lane (entries at or past n are 0 and never
 // taken). Returns the lane's mask of the k largest (bit i: value i of this lane;
 // unsigned order; equal values: lower index first). One wave; `list` is its LDS
-// scratch of SEL_LIST values.
+// scratch of SEL_LSTRIDE values (SEL_LIST, then a discard slot per lane).
 //
 // The k-th largest value p is the largest threshold with #{u >= p} >= k, built
 // bit by bit. For k <= 64 the 64th largest of the lanes' two largest values, lo,
@@ -73,7 +74,10 @@ __device__ __forceinline__ int wave_sum(int v) {
 // values (3-4 times the work: with the smallest lane maximum as the bound and a
 // 256-entry list this path ran for most probes). Thresholds are >= 1, so zero
 // entries never count; values are visited in chunks of 16 and a chunk past n is
-// skipped.
+// skipped. Within a chunk nothing branches (a branch per value ends the
+// scheduling region): entries past n are 0, so they fail every comparison with
+// a positive threshold, and the list is filled by writing every value, those
+// below lo to the lane's discard slot.
 template <int NU>
 __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[NU], int n, int k, unsigned* list, int lane) {
   // (every loop is fully unrolled with constant indices, so u stays in registers)
@@ -114,24 +118,29 @@ __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[NU], int n, in
       const unsigned cand = lo | (1u << b);
       if (__popcll(__ballot(m1 >= cand)) + __popcll(__ballot(m2 >= cand)) >= 64) lo = cand;
     }
+    const unsigned lo1 = max(lo, 1u);
     int mine = 0;
 #pragma unroll
     for (int c0 = 0; c0 < NU; c0 += CH) {
       if (c0 * 64 < n) {
 #pragma unroll
-        for (int i = c0; i < c0 + CH; ++i) mine += (u[i] >= lo && u[i] > 0u) ? 1 : 0;
+        for (int i = c0; i < c0 + CH; ++i) mine += u[i] >= lo1 ? 1 : 0;
       }
     }
     const int incl = wave_incl_scan(mine, lane);
     const int total = __shfl(incl, 63);
     if (lo > 0u && total <= SEL_LIST) {
       int off = incl - mine;
+      const int discard = SEL_LIST + lane;
 #pragma unroll
       for (int c0 = 0; c0 < NU; c0 += CH) {
         if (c0 * 64 < n) {
 #pragma unroll
-          for (int i = c0; i < c0 + CH; ++i)
-            if (u[i] >= lo) list[off++] = u[i];
+          for (int i = c0; i < c0 + CH; ++i) {
+            const bool in = u[i] >= lo;
+            list[in ? off : discard] = u[i];
+            off += in ? 1 : 0;
+          }
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -178,42 +187,60 @@ __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[NU], int n, in
   }
   // copies of p to take, lowest index first; usually every copy (no tie at the cut)
   const int need = k - greater;
-  uint64_t sel = 0ull;
+  // (the mask in two 32-bit halves: constant shifts, no 64-bit shifts per value)
+  unsigned sel[2] = {0u, 0u};
   if (p > 0u && equal == need) {
 #pragma unroll
-    for (int i = 0; i < NU; ++i)
-      if (i * 64 < n) sel |= (uint64_t)(u[i] >= p) << i;  // (entries past n are 0 < p)
-    return sel;
+    for (int c0 = 0; c0 < NU; c0 += CH) {
+      if (c0 * 64 < n) {
+#pragma unroll
+        for (int i = c0; i < c0 + CH; ++i) sel[i >> 5] |= u[i] >= p ? 1u << (i & 31) : 0u;  // (past n: 0 < p)
+      }
+    }
+    return (uint64_t)sel[1] << 32 | sel[0];
   }
   int taken = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int i = 0; i < NU; ++i) {
-    if (i * 64 < n) {
-      const bool valid = i * 64 + lane < n;
-      const bool eq = valid && u[i] == p;
-      const unsigned long long be = __ballot(eq);
-      const int rank = taken + __popcll(be & ((1ull << lane) - 1ull));
-      sel |= (uint64_t)(valid && (u[i] > p || (eq && rank < need))) << i;
-      taken += __popcll(be);
+  for (int c0 = 0; c0 < NU; c0 += CH) {
+    if (c0 * 64 < n) {
+#pragma unroll
+      for (int i = c0; i < c0 + CH; ++i) {
+        const bool valid = i * 64 + lane < n;
+        const bool eq = valid && u[i] == p;
+        const unsigned long long be = __ballot(eq);
+        const int rank = taken + __popcll(be & below);
+        sel[i >> 5] |= valid && (u[i] > p || (eq && rank < need)) ? 1u << (i & 31) : 0u;
+        taken += __popcll(be);
+      }
     }
   }
-  return sel;
+  return (uint64_t)sel[1] << 32 | sel[0];
 }
 
 // Adds a wave's selection masks (bit i of lane l: token i * 64 + l) to a bitmap of
 // 32-bit words (token t: bit t % 32 of word t / 32; 8-byte aligned): the ballot of
-// bit i is words 2i and 2i+1.
+// bit i is words 2i and 2i+1. Lane i collects that ballot, then every
+// lane with a nonzero word ORs it in: one LDS atomic per lane, no branch per bit.
 __device__ __forceinline__ void add_to_bitmap(uint64_t sel, int n, unsigned* words, int lane) {
+  const unsigned s0 = (unsigned)sel, s1 = (unsigned)(sel >> 32);
+  int w0 = 0, w1 = 0;
 #pragma unroll
-  for (int i = 0; i < SEL_MAXV; ++i) {
-    if (i * 64 < n) {
-      const unsigned long long b = __ballot((sel >> i) & 1ull);
-      if (b != 0ull && lane == 0) atomicOr(reinterpret_cast<unsigned long long*>(words + 2 * i), b);
+  for (int c0 = 0; c0 < SEL_MAXV; c0 += 16) {
+    if (c0 * 64 < n) {
+#pragma unroll
+      for (int i = c0; i < c0 + 16; ++i) {
+        const unsigned long long b = __ballot(((i < 32 ? s0 : s1) >> (i & 31)) & 1u);
+        w0 = lane == i ? (int)(unsigned)b : w0;
+        w1 = lane == i ? (int)(unsigned)(b >> 32) : w1;
+      }
     }
   }
+  const unsigned long long w = (unsigned long long)(unsigned)w1 << 32 | (unsigned)w0;
+  if (w != 0ull) atomicOr(reinterpret_cast<unsigned long long*>(words) + lane, w);
 }
 
-// LDS: [embedding stage] | stats [NW][H][32] float2 | fin [H][32] | lists [NW][SEL_LIST] |
+// LDS: [embedding stage] | stats [NW][H][32] float2 | fin [H][32] | lists [NW][SEL_LSTRIDE] |
 //      bits [GB*NS][wst] | bits2 [GB*NS][wst] | cnt [GB*NS] | (cand [NW][SEL_LIST])
 //      (NS sets per block: H with per-head sets, else 1; wst = sel_wstride(M) words
 //      per set, an even number). Chunked rows (M > SEL_CHUNK) keep each wave's token
@@ -228,7 +255,7 @@ struct SelCfg {
   static constexpr int STATS = (EMB_END + 15) & ~15;
   static constexpr int FIN = STATS + SEL_NW * H * 32 * 8;
   static constexpr int LISTS = FIN + H * 32 * 4;
-  static constexpr int BITS = LISTS + SEL_NW * SEL_LIST * 4;
+  static constexpr int BITS = LISTS + SEL_NW * SEL_LSTRIDE * 4;
   static constexpr int CAND_BYTES = SEL_NW * SEL_LIST * 4;
   static constexpr bool CAND_LOW = FIN >= CAND_BYTES;
   static_assert(BITS % 16 == 0, "16-byte aligned bitmaps");
@@ -250,17 +277,17 @@ static_assert(SelCfg<bf16, 4, 1>::total(SEL_MAX_M) <= SEL_LDS_MAX && SelCfg<bf16
 // per-workgroup scratch: SEL_BQ rows of Mpad scores
 __host__ __device__ inline int sel_mpad(int M) { return (M + 63) / 64 * 64; }
 
-// Scores row r, element c0 + i * 64 + lane, for i = 0 .. SEL_MAXV-1, as unsigned
-// bits (0 past M). Buffer loads: a scalar offset per i, so no per-element address
-// registers are kept live.
-__device__ __forceinline__ void load_scores(__amdgpu_buffer_rsrc_t buf, int row, int Mp, int M, int lane,
+// Scores row r (of the rows starting at `scores`, Mp apart), element c0 + i * 64 +
+// lane, for i = 0 .. SEL_MAXV-1, as unsigned bits. The buffer covers the row's M
+// values only, so loads past M return 0 without touching memory. Buffer loads: a
+// scalar offset per i, so no per-element address registers are kept live.
+__device__ __forceinline__ void load_scores(const float* scores, int row, int Mp, int M, int lane,
                                             unsigned (&u)[SEL_MAXV], int c0 = 0) {
-  const int voff = (row * Mp + c0 + lane) * 4;
+  const __amdgpu_buffer_rsrc_t buf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scores) + (int64_t)row * Mp, (short)0, M * 4, 0x00020000 /* raw buffer */);
+  const int voff = (c0 + lane) * 4;
 #pragma unroll
-  for (int i = 0; i < SEL_MAXV; ++i) {
-    const unsigned v = __builtin_amdgcn_raw_buffer_load_b32(buf, voff, i * 256, 0);
-    u[i] = c0 + i * 64 + lane < M ? v : 0u;
-  }
+  for (int i = 0; i < SEL_MAXV; ++i) u[i] = __builtin_amdgcn_raw_buffer_load_b32(buf, voff, i * 256, 0);
 }
 
 // Rows of more than SEL_MAXV * 64 tokens are searched in chunks of that many. A
@@ -351,7 +378,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   unsigned* bits2 = bits + SEL_GB * NS * wst;                       // [GB][NS][wst]
   int* ucount = reinterpret_cast<int*>(bits2 + SEL_GB * NS * wst);  // [GB][NS]
   float* scores = A.scores + (int64_t)blockIdx.x * SEL_BQ * NS * Mp;   // [BQ][NS][Mp], this workgroup's rows
-  unsigned* wlist = reinterpret_cast<unsigned*>(lds + CF::LISTS) + wave * SEL_LIST;  // this wave's top-k list
+  unsigned* wlist = reinterpret_cast<unsigned*>(lds + CF::LISTS) + wave * SEL_LSTRIDE;  // this wave's top-k list
   int* cand = reinterpret_cast<int*>(lds + CF::cand(M)) + wave * SEL_LIST;          // chunked rows: token list
   const __amdgpu_buffer_rsrc_t sbuf =
       __builtin_amdgcn_make_buffer_rsrc(scores, (short)0, SEL_BQ * NS * Mp * 4, 0x00020000 /* raw buffer */);
@@ -475,7 +502,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
     float kcol[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) kcol[h] = fin[h * 32 + col];
-    float* tb = reinterpret_cast<float*>(lds + CF::LISTS) + wave * 1024;  // [32 probes][32 tokens], swizzled
+    float* tb = reinterpret_cast<float*>(lds + CF::LISTS) + wave * SEL_LSTRIDE;  // [32 probes][32 tokens], swizzled
     const int rr = lane >> 5, kk = lane & 31;
     auto transpose_store = [&](const float (&v)[16], float* dst0, int rstride) {
 #pragma unroll
@@ -540,14 +567,14 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
         const int srow = ((set / NS) * SEL_NP + pr) * NS + set % NS;
         if constexpr (!BIG) {
           unsigned u[SEL_MAXV];
-          load_scores(sbuf, srow, Mp, M, lane, u);
+          load_scores(scores, srow, Mp, M, lane, u);
           acc |= topk_mask(u, M, A.k, wlist, lane);
         } else {
           // each chunk's k largest, then the k largest of those (token order kept)
           int nc = 0;
           for (int c0 = 0; c0 < M; c0 += SEL_CHUNK) {
             unsigned u[SEL_MAXV];
-            load_scores(sbuf, srow, Mp, M, lane, u, c0);
+            load_scores(scores, srow, Mp, M, lane, u, c0);
             const int n = min(SEL_CHUNK, M - c0);
             nc = append_tokens(topk_mask(u, n, A.k, wlist, lane), c0, n, cand, nc, lane);
           }
@@ -619,7 +646,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       } else if (!BIG && cnt > A.cap) {
         // keep the cap tokens of largest max-over-probes score (members rank above non-members)
         unsigned u[SEL_MAXV];
-        load_scores(sbuf, (blk * SEL_NP) * NS + hs, Mp, M, lane, u);
+        load_scores(scores, (blk * SEL_NP) * NS + hs, Mp, M, lane, u);
         for (int q = 1; q < SEL_NP; ++q) {
           const int voff = (((blk * SEL_NP + q) * NS + hs) * Mp + lane) * 4;
 #pragma unroll
