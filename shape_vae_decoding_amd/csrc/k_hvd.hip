@@ -719,42 +719,97 @@ hipError_t launch_bits_to_bytes(const uint64_t* m, int n, int NB, uint8_t* out, 
 // only on its own block's token set). A run of a valid list (unique entries) holds
 // at most block^3 entries. An entry outside [0, (R+1)^3) belongs to no block: it
 // gets no item, ends the run it interrupts, and its output is set to NaN here.
-__global__ void items_from_list_kernel(const int32_t* __restrict__ list, int64_t N, int R, int block,
-                                       const int32_t* __restrict__ block_row, int bq, Item* __restrict__ items,
-                                       int32_t* n_items, float* __restrict__ out) {
-  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= N) return;
-  const int64_t P = R + 1;
-  const int NB = (R + block) / block;
-  auto blk = [&](int64_t lin) -> int64_t {  // -1: not a grid point
-    if (lin < 0 || lin >= P * P * P) return -1;
-    const int i = (int)(lin / (P * P));
-    const int64_t r = lin - (int64_t)i * P * P;
-    const int j = (int)(r / P), k = (int)(r - (int64_t)j * P);
-    return ((int64_t)(i / block) * NB + j / block) * NB + k / block;
-  };
-  const int64_t b = blk(list[q]);
-  if (b < 0) {
-    out[q] = __builtin_nanf("");
-    return;
+// One wave per 64 consecutive entries: the lanes compute the entries' blocks at
+// once, find the runs that start among them by ballot, and the whole wave looks
+// for each run's end 512 entries at a time; the lane of a run's start keeps its
+// chunk count, and the item slots of a workgroup's runs are taken with one atomic
+// (a serial scan per run by one thread, and an atomic per run, took about 1 ms for
+// 720,600 entries in 8^3 blocks; the atomics alone about 0.2 ms in 4^3 blocks).
+constexpr int ITEMS_NT = 1024;
+
+__device__ __forceinline__ int list_block(const int32_t* __restrict__ list, int64_t q, int64_t N, int R, int block) {
+  if (q < 0 || q >= N) return -2;  // (no entry)
+  const unsigned P = (unsigned)R + 1u, lin = (unsigned)list[q];
+  if (list[q] < 0 || lin >= P * P * P) return -1;  // (outside the grid; P^3 < 2^31)
+  const unsigned i = lin / (P * P), r = lin - i * P * P, j = r / P, k = r - j * P;
+  const unsigned NB = ((unsigned)R + (unsigned)block) / (unsigned)block;
+  return (int)(((i / block) * NB + j / block) * NB + k / block);
+}
+
+__global__ __launch_bounds__(ITEMS_NT) void items_from_list_kernel(const int32_t* __restrict__ list, int64_t N, int R,
+                                                                  int block, const int32_t* __restrict__ block_row,
+                                                                  int bq, Item* __restrict__ items, int32_t* n_items,
+                                                                  float* __restrict__ out) {
+  __shared__ int wtot[ITEMS_NT / 64];
+  __shared__ int base;
+  const int lane = (int)(threadIdx.x & 63), wave = (int)(threadIdx.x >> 6);
+  const int64_t seg0 = (int64_t)blockIdx.x * ITEMS_NT + 64 * wave;
+  const int64_t q = seg0 + lane;
+  int b = -2, nch = 0;  // this lane's block; chunks of the run starting here
+  int64_t e = 0;        // ... and that run's end
+  if (seg0 < N) {  // (wave-uniform)
+    b = list_block(list, q, N, R, block);
+    if (b == -1) out[q] = __builtin_nanf("");
+    const bool start = b >= 0 && (q == 0 || list_block(list, q - 1, N, R, block) != b);
+    for (unsigned long long st = __ballot(start); st; st &= st - 1ull) {
+      const int l = __ffsll((long long)st) - 1;
+      const int bs = __shfl(b, l);
+      // first entry after the start in another block (or past the list)
+      unsigned long long d = __ballot(lane > l && b != bs);
+      int64_t c = seg0;
+      // 8 x 64 entries per step, so that their loads overlap (past N: -2, a mismatch)
+      for (int64_t c8 = seg0 + 64; d == 0ull; c8 += 8 * 64) {
+        int blks[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) blks[u] = list_block(list, c8 + 64 * u + lane, N, R, block);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const unsigned long long du = __ballot(blks[u] != bs);
+          if (d == 0ull && du != 0ull) {
+            d = du;
+            c = c8 + 64 * u;
+          }
+        }
+      }
+      if (lane == l) {
+        e = c + __ffsll((long long)d) - 1;
+        nch = (int)((e - q + bq - 1) / bq);
+      }
+    }
   }
-  if (q > 0 && blk(list[q - 1]) == b) return;
-  int64_t e = q + 1;
-  while (e < N && blk(list[e]) == b) ++e;
-  const int nch = (int)((e - q + bq - 1) / bq);
-  const int at = atomicAdd(n_items, nch);
-  const int row = block_row ? block_row[b] : (int)b;
-  (void)VDM_BOUND(row >= 0, BC_LIST_ROW);
-  for (int c = 0; c < nch; ++c) {
-    const int64_t q0 = q + (int64_t)c * bq;
-    items[at + c] = Item{(int32_t)q0, (int32_t)min(q0 + bq, e), row, 0};
+  int incl = nch;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int w = 0; w < ITEMS_NT / 64; ++w) {
+      const int v = wtot[w];
+      wtot[w] = t;
+      t += v;
+    }
+    base = t > 0 ? atomicAdd(n_items, t) : 0;
+  }
+  __syncthreads();
+  if (nch > 0) {
+    const int at = base + wtot[wave] + incl - nch;
+    const int row = block_row ? block_row[b] : b;
+    (void)VDM_BOUND(row >= 0, BC_LIST_ROW);
+    for (int ch = 0; ch < nch; ++ch) {
+      const int64_t q0 = q + (int64_t)ch * bq;
+      items[at + ch] = Item{(int32_t)q0, (int32_t)min(q0 + bq, e), row, 0};
+    }
   }
 }
 
 hipError_t launch_items_from_list(const int32_t* list, int64_t N, int R, int block, const int32_t* block_row, int bq,
                                   Item* items, int32_t* n_items, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(items_from_list_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, list, N, R, block,
-                     block_row, bq, items, n_items, out);
+  hipLaunchKernelGGL(items_from_list_kernel, dim3((unsigned)((N + ITEMS_NT - 1) / ITEMS_NT)), dim3(ITEMS_NT), 0, s,
+                     list, N, R, block, block_row, bq, items, n_items, out);
   return hipGetLastError();
 }
 
