@@ -199,14 +199,20 @@ __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[NU], int n, in
     }
     return (uint64_t)sel[1] << 32 | sel[0];
   }
+  // (ties at the cut, rare: entries past n are 0, so only a cut of 0 needs the
+  // index test; the lane comes through an opaque copy so that those 64 compares
+  // are not hoisted out of the callers' loops, where they took 64 VGPRs and 128
+  // spilled SGPRs)
   int taken = 0;
-  const uint64_t below = (1ull << lane) - 1ull;
+  const int ln = opaque(lane);
+  const uint64_t below = (1ull << ln) - 1ull;
+  const bool zero_cut = p == 0u;
 #pragma unroll
   for (int c0 = 0; c0 < NU; c0 += CH) {
     if (c0 * 64 < n) {
 #pragma unroll
       for (int i = c0; i < c0 + CH; ++i) {
-        const bool valid = i * 64 + lane < n;
+        const bool valid = !zero_cut || i * 64 + ln < n;
         const bool eq = valid && u[i] == p;
         const unsigned long long be = __ballot(eq);
         const int rank = taken + __popcll(be & below);
@@ -225,6 +231,7 @@ __device__ __forceinline__ uint64_t topk_mask(const unsigned (&u)[NU], int n, in
 __device__ __forceinline__ void add_to_bitmap(uint64_t sel, int n, unsigned* words, int lane) {
   const unsigned s0 = (unsigned)sel, s1 = (unsigned)(sel >> 32);
   int w0 = 0, w1 = 0;
+  lane = opaque(lane);  // (the 64 tests lane == i are not hoisted into spilled scalar masks)
 #pragma unroll
   for (int c0 = 0; c0 < SEL_MAXV; c0 += 16) {
     if (c0 * 64 < n) {
@@ -653,9 +660,10 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
           for (int i = 0; i < SEL_MAXV; ++i)  // scores >= 0: bit order is float order
             u[i] = max(u[i], __builtin_amdgcn_raw_buffer_load_b32(sbuf, voff, i * 256, 0));
         }
+        const int ln = opaque(lane);  // (the 64 indices are not hoisted out of the set loop)
 #pragma unroll
         for (int i = 0; i < SEL_MAXV; ++i) {
-          const int idx = i * 64 + lane;
+          const int idx = i * 64 + ln;
           const bool member = idx < M && ((ub[idx >> 5] >> (idx & 31)) & 1u);
           u[i] = member ? u[i] + 1u : 0u;
         }
