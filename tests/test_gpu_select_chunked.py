@@ -145,3 +145,22 @@ def test_hier_with_selection_many_tokens(big):
             worst = max(worst, np.abs(volL[m].astype(np.float64) - ref).max())
         report(f"40,960-token selection, level {L}: sampled work items vs restricted attention", worst, TOL_BF16)
         assert worst <= TOL_BF16
+
+
+@pytest.mark.parametrize("dtype,M", [("f32", 5000), ("bf16", 9000)])
+def test_select_many_tokens_one_head(dtype, M):
+    # the one-head decoders (D = 64, bf16 and float32) over chunked rows: the cap
+    # of 100 binds, so the member-list ranking runs too; per-head sets of one head
+    # are the head-mean sets
+    w = W.gen.small_decoder(70 + M, 64, 128, M, dtype)
+    dec = gpu_decoder(w)
+    K, _ = gpu_kv(dec, w)
+    R = 75
+    blocks = _blocks(R, 16, M)
+    for cap in (512, 100):
+        sel_idx, sel_cnt = run_select(dec, w, K, R, blocks, 64, cap)
+        assert np.all(sel_cnt <= cap) and np.all(sel_cnt >= 64)
+        compare_sets(dec, w, K, R, blocks, 64, cap, sel_idx, sel_cnt)
+    hi, hc = run_select_heads(dec, w, K, R, blocks, 64, 100)
+    si, sc = run_select(dec, w, K, R, blocks, 64, 100)
+    assert np.array_equal(hc[:, 0], sc) and np.array_equal(hi[:, 0], si)
