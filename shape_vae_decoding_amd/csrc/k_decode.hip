@@ -633,6 +633,95 @@ __device__ __forceinline__ void dense_attention(const DecodeArgs& A, int shape, 
                                   l_run);
 }
 
+// dense_attention with the tile's work in two phases (16-bit types, two query
+// groups): per 32-token tile k the wave runs the softmax of S(k), then the MFMAs
+// S(k+1) = K(k+1) Q and O += V(k) P(k) (the same products, summed in the same
+// order as dense_attention). The two waves that share a SIMD (same head, query
+// groups 0 and 1) are given different instruction schedules: group 0 has a
+// scheduling barrier between its softmax and its MFMAs, so the compiler overlaps
+// a tile's P.V with the next tile's softmax; group 1 has one at each tile
+// boundary, so it overlaps the next tile's S MFMAs with the current softmax.
+// Side by side the two mixes keep the matrix pipe busier: 4-5 % less time per
+// dense launch than the interleaved schedule of dense_attention, while either
+// schedule on every wave was no faster (nor were hardware barriers that forced
+// the waves into opposite phases: 9 % slower).
+template <typename C, bool SHIFT>
+__device__ __forceinline__ void dense_attention_2phase(const DecodeArgs& A, int shape, int kt0, int nkeys, int hw,
+                                                       int qg, int lane,
+                                                       const typename Mma<typename C::T>::frag (&qf)[C::QB][C::KSTEPS],
+                                                       const float (&nb)[C::QB], f32x16 (&O)[2][C::QB],
+                                                       float (&l_run)[C::QB]) {
+  using T = typename C::T;
+  using MM = Mma<T>;
+  using Frag = typename MM::frag;
+  const int nkt = (nkeys + C::KT - 1) / C::KT;
+  if (nkt == 0) return;
+  const int64_t packed_bytes = (int64_t)nkt * C::KT * C::D * C::SZ;
+  const int64_t first = shape * A.kv_stride + (int64_t)kt0 * C::KT * C::D * C::SZ;
+  const __amdgpu_buffer_rsrc_t Kg = buffer_of((const char*)A.Kp + first, packed_bytes);
+  const __amdgpu_buffer_rsrc_t Vg = buffer_of((const char*)A.Vt + first, packed_bytes);
+  const bool g0 = qg == 0;  // (wave-uniform)
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  uint4 kb[2][C::RUN_U4], vb[2][C::RUN_U4];
+  f32x16 S[C::QB];
+  Frag P[C::QB][C::PSTEPS];
+  load_run<C>(Kg, 0, hw, lane, kb[0]);
+  load_run<C>(Vg, 0, hw, lane, vb[0]);
+  load_run<C>(Kg, nkt > 1 ? 1 : 0, hw, lane, kb[1]);
+  {
+    const Frag* kp = reinterpret_cast<const Frag*>(kb[0]);
+    Frag kf[C::KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = kp[ks];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) S[qb] = s_block<C>(kf, qf[qb]);
+  }
+  if (!g0) fence();
+  // tile kt: S holds S(kt), kn K(kt+1), vc V(kt); kl and vl receive K(kt+2), V(kt+1)
+  auto tile = [&](auto last_tag, const uint4 (&kn)[C::RUN_U4], const uint4 (&vc)[C::RUN_U4],
+                  uint4 (&kl)[C::RUN_U4], uint4 (&vl)[C::RUN_U4], int kt) {
+    constexpr bool LAST = decltype(last_tag)::value;  // (the last tile may be partial)
+    if constexpr (!LAST) {
+      load_run<C>(Kg, kt + 2 < nkt ? kt + 2 : nkt - 1, hw, lane, kl);
+      load_run<C>(Vg, kt + 1, hw, lane, vl);
+    }
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+      softmax_block<T, LAST, SHIFT>(S[qb], nb[qb], l_run[qb], kt * C::KT, nkeys, lane, P[qb]);
+    if (g0) fence();
+    Frag kf[C::KSTEPS], vf[2][C::PSTEPS];
+    as_frags<C>(kn, vc, kf, vf);
+    if constexpr (!LAST) {
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) S[qb] = s_block<C>(kf, qf[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int ps = 0; ps < C::PSTEPS; ++ps) O[db][qb] = MM::mma(vf[db][ps], P[qb][ps], O[db][qb]);
+    if (!g0 && !LAST) fence();
+  };
+  using No = std::integral_constant<bool, false>;
+  using Yes = std::integral_constant<bool, true>;
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {  // two tiles per step, so the buffers are static
+    tile(No(), kb[1], vb[0], kb[0], vb[1], kt);
+    tile(No(), kb[0], vb[1], kb[1], vb[0], kt + 1);
+  }
+  if (kt + 1 < nkt) {  // one more full tile (kt even)
+    tile(No(), kb[1], vb[0], kb[0], vb[1], kt);
+    ++kt;
+  }
+  // the last tile, kt = nkt - 1: V(kt) is in vb[kt & 1]
+  if (kt & 1) {
+#pragma unroll
+    for (int i = 0; i < C::RUN_U4; ++i) vb[0][i] = vb[1][i];
+  }
+  tile(Yes(), kb[0], vb[0], kb[1], vb[1], kt);
+}
+
 // V^T fragment (A operand of O^T += V^T P^T) for dims d0 .. d0+31 and MFMA step
 // ps, read from row-major V [KT][VROW] in LDS with two transposing reads. Within
 // each 16-lane group, ds_read_b64_tr_b16 gives lane i element i%4 of the 8-byte
@@ -1042,6 +1131,11 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       }
       if (!active) {
         // (every query of this wave lies past the tile's end: nothing to attend)
+      } else if constexpr (C::SCHED_ATT) {
+        if (shift)
+          dense_attention_2phase<C, true>(A, shape, kt0, nk, hw, qg, lane, qf, nb, O, l_run);
+        else
+          dense_attention_2phase<C, false>(A, shape, kt0, nk, hw, qg, lane, qf, nb, O, l_run);
       } else if (shift) {
         dense_attention<C, true>(A, shape, kt0, nk, hw, lane, qf, nb, O, l_run);
       } else {
