@@ -566,7 +566,8 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       for (int it = wave * per; it < it1; ++it) {
         const int set = it / SEL_NP, pr = it % SEL_NP;
         if (set != cur) {
-          if (cur >= 0) add_to_bitmap(acc, M, bits + cur * wst, lane);
+          if constexpr (!BIG)  // (chunked rows mark their tokens directly)
+            if (cur >= 0) add_to_bitmap(acc, M, bits + cur * wst, lane);
           acc = 0ull;
           cur = set;
         }
