@@ -1312,13 +1312,23 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     }
     };
     if constexpr (C::CPW == C::CB && GATHER) {
-      // (work items of a block's token set often end part-way through a tile;
-      // wave-uniform: the item's query count)
+      // (work items of a block's token set often end part-way through a tile: the
+      // epilogue runs on the item's 32-query column blocks only; wave-uniform)
       const int ncb = (int)((q1 - q0 + 31) / 32);
-      if (2 * ncb > C::CB)
+      if constexpr (C::CB == 4) {
+        if (ncb > 3)
+          epilogue(std::integral_constant<int, 4>{});
+        else if (ncb == 3)
+          epilogue(std::integral_constant<int, 3>{});
+        else if (ncb == 2)
+          epilogue(std::integral_constant<int, 2>{});
+        else
+          epilogue(std::integral_constant<int, 1>{});
+      } else if (2 * ncb > C::CB) {
         epilogue(std::integral_constant<int, C::CB>{});
-      else
+      } else {
         epilogue(std::integral_constant<int, C::CB / 2>{});
+      }
     } else {
       epilogue(std::integral_constant<int, C::CPW>{});
     }
