@@ -30,11 +30,13 @@
 //
 // Dense mode: each wave streams its head's pre-packed K and V^T operand runs
 // straight from L2 into registers (no LDS, no barriers in the token loop), in a
-// software pipeline that overlaps the loads, the P.V and S MFMAs and the softmax.
-// Gathered mode reads the selected tokens' rows into an LDS double buffer
-// (V transposed on the way in), one barrier per 32-token tile.
-// The epilogue streams each weight row once per workgroup from L2 with a 4-deep
-// register prefetch ring.
+// software pipeline that overlaps the loads, the P.V and S MFMAs and the softmax;
+// for bf16 the two waves of a head that share a SIMD (its two query groups) run
+// that loop under different instruction schedules (dense_attention_2phase).
+// Gathered mode reads the selected tokens' rows into LDS stages (two K, three V;
+// V read transposed), one barrier per 32-token tile.
+// The epilogue streams each weight row once per workgroup from L2 with an
+// 8-deep register prefetch ring.
 #include "vdm_device.hpp"
 
 namespace vdm {
