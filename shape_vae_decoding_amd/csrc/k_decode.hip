@@ -35,8 +35,10 @@
 // that loop under different instruction schedules (dense_attention_2phase).
 // Gathered mode reads the selected tokens' rows into LDS stages (two K, three V;
 // V read transposed), one barrier per 32-token tile.
-// The epilogue streams each weight row once per workgroup from L2 with an
-// 8-deep register prefetch ring.
+// The epilogue streams each weight row once per workgroup from L2 through a
+// 4-deep register prefetch ring that runs through the chain of products (Wo,
+// then W1 and W2 per hidden chunk): each product starts with its first weights
+// already requested, across the barrier before it.
 #include "vdm_device.hpp"
 
 namespace vdm {
@@ -336,6 +338,68 @@ __device__ __forceinline__ void gemm_rows(const T* __restrict__ W, int ldw, cons
     for (int r = 0; r < NR; ++r) {
       a[r] = ring[r][ks % PF];
       if (ks + PF < NKS) ring[r][ks % PF] = wfrag(r, ks + PF);
+    }
+    if (ks + BD - 1 < NKS) {
+#pragma unroll
+      for (int i = 0; i < NC; ++i) b[(ks + BD - 1) % BD][i] = bfrag(i, ks + BD - 1);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < NC; ++i) acc[r][i] = MM::mma(a[r], b[ks % BD][i], acc[r][i]);
+  }
+}
+
+// Weight fragment of row block r, MFMA step ks, as gemm_rows reads it.
+template <typename T, bool PACKED>
+__device__ __forceinline__ typename Mma<T>::frag wfrag_at(const T* __restrict__ W, int ldw, int r, int ks, int lane) {
+  using MM = Mma<T>;
+  if constexpr (PACKED)
+    return *reinterpret_cast<const typename MM::frag*>(W + ((int64_t)r * (ldw / MM::KS) + ks) * (32 * MM::KS) +
+                                                       lane * MM::KW);
+  else
+    return load_frag<T>(W + (int64_t)(32 * r) * ldw + ks * MM::KS, ldw, lane);
+}
+
+// The first PF weight steps of W for NR row blocks, into a prefetch ring.
+template <typename T, int NR, int PF, bool PACKED>
+__device__ __forceinline__ void wring_fill(const T* __restrict__ W, int ldw, typename Mma<T>::frag (&ring)[NR][PF],
+                                           int lane) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int p = 0; p < PF; ++p) ring[r][p] = wfrag_at<T, PACKED>(W, ldw, r, p, lane);
+}
+
+// gemm_rows with the weight ring passed in already holding W's first PF steps.
+// With NEXT, the steps freed at the end take the first PF steps of Wn, so the
+// next product of the chain starts with its weights in flight or landed: the
+// loads cross the barrier between the two products (weights do not depend on
+// it), instead of each product waiting for a full L2 round trip at its start.
+template <typename T, int NKS, int NR, int NC, bool PACKED, int PF, bool NEXT, int BPF = 2>
+__device__ __forceinline__ void gemm_rows_chained(const T* __restrict__ W, int ldw, const T* __restrict__ Wn, int ldwn,
+                                                  const T* B, int ldb, int cb0, f32x16 (&acc)[NR][NC],
+                                                  typename Mma<T>::frag (&ring)[NR][PF], int lane) {
+  using MM = Mma<T>;
+  using Frag = typename MM::frag;
+  static_assert(NKS % PF == 0, "the next product's steps land in the slots its loop reads");
+  auto bfrag = [&](int i, int ks) -> Frag { return load_frag<T>(B + (32 * (cb0 + i)) * ldb + ks * MM::KS, ldb, lane); };
+  constexpr int BD = NKS < BPF + 1 ? NKS : BPF + 1;  // B steps held (LDS reads BD - 1 steps ahead)
+  Frag b[BD][NC];
+#pragma unroll
+  for (int d = 0; d < BD - 1; ++d)
+#pragma unroll
+    for (int i = 0; i < NC; ++i) b[d][i] = bfrag(i, d);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    Frag a[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      a[r] = ring[r][ks % PF];
+      if (ks + PF < NKS)
+        ring[r][ks % PF] = wfrag_at<T, PACKED>(W, ldw, r, ks + PF, lane);
+      else if constexpr (NEXT)
+        ring[r][ks % PF] = wfrag_at<T, PACKED>(Wn, ldwn, r, ks + PF - NKS, lane);
     }
     if (ks + BD - 1 < NKS) {
 #pragma unroll
@@ -1223,6 +1287,21 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     // ---------------------------------------------------------------- o = sum p v / sum p
     tid = opaque(tid);
     lane = opaque(lane);
+    // this wave's epilogue tiles: weight row blocks rb0 .. rb0 + RPW - 1, column
+    // blocks cb0 .. cb0 + NCB - 1. In gathered mode, when every wave covers all
+    // column blocks, a work item with at most half a tile of queries computes only
+    // the first half of the column blocks.
+    const int rb0 = C::TPW >= C::CB ? wave * C::RPW : (wave * C::TPW) / C::CB;
+    const int cb0 = C::TPW >= C::CB ? 0 : (wave * C::TPW) % C::CB;
+    const int rh0 = C::TPH >= C::CB ? wave * C::RPH : (wave * C::TPH) / C::CB;
+    const int ch0 = C::TPH >= C::CB ? 0 : (wave * C::TPH) % C::CB;
+    // one weight prefetch ring runs through the chain Wo, W1, W2, W1, ... W2; its
+    // first Wo steps are issued before the O stores and their barrier
+    constexpr int NKD = C::D / MM::KS;
+    constexpr int PFE = NKD < 4 ? NKD : 4;
+    static_assert(C::FC == C::D && C::RPH == C::RPW, "one ring shape serves Wo, W1 and W2");
+    Frag wring[C::RPW][PFE];
+    wring_fill<T, C::RPW, PFE, C::PACKED_W>(wblock<C>(Wo, rb0, 0, C::D), C::D, wring, lane);
     T* Ob = reinterpret_cast<T*>(lds + C::OBUF);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
@@ -1238,14 +1317,6 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     __syncthreads();
 
     // ---------------------------------------------------------------- a = Wo o  (kept in fp32 as y)
-    // this wave's epilogue tiles: weight row blocks rb0 .. rb0 + RPW - 1, column
-    // blocks cb0 .. cb0 + NCB - 1. In gathered mode, when every wave covers all
-    // column blocks, a work item with at most half a tile of queries computes only
-    // the first half of the column blocks.
-    const int rb0 = C::TPW >= C::CB ? wave * C::RPW : (wave * C::TPW) / C::CB;
-    const int cb0 = C::TPW >= C::CB ? 0 : (wave * C::TPW) % C::CB;
-    const int rh0 = C::TPH >= C::CB ? wave * C::RPH : (wave * C::TPH) / C::CB;
-    const int ch0 = C::TPH >= C::CB ? 0 : (wave * C::TPH) % C::CB;
     T* Ab = reinterpret_cast<T*>(lds + C::ABUF);
     T* Hb = reinterpret_cast<T*>(lds + C::OBUF);
     float* red = reinterpret_cast<float*>(lds + C::RED);
@@ -1257,8 +1328,8 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     for (int r = 0; r < C::RPW; ++r)
 #pragma unroll
       for (int i = 0; i < NCB; ++i) Y[r][i] = zero16();
-    gemm_rows<T, C::D / MM::KS, C::RPW, NCB, C::PACKED_W>(wblock<C>(Wo, rb0, 0, C::D), C::D, Ob, C::DPAD, cb0,
-                                                          Y, lane);
+    gemm_rows_chained<T, NKD, C::RPW, NCB, C::PACKED_W, PFE, true>(
+        wblock<C>(Wo, rb0, 0, C::D), C::D, wblock<C>(W1, rh0, 0, C::D), C::D, Ob, C::DPAD, cb0, Y, wring, lane);
 #pragma unroll
     for (int r = 0; r < C::RPW; ++r)
 #pragma unroll
@@ -1267,14 +1338,17 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     __syncthreads();
 
     // ---------------------------------------------------------------- y = a + W2 GELU(W1 a)
-    for (int f0 = 0; f0 < A.F; f0 += C::FC) {
+    // (hidden chunks of FC; the last W2 product ends the weight chain)
+    auto chunk = [&](int f0, auto last_tag) {
+      constexpr bool LASTC = decltype(last_tag)::value;
       f32x16 Hc[C::RPH][NCH];
 #pragma unroll
       for (int r = 0; r < C::RPH; ++r)
 #pragma unroll
         for (int j = 0; j < NCH; ++j) Hc[r][j] = zero16();
-      gemm_rows<T, C::D / MM::KS, C::RPH, NCH, C::PACKED_W>(wblock<C>(W1, f0 / 32 + rh0, 0, C::D), C::D, Ab, C::DPAD,
-                                                            ch0, Hc, lane);
+      gemm_rows_chained<T, NKD, C::RPH, NCH, C::PACKED_W, PFE, true>(
+          wblock<C>(W1, f0 / 32 + rh0, 0, C::D), C::D, wblock<C>(W2, rb0, f0 / MM::KS, A.F), A.F, Ab, C::DPAD, ch0,
+          Hc, wring, lane);
 #pragma unroll
       for (int r = 0; r < C::RPH; ++r)
 #pragma unroll
@@ -1283,10 +1357,14 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
           store_ct<T>(Hb + (32 * (ch0 + j)) * C::HPAD + 32 * (rh0 + r), C::HPAD, Hc[r][j], lane);
         }
       __syncthreads();
-      gemm_rows<T, C::FC / MM::KS, C::RPW, NCB, C::PACKED_W>(wblock<C>(W2, rb0, f0 / MM::KS, A.F), A.F, Hb, C::HPAD,
-                                                             cb0, Y, lane);
+      gemm_rows_chained<T, C::FC / MM::KS, C::RPW, NCB, C::PACKED_W, PFE, !LASTC>(
+          wblock<C>(W2, rb0, f0 / MM::KS, A.F), A.F, wblock<C>(W1, (f0 + C::FC) / 32 + rh0, 0, C::D), C::D, Hb,
+          C::HPAD, cb0, Y, wring, lane);
       __syncthreads();
-    }
+    };
+    int f0 = 0;
+    for (; f0 + C::FC < A.F; f0 += C::FC) chunk(f0, std::false_type());
+    chunk(f0, std::true_type());  // (F >= FC, checked when the decoder is created)
 
     // ---------------------------------------------------------------- net = w_head . y, SDF
     {
