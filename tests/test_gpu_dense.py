@@ -120,6 +120,27 @@ def test_dense_small_decoder_bf16_d64():
     assert err <= TOL_BF16
 
 
+@pytest.mark.parametrize("D,F,dtype", [(256, 256, "bf16"), (256, 768, "bf16"), (256, 4096, "bf16"),
+                                       (64, 64, "bf16"), (64, 64, "f32"), (64, 192, "f32")])
+def test_dense_mlp_widths(D, F, dtype):
+    # the epilogue's weight ring runs through Wo, then W1 and W2 per hidden chunk
+    # (256 wide for D = 256, 64 for D = 64): one chunk, an odd count and the
+    # widest MLP the library accepts, over a ragged grid (13^3 = 2,197 points:
+    # 17 tiles, the last one partial) and a ragged token count
+    w = W.gen.small_decoder(90 + F + D, D, F, 100, dtype)
+    dec = gpu_decoder(w)
+    K, Vv = gpu_kv(dec, w)
+    R = 12
+    sdf = torch.empty((R + 1) ** 3, dtype=torch.float32, device=dev())
+    V().vdm_decode_dense(dec, V().queries_grid(R), K, Vv, sdf)
+    torch.cuda.synchronize()
+    od = _bf16_identical_inputs(w, K, Vv) if dtype == "bf16" else oracle_decoder(w)
+    err = np.abs(f64(sdf) - od.sdf_grid(R)).max()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    report(f"{dtype} D={D} F={F} 13^3", err, tol)
+    assert err <= tol
+
+
 def test_dense_modes_agree_bitwise():
     # every query's value depends only on its own position: grid, list and point
     # modes (different tile compositions) give identical bits
