@@ -1057,7 +1057,9 @@ __device__ __forceinline__ void gathered_attention(const typename C::T* __restri
   }
 }
 
-template <typename C, bool GATHER>
+// RAGGED: a batch whose shapes have their own device-side counts (tile_prefix);
+// a separate instance, so that the single-shape kernels keep their registers.
+template <typename C, bool GATHER, bool RAGGED>
 __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   extern __shared__ __align__(16) char lds[];
   using T = typename C::T;
@@ -1068,12 +1070,11 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   const int tid0 = threadIdx.x, lane0 = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // wave-uniform: scalar registers
   const int hw = wave % C::H, qg = wave / C::H;
-  const int64_t nq = A.d_N ? (int64_t)*A.d_N : A.N;
   const int nbatch = A.batch > 1 ? A.batch : 1;
-  const int64_t tps = (nq + C::BQ - 1) / C::BQ;  // dense tiles per shape
-  const int64_t n_tiles = A.items ? (A.d_n_items ? (int64_t)*A.d_n_items : A.n_tiles) : tps * nbatch;
-  const T* __restrict__ Kg = (const T*)A.Kp;
-  const T* __restrict__ Vg = (const T*)A.Vt;
+  const int64_t nq_all = A.d_N ? (int64_t)*A.d_N : A.N;
+  const int64_t tps = (nq_all + C::BQ - 1) / C::BQ;  // dense tiles per shape (same-size batch)
+  const int64_t n_tiles = RAGGED ? A.tile_prefix[nbatch]
+                                 : A.items ? (A.d_n_items ? (int64_t)*A.d_n_items : A.n_tiles) : tps * nbatch;
   const T* __restrict__ Wo = (const T*)A.Wo;
   const T* __restrict__ W1 = (const T*)A.W1;
   const T* __restrict__ W2 = (const T*)A.W2;
@@ -1107,9 +1108,34 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     int tid = opaque(tid0), lane = opaque(lane0);
     int64_t q0, q1;
     int row = -1, shape = 0;
+    int64_t nq = nq_all;
+    const Item* items = A.items;
+    const int32_t* sel_cnt = A.sel_cnt;
+    const int32_t* sel_idx = A.sel_idx;
+    const T* __restrict__ Kg = (const T*)A.Kp;
+    const T* __restrict__ Vg = (const T*)A.Vt;
+    if constexpr (RAGGED) {
+      // the shape whose tiles hold this one: tile_prefix[shape] <= tile <
+      // tile_prefix[shape + 1] (a shape without tiles has equal neighbours and is
+      // passed over); then that shape's count, items, selection and K/V
+      int lo = 0;
+#pragma unroll
+      for (int step = 2048; step >= 1; step >>= 1) {  // (batches of at most 4096 shapes)
+        const int mid = lo + step;
+        lo = mid < nbatch && A.tile_prefix[mid] <= tile ? mid : lo;
+      }
+      shape = __builtin_amdgcn_readfirstlane(lo);
+      tile -= A.tile_prefix[shape];
+      nq = A.d_N[shape * A.cnt_stride];
+      items = reinterpret_cast<const Item*>((const char*)A.items + shape * A.items_stride);
+      sel_cnt = reinterpret_cast<const int32_t*>((const char*)A.sel_cnt + shape * A.sel_stride);
+      sel_idx = reinterpret_cast<const int32_t*>((const char*)A.sel_idx + shape * A.sel_stride);
+      Kg = reinterpret_cast<const T*>((const char*)A.Kp + shape * A.kv_stride);
+      Vg = reinterpret_cast<const T*>((const char*)A.Vt + shape * A.kv_stride);
+    }
     if (A.items) {
       // one item per workgroup: its fields are uniform (scalar registers)
-      const Item it = A.items[tile];
+      const Item it = items[tile];
       q0 = __builtin_amdgcn_readfirstlane(it.q0);
       q1 = __builtin_amdgcn_readfirstlane(it.q1);
       row = __builtin_amdgcn_readfirstlane(it.row);
@@ -1118,18 +1144,23 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       if (!VDM_BOUND(!GATHER || row >= 0, BC_DECODE_ROW)) continue;
     } else {
       int64_t lt = tile;
-      if (nbatch > 1) {
+      if (!RAGGED && nbatch > 1) {
         shape = (int)(tile / tps);
         lt = tile - (int64_t)shape * tps;
       }
       q0 = lt * C::BQ;
       q1 = q0 + C::BQ < nq ? q0 + C::BQ : nq;
     }
-    const float kmax = A.kmax[shape * C::H + hw];
+    const float kmax = A.kmax[shape * (RAGGED ? A.kmax_stride : C::H) + hw];
 
     // ---------------------------------------------------------------- Q = Wq e(p)
     // (scaled by log2(e)/sqrt(64) before the one rounding, so logits come out in base 2)
-    embed_qproj<T, C::BQ, C::D, C::NT>(A.qs, q0, q1, (const T*)A.Wq, lds, tid, SOFTMAX_SCALE_LOG2);
+    auto query_src = [&] {  // (rebuilt where used: not held across the token loop)
+      QuerySrc q = A.qs;
+      if constexpr (RAGGED) q.list = reinterpret_cast<const int32_t*>((const char*)A.qs.list + shape * A.list_stride);
+      return q;
+    };
+    embed_qproj<T, C::BQ, C::D, C::NT>(query_src(), q0, q1, (const T*)A.Wq, lds, tid, SOFTMAX_SCALE_LOG2);
     lane = opaque(lane);
     Frag qf[C::QB][KS];
     float nb[C::QB];  // the fixed softmax shift of this lane's query (if one is needed), per block
@@ -1159,9 +1190,9 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
     // ---------------------------------------------------------------- attention
     // gathered: this wave's token set (per-head sets: selection row row * H + head)
     const int64_t srow = GATHER ? (A.heads ? (int64_t)row * C::H + hw : row) : 0;
-    const int nkeys = GATHER ? min(max(A.sel_cnt[srow], 0), A.cap) : A.M;
-    if (GATHER) (void)VDM_BOUND(A.sel_cnt[srow] >= 0 && A.sel_cnt[srow] <= A.cap, BC_DECODE_SET);
-    const int32_t* sel = GATHER ? A.sel_idx + srow * A.cap : nullptr;
+    const int nkeys = GATHER ? min(max(sel_cnt[srow], 0), A.cap) : A.M;
+    if (GATHER) (void)VDM_BOUND(sel_cnt[srow] >= 0 && sel_cnt[srow] <= A.cap, BC_DECODE_SET);
+    const int32_t* sel = GATHER ? sel_idx + srow * A.cap : nullptr;
 
     f32x16 O[2][C::QB];
     float l_run[C::QB];
@@ -1256,12 +1287,12 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
         constexpr int CPR = C::D / C::EPC;
         const int hs = ((tid % CPR) * C::EPC) / 64;
         const int64_t st_row = (int64_t)row * C::H + hs;
-        const int nk_st = min(max(A.sel_cnt[st_row], 0), A.cap);
+        const int nk_st = min(max(sel_cnt[st_row], 0), A.cap);
         int nmax = 0;
 #pragma unroll
-        for (int h = 0; h < C::H; ++h) nmax = max(nmax, min(max(A.sel_cnt[(int64_t)row * C::H + h], 0), A.cap));
+        for (int h = 0; h < C::H; ++h) nmax = max(nmax, min(max(sel_cnt[(int64_t)row * C::H + h], 0), A.cap));
         const int nkt = (nmax + C::KT - 1) / C::KT;
-        const int32_t* sel_st = A.sel_idx + st_row * A.cap;
+        const int32_t* sel_st = sel_idx + st_row * A.cap;
         if (shift)
           gathered_attention<C, true>(Kg, Vg, sel_st, nk_st, nkeys, nkt, A.M, tid, lane, hw, lds, vpos, active, qf, nb,
                                       O, l_run);
@@ -1413,16 +1444,17 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
       epilogue(std::integral_constant<int, C::CPW>{});
     }
     __syncthreads();
+    const QuerySrc qs = query_src();
     for (int t = tid; t < C::BQ; t += C::NT) {
       const int64_t q = q0 + t;
       if (q < q1) {
         float net = 0.f;
 #pragma unroll
         for (int w = 0; w < C::NW; ++w) net += red[w * C::BQ + t];
-        const Coords p = query_coords(A.qs, q);
+        const Coords p = query_coords(qs, q);
         const float sdf = analytic_sdf(p, A.prims) + A.net_scale * net;
         int64_t o = q;
-        if (A.scatter) o = A.qs.mode == 1 ? q : (int64_t)A.qs.list[q];
+        if (A.scatter) o = qs.mode == 1 ? q : (int64_t)qs.list[q];
         A.out[o + shape * A.out_stride] = sdf;
       }
     }
@@ -1435,29 +1467,30 @@ typedef DecCfg<bf16, 1, 4, 32, 64> CfgB64;
 typedef DecCfg<float, 1, 4, 32, 64> CfgF64;
 
 // workgroups of the persistent decode grid
-template <typename C, bool GATHER>
+template <typename C, bool GATHER, bool RAGGED = false>
 static hipError_t decode_grid(int64_t* grid) {
   constexpr int lds = C::LDS;
   static bool attr = false;
-  const void* fn = reinterpret_cast<const void*>(&decode_kernel<C, GATHER>);
+  const void* fn = reinterpret_cast<const void*>(&decode_kernel<C, GATHER, RAGGED>);
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<C, GATHER>, C::NT, lds);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<C, GATHER, RAGGED>, C::NT, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   *grid = (int64_t)dev_info().cus * per_cu;
   return hipSuccess;
 }
 
-template <typename C, bool GATHER>
+template <typename C, bool GATHER, bool RAGGED = false>
 static hipError_t run(const DecodeArgs& a, hipStream_t s) {
   constexpr int lds = C::LDS;
+  if (!RAGGED && a.batch > 1 && a.tile_prefix) return run<C, GATHER, true>(a, s);
   int64_t grid = 0;
-  hipError_t e = decode_grid<C, GATHER>(&grid);
+  hipError_t e = decode_grid<C, GATHER, RAGGED>(&grid);
   if (e != hipSuccess) return e;
   if (!a.d_N && !a.d_n_items) {
     const int64_t host_tiles = a.items ? a.n_tiles : (a.N + C::BQ - 1) / C::BQ * (a.batch > 1 ? a.batch : 1);
@@ -1465,7 +1498,7 @@ static hipError_t run(const DecodeArgs& a, hipStream_t s) {
     if (host_units < grid) grid = host_units;
   }
   if (grid < 1) return hipSuccess;
-  hipLaunchKernelGGL((decode_kernel<C, GATHER>), dim3((unsigned)grid), dim3(C::NT), lds, s, a);
+  hipLaunchKernelGGL((decode_kernel<C, GATHER, RAGGED>), dim3((unsigned)grid), dim3(C::NT), lds, s, a);
   return hipGetLastError();
 }
 

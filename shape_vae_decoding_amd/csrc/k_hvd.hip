@@ -692,6 +692,52 @@ hipError_t launch_fill(BP<const float> prev, int Pp, BP<float> next, int Pn, int
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ tiles of a batch
+// Exclusive prefix of the per-shape decode units of a batch (each shape's count is
+// on the device, written by its scan): thread t sums the units of shapes
+// t*S .. t*S+S-1 (S = ceil(B / 1024)), the 1024 sums are scanned in LDS, and each
+// thread writes its shapes' prefixes; prefix[B] = every unit.
+constexpr int PREFIX_NT = 1024;
+
+__global__ __launch_bounds__(PREFIX_NT) void batch_prefix_kernel(const int32_t* __restrict__ cnt, int64_t stride, int B,
+                                                                 int per, int64_t* __restrict__ prefix) {
+  __shared__ int64_t part[PREFIX_NT];
+  const int t = threadIdx.x;
+  const int S = (B + PREFIX_NT - 1) / PREFIX_NT;
+  auto units = [&](int b) -> int64_t {
+    const int64_t c = cnt[(int64_t)b * stride];
+    return c > 0 ? (c + per - 1) / per : 0;
+  };
+  int64_t sum = 0;
+  for (int i = 0; i < S; ++i) {
+    const int b = t * S + i;
+    if (b < B) sum += units(b);
+  }
+  part[t] = sum;
+  __syncthreads();
+  for (int o = 1; o < PREFIX_NT; o <<= 1) {  // inclusive scan of the thread sums
+    const int64_t v = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int64_t run = t > 0 ? part[t - 1] : 0;
+  for (int i = 0; i < S; ++i) {
+    const int b = t * S + i;
+    if (b < B) {
+      prefix[b] = run;
+      run += units(b);
+    }
+  }
+  if (t == PREFIX_NT - 1) prefix[B] = part[PREFIX_NT - 1];
+}
+
+hipError_t launch_batch_prefix(const int32_t* cnt, int64_t stride, int B, int per, int64_t* prefix, hipStream_t s) {
+  if (B < 1 || B > 4096 || per < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(batch_prefix_kernel, dim3(1), dim3(PREFIX_NT), 0, s, cnt, stride, B, per, prefix);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ inspection export
 // Row-major byte mask of an n^3 region of a blocked bit mask.
 __global__ void bits_to_bytes_kernel(const uint64_t* __restrict__ m, int n, int NB, uint8_t* __restrict__ out) {

@@ -291,7 +291,8 @@ struct HierWs {
   int32_t* sel_cnt;
   float* sel_scores;
   int64_t* stats;
-  int64_t* part;  // spread partial counters of the mask stages
+  int64_t* part;     // spread partial counters of the mask stages
+  int64_t* bprefix;  // a batch's decode units per shape, prefixed (slice 0 of a batch)
 };
 
 static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M, void* base, HierWs* w) {
@@ -335,6 +336,7 @@ static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M,
   }
   x.stats = c.take<int64_t>((size_t)VDM_MAX_LEVELS * VDM_STAT_FIELDS * 8);
   x.part = c.take<int64_t>((size_t)stat_part_words() * 8);
+  x.bprefix = c.take<int64_t>((size_t)(4096 + 1) * 8);
   if (w) *w = x;
   return c.off + 256;
 }
@@ -935,8 +937,9 @@ vdm_status vdm_select_kv_heads(const vdm_decoder* dec, int32_t R, int32_t block,
 // offset b * kv_bytes, its volume at vol + b * vol_stride floats, its counters at
 // S + b * st_stride int64 and workspace slice ws + b * ws_stride bytes (each
 // slice laid out by hier_ws). Every mask stage is one launch for all B shapes
-// (gridDim.y = B); the decode (and selection) of a level is one launch per
-// shape. The packed epilogue weights of slice 0 serve every shape. dbg: B = 1 only.
+// (gridDim.y = B), and so is the decode of a level; the selection of a level is
+// one launch per shape. The packed epilogue weights of slice 0 serve every shape.
+// dbg: B = 1 only.
 static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int B, const void* K, const void* V,
                            int64_t M, size_t kv_bytes, float* vol, int64_t vol_stride, int64_t* S, int64_t st_stride,
                            const vdm_hier_debug* dbg, void* ws, size_t ws_stride, hipStream_t s) {
@@ -969,12 +972,14 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
   auto vol_of = [&](int L) { return L == p->levels - 1 ? vol : w.vol[L]; };
   auto vstride = [&](int L) { return L == p->levels - 1 ? vst : wst; };
   // list, items and occupied blocks of level L are in w.list / w.items / w.occ
+  // Selection of every shape (one launch per shape), then one decode launch for
+  // all of them: with B > 1 the decode takes its tiles (or work items) shape by
+  // shape from a device-side prefix of the shapes' counts.
   auto decode_level = [&](int L) -> vdm_status {
     const int R = p->R0 << L;
     for (int b = 0; b < B; ++b) {
       int32_t* tot = shape_of(w.totals, b) + 4 * L;
       const void* Kb = off(K, (int64_t)b * kv_bytes);
-      const void* Vb = off(V, (int64_t)b * kv_bytes);
       if (kv) {
         SelectArgs sa;
         memset(&sa, 0, sizeof sa);
@@ -1000,29 +1005,43 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
         sa.per_head = p->heads;
         VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, sa, s), "select launch");
       }
-      DecodeArgs a = packed;
-      a.qs = QuerySrc{VDM_Q_GRID_LIST, R, nullptr, shape_of(w.list, b), 0};
-      a.kmax = shape_of(w.kmax, b);
-      a.out = (float*)((char*)vol_of(L) + (int64_t)b * vstride(L));
-      a.scatter = 1;
-      a.M = (int)M;
-      a.d_N = tot;  // the level's query count (the list length)
-      if (kv) {
-        a.Kp = Kb;
-        a.Vt = Vb;
-        a.items = shape_of(w.items, b);
-        a.d_n_items = tot + 1;
-        a.sel_idx = shape_of(w.sel_idx, b);
-        a.sel_cnt = shape_of(w.sel_cnt, b);
-        a.cap = p->cap;
-        a.heads = p->heads;
-      } else {
-        a.Kp = shape_of(w.Kp, b);
-        a.Vt = shape_of(w.Vt, b);
-      }
-      VDM_HIP_T(kv ? VDM_TIME_DECODE_GATHERED : VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, kv, a, s),
-                "decode launch");
     }
+    int32_t* tot = w.totals + 4 * L;  // shape 0's counts: queries, work items
+    DecodeArgs a = packed;
+    a.qs = QuerySrc{VDM_Q_GRID_LIST, R, nullptr, w.list, 0};
+    a.kmax = w.kmax;
+    a.out = (float*)vol_of(L);
+    a.scatter = 1;
+    a.M = (int)M;
+    a.d_N = tot;  // the level's query count (the list length)
+    if (kv) {
+      a.Kp = K;
+      a.Vt = V;
+      a.items = w.items;
+      a.d_n_items = tot + 1;
+      a.sel_idx = w.sel_idx;
+      a.sel_cnt = w.sel_cnt;
+      a.cap = p->cap;
+      a.heads = p->heads;
+    } else {
+      a.Kp = w.Kp;
+      a.Vt = w.Vt;
+    }
+    if (B > 1) {
+      VDM_HIP_T(VDM_TIME_SCAN, s,
+                launch_batch_prefix(kv ? tot + 1 : tot, wst / 4, B, kv ? 1 : bq, w.bprefix, s), "prefix launch");
+      a.batch = B;
+      a.tile_prefix = w.bprefix;
+      a.cnt_stride = wst / 4;
+      a.list_stride = wst;
+      a.items_stride = wst;
+      a.sel_stride = wst;
+      a.kmax_stride = wst / 4;
+      a.kv_stride = kv ? (int64_t)kv_bytes : wst;
+      a.out_stride = vstride(L) / 4;
+    }
+    VDM_HIP_T(kv ? VDM_TIME_DECODE_GATHERED : VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, kv, a, s),
+              "decode launch");
     return VDM_OK;
   };
 

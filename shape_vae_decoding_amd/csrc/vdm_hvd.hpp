@@ -55,6 +55,9 @@ hipError_t launch_emit(BP<const uint64_t> newmask, BP<const int32_t> counts, BP<
                        BP<const int32_t> occ, BP<const int32_t> tot, int Rn, int bq, BP<int32_t> list,
                        int64_t list_cap, BP<Item> items, int64_t item_cap, int B, hipStream_t s);
 hipError_t launch_fill(BP<const float> prev, int Pp, BP<float> next, int Pn, int B, hipStream_t s);
+// prefix[b] = sum over shapes b' < b of ceil(max(cnt[b' * stride], 0) / per), b = 0 .. B
+// (the tiles or work items of a ragged batched decode); one workgroup, B <= 4096
+hipError_t launch_batch_prefix(const int32_t* cnt, int64_t stride, int B, int per, int64_t* prefix, hipStream_t s);
 hipError_t launch_bits_to_bytes(const uint64_t* m, int n, int NB, uint8_t* out, hipStream_t s);
 hipError_t launch_items_from_list(const int32_t* list, int64_t N, int R, int block, const int32_t* block_row, int bq,
                                   Item* items, int32_t* n_items, float* out, hipStream_t s);

@@ -138,6 +138,19 @@ struct DecodeArgs {
   int batch;
   int64_t kv_stride;
   int64_t out_stride;
+  // ragged batch (batch > 1 and tile_prefix set): shape b has its own device count,
+  // *(d_N + b * cnt_stride) queries (dense tiles of BQ) or *(d_n_items + b *
+  // cnt_stride) work items; tile_prefix[b] = the tiles or items of shapes before b
+  // (tile_prefix[batch] = all of them). Shape b's query list is at qs.list +
+  // b * list_stride bytes, its items at items + b * items_stride bytes, its
+  // selection at sel_idx and sel_cnt + b * sel_stride bytes (each), its key norms at
+  // kmax + b * kmax_stride floats; K/V and outputs use kv_stride and out_stride.
+  const int64_t* tile_prefix = nullptr;
+  int64_t cnt_stride = 0;
+  int64_t list_stride = 0;
+  int64_t items_stride = 0;
+  int64_t sel_stride = 0;
+  int64_t kmax_stride = 0;
   // dense split of the tail (decode_split_plan): the last split_tiles tiles are each
   // cut into `split` ranges of token tiles, one work unit per range; each unit
   // writes its partial O and row sums to part, and the unit that arrives last at a
