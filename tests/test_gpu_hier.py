@@ -289,3 +289,49 @@ def test_hier_batch_fp32_and_one_launch_per_mask_stage():
         V().vdm_decode_hier(dec, params, K[b], Vv[b], one)
         torch.cuda.synchronize()
         assert torch.equal(vol[b], one), b
+
+
+@pytest.mark.parametrize("kvsel", [False, True])
+def test_hier_batch_with_shapes_that_have_no_queries(kvsel):
+    # A shape whose every V row is the same large vector has a constant decoder
+    # output (the softmax weights sum to one), so its SDF stays on one side of
+    # +-tau over the whole volume: no cell is active after level 0 and its later
+    # levels have no queries. In a batch, such shapes (first and in the middle)
+    # contribute no decode tiles or work items, and every shape still equals its
+    # own vdm_decode_hier call bit for bit.
+    w = W.make(1)
+    dec = gpu_decoder(w)
+    params = V().hier_params(R0=16, levels=3, tau=2 * 2 / 64, dilation=1,
+                             kvsel=dict(k=32, cap=256) if kvsel else None)
+    P3 = 65 ** 3
+    K0, V0 = gpu_kv(dec, w)
+    u = torch.from_numpy(np.random.default_rng(31).standard_normal(w.D).astype(np.float32))
+
+    def single(K, Vv):
+        one = torch.empty(P3, dtype=torch.float32, device=dev())
+        st = torch.zeros(3 * V().STAT_FIELDS, dtype=torch.int64, device=dev())
+        V().vdm_decode_hier(dec, params, K, Vv, one, st)
+        torch.cuda.synchronize()
+        return one, st
+
+    flat = None
+    for sign in (1.0, -1.0):
+        Vc = (u * sign * 1000.0).to(V0.dtype).to(dev()).expand(w.M, w.D).contiguous()
+        _, st = single(K0, Vc)
+        levels = V().stats_dict(st, 3)
+        if levels[1]["queries"] == 0 and levels[2]["queries"] == 0:
+            flat = Vc
+            break
+    assert flat is not None, "no constant V made the volume one-signed"
+    Ks = torch.stack([K0, K0, K0, K0]).contiguous()
+    Vs = torch.stack([flat, V0, flat, V0 * 0.9]).contiguous()
+    print(f"[hier batch] empty shapes 0 and 2, kvsel={kvsel}", flush=True)
+    vol = torch.full((4, P3), float("nan"), dtype=torch.float32, device=dev())
+    stats = torch.zeros((4, 3 * V().STAT_FIELDS), dtype=torch.int64, device=dev())
+    V().vdm_decode_hier_batch(dec, params, Ks, Vs, vol, stats)
+    torch.cuda.synchronize()
+    for b in range(4):
+        one, st = single(Ks[b], Vs[b])
+        assert torch.equal(vol[b], one), b
+        assert torch.equal(stats[b], st), b
+    assert V().stats_dict(stats[1], 3)[2]["queries"] > 0
