@@ -526,7 +526,8 @@ def batched_decode(V, W, dec, dev, B: int = 4, R: int = 32, reps: int = 5):
 
 def batched_hier(V, W, dec, dev, params_of, B: int = 4, reps: int = 3):
     """B vecsets through the hierarchical decode: one vdm_decode_hier_batch call
-    (every mask stage one launch for all B shapes) against B single-shape calls,
+    (every mask stage and each level's decode one launch for all B shapes) against
+    B single-shape calls,
     for plain HVD and HVD with KV selection at 75 -> 300, and for 16 small volumes
     (10 -> 20 -> 40) where launch latency dominates (call time, HIP events)."""
     import numpy as np
