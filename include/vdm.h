@@ -307,10 +307,9 @@ vdm_status vdm_decode_hier(const vdm_decoder* dec, const vdm_hier_params* params
  * stats is not NULL, stats + b * levels * VDM_STAT_FIELDS, with workspace slice b
  * of vdm_hier_batch_workspace_size(dec, params, B, M) / B bytes. Every mask stage
  * of a level (cell test, dilation, marking, scans, list emission, fill) is one
- * launch for all B shapes, and so is each level's decode: its tiles (or, with KV
- * selection, work items) run shape after shape in one persistent launch, found
- * from a device-side prefix of the shapes' counts (no host sync). Each level's KV
- * selection is one launch per shape. Shape b's volume and counters equal, bit for bit, those of
+ * launch for all B shapes, and so are each level's KV selection and decode: their
+ * groups of blocks, tiles or work items run shape after shape in one persistent
+ * launch, found from a device-side prefix of the shapes' counts (no host sync). Shape b's volume and counters equal, bit for bit, those of
  * vdm_decode_hier on that shape alone. No inspection outputs. Requires
  * 1 <= B <= 4096. */
 vdm_status vdm_decode_hier_batch(const vdm_decoder* dec, const vdm_hier_params* params, int32_t B,

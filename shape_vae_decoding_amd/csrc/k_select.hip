@@ -341,8 +341,8 @@ struct KTile {
 };
 
 template <typename T, int H>
-__device__ __forceinline__ void load_ktile(const SelectArgs& A, __amdgpu_buffer_rsrc_t kbuf, int kb, int lane,
-                                           KTile<T, H>& t) {
+__device__ __forceinline__ void load_ktile(const SelectArgs& A, const void* Kraw, __amdgpu_buffer_rsrc_t kbuf, int kb,
+                                           int lane, KTile<T, H>& t) {
   using MM = Mma<T>;
   using Frag = typename MM::frag;
   constexpr int KS_H = KTile<T, H>::KS_H;
@@ -358,7 +358,7 @@ __device__ __forceinline__ void load_ktile(const SelectArgs& A, __amdgpu_buffer_
       }
   } else {
     const int key = min(kb * 32 + (lane & 31), A.M - 1);
-    const T* krow = (const T*)A.K + (int64_t)key * (64 * H) + MM::KW * (lane >> 5);
+    const T* krow = (const T*)Kraw + (int64_t)key * (64 * H) + MM::KW * (lane >> 5);
 #pragma unroll
     for (int h = 0; h < H; ++h)
 #pragma unroll
@@ -366,7 +366,9 @@ __device__ __forceinline__ void load_ktile(const SelectArgs& A, __amdgpu_buffer_
   }
 }
 
-template <typename T, int H, bool PH, bool BIG>
+// RG: a ragged batch of shapes (grp_prefix); a separate instance, so that the
+// single-shape kernels keep their registers.
+template <typename T, int H, bool PH, bool BIG, bool RG>
 __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   extern __shared__ __align__(16) char lds[];
   using MM = Mma<T>;
@@ -389,26 +391,68 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
   int* cand = reinterpret_cast<int*>(lds + CF::cand(M)) + wave * SEL_LIST;          // chunked rows: token list
   const __amdgpu_buffer_rsrc_t sbuf =
       __builtin_amdgcn_make_buffer_rsrc(scores, (short)0, SEL_BQ * NS * Mp * 4, 0x00020000 /* raw buffer */);
-  const int64_t nblk = A.d_n_blocks ? (int64_t)*A.d_n_blocks : A.n_blocks;
-  const int64_t ngroups = (nblk + SEL_GB - 1) / SEL_GB;
-  const __amdgpu_buffer_rsrc_t kbuf =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(A.Kp), (short)0, sizeof(T) == 2 ? (M + 31) / 32 * 32 * D * 2 : 0,
-                                        0x00020000 /* raw buffer */);
-  QuerySrc qs;
-  qs.mode = 3;
-  qs.R = A.R;
-  qs.xyz = nullptr;
-  qs.list = A.blocks;
-  qs.block = A.block;
-  qs.probes = A.probes;
-  qs.seed = A.seed;
+  const int64_t nblk_all = A.d_n_blocks ? (int64_t)*A.d_n_blocks : A.n_blocks;
+  const int64_t ngroups = RG ? A.grp_prefix[A.batch] : (nblk_all + SEL_GB - 1) / SEL_GB;
+  // a shape's inputs (RG: per group; otherwise shape 0's, once)
+  struct In {
+    const int32_t* blocks;
+    const void* Kraw;
+    int32_t* sel_idx;
+    int32_t* sel_cnt;
+    int64_t* stat_selected;
+    __amdgpu_buffer_rsrc_t kbuf;
+  };
+  auto inputs_of = [&](int shape) {
+    auto at = [&](auto* p, int64_t stride) { return (decltype(p))((char*)p + shape * stride); };
+    In in;
+    in.blocks = A.blocks ? at(A.blocks, A.blocks_stride) : nullptr;
+    in.Kraw = at(A.K, A.k_stride);
+    in.sel_idx = at(A.sel_idx, A.sel_stride);
+    in.sel_cnt = at(A.sel_cnt, A.sel_stride);
+    in.stat_selected = A.stat_selected ? at(A.stat_selected, A.stat_stride) : nullptr;
+    in.kbuf = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(at(A.Kp, A.kp_stride)), (short)0,
+                                                sizeof(T) == 2 ? (M + 31) / 32 * 32 * D * 2 : 0,
+                                                0x00020000 /* raw buffer */);
+    return in;
+  };
+  const In in0 = inputs_of(0);
   const int nkb = (M + 31) / 32;
   const int per = (nkb + SEL_NW - 1) / SEL_NW;
   const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
   const float NEG = -__builtin_inff();
 
   for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-    const int64_t row0 = grp * SEL_GB;
+    // this group's shape (ragged batch: grp_prefix[shape] <= grp < grp_prefix[shape + 1];
+    // a shape without blocks has equal neighbours and is passed over) and its inputs
+    int64_t lgrp = grp, nblk = nblk_all;
+    In in = in0;
+    if constexpr (RG) {
+      int lo = 0;
+#pragma unroll
+      for (int step = 2048; step >= 1; step >>= 1) {  // (batches of at most 4096 shapes)
+        const int mid = lo + step;
+        lo = mid < A.batch && A.grp_prefix[mid] <= grp ? mid : lo;
+      }
+      const int shape = __builtin_amdgcn_readfirstlane(lo);
+      lgrp = grp - A.grp_prefix[shape];
+      nblk = A.d_n_blocks[shape * A.cnt_stride];
+      in = inputs_of(shape);
+    }
+    const int32_t* blocks = in.blocks;
+    const void* Kraw = in.Kraw;
+    int32_t* sel_idx = in.sel_idx;
+    int32_t* sel_cnt = in.sel_cnt;
+    int64_t* stat_selected = in.stat_selected;
+    const __amdgpu_buffer_rsrc_t kbuf = in.kbuf;
+    QuerySrc qs;
+    qs.mode = 3;
+    qs.R = A.R;
+    qs.xyz = nullptr;
+    qs.list = blocks;
+    qs.block = A.block;
+    qs.probes = A.probes;
+    qs.seed = A.seed;
+    const int64_t row0 = lgrp * SEL_GB;
     const int nb = (int)min<int64_t>(SEL_GB, nblk - row0);
     // thread and lane indices re-derived opaquely per phase, so the address
     // arithmetic of a phase is not hoisted out of the group loop (and kept live
@@ -421,12 +465,12 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
     auto over_key_tiles = [&](auto&& work) {
       if (kb0 >= kb1) return;
       KTile<T, H> ta, tb;
-      load_ktile<T, H>(A, kbuf, kb0, lane, ta);
+      load_ktile<T, H>(A, Kraw, kbuf, kb0, lane, ta);
       int kb = kb0;
       for (; kb + 1 < kb1; kb += 2) {
-        load_ktile<T, H>(A, kbuf, kb + 1, lane, tb);
+        load_ktile<T, H>(A, Kraw, kbuf, kb + 1, lane, tb);
         work(ta, kb);
-        load_ktile<T, H>(A, kbuf, kb + 2 < kb1 ? kb + 2 : kb1 - 1, lane, ta);
+        load_ktile<T, H>(A, Kraw, kbuf, kb + 2 < kb1 ? kb + 2 : kb1 - 1, lane, ta);
         work(tb, kb + 1);
       }
       if (kb < kb1) work(ta, kb);
@@ -675,11 +719,11 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
 #if VDM_DEBUG
       if (lane == 0) {
         const int NBs = (A.R + A.block) / A.block;
-        const int64_t bid = A.blocks ? A.blocks[row0 + blk] : row0 + blk;
+        const int64_t bid = blocks ? blocks[row0 + blk] : row0 + blk;
         (void)VDM_BOUND(bid >= 0 && bid < (int64_t)NBs * NBs * NBs, BC_SELECT_BLOCK);
       }
 #endif
-      int32_t* out = A.sel_idx + row * (int64_t)A.cap;
+      int32_t* out = sel_idx + row * (int64_t)A.cap;
       int base = 0;
       for (int w0 = 0; w0 < nwords; w0 += 64) {
         const int wi = w0 + lane;
@@ -697,39 +741,42 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs A) {
       }
       for (int i = base + lane; i < A.cap; i += 64) out[i] = -1;
       if (lane == 0) {
-        A.sel_cnt[row] = base;
+        sel_cnt[row] = base;
         ucount[set] = base;
       }
     }
     __syncthreads();
-    if (tid == 0 && A.stat_selected) {
+    if (tid == 0 && stat_selected) {
       int64_t t = 0;
       for (int b = 0; b < nb * NS; ++b) t += ucount[b];
-      atomicAdd((unsigned long long*)A.stat_selected, (unsigned long long)t);
+      atomicAdd((unsigned long long*)stat_selected, (unsigned long long)t);
     }
   }
 }
 
-template <typename T, int H, bool PH, bool BIG>
+template <typename T, int H, bool PH, bool BIG, bool RG = false>
 static hipError_t run_select(const SelectArgs& a, hipStream_t s) {
+  if (!RG && a.batch > 1 && a.grp_prefix) return run_select<T, H, PH, BIG, true>(a, s);
   const int lds = SelCfg<T, H, PH ? H : 1>::total(a.M);
-  const void* fn = reinterpret_cast<const void*>(&select_kernel<T, H, PH, BIG>);
+  const void* fn = reinterpret_cast<const void*>(&select_kernel<T, H, PH, BIG, RG>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   int64_t grid = dev_info().cus;
   if (grid > SEL_GRID_MAX) grid = SEL_GRID_MAX;
-  if (!a.d_n_blocks) {
+  if (!a.d_n_blocks) {  // (a ragged batch counts on the device)
     const int64_t groups = (a.n_blocks + SEL_GB - 1) / SEL_GB;
     if (groups < grid) grid = groups;
   }
   if (grid < 1) return hipSuccess;
-  hipLaunchKernelGGL((select_kernel<T, H, PH, BIG>), dim3((unsigned)grid), dim3(SEL_NT), lds, s, a);
+  hipLaunchKernelGGL((select_kernel<T, H, PH, BIG, RG>), dim3((unsigned)grid), dim3(SEL_NT), lds, s, a);
   return hipGetLastError();
 }
 
 size_t select_scratch_bytes(int M, int sets) {
   return (size_t)SEL_GRID_MAX * SEL_BQ * sets * sel_mpad(M) * sizeof(float);
 }
+
+int select_blocks_per_group() { return SEL_GB; }
 
 int select_max_tokens(bool per_head) { return per_head ? SEL_MAX_M_PH : SEL_MAX_M; }
 

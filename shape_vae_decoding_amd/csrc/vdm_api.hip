@@ -937,9 +937,8 @@ vdm_status vdm_select_kv_heads(const vdm_decoder* dec, int32_t R, int32_t block,
 // offset b * kv_bytes, its volume at vol + b * vol_stride floats, its counters at
 // S + b * st_stride int64 and workspace slice ws + b * ws_stride bytes (each
 // slice laid out by hier_ws). Every mask stage is one launch for all B shapes
-// (gridDim.y = B), and so is the decode of a level; the selection of a level is
-// one launch per shape. The packed epilogue weights of slice 0 serve every shape.
-// dbg: B = 1 only.
+// (gridDim.y = B), and so are the selection and the decode of a level. The packed
+// epilogue weights of slice 0 serve every shape. dbg: B = 1 only.
 static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int B, const void* K, const void* V,
                            int64_t M, size_t kv_bytes, float* vol, int64_t vol_stride, int64_t* S, int64_t st_stride,
                            const vdm_hier_debug* dbg, void* ws, size_t ws_stride, hipStream_t s) {
@@ -972,14 +971,14 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
   auto vol_of = [&](int L) { return L == p->levels - 1 ? vol : w.vol[L]; };
   auto vstride = [&](int L) { return L == p->levels - 1 ? vst : wst; };
   // list, items and occupied blocks of level L are in w.list / w.items / w.occ
-  // Selection of every shape (one launch per shape), then one decode launch for
-  // all of them: with B > 1 the decode takes its tiles (or work items) shape by
-  // shape from a device-side prefix of the shapes' counts.
+  // The selection, then the decode, each one launch for all shapes: with B > 1
+  // they take their groups of blocks, tiles or work items shape by shape from a
+  // device-side prefix of the shapes' counts.
   auto decode_level = [&](int L) -> vdm_status {
     const int R = p->R0 << L;
-    for (int b = 0; b < B; ++b) {
-      int32_t* tot = shape_of(w.totals, b) + 4 * L;
-      const void* Kb = off(K, (int64_t)b * kv_bytes);
+    {
+      int32_t* tot = w.totals + 4 * L;  // shape 0's counts: queries, work items, occupied blocks
+      const void* Kb = K;
       if (kv) {
         SelectArgs sa;
         memset(&sa, 0, sizeof sa);
@@ -994,15 +993,28 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
         sa.D = dec->D;
         sa.Wq = dec->Wq;
         sa.K = Kb;
-        sa.Kp = shape_of(w.Kp, b);
-        sa.blocks = shape_of(w.occ, b);
+        sa.Kp = w.Kp;
+        sa.blocks = w.occ;
         sa.n_blocks = 0;
         sa.d_n_blocks = tot + 2;
-        sa.sel_idx = shape_of(w.sel_idx, b);
-        sa.sel_cnt = shape_of(w.sel_cnt, b);
-        sa.stat_selected = S + (int64_t)b * st_stride + L * VDM_STAT_FIELDS + VDM_STAT_SELECTED;
-        sa.scores = shape_of(w.sel_scores, b);
+        sa.sel_idx = w.sel_idx;
+        sa.sel_cnt = w.sel_cnt;
+        sa.stat_selected = S + L * VDM_STAT_FIELDS + VDM_STAT_SELECTED;
+        sa.scores = w.sel_scores;  // (per workgroup, so slice 0's serves the batch)
         sa.per_head = p->heads;
+        if (B > 1) {
+          VDM_HIP_T(VDM_TIME_SCAN, s,
+                    launch_batch_prefix(tot + 2, wst / 4, B, select_blocks_per_group(), w.bprefix, s),
+                    "prefix launch");
+          sa.batch = B;
+          sa.grp_prefix = w.bprefix;
+          sa.cnt_stride = wst / 4;
+          sa.blocks_stride = wst;
+          sa.k_stride = (int64_t)kv_bytes;
+          sa.kp_stride = wst;
+          sa.sel_stride = wst;
+          sa.stat_stride = sst;
+        }
         VDM_HIP_T(VDM_TIME_SELECT, s, launch_select(dec->dtype, sa, s), "select launch");
       }
     }

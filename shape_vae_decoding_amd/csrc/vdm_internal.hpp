@@ -221,8 +221,17 @@ struct SelectArgs {
   int64_t* stat_selected;  // optional: += sum of sel_cnt
   float* scores;           // scratch of select_scratch_bytes(M, per_head ? H : 1)
   int per_head;            // 1: one set per (block, head), rows [block][H]; 0: one per block
+  // ragged batch (batch > 1): shape b has *(d_n_blocks + b * cnt_stride) blocks;
+  // grp_prefix[b] = the groups of SEL_GB blocks of shapes before b (grp_prefix[batch]
+  // = all). Shape b's block list, K, packed K, selection (sel_idx and sel_cnt each)
+  // and counter are at byte offsets b * blocks_stride, b * k_stride, b * kp_stride,
+  // b * sel_stride and b * stat_stride; the score scratch is per workgroup.
+  int batch = 1;
+  const int64_t* grp_prefix = nullptr;
+  int64_t cnt_stride = 0, blocks_stride = 0, k_stride = 0, kp_stride = 0, sel_stride = 0, stat_stride = 0;
 };
 hipError_t launch_select(int dtype, const SelectArgs& a, hipStream_t s);
+int select_blocks_per_group();  // blocks one workgroup of the selection takes at a time
 size_t select_scratch_bytes(int M, int sets);
 // largest token count of a selection; whether (M, k, cap) fits the kernel's lists
 int select_max_tokens(bool per_head);
