@@ -568,29 +568,32 @@ def batched_hier(V, W, dec, dev, params_of, B: int = 4, reps: int = 3):
         r["ms_per_volume_single"] = round(r["single_calls"] / B, 3)
         res[mode] = {"ms_per_batch": r, "speedup": round(r["single_calls"] / r["batched"], 3)}
         del vol, ws_b, ws_1
-    # many small volumes: 16 shapes at 10 -> 20 -> 40 (41^3 points)
+    # many small volumes: 16 shapes at 10 -> 20 -> 40 (41^3 points), without and
+    # with KV selection (k = 64, cap 512)
     Bs = 16
     Ks16 = torch.stack([K[b % B] for b in range(Bs)]).contiguous()
     Vs16 = torch.stack([Vv[b % B] for b in range(Bs)]).contiguous()
-    params = V.hier_params(R0=10, levels=3, tau=2 * 2 / 40, dilation=1)
-    P3 = 41 ** 3
-    vol = torch.empty((Bs, P3), dtype=torch.float32, device=dev)
-    ws_b = V.workspace(V.vdm_hier_batch_workspace_size(dec, params, Bs, w.M), dev)
-    ws_1 = V.workspace(V.vdm_hier_workspace_size(dec, params, w.M), dev)
-    r = {}
-    for name, fn in (("batched", lambda: V.vdm_decode_hier_batch(dec, params, Ks16, Vs16, vol, ws=ws_b)),
-                     ("single_calls", lambda: [V.vdm_decode_hier(dec, params, Ks16[b], Vs16[b], vol[b], ws=ws_1)
-                                               for b in range(Bs)])):
-        fn()
-        torch.cuda.synchronize()
-        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
+    for key, kvsel in (("hvd_16x41cubed", None), ("hvd_akvs_16x41cubed", dict(k=64, cap=512))):
+        params = V.hier_params(R0=10, levels=3, tau=2 * 2 / 40, dilation=1, kvsel=kvsel)
+        P3 = 41 ** 3
+        vol = torch.empty((Bs, P3), dtype=torch.float32, device=dev)
+        ws_b = V.workspace(V.vdm_hier_batch_workspace_size(dec, params, Bs, w.M), dev)
+        ws_1 = V.workspace(V.vdm_hier_workspace_size(dec, params, w.M), dev)
+        r = {}
+        for name, fn in (("batched", lambda: V.vdm_decode_hier_batch(dec, params, Ks16, Vs16, vol, ws=ws_b)),
+                         ("single_calls", lambda: [V.vdm_decode_hier(dec, params, Ks16[b], Vs16[b], vol[b], ws=ws_1)
+                                                   for b in range(Bs)])):
             fn()
-        e.record()
-        torch.cuda.synchronize()
-        r[name] = round(a.elapsed_time(e) / reps, 3)
-    res["hvd_16x41cubed"] = {"shapes": Bs, "ms_per_batch": r, "speedup": round(r["single_calls"] / r["batched"], 3)}
+            torch.cuda.synchronize()
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            r[name] = round(a.elapsed_time(e) / reps, 3)
+        res[key] = {"shapes": Bs, "ms_per_batch": r, "speedup": round(r["single_calls"] / r["batched"], 3)}
+        del vol, ws_b, ws_1
     return res
 
 
