@@ -779,6 +779,9 @@ def main():
             "hier_volume_points_per_s": round(Pf ** 3 / (row_ms[2] / 1e3), 1),
             "akvs_ms_per_300cubed_volume": round(float(row_ms[3]), 4),
             "akvs_volume_points_per_s": round(Pf ** 3 / (row_ms[3] / 1e3), 1),
+            "median_min_ms_over_timed_steps": {
+                name: [round(float(np.median(rows[:, j])), 4), round(float(rows[:, j].min()), 4)]
+                for j, name in enumerate(["kv_projection", "dense_129cubed", "hier_300cubed", "akvs_300cubed"])},
             "kernel_kinds_one_step": kinds,
             "hier_levels": sh,
             "akvs_levels": sa,
@@ -866,7 +869,9 @@ def main():
         loc["vs_dense_200k_x_40960"] = round(out["breakdown"]["large_tokens_200k_points"]["launch_ms"] / loc["call_ms"], 2)
         out["breakdown"]["local_knn_200k_points"] = loc
         props = torch.cuda.get_device_properties(0)
-        out["breakdown"]["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
+        di = V.vdm_device_info()
+        out["breakdown"]["device"] = {"name": props.name, "compute_units": di["compute_units"],
+                                      "peak_sclk_MHz": round(di["peak_clock_khz"] / 1e3, 1),
                                       "copy_GB_per_s": copy_bandwidth(dev), "hbm_peak_GB_per_s": PEAK_HBM_GBS}
     if args.copy_calib:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

@@ -445,6 +445,11 @@ vdm_status vdm_timing_read(int32_t kind, int64_t* launches, double* total_ms);
 /* VDM_VERSION of the built library. */
 int32_t vdm_version(void);
 
+/* The current HIP device's compute units and peak shader clock in kHz, as the
+ * runtime reports them (the figures the bf16 MFMA peak is quoted at). Either
+ * pointer may be NULL. VDM_ERR_HIP when the runtime has no device. */
+vdm_status vdm_device_info(int32_t* compute_units, int32_t* peak_clock_khz);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* vdm_last_error(void);
 

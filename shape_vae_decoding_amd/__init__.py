@@ -36,7 +36,7 @@ EXPORTS = [
     "vdm_timing_read", "vdm_version", "vdm_last_error", "vdm_extract_surface", "vdm_surface_workspace_size",
     "vdm_decode_dense_batch", "vdm_dense_batch_workspace_size", "vdm_decode_hier_batch",
     "vdm_hier_batch_workspace_size", "vdm_decode_dense_noalloc", "vdm_decode_local", "vdm_local_workspace_size",
-    "vdm_select_kv_heads", "vdm_select_heads_workspace_size",
+    "vdm_select_kv_heads", "vdm_select_heads_workspace_size", "vdm_device_info",
 ]
 TIME_KINDS = ["decode", "decode_gathered", "select", "embed", "project_kv", "cell_test", "dilate", "mark", "scan",
               "emit", "fill", "surface", "local_grid", "local_knn", "local_fuse", "local_head"]
@@ -152,6 +152,8 @@ def _bind(lib) -> None:
     lib.vdm_timing_read.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
     lib.vdm_timing_read.restype = C.c_int
     lib.vdm_version.restype = C.c_int32
+    lib.vdm_device_info.argtypes = [C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
+    lib.vdm_device_info.restype = _st
     lib.vdm_last_error.restype = C.c_char_p
 
 
@@ -174,6 +176,12 @@ def debug_library():
 
 def vdm_version() -> int:
     return int(_lib.vdm_version())
+
+
+def vdm_device_info() -> dict:
+    cus, khz = C.c_int32(0), C.c_int32(0)
+    _check(_lib.vdm_device_info(C.byref(cus), C.byref(khz)))
+    return {"compute_units": cus.value, "peak_clock_khz": khz.value}
 
 
 def vdm_last_error() -> str:

@@ -449,6 +449,16 @@ vdm_status vdm_timing_read(int32_t kind, int64_t* launches, double* total_ms) {
 
 int32_t vdm_version(void) { return VDM_VERSION; }
 
+vdm_status vdm_device_info(int32_t* compute_units, int32_t* peak_clock_khz) {
+  int dev = 0, cus = 0, khz = 0;
+  VDM_HIP(hipGetDevice(&dev), "no HIP device");
+  VDM_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "device attribute");
+  VDM_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev), "device attribute");
+  if (compute_units) *compute_units = cus;
+  if (peak_clock_khz) *peak_clock_khz = khz;
+  return VDM_OK;
+}
+
 size_t vdm_dense_workspace_size(const vdm_decoder* dec, int64_t M, int64_t N, int32_t with_sel) {
   if (check_decoder(dec) != VDM_OK) return 0;
   if (M < 1 || N < 0) {

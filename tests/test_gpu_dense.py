@@ -384,3 +384,11 @@ def test_batched_decode_equals_single_shape_calls_bitwise(mode):
     err = np.abs(out[0].cpu().numpy()[pick].astype(np.float64) - ref).max()
     report(f"batched decode ({mode}), shape 0 vs oracle", err, TOL_BF16)
     assert err <= TOL_BF16
+
+
+def test_device_info_matches_the_runtime():
+    # compute units as torch reports them; a peak shader clock in a plausible range
+    di = V().vdm_device_info()
+    props = torch.cuda.get_device_properties(0)
+    assert di["compute_units"] == props.multi_processor_count
+    assert 500_000 <= di["peak_clock_khz"] <= 5_000_000, di
