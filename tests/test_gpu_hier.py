@@ -213,7 +213,7 @@ def test_hier_computed_points_equal_dense_decode():
     assert flips <= 1e-4 * inh.sum()
 
 
-@pytest.mark.parametrize("kvsel", [False, True])
+@pytest.mark.parametrize("kvsel", [False, True, "heads", "random"])
 def test_hier_batch_equals_single_shape_calls_bitwise(kvsel):
     # B = 5 vecsets through vdm_decode_hier_batch (every mask stage one launch for
     # the five shapes): each shape's volume and counters equal its own
@@ -226,8 +226,10 @@ def test_hier_batch_equals_single_shape_calls_bitwise(kvsel):
     KV = [gpu_kv(dec, w, Z) for Z in Zs]
     K = torch.stack([k for k, _ in KV]).contiguous()
     Vv = torch.stack([v for _, v in KV]).contiguous()
-    params = V().hier_params(R0=24, levels=3, tau=2 * 2 / 96, dilation=1,
-                             kvsel=dict(k=32, cap=256) if kvsel else None)
+    # KV selection with one set per block, one per (block, head), or random probes
+    sel = {False: None, True: dict(k=32, cap=256), "heads": dict(k=32, cap=256, heads=True),
+           "random": dict(k=32, cap=256, probes="random", seed=7)}[kvsel]
+    params = V().hier_params(R0=24, levels=3, tau=2 * 2 / 96, dilation=1, kvsel=sel)
     B, P3 = len(Zs), 97 ** 3
     print(f"[hier batch] B={B} kvsel={kvsel} R0=24 levels=3", flush=True)
     vol = torch.full((B, P3), float("nan"), dtype=torch.float32, device=dev())
