@@ -23,11 +23,19 @@ namespace vdm {
 // lane's run contiguous) makes every such load touch 4 KB and halves the
 // vector-memory throughput. Tokens past M are zero.
 
+// A batch of shapes runs on the second grid dimension: shape blockIdx.y reads K
+// and V at byte offset y * in_stride and writes Kp and Vt at y * out_stride.
 template <typename T>
 __global__ void pack_kv_kernel(const T* __restrict__ K, const T* __restrict__ V, int M, int D, int Mpad,
-                               T* __restrict__ Kp, T* __restrict__ Vt) {
+                               T* __restrict__ Kp, T* __restrict__ Vt, int64_t in_stride, int64_t out_stride) {
   using MM = Mma<T>;
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  K = reinterpret_cast<const T*>((const char*)K + blockIdx.y * in_stride);
+  Kp = reinterpret_cast<T*>((char*)Kp + blockIdx.y * out_stride);
+  if (Vt) {
+    V = reinterpret_cast<const T*>((const char*)V + blockIdx.y * in_stride);
+    Vt = reinterpret_cast<T*>((char*)Vt + blockIdx.y * out_stride);
+  }
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (int64_t)Mpad * D;
   if (i >= n) return;
@@ -72,26 +80,30 @@ hipError_t launch_pack_w(const void* W, int rows, int cols, void* Wp, hipStream_
 }
 
 hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D, int Mpad, void* Kp,
-                          void* Vt, hipStream_t s) {
+                          void* Vt, hipStream_t s, int B, int64_t in_stride, int64_t out_stride) {
   const int64_t n = (int64_t)Mpad * D;
   const int bs = 256;
-  const dim3 g((unsigned)((n + bs - 1) / bs));
+  const dim3 g((unsigned)((n + bs - 1) / bs), (unsigned)B);
   if (dtype == VDM_BF16)
     hipLaunchKernelGGL(pack_kv_kernel<bf16>, g, dim3(bs), 0, s, (const bf16*)K, (const bf16*)V, M, D, Mpad,
-                       (bf16*)Kp, (bf16*)Vt);
+                       (bf16*)Kp, (bf16*)Vt, in_stride, out_stride);
   else
     hipLaunchKernelGGL(pack_kv_kernel<float>, g, dim3(bs), 0, s, (const float*)K, (const float*)V, M, D, Mpad,
-                       (float*)Kp, (float*)Vt);
+                       (float*)Kp, (float*)Vt, in_stride, out_stride);
   return hipGetLastError();
 }
 
 // kmax[h] = max over tokens of the Euclidean norm of head h's 64 key columns
 // (float32; norms are non-negative, so their bit patterns order like integers).
 // Thread i takes token i / H, head i % H (16-byte loads); the lanes of a wave that
-// share a head reduce first, so each wave issues H atomics. H divides 64.
+// share a head reduce first, so each wave issues H atomics. H divides 64. A batch
+// of shapes runs on the second grid dimension (K and kmax at byte strides).
 template <typename T>
-__global__ void key_norms_kernel(const T* __restrict__ K, int M, int H, float* kmax) {
+__global__ void key_norms_kernel(const T* __restrict__ K, int M, int H, float* kmax, int64_t k_stride,
+                                 int64_t kmax_stride) {
   constexpr int EPC = 16 / (int)sizeof(T);
+  K = reinterpret_cast<const T*>((const char*)K + blockIdx.y * k_stride);
+  kmax = reinterpret_cast<float*>((char*)kmax + blockIdx.y * kmax_stride);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int h = (int)(i % H);
   float s = 0.f;
@@ -110,13 +122,15 @@ __global__ void key_norms_kernel(const T* __restrict__ K, int M, int H, float* k
   if ((threadIdx.x & 63) < H) atomicMax(reinterpret_cast<unsigned*>(kmax + h), __float_as_uint(n));
 }
 
-hipError_t launch_key_norms(int dtype, const void* K, int M, int H, float* kmax, hipStream_t s) {
+hipError_t launch_key_norms(int dtype, const void* K, int M, int H, float* kmax, hipStream_t s, int B,
+                            int64_t k_stride, int64_t kmax_stride) {
   const int64_t n = (int64_t)M * H;
-  const dim3 g((unsigned)((n + 255) / 256));
+  const dim3 g((unsigned)((n + 255) / 256), (unsigned)B);
   if (dtype == VDM_BF16)
-    hipLaunchKernelGGL(key_norms_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)K, M, H, kmax);
+    hipLaunchKernelGGL(key_norms_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)K, M, H, kmax, k_stride, kmax_stride);
   else
-    hipLaunchKernelGGL(key_norms_kernel<float>, g, dim3(256), 0, s, (const float*)K, M, H, kmax);
+    hipLaunchKernelGGL(key_norms_kernel<float>, g, dim3(256), 0, s, (const float*)K, M, H, kmax, k_stride,
+                       kmax_stride);
   return hipGetLastError();
 }
 

@@ -832,13 +832,12 @@ static vdm_status decode_dense_batch_body(const vdm_decoder* dec, const vdm_quer
   const size_t shape_bytes = (size_t)M * dec->D * esize(dec->dtype);
   VDM_HIP(launch_zero(w.kmax, ((size_t)B * dec->H * 4 + 7) / 8 * 8, s), "zero launch");  // (within its 256-byte slot)
   VDM_HIP(pack_weights(dec, w.Wp, a, s), "weight packing launch");
-  for (int b = 0; b < B; ++b) {
-    const char* Kb = (const char*)K + b * shape_bytes;
-    const char* Vb = (const char*)V + b * shape_bytes;
-    VDM_HIP(launch_key_norms(dec->dtype, Kb, (int)M, dec->H, w.kmax + (size_t)b * dec->H, s), "key norms launch");
-    VDM_HIP(launch_pack_kv(dec->dtype, Kb, Vb, (int)M, dec->D, (int)mpad(M), w.Kp + b * w.kv, w.Vt + b * w.kv, s),
-            "pack_kv launch");
-  }
+  // every shape's key norms and packed K/V, one launch each for the batch
+  VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s, B, (int64_t)shape_bytes, (int64_t)dec->H * 4),
+          "key norms launch");
+  VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s, B, (int64_t)shape_bytes,
+                         (int64_t)w.kv),
+          "pack_kv launch");
   a.Kp = w.Kp;
   a.Vt = w.Vt;
   a.M = (int)M;
@@ -963,17 +962,16 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
   VDM_HIP(launch_stats_init(bp(S, sst), p->levels, p->R0, B, s), "stats init");
   VDM_HIP(launch_zero_b(BP<void>{w.part, wst}, (size_t)stat_part_words() * 8, B, s), "zero launch");
   VDM_HIP(launch_zero_b(BP<void>{w.kmax, wst}, 256, B, s), "zero launch");
-  for (int b = 0; b < B; ++b) {
-    const void* Kb = off(K, (int64_t)b * kv_bytes);
-    const void* Vb = off(V, (int64_t)b * kv_bytes);
-    VDM_HIP(launch_key_norms(dec->dtype, Kb, (int)M, dec->H, shape_of(w.kmax, b), s), "key norms launch");
-    if (!kv)
-      VDM_HIP(launch_pack_kv(dec->dtype, Kb, Vb, (int)M, dec->D, (int)mpad(M), shape_of(w.Kp, b), shape_of(w.Vt, b), s),
-              "pack_kv launch");
-    else if (dec->dtype == VDM_BF16)  // the selection streams packed K
-      VDM_HIP(launch_pack_kv(dec->dtype, Kb, nullptr, (int)M, dec->D, (int)mpad(M), shape_of(w.Kp, b), nullptr, s),
-              "pack K launch");
-  }
+  // every shape's key norms and packed K/V (packed K only with KV selection, which
+  // streams it; bf16), one launch each for the batch
+  VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s, B, (int64_t)kv_bytes, wst), "key norms launch");
+  if (!kv)
+    VDM_HIP(launch_pack_kv(dec->dtype, K, V, (int)M, dec->D, (int)mpad(M), w.Kp, w.Vt, s, B, (int64_t)kv_bytes, wst),
+            "pack_kv launch");
+  else if (dec->dtype == VDM_BF16)
+    VDM_HIP(launch_pack_kv(dec->dtype, K, nullptr, (int)M, dec->D, (int)mpad(M), w.Kp, nullptr, s, B,
+                           (int64_t)kv_bytes, wst),
+            "pack K launch");
   DecodeArgs packed = base_args(dec);
   VDM_HIP(pack_weights(dec, w.Wp, packed, s), "weight packing launch");
 

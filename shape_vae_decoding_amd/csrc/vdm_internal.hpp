@@ -186,14 +186,17 @@ DevInfo dev_info();
 
 // K, V [M][D] -> per-(32-token tile, head) operand runs of 64 lanes x 32 elements,
 // stored chunk-major (see k_prep.hip); V and Vt may be null (K only)
+// B shapes: K/V at byte stride in_stride, Kp/Vt at out_stride (one launch)
 hipError_t launch_pack_kv(int dtype, const void* K, const void* V, int M, int D, int Mpad, void* Kp,
-                          void* Vt, hipStream_t s);
+                          void* Vt, hipStream_t s, int B = 1, int64_t in_stride = 0, int64_t out_stride = 0);
 // bf16 W [rows][cols] -> MFMA A-operand fragments: block (rb, ks) of 32 rows x 16
 // columns is 64 lanes x 8 elements, lane l holding W[32rb + l%32][16ks + 8(l/32) + 0..7];
 // blocks in (rb, ks) order. rows % 32 == 0, cols % 16 == 0.
 hipError_t launch_pack_w(const void* W, int rows, int cols, void* Wp, hipStream_t s);
 // kmax[h] = max_m ||K[m][64h .. 64h+63]||_2 (kmax must be zeroed first)
-hipError_t launch_key_norms(int dtype, const void* K, int M, int H, float* kmax, hipStream_t s);
+// B shapes: K at byte stride k_stride, kmax at kmax_stride (one launch)
+hipError_t launch_key_norms(int dtype, const void* K, int M, int H, float* kmax, hipStream_t s, int B = 1,
+                            int64_t k_stride = 0, int64_t kmax_stride = 0);
 // K = Z Wk^T, V = Z Wv^T
 hipError_t launch_project_kv(int dtype, const void* Z, const void* Wk, const void* Wv, int M, int D,
                              void* K, void* V, hipStream_t s);
