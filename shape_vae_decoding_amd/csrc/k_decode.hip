@@ -1091,10 +1091,36 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   }
 
   // work units: whole tiles, then (dense tail split) split_tiles tiles of `split`
-  // token ranges each, a tile's ranges on consecutive units
+  // token ranges each, a tile's ranges on consecutive units. Dense tiles cost the
+  // same and go round-robin; gathered work items differ (set sizes, query counts),
+  // so workgroups take them in order from A.queue: thread 0 fetches the next
+  // index at the start of each item (the atomic's latency hides behind the item)
+  // and the loop's end hands it to the workgroup through LDS.
   const int64_t n_whole = n_tiles - A.split_tiles;
   const int64_t n_units = n_whole + A.split_tiles * A.split;
-  for (int64_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+  __shared__ int64_t unit_slot;
+  int64_t pending = 0;  // thread 0: the next work item (gathered)
+  auto fetch = [&] {
+    if (GATHER && tid0 == 0) pending = (int64_t)atomicAdd(A.queue, 1ull);
+  };
+  auto next_unit = [&](int64_t u) -> int64_t {
+    if constexpr (!GATHER) {
+      return u + gridDim.x;
+    } else {
+      if (tid0 == 0) unit_slot = pending;
+      __syncthreads();
+      const int64_t v = unit_slot;
+      __syncthreads();  // (read by every thread before thread 0 writes it again)
+      return v;
+    }
+  };
+  int64_t first = blockIdx.x;
+  if constexpr (GATHER) {
+    fetch();
+    first = next_unit(0);
+  }
+  for (int64_t unit = first; unit < n_units; unit = next_unit(unit)) {
+    fetch();
     int64_t tile = unit;
     int part = -1;  // this unit's token range of a split tile, or -1
     if (!GATHER && unit >= n_whole) {
@@ -1523,6 +1549,7 @@ SplitPlan decode_split_plan(int dtype, int D, int64_t M, int64_t n_tiles) {
 }
 
 hipError_t launch_decode(int dtype, int D, bool gathered, const DecodeArgs& a, hipStream_t s) {
+  if (gathered && !a.queue) return hipErrorInvalidValue;  // (the work-item counter is required)
   if (dtype == VDM_BF16 && D == 256) return gathered ? run<CfgB256, true>(a, s) : run<CfgB256, false>(a, s);
   if (dtype == VDM_BF16 && D == 64) return gathered ? run<CfgB64, true>(a, s) : run<CfgB64, false>(a, s);
   return gathered ? run<CfgF64, true>(a, s) : run<CfgF64, false>(a, s);

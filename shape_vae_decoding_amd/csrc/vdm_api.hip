@@ -293,6 +293,7 @@ struct HierWs {
   int64_t* stats;
   int64_t* part;     // spread partial counters of the mask stages
   int64_t* bprefix;  // a batch's decode units per shape, prefixed (slice 0 of a batch)
+  unsigned long long* queues;  // per level: the gathered decode's work-item counter (slice 0)
 };
 
 static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M, void* base, HierWs* w) {
@@ -337,6 +338,7 @@ static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M,
   x.stats = c.take<int64_t>((size_t)VDM_MAX_LEVELS * VDM_STAT_FIELDS * 8);
   x.part = c.take<int64_t>((size_t)stat_part_words() * 8);
   x.bprefix = c.take<int64_t>((size_t)(4096 + 1) * 8);
+  x.queues = c.take<unsigned long long>((size_t)VDM_MAX_LEVELS * 8);
   if (w) *w = x;
   return c.off + 256;
 }
@@ -750,6 +752,8 @@ static vdm_status decode_dense_body(const vdm_decoder* dec, const vdm_queries* q
     a.sel_cnt = sel->sel_cnt;
     a.cap = sel->cap;
     a.heads = sel->heads;
+    // the work-item queue: byte 128 of the item count's 256-byte slot, zeroed with it
+    a.queue = reinterpret_cast<unsigned long long*>((char*)w.n_items + 128);
     VDM_HIP_T(VDM_TIME_DECODE_GATHERED, s, launch_decode(dec->dtype, dec->D, true, a, s), "gathered decode launch");
   }
   return VDM_OK;
@@ -962,6 +966,7 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
   VDM_HIP(launch_stats_init(bp(S, sst), p->levels, p->R0, B, s), "stats init");
   VDM_HIP(launch_zero_b(BP<void>{w.part, wst}, (size_t)stat_part_words() * 8, B, s), "zero launch");
   VDM_HIP(launch_zero_b(BP<void>{w.kmax, wst}, 256, B, s), "zero launch");
+  if (kv) VDM_HIP(launch_zero(w.queues, (size_t)VDM_MAX_LEVELS * 8, s), "zero launch");
   // every shape's key norms and packed K/V (packed K only with KV selection, which
   // streams it; bf16), one launch each for the batch
   VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s, B, (int64_t)kv_bytes, wst), "key norms launch");
@@ -1043,6 +1048,7 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
       a.sel_cnt = w.sel_cnt;
       a.cap = p->cap;
       a.heads = p->heads;
+      a.queue = w.queues + L;  // (zeroed once, before level 0)
     } else {
       a.Kp = w.Kp;
       a.Vt = w.Vt;

@@ -160,6 +160,9 @@ struct DecodeArgs {
   int64_t split_tiles = 0;
   float* part = nullptr;
   int32_t* part_cnt = nullptr;
+  // gathered mode: a counter, zero before the launch, from which workgroups take
+  // their work items in order (items differ in cost: set sizes and query counts)
+  unsigned long long* queue = nullptr;
 };
 
 // The tail split of a dense full-attention launch of n_tiles tiles over M tokens:
