@@ -1091,31 +1091,30 @@ __global__ __launch_bounds__(C::NT) void decode_kernel(DecodeArgs A) {
   }
 
   // work units: whole tiles, then (dense tail split) split_tiles tiles of `split`
-  // token ranges each, a tile's ranges on consecutive units. Dense tiles cost the
-  // same and go round-robin; gathered work items differ (set sizes, query counts),
-  // so workgroups take them in order from A.queue: thread 0 fetches the next
-  // index at the start of each item (the atomic's latency hides behind the item)
-  // and the loop's end hands it to the workgroup through LDS.
+  // token ranges each, a tile's ranges on consecutive units. Workgroups take units
+  // in order from the counter A.queue (required in gathered mode, where work items
+  // differ in set size and query count; with dense tiles it lets faster compute
+  // units take more of them; without it, units go round-robin): thread 0 fetches
+  // the next index at the start of each unit (the atomic's latency hides behind
+  // the unit) and the loop's end hands it to the workgroup through LDS.
   const int64_t n_whole = n_tiles - A.split_tiles;
   const int64_t n_units = n_whole + A.split_tiles * A.split;
   __shared__ int64_t unit_slot;
   int64_t pending = 0;  // thread 0: the next work item (gathered)
+  const bool dyn = GATHER || A.queue != nullptr;  // (uniform)
   auto fetch = [&] {
-    if (GATHER && tid0 == 0) pending = (int64_t)atomicAdd(A.queue, 1ull);
+    if (dyn && tid0 == 0) pending = (int64_t)atomicAdd(A.queue, 1ull);
   };
   auto next_unit = [&](int64_t u) -> int64_t {
-    if constexpr (!GATHER) {
-      return u + gridDim.x;
-    } else {
-      if (tid0 == 0) unit_slot = pending;
-      __syncthreads();
-      const int64_t v = unit_slot;
-      __syncthreads();  // (read by every thread before thread 0 writes it again)
-      return v;
-    }
+    if (!dyn) return u + gridDim.x;
+    if (tid0 == 0) unit_slot = pending;
+    __syncthreads();
+    const int64_t v = unit_slot;
+    __syncthreads();  // (read by every thread before thread 0 writes it again)
+    return v;
   };
   int64_t first = blockIdx.x;
-  if constexpr (GATHER) {
+  if (dyn) {
     fetch();
     first = next_unit(0);
   }

@@ -253,6 +253,7 @@ struct BatchWs {
   void* Wp;
   float* kmax;
   size_t kv;  // packed bytes per shape (K or V)
+  unsigned long long* queue;  // the decode's work-unit counter
 };
 
 static size_t batch_ws(const vdm_decoder* d, int64_t B, int64_t M, void* base, BatchWs* w) {
@@ -263,6 +264,7 @@ static size_t batch_ws(const vdm_decoder* d, int64_t B, int64_t M, void* base, B
   x.Vt = c.take<char>(x.kv * B);
   x.Wp = c.take<char>(packed_w_bytes(d));
   x.kmax = c.take<float>((size_t)B * d->H * 4);
+  x.queue = c.take<unsigned long long>(256);
   if (w) *w = x;
   return c.off + 256;
 }
@@ -293,7 +295,7 @@ struct HierWs {
   int64_t* stats;
   int64_t* part;     // spread partial counters of the mask stages
   int64_t* bprefix;  // a batch's decode units per shape, prefixed (slice 0 of a batch)
-  unsigned long long* queues;  // per level: the gathered decode's work-item counter (slice 0)
+  unsigned long long* queues;  // per level: the decode's work-unit counter (slice 0)
 };
 
 static size_t hier_ws(const vdm_decoder* d, const vdm_hier_params* p, int64_t M, void* base, HierWs* w) {
@@ -676,6 +678,8 @@ static vdm_status dense_full(const vdm_decoder* dec, const vdm_queries* q, const
     a.part_cnt = w.part_cnt;
     VDM_HIP(launch_zero(w.part_cnt, w.split.cnt_bytes, s), "zero launch");
   }
+  // the work-unit counter: byte 128 of the key-norm slot (256 bytes, zeroed above)
+  a.queue = reinterpret_cast<unsigned long long*>((char*)w.kmax + 128);
   if (timed)
     VDM_HIP_T(VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, false, a, s), "decode launch");
   else
@@ -848,6 +852,8 @@ static vdm_status decode_dense_batch_body(const vdm_decoder* dec, const vdm_quer
   a.batch = B;
   a.kv_stride = (int64_t)w.kv;
   a.out_stride = q->N;
+  VDM_HIP(launch_zero(w.queue, 256, s), "zero launch");
+  a.queue = w.queue;
   VDM_HIP_T(VDM_TIME_DECODE, s, launch_decode(dec->dtype, dec->D, false, a, s), "batched decode launch");
   return VDM_OK;
 }
@@ -966,7 +972,7 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
   VDM_HIP(launch_stats_init(bp(S, sst), p->levels, p->R0, B, s), "stats init");
   VDM_HIP(launch_zero_b(BP<void>{w.part, wst}, (size_t)stat_part_words() * 8, B, s), "zero launch");
   VDM_HIP(launch_zero_b(BP<void>{w.kmax, wst}, 256, B, s), "zero launch");
-  if (kv) VDM_HIP(launch_zero(w.queues, (size_t)VDM_MAX_LEVELS * 8, s), "zero launch");
+  VDM_HIP(launch_zero(w.queues, (size_t)VDM_MAX_LEVELS * 8, s), "zero launch");
   // every shape's key norms and packed K/V (packed K only with KV selection, which
   // streams it; bf16), one launch each for the batch
   VDM_HIP(launch_key_norms(dec->dtype, K, (int)M, dec->H, w.kmax, s, B, (int64_t)kv_bytes, wst), "key norms launch");
@@ -1048,11 +1054,11 @@ static vdm_status hier_run(const vdm_decoder* dec, const vdm_hier_params* p, int
       a.sel_cnt = w.sel_cnt;
       a.cap = p->cap;
       a.heads = p->heads;
-      a.queue = w.queues + L;  // (zeroed once, before level 0)
     } else {
       a.Kp = w.Kp;
       a.Vt = w.Vt;
     }
+    a.queue = w.queues + L;  // the level's work-unit counter (zeroed once, before level 0)
     if (B > 1) {
       VDM_HIP_T(VDM_TIME_SCAN, s,
                 launch_batch_prefix(kv ? tot + 1 : tot, wst / 4, B, kv ? 1 : bq, w.bprefix, s), "prefix launch");

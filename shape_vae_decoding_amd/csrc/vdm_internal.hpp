@@ -160,8 +160,8 @@ struct DecodeArgs {
   int64_t split_tiles = 0;
   float* part = nullptr;
   int32_t* part_cnt = nullptr;
-  // gathered mode: a counter, zero before the launch, from which workgroups take
-  // their work items in order (items differ in cost: set sizes and query counts)
+  // a counter, zero before the launch, from which workgroups take their work units
+  // in order (required in gathered mode; null: dense units go round-robin)
   unsigned long long* queue = nullptr;
 };
 
